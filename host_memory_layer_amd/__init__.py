@@ -1,0 +1,352 @@
+"""Python binding of libmt.so, the MI355X layer-streamed training library.
+
+Argument marshalling only: every step of the training step runs in the HIP
+library (include/mt.h, include/mt_kernels.h).  PyTorch provides the device
+arena and the three streams; the pinned host store comes from the library.
+The binding raises if the library has not been built — there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libmt.so")
+
+MT_OK = 0
+MT_E_INVALID, MT_E_SIZE, MT_E_ALIGN, MT_E_NOT_BOUND, MT_E_HIP, MT_E_NONFINITE, MT_E_OOM, MT_E_STATE = range(-1, -9, -1)
+MT_F32, MT_BF16 = 0, 1
+MT_STREAMED, MT_SERIALIZED, MT_RESIDENT = 0, 1, 2
+MODES = {"streamed": MT_STREAMED, "serialized": MT_SERIALIZED, "resident": MT_RESIDENT}
+MT_BLOCK_EMBED, MT_BLOCK_LAYER, MT_BLOCK_HEAD = 0, 1, 2
+MT_FLAG_TIME_KERNELS, MT_FLAG_POISON = 1, 2
+EPI_STORE, EPI_F32, EPI_ADD_F32 = 0, 1, 2
+
+
+class MtConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("n_layers", "d_model", "n_heads", "head_dim", "d_ff", "vocab", "batch", "seq_len", "store_dtype")] + \
+               [(n, ctypes.c_double) for n in ("rms_eps", "rope_theta", "lr", "beta1", "beta2", "adam_eps")] + \
+               [(n, ctypes.c_int32) for n in ("mode", "host_threads", "flags")]
+
+
+class MtTensorDesc(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_uint64), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32)]
+
+
+class MtBlockDesc(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("layer", ctypes.c_int32), ("n_tensors", ctypes.c_int32),
+                ("pad_", ctypes.c_int32)] + \
+               [(n, ctypes.c_uint64) for n in ("base", "w_off", "g_off", "m_off", "v_off", "region_elems", "w_bytes",
+                                               "mv_bytes")] + \
+               [("tensors", MtTensorDesc * 8)]
+
+
+class MtStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_double) for n in
+                ("step_ms", "device_ms", "fwd_ms", "bwd_ms", "h2d_ms", "d2h_ms", "h2d_bytes", "d2h_bytes",
+                 "stall_ms", "adam_ms", "adam_tail_ms", "gemm_ms", "gemm_flops", "attn_ms", "attn_flops")] + \
+               [("gemm_launches", ctypes.c_int64), ("attn_launches", ctypes.c_int64), ("loss", ctypes.c_double),
+                ("n_blocks", ctypes.c_int32), ("pad_", ctypes.c_int32)]
+
+
+class MtBlockStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_double) for n in
+                ("fwd_ms", "bwd_ms", "h2d_fwd_ms", "h2d_bwd_ms", "d2h_ms", "stall_fwd_ms", "stall_bwd_ms",
+                 "adam_ms")]
+
+
+class MtError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{msg} (code {code})")
+        self.code = code
+
+
+_lib = None
+
+_SIGS = {
+    "mt_host_store_bytes": (ctypes.c_size_t, [ctypes.POINTER(MtConfig)]),
+    "mt_block_count": (ctypes.c_int, [ctypes.POINTER(MtConfig)]),
+    "mt_block_info": (ctypes.c_int, [ctypes.POINTER(MtConfig), ctypes.c_int, ctypes.POINTER(MtBlockDesc)]),
+    "mt_device_bytes": (ctypes.c_size_t, [ctypes.POINTER(MtConfig)]),
+    "mt_alloc_host_store": (ctypes.c_int, [ctypes.c_size_t, ctypes.POINTER(ctypes.c_void_p)]),
+    "mt_free_host_store": (None, [ctypes.c_void_p]),
+    "mt_init_store_header": (ctypes.c_int, [ctypes.POINTER(MtConfig), ctypes.c_void_p, ctypes.c_size_t]),
+    "mt_store_step": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]),
+    "mt_create_model": (ctypes.c_int, [ctypes.POINTER(MtConfig), ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p)]),
+    "mt_bind_host_store": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]),
+    "mt_train_step": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
+    "mt_get_loss": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]),
+    "mt_get_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(MtStats)]),
+    "mt_get_block_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(MtBlockStats)]),
+    "mt_debug_buffers": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
+                                        ctypes.POINTER(ctypes.c_void_p)]),
+    "mt_destroy_model": (None, [ctypes.c_void_p]),
+    "mt_host_adam": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_double,
+                                    ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_int32]),
+    "mt_last_error": (ctypes.c_char_p, []),
+    "mt_version": (ctypes.c_char_p, []),
+    "mt_gemm": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                               ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
+    "mt_transpose": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
+    "mt_rope_tables": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p,
+                                      ctypes.c_void_p]),
+    "mt_rope_qkv": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_void_p]),
+    "mt_attention_fwd": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_void_p]),
+    "mt_attention_bwd": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_void_p]),
+}
+
+
+def lib():
+    """The loaded libmt.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def check(rc):
+    if rc != MT_OK:
+        raise MtError(rc, lib().mt_last_error().decode())
+    return rc
+
+
+def make_config(shape, mode="streamed", host_threads=0, flags=0) -> MtConfig:
+    """mt_config from any object with the model-shape attributes
+    (n_layers, d_model, n_heads, head_dim, d_ff, vocab, batch, seq_len,
+    store_dtype 'f32'|'bf16', rms_eps, rope_theta, lr, beta1, beta2, adam_eps)."""
+    c = MtConfig()
+    for f in ("n_layers", "d_model", "n_heads", "head_dim", "d_ff", "vocab", "batch", "seq_len"):
+        setattr(c, f, int(getattr(shape, f)))
+    c.store_dtype = MT_BF16 if getattr(shape, "store_dtype", "bf16") == "bf16" else MT_F32
+    for f in ("rms_eps", "rope_theta", "lr", "beta1", "beta2", "adam_eps"):
+        setattr(c, f, float(getattr(shape, f)))
+    c.mode = MODES[mode] if isinstance(mode, str) else int(mode)
+    c.host_threads = int(host_threads)
+    c.flags = int(flags)
+    return c
+
+
+def host_store_bytes(cfg: MtConfig) -> int:
+    n = lib().mt_host_store_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise MtError(MT_E_INVALID, lib().mt_last_error().decode())
+    return n
+
+
+def device_bytes(cfg: MtConfig) -> int:
+    n = lib().mt_device_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise MtError(MT_E_INVALID, lib().mt_last_error().decode())
+    return n
+
+
+def block_infos(cfg: MtConfig) -> list:
+    n = lib().mt_block_count(ctypes.byref(cfg))
+    if n < 0:
+        check(n)
+    out = []
+    for i in range(n):
+        b = MtBlockDesc()
+        check(lib().mt_block_info(ctypes.byref(cfg), i, ctypes.byref(b)))
+        out.append(b)
+    return out
+
+
+def _view(addr: int, nbytes: int, dtype) -> np.ndarray:
+    buf = (ctypes.c_uint8 * nbytes).from_address(addr)
+    return np.frombuffer(buf, dtype=dtype)
+
+
+class HostStore:
+    """Pinned host store: header page + per-block [W | G | m | v] regions."""
+
+    def __init__(self, cfg: MtConfig):
+        self.cfg = cfg
+        self.nbytes = host_store_bytes(cfg)
+        p = ctypes.c_void_p()
+        check(lib().mt_alloc_host_store(self.nbytes, ctypes.byref(p)))
+        self.ptr = p.value
+        check(lib().mt_init_store_header(ctypes.byref(cfg), self.ptr, self.nbytes))
+        self.blocks = block_infos(cfg)
+        self.wdtype = np.uint16 if cfg.store_dtype == MT_BF16 else np.float32
+
+    def region(self, block: int, which: str) -> np.ndarray:
+        b = self.blocks[block]
+        off = {"w": b.w_off, "g": b.g_off, "m": b.m_off, "v": b.v_off}[which]
+        dt = self.wdtype if which in "wg" else np.float32
+        n = b.region_elems
+        return _view(self.ptr + off, n * np.dtype(dt).itemsize, dt)
+
+    def tensor(self, block: int, index: int, which: str = "w") -> np.ndarray:
+        b = self.blocks[block]
+        t = b.tensors[index]
+        reg = self.region(block, which)
+        return reg[t.offset:t.offset + t.rows * t.cols].reshape(t.rows, t.cols)
+
+    def step_count(self) -> int:
+        t = ctypes.c_int64()
+        check(lib().mt_store_step(self.ptr, ctypes.byref(t)))
+        return t.value
+
+    def zero_state(self):
+        """Zero every G, m and v region (W untouched)."""
+        for i in range(len(self.blocks)):
+            for w in "gmv":
+                self.region(i, w)[:] = 0
+
+    def free(self):
+        if self.ptr:
+            lib().mt_free_host_store(self.ptr)
+            self.ptr = None
+
+    # Logical tensors of the decoder inside the store (weights are [out x in]).
+    def logical(self, name: str, layer: int | None = None, which: str = "w") -> np.ndarray:
+        c = self.cfg
+        d, F, L = c.d_model, c.d_ff, c.n_layers
+        if name == "E":
+            return self.tensor(0, 0, which)
+        if name == "wh":
+            return self.tensor(L + 1, 0, which)
+        if name == "final_norm":
+            return self.tensor(L + 1, 1, which)[0]
+        blk = layer + 1
+        if name in ("wq", "wk", "wv"):
+            i = "qkv".index(name[1])
+            return self.tensor(blk, 0, which)[i * d:(i + 1) * d]
+        if name == "wo":
+            return self.tensor(blk, 1, which)
+        if name in ("wg", "wu"):
+            i = "gu".index(name[1])
+            return self.tensor(blk, 2, which)[i * F:(i + 1) * F]
+        if name == "wd":
+            return self.tensor(blk, 3, which)
+        if name == "attn_norm":
+            return self.tensor(blk, 4, which)[0]
+        if name == "ffn_norm":
+            return self.tensor(blk, 5, which)[0]
+        raise KeyError(name)
+
+    def logical_names(self):
+        names = [("E", None)]
+        for l in range(self.cfg.n_layers):
+            names += [("attn_norm", l), ("wq", l), ("wk", l), ("wv", l), ("wo", l), ("ffn_norm", l),
+                      ("wg", l), ("wu", l), ("wd", l)]
+        names += [("final_norm", None), ("wh", None)]
+        return names
+
+
+class Model:
+    """A model handle bound to a host store; device arena and streams from torch."""
+
+    def __init__(self, cfg: MtConfig, store: HostStore, device: str = "cuda:0"):
+        import torch
+        self.torch = torch
+        self.cfg = cfg
+        self.store = store
+        self.device = torch.device(device)
+        nbytes = device_bytes(cfg)
+        self.arena = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        self.streams = [torch.cuda.Stream(device=self.device) for _ in range(3)]
+        handles = (ctypes.c_void_p * 3)(*[s.cuda_stream for s in self.streams])
+        h = ctypes.c_void_p()
+        torch.cuda.synchronize(self.device)
+        check(lib().mt_create_model(ctypes.byref(cfg), self.arena.data_ptr(), nbytes, handles, ctypes.byref(h)))
+        self.handle = h.value
+        check(lib().mt_bind_host_store(self.handle, store.ptr, store.nbytes))
+
+    def step(self, tokens: np.ndarray) -> float:
+        tok = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
+        if tok.size != self.cfg.batch * self.cfg.seq_len:
+            raise ValueError("tokens must hold batch*seq_len values")
+        check(lib().mt_train_step(self.handle, tok.ctypes.data))
+        return self.loss()
+
+    def loss(self) -> float:
+        v = ctypes.c_float()
+        check(lib().mt_get_loss(self.handle, ctypes.byref(v)))
+        return float(v.value)
+
+    def stats(self) -> dict:
+        s = MtStats()
+        check(lib().mt_get_stats(self.handle, ctypes.byref(s)))
+        return {f: getattr(s, f) for f, _ in MtStats._fields_ if f != "pad_"}
+
+    def block_stats(self, block: int) -> dict:
+        s = MtBlockStats()
+        check(lib().mt_get_block_stats(self.handle, block, ctypes.byref(s)))
+        return {f: getattr(s, f) for f, _ in MtBlockStats._fields_}
+
+    def _arena_view(self, ptr: int, nelem: int, dtype):
+        torch = self.torch
+        off = ptr - self.arena.data_ptr()
+        esz = torch.tensor([], dtype=dtype).element_size()
+        return self.arena[off:off + nelem * esz].view(dtype)
+
+    def checkpoint(self, layer: int):
+        """fp32 layer-boundary activation x^layer [B*T x d] (device tensor view)."""
+        p = ctypes.c_void_p()
+        check(lib().mt_debug_buffers(self.handle, layer, ctypes.byref(p), None))
+        c = self.cfg
+        return self._arena_view(p.value, c.batch * c.seq_len * c.d_model, self.torch.float32).view(
+            c.batch * c.seq_len, c.d_model)
+
+    def row_loss(self):
+        p = ctypes.c_void_p()
+        check(lib().mt_debug_buffers(self.handle, 0, None, ctypes.byref(p)))
+        c = self.cfg
+        return self._arena_view(p.value, c.batch * c.seq_len, self.torch.float32)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().mt_destroy_model(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def init_store_weights(store: HostStore, draw, threads: int = 0):
+    """Fill every weight tensor from ``draw(name, layer, out, pool)``, which
+    writes the initial value of a logical tensor into ``out`` (a flat uint16
+    bf16 view or float32 view of the store).  Gains are set to 1.  G, m, v
+    and the padding were zeroed when the store header was written."""
+    from concurrent.futures import ThreadPoolExecutor
+    one = np.float32(1.0)
+    one_bits = np.uint16(0x3F80)
+    jobs = []
+    for name, layer in store.logical_names():
+        view = store.logical(name, layer, "w")
+        if name.endswith("norm"):
+            view[...] = one_bits if view.dtype == np.uint16 else one
+        else:
+            jobs.append((name, layer, view))
+    nthreads = threads or (len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 1)
+    with ThreadPoolExecutor(max(1, nthreads)) as pool:
+        for name, layer, view in jobs:
+            draw(name, layer, view.reshape(-1), pool)

@@ -1,0 +1,220 @@
+// extern "C" entry points of include/mt.h: argument checks and translation
+// of internal errors into MT_E_* codes; no exception crosses the ABI.
+#include <sched.h>
+
+#include <algorithm>
+#include <new>
+
+#include "adam.h"
+#include "engine.h"
+#include "store.h"
+
+namespace mt {
+
+static thread_local std::string g_last_error;
+void set_error(const std::string& msg) { g_last_error = msg; }
+const char* last_error() { return g_last_error.c_str(); }
+
+template <typename F>
+static int guarded(F&& f) {
+  try {
+    return f();
+  } catch (const ApiError& e) {
+    set_error(e.msg);
+    return e.code;
+  } catch (const HipError& e) {
+    set_error(std::string(hipGetErrorString(e.code)) + " in " + e.where);
+    return MT_E_HIP;
+  } catch (const std::bad_alloc&) {
+    set_error("host allocation failed");
+    return MT_E_OOM;
+  } catch (const std::exception& e) {
+    set_error(e.what());
+    return MT_E_INVALID;
+  }
+}
+
+}  // namespace mt
+
+using namespace mt;
+
+extern "C" {
+
+size_t mt_host_store_bytes(const mt_config* cfg) {
+  std::string why;
+  if (!cfg || validate_config(*cfg, &why) != MT_OK) {
+    set_error(cfg ? why : "null config");
+    return 0;
+  }
+  uint64_t total = 0;
+  store_layout(*cfg, &total);
+  return total;
+}
+
+int mt_block_count(const mt_config* cfg) {
+  std::string why;
+  if (!cfg || validate_config(*cfg, &why) != MT_OK) {
+    set_error(cfg ? why : "null config");
+    return MT_E_INVALID;
+  }
+  return cfg->n_layers + 2;
+}
+
+int mt_block_info(const mt_config* cfg, int block, mt_block_desc* out) {
+  return guarded([&] {
+    std::string why;
+    if (!cfg || !out) throw ApiError{MT_E_INVALID, "null argument"};
+    if (validate_config(*cfg, &why) != MT_OK) throw ApiError{MT_E_INVALID, why};
+    if (block < 0 || block >= cfg->n_layers + 2) throw ApiError{MT_E_INVALID, "block index"};
+    uint64_t total = 0;
+    *out = store_layout(*cfg, &total)[block];
+    return MT_OK;
+  });
+}
+
+size_t mt_device_bytes(const mt_config* cfg) {
+  size_t r = 0;
+  int rc = guarded([&] {
+    if (!cfg) throw ApiError{MT_E_INVALID, "null config"};
+    r = device_bytes_for(*cfg);
+    return MT_OK;
+  });
+  return rc == MT_OK ? r : 0;
+}
+
+int mt_alloc_host_store(size_t bytes, void** out) {
+  return guarded([&] {
+    if (!out || bytes == 0) throw ApiError{MT_E_INVALID, "null out or zero size"};
+    void* p = nullptr;
+    const size_t n = round_up(bytes, kStoreAlign);
+    hipError_t e = hipHostMalloc(&p, n, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      throw ApiError{MT_E_OOM, std::string("hipHostMalloc: ") + hipGetErrorString(e)};
+    }
+    if ((uintptr_t)p % kStoreAlign) {
+      hipHostFree(p);
+      throw ApiError{MT_E_ALIGN, "pinned allocation not 4 KiB aligned"};
+    }
+    *out = p;
+    return MT_OK;
+  });
+}
+
+void mt_free_host_store(void* p) {
+  if (p) hipHostFree(p);
+}
+
+int mt_init_store_header(const mt_config* cfg, void* host_base, size_t bytes) {
+  return guarded([&] {
+    std::string why;
+    if (!cfg || !host_base) throw ApiError{MT_E_INVALID, "null argument"};
+    if (validate_config(*cfg, &why) != MT_OK) throw ApiError{MT_E_INVALID, why};
+    if ((uintptr_t)host_base % kStoreAlign) throw ApiError{MT_E_ALIGN, "store not 4 KiB aligned"};
+    uint64_t total = 0;
+    store_layout(*cfg, &total);
+    if (bytes < total) throw ApiError{MT_E_SIZE, "store smaller than mt_host_store_bytes"};
+    StoreHeader h{};
+    h.magic = kStoreMagic;
+    h.version = kStoreVersion;
+    h.n_blocks = cfg->n_layers + 2;
+    h.cfg = *cfg;
+    h.step = 0;
+    h.total_bytes = total;
+    memset(host_base, 0, kHeaderBytes);
+    memcpy(host_base, &h, sizeof(h));
+    int threads = cfg->host_threads;
+    if (threads <= 0) {
+      cpu_set_t set;
+      threads = sched_getaffinity(0, sizeof(set), &set) == 0 ? CPU_COUNT(&set) : 1;
+    }
+    ThreadPool pool(std::max(1, threads));
+    const uint64_t chunk = 64ull << 20;
+    const uint64_t body = total - kHeaderBytes;
+    pool.run((int64_t)((body + chunk - 1) / chunk), [&](int64_t i) {
+      const uint64_t lo = kHeaderBytes + (uint64_t)i * chunk;
+      memset((uint8_t*)host_base + lo, 0, std::min(chunk, total - lo));
+    });
+    return MT_OK;
+  });
+}
+
+int mt_store_step(const void* host_base, int64_t* t) {
+  return guarded([&] {
+    if (!host_base || !t) throw ApiError{MT_E_INVALID, "null argument"};
+    const StoreHeader* h = (const StoreHeader*)host_base;
+    if (h->magic != kStoreMagic) throw ApiError{MT_E_INVALID, "bad store magic"};
+    *t = h->step;
+    return MT_OK;
+  });
+}
+
+int mt_create_model(const mt_config* cfg, void* dev_arena, size_t arena_bytes, void* const streams[3], void** out) {
+  return guarded([&] {
+    if (!cfg || !out) throw ApiError{MT_E_INVALID, "null argument"};
+    *out = create_model(cfg, dev_arena, arena_bytes, streams);
+    return MT_OK;
+  });
+}
+
+int mt_bind_host_store(void* model, void* host_base, size_t bytes) {
+  return guarded([&] {
+    if (!model) throw ApiError{MT_E_INVALID, "null model"};
+    return bind_store((Model*)model, host_base, bytes);
+  });
+}
+
+int mt_train_step(void* model, const int32_t* tokens) {
+  return guarded([&] {
+    if (!model) throw ApiError{MT_E_INVALID, "null model"};
+    return model_step((Model*)model, tokens);
+  });
+}
+
+int mt_get_loss(const void* model, float* out) {
+  return guarded([&] {
+    if (!model || !out) throw ApiError{MT_E_INVALID, "null argument"};
+    return model_loss((const Model*)model, out);
+  });
+}
+
+int mt_get_stats(const void* model, mt_stats* out) {
+  return guarded([&] {
+    if (!model || !out) throw ApiError{MT_E_INVALID, "null argument"};
+    return model_stats((const Model*)model, out);
+  });
+}
+
+int mt_get_block_stats(const void* model, int block, mt_block_stats* out) {
+  return guarded([&] {
+    if (!model || !out) throw ApiError{MT_E_INVALID, "null argument"};
+    return model_block_stats((const Model*)model, block, out);
+  });
+}
+
+int mt_debug_buffers(const void* model, int layer, void** ckpt, void** row_loss) {
+  return guarded([&] {
+    if (!model) throw ApiError{MT_E_INVALID, "null model"};
+    return model_debug((const Model*)model, layer, ckpt, row_loss);
+  });
+}
+
+void mt_destroy_model(void* model) { destroy_model((Model*)model); }
+
+int mt_host_adam(int32_t store_dtype, void* w, const void* g, float* m, float* v, size_t n, int64_t t, double lr,
+                 double beta1, double beta2, double eps, int32_t threads) {
+  return guarded([&] {
+    if ((!w || !g || !m || !v) && n) throw ApiError{MT_E_INVALID, "null buffer"};
+    if (store_dtype != MT_F32 && store_dtype != MT_BF16) throw ApiError{MT_E_INVALID, "store_dtype"};
+    if (t < 1) throw ApiError{MT_E_INVALID, "step t must be >= 1"};
+    const AdamConsts k = adam_consts(t, lr, beta1, beta2, eps);
+    ThreadPool pool(threads > 0 ? threads : 1);
+    adam_parallel(pool, store_dtype, w, g, m, v, n, k);
+    return MT_OK;
+  });
+}
+
+const char* mt_last_error(void) { return last_error(); }
+const char* mt_version(void) { return "megatrain-mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,923 @@
+// The layer-streamed training step: device arena, stateless layer
+// templates, the three-stream prefetch / compute / offload schedule and the
+// host Adam worker.
+//
+// MegaTrain (chatpaper.ai abstract; radar.chestersoft.de "Methodik"):
+//  * parameters and optimizer state stay in host memory; the GPU is a
+//    transient engine that receives one layer's weights, runs its forward or
+//    backward, returns the gradients and drops the weights;
+//  * a pipelined, double-buffered engine overlaps weight prefetch, compute
+//    and gradient offload on three streams: while layer i computes, layer
+//    i+1 loads into the second buffer (ping-pong);
+//  * stateless layer templates bind the weights of whichever buffer holds
+//    the layer (here: pointer arithmetic on the slot base, no graph state);
+//  * the Adam step runs on the host CPU, block by block, as the gradients
+//    of each block arrive, while the device continues its backward sweep.
+// Only the layer-boundary activations x^l are kept (fp32, device-resident);
+// each layer's forward is recomputed from x^l inside the backward sweep.
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <cmath>
+#include <condition_variable>
+#include <memory>
+#include <mutex>
+#include <thread>
+#include <vector>
+
+#include "adam.h"
+#include "engine.h"
+#include "kernels.h"
+#include "store.h"
+
+namespace mt {
+
+namespace {
+
+struct Carver {
+  uint8_t* base;
+  uint64_t off = 0;
+  template <typename P>
+  P* take(uint64_t bytes) {
+    off = round_up(off, 256);
+    P* p = base ? (P*)(base + off) : nullptr;
+    off += round_up(bytes, 256);
+    return p;
+  }
+};
+
+double ms_between(hipEvent_t a, hipEvent_t b) {
+  float ms = 0.f;
+  if (hipEventElapsedTime(&ms, a, b) != hipSuccess) return 0.0;
+  return ms;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ buffers --
+template <typename T>
+struct Acts {  // forward intermediates of one layer
+  T *h, *qkv, *qkvT, *o, *h2, *gu, *y;
+  float *r1, *lse, *x1, *r2;
+};
+
+template <typename T>
+struct BwdWs {  // backward workspace (one set)
+  T *dxb, *dxbT, *tmpT, *dy, *dgu, *dguT, *do_, *doT, *dqkvT, *dqkv;
+  float *dh, *dx1, *Dsum, *part, *dxA, *dxB;
+};
+
+template <typename T>
+struct HeadWs {
+  T *z, *dlogits, *dlogitsT;
+  float *rz, *logits, *row_loss, *loss;
+};
+
+template <typename T>
+struct LayerW {  // a stateless layer template bound to a weight (or grad) region
+  T *qkv, *o, *gu, *d, *anorm, *fnorm;
+};
+
+template <typename T>
+struct LayerWT {  // transposed weights for the data-gradient contractions
+  T *qkv, *o, *gu, *d;
+};
+
+template <typename T>
+static LayerW<T> bind_layer(uint8_t* region, const mt_block_desc& b) {
+  T* base = (T*)region;
+  return LayerW<T>{base + b.tensors[T_QKV].offset, base + b.tensors[T_O].offset, base + b.tensors[T_GU].offset,
+                   base + b.tensors[T_D].offset,   base + b.tensors[T_ANORM].offset, base + b.tensors[T_FNORM].offset};
+}
+
+// ---------------------------------------------------------------- model --
+struct Model {
+  mt_config cfg;
+  std::vector<mt_block_desc> blocks;
+  uint64_t store_bytes = 0, slot_bytes = 0;
+  int L, d, H, hd, F, V, B, Tq, M;
+  int E;  // bytes per weight element
+
+  uint8_t* arena = nullptr;
+  size_t arena_bytes = 0;
+  hipStream_t sp, sc, so;
+  uint8_t* host = nullptr;
+
+  // device
+  uint8_t *wslot[2], *gslot[2], *wt;
+  uint8_t *wres = nullptr, *gres = nullptr;  // resident mode: every block's W and G
+  float* ckpt;
+  float *cosb, *sinb;
+  int32_t *d_tok, *d_order, *d_seg;
+  std::vector<uint8_t*> acts_mem;  // Acts storage per layer (1 in streamed modes)
+  uint8_t* bwd_mem;
+  uint8_t* head_mem;
+
+  // host pinned
+  int32_t *h_tok = nullptr, *h_order = nullptr, *h_seg = nullptr;
+  float* h_loss = nullptr;
+
+  // events per use: 0..L+1 forward (embed, layers, head), then backward L..1, 0
+  int n_uses;
+  std::vector<hipEvent_t> ev_h2d_s, ev_h2d_e, ev_wait, ev_c_s, ev_c_e, ev_d2h_s, ev_d2h_e;
+  hipEvent_t ev_loss, ev_start, ev_end;
+  std::vector<hipEvent_t> kev;  // kernel timing pairs
+  std::vector<std::pair<double, int>> kev_meta;  // flops, kind (0 gemm, 1 attention)
+  size_t kev_used = 0;
+
+  std::unique_ptr<ThreadPool> pool;
+  mt_stats stats{};
+  std::vector<mt_block_stats> bstats;
+  float last_loss = NAN;
+  bool have_loss = false;
+
+  // ------------------------------------------------------------ layout --
+  template <typename T>
+  void carve_acts(Carver& c, Acts<T>& a) {
+    const uint64_t Md = (uint64_t)M * d;
+    a.h = c.take<T>(Md * E);
+    a.qkv = c.take<T>(3 * Md * E);
+    a.qkvT = c.take<T>(3 * Md * E);
+    a.o = c.take<T>(Md * E);
+    a.h2 = c.take<T>(Md * E);
+    a.gu = c.take<T>((uint64_t)M * 2 * F * E);
+    a.y = c.take<T>((uint64_t)M * F * E);
+    a.r1 = c.take<float>((uint64_t)M * 4);
+    a.lse = c.take<float>((uint64_t)M * H * 4);
+    a.x1 = c.take<float>(Md * 4);
+    a.r2 = c.take<float>((uint64_t)M * 4);
+  }
+  template <typename T>
+  void carve_bwd(Carver& c, BwdWs<T>& w) {
+    const uint64_t Md = (uint64_t)M * d, MF = (uint64_t)M * F;
+    w.dxb = c.take<T>(Md * E);
+    w.dxbT = c.take<T>(Md * E);
+    w.tmpT = c.take<T>(std::max(Md, MF) * E);
+    w.dy = c.take<T>(MF * E);
+    w.dgu = c.take<T>(2 * MF * E);
+    w.dguT = c.take<T>(2 * MF * E);
+    w.do_ = c.take<T>(Md * E);
+    w.doT = c.take<T>(Md * E);
+    w.dqkvT = c.take<T>(3 * Md * E);
+    w.dqkv = c.take<T>(3 * Md * E);
+    w.dh = c.take<float>(Md * 4);
+    w.dx1 = c.take<float>(Md * 4);
+    w.Dsum = c.take<float>((uint64_t)M * H * 4);
+    w.part = c.take<float>(rmsnorm_dg_partial_elems(M, d) * 4);
+    w.dxA = c.take<float>(Md * 4);
+    w.dxB = c.take<float>(Md * 4);
+  }
+  template <typename T>
+  void carve_head(Carver& c, HeadWs<T>& w) {
+    const uint64_t MV = (uint64_t)M * V;
+    w.z = c.take<T>((uint64_t)M * d * E);
+    w.dlogits = c.take<T>(MV * E);
+    w.dlogitsT = c.take<T>(MV * E);
+    w.rz = c.take<float>((uint64_t)M * 4);
+    w.logits = c.take<float>(MV * 4);
+    w.row_loss = c.take<float>((uint64_t)M * 4);
+    w.loss = c.take<float>(256);
+  }
+
+  template <typename T>
+  uint64_t carve_all(uint8_t* base) {
+    Carver c{base};
+    for (int s = 0; s < 2; ++s) wslot[s] = c.take<uint8_t>(slot_bytes);
+    for (int s = 0; s < 2; ++s) gslot[s] = c.take<uint8_t>(slot_bytes);
+    wt = c.take<uint8_t>(slot_bytes);
+    if (cfg.mode == MT_RESIDENT) {
+      uint64_t tot = 0;
+      for (auto& b : blocks) tot += round_up(b.w_bytes, 256);
+      wres = c.take<uint8_t>(tot);
+      gres = c.take<uint8_t>(tot);
+    }
+    ckpt = c.take<float>((uint64_t)(L + 1) * M * d * 4);
+    cosb = c.take<float>((uint64_t)Tq * (hd / 2) * 4);
+    sinb = c.take<float>((uint64_t)Tq * (hd / 2) * 4);
+    d_tok = c.take<int32_t>((uint64_t)M * 4);
+    d_order = c.take<int32_t>((uint64_t)M * 4);
+    d_seg = c.take<int32_t>((uint64_t)(V + 1) * 4);
+    const int nacts = cfg.mode == MT_RESIDENT ? L : 1;
+    acts_mem.assign(nacts, nullptr);
+    for (int i = 0; i < nacts; ++i) {
+      uint64_t start = round_up(c.off, 256);
+      Acts<T> a;
+      carve_acts(c, a);
+      acts_mem[i] = base ? base + start : nullptr;
+      (void)a;
+    }
+    {
+      uint64_t start = round_up(c.off, 256);
+      BwdWs<T> w;
+      carve_bwd(c, w);
+      bwd_mem = base ? base + start : nullptr;
+    }
+    {
+      uint64_t start = round_up(c.off, 256);
+      HeadWs<T> w;
+      carve_head(c, w);
+      head_mem = base ? base + start : nullptr;
+    }
+    return c.off;
+  }
+  template <typename T>
+  Acts<T> acts(int layer) {
+    Carver c{acts_mem[cfg.mode == MT_RESIDENT ? layer : 0]};
+    Acts<T> a;
+    carve_acts(c, a);
+    return a;
+  }
+  template <typename T>
+  BwdWs<T> bwdws() {
+    Carver c{bwd_mem};
+    BwdWs<T> w;
+    carve_bwd(c, w);
+    return w;
+  }
+  template <typename T>
+  HeadWs<T> headws() {
+    Carver c{head_mem};
+    HeadWs<T> w;
+    carve_head(c, w);
+    return w;
+  }
+
+  void init_dims(const mt_config& c) {
+    cfg = c;
+    blocks = store_layout(c, &store_bytes);
+    slot_bytes = 0;
+    for (auto& b : blocks) slot_bytes = std::max<uint64_t>(slot_bytes, b.w_bytes);
+    L = c.n_layers;
+    d = c.d_model;
+    H = c.n_heads;
+    hd = c.head_dim;
+    F = c.d_ff;
+    V = c.vocab;
+    B = c.batch;
+    Tq = c.seq_len;
+    M = B * Tq;
+    E = wbytes(c);
+    n_uses = 2 * L + 3;
+  }
+  uint64_t device_bytes() { return cfg.store_dtype == MT_BF16 ? carve_all<uint16_t>(nullptr) : carve_all<float>(nullptr); }
+
+  float* x_ckpt(int l) { return ckpt + (uint64_t)l * M * d; }
+
+  // --------------------------------------------------------- kernels --
+  template <typename T>
+  void gemm(const T* A, int64_t lda, const T* Bm, int64_t ldb, void* C, int64_t ldc, const float* R, int64_t ldr,
+            int m, int n, int k, Epi epi) {
+    const bool timed = cfg.flags & MT_FLAG_TIME_KERNELS;
+    if (timed) record_kernel_start(2.0 * m * n * k, 0);
+    gemm_nt<T>(A, lda, Bm, ldb, C, ldc, R, ldr, m, n, k, epi, sc);
+    if (timed) record_kernel_end();
+  }
+  void record_kernel_start(double flops, int kind) {
+    if (kev_used + 2 > kev.size()) {
+      hipEvent_t e0, e1;
+      MT_HIP(hipEventCreate(&e0));
+      MT_HIP(hipEventCreate(&e1));
+      kev.push_back(e0);
+      kev.push_back(e1);
+      kev_meta.emplace_back(0.0, 0);
+    }
+    kev_meta[kev_used / 2] = {flops, kind};
+    MT_HIP(hipEventRecord(kev[kev_used], sc));
+  }
+  void record_kernel_end() {
+    MT_HIP(hipEventRecord(kev[kev_used + 1], sc));
+    kev_used += 2;
+  }
+  // Causal attention flops per layer: QK^T and PV over the lower triangle.
+  double attn_fwd_flops() const { return 2.0 * 2.0 * B * H * ((double)Tq * (Tq + 1) / 2) * hd; }
+
+  template <typename T>
+  void layer_fwd(const LayerW<T>& w, const float* x, const Acts<T>& a, float* x_out, bool full) {
+    const float eps = (float)cfg.rms_eps;
+    rmsnorm_fwd<T>(x, w.anorm, a.h, a.r1, M, d, eps, sc);
+    gemm<T>(a.h, d, w.qkv, d, a.qkv, 3 * d, nullptr, 0, M, 3 * d, d, EPI_STORE);
+    rope_qkv_fwd<T>(a.qkv, a.qkvT, cosb, sinb, M, Tq, d, hd, sc);
+    const bool timed = cfg.flags & MT_FLAG_TIME_KERNELS;
+    if (timed) record_kernel_start(attn_fwd_flops(), 1);
+    attn_fwd<T>(a.qkv, a.qkvT, a.o, a.lse, B, Tq, H, hd, sc);
+    if (timed) record_kernel_end();
+    gemm<T>(a.o, d, w.o, d, a.x1, d, x, d, M, d, d, EPI_ADD_F32);
+    rmsnorm_fwd<T>(a.x1, w.fnorm, a.h2, a.r2, M, d, eps, sc);
+    gemm<T>(a.h2, d, w.gu, d, a.gu, 2 * F, nullptr, 0, M, 2 * F, d, EPI_STORE);
+    swiglu_fwd<T>(a.gu, a.y, M, F, sc);
+    if (full) gemm<T>(a.y, F, w.d, F, x_out, d, a.x1, d, M, d, F, EPI_ADD_F32);
+  }
+
+  template <typename T>
+  void weight_transposes(const LayerW<T>& w, const LayerWT<T>& t) {
+    transpose<T>(w.qkv, d, t.qkv, 3 * d, 3 * d, d, sc);
+    transpose<T>(w.o, d, t.o, d, d, d, sc);
+    transpose<T>(w.gu, d, t.gu, 2 * F, 2 * F, d, sc);
+    transpose<T>(w.d, F, t.d, d, d, F, sc);
+  }
+
+  template <typename T>
+  void layer_bwd(const LayerW<T>& w, const LayerWT<T>& wt_, const float* x, const Acts<T>& a, const float* dx2,
+                 float* dx_out, const LayerW<T>& g) {
+    BwdWs<T> ws = bwdws<T>();
+    const uint64_t Mu = M;
+    // down projection
+    cast_transpose<T>(dx2, ws.dxb, ws.dxbT, M, d, sc);
+    transpose<T>(a.y, F, ws.tmpT, Mu, M, F, sc);
+    gemm<T>(ws.dxbT, M, ws.tmpT, M, g.d, F, nullptr, 0, d, F, M, EPI_STORE);
+    gemm<T>(ws.dxb, d, wt_.d, d, ws.dy, F, nullptr, 0, M, F, d, EPI_STORE);
+    // SwiGLU and gate/up projection
+    swiglu_bwd<T>(ws.dy, a.gu, ws.dgu, M, F, sc);
+    transpose<T>(ws.dgu, 2 * F, ws.dguT, Mu, M, 2 * F, sc);
+    transpose<T>(a.h2, d, ws.tmpT, Mu, M, d, sc);
+    gemm<T>(ws.dguT, M, ws.tmpT, M, g.gu, d, nullptr, 0, 2 * F, d, M, EPI_STORE);
+    gemm<T>(ws.dgu, 2 * F, wt_.gu, 2 * F, ws.dh, d, nullptr, 0, M, d, 2 * F, EPI_F32);
+    rmsnorm_bwd<T>(ws.dh, a.x1, w.fnorm, a.r2, dx2, ws.dx1, M, d, sc);
+    rmsnorm_dg<T>(ws.dh, a.x1, a.r2, ws.part, g.fnorm, M, d, sc);
+    // attention output projection
+    cast_transpose<T>(ws.dx1, ws.dxb, ws.dxbT, M, d, sc);
+    transpose<T>(a.o, d, ws.tmpT, Mu, M, d, sc);
+    gemm<T>(ws.dxbT, M, ws.tmpT, M, g.o, d, nullptr, 0, d, d, M, EPI_STORE);
+    gemm<T>(ws.dxb, d, wt_.o, d, ws.do_, d, nullptr, 0, M, d, d, EPI_STORE);
+    // attention
+    transpose<T>(ws.do_, d, ws.doT, Mu, M, d, sc);
+    attn_bwd_dsum<T>(ws.do_, a.o, ws.Dsum, B, Tq, H, hd, sc);
+    const bool timed = cfg.flags & MT_FLAG_TIME_KERNELS;
+    if (timed) record_kernel_start(2.5 * attn_fwd_flops(), 1);
+    attn_bwd<T>(a.qkv, a.qkvT, ws.do_, ws.doT, a.lse, ws.Dsum, ws.dqkvT, B, Tq, H, hd, sc);
+    if (timed) record_kernel_end();
+    rope_bwd_T<T>(ws.dqkvT, cosb, sinb, M, Tq, d, hd, sc);
+    // QKV projection
+    transpose<T>(ws.dqkvT, M, ws.dqkv, 3 * d, 3 * d, M, sc);
+    transpose<T>(a.h, d, ws.tmpT, Mu, M, d, sc);
+    gemm<T>(ws.dqkvT, M, ws.tmpT, M, g.qkv, d, nullptr, 0, 3 * d, d, M, EPI_STORE);
+    gemm<T>(ws.dqkv, 3 * d, wt_.qkv, 3 * d, ws.dh, d, nullptr, 0, M, d, 3 * d, EPI_F32);
+    rmsnorm_bwd<T>(ws.dh, x, w.anorm, a.r1, ws.dx1, dx_out, M, d, sc);
+    rmsnorm_dg<T>(ws.dh, x, a.r1, ws.part, g.anorm, M, d, sc);
+  }
+
+  // Final norm, logits, loss, and the head's backward.  Returns dx^L in dx_out.
+  template <typename T>
+  void head_fwd_bwd(const mt_block_desc& b, uint8_t* wreg, uint8_t* greg, float* dx_out) {
+    HeadWs<T> hw = headws<T>();
+    BwdWs<T> ws = bwdws<T>();
+    const T* wh = (const T*)wreg + b.tensors[T_WH].offset;
+    const T* fin = (const T*)wreg + b.tensors[T_FINAL].offset;
+    T* gwh = (T*)greg + b.tensors[T_WH].offset;
+    T* gfin = (T*)greg + b.tensors[T_FINAL].offset;
+    const float* xL = x_ckpt(L);
+    const float inv_n = 1.0f / (float)((int64_t)B * (Tq - 1));
+    rmsnorm_fwd<T>(xL, fin, hw.z, hw.rz, M, d, (float)cfg.rms_eps, sc);
+    gemm<T>(hw.z, d, wh, d, hw.logits, V, nullptr, 0, M, V, d, EPI_F32);
+    xent<T>(hw.logits, d_tok, hw.row_loss, hw.dlogits, M, Tq, V, inv_n, sc);
+    sum_fixed(hw.row_loss, hw.loss, M, inv_n, sc);
+    MT_HIP(hipMemcpyAsync(h_loss, hw.loss, sizeof(float), hipMemcpyDeviceToHost, sc));
+    MT_HIP(hipEventRecord(ev_loss, sc));
+    transpose<T>(hw.dlogits, V, hw.dlogitsT, M, M, V, sc);
+    transpose<T>(hw.z, d, ws.tmpT, M, M, d, sc);
+    gemm<T>(hw.dlogitsT, M, ws.tmpT, M, gwh, d, nullptr, 0, V, d, M, EPI_STORE);
+    T* whT = (T*)wt;
+    transpose<T>(wh, d, whT, V, V, d, sc);
+    gemm<T>(hw.dlogits, V, whT, V, ws.dh, d, nullptr, 0, M, d, V, EPI_F32);
+    rmsnorm_bwd<T>(ws.dh, xL, fin, hw.rz, nullptr, dx_out, M, d, sc);
+    rmsnorm_dg<T>(ws.dh, xL, hw.rz, ws.part, gfin, M, d, sc);
+  }
+
+  // ------------------------------------------------------------ step --
+  template <typename T>
+  void compute_block_fwd(int j, uint8_t* wreg) {
+    const mt_block_desc& b = blocks[j];
+    if (b.kind == MT_BLOCK_EMBED) {
+      embed_fwd<T>(d_tok, (const T*)wreg + b.tensors[0].offset, x_ckpt(0), M, d, sc);
+    } else {
+      const int l = b.layer;
+      layer_fwd<T>(bind_layer<T>(wreg, b), x_ckpt(l), acts<T>(l), x_ckpt(l + 1), true);
+    }
+  }
+
+  template <typename T>
+  void compute_layer_bwd(int j, uint8_t* wreg, uint8_t* greg, const float* dx_in, float* dx_out) {
+    const mt_block_desc& b = blocks[j];
+    const int l = b.layer;
+    LayerW<T> w = bind_layer<T>(wreg, b);
+    LayerW<T> g = bind_layer<T>(greg, b);
+    LayerWT<T> t{(T*)wt, (T*)wt + (uint64_t)3 * d * d, (T*)wt + (uint64_t)4 * d * d,
+                 (T*)wt + (uint64_t)4 * d * d + (uint64_t)2 * F * d};
+    Acts<T> a = acts<T>(l);
+    if (cfg.mode != MT_RESIDENT) layer_fwd<T>(w, x_ckpt(l), a, nullptr, false);  // recompute
+    weight_transposes<T>(w, t);
+    layer_bwd<T>(w, t, x_ckpt(l), a, dx_in, dx_out, g);
+  }
+
+  template <typename T>
+  void step_streamed(hipStream_t P, hipStream_t O);
+  template <typename T>
+  void step_resident();
+  int train_step(const int32_t* tokens);
+  void finish_stats(bool streamed, double wall_ms);
+
+  // Adam worker coordination
+  std::mutex q_mu;
+  std::condition_variable q_cv;
+  std::vector<int> q_blocks;   // blocks whose D2H has been enqueued, in order
+  std::vector<hipEvent_t> q_events;
+  bool q_closed = false;
+  std::atomic<bool> nonfinite{false};
+  std::string adam_error;
+
+  void push_adam(int block, hipEvent_t ev) {
+    {
+      std::lock_guard<std::mutex> g(q_mu);
+      q_blocks.push_back(block);
+      q_events.push_back(ev);
+    }
+    q_cv.notify_all();
+  }
+  void close_adam() {
+    {
+      std::lock_guard<std::mutex> g(q_mu);
+      q_closed = true;
+    }
+    q_cv.notify_all();
+  }
+  void adam_worker(int64_t t, double* adam_total, double* adam_tail, std::atomic<bool>* device_done);
+};
+
+// ---------------------------------------------------------------- Adam --
+void Model::adam_worker(int64_t t, double* adam_total, double* adam_tail, std::atomic<bool>* device_done) {
+  try {
+    // The loss must be finite before any parameter changes.
+    {
+      std::unique_lock<std::mutex> lk(q_mu);
+      q_cv.wait(lk, [&] { return !q_blocks.empty() || q_closed; });
+    }
+    MT_HIP(hipEventSynchronize(ev_loss));
+    if (!std::isfinite(*h_loss)) nonfinite = true;
+    const AdamConsts k = adam_consts(t, cfg.lr, cfg.beta1, cfg.beta2, cfg.adam_eps);
+    size_t next = 0;
+    for (;;) {
+      int blk;
+      hipEvent_t ev;
+      {
+        std::unique_lock<std::mutex> lk(q_mu);
+        q_cv.wait(lk, [&] { return next < q_blocks.size() || q_closed; });
+        if (next >= q_blocks.size()) break;
+        blk = q_blocks[next];
+        ev = q_events[next];
+        ++next;
+      }
+      MT_HIP(hipEventSynchronize(ev));
+      if (nonfinite) continue;
+      auto t0 = std::chrono::steady_clock::now();
+      const mt_block_desc& b = blocks[blk];
+      adam_parallel(*pool, cfg.store_dtype, host + b.w_off, host + b.g_off, (float*)(host + b.m_off),
+                    (float*)(host + b.v_off), b.region_elems, k);
+      double ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+      *adam_total += ms;
+      bstats[blk].adam_ms = ms;
+      if (device_done->load()) *adam_tail += ms;
+    }
+  } catch (const HipError& e) {
+    adam_error = std::string(hipGetErrorString(e.code)) + " in " + e.where;
+  } catch (const std::exception& e) {
+    adam_error = e.what();
+  }
+}
+
+// Streamed (and serialized) schedule.  Uses: u = j for the forward of block
+// j (0 embed, 1..L layers, L+1 head, whose use also runs the head backward);
+// u = L+2+i for the backward of block L-i (i = 0..L-1: layers), and
+// u = 2L+2 for the embedding backward.  Block j always uses weight slot j%2.
+template <typename T>
+void Model::step_streamed(hipStream_t P, hipStream_t O) {
+  const bool poison = cfg.flags & MT_FLAG_POISON;
+  const uint32_t nan_word = E == 2 ? 0x7FC07FC0u : 0x7FC00000u;
+  std::vector<int> slot_last_use(2, -1);  // use that last bound each slot
+  std::vector<int> gslot_last(2, -1);     // use that last filled each grad slot
+  int gcount = 0;
+
+  auto fetch = [&](int u, int j) {
+    const int s = j % 2;
+    if (slot_last_use[s] >= 0) MT_HIP(hipStreamWaitEvent(P, ev_c_e[slot_last_use[s]], 0));
+    if (poison) fill_u32(wslot[s], nan_word, slot_bytes / 4, P);
+    MT_HIP(hipEventRecord(ev_h2d_s[u], P));
+    MT_HIP(hipMemcpyAsync(wslot[s], host + blocks[j].w_off, blocks[j].w_bytes, hipMemcpyHostToDevice, P));
+    MT_HIP(hipEventRecord(ev_h2d_e[u], P));
+  };
+  auto begin = [&](int u, int fetched_use) {
+    MT_HIP(hipEventRecord(ev_wait[u], sc));
+    if (fetched_use >= 0) MT_HIP(hipStreamWaitEvent(sc, ev_h2d_e[fetched_use], 0));
+    MT_HIP(hipEventRecord(ev_c_s[u], sc));
+  };
+  auto end = [&](int u, int j) {
+    MT_HIP(hipEventRecord(ev_c_e[u], sc));
+    slot_last_use[j % 2] = u;
+  };
+  // Grad slot for a backward use: wait until its previous offload finished.
+  auto grad_slot = [&](int u) -> int {
+    const int g = gcount % 2;
+    if (gslot_last[g] >= 0) MT_HIP(hipStreamWaitEvent(sc, ev_d2h_e[gslot_last[g]], 0));
+    (void)u;
+    return g;
+  };
+  auto offload = [&](int u, int j, int g) {
+    MT_HIP(hipStreamWaitEvent(O, ev_c_e[u], 0));
+    MT_HIP(hipEventRecord(ev_d2h_s[u], O));
+    MT_HIP(hipMemcpyAsync(host + blocks[j].g_off, gslot[g], blocks[j].w_bytes, hipMemcpyDeviceToHost, O));
+    MT_HIP(hipEventRecord(ev_d2h_e[u], O));
+    gslot_last[g] = u;
+    ++gcount;
+    push_adam(j, ev_d2h_e[u]);
+  };
+
+  BwdWs<T> ws = bwdws<T>();
+  // ---- forward sweep (blocks 0 .. L+1)
+  fetch(0, 0);
+  for (int j = 0; j <= L + 1; ++j) {
+    if (j + 1 <= L + 1) fetch(j + 1, j + 1);
+    if (j <= L) {
+      begin(j, j);
+      compute_block_fwd<T>(j, wslot[j % 2]);
+      end(j, j);
+    } else {
+      // head: forward, loss, backward; weights stay bound for both
+      MT_HIP(hipEventRecord(ev_wait[j], sc));
+      const int g = grad_slot(j);
+      MT_HIP(hipStreamWaitEvent(sc, ev_h2d_e[j], 0));
+      MT_HIP(hipEventRecord(ev_c_s[j], sc));
+      head_fwd_bwd<T>(blocks[j], wslot[j % 2], gslot[g], ws.dxA);
+      end(j, j);
+      offload(j, j, g);
+    }
+  }
+  // ---- backward sweep: layers L-1 .. 0 (blocks L .. 1), then the embedding
+  float* dx_in = ws.dxA;
+  float* dx_out = ws.dxB;
+  for (int i = 0; i < L; ++i) {
+    const int j = L - i;
+    const int u = L + 2 + i;
+    const bool refetch = (j != L);  // block L is still in its slot from the forward
+    if (j - 1 >= 1) fetch(u + 1, j - 1);
+    MT_HIP(hipEventRecord(ev_wait[u], sc));
+    const int g = grad_slot(u);
+    if (refetch) MT_HIP(hipStreamWaitEvent(sc, ev_h2d_e[u], 0));
+    MT_HIP(hipEventRecord(ev_c_s[u], sc));
+    compute_layer_bwd<T>(j, wslot[j % 2], gslot[g], dx_in, dx_out);
+    end(u, j);
+    offload(u, j, g);
+    std::swap(dx_in, dx_out);
+  }
+  {
+    const int u = 2 * L + 2;
+    MT_HIP(hipEventRecord(ev_wait[u], sc));
+    const int g = grad_slot(u);
+    MT_HIP(hipEventRecord(ev_c_s[u], sc));
+    const mt_block_desc& b = blocks[0];
+    embed_bwd<T>(dx_in, d_order, d_seg, (T*)gslot[g] + b.tensors[0].offset, V, d, sc);
+    MT_HIP(hipEventRecord(ev_c_e[u], sc));
+    offload(u, 0, g);
+  }
+}
+
+// Resident schedule: every block's weights are copied once into device
+// memory, every layer keeps its forward intermediates (no recompute), and
+// all gradients are offloaded at the end; the same kernels run in the same
+// order on the same data as in the streamed schedule.
+template <typename T>
+void Model::step_resident() {
+  std::vector<uint8_t*> wr(blocks.size()), gr(blocks.size());
+  uint64_t off = 0;
+  for (size_t j = 0; j < blocks.size(); ++j) {
+    wr[j] = wres + off;
+    gr[j] = gres + off;
+    off += round_up(blocks[j].w_bytes, 256);
+  }
+  MT_HIP(hipEventRecord(ev_h2d_s[0], sc));
+  for (size_t j = 0; j < blocks.size(); ++j)
+    MT_HIP(hipMemcpyAsync(wr[j], host + blocks[j].w_off, blocks[j].w_bytes, hipMemcpyHostToDevice, sc));
+  MT_HIP(hipEventRecord(ev_h2d_e[0], sc));
+  MT_HIP(hipEventRecord(ev_c_s[0], sc));
+  for (int j = 0; j <= L; ++j) compute_block_fwd<T>(j, wr[j]);
+  BwdWs<T> ws = bwdws<T>();
+  head_fwd_bwd<T>(blocks[L + 1], wr[L + 1], gr[L + 1], ws.dxA);
+  float* dx_in = ws.dxA;
+  float* dx_out = ws.dxB;
+  for (int j = L; j >= 1; --j) {
+    compute_layer_bwd<T>(j, wr[j], gr[j], dx_in, dx_out);
+    std::swap(dx_in, dx_out);
+  }
+  embed_bwd<T>(dx_in, d_order, d_seg, (T*)gr[0] + blocks[0].tensors[0].offset, V, d, sc);
+  MT_HIP(hipEventRecord(ev_c_e[0], sc));
+  MT_HIP(hipEventRecord(ev_d2h_s[0], sc));
+  for (size_t j = 0; j < blocks.size(); ++j)
+    MT_HIP(hipMemcpyAsync(host + blocks[j].g_off, gr[j], blocks[j].w_bytes, hipMemcpyDeviceToHost, sc));
+  MT_HIP(hipEventRecord(ev_d2h_e[0], sc));
+  for (size_t j = 0; j < blocks.size(); ++j) push_adam((int)j, ev_d2h_e[0]);
+}
+
+int Model::train_step(const int32_t* tokens) {
+  auto t0 = std::chrono::steady_clock::now();
+  StoreHeader* hdr = (StoreHeader*)host;
+  const int64_t t = hdr->step + 1;
+  // tokens and the stable token-sorted order for the embedding backward
+  std::vector<int32_t> count(V + 1, 0);
+  for (int m = 0; m < M; ++m) {
+    if (tokens[m] < 0 || tokens[m] >= V) throw ApiError{MT_E_INVALID, "token out of range [0, vocab)"};
+    count[tokens[m] + 1]++;
+  }
+  memcpy(h_tok, tokens, sizeof(int32_t) * M);
+  h_seg[0] = 0;
+  for (int v = 0; v < V; ++v) h_seg[v + 1] = h_seg[v] + count[v + 1];
+  std::vector<int32_t> pos(h_seg, h_seg + V);
+  for (int m = 0; m < M; ++m) h_order[pos[tokens[m]]++] = m;
+  MT_HIP(hipEventRecord(ev_start, sc));
+  MT_HIP(hipMemcpyAsync(d_tok, h_tok, sizeof(int32_t) * M, hipMemcpyHostToDevice, sc));
+  MT_HIP(hipMemcpyAsync(d_order, h_order, sizeof(int32_t) * M, hipMemcpyHostToDevice, sc));
+  MT_HIP(hipMemcpyAsync(d_seg, h_seg, sizeof(int32_t) * (V + 1), hipMemcpyHostToDevice, sc));
+  // Copies on the other streams start after ev_start, so that device_ms
+  // (ev_start to ev_end) spans the whole step.
+  MT_HIP(hipStreamWaitEvent(sp, ev_start, 0));
+  MT_HIP(hipStreamWaitEvent(so, ev_start, 0));
+
+  {
+    std::lock_guard<std::mutex> g(q_mu);
+    q_blocks.clear();
+    q_events.clear();
+    q_closed = false;
+  }
+  nonfinite = false;
+  adam_error.clear();
+  kev_used = 0;
+  for (auto& s : bstats) s = mt_block_stats{};
+  double adam_total = 0, adam_tail = 0;
+  std::atomic<bool> device_done{false};
+  std::thread worker([&] { adam_worker(t, &adam_total, &adam_tail, &device_done); });
+
+  std::string enqueue_error;
+  int enqueue_code = MT_OK;
+  try {
+    const bool bf = cfg.store_dtype == MT_BF16;
+    if (cfg.mode == MT_RESIDENT) {
+      bf ? step_resident<uint16_t>() : step_resident<float>();
+    } else {
+      hipStream_t P = cfg.mode == MT_SERIALIZED ? sc : sp;
+      hipStream_t O = cfg.mode == MT_SERIALIZED ? sc : so;
+      bf ? step_streamed<uint16_t>(P, O) : step_streamed<float>(P, O);
+    }
+    MT_HIP(hipEventRecord(ev_end, so));
+  } catch (const HipError& e) {
+    enqueue_code = MT_E_HIP;
+    enqueue_error = std::string(hipGetErrorString(e.code)) + " in " + e.where;
+  } catch (const ApiError& e) {
+    enqueue_code = e.code;
+    enqueue_error = e.msg;
+  }
+  close_adam();
+  hipError_t e1 = hipStreamSynchronize(sc);
+  hipError_t e2 = hipStreamSynchronize(sp);
+  hipError_t e3 = hipStreamSynchronize(so);
+  device_done = true;
+  worker.join();
+  if (enqueue_code != MT_OK) throw ApiError{enqueue_code, enqueue_error};
+  if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) {
+    hipError_t e = e1 != hipSuccess ? e1 : (e2 != hipSuccess ? e2 : e3);
+    throw ApiError{MT_E_HIP, std::string("stream synchronize: ") + hipGetErrorString(e)};
+  }
+  if (!adam_error.empty()) throw ApiError{MT_E_HIP, "host Adam: " + adam_error};
+  last_loss = *h_loss;
+  have_loss = true;
+  double wall = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+  stats.adam_ms = adam_total;
+  stats.adam_tail_ms = adam_tail;
+  finish_stats(cfg.mode != MT_RESIDENT, wall);
+  if (nonfinite) throw ApiError{MT_E_NONFINITE, "loss is not finite; Adam skipped, W/m/v unchanged"};
+  hdr->step = t;
+  return MT_OK;
+}
+
+void Model::finish_stats(bool streamed, double wall_ms) {
+  mt_stats& s = stats;
+  double adam_ms = s.adam_ms, adam_tail = s.adam_tail_ms;
+  s = mt_stats{};
+  s.adam_ms = adam_ms;
+  s.adam_tail_ms = adam_tail;
+  s.step_ms = wall_ms;
+  s.loss = last_loss;
+  s.n_blocks = (int)blocks.size();
+  s.device_ms = ms_between(ev_start, ev_end);
+  if (streamed) {
+    for (int u = 0; u < n_uses; ++u) {
+      const bool has_h2d = (u <= L + 1) || (u >= L + 3 && u <= 2 * L + 1);
+      const bool has_d2h = (u >= L + 1);
+      const int j = u <= L + 1 ? u : (u <= 2 * L + 1 ? L - (u - (L + 2)) : 0);
+      const double c = ms_between(ev_c_s[u], ev_c_e[u]);
+      const double st = ms_between(ev_wait[u], ev_c_s[u]);
+      double h = 0, dd = 0;
+      if (has_h2d) {
+        h = ms_between(ev_h2d_s[u], ev_h2d_e[u]);
+        s.h2d_ms += h;
+        s.h2d_bytes += (double)blocks[j].w_bytes;
+      }
+      if (has_d2h) {
+        dd = ms_between(ev_d2h_s[u], ev_d2h_e[u]);
+        s.d2h_ms += dd;
+        s.d2h_bytes += (double)blocks[j].w_bytes;
+      }
+      s.stall_ms += st;
+      mt_block_stats& bs = bstats[j];
+      if (u <= L + 1) {
+        s.fwd_ms += c;
+        bs.fwd_ms = c;
+        bs.h2d_fwd_ms = h;
+        bs.stall_fwd_ms = st;
+        if (u == L + 1) bs.d2h_ms = dd;
+      } else {
+        s.bwd_ms += c;
+        bs.bwd_ms = c;
+        bs.h2d_bwd_ms = h;
+        bs.stall_bwd_ms = st;
+        bs.d2h_ms = dd;
+      }
+    }
+  } else {
+    s.h2d_ms = ms_between(ev_h2d_s[0], ev_h2d_e[0]);
+    s.d2h_ms = ms_between(ev_d2h_s[0], ev_d2h_e[0]);
+    for (auto& b : blocks) {
+      s.h2d_bytes += (double)b.w_bytes;
+      s.d2h_bytes += (double)b.w_bytes;
+    }
+    s.fwd_ms = ms_between(ev_c_s[0], ev_c_e[0]);
+  }
+  for (size_t i = 0; i + 1 < kev_used + 1 && i < kev_used; i += 2) {
+    const double ms = ms_between(kev[i], kev[i + 1]);
+    const auto& meta = kev_meta[i / 2];
+    if (meta.second == 0) {
+      s.gemm_ms += ms;
+      s.gemm_flops += meta.first;
+      s.gemm_launches++;
+    } else {
+      s.attn_ms += ms;
+      s.attn_flops += meta.first;
+      s.attn_launches++;
+    }
+  }
+}
+
+// -------------------------------------------------------------- create --
+static std::vector<float> rope_table(int T, int hd, double theta, bool sine) {
+  std::vector<float> out((size_t)T * (hd / 2));
+  for (int t = 0; t < T; ++t)
+    for (int i = 0; i < hd / 2; ++i) {
+      const double w = std::pow(theta, -2.0 * i / hd);
+      const double a = (double)t * w;
+      out[(size_t)t * (hd / 2) + i] = (float)(sine ? std::sin(a) : std::cos(a));
+    }
+  return out;
+}
+
+Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void* const streams[3]) {
+  std::string why;
+  if (validate_config(*cfg, &why) != MT_OK) throw ApiError{MT_E_INVALID, why};
+  if (!arena || !streams || !streams[1]) throw ApiError{MT_E_INVALID, "null arena or compute stream"};
+  if ((uintptr_t)arena & 255) throw ApiError{MT_E_ALIGN, "device arena must be 256-byte aligned"};
+  std::unique_ptr<Model> m(new Model());
+  m->init_dims(*cfg);
+  const uint64_t need = m->device_bytes();
+  if (arena_bytes < need) throw ApiError{MT_E_SIZE, "device arena smaller than mt_device_bytes"};
+  m->arena = (uint8_t*)arena;
+  m->arena_bytes = arena_bytes;
+  m->sc = (hipStream_t)streams[1];
+  m->sp = streams[0] ? (hipStream_t)streams[0] : m->sc;
+  m->so = streams[2] ? (hipStream_t)streams[2] : m->sc;
+  if (cfg->store_dtype == MT_BF16)
+    m->carve_all<uint16_t>(m->arena);
+  else
+    m->carve_all<float>(m->arena);
+  // RoPE tables (float64 angles rounded to float32) and zeroed grad slots:
+  // tensor padding inside a grad slot is never written and must stay 0.
+  auto c = rope_table(m->Tq, m->hd, cfg->rope_theta, false);
+  auto s = rope_table(m->Tq, m->hd, cfg->rope_theta, true);
+  MT_HIP(hipMemcpy(m->cosb, c.data(), c.size() * 4, hipMemcpyHostToDevice));
+  MT_HIP(hipMemcpy(m->sinb, s.data(), s.size() * 4, hipMemcpyHostToDevice));
+  for (int g = 0; g < 2; ++g) MT_HIP(hipMemset(m->gslot[g], 0, m->slot_bytes));
+  if (m->gres) {
+    uint64_t tot = 0;
+    for (auto& b : m->blocks) tot += round_up(b.w_bytes, 256);
+    MT_HIP(hipMemset(m->gres, 0, tot));
+  }
+  MT_HIP(hipDeviceSynchronize());
+  MT_HIP(hipHostMalloc((void**)&m->h_tok, sizeof(int32_t) * m->M, hipHostMallocDefault));
+  MT_HIP(hipHostMalloc((void**)&m->h_order, sizeof(int32_t) * m->M, hipHostMallocDefault));
+  MT_HIP(hipHostMalloc((void**)&m->h_seg, sizeof(int32_t) * (m->V + 1), hipHostMallocDefault));
+  MT_HIP(hipHostMalloc((void**)&m->h_loss, 256, hipHostMallocDefault));
+  *m->h_loss = NAN;
+  auto mk = [&](std::vector<hipEvent_t>& v) {
+    v.resize(m->n_uses);
+    for (auto& e : v) MT_HIP(hipEventCreate(&e));
+  };
+  mk(m->ev_h2d_s);
+  mk(m->ev_h2d_e);
+  mk(m->ev_wait);
+  mk(m->ev_c_s);
+  mk(m->ev_c_e);
+  mk(m->ev_d2h_s);
+  mk(m->ev_d2h_e);
+  MT_HIP(hipEventCreate(&m->ev_loss));
+  MT_HIP(hipEventCreate(&m->ev_start));
+  MT_HIP(hipEventCreate(&m->ev_end));
+  int threads = cfg->host_threads;
+  if (threads <= 0) {
+    cpu_set_t set;
+    threads = sched_getaffinity(0, sizeof(set), &set) == 0 ? CPU_COUNT(&set) : (int)std::thread::hardware_concurrency();
+    threads = std::max(1, threads);
+  }
+  m->pool.reset(new ThreadPool(threads));
+  m->bstats.assign(m->blocks.size(), mt_block_stats{});
+  return m.release();
+}
+
+void destroy_model(Model* m) {
+  if (!m) return;
+  hipStreamSynchronize(m->sc);
+  if (m->sp) hipStreamSynchronize(m->sp);
+  if (m->so) hipStreamSynchronize(m->so);
+  for (auto* v : {&m->ev_h2d_s, &m->ev_h2d_e, &m->ev_wait, &m->ev_c_s, &m->ev_c_e, &m->ev_d2h_s, &m->ev_d2h_e})
+    for (auto e : *v) hipEventDestroy(e);
+  for (auto e : m->kev) hipEventDestroy(e);
+  hipEventDestroy(m->ev_loss);
+  hipEventDestroy(m->ev_start);
+  hipEventDestroy(m->ev_end);
+  hipHostFree(m->h_tok);
+  hipHostFree(m->h_order);
+  hipHostFree(m->h_seg);
+  hipHostFree(m->h_loss);
+  delete m;
+}
+
+uint64_t device_bytes_for(const mt_config& cfg) {
+  std::string why;
+  if (validate_config(cfg, &why) != MT_OK) throw ApiError{MT_E_INVALID, why};
+  Model m;
+  m.init_dims(cfg);
+  return m.device_bytes();
+}
+
+int bind_store(Model* m, void* host, size_t bytes) {
+  if (!host) throw ApiError{MT_E_INVALID, "null store"};
+  if ((uintptr_t)host % kStoreAlign) throw ApiError{MT_E_ALIGN, "host store must be 4 KiB aligned"};
+  if (bytes < m->store_bytes) throw ApiError{MT_E_SIZE, "host store smaller than mt_host_store_bytes"};
+  const StoreHeader* h = (const StoreHeader*)host;
+  if (h->magic != kStoreMagic || h->version != kStoreVersion) throw ApiError{MT_E_INVALID, "store header magic/version"};
+  const mt_config& a = h->cfg;
+  const mt_config& c = m->cfg;
+  if (a.n_layers != c.n_layers || a.d_model != c.d_model || a.n_heads != c.n_heads || a.head_dim != c.head_dim ||
+      a.d_ff != c.d_ff || a.vocab != c.vocab || a.store_dtype != c.store_dtype)
+    throw ApiError{MT_E_INVALID, "store header describes another model shape"};
+  unsigned int flags = 0;
+  if (hipHostGetFlags(&flags, host) != hipSuccess) {
+    (void)hipGetLastError();
+    throw ApiError{MT_E_INVALID, "host store is not pinned (use mt_alloc_host_store)"};
+  }
+  m->host = (uint8_t*)host;
+  return MT_OK;
+}
+
+int model_step(Model* m, const int32_t* tokens) {
+  if (!m->host) throw ApiError{MT_E_NOT_BOUND, "no host store bound"};
+  if (!tokens) throw ApiError{MT_E_INVALID, "null tokens"};
+  return m->train_step(tokens);
+}
+
+int model_loss(const Model* m, float* out) {
+  if (!m->have_loss) throw ApiError{MT_E_STATE, "no completed step"};
+  *out = m->last_loss;
+  return MT_OK;
+}
+
+int model_stats(const Model* m, mt_stats* out) {
+  *out = m->stats;
+  return MT_OK;
+}
+
+int model_block_stats(const Model* m, int block, mt_block_stats* out) {
+  if (block < 0 || block >= (int)m->bstats.size()) throw ApiError{MT_E_INVALID, "block index"};
+  *out = m->bstats[block];
+  return MT_OK;
+}
+
+int model_debug(const Model* m, int layer, void** ckpt, void** row_loss) {
+  if (layer < 0 || layer > m->L) throw ApiError{MT_E_INVALID, "layer index"};
+  if (ckpt) *ckpt = m->ckpt + (uint64_t)layer * m->M * m->d;
+  if (row_loss) {
+    if (m->cfg.store_dtype == MT_BF16) {
+      HeadWs<uint16_t> h = const_cast<Model*>(m)->headws<uint16_t>();
+      *row_loss = h.row_loss;
+    } else {
+      HeadWs<float> h = const_cast<Model*>(m)->headws<float>();
+      *row_loss = h.row_loss;
+    }
+  }
+  return MT_OK;
+}
+
+}  // namespace mt

@@ -1,0 +1,124 @@
+// extern "C" entry points of include/mt_kernels.h.
+#include <cmath>
+#include <vector>
+
+#include "kernels.h"
+#include "mt_kernels.h"
+
+namespace mt {
+template <typename F>
+static int kguard(F&& f) {
+  try {
+    f();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) throw HipError{e, "kernel launch"};
+    return MT_OK;
+  } catch (const ApiError& e) {
+    set_error(e.msg);
+    return e.code;
+  } catch (const HipError& e) {
+    set_error(std::string(hipGetErrorString(e.code)) + " in " + e.where);
+    return MT_E_HIP;
+  }
+}
+static void need(bool ok, const char* msg) {
+  if (!ok) throw ApiError{MT_E_INVALID, msg};
+}
+}  // namespace mt
+
+using namespace mt;
+
+extern "C" {
+
+int mt_gemm(int32_t dtype, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+            const float* R, int64_t ldr, int32_t M, int32_t N, int32_t K, int32_t epi, void* stream) {
+  return kguard([&] {
+    need(epi >= 0 && epi <= 2, "epi");
+    need(M >= 0 && N >= 0 && K >= 0, "negative size");
+    need(lda >= K && ldb >= K && ldc >= N, "leading dimensions");
+    need(epi != 2 || (R && ldr >= N), "R");
+    if (dtype == MT_BF16)
+      gemm_nt<uint16_t>((const uint16_t*)A, lda, (const uint16_t*)B, ldb, C, ldc, R, ldr, M, N, K, (Epi)epi,
+                        (hipStream_t)stream);
+    else if (dtype == MT_F32)
+      gemm_nt<float>((const float*)A, lda, (const float*)B, ldb, C, ldc, R, ldr, M, N, K, (Epi)epi,
+                     (hipStream_t)stream);
+    else
+      need(false, "dtype");
+  });
+}
+
+int mt_transpose(int32_t dtype, const void* in, int64_t ld_in, void* out, int64_t ld_out, int32_t R, int32_t C,
+                 void* stream) {
+  return kguard([&] {
+    need(ld_in >= C && ld_out >= R, "leading dimensions");
+    if (dtype == MT_BF16)
+      transpose<uint16_t>((const uint16_t*)in, ld_in, (uint16_t*)out, ld_out, R, C, (hipStream_t)stream);
+    else if (dtype == MT_F32)
+      transpose<float>((const float*)in, ld_in, (float*)out, ld_out, R, C, (hipStream_t)stream);
+    else
+      need(false, "dtype");
+  });
+}
+
+int mt_rope_tables(int32_t T, int32_t hd, double theta, float* cos_out, float* sin_out) {
+  return kguard([&] {
+    need(T > 0 && hd > 0 && hd % 2 == 0 && cos_out && sin_out, "arguments");
+    for (int t = 0; t < T; ++t)
+      for (int i = 0; i < hd / 2; ++i) {
+        const double a = (double)t * std::pow(theta, -2.0 * i / hd);
+        cos_out[(size_t)t * (hd / 2) + i] = (float)std::cos(a);
+        sin_out[(size_t)t * (hd / 2) + i] = (float)std::sin(a);
+      }
+  });
+}
+
+int mt_rope_qkv(int32_t dtype, void* qkv, void* qkvT, const float* cos_t, const float* sin_t, int32_t B, int32_t T,
+                int32_t H, int32_t hd, void* stream) {
+  return kguard([&] {
+    need(B > 0 && T > 0 && H > 0 && hd > 0 && hd % 2 == 0 && hd <= 128, "shape");
+    const int M = B * T, d = H * hd;
+    if (dtype == MT_BF16)
+      rope_qkv_fwd<uint16_t>((uint16_t*)qkv, (uint16_t*)qkvT, cos_t, sin_t, M, T, d, hd, (hipStream_t)stream);
+    else if (dtype == MT_F32)
+      rope_qkv_fwd<float>((float*)qkv, (float*)qkvT, cos_t, sin_t, M, T, d, hd, (hipStream_t)stream);
+    else
+      need(false, "dtype");
+  });
+}
+
+int mt_attention_fwd(int32_t dtype, const void* qkv, const void* qkvT, void* o, float* lse, int32_t B, int32_t T,
+                     int32_t H, int32_t hd, void* stream) {
+  return kguard([&] {
+    need(B > 0 && T > 0 && H > 0 && hd > 0, "shape");
+    if (dtype == MT_BF16)
+      attn_fwd<uint16_t>((const uint16_t*)qkv, (const uint16_t*)qkvT, (uint16_t*)o, lse, B, T, H, hd,
+                         (hipStream_t)stream);
+    else if (dtype == MT_F32)
+      attn_fwd<float>((const float*)qkv, (const float*)qkvT, (float*)o, lse, B, T, H, hd, (hipStream_t)stream);
+    else
+      need(false, "dtype");
+  });
+}
+
+int mt_attention_bwd(int32_t dtype, const void* qkv, const void* qkvT, const void* o, const void* dO,
+                     const void* dOT, const float* lse, float* Dsum, void* dqkvT, int32_t B, int32_t T, int32_t H,
+                     int32_t hd, void* stream) {
+  return kguard([&] {
+    need(B > 0 && T > 0 && H > 0 && hd > 0, "shape");
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == MT_BF16) {
+      attn_bwd_dsum<uint16_t>((const uint16_t*)dO, (const uint16_t*)o, Dsum, B, T, H, hd, s);
+      attn_bwd<uint16_t>((const uint16_t*)qkv, (const uint16_t*)qkvT, (const uint16_t*)dO, (const uint16_t*)dOT, lse,
+                         Dsum, (uint16_t*)dqkvT, B, T, H, hd, s);
+    } else if (dtype == MT_F32) {
+      attn_bwd_dsum<float>((const float*)dO, (const float*)o, Dsum, B, T, H, hd, s);
+      attn_bwd<float>((const float*)qkv, (const float*)qkvT, (const float*)dO, (const float*)dOT, lse, Dsum,
+                      (float*)dqkvT, B, T, H, hd, s);
+    } else {
+      need(false, "dtype");
+    }
+  });
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Launchers of the device kernels.  T is the storage type of weights and of
+// GEMM operands: float (all-fp32 store) or uint16_t (bf16 bit patterns).
+// Every launcher enqueues on `s` and returns without synchronising.
+#pragma once
+
+#include "common.h"
+
+namespace mt {
+
+// ---------------------------------------------------------------- GEMM --
+// C[M x N] = A[M x K] . B[N x K]^T, both operands K-contiguous (row stride
+// lda / ldb elements), fp32 accumulation.  Epilogues:
+enum Epi {
+  EPI_STORE = 0,   // C (type T) = acc, rounded to nearest-even for bf16
+  EPI_F32 = 1,     // C (float) = acc
+  EPI_ADD_F32 = 2  // C (float) = R + acc, R float [M x N] with row stride ldr
+};
+template <typename T>
+void gemm_nt(const T* A, int64_t lda, const T* B, int64_t ldb, void* C, int64_t ldc, const float* R,
+             int64_t ldr, int M, int N, int K, Epi epi, hipStream_t s);
+
+// ---------------------------------------------------------- elementwise --
+template <typename T>
+void embed_fwd(const int32_t* tok, const T* E, float* x, int M, int d, hipStream_t s);
+// dE[v] = sum over positions m with tok[m] == v, in increasing m, of dx[m];
+// order[] lists positions sorted by token (stable), seg[v]..seg[v+1] its range.
+template <typename T>
+void embed_bwd(const float* dx, const int32_t* order, const int32_t* seg, T* dE, int V, int d, hipStream_t s);
+template <typename T>
+void rmsnorm_fwd(const float* x, const T* g, T* y, float* rstd, int M, int d, float eps, hipStream_t s);
+// dx = resid + r*(dy*g - xh*mean(dy*g*xh)), xh = x*r; resid may be null.
+template <typename T>
+void rmsnorm_bwd(const float* dy, const float* x, const T* g, const float* rstd, const float* resid, float* dx,
+                 int M, int d, hipStream_t s);
+// dg = sum_rows dy*x*r (two deterministic passes through `partial`,
+// which holds rmsnorm_dg_partial_elems(M, d) floats), written as T.
+size_t rmsnorm_dg_partial_elems(int M, int d);
+template <typename T>
+void rmsnorm_dg(const float* dy, const float* x, const float* rstd, float* partial, T* dg, int M, int d,
+                hipStream_t s);
+// Rotate q and k of qkv [M x 3d] in place (pairs (i, i+hd/2), angle
+// t*theta^(-2i/hd), t = m mod T) and write the transpose qkvT [3d x M].
+template <typename T>
+void rope_qkv_fwd(T* qkv, T* qkvT, const float* cosb, const float* sinb, int M, int T_, int d, int hd,
+                  hipStream_t s);
+// Inverse rotation of the dq, dk rows of dqkvT [3d x M], in place.
+template <typename T>
+void rope_bwd_T(T* dqkvT, const float* cosb, const float* sinb, int M, int T_, int d, int hd, hipStream_t s);
+template <typename T>
+void swiglu_fwd(const T* gu, T* y, int M, int F, hipStream_t s);
+template <typename T>
+void swiglu_bwd(const T* dy, const T* gu, T* dgu, int M, int F, hipStream_t s);
+// Row-wise loss and gradient of the mean next-token cross-entropy:
+// rows with t = m mod T < T-1 have label tok[m+1]; others get loss 0, grad 0.
+template <typename T>
+void xent(const float* logits, const int32_t* tok, float* row_loss, T* dlogits, int M, int T_, int V,
+          float inv_n, hipStream_t s);
+// out[0] = (sum of x[0..n) in a fixed order) * scale.
+void sum_fixed(const float* x, float* out, int n, float scale, hipStream_t s);
+// out[C x R] = in[R x C]^T.
+template <typename T>
+void transpose(const T* in, int64_t ld_in, T* out, int64_t ld_out, int R, int C, hipStream_t s);
+// out = T(in) and outT = T(in)^T for in float [R x C].
+template <typename T>
+void cast_transpose(const float* in, T* out, T* outT, int R, int C, hipStream_t s);
+void fill_u32(void* p, uint32_t value, size_t n_words, hipStream_t s);
+
+// ------------------------------------------------------------ attention --
+// qkv [M x 3d] (q, k rotated), qkvT [3d x M]; o [M x d]; lse [B*H x T]
+// (base-2 log-sum-exp of the scaled scores).
+template <typename T>
+void attn_fwd(const T* qkv, const T* qkvT, T* o, float* lse, int B, int T_, int H, int hd, hipStream_t s);
+// Dsum[b*H+h][t] = sum_i dO . O over the head.
+template <typename T>
+void attn_bwd_dsum(const T* dO, const T* O, float* Dsum, int B, int T_, int H, int hd, hipStream_t s);
+// dqkvT [3d x M] receives dq, dk, dv (transposed layout).
+template <typename T>
+void attn_bwd(const T* qkv, const T* qkvT, const T* dO, const T* dOT, const float* lse, const float* Dsum,
+              T* dqkvT, int B, int T_, int H, int hd, hipStream_t s);
+
+}  // namespace mt

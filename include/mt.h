@@ -1,0 +1,183 @@
+/*
+ * mt.h — C ABI of the MI355X layer-streamed training library.
+ *
+ * The method (MegaTrain, arXiv 2026; chatpaper.ai abstract and
+ * radar.chestersoft.de "Methodik"): parameters and optimizer state live in
+ * host memory; for each layer the weights stream in to the GPU and the
+ * gradients stream out; a double-buffered engine overlaps prefetch, compute
+ * and gradient offload on three streams; stateless layer templates bind the
+ * incoming weights; every state of a layer (bf16 weights, bf16 gradients,
+ * fp32 Adam moments) sits in one contiguous 4 KiB-aligned block; the Adam
+ * step runs on the host CPU.
+ *
+ * Conventions of every call:
+ *   - return 0 (MT_OK) on success or a negative MT_E_* code; no exception or
+ *     abort crosses the ABI; mt_last_error() gives a message (thread-local);
+ *   - pointers are plain host or device addresses as stated per argument;
+ *   - the caller owns the device arena, the three streams, the host store and
+ *     the token buffer; all of them must outlive the model handle;
+ *   - calls on one model handle are not thread-safe; use one thread per model.
+ */
+#ifndef MT_H
+#define MT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- errors -- */
+#define MT_OK 0
+#define MT_E_INVALID (-1)    /* bad configuration or argument */
+#define MT_E_SIZE (-2)       /* buffer too small */
+#define MT_E_ALIGN (-3)      /* buffer not 4 KiB (store) or 256 B (arena) aligned */
+#define MT_E_NOT_BOUND (-4)  /* mt_train_step before mt_bind_host_store */
+#define MT_E_HIP (-5)        /* a HIP runtime call failed; see mt_last_error() */
+#define MT_E_NONFINITE (-6)  /* loss not finite: no Adam ran, the store's W/m/v are untouched */
+#define MT_E_OOM (-7)        /* host allocation failed */
+#define MT_E_STATE (-8)      /* wrong call order or unsupported mode for this call */
+
+/* ------------------------------------------------------------- constants -- */
+#define MT_F32 0             /* all-fp32 store: W, G, m, v in float32 */
+#define MT_BF16 1            /* bf16 W and G, fp32 m and v */
+
+#define MT_STREAMED 0        /* two weight slots, three streams (the method) */
+#define MT_SERIALIZED 1      /* the streamed schedule on the compute stream only */
+#define MT_RESIDENT 2        /* every block's W on the device, no recompute */
+
+#define MT_BLOCK_EMBED 0
+#define MT_BLOCK_LAYER 1
+#define MT_BLOCK_HEAD 2
+
+#define MT_STORE_ALIGN 4096
+#define MT_MAX_TENSORS 8
+
+/* Model and step configuration.  The architecture is a pre-norm decoder:
+ * RMSNorm, causal multi-head attention with rotary positions (half-split
+ * pairs), SwiGLU feed-forward, untied output head, mean next-token
+ * cross-entropy over batch*(seq_len-1) positions; Adam without weight decay. */
+typedef struct mt_config {
+  int32_t n_layers, d_model, n_heads, head_dim, d_ff, vocab, batch, seq_len;
+  int32_t store_dtype;   /* MT_F32 or MT_BF16 */
+  double rms_eps;        /* added inside the square root (used as float32 on the device) */
+  double rope_theta;     /* rotation frequency base */
+  double lr, beta1, beta2, adam_eps;  /* Adam: rounded to float32 as the host update uses them */
+  int32_t mode;          /* MT_STREAMED, MT_SERIALIZED or MT_RESIDENT */
+  int32_t host_threads;  /* Adam worker threads; 0 = every core in the affinity mask */
+  int32_t flags;         /* MT_FLAG_* bits */
+} mt_config;
+
+#define MT_FLAG_TIME_KERNELS 1  /* bracket every GEMM and attention launch with events */
+#define MT_FLAG_POISON 2        /* fill a weight slot with NaN before each prefetch */
+
+/* One tensor inside a block region: element offset from the region start,
+ * row-major [rows x cols]. */
+typedef struct mt_tensor_desc {
+  uint64_t offset;
+  int32_t rows, cols;
+} mt_tensor_desc;
+
+/* One block of the host store: [W | G | m | v], each region 4 KiB-aligned.
+ * All offsets are bytes from the start of the store.  Region element counts
+ * are equal for the four regions; W and G hold wb-byte elements (2 for
+ * bf16, 4 for f32), m and v hold float32.
+ * Tensor order — embed: E [V x d]; layer: Wqkv [3d x d] (q, k, v rows),
+ * Wo [d x d], Wgu [2F x d] (gate rows then up rows), Wd [d x F],
+ * attn_norm [1 x d], ffn_norm [1 x d]; head: Wh [V x d], final_norm [1 x d]. */
+typedef struct mt_block_desc {
+  int32_t kind, layer, n_tensors, pad_;
+  uint64_t base, w_off, g_off, m_off, v_off;
+  uint64_t region_elems;
+  uint64_t w_bytes, mv_bytes;
+  mt_tensor_desc tensors[MT_MAX_TENSORS];
+} mt_block_desc;
+
+/* Step statistics (milliseconds unless named otherwise); filled by
+ * mt_train_step, read by mt_get_stats. */
+typedef struct mt_stats {
+  double step_ms;            /* wall time of the last mt_train_step */
+  double device_ms;          /* first prefetch start to last offload end (compute-stream events) */
+  double fwd_ms, bwd_ms;     /* compute stream: forward sweep, head, backward sweep */
+  double h2d_ms, d2h_ms;     /* summed copy durations */
+  double h2d_bytes, d2h_bytes;
+  double stall_ms;           /* compute stream waiting for a weight slot to arrive */
+  double adam_ms;            /* summed host Adam time */
+  double adam_tail_ms;       /* host Adam time after the device finished */
+  double gemm_ms, gemm_flops;/* MT_FLAG_TIME_KERNELS: summed GEMM launch time and flops */
+  double attn_ms, attn_flops;
+  int64_t gemm_launches, attn_launches;
+  double loss;
+  int32_t n_blocks, pad_;
+} mt_stats;
+
+/* Per-block timing of the last step: forward and backward compute time on
+ * the compute stream, prefetch and offload copy time, and the stall of the
+ * compute stream before the block's weights were ready. */
+typedef struct mt_block_stats {
+  double fwd_ms, bwd_ms, h2d_fwd_ms, h2d_bwd_ms, d2h_ms, stall_fwd_ms, stall_bwd_ms, adam_ms;
+} mt_block_stats;
+
+/* ------------------------------------------------------------ layout ----- */
+/* Bytes of the host store for cfg (header page + every block). */
+size_t mt_host_store_bytes(const mt_config* cfg);
+/* Number of blocks: embed, n_layers layers, head. */
+int mt_block_count(const mt_config* cfg);
+/* Layout of block i (0 = embed, 1..L = layers, L+1 = head). */
+int mt_block_info(const mt_config* cfg, int block, mt_block_desc* out);
+/* Bytes of the device arena the caller must allocate for cfg. */
+size_t mt_device_bytes(const mt_config* cfg);
+
+/* Pinned host store: hipHostMalloc of `bytes` (rounded up to 4 KiB);
+ * *out receives the host address.  Free with mt_free_host_store. */
+int mt_alloc_host_store(size_t bytes, void** out);
+void mt_free_host_store(void* p);
+/* Write the 4 KiB header page (magic, version, config, Adam step 0) and
+ * zero every block (W, G, m, v and the padding between tensors), using the
+ * host threads of cfg (host_threads, 0 = all allowed cores). */
+int mt_init_store_header(const mt_config* cfg, void* host_base, size_t bytes);
+/* Adam step counter t stored in the header (number of completed steps). */
+int mt_store_step(const void* host_base, int64_t* t);
+
+/* ------------------------------------------------------------- model ----- */
+/* Create a model.  dev_arena: device memory of at least mt_device_bytes(cfg),
+ * 256-byte aligned, caller-owned.  streams: prefetch, compute, offload
+ * hipStream_t handles (default priority), caller-owned; in MT_SERIALIZED
+ * mode only streams[1] is used.  No device work except uploading the RoPE
+ * table; *out receives the handle. */
+int mt_create_model(const mt_config* cfg, void* dev_arena, size_t arena_bytes,
+                    void* const streams[3], void** out);
+/* Bind a host store (from mt_alloc_host_store, header written, weights
+ * initialised).  Checked: size >= mt_host_store_bytes, 4 KiB alignment,
+ * header magic and config; the store must be pinned. */
+int mt_bind_host_store(void* model, void* host_base, size_t bytes);
+/* One training step on tokens (host int32 [batch*seq_len], values in
+ * [0, vocab)).  Synchronous: on return 0 the store holds the post-Adam W, m,
+ * v, this step's G, and t+1 in the header.  On MT_E_NONFINITE no Adam ran. */
+int mt_train_step(void* model, const int32_t* tokens);
+/* Loss of the last completed step. */
+int mt_get_loss(const void* model, float* out);
+int mt_get_stats(const void* model, mt_stats* out);
+int mt_get_block_stats(const void* model, int block, mt_block_stats* out);
+/* Device addresses inside the arena for inspection by tests: the fp32
+ * layer-boundary checkpoint x^l [batch*seq_len x d_model] (l = 0..n_layers)
+ * and the fp32 per-position loss [batch*seq_len] (0 on the last position of
+ * each sequence).  Valid until the next step. */
+int mt_debug_buffers(const void* model, int layer, void** ckpt, void** row_loss);
+void mt_destroy_model(void* model);
+
+/* ------------------------------------------------------------ host Adam -- */
+/* One Adam step over n elements on the host (the routine mt_train_step
+ * uses per block): w, g of store dtype (bf16 as uint16 bits, or f32), m, v
+ * float32; updated in place; step number t >= 1; threads as in mt_config. */
+int mt_host_adam(int32_t store_dtype, void* w, const void* g, float* m, float* v, size_t n,
+                 int64_t t, double lr, double beta1, double beta2, double eps, int32_t threads);
+
+const char* mt_last_error(void);
+const char* mt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MT_H */

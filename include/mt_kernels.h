@@ -1,0 +1,63 @@
+/*
+ * mt_kernels.h — C ABI of the individual device kernels that one training
+ * step of the layer-streamed decoder is made of (the same code mt_train_step
+ * launches), for testing and reuse.
+ *
+ * Pointers are device addresses unless said otherwise; `stream` is a
+ * hipStream_t (null = the default stream).  Calls enqueue and return without
+ * synchronising; they return 0 or a negative MT_E_* code (mt.h) and set
+ * mt_last_error().  dtype is MT_BF16 (elements are bfloat16 bit patterns,
+ * uint16) or MT_F32.
+ */
+#ifndef MT_KERNELS_H
+#define MT_KERNELS_H
+
+#include "mt.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* C[M x N] = A[M x K] . B[N x K]^T, fp32 accumulation.  A, B row-major with
+ * row strides lda, ldb (elements).  epi 0: C has dtype (bf16 rounded to
+ * nearest-even); epi 1: C is float; epi 2: C (float) = R + A.B^T with R float
+ * [M x N], row stride ldr.  bf16 needs K, lda, ldb multiples of 8 and 16-byte
+ * aligned A, B.  Every dense projection of the layer (forward, data gradient,
+ * weight gradient) is this contraction once the operand that is not
+ * contraction-contiguous is transposed. */
+int mt_gemm(int32_t dtype, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+            const float* R, int64_t ldr, int32_t M, int32_t N, int32_t K, int32_t epi, void* stream);
+
+/* out[C x R] = in[R x C]^T (row strides ld_in, ld_out). */
+int mt_transpose(int32_t dtype, const void* in, int64_t ld_in, void* out, int64_t ld_out, int32_t R, int32_t C,
+                 void* stream);
+
+/* Host: RoPE tables cos/sin [T x hd/2] of angle t * theta^(-2i/hd), computed
+ * in double and rounded to float (host buffers of T*hd/2 floats). */
+int mt_rope_tables(int32_t T, int32_t hd, double theta, float* cos_out, float* sin_out);
+
+/* qkv [B*T x 3d] (q | k | v columns, head-major inside each): rotate q and k
+ * in place by +t*w_i on pairs (i, i+hd/2), t = position in the sequence, and
+ * write the transpose qkvT [3d x B*T].  cos/sin: device tables from
+ * mt_rope_tables. */
+int mt_rope_qkv(int32_t dtype, void* qkv, void* qkvT, const float* cos_t, const float* sin_t, int32_t B, int32_t T,
+                int32_t H, int32_t hd, void* stream);
+
+/* Causal softmax attention per (batch, head) with scale 1/sqrt(hd).
+ * Inputs: rotated qkv and qkvT as left by mt_rope_qkv.  Outputs:
+ * o [B*T x d] (dtype) and lse [B*H x T] (float, base-2 log-sum-exp of the
+ * scaled scores times log2(e)).  bf16: hd = 128 and T % 64 == 0; f32: hd <= 64. */
+int mt_attention_fwd(int32_t dtype, const void* qkv, const void* qkvT, void* o, float* lse, int32_t B, int32_t T,
+                     int32_t H, int32_t hd, void* stream);
+
+/* Backward of mt_attention_fwd given dO [B*T x d] and dOT [d x B*T]:
+ * writes Dsum [B*H x T] (float scratch, rowsum(dO * O)) and
+ * dqkvT [3d x B*T] = (dq | dk | dv)^T with respect to the rotated q, k. */
+int mt_attention_bwd(int32_t dtype, const void* qkv, const void* qkvT, const void* o, const void* dO,
+                     const void* dOT, const float* lse, float* Dsum, void* dqkvT, int32_t B, int32_t T, int32_t H,
+                     int32_t hd, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MT_KERNELS_H */

@@ -1,0 +1,227 @@
+"""Kernel parity on the GPU through the C ABI (include/mt_kernels.h).
+
+References: the definitions the oracle uses (a projection is x @ W.T;
+attention, RoPE as in oracle.model), evaluated in float64 on exactly the
+bf16 values the kernel reads.  Shapes span several tiles with ragged tails,
+and the full 14B-shape projections are checked on sampled outputs.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import datagen
+import host_memory_layer_amd as mt
+from oracle import attention_bwd, attention_fwd, rope_apply, rope_tables
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def bf16_tensor(x_f32):
+    """float32 array -> (device uint16 tensor of bf16 bits, float64 values)."""
+    bits = datagen.f32_to_bf16_bits(np.ascontiguousarray(x_f32, np.float32))
+    t = torch.from_numpy(bits.view(np.int16)).to(dev())
+    return t, datagen.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def to_f32(t_bits):
+    return datagen.bf16_bits_to_f32(t_bits.cpu().numpy().view(np.uint16)).astype(np.float64)
+
+
+def gemm(dtype, A, lda, B, ldb, C, ldc, M, N, K, epi, R=None, ldr=0):
+    mt.check(mt.lib().mt_gemm(dtype, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
+                              R.data_ptr() if R is not None else None, ldr, M, N, K, epi, None))
+
+
+def acc_bound(a, b):
+    """Worst-case fp32 accumulation error of a @ b.T: K * 2^-24 * |a| @ |b|.T."""
+    K = a.shape[1]
+    return K * 2.0 ** -24 * (np.abs(a) @ np.abs(b).T)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 520, 200), (64, 8, 8), (513, 257, 1032), (1, 1, 8)])
+def test_gemm_bf16_small(M, N, K):
+    rng = np.random.default_rng(M * 7 + N)
+    A, a = bf16_tensor(rng.standard_normal((M, K)).astype(np.float32))
+    B, b = bf16_tensor(rng.standard_normal((N, K)).astype(np.float32))
+    ref = a @ b.T
+    bound = acc_bound(a, b)
+    # fp32 output
+    C = torch.empty((M, N), dtype=torch.float32, device=dev())
+    gemm(mt.MT_BF16, A, K, B, K, C, N, M, N, K, mt.EPI_F32)
+    torch.cuda.synchronize()
+    c = C.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(c - ref) <= bound + 1e-30)
+    # bf16 output: the fp32 result rounded to nearest even
+    Cb = torch.empty((M, N), dtype=torch.int16, device=dev())
+    gemm(mt.MT_BF16, A, K, B, K, Cb, N, M, N, K, mt.EPI_STORE)
+    # residual add
+    R = torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32)).to(dev())
+    Cr = torch.empty((M, N), dtype=torch.float32, device=dev())
+    gemm(mt.MT_BF16, A, K, B, K, Cr, N, M, N, K, mt.EPI_ADD_F32, R, N)
+    torch.cuda.synchronize()
+    cb = Cb.cpu().numpy().view(np.uint16)
+    assert np.array_equal(cb, datagen.f32_to_bf16_bits(C.cpu().numpy()))
+    cr = Cr.cpu().numpy().astype(np.float64)
+    r = R.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(cr - (r + ref)) <= bound + np.abs(r + ref) * 2.0 ** -23 + 1e-30)
+
+
+def test_gemm_bf16_strided_operands():
+    """Row strides larger than K (views into wider matrices)."""
+    rng = np.random.default_rng(5)
+    M, N, K, lda, ldb, ldc = 260, 300, 136, 200, 144, 320
+    A, a = bf16_tensor(rng.standard_normal((M, lda)).astype(np.float32))
+    B, b = bf16_tensor(rng.standard_normal((N, ldb)).astype(np.float32))
+    C = torch.full((M, ldc), 7.0, dtype=torch.float32, device=dev())
+    gemm(mt.MT_BF16, A, lda, B, ldb, C, ldc, M, N, K, mt.EPI_F32)
+    torch.cuda.synchronize()
+    c = C.cpu().numpy().astype(np.float64)
+    ref = a[:, :K] @ b[:, :K].T
+    assert np.all(np.abs(c[:, :N] - ref) <= acc_bound(a[:, :K], b[:, :K]) + 1e-30)
+    assert np.all(c[:, N:] == 7.0)
+
+
+def test_gemm_f32_small():
+    rng = np.random.default_rng(9)
+    M, N, K = 130, 77, 45
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    b = rng.standard_normal((N, K)).astype(np.float32)
+    A = torch.from_numpy(a).to(dev())
+    B = torch.from_numpy(b).to(dev())
+    C = torch.empty((M, N), dtype=torch.float32, device=dev())
+    gemm(mt.MT_F32, A, K, B, K, C, N, M, N, K, mt.EPI_STORE)
+    torch.cuda.synchronize()
+    ref = a.astype(np.float64) @ b.astype(np.float64).T
+    assert np.all(np.abs(C.cpu().numpy() - ref) <= acc_bound(a, b) + 1e-30)
+
+
+# Full-size projections of the 14B shape (32768 tokens, d 5120, F 13824):
+# forward QKV, down-projection data gradient, and a weight gradient with
+# K = 32768 tokens; 4096 sampled outputs each.
+@pytest.mark.parametrize("M,N,K", [(32768, 15360, 5120), (32768, 5120, 13824), (5120, 5120, 32768)])
+def test_gemm_bf16_14b_shapes_sampled(M, N, K):
+    print(f"gemm {M}x{N}x{K}", flush=True)
+    g = torch.Generator(device=dev()).manual_seed(M + N + K)
+    A = torch.randn((M, K), generator=g, device=dev(), dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
+    B = torch.randn((N, K), generator=g, device=dev(), dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev())
+    gemm(mt.MT_BF16, A, K, B, K, C, N, M, N, K, mt.EPI_F32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = rng.integers(0, M, 4096)
+    cols = rng.integers(0, N, 4096)
+    ri = torch.from_numpy(rows).to(dev())
+    ci = torch.from_numpy(cols).to(dev())
+    a = to_f32(A[ri])
+    b = to_f32(B[ci])
+    got = C[ri, ci].cpu().numpy().astype(np.float64)
+    ref = np.einsum("ij,ij->i", a, b)
+    bound = K * 2.0 ** -24 * np.einsum("ij,ij->i", np.abs(a), np.abs(b))
+    assert np.all(np.abs(got - ref) <= bound)
+    # typical error far below the worst case
+    assert np.sqrt(np.mean((got - ref) ** 2)) < 1e-3 * np.sqrt(np.mean(ref ** 2))
+
+
+# ---------------------------------------------------------------- attention --
+def run_attention(dtype, B, T, H, hd, seed, theta=10000.0):
+    rng = np.random.default_rng(seed)
+    d = H * hd
+    M = B * T
+    qkv = (rng.standard_normal((M, 3 * d)) * 1.5).astype(np.float32)
+    dO = rng.standard_normal((M, d)).astype(np.float32)
+    cos = np.empty((T, hd // 2), np.float32)
+    sin = np.empty((T, hd // 2), np.float32)
+    mt.check(mt.lib().mt_rope_tables(T, hd, theta, cos.ctypes.data, sin.ctypes.data))
+    cos_t = torch.from_numpy(cos).to(dev())
+    sin_t = torch.from_numpy(sin).to(dev())
+    if dtype == mt.MT_BF16:
+        q_dev, qkv64 = bf16_tensor(qkv)
+        do_dev, do64 = bf16_tensor(dO)
+        et = torch.int16
+    else:
+        q_dev = torch.from_numpy(qkv).to(dev())
+        do_dev = torch.from_numpy(dO).to(dev())
+        qkv64, do64 = qkv.astype(np.float64), dO.astype(np.float64)
+        et = torch.float32
+    qkvT = torch.empty((3 * d, M), dtype=et, device=dev())
+    mt.check(mt.lib().mt_rope_qkv(dtype, q_dev.data_ptr(), qkvT.data_ptr(), cos_t.data_ptr(), sin_t.data_ptr(),
+                                  B, T, H, hd, None))
+    o = torch.empty((M, d), dtype=et, device=dev())
+    lse = torch.empty((B * H, T), dtype=torch.float32, device=dev())
+    mt.check(mt.lib().mt_attention_fwd(dtype, q_dev.data_ptr(), qkvT.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                       B, T, H, hd, None))
+    doT = torch.empty((d, M), dtype=et, device=dev())
+    mt.check(mt.lib().mt_transpose(dtype, do_dev.data_ptr(), d, doT.data_ptr(), M, M, d, None))
+    Dsum = torch.empty((B * H, T), dtype=torch.float32, device=dev())
+    dqkvT = torch.empty((3 * d, M), dtype=et, device=dev())
+    mt.check(mt.lib().mt_attention_bwd(dtype, q_dev.data_ptr(), qkvT.data_ptr(), o.data_ptr(), do_dev.data_ptr(),
+                                       doT.data_ptr(), lse.data_ptr(), Dsum.data_ptr(), dqkvT.data_ptr(),
+                                       B, T, H, hd, None))
+    torch.cuda.synchronize()
+    conv = to_f32 if dtype == mt.MT_BF16 else (lambda t: t.cpu().numpy().astype(np.float64))
+    out = dict(qkv=conv(q_dev), qkvT=conv(qkvT), o=conv(o), lse=lse.cpu().numpy(), dqkvT=conv(dqkvT))
+    # oracle in float64 on the values the kernel read
+    c64, s64 = rope_tables(T, hd, theta, np.float64)
+    heads = lambda x: x.reshape(B, T, H, hd).transpose(0, 2, 1, 3)
+    q = rope_apply(heads(qkv64[:, :d]), c64, s64)
+    k = rope_apply(heads(qkv64[:, d:2 * d]), c64, s64)
+    v = heads(qkv64[:, 2 * d:])
+    ref = dict(q=q, k=k, v=v, o=np.empty_like(q), dq=np.empty_like(q), dk=np.empty_like(q), dv=np.empty_like(q))
+    dOh = heads(do64)
+    for bb in range(B):
+        ob, p = attention_fwd(q[bb], k[bb], v[bb])
+        ref["o"][bb] = ob
+        ref["dq"][bb], ref["dk"][bb], ref["dv"][bb] = attention_bwd(dOh[bb], q[bb], k[bb], v[bb], p)
+    return out, ref, heads
+
+
+def close(got, ref, cos_min, rel_max):
+    from tests.harness import cosine, maxnorm_rel
+    c, r = cosine(got, ref), maxnorm_rel(got, ref)
+    assert c >= cos_min and r <= rel_max, (c, r)
+
+
+@pytest.mark.parametrize("B,T,H", [(2, 192, 2), (1, 64, 1), (1, 512, 3)])
+def test_attention_bf16(B, T, H):
+    hd = 128
+    d = H * hd
+    out, ref, heads = run_attention(mt.MT_BF16, B, T, H, hd, seed=T + H)
+    # rotated q, k stored back in qkv and transposed in qkvT
+    close(heads(out["qkv"][:, :d]), ref["q"], 0.99999, 1e-2)
+    close(heads(out["qkv"][:, d:2 * d]), ref["k"], 0.99999, 1e-2)
+    assert np.array_equal(out["qkvT"], out["qkv"].T)
+    close(heads(out["o"]), ref["o"], 0.9999, 2e-2)
+    dq = heads(out["dqkvT"][:d].T)
+    dk = heads(out["dqkvT"][d:2 * d].T)
+    dv = heads(out["dqkvT"][2 * d:].T)
+    close(dq, ref["dq"], 0.999, 3e-2)
+    close(dk, ref["dk"], 0.999, 3e-2)
+    close(dv, ref["dv"], 0.999, 3e-2)
+
+
+def test_attention_f32():
+    B, T, H, hd = 2, 64, 4, 32
+    d = H * hd
+    out, ref, heads = run_attention(mt.MT_F32, B, T, H, hd, seed=3)
+    close(heads(out["o"]), ref["o"], 0.9999999, 1e-5)
+    close(heads(out["dqkvT"][:d].T), ref["dq"], 0.9999999, 1e-4)
+    close(heads(out["dqkvT"][d:2 * d].T), ref["dk"], 0.9999999, 1e-4)
+    close(heads(out["dqkvT"][2 * d:].T), ref["dv"], 0.9999999, 1e-4)
+
+
+def test_attention_bf16_14b_head_sampled():
+    """One (batch, head) pair at the 14B shape's sequence length, T = 4096."""
+    out, ref, heads = run_attention(mt.MT_BF16, 1, 4096, 1, 128, seed=11)
+    close(heads(out["o"]), ref["o"], 0.9999, 2e-2)
+    close(heads(out["dqkvT"][:128].T), ref["dq"], 0.999, 3e-2)
+    close(heads(out["dqkvT"][128:256].T), ref["dk"], 0.999, 3e-2)
+    close(heads(out["dqkvT"][256:].T), ref["dv"], 0.999, 3e-2)

@@ -1,0 +1,119 @@
+"""Whole training step on the GPU through the C ABI, against the oracle.
+
+Tolerances (tests/harness.py): loss relative error <= 1e-2; per logical
+tensor, gradient cosine >= 0.999 and max-norm relative error <= 3e-2;
+post-Adam weights Frobenius relative error <= 1e-2.  The streamed,
+serialized and resident schedules must agree bit for bit.
+"""
+import numpy as np
+import pytest
+
+import datagen
+import host_memory_layer_amd as mt
+from oracle import Oracle
+from tests.harness import assert_parity, make_store, read_all
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+# A small bf16 decoder: two layers, head_dim 128, ragged vocabulary.
+SMALL_BF16 = datagen.ModelShape("small-bf16", 2, 256, 2, 128, 512, 1000, 2, 128)
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_step(shape, mode="streamed", flags=0, steps=1):
+    cfg, store = make_store(shape, mode, flags=flags)
+    model = mt.Model(cfg, store, "cuda:0")
+    tok = datagen.tokens(shape)
+    losses = [model.step(tok) for _ in range(steps)]
+    out = dict(loss=losses[-1], losses=losses, g=read_all(store, "g"), w=read_all(store, "w"),
+               m=read_all(store, "m"), v=read_all(store, "v"), stats=model.stats(), t=store.step_count())
+    model.close()
+    store.free()
+    return out
+
+
+def oracle_step(shape):
+    P = datagen.init_params(shape)
+    tok = datagen.tokens(shape)
+    loss, g, w, _ = Oracle(shape, np.float32).step(P, tok, mode="streamed")
+    return float(loss), g, w
+
+
+@pytest.mark.parametrize("shape", [datagen.PRESETS["tiny"], SMALL_BF16], ids=["tiny-f32", "small-bf16"])
+def test_step_matches_oracle(shape):
+    need_gpu()
+    print(f"step parity {shape.name}", flush=True)
+    r = run_step(shape)
+    o_loss, o_g, o_w = oracle_step(shape)
+    lrel, rows = assert_parity(r["loss"], r["g"], r["w"], o_loss, o_g, o_w)
+    assert r["t"] == 1
+    print(f"loss {r['loss']:.6f} vs {o_loss:.6f} rel {lrel:.2e}; min cos {min(x[1] for x in rows):.6f}; "
+          f"max grad rel {max(x[2] for x in rows):.2e}; max w rel {max(x[3] for x in rows):.2e}")
+
+
+@pytest.mark.parametrize("shape", [datagen.PRESETS["tiny"], SMALL_BF16], ids=["tiny-f32", "small-bf16"])
+def test_schedules_bitwise_equal(shape):
+    need_gpu()
+    ref = run_step(shape, "streamed")
+    for mode, flags in (("serialized", 0), ("resident", 0), ("streamed", mt.MT_FLAG_POISON)):
+        r = run_step(shape, mode, flags)
+        assert r["loss"] == ref["loss"], mode
+        for key in ("g", "w", "m", "v"):
+            for k in ref[key]:
+                assert np.array_equal(r[key][k], ref[key][k]), (mode, flags, key, k)
+
+
+def test_repeated_step_is_deterministic_and_t_advances():
+    need_gpu()
+    shape = datagen.PRESETS["tiny"]
+    a = run_step(shape, steps=2)
+    b = run_step(shape, steps=2)
+    assert a["t"] == 2 and a["losses"] == b["losses"]
+    for k in a["w"]:
+        assert np.array_equal(a["w"][k], b["w"][k])
+    # two steps of the oracle with its own Adam state
+    P = datagen.init_params(shape)
+    tok = datagen.tokens(shape)
+    o = Oracle(shape, np.float32)
+    l1, _, P1, M1 = o.step(P, tok, t=1)
+    l2, g2, P2, _ = o.step(P1, tok, t=2, moments=M1)
+    assert abs(a["losses"][1] - l2) / abs(l2) < 1e-2
+    assert a["losses"][1] < a["losses"][0]
+
+
+def test_nonfinite_loss_leaves_store_untouched():
+    need_gpu()
+    shape = datagen.PRESETS["tiny"]
+    cfg, store = make_store(shape)
+    store.logical("wh", None, "w")[3, 5] = np.float32(np.nan)
+    w0 = read_all(store, "w")
+    model = mt.Model(cfg, store, "cuda:0")
+    with pytest.raises(mt.MtError) as e:
+        model.step(datagen.tokens(shape))
+    assert e.value.code == mt.MT_E_NONFINITE
+    w1 = read_all(store, "w")
+    for k in w0:
+        assert np.array_equal(w0[k], w1[k], equal_nan=True)
+    assert store.step_count() == 0
+    assert not np.any(read_all(store, "m")["wh"])
+    model.close()
+    store.free()
+
+
+def test_bad_tokens_rejected():
+    need_gpu()
+    shape = datagen.PRESETS["tiny"]
+    cfg, store = make_store(shape)
+    model = mt.Model(cfg, store, "cuda:0")
+    tok = datagen.tokens(shape).copy()
+    tok[0, 3] = shape.vocab
+    with pytest.raises(mt.MtError) as e:
+        model.step(tok)
+    assert e.value.code == mt.MT_E_INVALID
+    model.close()
+    store.free()

@@ -1,0 +1,159 @@
+"""Host-side tests of the C-ABI library (no GPU calls): symbols, store
+layout, configuration checks, and the host Adam against the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import datagen
+import host_memory_layer_amd as mt
+from oracle import adam_update
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    names = set()
+    for h in ("mt.h", "mt_kernels.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(mt_[a-z0-9_]+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    L = mt.lib()
+    names = declared_symbols()
+    assert len(names) >= 20
+    for n in sorted(names):
+        assert hasattr(L, n), n
+    assert set(mt._SIGS) == names
+
+
+def test_struct_sizes_match_header():
+    # layout of the C structs, mirrored by ctypes
+    assert ctypes.sizeof(mt.MtConfig) == 9 * 4 + 4 + 6 * 8 + 3 * 4 + 4
+    assert ctypes.sizeof(mt.MtTensorDesc) == 16
+    assert ctypes.sizeof(mt.MtBlockDesc) == 16 + 8 * 8 + 8 * 16
+
+
+@pytest.mark.parametrize("name", list(datagen.PRESETS))
+def test_store_layout(name):
+    shape = datagen.PRESETS[name]
+    cfg = mt.make_config(shape)
+    blocks = mt.block_infos(cfg)
+    total = mt.host_store_bytes(cfg)
+    wb = 2 if shape.store_dtype == "bf16" else 4
+    d, F, V, L = shape.d_model, shape.d_ff, shape.vocab, shape.n_layers
+    assert len(blocks) == L + 2
+    prev_end = 4096
+    n_params = 0
+    for i, b in enumerate(blocks):
+        assert b.kind == (mt.MT_BLOCK_EMBED if i == 0 else mt.MT_BLOCK_HEAD if i == L + 1 else mt.MT_BLOCK_LAYER)
+        for off in (b.base, b.w_off, b.g_off, b.m_off, b.v_off):
+            assert off % 4096 == 0
+        # one contiguous block per layer: W | G | m | v
+        assert b.base == prev_end == b.w_off
+        assert b.g_off == b.w_off + b.w_bytes and b.m_off == b.g_off + b.w_bytes
+        assert b.v_off == b.m_off + b.mv_bytes
+        prev_end = b.v_off + b.mv_bytes
+        assert b.w_bytes == b.region_elems * wb and b.mv_bytes == b.region_elems * 4
+        end = 0
+        for t in range(b.n_tensors):
+            tt = b.tensors[t]
+            assert (tt.offset * wb) % 4096 == 0 and tt.offset >= end
+            end = tt.offset + tt.rows * tt.cols
+            n_params += tt.rows * tt.cols
+        assert end <= b.region_elems
+    assert total == prev_end
+    assert n_params == shape.n_params()
+    b1 = blocks[1]
+    shapes = [(b1.tensors[t].rows, b1.tensors[t].cols) for t in range(b1.n_tensors)]
+    assert shapes == [(3 * d, d), (d, d), (2 * F, d), (d, F), (1, d), (1, d)]
+
+
+def test_store_sizes_of_the_14b_shape():
+    """Layer weight block 634.4 MB and 186.64 GB store at 12 bytes/param."""
+    cfg = mt.make_config(datagen.PRESETS["14b"])
+    blocks = mt.block_infos(cfg)
+    assert abs(blocks[1].w_bytes / 1e6 - 634.4) < 0.1
+    assert abs(mt.host_store_bytes(cfg) / 1e9 - 186.64) < 0.05
+
+
+def test_config_validation():
+    shape = datagen.PRESETS["tiny"]
+    bad = [shape.replace(n_heads=3), shape.replace(n_layers=0), shape.replace(vocab=1),
+           datagen.PRESETS["1.3b"].replace(head_dim=64, n_heads=32), datagen.PRESETS["1.3b"].replace(d_ff=5500)]
+    for s in bad:
+        with pytest.raises(mt.MtError):
+            mt.host_store_bytes(mt.make_config(s))
+    c = mt.make_config(shape)
+    c.mode = 7
+    with pytest.raises(mt.MtError):
+        mt.device_bytes(c)
+
+
+def test_device_bytes_fit_one_gpu():
+    for name in ("1.3b", "7b", "14b"):
+        nb = mt.device_bytes(mt.make_config(datagen.PRESETS[name]))
+        assert 0 < nb < 200e9, (name, nb)
+
+
+def test_host_adam_f32_bitwise_equals_oracle():
+    rng = np.random.default_rng(1)
+    n = 100003
+    w = rng.standard_normal(n).astype(np.float32) * 0.02
+    g = (rng.standard_normal(n) * 10.0 ** rng.uniform(-9, -1, n)).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    v = (rng.random(n) * 1e-5).astype(np.float32)
+    for t in (1, 2, 7):
+        ow, om, ov = adam_update(w, g, m, v, t, 1e-3, 0.9, 0.95, 1e-8)
+        w2, m2, v2 = w.copy(), m.copy(), v.copy()
+        mt.check(mt.lib().mt_host_adam(mt.MT_F32, w2.ctypes.data, g.ctypes.data, m2.ctypes.data, v2.ctypes.data, n,
+                                       t, 1e-3, 0.9, 0.95, 1e-8, 4))
+        assert np.array_equal(w2, ow) and np.array_equal(m2, om) and np.array_equal(v2, ov), t
+
+
+def test_host_adam_bf16_rounds_the_fp32_update():
+    """bf16 store: the fp32 update of the widened values, rounded to nearest
+    even, for every one of the 65536 bf16 weight patterns that is finite."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    wf = datagen.bf16_bits_to_f32(bits)
+    keep = np.isfinite(wf) & (np.abs(wf) < 1e30)
+    bits = bits[keep]
+    n = bits.size
+    rng = np.random.default_rng(2)
+    gbits = datagen.f32_to_bf16_bits((rng.standard_normal(n) * 1e-3).astype(np.float32))
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    w2 = bits.copy()
+    mt.check(mt.lib().mt_host_adam(mt.MT_BF16, w2.ctypes.data, gbits.ctypes.data, m.ctypes.data, v.ctypes.data, n,
+                                   1, 1e-3, 0.9, 0.95, 1e-8, 3))
+    ow, om, ov = adam_update(datagen.bf16_bits_to_f32(bits), datagen.bf16_bits_to_f32(gbits), np.zeros(n, np.float32),
+                             np.zeros(n, np.float32), 1, 1e-3, 0.9, 0.95, 1e-8)
+    assert np.array_equal(w2, datagen.f32_to_bf16_bits(ow))
+    assert np.array_equal(m, om) and np.array_equal(v, ov)
+
+
+def test_host_adam_rejects_bad_arguments():
+    assert mt.lib().mt_host_adam(5, None, None, None, None, 0, 1, 1e-3, 0.9, 0.95, 1e-8, 1) == mt.MT_E_INVALID
+    x = np.zeros(4, np.float32)
+    assert mt.lib().mt_host_adam(mt.MT_F32, x.ctypes.data, x.ctypes.data, x.ctypes.data, x.ctypes.data, 4, 0,
+                                 1e-3, 0.9, 0.95, 1e-8, 1) == mt.MT_E_INVALID
+
+
+def test_api_errors_without_device():
+    L = mt.lib()
+    assert L.mt_train_step(None, None) == mt.MT_E_INVALID
+    assert b"null" in L.mt_last_error()
+    assert L.mt_get_loss(None, None) == mt.MT_E_INVALID
+    cfg = mt.make_config(datagen.PRESETS["tiny"])
+    h = ctypes.c_void_p()
+    streams = (ctypes.c_void_p * 3)()
+    assert L.mt_create_model(ctypes.byref(cfg), None, 0, streams, ctypes.byref(h)) == mt.MT_E_INVALID
+    assert L.mt_create_model(ctypes.byref(cfg), 0x1001, 1 << 30, streams, ctypes.byref(h)) == mt.MT_E_INVALID
+    streams[1] = 1
+    assert L.mt_create_model(ctypes.byref(cfg), 0x1001, 1 << 30, streams, ctypes.byref(h)) == mt.MT_E_ALIGN
+    assert L.mt_create_model(ctypes.byref(cfg), 0x1000, 16, streams, ctypes.byref(h)) == mt.MT_E_SIZE
