@@ -1,0 +1,244 @@
+"""Benchmark of the layer-streamed training step on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 14b]
+
+Runs W untimed and K timed training steps (forward, loss, backward with
+recompute, gradient offload and host Adam: the whole step) of the selected
+decoder shape with every weight and Adam moment in the pinned host store,
+and prints one JSON line: model TFLOPS per step (model FLOPs exclude the
+recompute; attention counted over the causal half), the host-link figures,
+the GEMM roofline measured with HIP events around every GEMM launch, and
+the oracle's throughput on the host cores for a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import datagen  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def flops(shape, n_layers=None):
+    L = shape.n_layers if n_layers is None else n_layers
+    M, d, F, V, B, T = shape.tokens, shape.d_model, shape.d_ff, shape.vocab, shape.batch, shape.seq_len
+    fwd_layer = 2.0 * M * (4 * d * d + 3 * d * F) + 2.0 * B * T * T * d
+    model = 3.0 * (L * fwd_layer + 2.0 * M * d * V)
+    return fwd_layer, model, model + L * fwd_layer
+
+
+def link_probe(torch, dev, nbytes, reps=4):
+    """Pinned host <-> device copy bandwidth (GB/s): H2D, D2H, and both at once."""
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    host2 = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    devb = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    devb2 = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    s1, s2 = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+
+    def timed(fn_list):
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            for s, fn in fn_list:
+                with torch.cuda.stream(s):
+                    fn()
+        torch.cuda.synchronize(dev)
+        return time.perf_counter() - t0
+
+    h2d = lambda: devb.copy_(host, non_blocking=True)
+    d2h = lambda: host2.copy_(devb2, non_blocking=True)
+    timed([(s1, h2d)])
+    t_h2d = timed([(s1, h2d)])
+    t_d2h = timed([(s2, d2h)])
+    t_bi = timed([(s1, h2d), (s2, d2h)])
+    gb = nbytes * reps / 1e9
+    out = {"h2d_gbs": gb / t_h2d, "d2h_gbs": gb / t_d2h, "bidir_gbs": 2 * gb / t_bi, "bytes": nbytes}
+    del host, host2, devb, devb2
+    return out
+
+
+def cpu_baseline(shape, tokens_sample, seconds_hint):
+    """The oracle, as it stands, on one decoder layer of `shape` over one
+    sequence of `tokens_sample` tokens: forward, recompute, backward and Adam
+    of that layer (float32 NumPy, BLAS on every allowed core)."""
+    from oracle import Oracle, adam_update
+    sub = shape.replace(n_layers=1, batch=1, seq_len=tokens_sample)
+    P = {}
+    P["0.attn_norm"] = datagen.init_tensor(sub, "attn_norm")
+    P["0.ffn_norm"] = datagen.init_tensor(sub, "ffn_norm")
+    for nm in datagen.LAYER_TENSORS:
+        P[f"0.{nm}"] = datagen.init_tensor(sub, nm, 0)
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((tokens_sample, sub.d_model)).astype(np.float32)
+    dx = (rng.standard_normal((tokens_sample, sub.d_model)) * 1e-3).astype(np.float32)
+    o = Oracle(sub, np.float32)
+    t0 = time.perf_counter()
+    _, cache = o.layer_fwd(x, P, 0)          # forward (keeps only x^l in streamed mode)
+    _, cache = o.layer_fwd(x, P, 0)          # recompute inside the backward sweep
+    grads = {}
+    o.layer_bwd(dx, cache, P, 0, grads)
+    for k in P:
+        adam_update(P[k], grads[k], np.zeros_like(P[k]), np.zeros_like(P[k]), 1, sub.lr, sub.beta1, sub.beta2,
+                    sub.adam_eps)
+    dt = time.perf_counter() - t0
+    fwd_layer = 2.0 * tokens_sample * (4 * sub.d_model ** 2 + 3 * sub.d_model * sub.d_ff) + \
+        2.0 * tokens_sample ** 2 * sub.d_model
+    model_flops = 3.0 * fwd_layer
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count()
+    return {"value": model_flops / dt / 1e12, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
+            "sample": f"one {shape.name}-shape decoder layer (d {sub.d_model}, F {sub.d_ff}, {sub.n_heads} heads) "
+                      f"on 1 x {tokens_sample} tokens: forward + recompute + backward + Adam, float32 NumPy; "
+                      f"{dt:.1f} s",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="14b", choices=list(datagen.PRESETS))
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (same per-layer shape)")
+    ap.add_argument("--mode", default="streamed", choices=["streamed", "serialized", "resident"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; the multi-GPU path is design-only",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import host_memory_layer_amd as mt
+
+    shape = datagen.PRESETS[args.config]
+    if args.layers:
+        shape = shape.replace(n_layers=args.layers)
+    dev = torch.device("cuda:0")
+    flags = 0 if args.no_kernel_timing else mt.MT_FLAG_TIME_KERNELS
+    cfg = mt.make_config(shape, mode=args.mode, flags=flags)
+
+    t0 = time.perf_counter()
+    store = mt.HostStore(cfg)
+    log(f"pinned host store {store.nbytes / 1e9:.2f} GB in {time.perf_counter() - t0:.1f} s")
+    t0 = time.perf_counter()
+    mt.init_store_weights(store, datagen.store_filler(shape))
+    log(f"initialised weights in {time.perf_counter() - t0:.1f} s")
+    model = mt.Model(cfg, store, "cuda:0")
+    log(f"device arena {model.arena.numel() / 1e9:.2f} GB")
+    layer_bytes = store.blocks[1].w_bytes
+    link = link_probe(torch, dev, layer_bytes)
+    log(f"host link: {link}")
+    tokens = datagen.tokens(shape)
+
+    for i in range(args.warmup):
+        t0 = time.perf_counter()
+        loss = model.step(tokens)
+        log(f"warmup step {i}: loss {loss:.4f} {time.perf_counter() - t0:.2f} s")
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    gemm_ms = gemm_fl = attn_ms = attn_fl = 0.0
+    gemm_n = 0
+    st_acc = []
+    for i in range(args.steps):
+        loss = model.step(tokens)
+        st = model.stats()
+        st_acc.append(st)
+        gemm_ms += st["gemm_ms"]
+        gemm_fl += st["gemm_flops"]
+        gemm_n += st["gemm_launches"]
+        attn_ms += st["attn_ms"]
+        attn_fl += st["attn_flops"]
+        log(f"step {i}: loss {loss:.4f} step {st['step_ms']:.0f} ms device {st['device_ms']:.0f} ms "
+            f"stall {st['stall_ms']:.1f} ms adam {st['adam_ms']:.0f} ms (tail {st['adam_tail_ms']:.0f})")
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+
+    fwd_layer, model_flops, hw_flops = flops(shape)
+    value = model_flops * args.steps / elapsed / 1e12
+    last = st_acc[-1]
+    L = shape.n_layers
+    per_layer = [model.block_stats(j) for j in range(1, L + 1)]
+    mid = per_layer[1:-1] or per_layer
+    comp_f = float(np.mean([b["fwd_ms"] for b in mid]))
+    comp_b = float(np.mean([b["bwd_ms"] for b in mid]))
+    h2d_f = float(np.mean([b["h2d_fwd_ms"] for b in mid]))
+    h2d_b = float(np.mean([b["h2d_bwd_ms"] for b in mid]))
+    d2h = float(np.mean([b["d2h_ms"] for b in mid]))
+    h2d_gbs = last["h2d_bytes"] / (last["h2d_ms"] / 1e3) / 1e9 if last["h2d_ms"] > 0 else None
+    d2h_gbs = last["d2h_bytes"] / (last["d2h_ms"] / 1e3) / 1e9 if last["d2h_ms"] > 0 else None
+    bf = shape.store_dtype == "bf16"
+    roof = None
+    if gemm_ms > 0:
+        achieved = gemm_fl / (gemm_ms / 1e3) / 1e12
+        peak = PEAK_BF16_TFLOPS if bf else PEAK_F32_TFLOPS
+        roof = {"bound": "mfma" if bf else "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": None, "kernel": "k_gemm_bf16 (all launches)",
+                "launches_per_step": gemm_n / args.steps,
+                "flops_per_launch": gemm_fl / max(gemm_n, 1),
+                "avg_launch_ms": gemm_ms / max(gemm_n, 1)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("oracle CPU baseline ...")
+        cpu = cpu_baseline(shape, args.cpu_tokens, 20)
+        log(f"oracle: {cpu}")
+    out = {
+        "metric": "model TFLOPS/step on 1 MI355X (14B-shape) + H2D GB/s vs host-link peak",
+        "value": value,
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{shape.name}-shape decoder: {L} layers, d {shape.d_model}, "
+                               f"{shape.n_heads}x{shape.head_dim} heads, SwiGLU {shape.d_ff}, vocab {shape.vocab}; "
+                               f"batch {shape.batch} x seq {shape.seq_len}; {args.mode} from a pinned host store "
+                               f"({store.nbytes / 1e9:.1f} GB: bf16 W/G, fp32 Adam m/v)",
+                   "global_batch": shape.batch, "seq_len": shape.seq_len, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "detail": {
+            "model_flops_per_step": model_flops, "hw_flops_per_step": hw_flops,
+            "hw_tflops": hw_flops * args.steps / elapsed / 1e12,
+            "device_ms": last["device_ms"], "step_ms": last["step_ms"], "loss": loss,
+            "h2d_gbs_achieved": h2d_gbs, "d2h_gbs_achieved": d2h_gbs,
+            "link_peak": link,
+            "h2d_frac_of_link_peak": h2d_gbs / link["h2d_gbs"] if h2d_gbs else None,
+            "stall_ms": last["stall_ms"], "adam_ms": last["adam_ms"], "adam_tail_ms": last["adam_tail_ms"],
+            "per_layer_ms": {"fwd_compute": comp_f, "bwd_compute": comp_b, "h2d_fwd": h2d_f, "h2d_bwd": h2d_b,
+                             "d2h": d2h},
+            "attention": {"ms_per_step": attn_ms / args.steps,
+                          "tflops": attn_fl / (attn_ms / 1e3) / 1e12 if attn_ms > 0 else None},
+        },
+    }
+    model.close()
+    store.free()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

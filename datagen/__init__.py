@@ -135,8 +135,10 @@ def draw_flat(seed: int, tid: int, start: int, stop: int, store_dtype: str,
     def work(c):
         lo = max(start, c * CHUNK)
         hi = min(stop, (c + 1) * CHUNK)
-        full = _chunk_draw(seed, tid, c, min(CHUNK, (c + 1) * CHUNK) - c * CHUNK)
-        vals = full[lo - c * CHUNK: hi - c * CHUNK]
+        # a chunk's draws form one sequential stream, so drawing its first
+        # (hi - c*CHUNK) values gives the same prefix as drawing all CHUNK
+        full = _chunk_draw(seed, tid, c, hi - c * CHUNK)
+        vals = full[lo - c * CHUNK:]
         if res.dtype == np.uint16:
             res[lo - start: hi - start] = f32_to_bf16_bits(vals)
         elif store_dtype == BF16:
@@ -183,6 +185,14 @@ def init_params(cfg: ModelShape) -> dict:
     p["final_norm"] = init_tensor(cfg, "final_norm")
     p["wh"] = init_tensor(cfg, "wh")
     return p
+
+
+def store_filler(cfg: ModelShape):
+    """draw(name, layer, out, pool): write the initial value of a logical
+    weight tensor into the flat buffer ``out`` (uint16 bf16 bits or float32)."""
+    def draw(name, layer, out, pool=None):
+        draw_flat(cfg.seed, tensor_id(cfg, name, layer), 0, out.size, cfg.store_dtype, out=out, pool=pool)
+    return draw
 
 
 def tokens(cfg: ModelShape) -> np.ndarray:

@@ -8,17 +8,10 @@ import datagen
 import host_memory_layer_amd as mt
 
 
-def draw_fn(shape):
-    def draw(name, layer, out, pool):
-        tid = datagen.tensor_id(shape, name, layer)
-        datagen.draw_flat(shape.seed, tid, 0, out.size, shape.store_dtype, out=out, pool=pool)
-    return draw
-
-
 def make_store(shape, mode="streamed", flags=0, host_threads=0):
     cfg = mt.make_config(shape, mode=mode, flags=flags, host_threads=host_threads)
     store = mt.HostStore(cfg)
-    mt.init_store_weights(store, draw_fn(shape))
+    mt.init_store_weights(store, datagen.store_filler(shape))
     return cfg, store
 
 
