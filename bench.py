@@ -139,7 +139,8 @@ def main():
 
     t0 = time.perf_counter()
     store = mt.HostStore(cfg)
-    log(f"pinned host store {store.nbytes / 1e9:.2f} GB in {time.perf_counter() - t0:.1f} s")
+    log(f"host store: pinned W|G part {store.nbytes / 1e9:.2f} GB, pageable m|v part "
+        f"{store.opt_nbytes / 1e9:.2f} GB, in {time.perf_counter() - t0:.1f} s")
     t0 = time.perf_counter()
     mt.init_store_weights(store, datagen.store_filler(shape))
     log(f"initialised weights in {time.perf_counter() - t0:.1f} s")
@@ -216,8 +217,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{shape.name}-shape decoder: {L} layers, d {shape.d_model}, "
                                f"{shape.n_heads}x{shape.head_dim} heads, SwiGLU {shape.d_ff}, vocab {shape.vocab}; "
-                               f"batch {shape.batch} x seq {shape.seq_len}; {args.mode} from a pinned host store "
-                               f"({store.nbytes / 1e9:.1f} GB: bf16 W/G, fp32 Adam m/v)",
+                               f"batch {shape.batch} x seq {shape.seq_len}; {args.mode} from the host store "
+                               f"({store.nbytes / 1e9:.1f} GB pinned W/G + {store.opt_nbytes / 1e9:.1f} GB "
+                               f"Adam m/v)",
                    "global_batch": shape.batch, "seq_len": shape.seq_len, "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,

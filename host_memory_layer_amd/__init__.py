@@ -69,16 +69,21 @@ _lib = None
 
 _SIGS = {
     "mt_host_store_bytes": (ctypes.c_size_t, [ctypes.POINTER(MtConfig)]),
+    "mt_host_opt_bytes": (ctypes.c_size_t, [ctypes.POINTER(MtConfig)]),
+    "mt_alloc_host_opt": (ctypes.c_int, [ctypes.c_size_t, ctypes.POINTER(ctypes.c_void_p)]),
+    "mt_free_host_opt": (None, [ctypes.c_void_p, ctypes.c_size_t]),
     "mt_block_count": (ctypes.c_int, [ctypes.POINTER(MtConfig)]),
     "mt_block_info": (ctypes.c_int, [ctypes.POINTER(MtConfig), ctypes.c_int, ctypes.POINTER(MtBlockDesc)]),
     "mt_device_bytes": (ctypes.c_size_t, [ctypes.POINTER(MtConfig)]),
     "mt_alloc_host_store": (ctypes.c_int, [ctypes.c_size_t, ctypes.POINTER(ctypes.c_void_p)]),
     "mt_free_host_store": (None, [ctypes.c_void_p]),
-    "mt_init_store_header": (ctypes.c_int, [ctypes.POINTER(MtConfig), ctypes.c_void_p, ctypes.c_size_t]),
+    "mt_init_store_header": (ctypes.c_int, [ctypes.POINTER(MtConfig), ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_void_p, ctypes.c_size_t]),
     "mt_store_step": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]),
     "mt_create_model": (ctypes.c_int, [ctypes.POINTER(MtConfig), ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p)]),
-    "mt_bind_host_store": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]),
+    "mt_bind_host_store": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.c_size_t]),
     "mt_train_step": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
     "mt_get_loss": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]),
     "mt_get_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(MtStats)]),
@@ -156,6 +161,13 @@ def host_store_bytes(cfg: MtConfig) -> int:
     return n
 
 
+def host_opt_bytes(cfg: MtConfig) -> int:
+    n = lib().mt_host_opt_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise MtError(MT_E_INVALID, lib().mt_last_error().decode())
+    return n
+
+
 def device_bytes(cfg: MtConfig) -> int:
     n = lib().mt_device_bytes(ctypes.byref(cfg))
     if n == 0:
@@ -181,24 +193,33 @@ def _view(addr: int, nbytes: int, dtype) -> np.ndarray:
 
 
 class HostStore:
-    """Pinned host store: header page + per-block [W | G | m | v] regions."""
+    """Host store: pinned DMA part (header page + per-block [W | G]) and
+    pageable optimizer part (per-block [m | v])."""
 
     def __init__(self, cfg: MtConfig):
         self.cfg = cfg
         self.nbytes = host_store_bytes(cfg)
+        self.opt_nbytes = host_opt_bytes(cfg)
         p = ctypes.c_void_p()
         check(lib().mt_alloc_host_store(self.nbytes, ctypes.byref(p)))
         self.ptr = p.value
-        check(lib().mt_init_store_header(ctypes.byref(cfg), self.ptr, self.nbytes))
+        q = ctypes.c_void_p()
+        rc = lib().mt_alloc_host_opt(self.opt_nbytes, ctypes.byref(q))
+        if rc != MT_OK:
+            lib().mt_free_host_store(self.ptr)
+            check(rc)
+        self.opt_ptr = q.value
+        check(lib().mt_init_store_header(ctypes.byref(cfg), self.ptr, self.nbytes, self.opt_ptr, self.opt_nbytes))
         self.blocks = block_infos(cfg)
         self.wdtype = np.uint16 if cfg.store_dtype == MT_BF16 else np.float32
 
     def region(self, block: int, which: str) -> np.ndarray:
         b = self.blocks[block]
+        base = self.ptr if which in "wg" else self.opt_ptr
         off = {"w": b.w_off, "g": b.g_off, "m": b.m_off, "v": b.v_off}[which]
         dt = self.wdtype if which in "wg" else np.float32
         n = b.region_elems
-        return _view(self.ptr + off, n * np.dtype(dt).itemsize, dt)
+        return _view(base + off, n * np.dtype(dt).itemsize, dt)
 
     def tensor(self, block: int, index: int, which: str = "w") -> np.ndarray:
         b = self.blocks[block]
@@ -211,16 +232,13 @@ class HostStore:
         check(lib().mt_store_step(self.ptr, ctypes.byref(t)))
         return t.value
 
-    def zero_state(self):
-        """Zero every G, m and v region (W untouched)."""
-        for i in range(len(self.blocks)):
-            for w in "gmv":
-                self.region(i, w)[:] = 0
-
     def free(self):
         if self.ptr:
             lib().mt_free_host_store(self.ptr)
             self.ptr = None
+        if self.opt_ptr:
+            lib().mt_free_host_opt(self.opt_ptr, self.opt_nbytes)
+            self.opt_ptr = None
 
     # Logical tensors of the decoder inside the store (weights are [out x in]).
     def logical(self, name: str, layer: int | None = None, which: str = "w") -> np.ndarray:
@@ -275,7 +293,7 @@ class Model:
         torch.cuda.synchronize(self.device)
         check(lib().mt_create_model(ctypes.byref(cfg), self.arena.data_ptr(), nbytes, handles, ctypes.byref(h)))
         self.handle = h.value
-        check(lib().mt_bind_host_store(self.handle, store.ptr, store.nbytes))
+        check(lib().mt_bind_host_store(self.handle, store.ptr, store.nbytes, store.opt_ptr, store.opt_nbytes))
 
     def step(self, tokens: np.ndarray) -> float:
         tok = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)

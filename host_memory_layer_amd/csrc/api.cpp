@@ -1,6 +1,7 @@
 // extern "C" entry points of include/mt.h: argument checks and translation
 // of internal errors into MT_E_* codes; no exception crosses the ABI.
 #include <sched.h>
+#include <sys/mman.h>
 
 #include <algorithm>
 #include <new>
@@ -49,6 +50,17 @@ size_t mt_host_store_bytes(const mt_config* cfg) {
   uint64_t total = 0;
   store_layout(*cfg, &total);
   return total;
+}
+
+size_t mt_host_opt_bytes(const mt_config* cfg) {
+  std::string why;
+  if (!cfg || validate_config(*cfg, &why) != MT_OK) {
+    set_error(cfg ? why : "null config");
+    return 0;
+  }
+  uint64_t total = 0, opt = 0;
+  store_layout(*cfg, &total, &opt);
+  return opt;
 }
 
 int mt_block_count(const mt_config* cfg) {
@@ -105,15 +117,33 @@ void mt_free_host_store(void* p) {
   if (p) hipHostFree(p);
 }
 
-int mt_init_store_header(const mt_config* cfg, void* host_base, size_t bytes) {
+int mt_alloc_host_opt(size_t bytes, void** out) {
+  return guarded([&] {
+    if (!out || bytes == 0) throw ApiError{MT_E_INVALID, "null out or zero size"};
+    const size_t n = round_up(bytes, kStoreAlign);
+    void* p = mmap(nullptr, n, PROT_READ | PROT_WRITE, MAP_PRIVATE | MAP_ANONYMOUS | MAP_NORESERVE, -1, 0);
+    if (p == MAP_FAILED) throw ApiError{MT_E_OOM, "mmap of the optimizer part failed"};
+    madvise(p, n, MADV_HUGEPAGE);
+    *out = p;
+    return MT_OK;
+  });
+}
+
+void mt_free_host_opt(void* p, size_t bytes) {
+  if (p) munmap(p, round_up(bytes, kStoreAlign));
+}
+
+int mt_init_store_header(const mt_config* cfg, void* host_base, size_t bytes, void* opt_base, size_t opt_bytes) {
   return guarded([&] {
     std::string why;
-    if (!cfg || !host_base) throw ApiError{MT_E_INVALID, "null argument"};
+    if (!cfg || !host_base || !opt_base) throw ApiError{MT_E_INVALID, "null argument"};
     if (validate_config(*cfg, &why) != MT_OK) throw ApiError{MT_E_INVALID, why};
-    if ((uintptr_t)host_base % kStoreAlign) throw ApiError{MT_E_ALIGN, "store not 4 KiB aligned"};
-    uint64_t total = 0;
-    store_layout(*cfg, &total);
-    if (bytes < total) throw ApiError{MT_E_SIZE, "store smaller than mt_host_store_bytes"};
+    if ((uintptr_t)host_base % kStoreAlign || (uintptr_t)opt_base % kStoreAlign)
+      throw ApiError{MT_E_ALIGN, "store parts not 4 KiB aligned"};
+    uint64_t total = 0, opt = 0;
+    store_layout(*cfg, &total, &opt);
+    if (bytes < total) throw ApiError{MT_E_SIZE, "DMA part smaller than mt_host_store_bytes"};
+    if (opt_bytes < opt) throw ApiError{MT_E_SIZE, "optimizer part smaller than mt_host_opt_bytes"};
     StoreHeader h{};
     h.magic = kStoreMagic;
     h.version = kStoreVersion;
@@ -131,9 +161,15 @@ int mt_init_store_header(const mt_config* cfg, void* host_base, size_t bytes) {
     ThreadPool pool(std::max(1, threads));
     const uint64_t chunk = 64ull << 20;
     const uint64_t body = total - kHeaderBytes;
-    pool.run((int64_t)((body + chunk - 1) / chunk), [&](int64_t i) {
-      const uint64_t lo = kHeaderBytes + (uint64_t)i * chunk;
-      memset((uint8_t*)host_base + lo, 0, std::min(chunk, total - lo));
+    const int64_t n1 = (int64_t)((body + chunk - 1) / chunk), n2 = (int64_t)((opt + chunk - 1) / chunk);
+    pool.run(n1 + n2, [&](int64_t i) {
+      if (i < n1) {
+        const uint64_t lo = kHeaderBytes + (uint64_t)i * chunk;
+        memset((uint8_t*)host_base + lo, 0, std::min(chunk, total - lo));
+      } else {
+        const uint64_t lo = (uint64_t)(i - n1) * chunk;
+        memset((uint8_t*)opt_base + lo, 0, std::min(chunk, opt - lo));
+      }
     });
     return MT_OK;
   });
@@ -157,10 +193,10 @@ int mt_create_model(const mt_config* cfg, void* dev_arena, size_t arena_bytes, v
   });
 }
 
-int mt_bind_host_store(void* model, void* host_base, size_t bytes) {
+int mt_bind_host_store(void* model, void* host_base, size_t bytes, void* opt_base, size_t opt_bytes) {
   return guarded([&] {
     if (!model) throw ApiError{MT_E_INVALID, "null model"};
-    return bind_store((Model*)model, host_base, bytes);
+    return bind_store((Model*)model, host_base, bytes, opt_base, opt_bytes);
   });
 }
 

@@ -9,7 +9,7 @@ struct Model;
 Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void* const streams[3]);
 void destroy_model(Model* m);
 uint64_t device_bytes_for(const mt_config& cfg);
-int bind_store(Model* m, void* host, size_t bytes);
+int bind_store(Model* m, void* host, size_t bytes, void* opt, size_t opt_bytes);
 int model_step(Model* m, const int32_t* tokens);
 int model_loss(const Model* m, float* out);
 int model_stats(const Model* m, mt_stats* out);

@@ -94,14 +94,15 @@ static LayerW<T> bind_layer(uint8_t* region, const mt_block_desc& b) {
 struct Model {
   mt_config cfg;
   std::vector<mt_block_desc> blocks;
-  uint64_t store_bytes = 0, slot_bytes = 0;
+  uint64_t store_bytes = 0, opt_bytes = 0, slot_bytes = 0;
   int L, d, H, hd, F, V, B, Tq, M;
   int E;  // bytes per weight element
 
   uint8_t* arena = nullptr;
   size_t arena_bytes = 0;
   hipStream_t sp, sc, so;
-  uint8_t* host = nullptr;
+  uint8_t* host = nullptr;  // DMA part: header, [W | G] per block (pinned)
+  uint8_t* hopt = nullptr;  // optimizer part: [m | v] per block
 
   // device
   uint8_t *wslot[2], *gslot[2], *wt;
@@ -244,7 +245,7 @@ struct Model {
 
   void init_dims(const mt_config& c) {
     cfg = c;
-    blocks = store_layout(c, &store_bytes);
+    blocks = store_layout(c, &store_bytes, &opt_bytes);
     slot_bytes = 0;
     for (auto& b : blocks) slot_bytes = std::max<uint64_t>(slot_bytes, b.w_bytes);
     L = c.n_layers;
@@ -470,8 +471,8 @@ void Model::adam_worker(int64_t t, double* adam_total, double* adam_tail, std::a
       if (nonfinite) continue;
       auto t0 = std::chrono::steady_clock::now();
       const mt_block_desc& b = blocks[blk];
-      adam_parallel(*pool, cfg.store_dtype, host + b.w_off, host + b.g_off, (float*)(host + b.m_off),
-                    (float*)(host + b.v_off), b.region_elems, k);
+      adam_parallel(*pool, cfg.store_dtype, host + b.w_off, host + b.g_off, (float*)(hopt + b.m_off),
+                    (float*)(hopt + b.v_off), b.region_elems, k);
       double ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
       *adam_total += ms;
       bstats[blk].adam_ms = ms;
@@ -862,10 +863,12 @@ uint64_t device_bytes_for(const mt_config& cfg) {
   return m.device_bytes();
 }
 
-int bind_store(Model* m, void* host, size_t bytes) {
-  if (!host) throw ApiError{MT_E_INVALID, "null store"};
-  if ((uintptr_t)host % kStoreAlign) throw ApiError{MT_E_ALIGN, "host store must be 4 KiB aligned"};
-  if (bytes < m->store_bytes) throw ApiError{MT_E_SIZE, "host store smaller than mt_host_store_bytes"};
+int bind_store(Model* m, void* host, size_t bytes, void* opt, size_t opt_bytes) {
+  if (!host || !opt) throw ApiError{MT_E_INVALID, "null store part"};
+  if ((uintptr_t)host % kStoreAlign || (uintptr_t)opt % kStoreAlign)
+    throw ApiError{MT_E_ALIGN, "host store parts must be 4 KiB aligned"};
+  if (bytes < m->store_bytes) throw ApiError{MT_E_SIZE, "DMA part smaller than mt_host_store_bytes"};
+  if (opt_bytes < m->opt_bytes) throw ApiError{MT_E_SIZE, "optimizer part smaller than mt_host_opt_bytes"};
   const StoreHeader* h = (const StoreHeader*)host;
   if (h->magic != kStoreMagic || h->version != kStoreVersion) throw ApiError{MT_E_INVALID, "store header magic/version"};
   const mt_config& a = h->cfg;
@@ -876,9 +879,10 @@ int bind_store(Model* m, void* host, size_t bytes) {
   unsigned int flags = 0;
   if (hipHostGetFlags(&flags, host) != hipSuccess) {
     (void)hipGetLastError();
-    throw ApiError{MT_E_INVALID, "host store is not pinned (use mt_alloc_host_store)"};
+    throw ApiError{MT_E_INVALID, "DMA part of the host store is not pinned (use mt_alloc_host_store)"};
   }
   m->host = (uint8_t*)host;
+  m->hopt = (uint8_t*)opt;
   return MT_OK;
 }
 

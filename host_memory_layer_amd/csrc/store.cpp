@@ -38,11 +38,11 @@ static void add_tensor(mt_block_desc& b, uint64_t& cursor, int rows, int cols) {
   cursor = round_up(cursor + (uint64_t)rows * cols, kTensorAlignElems);
 }
 
-std::vector<mt_block_desc> store_layout(const mt_config& c, uint64_t* total_bytes) {
+std::vector<mt_block_desc> store_layout(const mt_config& c, uint64_t* dma_bytes, uint64_t* opt_bytes) {
   const uint64_t d = c.d_model, F = c.d_ff, V = c.vocab;
   const uint64_t wb = wbytes(c);
   std::vector<mt_block_desc> blocks(c.n_layers + 2);
-  uint64_t pos = kHeaderBytes;
+  uint64_t pos = kHeaderBytes, opos = 0;
   for (int i = 0; i < c.n_layers + 2; ++i) {
     mt_block_desc& b = blocks[i];
     memset(&b, 0, sizeof(b));
@@ -72,11 +72,13 @@ std::vector<mt_block_desc> store_layout(const mt_config& c, uint64_t* total_byte
     b.base = pos;
     b.w_off = pos;
     b.g_off = b.w_off + b.w_bytes;
-    b.m_off = b.g_off + b.w_bytes;
+    pos = b.g_off + b.w_bytes;
+    b.m_off = opos;
     b.v_off = b.m_off + b.mv_bytes;
-    pos = b.v_off + b.mv_bytes;
+    opos = b.v_off + b.mv_bytes;
   }
-  *total_bytes = pos;
+  *dma_bytes = pos;
+  if (opt_bytes) *opt_bytes = opos;
   return blocks;
 }
 

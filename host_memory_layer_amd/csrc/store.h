@@ -1,10 +1,12 @@
 // Layout of the host layer store and of the device arena.
 //
 // Host store (MegaTrain, radar.chestersoft.de "Methodik", layer-contiguous
-// tiling): a 4 KiB header page, then one block per embed / layer / head, each
-// block holding its weights, gradients and both Adam moments contiguously,
-// every region and tensor start 4 KiB-aligned so one DMA burst moves a
-// block's weights or gradients.
+// tiling): one block per embed / layer / head holding the block's weights,
+// gradients and both Adam moments, every region and tensor start 4 KiB-aligned
+// so one DMA burst moves a block's weights or gradients.  The weights and
+// gradients of all blocks sit in the pinned DMA part (after a 4 KiB header
+// page); the moments, which never leave the host, sit in a pageable
+// optimizer part with the same per-block order.
 #pragma once
 
 #include <vector>
@@ -34,6 +36,6 @@ enum { T_WH = 0, T_FINAL = 1 };
 
 int validate_config(const mt_config& c, std::string* why);
 inline int wbytes(const mt_config& c) { return c.store_dtype == MT_BF16 ? 2 : 4; }
-std::vector<mt_block_desc> store_layout(const mt_config& c, uint64_t* total_bytes);
+std::vector<mt_block_desc> store_layout(const mt_config& c, uint64_t* dma_bytes, uint64_t* opt_bytes = nullptr);
 
 }  // namespace mt

@@ -79,10 +79,17 @@ typedef struct mt_tensor_desc {
   int32_t rows, cols;
 } mt_tensor_desc;
 
-/* One block of the host store: [W | G | m | v], each region 4 KiB-aligned.
- * All offsets are bytes from the start of the store.  Region element counts
- * are equal for the four regions; W and G hold wb-byte elements (2 for
- * bf16, 4 for f32), m and v hold float32.
+/* One block of the host store.  The store has two parts:
+ *   - the DMA part (pinned, hipHostMalloc): a 4 KiB header page, then per
+ *     block [W | G] — the only state that crosses the host link, one burst
+ *     per region;
+ *   - the optimizer part (pageable host memory): per block [m | v], read and
+ *     written only by the host Adam.
+ * Every region and tensor start is 4 KiB-aligned and each block's regions
+ * are contiguous inside their part.  base, w_off, g_off are byte offsets in
+ * the DMA part; m_off, v_off byte offsets in the optimizer part.  Region
+ * element counts are equal for the four regions; W and G hold wb-byte
+ * elements (2 for bf16, 4 for f32), m and v hold float32.
  * Tensor order — embed: E [V x d]; layer: Wqkv [3d x d] (q, k, v rows),
  * Wo [d x d], Wgu [2F x d] (gate rows then up rows), Wd [d x F],
  * attn_norm [1 x d], ffn_norm [1 x d]; head: Wh [V x d], final_norm [1 x d]. */
@@ -120,8 +127,10 @@ typedef struct mt_block_stats {
 } mt_block_stats;
 
 /* ------------------------------------------------------------ layout ----- */
-/* Bytes of the host store for cfg (header page + every block). */
+/* Bytes of the DMA part of the host store (header page + [W | G] of every block). */
 size_t mt_host_store_bytes(const mt_config* cfg);
+/* Bytes of the optimizer part of the host store ([m | v] of every block). */
+size_t mt_host_opt_bytes(const mt_config* cfg);
 /* Number of blocks: embed, n_layers layers, head. */
 int mt_block_count(const mt_config* cfg);
 /* Layout of block i (0 = embed, 1..L = layers, L+1 = head). */
@@ -129,16 +138,21 @@ int mt_block_info(const mt_config* cfg, int block, mt_block_desc* out);
 /* Bytes of the device arena the caller must allocate for cfg. */
 size_t mt_device_bytes(const mt_config* cfg);
 
-/* Pinned host store: hipHostMalloc of `bytes` (rounded up to 4 KiB);
- * *out receives the host address.  Free with mt_free_host_store. */
+/* DMA part: pinned host memory (hipHostMalloc) of `bytes` rounded up to
+ * 4 KiB; *out receives the host address.  Free with mt_free_host_store. */
 int mt_alloc_host_store(size_t bytes, void** out);
 void mt_free_host_store(void* p);
-/* Write the 4 KiB header page (magic, version, config, Adam step 0) and
- * zero every block (W, G, m, v and the padding between tensors), using the
- * host threads of cfg (host_threads, 0 = all allowed cores). */
-int mt_init_store_header(const mt_config* cfg, void* host_base, size_t bytes);
+/* Optimizer part: anonymous pageable memory (4 KiB-aligned, transparent huge
+ * pages requested).  Free with mt_free_host_opt and the same byte count. */
+int mt_alloc_host_opt(size_t bytes, void** out);
+void mt_free_host_opt(void* p, size_t bytes);
+/* Write the 4 KiB header page (magic, version, config, Adam step 0) at the
+ * start of the DMA part and zero both parts (W, G, m, v and the padding
+ * between tensors), using the host threads of cfg (host_threads, 0 = all
+ * allowed cores). */
+int mt_init_store_header(const mt_config* cfg, void* dma_base, size_t dma_bytes, void* opt_base, size_t opt_bytes);
 /* Adam step counter t stored in the header (number of completed steps). */
-int mt_store_step(const void* host_base, int64_t* t);
+int mt_store_step(const void* dma_base, int64_t* t);
 
 /* ------------------------------------------------------------- model ----- */
 /* Create a model.  dev_arena: device memory of at least mt_device_bytes(cfg),
@@ -148,10 +162,12 @@ int mt_store_step(const void* host_base, int64_t* t);
  * table; *out receives the handle. */
 int mt_create_model(const mt_config* cfg, void* dev_arena, size_t arena_bytes,
                     void* const streams[3], void** out);
-/* Bind a host store (from mt_alloc_host_store, header written, weights
- * initialised).  Checked: size >= mt_host_store_bytes, 4 KiB alignment,
- * header magic and config; the store must be pinned. */
-int mt_bind_host_store(void* model, void* host_base, size_t bytes);
+/* Bind a host store (DMA part from mt_alloc_host_store, optimizer part from
+ * mt_alloc_host_opt or any 4 KiB-aligned host memory; header written,
+ * weights initialised).  Checked: sizes >= mt_host_store_bytes and
+ * mt_host_opt_bytes, 4 KiB alignment, header magic and shape; the DMA part
+ * must be pinned. */
+int mt_bind_host_store(void* model, void* dma_base, size_t dma_bytes, void* opt_base, size_t opt_bytes);
 /* One training step on tokens (host int32 [batch*seq_len], values in
  * [0, vocab)).  Synchronous: on return 0 the store holds the post-Adam W, m,
  * v, this step's G, and t+1 in the header.  On MT_E_NONFINITE no Adam ran. */

@@ -45,20 +45,23 @@ def test_store_layout(name):
     cfg = mt.make_config(shape)
     blocks = mt.block_infos(cfg)
     total = mt.host_store_bytes(cfg)
+    opt_total = mt.host_opt_bytes(cfg)
     wb = 2 if shape.store_dtype == "bf16" else 4
     d, F, V, L = shape.d_model, shape.d_ff, shape.vocab, shape.n_layers
     assert len(blocks) == L + 2
     prev_end = 4096
+    prev_opt = 0
     n_params = 0
     for i, b in enumerate(blocks):
         assert b.kind == (mt.MT_BLOCK_EMBED if i == 0 else mt.MT_BLOCK_HEAD if i == L + 1 else mt.MT_BLOCK_LAYER)
         for off in (b.base, b.w_off, b.g_off, b.m_off, b.v_off):
             assert off % 4096 == 0
-        # one contiguous block per layer: W | G | m | v
+        # per block: W | G contiguous in the DMA part, m | v contiguous in the optimizer part
         assert b.base == prev_end == b.w_off
-        assert b.g_off == b.w_off + b.w_bytes and b.m_off == b.g_off + b.w_bytes
-        assert b.v_off == b.m_off + b.mv_bytes
-        prev_end = b.v_off + b.mv_bytes
+        assert b.g_off == b.w_off + b.w_bytes
+        assert b.m_off == prev_opt and b.v_off == b.m_off + b.mv_bytes
+        prev_end = b.g_off + b.w_bytes
+        prev_opt = b.v_off + b.mv_bytes
         assert b.w_bytes == b.region_elems * wb and b.mv_bytes == b.region_elems * 4
         end = 0
         for t in range(b.n_tensors):
@@ -67,7 +70,7 @@ def test_store_layout(name):
             end = tt.offset + tt.rows * tt.cols
             n_params += tt.rows * tt.cols
         assert end <= b.region_elems
-    assert total == prev_end
+    assert total == prev_end and opt_total == prev_opt
     assert n_params == shape.n_params()
     b1 = blocks[1]
     shapes = [(b1.tensors[t].rows, b1.tensors[t].cols) for t in range(b1.n_tensors)]
@@ -75,11 +78,14 @@ def test_store_layout(name):
 
 
 def test_store_sizes_of_the_14b_shape():
-    """Layer weight block 634.4 MB and 186.64 GB store at 12 bytes/param."""
+    """Layer weight block 634.4 MB and 186.64 GB store at 12 bytes/param,
+    of which 4 bytes/param (W and G) are pinned."""
     cfg = mt.make_config(datagen.PRESETS["14b"])
     blocks = mt.block_infos(cfg)
     assert abs(blocks[1].w_bytes / 1e6 - 634.4) < 0.1
-    assert abs(mt.host_store_bytes(cfg) / 1e9 - 186.64) < 0.05
+    dma, opt = mt.host_store_bytes(cfg), mt.host_opt_bytes(cfg)
+    assert abs((dma + opt) / 1e9 - 186.64) < 0.05
+    assert abs(dma / (dma + opt) - 1 / 3) < 1e-3
 
 
 def test_config_validation():
