@@ -78,8 +78,8 @@ __device__ inline bf16x8_t acc_to_frag(const f32x16_t& a, int ks) {
 
 // ------------------------------------------------------------ forward ----
 __global__ void __launch_bounds__(256) k_attn_fwd_bf16(const uint16_t* __restrict__ qkv,
-                                                     const uint16_t* __restrict__ qkvT, uint16_t* __restrict__ o,
-                                                     float* __restrict__ lse, int T, int H, int M) {
+                                                     const uint16_t* __restrict__ qkvT, int64_t ldT,
+                                                     uint16_t* __restrict__ o, float* __restrict__ lse, int T, int H) {
   constexpr int HD = 128;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 32768];
   const int nqb = (T + 127) / 128;
@@ -110,7 +110,7 @@ __global__ void __launch_bounds__(256) k_attn_fwd_bf16(const uint16_t* __restric
       const int kr = id >> 4, kc = id & 15;
       rk[i] = *(const u32x4_t*)(qkv + (rowbase + key0 + kr) * ld + d + h * HD + 8 * kc);
       const int vr = id >> 3, vc = id & 7;
-      rv[i] = *(const u32x4_t*)(qkvT + (int64_t)(2 * d + h * HD + vr) * M + rowbase + key0 + 8 * vc);
+      rv[i] = *(const u32x4_t*)(qkvT + (int64_t)(2 * d + h * HD + vr) * ldT + rowbase + key0 + 8 * vc);
     }
   };
   auto sstore = [&](int buf) {
@@ -245,7 +245,7 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
                                                       const uint16_t* __restrict__ dO,
                                                       const uint16_t* __restrict__ dOT, const float* __restrict__ lse,
                                                       const float* __restrict__ Dsum, uint16_t* __restrict__ dqkvT,
-                                                      int T, int H, int M) {
+                                                      int64_t ldT, int T, int H) {
   constexpr int HD = 128;
   // K, V: [128 keys][128 hd]; per query tile: Q, dO [64][128]; Q^T, dO^T [128][64]; lse, D [64].
   __shared__ __attribute__((aligned(16))) uint8_t smem[32768 * 2 + 16384 * 4 + 512];
@@ -302,8 +302,9 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
       *(u32x4_t*)(dOs + sw256(r, ch)) = *(const u32x4_t*)(dO + (rowbase + qs0 + r) * d + h * HD + 8 * ch);
       const int tr = id >> 3, tc = id & 7;
       *(u32x4_t*)(QTs + sw128(tr, tc)) =
-          *(const u32x4_t*)(qkvT + (int64_t)(h * HD + tr) * M + rowbase + qs0 + 8 * tc);
-      *(u32x4_t*)(dOTs + sw128(tr, tc)) = *(const u32x4_t*)(dOT + (int64_t)(h * HD + tr) * M + rowbase + qs0 + 8 * tc);
+          *(const u32x4_t*)(qkvT + (int64_t)(h * HD + tr) * ldT + rowbase + qs0 + 8 * tc);
+      *(u32x4_t*)(dOTs + sw128(tr, tc)) =
+          *(const u32x4_t*)(dOT + (int64_t)(h * HD + tr) * ldT + rowbase + qs0 + 8 * tc);
     }
     if (tid < 64) {
       lse_s[tid] = lse[(int64_t)bh * T + qs0 + tid];
@@ -355,8 +356,8 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int hi = 32 * ht + acc_row(r, lane);
-      dqkvT[(int64_t)(d + h * HD + hi) * M + rowbase + key] = f32_to_bf16(acc_dk[ht][r] * scale);
-      dqkvT[(int64_t)(2 * d + h * HD + hi) * M + rowbase + key] = f32_to_bf16(acc_dv[ht][r]);
+      dqkvT[(int64_t)(d + h * HD + hi) * ldT + rowbase + key] = f32_to_bf16(acc_dk[ht][r] * scale);
+      dqkvT[(int64_t)(2 * d + h * HD + hi) * ldT + rowbase + key] = f32_to_bf16(acc_dv[ht][r]);
     }
 }
 
@@ -364,7 +365,7 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
 __global__ void __launch_bounds__(256) k_attn_dq_bf16(const uint16_t* __restrict__ qkv,
                                                     const uint16_t* __restrict__ qkvT, const uint16_t* __restrict__ dO,
                                                     const float* __restrict__ lse, const float* __restrict__ Dsum,
-                                                    uint16_t* __restrict__ dqkvT, int T, int H, int M) {
+                                                    uint16_t* __restrict__ dqkvT, int64_t ldT, int T, int H) {
   constexpr int HD = 128;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 49152];  // K, V [64][128], K^T [128][64]
   const int nqb = (T + 127) / 128;
@@ -405,7 +406,7 @@ __global__ void __launch_bounds__(256) k_attn_dq_bf16(const uint16_t* __restrict
       rk[i] = *(const u32x4_t*)(qkv + (rowbase + key0 + r) * ld + d + h * HD + 8 * ch);
       rv[i] = *(const u32x4_t*)(qkv + (rowbase + key0 + r) * ld + 2 * d + h * HD + 8 * ch);
       const int tr = id >> 3, tc = id & 7;
-      rt[i] = *(const u32x4_t*)(qkvT + (int64_t)(d + h * HD + tr) * M + rowbase + key0 + 8 * tc);
+      rt[i] = *(const u32x4_t*)(qkvT + (int64_t)(d + h * HD + tr) * ldT + rowbase + key0 + 8 * tc);
     }
   };
   auto sstore = [&](int buf) {
@@ -474,7 +475,7 @@ __global__ void __launch_bounds__(256) k_attn_dq_bf16(const uint16_t* __restrict
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int hi = 32 * ht + acc_row(r, lane);
-      dqkvT[(int64_t)(h * HD + hi) * M + rowbase + tq] = f32_to_bf16(acc_dq[ht][r] * scale);
+      dqkvT[(int64_t)(h * HD + hi) * ldT + rowbase + tq] = f32_to_bf16(acc_dq[ht][r] * scale);
     }
 }
 
@@ -519,7 +520,7 @@ __global__ void __launch_bounds__(64) k_attn_fwd_f32(const float* qkv, float* o,
 }
 
 __global__ void __launch_bounds__(64) k_attn_dq_f32(const float* qkv, const float* dO, const float* lse,
-                                                   const float* Dsum, float* dqkvT, int T, int H, int hd, int M) {
+                                                   const float* Dsum, float* dqkvT, int64_t ldT, int T, int H, int hd) {
   const int t = blockIdx.x * 64 + threadIdx.x;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   if (t >= T) return;
@@ -551,11 +552,12 @@ __global__ void __launch_bounds__(64) k_attn_dq_f32(const float* qkv, const floa
   }
 #pragma unroll
   for (int i = 0; i < kMaxHd; ++i)
-    if (i < hd) dqkvT[(int64_t)(h * hd + i) * M + rowbase + t] = acc[i] * scale;
+    if (i < hd) dqkvT[(int64_t)(h * hd + i) * ldT + rowbase + t] = acc[i] * scale;
 }
 
 __global__ void __launch_bounds__(64) k_attn_dkdv_f32(const float* qkv, const float* dO, const float* lse,
-                                                     const float* Dsum, float* dqkvT, int T, int H, int hd, int M) {
+                                                     const float* Dsum, float* dqkvT, int64_t ldT, int T, int H,
+                                                     int hd) {
   const int u = blockIdx.x * 64 + threadIdx.x;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   if (u >= T) return;
@@ -590,23 +592,23 @@ __global__ void __launch_bounds__(64) k_attn_dkdv_f32(const float* qkv, const fl
 #pragma unroll
   for (int i = 0; i < kMaxHd; ++i)
     if (i < hd) {
-      dqkvT[(int64_t)(d + h * hd + i) * M + rowbase + u] = dk[i] * scale;
-      dqkvT[(int64_t)(2 * d + h * hd + i) * M + rowbase + u] = dv[i];
+      dqkvT[(int64_t)(d + h * hd + i) * ldT + rowbase + u] = dk[i] * scale;
+      dqkvT[(int64_t)(2 * d + h * hd + i) * ldT + rowbase + u] = dv[i];
     }
 }
 
 }  // namespace
 
 template <>
-void attn_fwd<uint16_t>(const uint16_t* qkv, const uint16_t* qkvT, uint16_t* o, float* lse, int B, int T_, int H,
-                        int hd, hipStream_t s) {
+void attn_fwd<uint16_t>(const uint16_t* qkv, const uint16_t* qkvT, int64_t ldT, uint16_t* o, float* lse, int B,
+                        int T_, int H, int hd, hipStream_t s) {
   if (hd != 128 || T_ % 64) throw ApiError{MT_E_INVALID, "bf16 attention needs head_dim 128, seq_len % 64 == 0"};
-  const int M = B * T_;
-  hipLaunchKernelGGL(k_attn_fwd_bf16, dim3((T_ + 127) / 128, B * H), dim3(256), 0, s, qkv, qkvT, o, lse, T_, H, M);
+  if (ldT < (int64_t)B * T_ || ldT % 8) throw ApiError{MT_E_INVALID, "ldT must be >= batch*seq_len, multiple of 8"};
+  hipLaunchKernelGGL(k_attn_fwd_bf16, dim3((T_ + 127) / 128, B * H), dim3(256), 0, s, qkv, qkvT, ldT, o, lse, T_, H);
 }
 
 template <>
-void attn_fwd<float>(const float* qkv, const float*, float* o, float* lse, int B, int T_, int H, int hd,
+void attn_fwd<float>(const float* qkv, const float*, int64_t, float* o, float* lse, int B, int T_, int H, int hd,
                      hipStream_t s) {
   if (hd > kMaxHd) throw ApiError{MT_E_INVALID, "fp32 attention needs head_dim <= 64"};
   hipLaunchKernelGGL(k_attn_fwd_f32, dim3((T_ + 63) / 64, B * H), dim3(64), 0, s, qkv, o, lse, T_, H, hd);
@@ -623,25 +625,25 @@ template void attn_bwd_dsum<uint16_t>(const uint16_t*, const uint16_t*, float*, 
 
 template <>
 void attn_bwd<uint16_t>(const uint16_t* qkv, const uint16_t* qkvT, const uint16_t* dO, const uint16_t* dOT,
-                        const float* lse, const float* Dsum, uint16_t* dqkvT, int B, int T_, int H, int hd,
-                        hipStream_t s) {
+                        int64_t ldT, const float* lse, const float* Dsum, uint16_t* dqkvT, int B, int T_, int H,
+                        int hd, hipStream_t s) {
   if (hd != 128 || T_ % 64) throw ApiError{MT_E_INVALID, "bf16 attention needs head_dim 128, seq_len % 64 == 0"};
-  const int M = B * T_;
+  if (ldT < (int64_t)B * T_ || ldT % 8) throw ApiError{MT_E_INVALID, "ldT must be >= batch*seq_len, multiple of 8"};
   hipLaunchKernelGGL(k_attn_dkdv_bf16, dim3((T_ + 127) / 128, B * H), dim3(256), 0, s, qkv, qkvT, dO, dOT, lse, Dsum,
-                     dqkvT, T_, H, M);
+                     dqkvT, ldT, T_, H);
   hipLaunchKernelGGL(k_attn_dq_bf16, dim3((T_ + 127) / 128, B * H), dim3(256), 0, s, qkv, qkvT, dO, lse, Dsum, dqkvT,
-                     T_, H, M);
+                     ldT, T_, H);
 }
 
 template <>
-void attn_bwd<float>(const float* qkv, const float*, const float* dO, const float*, const float* lse,
+void attn_bwd<float>(const float* qkv, const float*, const float* dO, const float*, int64_t ldT, const float* lse,
                      const float* Dsum, float* dqkvT, int B, int T_, int H, int hd, hipStream_t s) {
   if (hd > kMaxHd) throw ApiError{MT_E_INVALID, "fp32 attention needs head_dim <= 64"};
-  const int M = B * T_;
-  hipLaunchKernelGGL(k_attn_dkdv_f32, dim3((T_ + 63) / 64, B * H), dim3(64), 0, s, qkv, dO, lse, Dsum, dqkvT, T_, H,
-                     hd, M);
-  hipLaunchKernelGGL(k_attn_dq_f32, dim3((T_ + 63) / 64, B * H), dim3(64), 0, s, qkv, dO, lse, Dsum, dqkvT, T_, H, hd,
-                     M);
+  if (ldT < (int64_t)B * T_) throw ApiError{MT_E_INVALID, "ldT must be >= batch*seq_len"};
+  hipLaunchKernelGGL(k_attn_dkdv_f32, dim3((T_ + 63) / 64, B * H), dim3(64), 0, s, qkv, dO, lse, Dsum, dqkvT, ldT, T_,
+                     H, hd);
+  hipLaunchKernelGGL(k_attn_dq_f32, dim3((T_ + 63) / 64, B * H), dim3(64), 0, s, qkv, dO, lse, Dsum, dqkvT, ldT, T_, H,
+                     hd);
 }
 
 }  // namespace mt

@@ -156,9 +156,15 @@ void rmsnorm_dg(const float* dy, const float* x, const float* rstd, float* parti
 // ----------------------------------------------------------------- RoPE --
 // One block: 64 tokens x one head of q, k or v.  q and k rotate in place;
 // all three are also written transposed into qkvT [3d x M].
+int64_t token_ld(int64_t M) {
+  int64_t ld = (M + 127) / 128 * 128;
+  if ((ld / 128) % 2 == 0) ld += 128;
+  return ld;
+}
+
 template <typename T>
-__global__ void __launch_bounds__(256) k_rope_qkv(T* qkv, T* qkvT, const float* cosb, const float* sinb, int M,
-                                                  int T_, int d, int hd) {
+__global__ void __launch_bounds__(256) k_rope_qkv(T* qkv, T* qkvT, int64_t ldT, const float* cosb, const float* sinb,
+                                                  int M, int T_, int d, int hd) {
   __shared__ float tile[64][129];
   const int64_t m0 = (int64_t)blockIdx.x * 64;
   const int part = blockIdx.y / (d / hd);  // 0 q, 1 k, 2 v
@@ -193,21 +199,21 @@ __global__ void __launch_bounds__(256) k_rope_qkv(T* qkv, T* qkvT, const float* 
   for (int idx = threadIdx.x; idx < 64 * hd; idx += 256) {
     int c = idx / 64, r = idx % 64;
     int64_t m = m0 + r;
-    if (m < M) qkvT[(col0 + c) * M + m] = stf<T>(tile[r][c]);
+    if (m < M) qkvT[(col0 + c) * ldT + m] = stf<T>(tile[r][c]);
   }
 }
 
 template <typename T>
-void rope_qkv_fwd(T* qkv, T* qkvT, const float* cosb, const float* sinb, int M, int T_, int d, int hd,
+void rope_qkv_fwd(T* qkv, T* qkvT, int64_t ldT, const float* cosb, const float* sinb, int M, int T_, int d, int hd,
                   hipStream_t s) {
   if (M <= 0) return;
-  hipLaunchKernelGGL(k_rope_qkv<T>, dim3(cdiv(M, 64), 3 * (d / hd)), dim3(256), 0, s, qkv, qkvT, cosb, sinb, M, T_,
-                     d, hd);
+  hipLaunchKernelGGL(k_rope_qkv<T>, dim3(cdiv(M, 64), 3 * (d / hd)), dim3(256), 0, s, qkv, qkvT, ldT, cosb, sinb, M,
+                     T_, d, hd);
 }
 
 template <typename T>
-__global__ void __launch_bounds__(256) k_rope_bwd_T(T* x, const float* cosb, const float* sinb, int M, int T_, int d,
-                                                    int hd) {
+__global__ void __launch_bounds__(256) k_rope_bwd_T(T* x, int64_t ldT, const float* cosb, const float* sinb, int M,
+                                                    int T_, int d, int hd) {
   const int64_t m = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (m >= M) return;
   const int pr = blockIdx.y;  // pair index over q and k: [0, d)
@@ -218,15 +224,16 @@ __global__ void __launch_bounds__(256) k_rope_bwd_T(T* x, const float* cosb, con
   const int64_t ra = (int64_t)part * d + (int64_t)head * hd + i, rb = ra + h2;
   const int t = (int)(m % T_);
   const float cs = cosb[(int64_t)t * h2 + i], sn = sinb[(int64_t)t * h2 + i];
-  const float a = ldf(x[ra * M + m]), b = ldf(x[rb * M + m]);
-  x[ra * M + m] = stf<T>(a * cs + b * sn);
-  x[rb * M + m] = stf<T>(b * cs - a * sn);
+  const float a = ldf(x[ra * ldT + m]), b = ldf(x[rb * ldT + m]);
+  x[ra * ldT + m] = stf<T>(a * cs + b * sn);
+  x[rb * ldT + m] = stf<T>(b * cs - a * sn);
 }
 
 template <typename T>
-void rope_bwd_T(T* dqkvT, const float* cosb, const float* sinb, int M, int T_, int d, int hd, hipStream_t s) {
+void rope_bwd_T(T* dqkvT, int64_t ldT, const float* cosb, const float* sinb, int M, int T_, int d, int hd,
+                hipStream_t s) {
   if (M <= 0) return;
-  hipLaunchKernelGGL(k_rope_bwd_T<T>, dim3(cdiv(M, 256), d), dim3(256), 0, s, dqkvT, cosb, sinb, M, T_, d, hd);
+  hipLaunchKernelGGL(k_rope_bwd_T<T>, dim3(cdiv(M, 256), d), dim3(256), 0, s, dqkvT, ldT, cosb, sinb, M, T_, d, hd);
 }
 
 // --------------------------------------------------------------- SwiGLU --
@@ -346,7 +353,7 @@ void transpose(const T* in, int64_t ld_in, T* out, int64_t ld_out, int R, int C,
 }
 
 template <typename T>
-__global__ void __launch_bounds__(256) k_cast_transpose(const float* in, T* out, T* outT, int R, int C) {
+__global__ void __launch_bounds__(256) k_cast_transpose(const float* in, T* out, T* outT, int64_t ldT, int R, int C) {
   __shared__ T tile[64][65];
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
   for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
@@ -360,14 +367,14 @@ __global__ void __launch_bounds__(256) k_cast_transpose(const float* in, T* out,
   __syncthreads();
   for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
     int c = idx / 64, r = idx % 64;
-    if (r0 + r < R && c0 + c < C) outT[(c0 + c) * R + r0 + r] = tile[r][c];
+    if (r0 + r < R && c0 + c < C) outT[(c0 + c) * ldT + r0 + r] = tile[r][c];
   }
 }
 
 template <typename T>
-void cast_transpose(const float* in, T* out, T* outT, int R, int C, hipStream_t s) {
+void cast_transpose(const float* in, T* out, T* outT, int64_t ldT, int R, int C, hipStream_t s) {
   if (R <= 0 || C <= 0) return;
-  hipLaunchKernelGGL(k_cast_transpose<T>, dim3(cdiv(C, 64), cdiv(R, 64)), dim3(256), 0, s, in, out, outT, R, C);
+  hipLaunchKernelGGL(k_cast_transpose<T>, dim3(cdiv(C, 64), cdiv(R, 64)), dim3(256), 0, s, in, out, outT, ldT, R, C);
 }
 
 __global__ void k_fill_u32(uint32_t* p, uint32_t v, size_t n) {
@@ -388,13 +395,13 @@ void fill_u32(void* p, uint32_t value, size_t n_words, hipStream_t s) {
   template void rmsnorm_bwd<T>(const float*, const float*, const T*, const float*, const float*, float*, int, int, \
                                hipStream_t);                                                                    \
   template void rmsnorm_dg<T>(const float*, const float*, const float*, float*, T*, int, int, hipStream_t);      \
-  template void rope_qkv_fwd<T>(T*, T*, const float*, const float*, int, int, int, int, hipStream_t);           \
-  template void rope_bwd_T<T>(T*, const float*, const float*, int, int, int, int, hipStream_t);                 \
+  template void rope_qkv_fwd<T>(T*, T*, int64_t, const float*, const float*, int, int, int, int, hipStream_t);  \
+  template void rope_bwd_T<T>(T*, int64_t, const float*, const float*, int, int, int, int, hipStream_t);        \
   template void swiglu_fwd<T>(const T*, T*, int, int, hipStream_t);                                             \
   template void swiglu_bwd<T>(const T*, const T*, T*, int, int, hipStream_t);                                   \
   template void xent<T>(const float*, const int32_t*, float*, T*, int, int, int, float, hipStream_t);           \
   template void transpose<T>(const T*, int64_t, T*, int64_t, int, int, hipStream_t);                            \
-  template void cast_transpose<T>(const float*, T*, T*, int, int, hipStream_t);
+  template void cast_transpose<T>(const float*, T*, T*, int64_t, int, int, hipStream_t);
 
 MT_INST(float)
 MT_INST(uint16_t)

@@ -96,6 +96,7 @@ struct Model {
   std::vector<mt_block_desc> blocks;
   uint64_t store_bytes = 0, opt_bytes = 0, slot_bytes = 0;
   int L, d, H, hd, F, V, B, Tq, M;
+  int64_t Mp;  // padded row stride of token-major transposed buffers
   int E;  // bytes per weight element
 
   uint8_t* arena = nullptr;
@@ -138,7 +139,7 @@ struct Model {
     const uint64_t Md = (uint64_t)M * d;
     a.h = c.take<T>(Md * E);
     a.qkv = c.take<T>(3 * Md * E);
-    a.qkvT = c.take<T>(3 * Md * E);
+    a.qkvT = c.take<T>(3 * (uint64_t)d * Mp * E);
     a.o = c.take<T>(Md * E);
     a.h2 = c.take<T>(Md * E);
     a.gu = c.take<T>((uint64_t)M * 2 * F * E);
@@ -152,14 +153,14 @@ struct Model {
   void carve_bwd(Carver& c, BwdWs<T>& w) {
     const uint64_t Md = (uint64_t)M * d, MF = (uint64_t)M * F;
     w.dxb = c.take<T>(Md * E);
-    w.dxbT = c.take<T>(Md * E);
-    w.tmpT = c.take<T>(std::max(Md, MF) * E);
+    w.dxbT = c.take<T>((uint64_t)d * Mp * E);
+    w.tmpT = c.take<T>((uint64_t)std::max(d, F) * Mp * E);
     w.dy = c.take<T>(MF * E);
     w.dgu = c.take<T>(2 * MF * E);
-    w.dguT = c.take<T>(2 * MF * E);
+    w.dguT = c.take<T>(2 * (uint64_t)F * Mp * E);
     w.do_ = c.take<T>(Md * E);
-    w.doT = c.take<T>(Md * E);
-    w.dqkvT = c.take<T>(3 * Md * E);
+    w.doT = c.take<T>((uint64_t)d * Mp * E);
+    w.dqkvT = c.take<T>(3 * (uint64_t)d * Mp * E);
     w.dqkv = c.take<T>(3 * Md * E);
     w.dh = c.take<float>(Md * 4);
     w.dx1 = c.take<float>(Md * 4);
@@ -173,7 +174,7 @@ struct Model {
     const uint64_t MV = (uint64_t)M * V;
     w.z = c.take<T>((uint64_t)M * d * E);
     w.dlogits = c.take<T>(MV * E);
-    w.dlogitsT = c.take<T>(MV * E);
+    w.dlogitsT = c.take<T>((uint64_t)V * Mp * E);
     w.rz = c.take<float>((uint64_t)M * 4);
     w.logits = c.take<float>(MV * 4);
     w.row_loss = c.take<float>((uint64_t)M * 4);
@@ -257,6 +258,7 @@ struct Model {
     B = c.batch;
     Tq = c.seq_len;
     M = B * Tq;
+    Mp = token_ld(M);
     E = wbytes(c);
     n_uses = 2 * L + 3;
   }
@@ -297,10 +299,10 @@ struct Model {
     const float eps = (float)cfg.rms_eps;
     rmsnorm_fwd<T>(x, w.anorm, a.h, a.r1, M, d, eps, sc);
     gemm<T>(a.h, d, w.qkv, d, a.qkv, 3 * d, nullptr, 0, M, 3 * d, d, EPI_STORE);
-    rope_qkv_fwd<T>(a.qkv, a.qkvT, cosb, sinb, M, Tq, d, hd, sc);
+    rope_qkv_fwd<T>(a.qkv, a.qkvT, Mp, cosb, sinb, M, Tq, d, hd, sc);
     const bool timed = cfg.flags & MT_FLAG_TIME_KERNELS;
     if (timed) record_kernel_start(attn_fwd_flops(), 1);
-    attn_fwd<T>(a.qkv, a.qkvT, a.o, a.lse, B, Tq, H, hd, sc);
+    attn_fwd<T>(a.qkv, a.qkvT, Mp, a.o, a.lse, B, Tq, H, hd, sc);
     if (timed) record_kernel_end();
     gemm<T>(a.o, d, w.o, d, a.x1, d, x, d, M, d, d, EPI_ADD_F32);
     rmsnorm_fwd<T>(a.x1, w.fnorm, a.h2, a.r2, M, d, eps, sc);
@@ -321,37 +323,36 @@ struct Model {
   void layer_bwd(const LayerW<T>& w, const LayerWT<T>& wt_, const float* x, const Acts<T>& a, const float* dx2,
                  float* dx_out, const LayerW<T>& g) {
     BwdWs<T> ws = bwdws<T>();
-    const uint64_t Mu = M;
     // down projection
-    cast_transpose<T>(dx2, ws.dxb, ws.dxbT, M, d, sc);
-    transpose<T>(a.y, F, ws.tmpT, Mu, M, F, sc);
-    gemm<T>(ws.dxbT, M, ws.tmpT, M, g.d, F, nullptr, 0, d, F, M, EPI_STORE);
+    cast_transpose<T>(dx2, ws.dxb, ws.dxbT, Mp, M, d, sc);
+    transpose<T>(a.y, F, ws.tmpT, Mp, M, F, sc);
+    gemm<T>(ws.dxbT, Mp, ws.tmpT, Mp, g.d, F, nullptr, 0, d, F, M, EPI_STORE);
     gemm<T>(ws.dxb, d, wt_.d, d, ws.dy, F, nullptr, 0, M, F, d, EPI_STORE);
     // SwiGLU and gate/up projection
     swiglu_bwd<T>(ws.dy, a.gu, ws.dgu, M, F, sc);
-    transpose<T>(ws.dgu, 2 * F, ws.dguT, Mu, M, 2 * F, sc);
-    transpose<T>(a.h2, d, ws.tmpT, Mu, M, d, sc);
-    gemm<T>(ws.dguT, M, ws.tmpT, M, g.gu, d, nullptr, 0, 2 * F, d, M, EPI_STORE);
+    transpose<T>(ws.dgu, 2 * F, ws.dguT, Mp, M, 2 * F, sc);
+    transpose<T>(a.h2, d, ws.tmpT, Mp, M, d, sc);
+    gemm<T>(ws.dguT, Mp, ws.tmpT, Mp, g.gu, d, nullptr, 0, 2 * F, d, M, EPI_STORE);
     gemm<T>(ws.dgu, 2 * F, wt_.gu, 2 * F, ws.dh, d, nullptr, 0, M, d, 2 * F, EPI_F32);
     rmsnorm_bwd<T>(ws.dh, a.x1, w.fnorm, a.r2, dx2, ws.dx1, M, d, sc);
     rmsnorm_dg<T>(ws.dh, a.x1, a.r2, ws.part, g.fnorm, M, d, sc);
     // attention output projection
-    cast_transpose<T>(ws.dx1, ws.dxb, ws.dxbT, M, d, sc);
-    transpose<T>(a.o, d, ws.tmpT, Mu, M, d, sc);
-    gemm<T>(ws.dxbT, M, ws.tmpT, M, g.o, d, nullptr, 0, d, d, M, EPI_STORE);
+    cast_transpose<T>(ws.dx1, ws.dxb, ws.dxbT, Mp, M, d, sc);
+    transpose<T>(a.o, d, ws.tmpT, Mp, M, d, sc);
+    gemm<T>(ws.dxbT, Mp, ws.tmpT, Mp, g.o, d, nullptr, 0, d, d, M, EPI_STORE);
     gemm<T>(ws.dxb, d, wt_.o, d, ws.do_, d, nullptr, 0, M, d, d, EPI_STORE);
     // attention
-    transpose<T>(ws.do_, d, ws.doT, Mu, M, d, sc);
+    transpose<T>(ws.do_, d, ws.doT, Mp, M, d, sc);
     attn_bwd_dsum<T>(ws.do_, a.o, ws.Dsum, B, Tq, H, hd, sc);
     const bool timed = cfg.flags & MT_FLAG_TIME_KERNELS;
     if (timed) record_kernel_start(2.5 * attn_fwd_flops(), 1);
-    attn_bwd<T>(a.qkv, a.qkvT, ws.do_, ws.doT, a.lse, ws.Dsum, ws.dqkvT, B, Tq, H, hd, sc);
+    attn_bwd<T>(a.qkv, a.qkvT, ws.do_, ws.doT, Mp, a.lse, ws.Dsum, ws.dqkvT, B, Tq, H, hd, sc);
     if (timed) record_kernel_end();
-    rope_bwd_T<T>(ws.dqkvT, cosb, sinb, M, Tq, d, hd, sc);
+    rope_bwd_T<T>(ws.dqkvT, Mp, cosb, sinb, M, Tq, d, hd, sc);
     // QKV projection
-    transpose<T>(ws.dqkvT, M, ws.dqkv, 3 * d, 3 * d, M, sc);
-    transpose<T>(a.h, d, ws.tmpT, Mu, M, d, sc);
-    gemm<T>(ws.dqkvT, M, ws.tmpT, M, g.qkv, d, nullptr, 0, 3 * d, d, M, EPI_STORE);
+    transpose<T>(ws.dqkvT, Mp, ws.dqkv, 3 * d, 3 * d, M, sc);
+    transpose<T>(a.h, d, ws.tmpT, Mp, M, d, sc);
+    gemm<T>(ws.dqkvT, Mp, ws.tmpT, Mp, g.qkv, d, nullptr, 0, 3 * d, d, M, EPI_STORE);
     gemm<T>(ws.dqkv, 3 * d, wt_.qkv, 3 * d, ws.dh, d, nullptr, 0, M, d, 3 * d, EPI_F32);
     rmsnorm_bwd<T>(ws.dh, x, w.anorm, a.r1, ws.dx1, dx_out, M, d, sc);
     rmsnorm_dg<T>(ws.dh, x, a.r1, ws.part, g.anorm, M, d, sc);
@@ -374,9 +375,9 @@ struct Model {
     sum_fixed(hw.row_loss, hw.loss, M, inv_n, sc);
     MT_HIP(hipMemcpyAsync(h_loss, hw.loss, sizeof(float), hipMemcpyDeviceToHost, sc));
     MT_HIP(hipEventRecord(ev_loss, sc));
-    transpose<T>(hw.dlogits, V, hw.dlogitsT, M, M, V, sc);
-    transpose<T>(hw.z, d, ws.tmpT, M, M, d, sc);
-    gemm<T>(hw.dlogitsT, M, ws.tmpT, M, gwh, d, nullptr, 0, V, d, M, EPI_STORE);
+    transpose<T>(hw.dlogits, V, hw.dlogitsT, Mp, M, V, sc);
+    transpose<T>(hw.z, d, ws.tmpT, Mp, M, d, sc);
+    gemm<T>(hw.dlogitsT, Mp, ws.tmpT, Mp, gwh, d, nullptr, 0, V, d, M, EPI_STORE);
     T* whT = (T*)wt;
     transpose<T>(wh, d, whT, V, V, d, sc);
     gemm<T>(hw.dlogits, V, whT, V, ws.dh, d, nullptr, 0, M, d, V, EPI_F32);

@@ -38,14 +38,20 @@ size_t rmsnorm_dg_partial_elems(int M, int d);
 template <typename T>
 void rmsnorm_dg(const float* dy, const float* x, const float* rstd, float* partial, T* dg, int M, int d,
                 hipStream_t s);
+// Token-major transposed buffers [C x M] use a padded row stride
+// (token_ld(M) >= M): a row stride that is a large power of two puts a
+// tile's rows on the same memory channels.
+int64_t token_ld(int64_t M);
 // Rotate q and k of qkv [M x 3d] in place (pairs (i, i+hd/2), angle
-// t*theta^(-2i/hd), t = m mod T) and write the transpose qkvT [3d x M].
+// t*theta^(-2i/hd), t = m mod T) and write the transpose qkvT [3d x M]
+// (row stride ldT).
 template <typename T>
-void rope_qkv_fwd(T* qkv, T* qkvT, const float* cosb, const float* sinb, int M, int T_, int d, int hd,
+void rope_qkv_fwd(T* qkv, T* qkvT, int64_t ldT, const float* cosb, const float* sinb, int M, int T_, int d, int hd,
                   hipStream_t s);
-// Inverse rotation of the dq, dk rows of dqkvT [3d x M], in place.
+// Inverse rotation of the dq, dk rows of dqkvT [3d x M] (row stride ldT), in place.
 template <typename T>
-void rope_bwd_T(T* dqkvT, const float* cosb, const float* sinb, int M, int T_, int d, int hd, hipStream_t s);
+void rope_bwd_T(T* dqkvT, int64_t ldT, const float* cosb, const float* sinb, int M, int T_, int d, int hd,
+                hipStream_t s);
 template <typename T>
 void swiglu_fwd(const T* gu, T* y, int M, int F, hipStream_t s);
 template <typename T>
@@ -60,22 +66,24 @@ void sum_fixed(const float* x, float* out, int n, float scale, hipStream_t s);
 // out[C x R] = in[R x C]^T.
 template <typename T>
 void transpose(const T* in, int64_t ld_in, T* out, int64_t ld_out, int R, int C, hipStream_t s);
-// out = T(in) and outT = T(in)^T for in float [R x C].
+// out = T(in) and outT = T(in)^T (row stride ldT) for in float [R x C].
 template <typename T>
-void cast_transpose(const float* in, T* out, T* outT, int R, int C, hipStream_t s);
+void cast_transpose(const float* in, T* out, T* outT, int64_t ldT, int R, int C, hipStream_t s);
 void fill_u32(void* p, uint32_t value, size_t n_words, hipStream_t s);
 
 // ------------------------------------------------------------ attention --
-// qkv [M x 3d] (q, k rotated), qkvT [3d x M]; o [M x d]; lse [B*H x T]
-// (base-2 log-sum-exp of the scaled scores).
+// qkv [M x 3d] (q, k rotated), qkvT [3d x M] (row stride ldT); o [M x d];
+// lse [B*H x T] (base-2 log-sum-exp of the scaled scores).
 template <typename T>
-void attn_fwd(const T* qkv, const T* qkvT, T* o, float* lse, int B, int T_, int H, int hd, hipStream_t s);
+void attn_fwd(const T* qkv, const T* qkvT, int64_t ldT, T* o, float* lse, int B, int T_, int H, int hd,
+              hipStream_t s);
 // Dsum[b*H+h][t] = sum_i dO . O over the head.
 template <typename T>
 void attn_bwd_dsum(const T* dO, const T* O, float* Dsum, int B, int T_, int H, int hd, hipStream_t s);
-// dqkvT [3d x M] receives dq, dk, dv (transposed layout).
+// dqkvT [3d x M] receives dq, dk, dv (transposed layout); qkvT, dOT and
+// dqkvT share the row stride ldT.
 template <typename T>
-void attn_bwd(const T* qkv, const T* qkvT, const T* dO, const T* dOT, const float* lse, const float* Dsum,
-              T* dqkvT, int B, int T_, int H, int hd, hipStream_t s);
+void attn_bwd(const T* qkv, const T* qkvT, const T* dO, const T* dOT, int64_t ldT, const float* lse,
+              const float* Dsum, T* dqkvT, int B, int T_, int H, int hd, hipStream_t s);
 
 }  // namespace mt

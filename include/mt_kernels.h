@@ -36,26 +36,34 @@ int mt_transpose(int32_t dtype, const void* in, int64_t ld_in, void* out, int64_
  * in double and rounded to float (host buffers of T*hd/2 floats). */
 int mt_rope_tables(int32_t T, int32_t hd, double theta, float* cos_out, float* sin_out);
 
+/* Row stride (elements) the library uses for token-major transposed
+ * buffers [C x tokens]: tokens rounded up to a multiple of 128 so that the
+ * stride in 256-byte units is odd (a large power-of-two stride puts a tile's
+ * rows on the same memory channels). */
+int64_t mt_token_ld(int64_t tokens);
+
 /* qkv [B*T x 3d] (q | k | v columns, head-major inside each): rotate q and k
  * in place by +t*w_i on pairs (i, i+hd/2), t = position in the sequence, and
- * write the transpose qkvT [3d x B*T].  cos/sin: device tables from
- * mt_rope_tables. */
-int mt_rope_qkv(int32_t dtype, void* qkv, void* qkvT, const float* cos_t, const float* sin_t, int32_t B, int32_t T,
-                int32_t H, int32_t hd, void* stream);
+ * write the transpose qkvT [3d x B*T] with row stride ldT >= B*T.  cos/sin:
+ * device tables from mt_rope_tables. */
+int mt_rope_qkv(int32_t dtype, void* qkv, void* qkvT, int64_t ldT, const float* cos_t, const float* sin_t, int32_t B,
+                int32_t T, int32_t H, int32_t hd, void* stream);
 
 /* Causal softmax attention per (batch, head) with scale 1/sqrt(hd).
- * Inputs: rotated qkv and qkvT as left by mt_rope_qkv.  Outputs:
- * o [B*T x d] (dtype) and lse [B*H x T] (float, base-2 log-sum-exp of the
- * scaled scores times log2(e)).  bf16: hd = 128 and T % 64 == 0; f32: hd <= 64. */
-int mt_attention_fwd(int32_t dtype, const void* qkv, const void* qkvT, void* o, float* lse, int32_t B, int32_t T,
-                     int32_t H, int32_t hd, void* stream);
+ * Inputs: rotated qkv and qkvT (row stride ldT) as left by mt_rope_qkv.
+ * Outputs: o [B*T x d] (dtype) and lse [B*H x T] (float, base-2
+ * log-sum-exp of the scaled scores times log2(e)).  bf16: hd = 128 and
+ * T % 64 == 0, ldT % 8 == 0; f32: hd <= 64. */
+int mt_attention_fwd(int32_t dtype, const void* qkv, const void* qkvT, int64_t ldT, void* o, float* lse, int32_t B,
+                     int32_t T, int32_t H, int32_t hd, void* stream);
 
 /* Backward of mt_attention_fwd given dO [B*T x d] and dOT [d x B*T]:
  * writes Dsum [B*H x T] (float scratch, rowsum(dO * O)) and
- * dqkvT [3d x B*T] = (dq | dk | dv)^T with respect to the rotated q, k. */
+ * dqkvT [3d x B*T] = (dq | dk | dv)^T with respect to the rotated q, k.
+ * qkvT, dOT and dqkvT have row stride ldT. */
 int mt_attention_bwd(int32_t dtype, const void* qkv, const void* qkvT, const void* o, const void* dO,
-                     const void* dOT, const float* lse, float* Dsum, void* dqkvT, int32_t B, int32_t T, int32_t H,
-                     int32_t hd, void* stream);
+                     const void* dOT, int64_t ldT, const float* lse, float* Dsum, void* dqkvT, int32_t B, int32_t T,
+                     int32_t H, int32_t hd, void* stream);
 
 #ifdef __cplusplus
 }

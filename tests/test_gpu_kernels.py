@@ -47,7 +47,8 @@ def acc_bound(a, b):
     return K * 2.0 ** -24 * (np.abs(a) @ np.abs(b).T)
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 520, 200), (64, 8, 8), (513, 257, 1032), (1, 1, 8)])
+@pytest.mark.parametrize("M,N,K", [(300, 520, 200), (64, 8, 8), (513, 257, 1032), (1, 1, 8),
+                                   (300, 520, 256), (513, 257, 1024), (70, 1000, 64), (256, 256, 640)])
 def test_gemm_bf16_small(M, N, K):
     rng = np.random.default_rng(M * 7 + N)
     A, a = bf16_tensor(rng.standard_normal((M, K)).astype(np.float32))
@@ -152,23 +153,26 @@ def run_attention(dtype, B, T, H, hd, seed, theta=10000.0):
         do_dev = torch.from_numpy(dO).to(dev())
         qkv64, do64 = qkv.astype(np.float64), dO.astype(np.float64)
         et = torch.float32
-    qkvT = torch.empty((3 * d, M), dtype=et, device=dev())
-    mt.check(mt.lib().mt_rope_qkv(dtype, q_dev.data_ptr(), qkvT.data_ptr(), cos_t.data_ptr(), sin_t.data_ptr(),
+    ldT = int(mt.lib().mt_token_ld(M))
+    assert ldT >= M and ldT % 128 == 0 and (ldT // 128) % 2 == 1
+    qkvT = torch.empty((3 * d, ldT), dtype=et, device=dev())
+    mt.check(mt.lib().mt_rope_qkv(dtype, q_dev.data_ptr(), qkvT.data_ptr(), ldT, cos_t.data_ptr(), sin_t.data_ptr(),
                                   B, T, H, hd, None))
     o = torch.empty((M, d), dtype=et, device=dev())
     lse = torch.empty((B * H, T), dtype=torch.float32, device=dev())
-    mt.check(mt.lib().mt_attention_fwd(dtype, q_dev.data_ptr(), qkvT.data_ptr(), o.data_ptr(), lse.data_ptr(),
+    mt.check(mt.lib().mt_attention_fwd(dtype, q_dev.data_ptr(), qkvT.data_ptr(), ldT, o.data_ptr(), lse.data_ptr(),
                                        B, T, H, hd, None))
-    doT = torch.empty((d, M), dtype=et, device=dev())
-    mt.check(mt.lib().mt_transpose(dtype, do_dev.data_ptr(), d, doT.data_ptr(), M, M, d, None))
+    doT = torch.empty((d, ldT), dtype=et, device=dev())
+    mt.check(mt.lib().mt_transpose(dtype, do_dev.data_ptr(), d, doT.data_ptr(), ldT, M, d, None))
     Dsum = torch.empty((B * H, T), dtype=torch.float32, device=dev())
-    dqkvT = torch.empty((3 * d, M), dtype=et, device=dev())
+    dqkvT = torch.empty((3 * d, ldT), dtype=et, device=dev())
     mt.check(mt.lib().mt_attention_bwd(dtype, q_dev.data_ptr(), qkvT.data_ptr(), o.data_ptr(), do_dev.data_ptr(),
-                                       doT.data_ptr(), lse.data_ptr(), Dsum.data_ptr(), dqkvT.data_ptr(),
+                                       doT.data_ptr(), ldT, lse.data_ptr(), Dsum.data_ptr(), dqkvT.data_ptr(),
                                        B, T, H, hd, None))
     torch.cuda.synchronize()
     conv = to_f32 if dtype == mt.MT_BF16 else (lambda t: t.cpu().numpy().astype(np.float64))
-    out = dict(qkv=conv(q_dev), qkvT=conv(qkvT), o=conv(o), lse=lse.cpu().numpy(), dqkvT=conv(dqkvT))
+    out = dict(qkv=conv(q_dev), qkvT=conv(qkvT[:, :M]), o=conv(o), lse=lse.cpu().numpy(),
+               dqkvT=conv(dqkvT[:, :M]))
     # oracle in float64 on the values the kernel read
     c64, s64 = rope_tables(T, hd, theta, np.float64)
     heads = lambda x: x.reshape(B, T, H, hd).transpose(0, 2, 1, 3)
