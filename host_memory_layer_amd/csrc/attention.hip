@@ -35,6 +35,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 namespace {
 
@@ -77,7 +78,7 @@ __device__ inline bf16x8_t acc_to_frag(const f32x16_t& a, int ks) {
 }
 
 // ------------------------------------------------------------ forward ----
-__global__ void __launch_bounds__(256) k_attn_fwd_bf16(const uint16_t* __restrict__ qkv,
+__global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __restrict__ qkv,
                                                      const uint16_t* __restrict__ qkvT, int64_t ldT,
                                                      uint16_t* __restrict__ o, float* __restrict__ lse, int T, int H) {
   constexpr int HD = 128;
@@ -101,26 +102,27 @@ __global__ void __launch_bounds__(256) k_attn_fwd_bf16(const uint16_t* __restric
   }
 
   const int nkb = min(T, (qb + 1) * 128) / 64;
-  u32x4_t rk[4], rv[4];
-  auto gload = [&](int kb) {
+  // K [64 keys x 256 B] and V^T [128 hd x 128 B] tiles go global -> LDS with
+  // buffer_load ... lds; kilobyte j = wave*4 + i of a tile is written by one
+  // instruction, so each lane's source is chosen to land in the swizzled
+  // layout the fragment reads expect.
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(qkv + rowbase * ld + d + h * HD), 0, (int)((int64_t)T * ld * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(qkvT + (int64_t)(2 * d + h * HD) * ldT + rowbase), 0, (int)((int64_t)HD * ldT * 2), 0x00020000);
+  auto issue = [&](int kb, int buf) {
+    uint8_t* Ks = smem + buf * 32768;
+    uint8_t* Vs = Ks + 16384;
     const int key0 = kb * 64;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int id = tid + 256 * i;
-      const int kr = id >> 4, kc = id & 15;
-      rk[i] = *(const u32x4_t*)(qkv + (rowbase + key0 + kr) * ld + d + h * HD + 8 * kc);
-      const int vr = id >> 3, vc = id & 7;
-      rv[i] = *(const u32x4_t*)(qkvT + (int64_t)(2 * d + h * HD + vr) * ldT + rowbase + key0 + 8 * vc);
-    }
-  };
-  auto sstore = [&](int buf) {
-    uint8_t* Ks = smem + buf * 32768;
-    uint8_t* Vs = Ks + 16384;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + 256 * i;
-      *(u32x4_t*)(Ks + sw256(id >> 4, id & 15)) = rk[i];
-      *(u32x4_t*)(Vs + sw128(id >> 3, id & 7)) = rv[i];
+      const int j = wave * 4 + i;
+      const int kr = 4 * j + (lane >> 4), kc = (lane & 15) ^ (kr & 15);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_t*)(Ks + j * 1024), 16, (int)((kr * ld + 8 * kc) * 2),
+                                               (int)((int64_t)key0 * ld * 2), 0, 0);
+      const int vr = 8 * j + (lane >> 3), vc = (lane & 7) ^ (vr & 7);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void_t*)(Vs + j * 1024), 16, (int)((vr * ldT + 8 * vc) * 2),
+                                               key0 * 2, 0, 0);
     }
   };
 
@@ -130,12 +132,12 @@ __global__ void __launch_bounds__(256) k_attn_fwd_bf16(const uint16_t* __restric
   for (int t = 0; t < 4; ++t) acc_o[t] = zero16();
   const int tq = q0 + (lane & 31);
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  issue(0, 0);
   for (int kb = 0; kb < nkb; ++kb) {
     const int buf = kb & 1;
-    if (kb + 1 < nkb) gload(kb + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kb + 1 < nkb) issue(kb + 1, buf ^ 1);
     const uint8_t* Ks = smem + buf * 32768;
     const uint8_t* Vs = Ks + 16384;
     if (active && kb * 64 <= q0 + 31) {
@@ -149,36 +151,45 @@ __global__ void __launch_bounds__(256) k_attn_fwd_bf16(const uint16_t* __restric
           s_acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], s_acc[kt], 0, 0, 0);
         }
       }
-      const bool need_mask = kb * 64 + 63 > q0;
+      // Only blocks that reach past the wave's first query need the causal
+      // mask (wave-uniform branch).
+      if (kb * 64 + 63 > q0) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kb * 64 + 32 * kt + acc_row(r, lane) > tq) s_acc[kt][r] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = s_acc[kt][r] * c;
-          if (need_mask && kb * 64 + 32 * kt + acc_row(r, lane) > tq) v = -INFINITY;
-          s_acc[kt][r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_i, mx);
-      const float alpha = exp2f(m_i - m_new);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_acc[kt][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+      // Lazy rescaling: the reference max m_i moves only when the block max
+      // exceeds it by more than 8 (in log2 units), so probabilities stay
+      // below 2^8; the final O / l uses the same reference, so the result is
+      // unchanged.  The branch is uniform across the wave.
+      if (__any(mx > m_i + 8.0f)) {
+        const float m_new = fmaxf(m_i, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_i - m_new);
+        l_i *= alpha;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_o[t][r] *= alpha;
+        m_i = m_new;
+      }
       float rs = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = exp2f(s_acc[kt][r] - m_new);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s_acc[kt][r], c, -m_i));
           s_acc[kt][r] = p;
           rs += p;
         }
-      rs += __shfl_xor(rs, 32);
-      l_i = l_i * alpha + rs;
-      m_i = m_new;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[t][r] *= alpha;
+      l_i += rs + __shfl_xor(rs, 32);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8_t pf = acc_to_frag(s_acc[ks >> 1], ks & 1);
@@ -189,9 +200,8 @@ __global__ void __launch_bounds__(256) k_attn_fwd_bf16(const uint16_t* __restric
         }
       }
     }
-    if (kb + 1 < nkb) sstore(buf ^ 1);
-    __syncthreads();
   }
+  __syncthreads();
 
   // O^T accumulators -> LDS [query][hd] -> coalesced rows of o.
   uint16_t* Os = (uint16_t*)(smem + wave * 8192);
@@ -240,6 +250,24 @@ __global__ void __launch_bounds__(256) k_dsum(const T* dO, const T* O, float* Ds
 }
 
 // ------------------------------------------------------- backward dK dV --
+// 64-byte rows (32 bf16): 16-byte chunk c stored at c ^ ((row >> 2) & 3).
+__device__ inline int sw64(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
+
+// Fragment of a transposed tile with 64-byte rows (32 columns) for the
+// contraction slice starting at column c0 (multiple of 16).
+__device__ inline bf16x8_t frag_T64(const uint8_t* base, int row, int c0, int lane) {
+  const int h = lane >> 5;
+  const int ch = c0 >> 3;
+  bf16x4_t lo = *(const bf16x4_t*)(base + sw64(row, ch) + 8 * h);
+  bf16x4_t hi = *(const bf16x4_t*)(base + sw64(row, ch + 1) + 8 * h);
+  bf16x8_t f;
+  f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+  f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+  return f;
+}
+
+// One block = 128 keys of one (batch, head); query tiles of 32 stream
+// through a double-buffered LDS ring filled by buffer_load ... lds.
 __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restrict__ qkv,
                                                       const uint16_t* __restrict__ qkvT,
                                                       const uint16_t* __restrict__ dO,
@@ -247,16 +275,12 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
                                                       const float* __restrict__ Dsum, uint16_t* __restrict__ dqkvT,
                                                       int64_t ldT, int T, int H) {
   constexpr int HD = 128;
-  // K, V: [128 keys][128 hd]; per query tile: Q, dO [64][128]; Q^T, dO^T [128][64]; lse, D [64].
-  __shared__ __attribute__((aligned(16))) uint8_t smem[32768 * 2 + 16384 * 4 + 512];
+  constexpr int QT = 32;                       // queries per tile
+  constexpr int TILE = QT * HD * 2;            // 8 KiB per operand tile
+  constexpr int STAGE = 4 * TILE + 512;        // Q, dO, Q^T, dO^T, lse, D
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 32768 + 2 * STAGE];
   uint8_t* Ks = smem;
   uint8_t* Vs = smem + 32768;
-  uint8_t* Qs = smem + 65536;
-  uint8_t* dOs = Qs + 16384;
-  uint8_t* QTs = dOs + 16384;
-  uint8_t* dOTs = QTs + 16384;
-  float* lse_s = (float*)(dOTs + 16384);
-  float* D_s = lse_s + 64;
 
   const int kblk = blockIdx.x;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
@@ -283,6 +307,47 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
     *(u32x4_t*)(Vs + sw256(r, ch)) = vv;
   }
 
+  const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(qkv + rowbase * ld + h * HD), 0, (int)((int64_t)T * ld * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(dO + rowbase * d + h * HD), 0, (int)((int64_t)T * d * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t qtrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(qkvT + (int64_t)(h * HD) * ldT + rowbase), 0, (int)((int64_t)HD * ldT * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t otrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(dOT + (int64_t)(h * HD) * ldT + rowbase), 0, (int)((int64_t)HD * ldT * 2), 0x00020000);
+  // Each operand tile is 8 KiB = 8 direct-load kilobytes: wave w writes
+  // kilobytes 2w and 2w+1 of each of the four tiles.
+  auto issue = [&](int n, int buf) {
+    uint8_t* st = smem + 65536 + buf * STAGE;
+    const int q0 = n * QT;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int j = wave * 2 + i;
+      // row-major tiles: 4 rows of 256 B per kilobyte
+      const int r = 4 * j + (lane >> 4), ch = (lane & 15) ^ (r & 15);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, (lds_void_t*)(st + j * 1024), 16, (int)((r * ld + 8 * ch) * 2),
+                                               (int)((int64_t)q0 * ld * 2), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(orsrc, (lds_void_t*)(st + TILE + j * 1024), 16,
+                                               (int)((r * d + 8 * ch) * 2), (int)((int64_t)q0 * d * 2), 0, 0);
+      // transposed tiles: 16 rows of 64 B per kilobyte
+      const int tr = 16 * j + (lane >> 2), tc = (lane & 3) ^ ((tr >> 2) & 3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qtrsrc, (lds_void_t*)(st + 2 * TILE + j * 1024), 16,
+                                               (int)((tr * ldT + 8 * tc) * 2), q0 * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(otrsrc, (lds_void_t*)(st + 3 * TILE + j * 1024), 16,
+                                               (int)((tr * ldT + 8 * tc) * 2), q0 * 2, 0, 0);
+    }
+  };
+  float ld_stat = 0.f;  // lse (threads 0..31) or D (threads 32..63) of the next tile
+  auto load_stats = [&](int n) {
+    if (tid < 64) {
+      const int q = n * QT + (tid & 31);
+      ld_stat = tid < 32 ? lse[(int64_t)bh * T + q] : Dsum[(int64_t)bh * T + q];
+    }
+  };
+  auto store_stats = [&](int buf) {
+    if (tid < 64) ((float*)(smem + 65536 + buf * STAGE + 4 * TILE))[tid] = ld_stat;
+  };
+
   f32x16_t acc_dk[4], acc_dv[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -290,50 +355,57 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
     acc_dv[t] = zero16();
   }
   const int key = k0 + (lane & 31);
+  const int n0 = kbase / QT, n1 = T / QT;
 
-  for (int qblk = kbase / 64; qblk < T / 64; ++qblk) {
-    const int qs0 = qblk * 64;
+  issue(n0, 0);
+  load_stats(n0);
+  store_stats(0);
+  for (int n = n0; n < n1; ++n) {
+    const int buf = (n - n0) & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + 256 * i;
-      const int r = id >> 4, ch = id & 15;
-      *(u32x4_t*)(Qs + sw256(r, ch)) = *(const u32x4_t*)(qkv + (rowbase + qs0 + r) * ld + h * HD + 8 * ch);
-      *(u32x4_t*)(dOs + sw256(r, ch)) = *(const u32x4_t*)(dO + (rowbase + qs0 + r) * d + h * HD + 8 * ch);
-      const int tr = id >> 3, tc = id & 7;
-      *(u32x4_t*)(QTs + sw128(tr, tc)) =
-          *(const u32x4_t*)(qkvT + (int64_t)(h * HD + tr) * ldT + rowbase + qs0 + 8 * tc);
-      *(u32x4_t*)(dOTs + sw128(tr, tc)) =
-          *(const u32x4_t*)(dOT + (int64_t)(h * HD + tr) * ldT + rowbase + qs0 + 8 * tc);
+    const bool more = n + 1 < n1;
+    if (more) {
+      issue(n + 1, buf ^ 1);
+      load_stats(n + 1);
     }
-    if (tid < 64) {
-      lse_s[tid] = lse[(int64_t)bh * T + qs0 + tid];
-      D_s[tid] = Dsum[(int64_t)bh * T + qs0 + tid];
-    }
-    __syncthreads();
-    if (!active) continue;
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-      const int qbase = qs0 + 32 * qs;
-      if (k0 > qbase + 31) continue;  // every key of the wave is after every query
+    const uint8_t* st = smem + 65536 + buf * STAGE;
+    const uint8_t* Qs = st;
+    const uint8_t* dOs = st + TILE;
+    const uint8_t* QTs = st + 2 * TILE;
+    const uint8_t* dOTs = st + 3 * TILE;
+    const float* lse_s = (const float*)(st + 4 * TILE);
+    const float* D_s = lse_s + 32;
+    const int qbase = n * QT;
+    if (active && k0 <= qbase + 31) {
       f32x16_t s_acc = zero16(), dp_acc = zero16();
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int ch = 2 * s + (lane >> 5);
-        const bf16x8_t qf = *(const bf16x8_t*)(Qs + sw256(32 * qs + (lane & 31), ch));
+        const bf16x8_t qf = *(const bf16x8_t*)(Qs + sw256(lane & 31, ch));
         const bf16x8_t kf = *(const bf16x8_t*)(Ks + sw256(32 * wave + (lane & 31), ch));
         s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, kf, s_acc, 0, 0, 0);
-        const bf16x8_t of = *(const bf16x8_t*)(dOs + sw256(32 * qs + (lane & 31), ch));
+        const bf16x8_t of = *(const bf16x8_t*)(dOs + sw256(lane & 31, ch));
         const bf16x8_t vf = *(const bf16x8_t*)(Vs + sw256(32 * wave + (lane & 31), ch));
         dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, vf, dp_acc, 0, 0, 0);
       }
-      // rows = queries, column = this lane's key
+      // rows = queries of the tile, column = this lane's key
+      if (k0 + 31 > qbase) {  // tile crosses the diagonal: mask keys after the query
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = 32 * qs + acc_row(r, lane);
-        const float p = (key <= qs0 + qi) ? exp2f(s_acc[r] * c - lse_s[qi]) : 0.f;
-        s_acc[r] = p;
-        dp_acc[r] = p * (dp_acc[r] - D_s[qi]);
+        for (int r = 0; r < 16; ++r) {
+          const int qi = acc_row(r, lane);
+          const float p = (key <= qbase + qi) ? __builtin_amdgcn_exp2f(fmaf(s_acc[r], c, -lse_s[qi])) : 0.f;
+          s_acc[r] = p;
+          dp_acc[r] = p * (dp_acc[r] - D_s[qi]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = acc_row(r, lane);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s_acc[r], c, -lse_s[qi]));
+          s_acc[r] = p;
+          dp_acc[r] = p * (dp_acc[r] - D_s[qi]);
+        }
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -341,13 +413,14 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
         const bf16x8_t dsf = acc_to_frag(dp_acc, ks);
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) {
-          const bf16x8_t oT = frag_T(dOTs, 32 * ht + (lane & 31), 32 * qs + 16 * ks, lane);
+          const bf16x8_t oT = frag_T64(dOTs, 32 * ht + (lane & 31), 16 * ks, lane);
           acc_dv[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oT, pf, acc_dv[ht], 0, 0, 0);
-          const bf16x8_t qT = frag_T(QTs, 32 * ht + (lane & 31), 32 * qs + 16 * ks, lane);
+          const bf16x8_t qT = frag_T64(QTs, 32 * ht + (lane & 31), 16 * ks, lane);
           acc_dk[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT, dsf, acc_dk[ht], 0, 0, 0);
         }
       }
     }
+    if (more) store_stats(buf ^ 1);
   }
   if (!active) return;
   // dK^T, dV^T: lane = key column, registers = hd rows.
@@ -396,29 +469,29 @@ __global__ void __launch_bounds__(256) k_attn_dq_bf16(const uint16_t* __restrict
   }
 
   const int nkb = min(T, (qb + 1) * 128) / 64;
-  u32x4_t rk[4], rv[4], rt[4];
-  auto gload = [&](int kb) {
-    const int key0 = kb * 64;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int id = tid + 256 * i;
-      const int r = id >> 4, ch = id & 15;
-      rk[i] = *(const u32x4_t*)(qkv + (rowbase + key0 + r) * ld + d + h * HD + 8 * ch);
-      rv[i] = *(const u32x4_t*)(qkv + (rowbase + key0 + r) * ld + 2 * d + h * HD + 8 * ch);
-      const int tr = id >> 3, tc = id & 7;
-      rt[i] = *(const u32x4_t*)(qkvT + (int64_t)(d + h * HD + tr) * ldT + rowbase + key0 + 8 * tc);
-    }
-  };
-  auto sstore = [&](int buf) {
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(qkv + rowbase * ld + d + h * HD), 0, (int)((int64_t)T * ld * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(qkv + rowbase * ld + 2 * d + h * HD), 0, (int)((int64_t)T * ld * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ktrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(qkvT + (int64_t)(d + h * HD) * ldT + rowbase), 0, (int)((int64_t)HD * ldT * 2), 0x00020000);
+  // K, V [64 keys x 256 B] and K^T [128 hd x 128 B]: 16 direct-load
+  // kilobytes each; wave w writes kilobytes 4w .. 4w+3 of each.
+  auto issue = [&](int kb, int buf) {
     uint8_t* Ks = smem + buf * 49152;
     uint8_t* Vs = Ks + 16384;
     uint8_t* KTs = Vs + 16384;
+    const int key0 = kb * 64;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int id = tid + 256 * i;
-      *(u32x4_t*)(Ks + sw256(id >> 4, id & 15)) = rk[i];
-      *(u32x4_t*)(Vs + sw256(id >> 4, id & 15)) = rv[i];
-      *(u32x4_t*)(KTs + sw128(id >> 3, id & 7)) = rt[i];
+      const int j = wave * 4 + i;
+      const int r = 4 * j + (lane >> 4), ch = (lane & 15) ^ (r & 15);
+      const int voff = (r * ld + 8 * ch) * 2, soff = (int)((int64_t)key0 * ld * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_t*)(Ks + j * 1024), 16, voff, soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void_t*)(Vs + j * 1024), 16, voff, soff, 0, 0);
+      const int tr = 8 * j + (lane >> 3), tc = (lane & 7) ^ (tr & 7);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ktrsrc, (lds_void_t*)(KTs + j * 1024), 16,
+                                               (int)((tr * ldT + 8 * tc) * 2), key0 * 2, 0, 0);
     }
   };
 
@@ -426,12 +499,12 @@ __global__ void __launch_bounds__(256) k_attn_dq_bf16(const uint16_t* __restrict
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc_dq[t] = zero16();
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  issue(0, 0);
   for (int kb = 0; kb < nkb; ++kb) {
     const int buf = kb & 1;
-    if (kb + 1 < nkb) gload(kb + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kb + 1 < nkb) issue(kb + 1, buf ^ 1);
     const uint8_t* Ks = smem + buf * 49152;
     const uint8_t* Vs = Ks + 16384;
     const uint8_t* KTs = Vs + 16384;
@@ -449,11 +522,19 @@ __global__ void __launch_bounds__(256) k_attn_dq_bf16(const uint16_t* __restrict
           const bf16x8_t vf = *(const bf16x8_t*)(Vs + sw256(32 * kt + (lane & 31), ch));
           dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, of[s], dp_acc, 0, 0, 0);
         }
+        if (kstart + 31 > q0) {  // sub-tile crosses the diagonal
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kstart + acc_row(r, lane);
-          const float p = (key <= tq) ? exp2f(s_acc[r] * c - lse_q) : 0.f;
-          dp_acc[r] = p * (dp_acc[r] - D_q);
+          for (int r = 0; r < 16; ++r) {
+            const int key = kstart + acc_row(r, lane);
+            const float p = (key <= tq) ? __builtin_amdgcn_exp2f(fmaf(s_acc[r], c, -lse_q)) : 0.f;
+            dp_acc[r] = p * (dp_acc[r] - D_q);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s_acc[r], c, -lse_q));
+            dp_acc[r] = p * (dp_acc[r] - D_q);
+          }
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -466,8 +547,6 @@ __global__ void __launch_bounds__(256) k_attn_dq_bf16(const uint16_t* __restrict
         }
       }
     }
-    if (kb + 1 < nkb) sstore(buf ^ 1);
-    __syncthreads();
   }
   if (!active) return;
 #pragma unroll

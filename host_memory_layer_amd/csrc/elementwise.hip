@@ -6,6 +6,9 @@
 // a time, weights streamed in and gradients streamed out).  Every reduction
 // runs in a fixed order that depends only on the shapes, so repeated runs
 // and the streamed / resident schedules give identical bits.
+#include <algorithm>
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace mt {
@@ -18,6 +21,27 @@ template <> __device__ inline float stf<float>(float x) { return x; }
 template <> __device__ inline uint16_t stf<uint16_t>(float x) { return f32_to_bf16(x); }
 
 static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Four consecutive elements of type T as a float4 (16-byte loads for float,
+// 8-byte for bf16); addresses must be aligned to 4 elements.
+template <typename T> struct V4;
+template <> struct V4<float> {
+  static __device__ inline float4 ld(const float* p) { return *(const float4*)p; }
+  static __device__ inline void st(float* p, float4 v) { *(float4*)p = v; }
+};
+template <> struct V4<uint16_t> {
+  static __device__ inline float4 ld(const uint16_t* p) {
+    const uint2 u = *(const uint2*)p;
+    return make_float4(bf16_to_f32(u.x & 0xFFFF), bf16_to_f32(u.x >> 16), bf16_to_f32(u.y & 0xFFFF),
+                       bf16_to_f32(u.y >> 16));
+  }
+  static __device__ inline void st(uint16_t* p, float4 v) {
+    uint2 u;
+    u.x = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
+    u.y = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
+    *(uint2*)p = u;
+  }
+};
 
 // Sum over a 256-thread block in a fixed tree order; every thread gets the result.
 __device__ inline float block_sum256(float v, float* red) {
@@ -71,65 +95,132 @@ void embed_bwd(const float* dx, const int32_t* order, const int32_t* seg, T* dE,
 }
 
 // -------------------------------------------------------------- RMSNorm --
-template <typename T>
-__global__ void __launch_bounds__(256) k_rmsnorm_fwd(const float* x, const T* g, T* y, float* rstd, int d, float eps) {
+// A row of d floats lives in registers: thread t owns the 4-wide chunks
+// t, t+256, ... (VPT of them); d must be a multiple of 4.
+template <typename T, int VPT>
+__global__ void __launch_bounds__(256) k_rmsnorm_fwd(const float* __restrict__ x, const T* __restrict__ g,
+                                                     T* __restrict__ y, float* __restrict__ rstd, int d, float eps) {
   __shared__ float red[4];
   const int64_t m = blockIdx.x;
   const float* xr = x + m * d;
+  float4 v[VPT];
   float ss = 0.f;
-  for (int i = threadIdx.x; i < d; i += 256) ss += xr[i] * xr[i];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int c = (threadIdx.x + 256 * k) * 4;
+    v[k] = c < d ? *(const float4*)(xr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
+  }
   ss = block_sum256(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)d + eps);
   if (threadIdx.x == 0) rstd[m] = r;
-  for (int i = threadIdx.x; i < d; i += 256) y[m * d + i] = stf<T>(xr[i] * r * ldf(g[i]));
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int c = (threadIdx.x + 256 * k) * 4;
+    if (c < d) {
+      const float4 gg = V4<T>::ld(g + c);
+      V4<T>::st(y + m * d + c, make_float4(v[k].x * r * gg.x, v[k].y * r * gg.y, v[k].z * r * gg.z, v[k].w * r * gg.w));
+    }
+  }
 }
+
+static int rms_vpt(int d) {
+  const int need = cdiv(d, 1024);
+  const int opts[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16};
+  for (int o : opts)
+    if (o >= need) return o;
+  throw ApiError{MT_E_INVALID, "RMSNorm supports d_model <= 16384"};
+}
+
+#define MT_RMS_DISPATCH(VPT_, LAUNCH) \
+  switch (VPT_) {                     \
+    case 1: LAUNCH(1); break;         \
+    case 2: LAUNCH(2); break;         \
+    case 3: LAUNCH(3); break;         \
+    case 4: LAUNCH(4); break;         \
+    case 5: LAUNCH(5); break;         \
+    case 6: LAUNCH(6); break;         \
+    case 8: LAUNCH(8); break;         \
+    case 10: LAUNCH(10); break;       \
+    case 12: LAUNCH(12); break;       \
+    default: LAUNCH(16); break;       \
+  }
 
 template <typename T>
 void rmsnorm_fwd(const float* x, const T* g, T* y, float* rstd, int M, int d, float eps, hipStream_t s) {
   if (M <= 0) return;
-  hipLaunchKernelGGL(k_rmsnorm_fwd<T>, dim3(M), dim3(256), 0, s, x, g, y, rstd, d, eps);
+  if (d % 4) throw ApiError{MT_E_INVALID, "RMSNorm needs d_model % 4 == 0"};
+#define L_(V) hipLaunchKernelGGL((k_rmsnorm_fwd<T, V>), dim3(M), dim3(256), 0, s, x, g, y, rstd, d, eps)
+  MT_RMS_DISPATCH(rms_vpt(d), L_)
+#undef L_
 }
 
-template <typename T>
-__global__ void __launch_bounds__(256) k_rmsnorm_bwd(const float* dy, const float* x, const T* g, const float* rstd,
-                                                     const float* resid, float* dx, int d) {
+// Backward of RMSNorm over kRmsRows consecutive rows per block:
+// dx = resid + r*(dy*g - xh*mean(dy*g*xh)) with xh = x*r, and the block's
+// partial dgain sum_rows dy*xh written to part[block][d].  A second kernel
+// adds the partials in block order.
+constexpr int kRmsRows = 32;
+
+size_t rmsnorm_dg_partial_elems(int M, int d) { return (size_t)std::max(1, cdiv(M, kRmsRows)) * d; }
+
+template <typename T, int VPT>
+__global__ void __launch_bounds__(256) k_rmsnorm_bwd(const float* __restrict__ dy, const float* __restrict__ x,
+                                                     const T* __restrict__ g, const float* __restrict__ rstd,
+                                                     const float* __restrict__ resid, float* __restrict__ dx,
+                                                     float* __restrict__ part, int M, int d) {
   __shared__ float red[4];
-  const int64_t m = blockIdx.x;
-  const float r = rstd[m];
-  const float* dyr = dy + m * d;
-  const float* xr = x + m * d;
-  float dot = 0.f;
-  for (int i = threadIdx.x; i < d; i += 256) dot += dyr[i] * ldf(g[i]) * (xr[i] * r);
-  dot = block_sum256(dot, red);
-  const float mean = dot / (float)d;
-  for (int i = threadIdx.x; i < d; i += 256) {
-    float xh = xr[i] * r;
-    float v = r * (dyr[i] * ldf(g[i]) - xh * mean);
-    if (resid) v = resid[m * d + i] + v;
-    dx[m * d + i] = v;
+  float4 gv[VPT], dg[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int c = (threadIdx.x + 256 * k) * 4;
+    gv[k] = c < d ? V4<T>::ld(g + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    dg[k] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-}
-
-template <typename T>
-void rmsnorm_bwd(const float* dy, const float* x, const T* g, const float* rstd, const float* resid, float* dx, int M,
-                 int d, hipStream_t s) {
-  if (M <= 0) return;
-  hipLaunchKernelGGL(k_rmsnorm_bwd<T>, dim3(M), dim3(256), 0, s, dy, x, g, rstd, resid, dx, d);
-}
-
-constexpr int kDgRows = 128;
-
-size_t rmsnorm_dg_partial_elems(int M, int d) { return (size_t)cdiv(M, kDgRows) * d; }
-
-__global__ void __launch_bounds__(256) k_dg_partial(const float* dy, const float* x, const float* rstd, float* part,
-                                                    int M, int d) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  const int chunk = blockIdx.y;
-  if (c >= d) return;
-  const int m0 = chunk * kDgRows, m1 = min(M, m0 + kDgRows);
-  float acc = 0.f;
-  for (int m = m0; m < m1; ++m) acc += dy[(int64_t)m * d + c] * (x[(int64_t)m * d + c] * rstd[m]);
-  part[(int64_t)chunk * d + c] = acc;
+  const int m0 = blockIdx.x * kRmsRows, m1 = min(M, m0 + kRmsRows);
+  for (int m = m0; m < m1; ++m) {
+    const float r = rstd[m];
+    const float* dyr = dy + (int64_t)m * d;
+    const float* xr = x + (int64_t)m * d;
+    float4 e[VPT], xh[VPT];
+    float dot = 0.f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int c = (threadIdx.x + 256 * k) * 4;
+      if (c < d) {
+        e[k] = *(const float4*)(dyr + c);
+        const float4 xv = *(const float4*)(xr + c);
+        xh[k] = make_float4(xv.x * r, xv.y * r, xv.z * r, xv.w * r);
+      } else {
+        e[k] = xh[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      dot += e[k].x * gv[k].x * xh[k].x + e[k].y * gv[k].y * xh[k].y + e[k].z * gv[k].z * xh[k].z +
+             e[k].w * gv[k].w * xh[k].w;
+    }
+    dot = block_sum256(dot, red);
+    const float mean = dot / (float)d;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int c = (threadIdx.x + 256 * k) * 4;
+      if (c < d) {
+        float4 o = make_float4(r * (e[k].x * gv[k].x - xh[k].x * mean), r * (e[k].y * gv[k].y - xh[k].y * mean),
+                               r * (e[k].z * gv[k].z - xh[k].z * mean), r * (e[k].w * gv[k].w - xh[k].w * mean));
+        if (resid) {
+          const float4 rv = *(const float4*)(resid + (int64_t)m * d + c);
+          o = make_float4(rv.x + o.x, rv.y + o.y, rv.z + o.z, rv.w + o.w);
+        }
+        *(float4*)(dx + (int64_t)m * d + c) = o;
+        dg[k].x += e[k].x * xh[k].x;
+        dg[k].y += e[k].y * xh[k].y;
+        dg[k].z += e[k].z * xh[k].z;
+        dg[k].w += e[k].w * xh[k].w;
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int c = (threadIdx.x + 256 * k) * 4;
+    if (c < d) *(float4*)(part + (int64_t)blockIdx.x * d + c) = dg[k];
+  }
 }
 
 template <typename T>
@@ -142,15 +233,18 @@ __global__ void __launch_bounds__(256) k_dg_reduce(const float* part, T* dg, int
 }
 
 template <typename T>
-void rmsnorm_dg(const float* dy, const float* x, const float* rstd, float* partial, T* dg, int M, int d,
-                hipStream_t s) {
-  const int chunks = cdiv(M, kDgRows);
-  if (chunks == 0) {
-    hipLaunchKernelGGL(k_dg_reduce<T>, dim3(cdiv(d, 256)), dim3(256), 0, s, partial, dg, 0, d);
-    return;
+void rmsnorm_bwd(const float* dy, const float* x, const T* g, const float* rstd, const float* resid, float* dx,
+                 float* partial, T* dg, int M, int d, hipStream_t s) {
+  if (d % 4) throw ApiError{MT_E_INVALID, "RMSNorm needs d_model % 4 == 0"};
+  const int blocks = cdiv(M, kRmsRows);
+  if (blocks > 0) {
+#define L_(V)                                                                                                    \
+  hipLaunchKernelGGL((k_rmsnorm_bwd<T, V>), dim3(blocks), dim3(256), 0, s, dy, x, g, rstd, resid, dx, partial, M, \
+                     d)
+    MT_RMS_DISPATCH(rms_vpt(d), L_)
+#undef L_
   }
-  hipLaunchKernelGGL(k_dg_partial, dim3(cdiv(d, 256), chunks), dim3(256), 0, s, dy, x, rstd, partial, M, d);
-  hipLaunchKernelGGL(k_dg_reduce<T>, dim3(cdiv(d, 256)), dim3(256), 0, s, partial, dg, chunks, d);
+  hipLaunchKernelGGL(k_dg_reduce<T>, dim3(cdiv(d, 256)), dim3(256), 0, s, partial, dg, blocks, d);
 }
 
 // ----------------------------------------------------------------- RoPE --
@@ -203,14 +297,89 @@ __global__ void __launch_bounds__(256) k_rope_qkv(T* qkv, T* qkvT, int64_t ldT, 
   }
 }
 
+// bf16, head_dim 128, 64 whole tokens per block: 16-byte global accesses.
+__device__ inline void unpack8(const uint4 u, float* f) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_to_f32(w[i] & 0xFFFF);
+    f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+}
+__device__ inline uint4 pack8(const float* f) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__global__ void __launch_bounds__(256) k_rope_qkv_bf16(uint16_t* __restrict__ qkv, uint16_t* __restrict__ qkvT,
+                                                       int64_t ldT, const float* __restrict__ cosb,
+                                                       const float* __restrict__ sinb, int T_, int d) {
+  constexpr int HD = 128, H2 = 64;
+  __shared__ float tile[64][129];
+  const int64_t m0 = (int64_t)blockIdx.x * 64;
+  const int part = blockIdx.y / (d / HD);
+  const int head = blockIdx.y % (d / HD);
+  const int64_t col0 = (int64_t)part * d + (int64_t)head * HD;
+  const int64_t ld = 3LL * d;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int id = threadIdx.x + 256 * k;
+    const int r = id >> 4, c8 = id & 15;
+    float f[8];
+    unpack8(*(const uint4*)(qkv + (m0 + r) * ld + col0 + 8 * c8), f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[r][8 * c8 + e] = f[e];
+  }
+  __syncthreads();
+  if (part < 2) {
+#pragma unroll 4
+    for (int idx = threadIdx.x; idx < 64 * H2; idx += 256) {
+      const int r = idx / H2, i = idx % H2;
+      const int t = (int)((m0 + r) % T_);
+      const float cs = cosb[(int64_t)t * H2 + i], sn = sinb[(int64_t)t * H2 + i];
+      const float a = tile[r][i], b = tile[r][i + H2];
+      tile[r][i] = a * cs - b * sn;
+      tile[r][i + H2] = a * sn + b * cs;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int id = threadIdx.x + 256 * k;
+      const int r = id >> 4, c8 = id & 15;
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = tile[r][8 * c8 + e];
+      *(uint4*)(qkv + (m0 + r) * ld + col0 + 8 * c8) = pack8(f);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int id = threadIdx.x + 256 * k;
+    const int c = id >> 3, t8 = id & 7;
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = tile[8 * t8 + e][c];
+    *(uint4*)(qkvT + (col0 + c) * ldT + m0 + 8 * t8) = pack8(f);
+  }
+}
+
 template <typename T>
 void rope_qkv_fwd(T* qkv, T* qkvT, int64_t ldT, const float* cosb, const float* sinb, int M, int T_, int d, int hd,
                   hipStream_t s) {
   if (M <= 0) return;
+  if (std::is_same<T, uint16_t>::value && hd == 128 && M % 64 == 0 && ldT % 8 == 0) {
+    hipLaunchKernelGGL(k_rope_qkv_bf16, dim3(M / 64, 3 * (d / hd)), dim3(256), 0, s, (uint16_t*)qkv, (uint16_t*)qkvT,
+                       ldT, cosb, sinb, T_, d);
+    return;
+  }
   hipLaunchKernelGGL(k_rope_qkv<T>, dim3(cdiv(M, 64), 3 * (d / hd)), dim3(256), 0, s, qkv, qkvT, ldT, cosb, sinb, M,
                      T_, d, hd);
 }
 
+// Inverse rotation on the transposed layout: one thread per (pair, 8 tokens)
+// when the token count is a multiple of 8, else per (pair, token).
 template <typename T>
 __global__ void __launch_bounds__(256) k_rope_bwd_T(T* x, int64_t ldT, const float* cosb, const float* sinb, int M,
                                                     int T_, int d, int hd) {
@@ -229,52 +398,97 @@ __global__ void __launch_bounds__(256) k_rope_bwd_T(T* x, int64_t ldT, const flo
   x[rb * ldT + m] = stf<T>(b * cs - a * sn);
 }
 
+__global__ void __launch_bounds__(256) k_rope_bwd_T8(uint16_t* x, int64_t ldT, const float* cosb, const float* sinb,
+                                                     int M, int T_, int d, int hd) {
+  const int64_t m = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (m >= M) return;
+  const int pr = blockIdx.y;
+  const int h2 = hd / 2;
+  const int part = pr / (d / 2);
+  const int rem = pr % (d / 2);
+  const int head = rem / h2, i = rem % h2;
+  const int64_t ra = (int64_t)part * d + (int64_t)head * hd + i, rb = ra + h2;
+  float a[8], b[8], oa[8], ob[8];
+  unpack8(*(const uint4*)(x + ra * ldT + m), a);
+  unpack8(*(const uint4*)(x + rb * ldT + m), b);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int t = (int)((m + e) % T_);
+    const float cs = cosb[(int64_t)t * h2 + i], sn = sinb[(int64_t)t * h2 + i];
+    oa[e] = a[e] * cs + b[e] * sn;
+    ob[e] = b[e] * cs - a[e] * sn;
+  }
+  *(uint4*)(x + ra * ldT + m) = pack8(oa);
+  *(uint4*)(x + rb * ldT + m) = pack8(ob);
+}
+
 template <typename T>
 void rope_bwd_T(T* dqkvT, int64_t ldT, const float* cosb, const float* sinb, int M, int T_, int d, int hd,
                 hipStream_t s) {
   if (M <= 0) return;
+  if (std::is_same<T, uint16_t>::value && M % 8 == 0 && ldT % 8 == 0) {
+    hipLaunchKernelGGL(k_rope_bwd_T8, dim3(cdiv(M / 8, 256), d), dim3(256), 0, s, (uint16_t*)dqkvT, ldT, cosb, sinb,
+                       M, T_, d, hd);
+    return;
+  }
   hipLaunchKernelGGL(k_rope_bwd_T<T>, dim3(cdiv(M, 256), d), dim3(256), 0, s, dqkvT, ldT, cosb, sinb, M, T_, d, hd);
 }
 
 // --------------------------------------------------------------- SwiGLU --
 __device__ inline float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
+__device__ inline float silu_(float g) { return g / (1.0f + expf(-g)); }
 
+// Four outputs per thread (F % 4 == 0): gate g = gu[m][j], up u = gu[m][F+j].
 template <typename T>
-__global__ void __launch_bounds__(256) k_swiglu_fwd(const T* gu, T* y, int64_t n, int F) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    int64_t m = i / F, j = i % F;
-    float g = ldf(gu[m * 2 * F + j]), u = ldf(gu[m * 2 * F + F + j]);
-    y[i] = stf<T>(g / (1.0f + expf(-g)) * u);
+__global__ void __launch_bounds__(256) k_swiglu_fwd(const T* __restrict__ gu, T* __restrict__ y, int64_t n4, int F) {
+  const int F4 = F / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    const int64_t m = i / F4, j = (i % F4) * 4;
+    const float4 g = V4<T>::ld(gu + m * 2 * F + j), u = V4<T>::ld(gu + m * 2 * F + F + j);
+    V4<T>::st(y + m * F + j, make_float4(silu_(g.x) * u.x, silu_(g.y) * u.y, silu_(g.z) * u.z, silu_(g.w) * u.w));
   }
 }
 
 template <typename T>
 void swiglu_fwd(const T* gu, T* y, int M, int F, hipStream_t s) {
-  int64_t n = (int64_t)M * F;
-  if (n <= 0) return;
-  int blocks = (int)std::min<int64_t>((n + 255) / 256, 65536);
-  hipLaunchKernelGGL(k_swiglu_fwd<T>, dim3(blocks), dim3(256), 0, s, gu, y, n, F);
+  if (F % 4) throw ApiError{MT_E_INVALID, "SwiGLU needs d_ff % 4 == 0"};
+  const int64_t n4 = (int64_t)M * F / 4;
+  if (n4 <= 0) return;
+  const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 65536);
+  hipLaunchKernelGGL(k_swiglu_fwd<T>, dim3(blocks), dim3(256), 0, s, gu, y, n4, F);
+}
+
+__device__ inline void swiglu_grad1(float e, float g, float u, float* dg, float* du) {
+  const float sg = sigmoidf_(g);
+  *dg = e * u * (sg * (1.0f + g * (1.0f - sg)));
+  *du = e * silu_(g);
 }
 
 template <typename T>
-__global__ void __launch_bounds__(256) k_swiglu_bwd(const T* dy, const T* gu, T* dgu, int64_t n, int F) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    int64_t m = i / F, j = i % F;
-    float g = ldf(gu[m * 2 * F + j]), u = ldf(gu[m * 2 * F + F + j]);
-    float e = ldf(dy[i]);
-    float sg = sigmoidf_(g);
-    float silu = g / (1.0f + expf(-g));
-    dgu[m * 2 * F + j] = stf<T>(e * u * (sg * (1.0f + g * (1.0f - sg))));
-    dgu[m * 2 * F + F + j] = stf<T>(e * silu);
+__global__ void __launch_bounds__(256) k_swiglu_bwd(const T* __restrict__ dy, const T* __restrict__ gu,
+                                                    T* __restrict__ dgu, int64_t n4, int F) {
+  const int F4 = F / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    const int64_t m = i / F4, j = (i % F4) * 4;
+    const float4 g = V4<T>::ld(gu + m * 2 * F + j), u = V4<T>::ld(gu + m * 2 * F + F + j);
+    const float4 e = V4<T>::ld(dy + m * F + j);
+    float4 a, b;
+    swiglu_grad1(e.x, g.x, u.x, &a.x, &b.x);
+    swiglu_grad1(e.y, g.y, u.y, &a.y, &b.y);
+    swiglu_grad1(e.z, g.z, u.z, &a.z, &b.z);
+    swiglu_grad1(e.w, g.w, u.w, &a.w, &b.w);
+    V4<T>::st(dgu + m * 2 * F + j, a);
+    V4<T>::st(dgu + m * 2 * F + F + j, b);
   }
 }
 
 template <typename T>
 void swiglu_bwd(const T* dy, const T* gu, T* dgu, int M, int F, hipStream_t s) {
-  int64_t n = (int64_t)M * F;
-  if (n <= 0) return;
-  int blocks = (int)std::min<int64_t>((n + 255) / 256, 65536);
-  hipLaunchKernelGGL(k_swiglu_bwd<T>, dim3(blocks), dim3(256), 0, s, dy, gu, dgu, n, F);
+  if (F % 4) throw ApiError{MT_E_INVALID, "SwiGLU needs d_ff % 4 == 0"};
+  const int64_t n4 = (int64_t)M * F / 4;
+  if (n4 <= 0) return;
+  const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 65536);
+  hipLaunchKernelGGL(k_swiglu_bwd<T>, dim3(blocks), dim3(256), 0, s, dy, gu, dgu, n4, F);
 }
 
 // -------------------------------------------------------- cross-entropy --
@@ -346,9 +560,50 @@ __global__ void __launch_bounds__(256) k_transpose(const T* in, int64_t ld_in, T
   }
 }
 
+// bf16 64x64 tile with 16-byte global loads and stores (8 elements per
+// access); rows and columns of the tile that fall outside R x C are skipped
+// per 8-element group, so R, C, ld_in, ld_out must be multiples of 8.
+__global__ void __launch_bounds__(256) k_transpose_bf16(const uint16_t* __restrict__ in, int64_t ld_in,
+                                                        uint16_t* __restrict__ out, int64_t ld_out, int R, int C) {
+  __shared__ uint16_t tile[64][66];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int id = threadIdx.x + 256 * k;
+    const int r = id >> 3, c8 = (id & 7) * 8;
+    if (r0 + r < R && c0 + c8 < C) {
+      const uint4 u = *(const uint4*)(in + (r0 + r) * ld_in + c0 + c8);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        tile[r][c8 + 2 * i] = (uint16_t)(w[i] & 0xFFFF);
+        tile[r][c8 + 2 * i + 1] = (uint16_t)(w[i] >> 16);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int id = threadIdx.x + 256 * k;
+    const int c = id >> 3, r8 = (id & 7) * 8;
+    if (c0 + c < C && r0 + r8 < R) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = (uint32_t)tile[r8 + 2 * i][c] | ((uint32_t)tile[r8 + 2 * i + 1][c] << 16);
+      *(uint4*)(out + (c0 + c) * ld_out + r0 + r8) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
 template <typename T>
 void transpose(const T* in, int64_t ld_in, T* out, int64_t ld_out, int R, int C, hipStream_t s) {
   if (R <= 0 || C <= 0) return;
+  if (std::is_same<T, uint16_t>::value && R % 8 == 0 && C % 8 == 0 && ld_in % 8 == 0 && ld_out % 8 == 0 &&
+      ((uintptr_t)in & 15) == 0 && ((uintptr_t)out & 15) == 0) {
+    hipLaunchKernelGGL(k_transpose_bf16, dim3(cdiv(C, 64), cdiv(R, 64)), dim3(256), 0, s, (const uint16_t*)in, ld_in,
+                       (uint16_t*)out, ld_out, R, C);
+    return;
+  }
   hipLaunchKernelGGL(k_transpose<T>, dim3(cdiv(C, 64), cdiv(R, 64)), dim3(256), 0, s, in, ld_in, out, ld_out, R, C);
 }
 
@@ -392,9 +647,8 @@ void fill_u32(void* p, uint32_t value, size_t n_words, hipStream_t s) {
   template void embed_fwd<T>(const int32_t*, const T*, float*, int, int, hipStream_t);                          \
   template void embed_bwd<T>(const float*, const int32_t*, const int32_t*, T*, int, int, hipStream_t);          \
   template void rmsnorm_fwd<T>(const float*, const T*, T*, float*, int, int, float, hipStream_t);               \
-  template void rmsnorm_bwd<T>(const float*, const float*, const T*, const float*, const float*, float*, int, int, \
-                               hipStream_t);                                                                    \
-  template void rmsnorm_dg<T>(const float*, const float*, const float*, float*, T*, int, int, hipStream_t);      \
+  template void rmsnorm_bwd<T>(const float*, const float*, const T*, const float*, const float*, float*, float*, T*, \
+                               int, int, hipStream_t);                                                          \
   template void rope_qkv_fwd<T>(T*, T*, int64_t, const float*, const float*, int, int, int, int, hipStream_t);  \
   template void rope_bwd_T<T>(T*, int64_t, const float*, const float*, int, int, int, int, hipStream_t);        \
   template void swiglu_fwd<T>(const T*, T*, int, int, hipStream_t);                                             \

@@ -334,8 +334,7 @@ struct Model {
     transpose<T>(a.h2, d, ws.tmpT, Mp, M, d, sc);
     gemm<T>(ws.dguT, Mp, ws.tmpT, Mp, g.gu, d, nullptr, 0, 2 * F, d, M, EPI_STORE);
     gemm<T>(ws.dgu, 2 * F, wt_.gu, 2 * F, ws.dh, d, nullptr, 0, M, d, 2 * F, EPI_F32);
-    rmsnorm_bwd<T>(ws.dh, a.x1, w.fnorm, a.r2, dx2, ws.dx1, M, d, sc);
-    rmsnorm_dg<T>(ws.dh, a.x1, a.r2, ws.part, g.fnorm, M, d, sc);
+    rmsnorm_bwd<T>(ws.dh, a.x1, w.fnorm, a.r2, dx2, ws.dx1, ws.part, g.fnorm, M, d, sc);
     // attention output projection
     cast_transpose<T>(ws.dx1, ws.dxb, ws.dxbT, Mp, M, d, sc);
     transpose<T>(a.o, d, ws.tmpT, Mp, M, d, sc);
@@ -354,8 +353,7 @@ struct Model {
     transpose<T>(a.h, d, ws.tmpT, Mp, M, d, sc);
     gemm<T>(ws.dqkvT, Mp, ws.tmpT, Mp, g.qkv, d, nullptr, 0, 3 * d, d, M, EPI_STORE);
     gemm<T>(ws.dqkv, 3 * d, wt_.qkv, 3 * d, ws.dh, d, nullptr, 0, M, d, 3 * d, EPI_F32);
-    rmsnorm_bwd<T>(ws.dh, x, w.anorm, a.r1, ws.dx1, dx_out, M, d, sc);
-    rmsnorm_dg<T>(ws.dh, x, a.r1, ws.part, g.anorm, M, d, sc);
+    rmsnorm_bwd<T>(ws.dh, x, w.anorm, a.r1, ws.dx1, dx_out, ws.part, g.anorm, M, d, sc);
   }
 
   // Final norm, logits, loss, and the head's backward.  Returns dx^L in dx_out.
@@ -381,8 +379,7 @@ struct Model {
     T* whT = (T*)wt;
     transpose<T>(wh, d, whT, V, V, d, sc);
     gemm<T>(hw.dlogits, V, whT, V, ws.dh, d, nullptr, 0, M, d, V, EPI_F32);
-    rmsnorm_bwd<T>(ws.dh, xL, fin, hw.rz, nullptr, dx_out, M, d, sc);
-    rmsnorm_dg<T>(ws.dh, xL, hw.rz, ws.part, gfin, M, d, sc);
+    rmsnorm_bwd<T>(ws.dh, xL, fin, hw.rz, nullptr, dx_out, ws.part, gfin, M, d, sc);
   }
 
   // ------------------------------------------------------------ step --

@@ -28,16 +28,13 @@ template <typename T>
 void embed_bwd(const float* dx, const int32_t* order, const int32_t* seg, T* dE, int V, int d, hipStream_t s);
 template <typename T>
 void rmsnorm_fwd(const float* x, const T* g, T* y, float* rstd, int M, int d, float eps, hipStream_t s);
-// dx = resid + r*(dy*g - xh*mean(dy*g*xh)), xh = x*r; resid may be null.
-template <typename T>
-void rmsnorm_bwd(const float* dy, const float* x, const T* g, const float* rstd, const float* resid, float* dx,
-                 int M, int d, hipStream_t s);
-// dg = sum_rows dy*x*r (two deterministic passes through `partial`,
-// which holds rmsnorm_dg_partial_elems(M, d) floats), written as T.
+// dx = resid + r*(dy*g - xh*mean(dy*g*xh)), xh = x*r (resid may be null),
+// and dg = sum_rows dy*xh written as T: per-block partial sums in `partial`
+// (rmsnorm_dg_partial_elems(M, d) floats), then added in block order.
 size_t rmsnorm_dg_partial_elems(int M, int d);
 template <typename T>
-void rmsnorm_dg(const float* dy, const float* x, const float* rstd, float* partial, T* dg, int M, int d,
-                hipStream_t s);
+void rmsnorm_bwd(const float* dy, const float* x, const T* g, const float* rstd, const float* resid, float* dx,
+                 float* partial, T* dg, int M, int d, hipStream_t s);
 // Token-major transposed buffers [C x M] use a padded row stride
 // (token_ld(M) >= M): a row stride that is a large power of two puts a
 // tile's rows on the same memory channels.

@@ -12,6 +12,8 @@ int validate_config(const mt_config& c, std::string* why) {
   if (c.n_heads * c.head_dim != c.d_model) return bad("n_heads * head_dim must equal d_model");
   if (c.head_dim % 2) return bad("head_dim must be even");
   if (c.d_ff < 1 || c.vocab < 2 || c.batch < 1 || c.seq_len < 2) return bad("bad sizes");
+  if (c.d_model % 4 || c.d_ff % 4) return bad("d_model and d_ff must be multiples of 4");
+  if (c.d_model > 16384) return bad("d_model > 16384");
   if (c.store_dtype != MT_F32 && c.store_dtype != MT_BF16) return bad("store_dtype");
   if (c.mode < MT_STREAMED || c.mode > MT_RESIDENT) return bad("mode");
   if (c.store_dtype == MT_BF16) {
