@@ -435,6 +435,178 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_v3(const uint16_t* __restr
       }
 }
 
+// ------------------------------------------------------------------ v4 --
+// 256x256x64 macro tile, two LDS stages of 64 KiB (A and B tiles of 256 rows
+// x 128 B), 4 waves (2 x 2) each owning 128x128 as 4x4 accumulators of
+// v_mfma_f32_32x32x16_bf16.  128-byte row segments make every global request
+// a whole cache line.  Chunk c of row r sits at c ^ ((r >> 1) & 7), so the 16
+// lanes a 16-byte LDS read serves per cycle (16 consecutive rows, one
+// logical chunk) fall on 16 disjoint bank groups.  Per K step k:
+//   sub-steps 0,1: MFMAs interleaved with the direct loads of step k+1 and
+//                  the fragment reads of sub-steps 1,2;
+//   sub-step 2:    MFMAs with the fragment reads of sub-step 3;
+//   barrier:       step k+1 has landed and every wave has its step-k data;
+//   sub-step 3:    MFMAs with the fragment reads of step k+1, sub-step 0.
+constexpr int BK4 = 64;
+constexpr int STAGE4 = 2 * BM * BK4 * 2;  // 64 KiB
+
+__device__ inline int swz128(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+
+template <int EPI, int DMA>
+__global__ void __launch_bounds__(256, 1) k_gemm_bf16_v4(const uint16_t* __restrict__ A, int64_t lda,
+                                                       const uint16_t* __restrict__ B, int64_t ldb, void* C,
+                                                       int64_t ldc, const float* R, int64_t ldr, int M, int N, int K,
+                                                       int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE4];
+  const int ntiles = tiles_m * tiles_n;
+  int pid = blockIdx.x;
+  const int per_xcd = ntiles / 8;
+  if (pid < per_xcd * 8) pid = (pid % 8) * per_xcd + pid / 8;
+  const int GROUP = 8;
+  const int group_size = GROUP * tiles_n;
+  const int g = pid / group_size;
+  const int first_m = g * GROUP;
+  const int gm_cnt = min(tiles_m - first_m, GROUP);
+  const int tm = first_m + (pid % group_size) % gm_cnt;
+  const int tn = (pid % group_size) / gm_cnt;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int arows = (int)min<int64_t>(BM, M - m0), brows = (int)min<int64_t>(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t arsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * lda), 0, (int)(arows * lda * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t brsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(B + n0 * ldb), 0, (int)(brows * ldb * 2), 0x00020000);
+  const int nk = K / BK4;
+  // Direct load i (0..15) of a step: operand i/8, kilobyte j = wave*8 + i%8,
+  // rows 8j .. 8j+7; lane l reads row 8j + l/8, logical chunk
+  // (l%8) ^ ((row >> 1) & 7).
+  auto issue_one = [&](int kt, int i) {
+    uint8_t* base = smem + (kt & 1) * STAGE4 + (i >> 3) * (STAGE4 / 2);
+    const int j = wave * 8 + (i & 7);
+    const int r = 8 * j + (lane >> 3);
+    const int lc = (lane & 7) ^ ((r >> 1) & 7);
+    const int kbytes = kt * BK4 * 2;
+    if (i < 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void_t*)(base + j * 1024), 16,
+                                               (int)((r * lda + 8 * lc) * 2), kbytes, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(brsrc, (lds_void_t*)(base + j * 1024), 16,
+                                               (int)((r * ldb + 8 * lc) * 2), kbytes, 0, 0);
+  };
+
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  bf16x8_t a[2][4], b[2][4];
+  auto read_one = [&](int kt, int ks, int set, int i) {
+    const uint8_t* As = smem + (kt & 1) * STAGE4;
+    const uint8_t* Bs = As + STAGE4 / 2;
+    const int c = ks * 2 + (lane >> 5);
+    if (i < 4)
+      a[set][i] = *(const bf16x8_t*)(As + swz128(wm + 32 * i + (lane & 31), c));
+    else
+      b[set][i & 3] = *(const bf16x8_t*)(Bs + swz128(wn + 32 * (i & 3) + (lane & 31), c));
+  };
+  auto mfma16 = [&](int set, int p) {
+    const int i = p >> 2, j = p & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[set][i], b[set][j], acc[i][j], 0, 0, 0);
+  };
+
+  // DMA == 0: step k+1's loads ride on sub-steps 0 and 1 of step k.
+  // DMA == 1: step k+2's loads ride on sub-step 3 of step k (its buffer was
+  //           freed by step k's barrier), doubling the prefetch distance.
+  // DMA == 2: as 1, half of them on sub-step 3 of step k, half on
+  //           sub-step 0 of step k+1.
+#pragma unroll
+  for (int i = 0; i < 16; ++i) issue_one(0, i);
+  if (DMA != 0 && nk > 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) issue_one(1, i);
+  }
+  if (DMA != 0 && nk > 1)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) read_one(0, 0, 0, i);
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool more = kt + 1 < nk;
+    const int kn = more ? kt + 1 : kt;
+    const bool more2 = kt + 2 < nk;
+    // sub-step 0 (set 0)
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      mfma16(0, p);
+      if (p & 1)
+        read_one(kt, 1, 1, p >> 1);
+      else if (DMA == 0 && more)
+        issue_one(kn, p >> 1);
+      else if (DMA == 2 && more && kt >= 1)
+        issue_one(kn, 8 + (p >> 1));  // second half of step k+1's loads (first half issued in step k-1)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // sub-step 1 (set 1)
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      mfma16(1, p);
+      if (p & 1)
+        read_one(kt, 2, 0, p >> 1);
+      else if (DMA == 0 && more)
+        issue_one(kn, 8 + (p >> 1));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // sub-step 2 (set 0)
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      mfma16(0, p);
+      if (p & 1) read_one(kt, 3, 1, p >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Every load still in flight here belongs to step k+1, which sub-step 3
+    // starts reading: wait for all of them, then the barrier.
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    // sub-step 3 (set 1)
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      mfma16(1, p);
+      if ((p & 1) && more) read_one(kn, 0, 0, p >> 1);
+      if (DMA == 1 && more2) issue_one(kt + 2, p);
+      if (DMA == 2 && more2 && !(p & 1)) issue_one(kt + 2, p >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int64_t gm = m0 + wm + 32 * i + row;
+        const int64_t gn = n0 + wn + 32 * j + (lane & 31);
+        if (gm < M && gn < N) {
+          const float v = acc[i][j][r];
+          if (EPI == EPI_STORE)
+            ((uint16_t*)C)[gm * ldc + gn] = f32_to_bf16(v);
+          else if (EPI == EPI_F32)
+            ((float*)C)[gm * ldc + gn] = v;
+          else
+            ((float*)C)[gm * ldc + gn] = R[gm * ldr + gn] + v;
+        }
+      }
+}
+
 // fp32 SIMT GEMM for the all-fp32 store: 64x64 tile, 4x4 per thread.
 template <int EPI>
 __global__ void __launch_bounds__(256) k_gemm_f32(const float* __restrict__ A, int64_t lda, const float* __restrict__ B,
@@ -477,7 +649,16 @@ static int gemm_variant() {
   static int v = -1;
   if (v < 0) {
     const char* e = getenv("MT_GEMM_VARIANT");
-    v = e ? atoi(e) : 3;
+    v = e ? atoi(e) : 4;
+  }
+  return v;
+}
+
+static int gemm_dma_mode() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("MT_GEMM_DMA");
+    v = e ? atoi(e) : 2;
   }
   return v;
 }
@@ -491,7 +672,29 @@ void gemm_nt<uint16_t>(const uint16_t* A, int64_t lda, const uint16_t* B, int64_
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const dim3 grid(tiles_m * tiles_n);
   const int variant = gemm_variant();
-  if (K % BK3 == 0 && K >= 2 * BK3 && (variant == 3 || variant == 4 || variant == 5)) {
+  if (K % BK4 == 0 && K >= BK4 && variant == 4) {
+    const dim3 block(256);
+#define MT_LAUNCH_V4(E, D) \
+  hipLaunchKernelGGL((k_gemm_bf16_v4<E, D>), grid, block, 0, s, A, lda, B, ldb, C, ldc, R, ldr, M, N, K, tiles_m, tiles_n)
+    const int dm = gemm_dma_mode();
+#define MT_V4_EPI(D)                                    \
+  switch (epi) {                                        \
+    case EPI_STORE: MT_LAUNCH_V4(EPI_STORE, D); break;   \
+    case EPI_F32: MT_LAUNCH_V4(EPI_F32, D); break;       \
+    case EPI_ADD_F32: MT_LAUNCH_V4(EPI_ADD_F32, D); break; \
+  }
+    if (dm == 1) {
+      MT_V4_EPI(1)
+    } else if (dm == 2) {
+      MT_V4_EPI(2)
+    } else {
+      MT_V4_EPI(0)
+    }
+#undef MT_V4_EPI
+#undef MT_LAUNCH_V4
+    return;
+  }
+  if (K % BK3 == 0 && K >= 2 * BK3 && (variant >= 3 && variant <= 5)) {
     const dim3 block(256);
 #define MT_LAUNCH_V3(E, S) \
   hipLaunchKernelGGL((k_gemm_bf16_v3<E, S>), grid, block, 0, s, A, lda, B, ldb, C, ldc, R, ldr, M, N, K, tiles_m, tiles_n)
