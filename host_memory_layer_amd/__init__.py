@@ -2,7 +2,7 @@
 
 Argument marshalling only: every step of the training step runs in the HIP
 library (include/mt.h, include/mt_kernels.h).  PyTorch provides the device
-arena and the three streams; the pinned host store comes from the library.
+arena and the compute stream; the pinned host store comes from the library.
 The binding raises if the library has not been built — there is no
 fallback path.
 """
@@ -81,7 +81,7 @@ _SIGS = {
                                             ctypes.c_void_p, ctypes.c_size_t]),
     "mt_store_step": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]),
     "mt_create_model": (ctypes.c_int, [ctypes.POINTER(MtConfig), ctypes.c_void_p, ctypes.c_size_t,
-                                       ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p)]),
+                                       ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]),
     "mt_bind_host_store": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                           ctypes.c_size_t]),
     "mt_train_step": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
@@ -278,7 +278,7 @@ class HostStore:
 
 
 class Model:
-    """A model handle bound to a host store; device arena and streams from torch."""
+    """A model handle bound to a host store; device arena and compute stream from torch."""
 
     def __init__(self, cfg: MtConfig, store: HostStore, device: str = "cuda:0"):
         import torch
@@ -288,11 +288,11 @@ class Model:
         self.device = torch.device(device)
         nbytes = device_bytes(cfg)
         self.arena = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
-        self.streams = [torch.cuda.Stream(device=self.device) for _ in range(3)]
-        handles = (ctypes.c_void_p * 3)(*[s.cuda_stream for s in self.streams])
+        self.stream = torch.cuda.Stream(device=self.device)  # compute
         h = ctypes.c_void_p()
         torch.cuda.synchronize(self.device)
-        check(lib().mt_create_model(ctypes.byref(cfg), self.arena.data_ptr(), nbytes, handles, ctypes.byref(h)))
+        check(lib().mt_create_model(ctypes.byref(cfg), self.arena.data_ptr(), nbytes, self.stream.cuda_stream,
+                                    ctypes.byref(h)))
         self.handle = h.value
         check(lib().mt_bind_host_store(self.handle, store.ptr, store.nbytes, store.opt_ptr, store.opt_nbytes))
 

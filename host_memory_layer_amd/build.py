@@ -26,7 +26,7 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I" + INCL
 GXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-I" + INCLUDE, "-I" + CSRC]
 
 HIP_SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "engine.hip"]
-HIPCC_HOST_SOURCES = ["store.cpp", "api.cpp", "kernel_api.cpp"]
+HIPCC_HOST_SOURCES = ["store.cpp", "api.cpp", "kernel_api.cpp", "dma.cpp"]
 GXX_SOURCES = ["adam.cpp"]
 
 
@@ -61,7 +61,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
             if verbose and out.strip():
                 print(out)
     tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs + ["-lpthread"])
+    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs + ["-L/opt/rocm/lib", "-lhsa-runtime64", "-lpthread"])
     os.replace(tmp, LIB)
     return LIB
 

@@ -185,10 +185,10 @@ int mt_store_step(const void* host_base, int64_t* t) {
   });
 }
 
-int mt_create_model(const mt_config* cfg, void* dev_arena, size_t arena_bytes, void* const streams[3], void** out) {
+int mt_create_model(const mt_config* cfg, void* dev_arena, size_t arena_bytes, void* stream, void** out) {
   return guarded([&] {
     if (!cfg || !out) throw ApiError{MT_E_INVALID, "null argument"};
-    *out = create_model(cfg, dev_arena, arena_bytes, streams);
+    *out = create_model(cfg, dev_arena, arena_bytes, stream);
     return MT_OK;
   });
 }

@@ -6,7 +6,7 @@
 namespace mt {
 
 struct Model;
-Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void* const streams[3]);
+Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void* stream);
 void destroy_model(Model* m);
 uint64_t device_bytes_for(const mt_config& cfg);
 int bind_store(Model* m, void* host, size_t bytes, void* opt, size_t opt_bytes);

@@ -26,6 +26,7 @@
 #include <vector>
 
 #include "adam.h"
+#include "dma.h"
 #include "engine.h"
 #include "kernels.h"
 #include "store.h"
@@ -101,7 +102,7 @@ struct Model {
 
   uint8_t* arena = nullptr;
   size_t arena_bytes = 0;
-  hipStream_t sp, sc, so;
+  hipStream_t sc;  // compute stream
   uint8_t* host = nullptr;  // DMA part: header, [W | G] per block (pinned)
   uint8_t* hopt = nullptr;  // optimizer part: [m | v] per block
 
@@ -121,7 +122,9 @@ struct Model {
 
   // events per use: 0..L+1 forward (embed, layers, head), then backward L..1, 0
   int n_uses;
-  std::vector<hipEvent_t> ev_h2d_s, ev_h2d_e, ev_wait, ev_c_s, ev_c_e, ev_d2h_s, ev_d2h_e;
+  std::vector<hipEvent_t> ev_c_s, ev_c_e;  // compute of each use: start, end
+  std::vector<hipEvent_t> ev_slot_free;    // MT_FLAG_POISON: slot NaN-filled, ready for the prefetch of a use
+  hipEvent_t ev_h2d_s, ev_h2d_e, ev_d2h_s, ev_d2h_e;  // resident schedule: all uploads, all offloads
   hipEvent_t ev_loss, ev_start, ev_end;
   std::vector<hipEvent_t> kev;  // kernel timing pairs
   std::vector<std::pair<double, int>> kev_meta;  // flops, kind (0 gemm, 1 attention)
@@ -409,7 +412,7 @@ struct Model {
   }
 
   template <typename T>
-  void step_streamed(hipStream_t P, hipStream_t O);
+  void step_streamed(bool serialize);
   template <typename T>
   void step_resident();
   int train_step(const int32_t* tokens);
@@ -440,6 +443,14 @@ struct Model {
     q_cv.notify_all();
   }
   void adam_worker(int64_t t, double* adam_total, double* adam_tail, std::atomic<bool>* device_done);
+
+  // Streamed schedules: weight prefetches and gradient offloads run on two
+  // SDMA engines, each fed in order by a worker thread (dma.h).  The
+  // enqueueing thread enqueues a block's compute once its weights have
+  // arrived, and reuses a gradient slot once the offload that read it is done.
+  std::unique_ptr<DmaEngines> dma;
+  std::unique_ptr<TransferQueue> xq_in, xq_out;
+  std::vector<double> h2d_host_ms, d2h_host_ms;  // per use: copy time (host clock)
 };
 
 // ---------------------------------------------------------------- Adam --
@@ -465,7 +476,7 @@ void Model::adam_worker(int64_t t, double* adam_total, double* adam_tail, std::a
         ev = q_events[next];
         ++next;
       }
-      MT_HIP(hipEventSynchronize(ev));
+      if (ev) MT_HIP(hipEventSynchronize(ev));
       if (nonfinite) continue;
       auto t0 = std::chrono::steady_clock::now();
       const mt_block_desc& b = blocks[blk];
@@ -486,47 +497,62 @@ void Model::adam_worker(int64_t t, double* adam_total, double* adam_tail, std::a
 // Streamed (and serialized) schedule.  Uses: u = j for the forward of block
 // j (0 embed, 1..L layers, L+1 head, whose use also runs the head backward);
 // u = L+2+i for the backward of block L-i (i = 0..L-1: layers), and
-// u = 2L+2 for the embedding backward.  Block j always uses weight slot j%2.
+// u = 2L+2 for the embedding backward.  Block j always uses weight slot j%2,
+// and consecutive backward uses alternate between the two gradient slots.
+// A slot's next prefetch starts when the compute of its last use has ended;
+// a block's compute is enqueued once its prefetch is done.  The serialized
+// schedule lets nothing overlap: every copy starts after all compute
+// enqueued so far and ends before more work is enqueued.
 template <typename T>
-void Model::step_streamed(hipStream_t P, hipStream_t O) {
+void Model::step_streamed(bool serialize) {
   const bool poison = cfg.flags & MT_FLAG_POISON;
   const uint32_t nan_word = E == 2 ? 0x7FC07FC0u : 0x7FC00000u;
-  std::vector<int> slot_last_use(2, -1);  // use that last bound each slot
-  std::vector<int> gslot_last(2, -1);     // use that last filled each grad slot
+  std::vector<int> slot_last_use(2, -1);  // use that last bound each weight slot
+  std::vector<int> fetch_job(n_uses, -1);  // prefetch job of each use
+  std::vector<int> gslot_last(2, -1);     // offload job that last read each grad slot
   int gcount = 0;
+  int last_out = -1;
 
   auto fetch = [&](int u, int j) {
     const int s = j % 2;
-    if (slot_last_use[s] >= 0) MT_HIP(hipStreamWaitEvent(P, ev_c_e[slot_last_use[s]], 0));
-    if (poison) fill_u32(wslot[s], nan_word, slot_bytes / 4, P);
-    MT_HIP(hipEventRecord(ev_h2d_s[u], P));
-    MT_HIP(hipMemcpyAsync(wslot[s], host + blocks[j].w_off, blocks[j].w_bytes, hipMemcpyHostToDevice, P));
-    MT_HIP(hipEventRecord(ev_h2d_e[u], P));
+    hipEvent_t ready = slot_last_use[s] >= 0 ? ev_c_e[slot_last_use[s]] : nullptr;
+    if (poison) {
+      // NaN-fill the slot on the compute stream, after its last use.
+      fill_u32(wslot[s], nan_word, slot_bytes / 4, sc);
+      MT_HIP(hipEventRecord(ev_slot_free[u], sc));
+      ready = ev_slot_free[u];
+    }
+    if (serialize) {
+      MT_HIP(hipStreamSynchronize(sc));
+      ready = nullptr;
+    }
+    fetch_job[u] = xq_in->push({u, j, ready, wslot[s], host + blocks[j].w_off, (size_t)blocks[j].w_bytes});
+    if (serialize) xq_in->wait(fetch_job[u]);
   };
-  auto begin = [&](int u, int fetched_use) {
-    MT_HIP(hipEventRecord(ev_wait[u], sc));
-    if (fetched_use >= 0) MT_HIP(hipStreamWaitEvent(sc, ev_h2d_e[fetched_use], 0));
+  auto begin = [&](int u) {
+    if (fetch_job[u] >= 0) xq_in->wait(fetch_job[u]);
     MT_HIP(hipEventRecord(ev_c_s[u], sc));
   };
   auto end = [&](int u, int j) {
     MT_HIP(hipEventRecord(ev_c_e[u], sc));
     slot_last_use[j % 2] = u;
   };
-  // Grad slot for a backward use: wait until its previous offload finished.
-  auto grad_slot = [&](int u) -> int {
+  // Grad slot for a backward use: the offload that last read it has finished.
+  auto grad_slot = [&]() -> int {
     const int g = gcount % 2;
-    if (gslot_last[g] >= 0) MT_HIP(hipStreamWaitEvent(sc, ev_d2h_e[gslot_last[g]], 0));
-    (void)u;
+    if (gslot_last[g] >= 0) xq_out->wait(gslot_last[g]);
     return g;
   };
   auto offload = [&](int u, int j, int g) {
-    MT_HIP(hipStreamWaitEvent(O, ev_c_e[u], 0));
-    MT_HIP(hipEventRecord(ev_d2h_s[u], O));
-    MT_HIP(hipMemcpyAsync(host + blocks[j].g_off, gslot[g], blocks[j].w_bytes, hipMemcpyDeviceToHost, O));
-    MT_HIP(hipEventRecord(ev_d2h_e[u], O));
-    gslot_last[g] = u;
+    hipEvent_t ready = ev_c_e[u];
+    if (serialize) {
+      MT_HIP(hipStreamSynchronize(sc));
+      ready = nullptr;
+    }
+    last_out = xq_out->push({u, j, ready, host + blocks[j].g_off, gslot[g], (size_t)blocks[j].w_bytes});
+    gslot_last[g] = last_out;
     ++gcount;
-    push_adam(j, ev_d2h_e[u]);
+    if (serialize) xq_out->wait(last_out);
   };
 
   BwdWs<T> ws = bwdws<T>();
@@ -535,15 +561,13 @@ void Model::step_streamed(hipStream_t P, hipStream_t O) {
   for (int j = 0; j <= L + 1; ++j) {
     if (j + 1 <= L + 1) fetch(j + 1, j + 1);
     if (j <= L) {
-      begin(j, j);
+      begin(j);
       compute_block_fwd<T>(j, wslot[j % 2]);
       end(j, j);
     } else {
       // head: forward, loss, backward; weights stay bound for both
-      MT_HIP(hipEventRecord(ev_wait[j], sc));
-      const int g = grad_slot(j);
-      MT_HIP(hipStreamWaitEvent(sc, ev_h2d_e[j], 0));
-      MT_HIP(hipEventRecord(ev_c_s[j], sc));
+      const int g = grad_slot();
+      begin(j);
       head_fwd_bwd<T>(blocks[j], wslot[j % 2], gslot[g], ws.dxA);
       end(j, j);
       offload(j, j, g);
@@ -555,12 +579,11 @@ void Model::step_streamed(hipStream_t P, hipStream_t O) {
   for (int i = 0; i < L; ++i) {
     const int j = L - i;
     const int u = L + 2 + i;
-    const bool refetch = (j != L);  // block L is still in its slot from the forward
+    // block L is still in its slot from the forward; the others are fetched
+    // again (the prefetch of use u+1 is issued before use u computes)
     if (j - 1 >= 1) fetch(u + 1, j - 1);
-    MT_HIP(hipEventRecord(ev_wait[u], sc));
-    const int g = grad_slot(u);
-    if (refetch) MT_HIP(hipStreamWaitEvent(sc, ev_h2d_e[u], 0));
-    MT_HIP(hipEventRecord(ev_c_s[u], sc));
+    const int g = grad_slot();
+    begin(u);
     compute_layer_bwd<T>(j, wslot[j % 2], gslot[g], dx_in, dx_out);
     end(u, j);
     offload(u, j, g);
@@ -568,14 +591,16 @@ void Model::step_streamed(hipStream_t P, hipStream_t O) {
   }
   {
     const int u = 2 * L + 2;
-    MT_HIP(hipEventRecord(ev_wait[u], sc));
-    const int g = grad_slot(u);
-    MT_HIP(hipEventRecord(ev_c_s[u], sc));
+    const int g = grad_slot();
+    begin(u);
     const mt_block_desc& b = blocks[0];
     embed_bwd<T>(dx_in, d_order, d_seg, (T*)gslot[g] + b.tensors[0].offset, V, d, sc);
     MT_HIP(hipEventRecord(ev_c_e[u], sc));
     offload(u, 0, g);
   }
+  // The step's device timeline ends once the last offload has landed.
+  xq_out->wait(last_out);
+  MT_HIP(hipEventRecord(ev_end, sc));
 }
 
 // Resident schedule: every block's weights are copied once into device
@@ -591,10 +616,10 @@ void Model::step_resident() {
     gr[j] = gres + off;
     off += round_up(blocks[j].w_bytes, 256);
   }
-  MT_HIP(hipEventRecord(ev_h2d_s[0], sc));
+  MT_HIP(hipEventRecord(ev_h2d_s, sc));
   for (size_t j = 0; j < blocks.size(); ++j)
     MT_HIP(hipMemcpyAsync(wr[j], host + blocks[j].w_off, blocks[j].w_bytes, hipMemcpyHostToDevice, sc));
-  MT_HIP(hipEventRecord(ev_h2d_e[0], sc));
+  MT_HIP(hipEventRecord(ev_h2d_e, sc));
   MT_HIP(hipEventRecord(ev_c_s[0], sc));
   for (int j = 0; j <= L; ++j) compute_block_fwd<T>(j, wr[j]);
   BwdWs<T> ws = bwdws<T>();
@@ -607,11 +632,12 @@ void Model::step_resident() {
   }
   embed_bwd<T>(dx_in, d_order, d_seg, (T*)gr[0] + blocks[0].tensors[0].offset, V, d, sc);
   MT_HIP(hipEventRecord(ev_c_e[0], sc));
-  MT_HIP(hipEventRecord(ev_d2h_s[0], sc));
+  MT_HIP(hipEventRecord(ev_d2h_s, sc));
   for (size_t j = 0; j < blocks.size(); ++j)
     MT_HIP(hipMemcpyAsync(host + blocks[j].g_off, gr[j], blocks[j].w_bytes, hipMemcpyDeviceToHost, sc));
-  MT_HIP(hipEventRecord(ev_d2h_e[0], sc));
-  for (size_t j = 0; j < blocks.size(); ++j) push_adam((int)j, ev_d2h_e[0]);
+  MT_HIP(hipEventRecord(ev_d2h_e, sc));
+  MT_HIP(hipEventRecord(ev_end, sc));
+  for (size_t j = 0; j < blocks.size(); ++j) push_adam((int)j, ev_d2h_e);
 }
 
 int Model::train_step(const int32_t* tokens) {
@@ -633,10 +659,6 @@ int Model::train_step(const int32_t* tokens) {
   MT_HIP(hipMemcpyAsync(d_tok, h_tok, sizeof(int32_t) * M, hipMemcpyHostToDevice, sc));
   MT_HIP(hipMemcpyAsync(d_order, h_order, sizeof(int32_t) * M, hipMemcpyHostToDevice, sc));
   MT_HIP(hipMemcpyAsync(d_seg, h_seg, sizeof(int32_t) * (V + 1), hipMemcpyHostToDevice, sc));
-  // Copies on the other streams start after ev_start, so that device_ms
-  // (ev_start to ev_end) spans the whole step.
-  MT_HIP(hipStreamWaitEvent(sp, ev_start, 0));
-  MT_HIP(hipStreamWaitEvent(so, ev_start, 0));
 
   {
     std::lock_guard<std::mutex> g(q_mu);
@@ -650,20 +672,30 @@ int Model::train_step(const int32_t* tokens) {
   for (auto& s : bstats) s = mt_block_stats{};
   double adam_total = 0, adam_tail = 0;
   std::atomic<bool> device_done{false};
+  const bool streamed = cfg.mode != MT_RESIDENT;
+  if (streamed && !dma) {
+    dma.reset(new DmaEngines(gslot[0], host));
+    xq_in.reset(new TransferQueue(dma.get(), DMA_H2D));
+    xq_out.reset(new TransferQueue(dma.get(), DMA_D2H));
+  }
+  h2d_host_ms.assign(n_uses, 0.0);
+  d2h_host_ms.assign(n_uses, 0.0);
   std::thread worker([&] { adam_worker(t, &adam_total, &adam_tail, &device_done); });
+  if (streamed) {
+    xq_in->start(&h2d_host_ms, nullptr);
+    xq_out->start(&d2h_host_ms, [this](const TransferQueue::Job& job) { push_adam(job.j, nullptr); });
+  }
 
   std::string enqueue_error;
   int enqueue_code = MT_OK;
   try {
     const bool bf = cfg.store_dtype == MT_BF16;
-    if (cfg.mode == MT_RESIDENT) {
+    if (!streamed) {
       bf ? step_resident<uint16_t>() : step_resident<float>();
     } else {
-      hipStream_t P = cfg.mode == MT_SERIALIZED ? sc : sp;
-      hipStream_t O = cfg.mode == MT_SERIALIZED ? sc : so;
-      bf ? step_streamed<uint16_t>(P, O) : step_streamed<float>(P, O);
+      const bool ser = cfg.mode == MT_SERIALIZED;
+      bf ? step_streamed<uint16_t>(ser) : step_streamed<float>(ser);
     }
-    MT_HIP(hipEventRecord(ev_end, so));
   } catch (const HipError& e) {
     enqueue_code = MT_E_HIP;
     enqueue_error = std::string(hipGetErrorString(e.code)) + " in " + e.where;
@@ -671,17 +703,18 @@ int Model::train_step(const int32_t* tokens) {
     enqueue_code = e.code;
     enqueue_error = e.msg;
   }
+  // Every copy that was enqueued finishes (or fails) before the Adam queue
+  // closes, so Adam sees every block whose gradients arrived.
+  if (streamed) {
+    xq_in->stop();
+    xq_out->stop();
+  }
   close_adam();
   hipError_t e1 = hipStreamSynchronize(sc);
-  hipError_t e2 = hipStreamSynchronize(sp);
-  hipError_t e3 = hipStreamSynchronize(so);
   device_done = true;
   worker.join();
   if (enqueue_code != MT_OK) throw ApiError{enqueue_code, enqueue_error};
-  if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess) {
-    hipError_t e = e1 != hipSuccess ? e1 : (e2 != hipSuccess ? e2 : e3);
-    throw ApiError{MT_E_HIP, std::string("stream synchronize: ") + hipGetErrorString(e)};
-  }
+  if (e1 != hipSuccess) throw ApiError{MT_E_HIP, std::string("stream synchronize: ") + hipGetErrorString(e1)};
   if (!adam_error.empty()) throw ApiError{MT_E_HIP, "host Adam: " + adam_error};
   last_loss = *h_loss;
   have_loss = true;
@@ -710,15 +743,18 @@ void Model::finish_stats(bool streamed, double wall_ms) {
       const bool has_d2h = (u >= L + 1);
       const int j = u <= L + 1 ? u : (u <= 2 * L + 1 ? L - (u - (L + 2)) : 0);
       const double c = ms_between(ev_c_s[u], ev_c_e[u]);
-      const double st = ms_between(ev_wait[u], ev_c_s[u]);
+      // compute-stream idle time before this use: the enqueueing thread
+      // held it back until the block's weights had arrived and its grad
+      // slot was free
+      const double st = ms_between(u == 0 ? ev_start : ev_c_e[u - 1], ev_c_s[u]);
       double h = 0, dd = 0;
       if (has_h2d) {
-        h = ms_between(ev_h2d_s[u], ev_h2d_e[u]);
+        h = h2d_host_ms[u];
         s.h2d_ms += h;
         s.h2d_bytes += (double)blocks[j].w_bytes;
       }
       if (has_d2h) {
-        dd = ms_between(ev_d2h_s[u], ev_d2h_e[u]);
+        dd = d2h_host_ms[u];
         s.d2h_ms += dd;
         s.d2h_bytes += (double)blocks[j].w_bytes;
       }
@@ -739,8 +775,8 @@ void Model::finish_stats(bool streamed, double wall_ms) {
       }
     }
   } else {
-    s.h2d_ms = ms_between(ev_h2d_s[0], ev_h2d_e[0]);
-    s.d2h_ms = ms_between(ev_d2h_s[0], ev_d2h_e[0]);
+    s.h2d_ms = ms_between(ev_h2d_s, ev_h2d_e);
+    s.d2h_ms = ms_between(ev_d2h_s, ev_d2h_e);
     for (auto& b : blocks) {
       s.h2d_bytes += (double)b.w_bytes;
       s.d2h_bytes += (double)b.w_bytes;
@@ -774,10 +810,10 @@ static std::vector<float> rope_table(int T, int hd, double theta, bool sine) {
   return out;
 }
 
-Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void* const streams[3]) {
+Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void* stream) {
   std::string why;
   if (validate_config(*cfg, &why) != MT_OK) throw ApiError{MT_E_INVALID, why};
-  if (!arena || !streams || !streams[1]) throw ApiError{MT_E_INVALID, "null arena or compute stream"};
+  if (!arena || !stream) throw ApiError{MT_E_INVALID, "null arena or compute stream"};
   if ((uintptr_t)arena & 255) throw ApiError{MT_E_ALIGN, "device arena must be 256-byte aligned"};
   std::unique_ptr<Model> m(new Model());
   m->init_dims(*cfg);
@@ -785,9 +821,7 @@ Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void*
   if (arena_bytes < need) throw ApiError{MT_E_SIZE, "device arena smaller than mt_device_bytes"};
   m->arena = (uint8_t*)arena;
   m->arena_bytes = arena_bytes;
-  m->sc = (hipStream_t)streams[1];
-  m->sp = streams[0] ? (hipStream_t)streams[0] : m->sc;
-  m->so = streams[2] ? (hipStream_t)streams[2] : m->sc;
+  m->sc = (hipStream_t)stream;
   if (cfg->store_dtype == MT_BF16)
     m->carve_all<uint16_t>(m->arena);
   else
@@ -814,13 +848,10 @@ Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void*
     v.resize(m->n_uses);
     for (auto& e : v) MT_HIP(hipEventCreate(&e));
   };
-  mk(m->ev_h2d_s);
-  mk(m->ev_h2d_e);
-  mk(m->ev_wait);
   mk(m->ev_c_s);
   mk(m->ev_c_e);
-  mk(m->ev_d2h_s);
-  mk(m->ev_d2h_e);
+  mk(m->ev_slot_free);
+  for (hipEvent_t* e : {&m->ev_h2d_s, &m->ev_h2d_e, &m->ev_d2h_s, &m->ev_d2h_e}) MT_HIP(hipEventCreate(e));
   MT_HIP(hipEventCreate(&m->ev_loss));
   MT_HIP(hipEventCreate(&m->ev_start));
   MT_HIP(hipEventCreate(&m->ev_end));
@@ -838,10 +869,9 @@ Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void*
 void destroy_model(Model* m) {
   if (!m) return;
   hipStreamSynchronize(m->sc);
-  if (m->sp) hipStreamSynchronize(m->sp);
-  if (m->so) hipStreamSynchronize(m->so);
-  for (auto* v : {&m->ev_h2d_s, &m->ev_h2d_e, &m->ev_wait, &m->ev_c_s, &m->ev_c_e, &m->ev_d2h_s, &m->ev_d2h_e})
+  for (auto* v : {&m->ev_c_s, &m->ev_c_e, &m->ev_slot_free})
     for (auto e : *v) hipEventDestroy(e);
+  for (hipEvent_t e : {m->ev_h2d_s, m->ev_h2d_e, m->ev_d2h_s, m->ev_d2h_e}) hipEventDestroy(e);
   for (auto e : m->kev) hipEventDestroy(e);
   hipEventDestroy(m->ev_loss);
   hipEventDestroy(m->ev_start);
@@ -879,6 +909,10 @@ int bind_store(Model* m, void* host, size_t bytes, void* opt, size_t opt_bytes) 
     (void)hipGetLastError();
     throw ApiError{MT_E_INVALID, "DMA part of the host store is not pinned (use mt_alloc_host_store)"};
   }
+  // the DMA engines are picked for the agents that own this store
+  m->xq_in.reset();
+  m->xq_out.reset();
+  m->dma.reset();
   m->host = (uint8_t*)host;
   m->hopt = (uint8_t*)opt;
   return MT_OK;

@@ -43,7 +43,7 @@ extern "C" {
 #define MT_F32 0             /* all-fp32 store: W, G, m, v in float32 */
 #define MT_BF16 1            /* bf16 W and G, fp32 m and v */
 
-#define MT_STREAMED 0        /* two weight slots, three streams (the method) */
+#define MT_STREAMED 0        /* two weight slots; prefetch, compute and offload overlap (the method) */
 #define MT_SERIALIZED 1      /* the streamed schedule on the compute stream only */
 #define MT_RESIDENT 2        /* every block's W on the device, no recompute */
 
@@ -105,11 +105,12 @@ typedef struct mt_block_desc {
  * mt_train_step, read by mt_get_stats. */
 typedef struct mt_stats {
   double step_ms;            /* wall time of the last mt_train_step */
-  double device_ms;          /* first prefetch start to last offload end (compute-stream events) */
+  double device_ms;          /* compute-stream events: step start to the end of the last offload */
   double fwd_ms, bwd_ms;     /* compute stream: forward sweep, head, backward sweep */
-  double h2d_ms, d2h_ms;     /* summed copy durations */
+  double h2d_ms, d2h_ms;     /* summed copy durations (offloads: host clock, issue to completion) */
   double h2d_bytes, d2h_bytes;
-  double stall_ms;           /* compute stream waiting for a weight slot to arrive */
+  double stall_ms;           /* compute stream idle between blocks: weights not yet arrived, or a
+                                gradient slot not yet offloaded */
   double adam_ms;            /* summed host Adam time */
   double adam_tail_ms;       /* host Adam time after the device finished */
   double gemm_ms, gemm_flops;/* MT_FLAG_TIME_KERNELS: summed GEMM launch time and flops */
@@ -120,8 +121,8 @@ typedef struct mt_stats {
 } mt_stats;
 
 /* Per-block timing of the last step: forward and backward compute time on
- * the compute stream, prefetch and offload copy time, and the stall of the
- * compute stream before the block's weights were ready. */
+ * the compute stream, prefetch and offload copy time, and the idle time of
+ * the compute stream before the block's compute began. */
 typedef struct mt_block_stats {
   double fwd_ms, bwd_ms, h2d_fwd_ms, h2d_bwd_ms, d2h_ms, stall_fwd_ms, stall_bwd_ms, adam_ms;
 } mt_block_stats;
@@ -156,12 +157,13 @@ int mt_store_step(const void* dma_base, int64_t* t);
 
 /* ------------------------------------------------------------- model ----- */
 /* Create a model.  dev_arena: device memory of at least mt_device_bytes(cfg),
- * 256-byte aligned, caller-owned.  streams: prefetch, compute, offload
- * hipStream_t handles (default priority), caller-owned; in MT_SERIALIZED
- * mode only streams[1] is used.  No device work except uploading the RoPE
+ * 256-byte aligned, caller-owned.  stream: the compute hipStream_t (default
+ * priority), caller-owned; every kernel of the step runs on it.  The other
+ * two streams of the method, weight prefetch and gradient offload, are
+ * queues on two of the GPU's SDMA engines, each fed in order by a host
+ * worker thread of the model.  No device work except uploading the RoPE
  * table; *out receives the handle. */
-int mt_create_model(const mt_config* cfg, void* dev_arena, size_t arena_bytes,
-                    void* const streams[3], void** out);
+int mt_create_model(const mt_config* cfg, void* dev_arena, size_t arena_bytes, void* stream, void** out);
 /* Bind a host store (DMA part from mt_alloc_host_store, optimizer part from
  * mt_alloc_host_opt or any 4 KiB-aligned host memory; header written,
  * weights initialised).  Checked: sizes >= mt_host_store_bytes and

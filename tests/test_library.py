@@ -157,9 +157,8 @@ def test_api_errors_without_device():
     assert L.mt_get_loss(None, None) == mt.MT_E_INVALID
     cfg = mt.make_config(datagen.PRESETS["tiny"])
     h = ctypes.c_void_p()
-    streams = (ctypes.c_void_p * 3)()
-    assert L.mt_create_model(ctypes.byref(cfg), None, 0, streams, ctypes.byref(h)) == mt.MT_E_INVALID
-    assert L.mt_create_model(ctypes.byref(cfg), 0x1001, 1 << 30, streams, ctypes.byref(h)) == mt.MT_E_INVALID
-    streams[1] = 1
-    assert L.mt_create_model(ctypes.byref(cfg), 0x1001, 1 << 30, streams, ctypes.byref(h)) == mt.MT_E_ALIGN
-    assert L.mt_create_model(ctypes.byref(cfg), 0x1000, 16, streams, ctypes.byref(h)) == mt.MT_E_SIZE
+    assert L.mt_create_model(ctypes.byref(cfg), None, 0, None, ctypes.byref(h)) == mt.MT_E_INVALID
+    assert L.mt_create_model(ctypes.byref(cfg), 0x1001, 1 << 30, None, ctypes.byref(h)) == mt.MT_E_INVALID
+    stream = 1  # never dereferenced: every call below fails its checks first
+    assert L.mt_create_model(ctypes.byref(cfg), 0x1001, 1 << 30, stream, ctypes.byref(h)) == mt.MT_E_ALIGN
+    assert L.mt_create_model(ctypes.byref(cfg), 0x1000, 16, stream, ctypes.byref(h)) == mt.MT_E_SIZE
