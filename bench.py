@@ -119,7 +119,7 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (same per-layer shape)")
     ap.add_argument("--mode", default="streamed", choices=["streamed", "serialized", "resident"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-kernel-timing", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
