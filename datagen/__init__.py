@@ -156,7 +156,7 @@ def draw_flat(seed: int, tid: int, start: int, stop: int, store_dtype: str,
 
 
 def init_tensor(cfg: ModelShape, name: str, layer: int | None = None,
-                rows: slice | None = None) -> np.ndarray:
+                rows: slice | None = None, pool: ThreadPoolExecutor | None = None) -> np.ndarray:
     """Initial value (float32, store-rounded) of a logical tensor, or of a row slice."""
     if name in ("attn_norm", "ffn_norm", "final_norm"):
         return np.ones(cfg.d_model, dtype=np.float32)
@@ -166,24 +166,31 @@ def init_tensor(cfg: ModelShape, name: str, layer: int | None = None,
         shape = layer_tensor_shape(cfg, name)
     tid = tensor_id(cfg, name, layer)
     r0, r1 = (0, shape[0]) if rows is None else (rows.start or 0, rows.stop if rows.stop is not None else shape[0])
-    flat = draw_flat(cfg.seed, tid, r0 * shape[1], r1 * shape[1], cfg.store_dtype)
+    flat = draw_flat(cfg.seed, tid, r0 * shape[1], r1 * shape[1], cfg.store_dtype, pool=pool)
     return flat.reshape(r1 - r0, shape[1])
 
 
-def init_params(cfg: ModelShape) -> dict:
+def init_params(cfg: ModelShape, threads: int = 1) -> dict:
     """All logical parameters as float32 arrays (store-rounded initial values).
 
     Keys: 'E', 'final_norm', 'wh', and per layer l: f'{l}.attn_norm',
-    f'{l}.wq', ..., f'{l}.wd', f'{l}.ffn_norm'.  Only for shapes that fit in RAM.
+    f'{l}.wq', ..., f'{l}.wd', f'{l}.ffn_norm'.  Only for shapes that fit in
+    RAM.  ``threads`` > 1 draws the chunks of a tensor on that many threads
+    (same values: every chunk has its own stream).
     """
-    p = {"E": init_tensor(cfg, "E")}
-    for l in range(cfg.n_layers):
-        p[f"{l}.attn_norm"] = init_tensor(cfg, "attn_norm")
-        for nm in LAYER_TENSORS:
-            p[f"{l}.{nm}"] = init_tensor(cfg, nm, l)
-        p[f"{l}.ffn_norm"] = init_tensor(cfg, "ffn_norm")
-    p["final_norm"] = init_tensor(cfg, "final_norm")
-    p["wh"] = init_tensor(cfg, "wh")
+    pool = ThreadPoolExecutor(threads) if threads > 1 else None
+    try:
+        p = {"E": init_tensor(cfg, "E", pool=pool)}
+        for l in range(cfg.n_layers):
+            p[f"{l}.attn_norm"] = init_tensor(cfg, "attn_norm")
+            for nm in LAYER_TENSORS:
+                p[f"{l}.{nm}"] = init_tensor(cfg, nm, l, pool=pool)
+            p[f"{l}.ffn_norm"] = init_tensor(cfg, "ffn_norm")
+        p["final_norm"] = init_tensor(cfg, "final_norm")
+        p["wh"] = init_tensor(cfg, "wh", pool=pool)
+    finally:
+        if pool is not None:
+            pool.shutdown()
     return p
 
 

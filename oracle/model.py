@@ -15,7 +15,22 @@ decoder.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
+
+
+def _per_sequence(fn, n):
+    """fn(b) for every sequence b < n.  Sequences are independent (attention
+    never looks across them), so they run on threads; each result lands in
+    its own slot, so the outcome does not depend on the order."""
+    if n == 1:
+        fn(0)
+        return
+    workers = min(n, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1))
+    with ThreadPoolExecutor(max(1, workers)) as ex:
+        list(ex.map(fn, range(n)))
 
 
 # ---------------------------------------------------------------- RMSNorm --
@@ -165,10 +180,12 @@ class Oracle:
         qr = rope_apply(q, self.cos, self.sin)
         kr = rope_apply(k, self.cos, self.sin)
         o = np.empty_like(qr)
-        probs = []
-        for b in range(c.batch):
-            o[b], pb = attention_fwd(qr[b], kr[b], v[b])
-            probs.append(pb)
+        probs = [None] * c.batch
+
+        def attend(b):
+            o[b], probs[b] = attention_fwd(qr[b], kr[b], v[b])
+
+        _per_sequence(attend, c.batch)
         om = self._merge(o)
         x1 = x + om @ P[f"{l}.wo"].T
         h2, r2 = rmsnorm_fwd(x1, f, c.rms_eps)
@@ -201,8 +218,10 @@ class Oracle:
         dq = np.empty_like(dom)
         dk = np.empty_like(dom)
         dv = np.empty_like(dom)
-        for b in range(c.batch):
+        def attend_bwd(b):
             dq[b], dk[b], dv[b] = attention_bwd(dom[b], C["qr"][b], C["kr"][b], C["v"][b], C["probs"][b])
+
+        _per_sequence(attend_bwd, c.batch)
         dq = self._merge(rope_apply(dq, self.cos, self.sin, inverse=True))
         dk = self._merge(rope_apply(dk, self.cos, self.sin, inverse=True))
         dv = self._merge(dv)
@@ -226,13 +245,16 @@ class Oracle:
         return loss, dxL, g, logits
 
     # ------------------------------------------------------------- step --
-    def forward_backward(self, P, tokens, mode="streamed", keep=None):
+    def forward_backward(self, P, tokens, mode="streamed", keep=None, bwd_layers=None):
         """Loss and gradients of every logical parameter.
 
         mode 'resident' keeps every layer's intermediates from the forward;
         mode 'streamed' keeps only the layer-boundary checkpoints x^l and
         recomputes each layer's forward inside the backward sweep.
         ``keep`` (optional dict) receives the checkpoints and logits.
+        ``bwd_layers`` (optional) stops the backward sweep after that many
+        layers from the top: the head's gradients and those layers' are
+        returned, the lower layers' and the embedding's are not computed.
         """
         c = self.cfg
         P = {k: np.asarray(v, dtype=self.dt) for k, v in P.items()}
@@ -245,15 +267,17 @@ class Oracle:
             ckpt.append(x)
             caches.append(cache if mode == "resident" else None)
         loss, dx, grads, logits = self.head(x, P, tok)
-        for l in reversed(range(c.n_layers)):
+        stop = -1 if bwd_layers is None else max(-1, c.n_layers - 1 - bwd_layers)
+        for l in range(c.n_layers - 1, stop, -1):
             cache = caches[l]
             if cache is None:
                 _, cache = self.layer_fwd(ckpt[l], P, l)
             dx = self.layer_bwd(dx, cache, P, l, grads)
             caches[l] = None
-        dE = np.zeros_like(P["E"])
-        np.add.at(dE, tok.reshape(-1), dx)
-        grads["E"] = dE
+        if stop == -1:
+            dE = np.zeros_like(P["E"])
+            np.add.at(dE, tok.reshape(-1), dx)
+            grads["E"] = dE
         if keep is not None:
             keep["ckpt"] = ckpt
             keep["logits"] = logits

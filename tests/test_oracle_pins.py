@@ -373,3 +373,28 @@ def test_micro_model_against_loops():
     tok = datagen.tokens(cfg)
     loss = Oracle(cfg, np.float64).loss_only(P, tok)
     assert abs(loss - _micro_forward_loops(P, tok, cfg)) < 1e-12
+
+
+def test_truncated_backward_equals_the_top_of_the_full_backward():
+    """bwd_layers=k returns exactly the head's and the top k layers' gradients
+    of the full sweep, and nothing below them."""
+    shape = datagen.PRESETS["tiny"].replace(n_layers=3)
+    P = datagen.init_params(shape)
+    tok = datagen.tokens(shape)
+    o = Oracle(shape, np.float32)
+    loss, full = o.forward_backward(P, tok)
+    loss1, top = o.forward_backward(P, tok, bwd_layers=1)
+    assert loss1 == loss
+    want = {"wh", "final_norm"} | {f"2.{n}" for n in datagen.LAYER_TENSORS + ("attn_norm", "ffn_norm")}
+    assert set(top) == want
+    for k in want:
+        assert np.array_equal(top[k], full[k]), k
+
+
+def test_threaded_init_draws_the_same_values():
+    shape = datagen.PRESETS["tiny"]
+    a = datagen.init_params(shape)
+    b = datagen.init_params(shape, threads=4)
+    assert a.keys() == b.keys()
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
