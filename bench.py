@@ -27,6 +27,28 @@ import datagen  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+
+# HBM traffic of the bf16 GEMM at the 14B shape, bytes per launch averaged
+# over the 723 launches of a step: rocprofv3 FETCH_SIZE and WRITE_SIZE,
+# scaled by what each reads for a plain 1 GiB copy kernel in the same run
+# (profiles/gemm_14b_pmc_traffic.md).  Valid only for the GEMM source it was
+# measured on; reported as null once that file changes.
+GEMM_TRAFFIC = {"source_sha256_16": "9fcde9899caba23f", "config": "14b", "layers": 48,
+                "bytes_per_launch": 8.545e9 + 0.764e9}
+
+
+def gemm_traffic(shape_name, layers):
+    """Measured bytes per GEMM launch, or None when the kernel has changed."""
+    import hashlib
+    src = os.path.join(ROOT, "host_memory_layer_amd", "csrc", "gemm.hip")
+    try:
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    t = GEMM_TRAFFIC
+    if h != t["source_sha256_16"] or shape_name != t["config"] or layers != t["layers"]:
+        return None
+    return t["bytes_per_launch"]
 PEAK_HBM_GBS = 8000.0
 
 
@@ -121,6 +143,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run a plain 1 GiB device copy kernel first (the reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; the multi-GPU path is design-only",
@@ -150,6 +174,16 @@ def main():
     link = link_probe(torch, dev, layer_bytes)
     log(f"host link: {link}")
     tokens = datagen.tokens(shape)
+    if args.copy_probe:
+        # 1 GiB read + 1 GiB written per launch: what FETCH_SIZE / WRITE_SIZE
+        # read for this kernel calibrates those counters to bytes
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize(dev)
+        del a, b
+        log("copy probe: 3 x torch.neg over 1 GiB")
 
     for i in range(args.warmup):
         t0 = time.perf_counter()
@@ -157,7 +191,7 @@ def main():
         log(f"warmup step {i}: loss {loss:.4f} {time.perf_counter() - t0:.2f} s")
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
-    gemm_ms = gemm_fl = attn_ms = attn_fl = 0.0
+    gemm_ms = gemm_fl = gemm_by = attn_ms = attn_fl = 0.0
     gemm_n = 0
     st_acc = []
     for i in range(args.steps):
@@ -166,6 +200,7 @@ def main():
         st_acc.append(st)
         gemm_ms += st["gemm_ms"]
         gemm_fl += st["gemm_flops"]
+        gemm_by += st["gemm_bytes"]
         gemm_n += st["gemm_launches"]
         attn_ms += st["attn_ms"]
         attn_fl += st["attn_flops"]
@@ -193,9 +228,10 @@ def main():
         achieved = gemm_fl / (gemm_ms / 1e3) / 1e12
         peak = PEAK_BF16_TFLOPS if bf else PEAK_F32_TFLOPS
         roof = {"bound": "mfma" if bf else "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": None, "kernel": "k_gemm_bf16 (all launches)",
+                "frac": achieved / peak, "traffic": gemm_traffic(args.config, L), "kernel": "k_gemm_bf16 (all launches)",
                 "launches_per_step": gemm_n / args.steps,
                 "flops_per_launch": gemm_fl / max(gemm_n, 1),
+                "algorithmic_bytes_per_launch": gemm_by / max(gemm_n, 1),
                 "avg_launch_ms": gemm_ms / max(gemm_n, 1)}
     cpu = None
     if not args.no_cpu_baseline:

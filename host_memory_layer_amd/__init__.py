@@ -50,7 +50,7 @@ class MtStats(ctypes.Structure):
                 ("step_ms", "device_ms", "fwd_ms", "bwd_ms", "h2d_ms", "d2h_ms", "h2d_bytes", "d2h_bytes",
                  "stall_ms", "adam_ms", "adam_tail_ms", "gemm_ms", "gemm_flops", "attn_ms", "attn_flops")] + \
                [("gemm_launches", ctypes.c_int64), ("attn_launches", ctypes.c_int64), ("loss", ctypes.c_double),
-                ("n_blocks", ctypes.c_int32), ("pad_", ctypes.c_int32)]
+                ("n_blocks", ctypes.c_int32), ("pad_", ctypes.c_int32), ("gemm_bytes", ctypes.c_double)]
 
 
 class MtBlockStats(ctypes.Structure):

@@ -127,7 +127,11 @@ struct Model {
   hipEvent_t ev_h2d_s, ev_h2d_e, ev_d2h_s, ev_d2h_e;  // resident schedule: all uploads, all offloads
   hipEvent_t ev_loss, ev_start, ev_end;
   std::vector<hipEvent_t> kev;  // kernel timing pairs
-  std::vector<std::pair<double, int>> kev_meta;  // flops, kind (0 gemm, 1 attention)
+  struct KernelMeta {
+    double flops, bytes;  // algorithmic work of the launch
+    int kind;             // 0 gemm, 1 attention
+  };
+  std::vector<KernelMeta> kev_meta;
   size_t kev_used = 0;
 
   std::unique_ptr<ThreadPool> pool;
@@ -274,20 +278,23 @@ struct Model {
   void gemm(const T* A, int64_t lda, const T* Bm, int64_t ldb, void* C, int64_t ldc, const float* R, int64_t ldr,
             int m, int n, int k, Epi epi) {
     const bool timed = cfg.flags & MT_FLAG_TIME_KERNELS;
-    if (timed) record_kernel_start(2.0 * m * n * k, 0);
+    // operands read once, result written once (and the residual read once)
+    const double out_b = epi == EPI_STORE ? sizeof(T) : 4.0;
+    const double bytes = ((double)m * k + (double)n * k) * sizeof(T) + (double)m * n * (out_b + (epi == EPI_ADD_F32 ? 4 : 0));
+    if (timed) record_kernel_start(2.0 * m * n * k, 0, bytes);
     gemm_nt<T>(A, lda, Bm, ldb, C, ldc, R, ldr, m, n, k, epi, sc);
     if (timed) record_kernel_end();
   }
-  void record_kernel_start(double flops, int kind) {
+  void record_kernel_start(double flops, int kind, double bytes = 0.0) {
     if (kev_used + 2 > kev.size()) {
       hipEvent_t e0, e1;
       MT_HIP(hipEventCreate(&e0));
       MT_HIP(hipEventCreate(&e1));
       kev.push_back(e0);
       kev.push_back(e1);
-      kev_meta.emplace_back(0.0, 0);
+      kev_meta.push_back(KernelMeta{0.0, 0.0, 0});
     }
-    kev_meta[kev_used / 2] = {flops, kind};
+    kev_meta[kev_used / 2] = KernelMeta{flops, bytes, kind};
     MT_HIP(hipEventRecord(kev[kev_used], sc));
   }
   void record_kernel_end() {
@@ -786,13 +793,14 @@ void Model::finish_stats(bool streamed, double wall_ms) {
   for (size_t i = 0; i + 1 < kev_used + 1 && i < kev_used; i += 2) {
     const double ms = ms_between(kev[i], kev[i + 1]);
     const auto& meta = kev_meta[i / 2];
-    if (meta.second == 0) {
+    if (meta.kind == 0) {
       s.gemm_ms += ms;
-      s.gemm_flops += meta.first;
+      s.gemm_flops += meta.flops;
+      s.gemm_bytes += meta.bytes;
       s.gemm_launches++;
     } else {
       s.attn_ms += ms;
-      s.attn_flops += meta.first;
+      s.attn_flops += meta.flops;
       s.attn_launches++;
     }
   }

@@ -118,6 +118,8 @@ typedef struct mt_stats {
   int64_t gemm_launches, attn_launches;
   double loss;
   int32_t n_blocks, pad_;
+  double gemm_bytes;         /* MT_FLAG_TIME_KERNELS: summed algorithmic bytes of the GEMM launches
+                                (operands and residual read once, result written once) */
 } mt_stats;
 
 /* Per-block timing of the last step: forward and backward compute time on

@@ -37,6 +37,7 @@ def test_struct_sizes_match_header():
     assert ctypes.sizeof(mt.MtConfig) == 9 * 4 + 4 + 6 * 8 + 3 * 4 + 4
     assert ctypes.sizeof(mt.MtTensorDesc) == 16
     assert ctypes.sizeof(mt.MtBlockDesc) == 16 + 8 * 8 + 8 * 16
+    assert ctypes.sizeof(mt.MtStats) == 15 * 8 + 2 * 8 + 8 + 2 * 4 + 8
 
 
 @pytest.mark.parametrize("name", list(datagen.PRESETS))
