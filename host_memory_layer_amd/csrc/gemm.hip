@@ -31,6 +31,7 @@
 // fp32 (all-fp32 store): 64x64 SIMT tile with LDS staging.
 //
 // Accumulation is fp32 in a fixed order, so results depend only on shapes.
+#include <algorithm>
 #include <type_traits>
 
 #include "kernels.h"
@@ -172,33 +173,56 @@ __device__ inline int swz128(int row, int chunk) { return row * 128 + ((chunk ^ 
 template <bool V>
 using Flag = std::integral_constant<bool, V>;
 
-template <int EPI>
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Grouped tile order: 8 tile-rows share their B panels while they are hot.
+__device__ inline void tile_of(int lin, int tiles_m, int tiles_n, int64_t& m0, int64_t& n0) {
+  const int GROUP = 8;
+  const int group_size = GROUP * tiles_n;
+  const int g = lin / group_size;
+  const int first_m = g * GROUP;
+  const int gm_cnt = min(tiles_m - first_m, GROUP);
+  m0 = (int64_t)(first_m + (lin % group_size) % gm_cnt) * BM;
+  n0 = (int64_t)((lin % group_size) / gm_cnt) * BN;
+}
+
+// VEC: N and ldc multiples of 4 and C 16-byte aligned, so every lane writes
+// 4 consecutive outputs per store through a buffer descriptor that drops
+// rows past M, while lanes past N aim beyond the descriptor.  Otherwise
+// element stores.
+template <int EPI, bool VEC>
 __global__ void __launch_bounds__(256, 1) k_gemm_bf16_nt(const uint16_t* __restrict__ A, int64_t lda,
                                                        const uint16_t* __restrict__ B, int64_t ldb, void* C,
                                                        int64_t ldc, const float* R, int64_t ldr, int M, int N, int K,
                                                        int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
   const int ntiles = tiles_m * tiles_n;
-  int pid = blockIdx.x;
-  const int per_xcd = ntiles / 8;
-  if (pid < per_xcd * 8) pid = (pid % 8) * per_xcd + pid / 8;
-  const int GROUP = 8;
-  const int group_size = GROUP * tiles_n;
-  const int g = pid / group_size;
-  const int first_m = g * GROUP;
-  const int gm_cnt = min(tiles_m - first_m, GROUP);
-  const int tm = first_m + (pid % group_size) % gm_cnt;
-  const int tn = (pid % group_size) / gm_cnt;
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  // Persistent schedule.  Workgroup w runs on XCD w % 8 (the dispatcher deals
+  // workgroups round-robin over the XCDs); XCD x owns a contiguous range of
+  // the grouped tile order, and its workgroups take turns through it.
+  const int nwg = gridDim.x, w = blockIdx.x;
+  int t, hi, stride;
+  if (nwg % 8 == 0 && nwg < ntiles) {
+    const int per = (ntiles + 7) / 8;
+    const int lo = (w % 8) * per;
+    hi = min(ntiles, lo + per);
+    t = lo + w / 8;
+    stride = nwg / 8;
+  } else {
+    t = w;
+    hi = ntiles;
+    stride = nwg;
+  }
+  if (t >= hi) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int arows = (int)min<int64_t>(BM, M - m0), brows = (int)min<int64_t>(BN, N - n0);
-  const __amdgpu_buffer_rsrc_t arsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * lda), 0, (int)(arows * lda * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t brsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(B + n0 * ldb), 0, (int)(brows * ldb * 2), 0x00020000);
   const int nk = K / BK;
+  auto rsrc_of = [&](const void* base, int64_t row0, int64_t rows_total, int64_t ld, int esize) {
+    const int rows = (int)min<int64_t>(BM, rows_total - row0);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)base + row0 * ld * esize), 0,
+                                             (int)(rows * ld * esize), 0x00020000);
+  };
 
   // Direct load i (0..7) of an operand tile: kilobyte j = wave*8 + i, rows
   // 8j .. 8j+7; lane l reads row 8j + l/8, logical chunk (l%8) ^ ((row>>1)&7),
@@ -211,24 +235,17 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_nt(const uint16_t* __restr
     aoff[i] = (int)((r * lda + 8 * lc) * 2);
     boff[i] = (int)((r * ldb + 8 * lc) * 2);
   }
-  auto load_a = [&](int kt, int i) {
+  auto load_a = [&](__amdgpu_buffer_rsrc_t rs, int kt, int i) {
     uint8_t* dst = smem + (kt & 1) * STAGE + (wave * 8 + i) * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void_t*)dst, 16, aoff[i], kt * BK * 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)dst, 16, aoff[i], kt * BK * 2, 0, 0);
   };
-  auto load_b = [&](int kt, int i) {
+  auto load_b = [&](__amdgpu_buffer_rsrc_t rs, int kt, int i) {
     uint8_t* dst = smem + (kt & 1) * STAGE + STAGE / 2 + (wave * 8 + i) * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(brsrc, (lds_void_t*)dst, 16, boff[i], kt * BK * 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)dst, 16, boff[i], kt * BK * 2, 0, 0);
   };
 
   const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
   f32x16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
   bf16x8_t a[2][4], b[2][4];
   // Fragment q (0..7) of a sub-step, in the order the next sub-step's MFMAs
   // first use them: a0, b0..b3, a1..a3.
@@ -243,10 +260,16 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_nt(const uint16_t* __restr
       b[set][q - 1] = *(const bf16x8_t*)(Bs + swz128(wn + 32 * (q - 1) + (lane & 31), c));
     }
   };
+  // B fragments are the MFMA's first operand: the accumulator then holds
+  // the tile transposed, so that a lane owns 4 consecutive output columns.
   auto mfma16 = [&](int set, int p) {
     const int i = p >> 2, j = p & 3;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[set][i], b[set][j], acc[i][j], 0, 0, 0);
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[set][j], a[set][i], acc[i][j], 0, 0, 0);
   };
+
+  int64_t m0, n0;
+  tile_of(t, tiles_m, tiles_n, m0, n0);
+  __amdgpu_buffer_rsrc_t ar = rsrc_of(A, m0, M, lda, 2), br = rsrc_of(B, n0, N, ldb, 2);
 
   // One K step.  LOAD_B: load B of step kt+1 during sub-step 0; LOAD_A2:
   // load A of step kt+2 during sub-step 3; NEXT: read step kt+1's first
@@ -261,7 +284,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_nt(const uint16_t* __restr
       if (p & 1)
         read_one(kt, 1, 1, p >> 1);
       else if (LOAD_B)
-        load_b(kt + 1, p >> 1);
+        load_b(br, kt + 1, p >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -276,73 +299,146 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_nt(const uint16_t* __restr
       if (p & 1) read_one(kt, 3, 1, p >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // Every load in flight belongs to step kt+1, which sub-step 3 starts
-    // reading; the barrier also frees step kt's stage for step kt+2.
+    // Step kt+1 must have landed before sub-step 3 reads it; the barrier
+    // also frees step kt's stage for step kt+2.
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
       mfma16(1, p);
       if (NEXT && (p & 1)) read_one(kt + 1, 0, 0, p >> 1);
-      if (LOAD_A2 && !(p & 1)) load_a(kt + 2, p >> 1);
+      if (LOAD_A2 && !(p & 1)) load_a(ar, kt + 2, p >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Prologue: steps 0 and 1 in full.
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    load_a(0, i);
-    load_b(0, i);
-  }
-  if (nk > 1) {
+  // Steps 0 and 1 of a tile (nk >= 3); both stages are free.
+  auto prologue = [&]() {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      load_a(1, i);
-      load_b(1, i);
+      load_a(ar, 0, i);
+      load_b(br, 0, i);
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      load_a(ar, 1, i);
+      load_b(br, 1, i);
+    }
+  };
+  prologue();
+
+  const Flag<true> T_;
+  const Flag<false> F_;
+  for (;;) {
+    // Step 0 of this tile (and everything issued before it, the previous
+    // tile's stores included) has landed; step 1 may still be in flight.
     asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-  __syncthreads();
+    __syncthreads();
+    read_one(0, 0, 0, 0);
+    read_one(0, 0, 0, 1);
+    read_one(0, 0, 0, 2);
+    read_one(0, 0, 0, 3);
+    read_one(0, 0, 0, 4);
+    read_one(0, 0, 0, 5);
+    read_one(0, 0, 0, 6);
+    read_one(0, 0, 0, 7);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) read_one(0, 0, 0, i);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    step(0, F_, T_, T_);  // step 1 came with step 0
+    for (int kt = 1; kt + 2 < nk; ++kt) step(kt, T_, T_, T_);
+    step(nk - 2, T_, F_, T_);
+    step(nk - 1, F_, F_, F_);
 
-  if (nk == 1) {
-    step(0, Flag<false>{}, Flag<false>{}, Flag<false>{});
-  } else {
-    // step 0: step 1 is already loaded
-    if (nk == 2)
-      step(0, Flag<false>{}, Flag<false>{}, Flag<true>{});
-    else
-      step(0, Flag<false>{}, Flag<true>{}, Flag<true>{});
-    for (int kt = 1; kt + 2 < nk; ++kt) step(kt, Flag<true>{}, Flag<true>{}, Flag<true>{});
-    if (nk >= 3) step(nk - 2, Flag<true>{}, Flag<false>{}, Flag<true>{});
-    step(nk - 1, Flag<false>{}, Flag<false>{}, Flag<false>{});
-  }
-
-  // Accumulator layout of a 32x32 MFMA tile: lane holds column (lane & 31);
-  // register r holds row 8*(r/4) + 4*(lane/32) + (r%4).
+    // Epilogue.  acc[i][j] register r holds row 32i + (lane & 31) and column
+    // 32j + 8(r/4) + 4(lane/32) + r%4 of the wave's 128 x 128 sub-tile.
+    if (VEC) {
+      const int esize = EPI == EPI_STORE ? 2 : 4;
+      const __amdgpu_buffer_rsrc_t crs = rsrc_of(C, m0, M, ldc, esize);
+      __amdgpu_buffer_rsrc_t rrs = crs;
+      if (EPI == EPI_ADD_F32) rrs = rsrc_of(R, m0, M, ldr, 4);
+      // column of this lane's first output relative to the sub-tile; lanes
+      // whose 4 columns lie past N aim beyond the descriptor
+      const int c0 = 4 * (lane >> 5);
+      const int ncol = (int)min<int64_t>(BN, N - n0) - wn;  // valid columns of the sub-tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm + 32 * i + (lane & 31);
+        const int cbase = row * (int)ldc + (int)(n0 + wn) + c0;
+        const int rbase = EPI == EPI_ADD_F32 ? row * (int)ldr + (int)(n0 + wn) + c0 : 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
+          u32x4_t rv[4];
+          if (EPI == EPI_ADD_F32) {
+            // the residual of this 32 x 32 block; the wait covers every
+            // earlier memory operation of the wave, earlier stores included
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int64_t gm = m0 + wm + 32 * i + row;
-        const int64_t gn = n0 + wn + 32 * j + (lane & 31);
-        if (gm < M && gn < N) {
-          const float v = acc[i][j][r];
-          if (EPI == EPI_STORE)
-            ((uint16_t*)C)[gm * ldc + gn] = f32_to_bf16(v);
-          else if (EPI == EPI_F32)
-            ((float*)C)[gm * ldc + gn] = v;
-          else
-            ((float*)C)[gm * ldc + gn] = R[gm * ldr + gn] + v;
+            for (int g = 0; g < 4; ++g) {
+              const int col = 32 * j + 8 * g;
+              const int off = col + c0 < ncol ? (rbase + col) * 4 : 0x7FFFFFF0;
+              rv[g] = __builtin_amdgcn_raw_buffer_load_b128(rrs, off, 0, 0);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = 32 * j + 8 * g;
+            const int off = col + c0 < ncol ? (cbase + col) * esize : 0x7FFFFFF0;
+            const f32x16_t& v = acc[i][j];
+            if (EPI == EPI_STORE) {
+              u32x2_t pk;
+              pk.x = (uint32_t)f32_to_bf16(v[4 * g]) | ((uint32_t)f32_to_bf16(v[4 * g + 1]) << 16);
+              pk.y = (uint32_t)f32_to_bf16(v[4 * g + 2]) | ((uint32_t)f32_to_bf16(v[4 * g + 3]) << 16);
+              __builtin_amdgcn_raw_buffer_store_b64(pk, crs, off, 0, 0);
+            } else {
+              float o0 = v[4 * g], o1 = v[4 * g + 1], o2 = v[4 * g + 2], o3 = v[4 * g + 3];
+              if (EPI == EPI_ADD_F32) {
+                o0 = __uint_as_float(rv[g].x) + o0;
+                o1 = __uint_as_float(rv[g].y) + o1;
+                o2 = __uint_as_float(rv[g].z) + o2;
+                o3 = __uint_as_float(rv[g].w) + o3;
+              }
+              u32x4_t pk = {__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2), __float_as_uint(o3)};
+              __builtin_amdgcn_raw_buffer_store_b128(pk, crs, off, 0, 0);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t gm = m0 + wm + 32 * i + (lane & 31);
+            const int64_t gn = n0 + wn + 32 * j + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (gm < M && gn < N) {
+              const float v = acc[i][j][r];
+              if (EPI == EPI_STORE)
+                ((uint16_t*)C)[gm * ldc + gn] = f32_to_bf16(v);
+              else if (EPI == EPI_F32)
+                ((float*)C)[gm * ldc + gn] = v;
+              else
+                ((float*)C)[gm * ldc + gn] = R[gm * ldr + gn] + v;
+            }
+          }
+    }
+    // Next tile: its loads go out right behind this tile's stores, so the
+    // store drain, the load latency and the next tile's start overlap.
+    t += stride;
+    if (t >= hi) break;
+    tile_of(t, tiles_m, tiles_n, m0, n0);
+    ar = rsrc_of(A, m0, M, lda, 2);
+    br = rsrc_of(B, n0, N, ldb, 2);
+    prologue();
+  }
 }
 
 // fp32 SIMT GEMM for the all-fp32 store: 64x64 tile, 4x4 per thread.
@@ -381,6 +477,20 @@ __global__ void __launch_bounds__(256) k_gemm_f32(const float* __restrict__ A, i
     }
 }
 
+// One workgroup per compute unit of the current device (LDS use allows one).
+int persistent_workgroups() {
+  static thread_local int dev = -1, cus = 0;
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess) d = 0;
+  if (d != dev) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess || n <= 0) n = 256;
+    dev = d;
+    cus = n;
+  }
+  return cus;
+}
+
 }  // namespace
 
 template <>
@@ -391,17 +501,31 @@ void gemm_nt<uint16_t>(const uint16_t* A, int64_t lda, const uint16_t* B, int64_
     throw ApiError{MT_E_INVALID, "bf16 GEMM needs K, lda, ldb multiples of 8 and 16-byte aligned operands"};
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const dim3 grid(tiles_m * tiles_n);
-  if (K % BK == 0 && K > 0) {
-    // buffer offsets are 32-bit: one operand panel of 256 rows must fit
-    if ((int64_t)BM * lda * 2 >= (int64_t)1 << 31 || (int64_t)BN * ldb * 2 >= (int64_t)1 << 31)
+  if (K % BK == 0 && K >= 3 * BK) {
+    // buffer offsets are 32-bit: one 256-row panel of every operand must fit
+    const int64_t lim = (int64_t)1 << 31;
+    if ((int64_t)BM * lda * 2 >= lim || (int64_t)BN * ldb * 2 >= lim || (int64_t)BM * ldc * 4 >= lim ||
+        (R && (int64_t)BM * ldr * 4 >= lim))
       throw ApiError{MT_E_INVALID, "bf16 GEMM row stride too large"};
-#define L_(E) \
-  hipLaunchKernelGGL((k_gemm_bf16_nt<E>), grid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, R, ldr, M, N, K, tiles_m, tiles_n)
+    const bool vec = N % 4 == 0 && ldc % 4 == 0 && ((uintptr_t)C & 15) == 0 &&
+                     (epi != EPI_ADD_F32 || (ldr % 4 == 0 && ((uintptr_t)R & 15) == 0));
+    const int ntiles = tiles_m * tiles_n;
+    const dim3 pgrid(std::min(ntiles, persistent_workgroups()));
+#define L_(E, V)                                                                                                  \
+  hipLaunchKernelGGL((k_gemm_bf16_nt<E, V>), pgrid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, R, ldr, M, N, K, tiles_m, \
+                     tiles_n)
+#define LV_(E) \
+  if (vec) {   \
+    L_(E, true);  \
+  } else {     \
+    L_(E, false); \
+  }
     switch (epi) {
-      case EPI_STORE: L_(EPI_STORE); break;
-      case EPI_F32: L_(EPI_F32); break;
-      case EPI_ADD_F32: L_(EPI_ADD_F32); break;
+      case EPI_STORE: LV_(EPI_STORE) break;
+      case EPI_F32: LV_(EPI_F32) break;
+      case EPI_ADD_F32: LV_(EPI_ADD_F32) break;
     }
+#undef LV_
 #undef L_
     return;
   }
