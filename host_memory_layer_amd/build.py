@@ -26,6 +26,10 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I" + INCL
 GXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-I" + INCLUDE, "-I" + CSRC]
 
 HIP_SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "engine.hip"]
+# The attention kernels feed MFMA results to vector ALU work (softmax) every
+# tile: MFMAs that write the general register file avoid copies through the
+# accumulation registers.
+FILE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 HIPCC_HOST_SOURCES = ["store.cpp", "api.cpp", "kernel_api.cpp", "dma.cpp"]
 GXX_SOURCES = ["adam.cpp"]
 
@@ -45,7 +49,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     objs = []
     for src in HIP_SOURCES:
         obj = os.path.join(OUT_DIR, src + ".o")
-        cmds.append([HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC] + HIP_FLAGS + FILE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in HIPCC_HOST_SOURCES:
         obj = os.path.join(OUT_DIR, src + ".o")

@@ -88,7 +88,8 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int d = H * HD;
   const int64_t ld = 3LL * d;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q0 = qb * 128 + wave * 32;
   const int64_t rowbase = (int64_t)b * T;
   const bool active = q0 < T;
@@ -140,7 +141,9 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
     if (kb + 1 < nkb) issue(kb + 1, buf ^ 1);
     const uint8_t* Ks = smem + buf * 32768;
     const uint8_t* Vs = Ks + 16384;
-    if (active && kb * 64 <= q0 + 31) {
+    // Every wave runs every key block: a block wholly after the wave's
+    // queries is fully masked (P = 0) and changes neither m nor l.
+    {
       f32x16_t s_acc[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -158,7 +161,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (kb * 64 + 32 * kt + acc_row(r, lane) > tq) s_acc[kt][r] = -INFINITY;
+            s_acc[kt][r] = kb * 64 + 32 * kt + acc_row(r, lane) > tq ? -INFINITY : s_acc[kt][r];
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -286,7 +289,8 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int d = H * HD;
   const int64_t ld = 3LL * d;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t rowbase = (int64_t)b * T;
   const int kbase = kblk * 128;
   const int k0 = kbase + wave * 32;
@@ -377,7 +381,10 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
     const float* lse_s = (const float*)(st + 4 * TILE);
     const float* D_s = lse_s + 32;
     const int qbase = n * QT;
-    if (active && k0 <= qbase + 31) {
+    // Every wave runs every tile: a tile wholly before the wave's keys gets
+    // P = 0 from the causal mask, so the accumulators never leave the MFMA
+    // register file inside the loop.
+    {
       f32x16_t s_acc = zero16(), dp_acc = zero16();
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
@@ -389,23 +396,24 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
         const bf16x8_t vf = *(const bf16x8_t*)(Vs + sw256(32 * wave + (lane & 31), ch));
         dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, vf, dp_acc, 0, 0, 0);
       }
-      // rows = queries of the tile, column = this lane's key
-      if (k0 + 31 > qbase) {  // tile crosses the diagonal: mask keys after the query
+      // rows = queries of the tile, column = this lane's key; the statistics
+      // of 4 consecutive rows come in one 16-byte read
+      float4 ls[4], ds[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = acc_row(r, lane);
-          const float p = (key <= qbase + qi) ? __builtin_amdgcn_exp2f(fmaf(s_acc[r], c, -lse_s[qi])) : 0.f;
-          s_acc[r] = p;
-          dp_acc[r] = p * (dp_acc[r] - D_s[qi]);
-        }
-      } else {
+      for (int g = 0; g < 4; ++g) {
+        ls[g] = *(const float4*)(lse_s + acc_row(4 * g, lane));
+        ds[g] = *(const float4*)(D_s + acc_row(4 * g, lane));
+      }
+      const bool masked = k0 + 31 > qbase;  // wave-uniform
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = acc_row(r, lane);
-          const float p = __builtin_amdgcn_exp2f(fmaf(s_acc[r], c, -lse_s[qi]));
-          s_acc[r] = p;
-          dp_acc[r] = p * (dp_acc[r] - D_s[qi]);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int qi = acc_row(r, lane);
+        const float lq = ((const float*)&ls[r >> 2])[r & 3];
+        const float dq = ((const float*)&ds[r >> 2])[r & 3];
+        const float e = __builtin_amdgcn_exp2f(fmaf(s_acc[r], c, -lq));
+        const float p = (!masked || key <= qbase + qi) ? e : 0.f;
+        s_acc[r] = p;
+        dp_acc[r] = p * (dp_acc[r] - dq);
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -446,7 +454,8 @@ __global__ void __launch_bounds__(256) k_attn_dq_bf16(const uint16_t* __restrict
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const int d = H * HD;
   const int64_t ld = 3LL * d;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q0 = qb * 128 + wave * 32;
   const int64_t rowbase = (int64_t)b * T;
   const bool active = q0 < T;
@@ -508,11 +517,12 @@ __global__ void __launch_bounds__(256) k_attn_dq_bf16(const uint16_t* __restrict
     const uint8_t* Ks = smem + buf * 49152;
     const uint8_t* Vs = Ks + 16384;
     const uint8_t* KTs = Vs + 16384;
-    if (active) {
+    // Every wave runs every key sub-tile: one wholly after the wave's
+    // queries gets P = 0 from the causal mask.
+    {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const int kstart = kb * 64 + 32 * kt;
-        if (kstart > q0 + 31) continue;
         f32x16_t s_acc = zero16(), dp_acc = zero16();
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
@@ -522,11 +532,12 @@ __global__ void __launch_bounds__(256) k_attn_dq_bf16(const uint16_t* __restrict
           const bf16x8_t vf = *(const bf16x8_t*)(Vs + sw256(32 * kt + (lane & 31), ch));
           dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, of[s], dp_acc, 0, 0, 0);
         }
-        if (kstart + 31 > q0) {  // sub-tile crosses the diagonal
+        if (kstart + 31 > q0) {  // sub-tile reaches past the wave's first query
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kstart + acc_row(r, lane);
-            const float p = (key <= tq) ? __builtin_amdgcn_exp2f(fmaf(s_acc[r], c, -lse_q)) : 0.f;
+            const float e = __builtin_amdgcn_exp2f(fmaf(s_acc[r], c, -lse_q));
+            const float p = key <= tq ? e : 0.f;
             dp_acc[r] = p * (dp_acc[r] - D_q);
           }
         } else {
