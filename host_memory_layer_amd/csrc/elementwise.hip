@@ -379,9 +379,10 @@ void rope_qkv_fwd(T* qkv, T* qkvT, int64_t ldT, const float* cosb, const float* 
 }
 
 // Inverse rotation on the transposed layout: one thread per (pair, 8 tokens)
-// when the token count is a multiple of 8, else per (pair, token).
+// when the token count is a multiple of 8, else per (pair, token).  The
+// tables come transposed, [hd/2][T], so a thread's 8 positions are adjacent.
 template <typename T>
-__global__ void __launch_bounds__(256) k_rope_bwd_T(T* x, int64_t ldT, const float* cosb, const float* sinb, int M,
+__global__ void __launch_bounds__(256) k_rope_bwd_T(T* x, int64_t ldT, const float* cosT, const float* sinT, int M,
                                                     int T_, int d, int hd) {
   const int64_t m = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (m >= M) return;
@@ -392,13 +393,13 @@ __global__ void __launch_bounds__(256) k_rope_bwd_T(T* x, int64_t ldT, const flo
   const int head = rem / h2, i = rem % h2;
   const int64_t ra = (int64_t)part * d + (int64_t)head * hd + i, rb = ra + h2;
   const int t = (int)(m % T_);
-  const float cs = cosb[(int64_t)t * h2 + i], sn = sinb[(int64_t)t * h2 + i];
+  const float cs = cosT[(int64_t)i * T_ + t], sn = sinT[(int64_t)i * T_ + t];
   const float a = ldf(x[ra * ldT + m]), b = ldf(x[rb * ldT + m]);
   x[ra * ldT + m] = stf<T>(a * cs + b * sn);
   x[rb * ldT + m] = stf<T>(b * cs - a * sn);
 }
 
-__global__ void __launch_bounds__(256) k_rope_bwd_T8(uint16_t* x, int64_t ldT, const float* cosb, const float* sinb,
+__global__ void __launch_bounds__(256) k_rope_bwd_T8(uint16_t* x, int64_t ldT, const float* cosT, const float* sinT,
                                                      int M, int T_, int d, int hd) {
   const int64_t m = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (m >= M) return;
@@ -411,27 +412,32 @@ __global__ void __launch_bounds__(256) k_rope_bwd_T8(uint16_t* x, int64_t ldT, c
   float a[8], b[8], oa[8], ob[8];
   unpack8(*(const uint4*)(x + ra * ldT + m), a);
   unpack8(*(const uint4*)(x + rb * ldT + m), b);
+  // T_ % 8 == 0, so the 8 positions t .. t+7 belong to one sequence
+  const int t = (int)(m % T_);
+  const float4* cp = (const float4*)(cosT + (int64_t)i * T_ + t);
+  const float4* sp = (const float4*)(sinT + (int64_t)i * T_ + t);
+  const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+  const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int t = (int)((m + e) % T_);
-    const float cs = cosb[(int64_t)t * h2 + i], sn = sinb[(int64_t)t * h2 + i];
-    oa[e] = a[e] * cs + b[e] * sn;
-    ob[e] = b[e] * cs - a[e] * sn;
+    oa[e] = a[e] * cs[e] + b[e] * sn[e];
+    ob[e] = b[e] * cs[e] - a[e] * sn[e];
   }
   *(uint4*)(x + ra * ldT + m) = pack8(oa);
   *(uint4*)(x + rb * ldT + m) = pack8(ob);
 }
 
 template <typename T>
-void rope_bwd_T(T* dqkvT, int64_t ldT, const float* cosb, const float* sinb, int M, int T_, int d, int hd,
+void rope_bwd_T(T* dqkvT, int64_t ldT, const float* cosT, const float* sinT, int M, int T_, int d, int hd,
                 hipStream_t s) {
   if (M <= 0) return;
-  if (std::is_same<T, uint16_t>::value && M % 8 == 0 && ldT % 8 == 0) {
-    hipLaunchKernelGGL(k_rope_bwd_T8, dim3(cdiv(M / 8, 256), d), dim3(256), 0, s, (uint16_t*)dqkvT, ldT, cosb, sinb,
+  if (std::is_same<T, uint16_t>::value && M % 8 == 0 && T_ % 8 == 0 && ldT % 8 == 0) {
+    hipLaunchKernelGGL(k_rope_bwd_T8, dim3(cdiv(M / 8, 256), d), dim3(256), 0, s, (uint16_t*)dqkvT, ldT, cosT, sinT,
                        M, T_, d, hd);
     return;
   }
-  hipLaunchKernelGGL(k_rope_bwd_T<T>, dim3(cdiv(M, 256), d), dim3(256), 0, s, dqkvT, ldT, cosb, sinb, M, T_, d, hd);
+  hipLaunchKernelGGL(k_rope_bwd_T<T>, dim3(cdiv(M, 256), d), dim3(256), 0, s, dqkvT, ldT, cosT, sinT, M, T_, d, hd);
 }
 
 // --------------------------------------------------------------- SwiGLU --

@@ -110,7 +110,8 @@ struct Model {
   uint8_t *wslot[2], *gslot[2], *wt;
   uint8_t *wres = nullptr, *gres = nullptr;  // resident mode: every block's W and G
   float* ckpt;
-  float *cosb, *sinb;
+  float *cosb, *sinb;  // RoPE tables [T x hd/2]
+  float *cosT, *sinT;  // the same, transposed [hd/2 x T]
   int32_t *d_tok, *d_order, *d_seg;
   std::vector<uint8_t*> acts_mem;  // Acts storage per layer (1 in streamed modes)
   uint8_t* bwd_mem;
@@ -203,6 +204,8 @@ struct Model {
     ckpt = c.take<float>((uint64_t)(L + 1) * M * d * 4);
     cosb = c.take<float>((uint64_t)Tq * (hd / 2) * 4);
     sinb = c.take<float>((uint64_t)Tq * (hd / 2) * 4);
+    cosT = c.take<float>((uint64_t)Tq * (hd / 2) * 4);
+    sinT = c.take<float>((uint64_t)Tq * (hd / 2) * 4);
     d_tok = c.take<int32_t>((uint64_t)M * 4);
     d_order = c.take<int32_t>((uint64_t)M * 4);
     d_seg = c.take<int32_t>((uint64_t)(V + 1) * 4);
@@ -357,7 +360,7 @@ struct Model {
     if (timed) record_kernel_start(2.5 * attn_fwd_flops(), 1);
     attn_bwd<T>(a.qkv, a.qkvT, ws.do_, ws.doT, Mp, a.lse, ws.Dsum, ws.dqkvT, B, Tq, H, hd, sc);
     if (timed) record_kernel_end();
-    rope_bwd_T<T>(ws.dqkvT, Mp, cosb, sinb, M, Tq, d, hd, sc);
+    rope_bwd_T<T>(ws.dqkvT, Mp, cosT, sinT, M, Tq, d, hd, sc);
     // QKV projection
     transpose<T>(ws.dqkvT, Mp, ws.dqkv, 3 * d, 3 * d, M, sc);
     transpose<T>(a.h, d, ws.tmpT, Mp, M, d, sc);
@@ -840,6 +843,17 @@ Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void*
   auto s = rope_table(m->Tq, m->hd, cfg->rope_theta, true);
   MT_HIP(hipMemcpy(m->cosb, c.data(), c.size() * 4, hipMemcpyHostToDevice));
   MT_HIP(hipMemcpy(m->sinb, s.data(), s.size() * 4, hipMemcpyHostToDevice));
+  {
+    const int h2 = m->hd / 2;
+    std::vector<float> ct(c.size()), st(s.size());
+    for (int t = 0; t < m->Tq; ++t)
+      for (int i = 0; i < h2; ++i) {
+        ct[(size_t)i * m->Tq + t] = c[(size_t)t * h2 + i];
+        st[(size_t)i * m->Tq + t] = s[(size_t)t * h2 + i];
+      }
+    MT_HIP(hipMemcpy(m->cosT, ct.data(), ct.size() * 4, hipMemcpyHostToDevice));
+    MT_HIP(hipMemcpy(m->sinT, st.data(), st.size() * 4, hipMemcpyHostToDevice));
+  }
   for (int g = 0; g < 2; ++g) MT_HIP(hipMemset(m->gslot[g], 0, m->slot_bytes));
   if (m->gres) {
     uint64_t tot = 0;

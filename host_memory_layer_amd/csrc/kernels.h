@@ -45,9 +45,10 @@ int64_t token_ld(int64_t M);
 template <typename T>
 void rope_qkv_fwd(T* qkv, T* qkvT, int64_t ldT, const float* cosb, const float* sinb, int M, int T_, int d, int hd,
                   hipStream_t s);
-// Inverse rotation of the dq, dk rows of dqkvT [3d x M] (row stride ldT), in place.
+// Inverse rotation of the dq, dk rows of dqkvT [3d x M] (row stride ldT), in
+// place; cosT, sinT are the rotation tables transposed, [hd/2 x T].
 template <typename T>
-void rope_bwd_T(T* dqkvT, int64_t ldT, const float* cosb, const float* sinb, int M, int T_, int d, int hd,
+void rope_bwd_T(T* dqkvT, int64_t ldT, const float* cosT, const float* sinT, int M, int T_, int d, int hd,
                 hipStream_t s);
 template <typename T>
 void swiglu_fwd(const T* gu, T* y, int M, int F, hipStream_t s);
