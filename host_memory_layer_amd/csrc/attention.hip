@@ -25,8 +25,14 @@
 // elements by (lane half, element), so any permutation of the contraction
 // index that both operands share is exact.  When P (or dS) comes from an
 // accumulator, element e of lane-half h holds key (or query) 8*(e/4)+4*h+(e%4)
-// of a 16-wide slice; the LDS operand is read with the same mapping (two
-// 8-byte reads per fragment).
+// of a 16-wide slice.  The transposed operands (qkvT, dOT) store tokens in
+// attention's token order (bits 2 and 3 swapped inside each 16-group), in
+// which exactly those 8 tokens are adjacent: the other operand's fragment is
+// one 16-byte LDS read of chunk 2*slice + h.
+//
+// LDS layouts are swizzled at 16-byte granularity so that the 16 lanes one
+// ds_read_b128 serves per cycle (16 consecutive tile rows, one logical
+// chunk) fall on 16 different 16-byte bank groups of the 256-byte bank row.
 #include "kernels.h"
 
 namespace mt {
@@ -41,9 +47,10 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Swizzled byte offsets: rows of 256 bytes (16 chunks) and of 128 bytes (8 chunks).
+// Swizzled byte offsets for rows of 256 bytes (16 chunks) and of 128 bytes
+// (8 chunks; two rows share a bank row, so the key is row/2).
 __device__ inline int sw256(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
-__device__ inline int sw128(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+__device__ inline int sw128(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 __device__ inline f32x16_t zero16() {
   f32x16_t z;
@@ -55,18 +62,11 @@ __device__ inline f32x16_t zero16() {
 // Row index inside a 32x32 accumulator tile for register r of this lane.
 __device__ inline int acc_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
 
-// Fragment of a transposed tile (rows of 64 bf16, 128 bytes) for a
-// contraction slice starting at column c0 (multiple of 16): two 8-byte reads
-// at columns c0 + 4h and c0 + 8 + 4h.
+// Fragment of a transposed tile in attention's token order (rows of 64
+// tokens, 128 bytes) for the contraction slice of 16 tokens starting at
+// column c0: chunk c0/8 + h.
 __device__ inline bf16x8_t frag_T(const uint8_t* base, int row, int c0, int lane) {
-  const int h = lane >> 5;
-  const int ch = c0 >> 3;  // 16-byte chunk of column c0
-  bf16x4_t lo = *(const bf16x4_t*)(base + sw128(row, ch) + 8 * h);
-  bf16x4_t hi = *(const bf16x4_t*)(base + sw128(row, ch + 1) + 8 * h);
-  bf16x8_t f;
-  f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
-  f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
-  return f;
+  return *(const bf16x8_t*)(base + sw128(row, (c0 >> 3) + (lane >> 5)));
 }
 
 // Registers 8*ks .. 8*ks+7 of an accumulator tile, as a bf16 B operand.
@@ -121,7 +121,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
       const int kr = 4 * j + (lane >> 4), kc = (lane & 15) ^ (kr & 15);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_t*)(Ks + j * 1024), 16, (int)((kr * ld + 8 * kc) * 2),
                                                (int)((int64_t)key0 * ld * 2), 0, 0);
-      const int vr = 8 * j + (lane >> 3), vc = (lane & 7) ^ (vr & 7);
+      const int vr = 8 * j + (lane >> 3), vc = (lane & 7) ^ ((vr >> 1) & 7);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void_t*)(Vs + j * 1024), 16, (int)((vr * ldT + 8 * vc) * 2),
                                                key0 * 2, 0, 0);
     }
@@ -256,17 +256,10 @@ __global__ void __launch_bounds__(256) k_dsum(const T* dO, const T* O, float* Ds
 // 64-byte rows (32 bf16): 16-byte chunk c stored at c ^ ((row >> 2) & 3).
 __device__ inline int sw64(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
-// Fragment of a transposed tile with 64-byte rows (32 columns) for the
-// contraction slice starting at column c0 (multiple of 16).
+// Fragment of a transposed tile in attention's token order with 64-byte
+// rows (32 tokens) for the contraction slice starting at column c0.
 __device__ inline bf16x8_t frag_T64(const uint8_t* base, int row, int c0, int lane) {
-  const int h = lane >> 5;
-  const int ch = c0 >> 3;
-  bf16x4_t lo = *(const bf16x4_t*)(base + sw64(row, ch) + 8 * h);
-  bf16x4_t hi = *(const bf16x4_t*)(base + sw64(row, ch + 1) + 8 * h);
-  bf16x8_t f;
-  f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
-  f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
-  return f;
+  return *(const bf16x8_t*)(base + sw64(row, (c0 >> 3) + (lane >> 5)));
 }
 
 // One block = 128 keys of one (batch, head); query tiles of 32 stream
@@ -498,7 +491,7 @@ __global__ void __launch_bounds__(256) k_attn_dq_bf16(const uint16_t* __restrict
       const int voff = (r * ld + 8 * ch) * 2, soff = (int)((int64_t)key0 * ld * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_t*)(Ks + j * 1024), 16, voff, soff, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void_t*)(Vs + j * 1024), 16, voff, soff, 0, 0);
-      const int tr = 8 * j + (lane >> 3), tc = (lane & 7) ^ (tr & 7);
+      const int tr = 8 * j + (lane >> 3), tc = (lane & 7) ^ ((tr >> 1) & 7);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ktrsrc, (lds_void_t*)(KTs + j * 1024), 16,
                                                (int)((tr * ldT + 8 * tc) * 2), key0 * 2, 0, 0);
     }

@@ -293,7 +293,7 @@ __global__ void __launch_bounds__(256) k_rope_qkv(T* qkv, T* qkvT, int64_t ldT, 
   for (int idx = threadIdx.x; idx < 64 * hd; idx += 256) {
     int c = idx / 64, r = idx % 64;
     int64_t m = m0 + r;
-    if (m < M) qkvT[(col0 + c) * ldT + m] = stf<T>(tile[r][c]);
+    if (m < M) qkvT[(col0 + c) * ldT + attn_token_col(m, M)] = stf<T>(tile[r][c]);
   }
 }
 
@@ -354,13 +354,15 @@ __global__ void __launch_bounds__(256) k_rope_qkv_bf16(uint16_t* __restrict__ qk
       *(uint4*)(qkv + (m0 + r) * ld + col0 + 8 * c8) = pack8(f);
     }
   }
+  // 64 whole tokens (m0 % 64 == 0): column m0 + j holds token m0 + j with
+  // bits 2 and 3 of j swapped (attention's token order).
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int id = threadIdx.x + 256 * k;
     const int c = id >> 3, t8 = id & 7;
     float f[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = tile[8 * t8 + e][c];
+    for (int e = 0; e < 8; ++e) f[e] = tile[(int)attn_token_col(8 * t8 + e, 64)][c];
     *(uint4*)(qkvT + (col0 + c) * ldT + m0 + 8 * t8) = pack8(f);
   }
 }
@@ -551,7 +553,8 @@ void sum_fixed(const float* x, float* out, int n, float scale, hipStream_t s) {
 }
 
 // ------------------------------------------------------------ transpose --
-template <typename T>
+// TOKENS: the rows of `in` are tokens, placed in attention's token order.
+template <typename T, bool TOKENS>
 __global__ void __launch_bounds__(256) k_transpose(const T* in, int64_t ld_in, T* out, int64_t ld_out, int R, int C) {
   __shared__ T tile[64][65];
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
@@ -562,13 +565,16 @@ __global__ void __launch_bounds__(256) k_transpose(const T* in, int64_t ld_in, T
   __syncthreads();
   for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
     int c = idx / 64, r = idx % 64;
-    if (r0 + r < R && c0 + c < C) out[(c0 + c) * ld_out + r0 + r] = tile[r][c];
+    if (r0 + r < R && c0 + c < C)
+      out[(c0 + c) * ld_out + (TOKENS ? attn_token_col(r0 + r, R) : r0 + r)] = tile[r][c];
   }
 }
 
 // bf16 64x64 tile with 16-byte global loads and stores (8 elements per
 // access); rows and columns of the tile that fall outside R x C are skipped
-// per 8-element group, so R, C, ld_in, ld_out must be multiples of 8.
+// per 8-element group, so R, C, ld_in, ld_out must be multiples of 8
+// (TOKENS: R a multiple of 16, so that every 16-group is whole).
+template <bool TOKENS>
 __global__ void __launch_bounds__(256) k_transpose_bf16(const uint16_t* __restrict__ in, int64_t ld_in,
                                                         uint16_t* __restrict__ out, int64_t ld_out, int R, int C) {
   __shared__ uint16_t tile[64][66];
@@ -595,22 +601,37 @@ __global__ void __launch_bounds__(256) k_transpose_bf16(const uint16_t* __restri
     if (c0 + c < C && r0 + r8 < R) {
       uint32_t w[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = (uint32_t)tile[r8 + 2 * i][c] | ((uint32_t)tile[r8 + 2 * i + 1][c] << 16);
+      for (int i = 0; i < 4; ++i) {
+        const int ra = TOKENS ? (int)attn_token_col(r8 + 2 * i, 64) : r8 + 2 * i;
+        const int rb = TOKENS ? (int)attn_token_col(r8 + 2 * i + 1, 64) : r8 + 2 * i + 1;
+        w[i] = (uint32_t)tile[ra][c] | ((uint32_t)tile[rb][c] << 16);
+      }
       *(uint4*)(out + (c0 + c) * ld_out + r0 + r8) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
 }
 
-template <typename T>
-void transpose(const T* in, int64_t ld_in, T* out, int64_t ld_out, int R, int C, hipStream_t s) {
+template <typename T, bool TOKENS>
+void transpose_any(const T* in, int64_t ld_in, T* out, int64_t ld_out, int R, int C, hipStream_t s) {
   if (R <= 0 || C <= 0) return;
-  if (std::is_same<T, uint16_t>::value && R % 8 == 0 && C % 8 == 0 && ld_in % 8 == 0 && ld_out % 8 == 0 &&
-      ((uintptr_t)in & 15) == 0 && ((uintptr_t)out & 15) == 0) {
-    hipLaunchKernelGGL(k_transpose_bf16, dim3(cdiv(C, 64), cdiv(R, 64)), dim3(256), 0, s, (const uint16_t*)in, ld_in,
-                       (uint16_t*)out, ld_out, R, C);
+  if (std::is_same<T, uint16_t>::value && R % (TOKENS ? 16 : 8) == 0 && C % 8 == 0 && ld_in % 8 == 0 &&
+      ld_out % 8 == 0 && ((uintptr_t)in & 15) == 0 && ((uintptr_t)out & 15) == 0) {
+    hipLaunchKernelGGL(k_transpose_bf16<TOKENS>, dim3(cdiv(C, 64), cdiv(R, 64)), dim3(256), 0, s, (const uint16_t*)in,
+                       ld_in, (uint16_t*)out, ld_out, R, C);
     return;
   }
-  hipLaunchKernelGGL(k_transpose<T>, dim3(cdiv(C, 64), cdiv(R, 64)), dim3(256), 0, s, in, ld_in, out, ld_out, R, C);
+  hipLaunchKernelGGL((k_transpose<T, TOKENS>), dim3(cdiv(C, 64), cdiv(R, 64)), dim3(256), 0, s, in, ld_in, out, ld_out,
+                     R, C);
+}
+
+template <typename T>
+void transpose(const T* in, int64_t ld_in, T* out, int64_t ld_out, int R, int C, hipStream_t s) {
+  transpose_any<T, false>(in, ld_in, out, ld_out, R, C, s);
+}
+
+template <typename T>
+void transpose_tokens(const T* in, int64_t ld_in, T* out, int64_t ld_out, int M, int C, hipStream_t s) {
+  transpose_any<T, true>(in, ld_in, out, ld_out, M, C, s);
 }
 
 template <typename T>
@@ -661,6 +682,7 @@ void fill_u32(void* p, uint32_t value, size_t n_words, hipStream_t s) {
   template void swiglu_bwd<T>(const T*, const T*, T*, int, int, hipStream_t);                                   \
   template void xent<T>(const float*, const int32_t*, float*, T*, int, int, int, float, hipStream_t);           \
   template void transpose<T>(const T*, int64_t, T*, int64_t, int, int, hipStream_t);                            \
+  template void transpose_tokens<T>(const T*, int64_t, T*, int64_t, int, int, hipStream_t);                     \
   template void cast_transpose<T>(const float*, T*, T*, int64_t, int, int, hipStream_t);
 
 MT_INST(float)

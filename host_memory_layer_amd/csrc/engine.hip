@@ -354,7 +354,7 @@ struct Model {
     gemm<T>(ws.dxbT, Mp, ws.tmpT, Mp, g.o, d, nullptr, 0, d, d, M, EPI_STORE);
     gemm<T>(ws.dxb, d, wt_.o, d, ws.do_, d, nullptr, 0, M, d, d, EPI_STORE);
     // attention
-    transpose<T>(ws.do_, d, ws.doT, Mp, M, d, sc);
+    transpose_tokens<T>(ws.do_, d, ws.doT, Mp, M, d, sc);
     attn_bwd_dsum<T>(ws.do_, a.o, ws.Dsum, B, Tq, H, hd, sc);
     const bool timed = cfg.flags & MT_FLAG_TIME_KERNELS;
     if (timed) record_kernel_start(2.5 * attn_fwd_flops(), 1);

@@ -61,6 +61,19 @@ int mt_transpose(int32_t dtype, const void* in, int64_t ld_in, void* out, int64_
   });
 }
 
+int mt_transpose_tokens(int32_t dtype, const void* in, int64_t ld_in, void* out, int64_t ld_out, int32_t M,
+                        int32_t C, void* stream) {
+  return kguard([&] {
+    need(ld_in >= C && ld_out >= M, "leading dimensions");
+    if (dtype == MT_BF16)
+      transpose_tokens<uint16_t>((const uint16_t*)in, ld_in, (uint16_t*)out, ld_out, M, C, (hipStream_t)stream);
+    else if (dtype == MT_F32)
+      transpose_tokens<float>((const float*)in, ld_in, (float*)out, ld_out, M, C, (hipStream_t)stream);
+    else
+      need(false, "dtype");
+  });
+}
+
 int mt_rope_tables(int32_t T, int32_t hd, double theta, float* cos_out, float* sin_out) {
   return kguard([&] {
     need(T > 0 && hd > 0 && hd % 2 == 0 && cos_out && sin_out, "arguments");
