@@ -59,6 +59,22 @@ __device__ inline f32x16_t zero16() {
   return z;
 }
 
+// Workgroups are dealt round-robin to the 8 XCDs in dispatch order (x
+// fastest), and each XCD has its own L2.  The grid's (x, y) is remapped so
+// that XCD k runs a contiguous range of the row-major order (y outer): the
+// blocks of one (batch, head), which read the same K, V (or Q, dO) tiles,
+// share an L2.
+struct BlockXY {
+  int x, y;
+};
+__device__ inline BlockXY xcd_block() {
+  const int n = gridDim.x * gridDim.y;
+  const int i = blockIdx.y * gridDim.x + blockIdx.x;
+  const int q = n / 8, r = n % 8, k = i % 8;
+  const int l = k * q + min(k, r) + i / 8;
+  return BlockXY{l % (int)gridDim.x, l / (int)gridDim.x};
+}
+
 // Row index inside a 32x32 accumulator tile for register r of this lane.
 __device__ inline int acc_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
 
@@ -84,8 +100,9 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
   constexpr int HD = 128;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 32768];
   const int nqb = (T + 127) / 128;
-  const int qb = nqb - 1 - blockIdx.x;
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const BlockXY blk = xcd_block();
+  const int qb = nqb - 1 - blk.x;
+  const int bh = blk.y, b = bh / H, h = bh % H;
   const int d = H * HD;
   const int64_t ld = 3LL * d;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -206,14 +223,24 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
   }
   __syncthreads();
 
-  // O^T accumulators -> LDS [query][hd] -> coalesced rows of o.
-  uint16_t* Os = (uint16_t*)(smem + wave * 8192);
+  // O^T accumulators -> LDS [query][hd] -> coalesced rows of o.  Registers
+  // 4g..4g+3 hold 4 adjacent hd rows of the lane's query: one 8-byte write.
+  // Rows are padded to 272 bytes, so the 32 queries of one write fall on 16
+  // bank groups.
+  constexpr int OLD = HD + 8;
+  uint16_t* Os = (uint16_t*)(smem + wave * (32 * OLD * 2));
   if (active) {
     const float inv_l = 1.0f / l_i;
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Os[(lane & 31) * HD + 32 * ht + acc_row(r, lane)] = f32_to_bf16(acc_o[ht][r] * inv_l);
+      for (int g = 0; g < 4; ++g) {
+        uint2 w;
+        w.x = (uint32_t)f32_to_bf16(acc_o[ht][4 * g] * inv_l) | ((uint32_t)f32_to_bf16(acc_o[ht][4 * g + 1] * inv_l) << 16);
+        w.y = (uint32_t)f32_to_bf16(acc_o[ht][4 * g + 2] * inv_l) |
+              ((uint32_t)f32_to_bf16(acc_o[ht][4 * g + 3] * inv_l) << 16);
+        *(uint2*)(Os + (lane & 31) * OLD + 32 * ht + acc_row(4 * g, lane)) = w;
+      }
     if (lane < 32) lse[(int64_t)bh * T + tq] = m_i + log2f(l_i);
   }
   __syncthreads();
@@ -222,7 +249,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
     for (int i = 0; i < 8; ++i) {
       const int id = lane + 64 * i;
       const int r = id >> 4, ch = id & 15;
-      *(u32x4_t*)(o + (rowbase + q0 + r) * d + h * HD + 8 * ch) = *(const u32x4_t*)(Os + r * HD + 8 * ch);
+      *(u32x4_t*)(o + (rowbase + q0 + r) * d + h * HD + 8 * ch) = *(const u32x4_t*)(Os + r * OLD + 8 * ch);
     }
   }
 }
@@ -278,8 +305,9 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
   uint8_t* Ks = smem;
   uint8_t* Vs = smem + 32768;
 
-  const int kblk = blockIdx.x;
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const BlockXY blk = xcd_block();
+  const int kblk = blk.x;
+  const int bh = blk.y, b = bh / H, h = bh % H;
   const int d = H * HD;
   const int64_t ld = 3LL * d;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -443,8 +471,9 @@ __global__ void __launch_bounds__(256) k_attn_dq_bf16(const uint16_t* __restrict
   constexpr int HD = 128;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 49152];  // K, V [64][128], K^T [128][64]
   const int nqb = (T + 127) / 128;
-  const int qb = nqb - 1 - blockIdx.x;
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const BlockXY blk = xcd_block();
+  const int qb = nqb - 1 - blk.x;
+  const int bh = blk.y, b = bh / H, h = bh % H;
   const int d = H * HD;
   const int64_t ld = 3LL * d;
   const int tid = threadIdx.x, lane = tid & 63;
