@@ -33,6 +33,8 @@
 // LDS layouts are swizzled at 16-byte granularity so that the 16 lanes one
 // ds_read_b128 serves per cycle (16 consecutive tile rows, one logical
 // chunk) fall on 16 different 16-byte bank groups of the 256-byte bank row.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace mt {
@@ -726,10 +728,39 @@ void attn_fwd<float>(const float* qkv, const float*, int64_t, float* o, float* l
   hipLaunchKernelGGL(k_attn_fwd_f32, dim3((T_ + 63) / 64, B * H), dim3(64), 0, s, qkv, o, lse, T_, H, hd);
 }
 
+// bf16, head_dim 128: 16 lanes per (token, head) row, 8 elements (16 bytes)
+// each, summed in a fixed butterfly.
+__global__ void __launch_bounds__(256) k_dsum_bf16(const uint16_t* __restrict__ dO, const uint16_t* __restrict__ O,
+                                                   float* __restrict__ Dsum, int T_, int H, int64_t rows) {
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;  // row = m*H + h
+  const int sub = threadIdx.x & 15;
+  if (row >= rows) return;  // whole 16-lane groups leave together
+  const int64_t off = row * 128 + sub * 8;
+  const u32x4_t a = *(const u32x4_t*)(dO + off);
+  const u32x4_t b = *(const u32x4_t*)(O + off);
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc += bf16_to_f32(a[i] & 0xFFFF) * bf16_to_f32(b[i] & 0xFFFF);
+    acc += bf16_to_f32(a[i] >> 16) * bf16_to_f32(b[i] >> 16);
+  }
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (sub == 0) {
+    const int64_t m = row / H, bb = m / T_, t = m % T_;
+    Dsum[(bb * H + row % H) * T_ + t] = acc;
+  }
+}
+
 template <typename T>
 void attn_bwd_dsum(const T* dO, const T* O, float* Dsum, int B, int T_, int H, int hd, hipStream_t s) {
   const int64_t rows = (int64_t)B * T_ * H;
   if (rows <= 0) return;
+  if (std::is_same<T, uint16_t>::value && hd == 128 && ((uintptr_t)dO & 15) == 0 && ((uintptr_t)O & 15) == 0) {
+    hipLaunchKernelGGL(k_dsum_bf16, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, (const uint16_t*)dO,
+                       (const uint16_t*)O, Dsum, T_, H, rows);
+    return;
+  }
   hipLaunchKernelGGL(k_dsum<T>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, dO, O, Dsum, T_, H, hd, rows);
 }
 template void attn_bwd_dsum<float>(const float*, const float*, float*, int, int, int, int, hipStream_t);

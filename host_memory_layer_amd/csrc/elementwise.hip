@@ -224,12 +224,38 @@ __global__ void __launch_bounds__(256) k_rmsnorm_bwd(const float* __restrict__ d
 }
 
 template <typename T>
-__global__ void __launch_bounds__(256) k_dg_reduce(const float* part, T* dg, int chunks, int d) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= d) return;
-  float acc = 0.f;
-  for (int k = 0; k < chunks; ++k) acc += part[(int64_t)k * d + c];
-  dg[c] = stf<T>(acc);
+__global__ void __launch_bounds__(256) k_dg_reduce(const float* __restrict__ part, T* __restrict__ dg, int chunks,
+                                                   int d) {
+  // One block: 32 columns (8 threads x float4) x 32 interleaved partial
+  // sums; partial g adds chunks g, g+32, g+64, ... in order, then the 32
+  // partials are added in order.  The order depends only on (chunks, d).
+  __shared__ float4 red[32][8];
+  const int c4 = threadIdx.x & 7, g = threadIdx.x >> 3;
+  const int c = (blockIdx.x * 8 + c4) * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (c < d) {
+#pragma unroll 4
+    for (int k = g; k < chunks; k += 32) {
+      const float4 v = *(const float4*)(part + (int64_t)k * d + c);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+  }
+  red[g][c4] = acc;
+  __syncthreads();
+  if (g == 0 && c < d) {
+    float4 t = red[0][c4];
+    for (int j = 1; j < 32; ++j) {
+      const float4 v = red[j][c4];
+      t.x += v.x;
+      t.y += v.y;
+      t.z += v.z;
+      t.w += v.w;
+    }
+    V4<T>::st(dg + c, t);
+  }
 }
 
 template <typename T>
@@ -244,7 +270,7 @@ void rmsnorm_bwd(const float* dy, const float* x, const T* g, const float* rstd,
     MT_RMS_DISPATCH(rms_vpt(d), L_)
 #undef L_
   }
-  hipLaunchKernelGGL(k_dg_reduce<T>, dim3(cdiv(d, 256)), dim3(256), 0, s, partial, dg, blocks, d);
+  hipLaunchKernelGGL(k_dg_reduce<T>, dim3(cdiv(d, 32)), dim3(256), 0, s, partial, dg, blocks, d);
 }
 
 // ----------------------------------------------------------------- RoPE --
@@ -574,40 +600,44 @@ __global__ void __launch_bounds__(256) k_transpose(const T* in, int64_t ld_in, T
 // access); rows and columns of the tile that fall outside R x C are skipped
 // per 8-element group, so R, C, ld_in, ld_out must be multiples of 8
 // (TOKENS: R a multiple of 16, so that every 16-group is whole).
+//
+// The tile sits in LDS row-major, 128 bytes per input row, 16-byte chunk j
+// of row r at chunk j ^ ((r >> 3) & 7).  Each thread reads the 4-byte column
+// pair (2p, 2p+1) of 8 consecutive rows and packs the two output runs with
+// byte permutes; the 8 lanes of one output row cover 128 contiguous bytes.
 template <bool TOKENS>
 __global__ void __launch_bounds__(256) k_transpose_bf16(const uint16_t* __restrict__ in, int64_t ld_in,
                                                         uint16_t* __restrict__ out, int64_t ld_out, int R, int C) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[64 * 128];
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int id = threadIdx.x + 256 * k;
-    const int r = id >> 3, c8 = (id & 7) * 8;
-    if (r0 + r < R && c0 + c8 < C) {
-      const uint4 u = *(const uint4*)(in + (r0 + r) * ld_in + c0 + c8);
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        tile[r][c8 + 2 * i] = (uint16_t)(w[i] & 0xFFFF);
-        tile[r][c8 + 2 * i + 1] = (uint16_t)(w[i] >> 16);
-      }
-    }
+    const int r = id >> 3, c8 = id & 7;
+    if (r0 + r < R && c0 + 8 * c8 < C)
+      *(uint4*)(tile + r * 128 + ((c8 ^ ((r >> 3) & 7)) << 4)) =
+          *(const uint4*)(in + (r0 + r) * ld_in + c0 + 8 * c8);
   }
   __syncthreads();
+  const int p = threadIdx.x >> 3, r8 = (threadIdx.x & 7) * 8;
+  if (c0 + 2 * p < C && r0 + r8 < R) {
+    uint32_t w[8];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int id = threadIdx.x + 256 * k;
-    const int c = id >> 3, r8 = (id & 7) * 8;
-    if (c0 + c < C && r0 + r8 < R) {
-      uint32_t w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ra = TOKENS ? (int)attn_token_col(r8 + 2 * i, 64) : r8 + 2 * i;
-        const int rb = TOKENS ? (int)attn_token_col(r8 + 2 * i + 1, 64) : r8 + 2 * i + 1;
-        w[i] = (uint32_t)tile[ra][c] | ((uint32_t)tile[rb][c] << 16);
-      }
-      *(uint4*)(out + (c0 + c) * ld_out + r0 + r8) = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int i = 0; i < 8; ++i) {
+      const int rr = TOKENS ? (int)attn_token_col(r8 + i, 64) : r8 + i;
+      w[i] = *(const uint32_t*)(tile + rr * 128 + (((p >> 2) ^ ((rr >> 3) & 7)) << 4) + ((p & 3) << 2));
     }
+    uint4 lo, hi;  // output columns 2p and 2p+1: the low and high halves of w
+    lo.x = __builtin_amdgcn_perm(w[1], w[0], 0x05040100u);
+    lo.y = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
+    lo.z = __builtin_amdgcn_perm(w[5], w[4], 0x05040100u);
+    lo.w = __builtin_amdgcn_perm(w[7], w[6], 0x05040100u);
+    hi.x = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
+    hi.y = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
+    hi.z = __builtin_amdgcn_perm(w[5], w[4], 0x07060302u);
+    hi.w = __builtin_amdgcn_perm(w[7], w[6], 0x07060302u);
+    *(uint4*)(out + (c0 + 2 * p) * ld_out + r0 + r8) = lo;
+    *(uint4*)(out + (c0 + 2 * p + 1) * ld_out + r0 + r8) = hi;
   }
 }
 

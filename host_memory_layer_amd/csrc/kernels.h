@@ -30,7 +30,8 @@ template <typename T>
 void rmsnorm_fwd(const float* x, const T* g, T* y, float* rstd, int M, int d, float eps, hipStream_t s);
 // dx = resid + r*(dy*g - xh*mean(dy*g*xh)), xh = x*r (resid may be null),
 // and dg = sum_rows dy*xh written as T: per-block partial sums in `partial`
-// (rmsnorm_dg_partial_elems(M, d) floats), then added in block order.
+// (rmsnorm_dg_partial_elems(M, d) floats), then added in a fixed order that
+// depends only on (M, d).
 size_t rmsnorm_dg_partial_elems(int M, int d);
 template <typename T>
 void rmsnorm_bwd(const float* dy, const float* x, const T* g, const float* rstd, const float* resid, float* dx,
