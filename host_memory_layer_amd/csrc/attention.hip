@@ -466,12 +466,15 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
 }
 
 // ----------------------------------------------------------- backward dQ --
-__global__ void __launch_bounds__(256) k_attn_dq_bf16(const uint16_t* __restrict__ qkv,
+__global__ void __launch_bounds__(256, 2) k_attn_dq_bf16(const uint16_t* __restrict__ qkv,
                                                     const uint16_t* __restrict__ qkvT, const uint16_t* __restrict__ dO,
                                                     const float* __restrict__ lse, const float* __restrict__ Dsum,
                                                     uint16_t* __restrict__ dqkvT, int64_t ldT, int T, int H) {
   constexpr int HD = 128;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 49152];  // K, V [64][128], K^T [128][64]
+  // Two stages of 32 keys: K, V [32 keys x 256 B] and K^T [128 hd x 64 B],
+  // 24 KiB each, so that two blocks share a CU.
+  constexpr int KB = 32, STAGE = 3 * 8192;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
   const int nqb = (T + 127) / 128;
   const BlockXY blk = xcd_block();
   const int qb = nqb - 1 - blk.x;
@@ -501,28 +504,28 @@ __global__ void __launch_bounds__(256) k_attn_dq_bf16(const uint16_t* __restrict
     D_q = Dsum[(int64_t)bh * T + tq];
   }
 
-  const int nkb = min(T, (qb + 1) * 128) / 64;
+  const int nkb = min(T, (qb + 1) * 128) / KB;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(qkv + rowbase * ld + d + h * HD), 0, (int)((int64_t)T * ld * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(qkv + rowbase * ld + 2 * d + h * HD), 0, (int)((int64_t)T * ld * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t ktrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(qkvT + (int64_t)(d + h * HD) * ldT + rowbase), 0, (int)((int64_t)HD * ldT * 2), 0x00020000);
-  // K, V [64 keys x 256 B] and K^T [128 hd x 128 B]: 16 direct-load
-  // kilobytes each; wave w writes kilobytes 4w .. 4w+3 of each.
+  // 8 direct-load kilobytes per tile; wave w writes kilobytes 2w, 2w+1 of
+  // each: 4 rows of 256 B (K, V) or 16 rows of 64 B (K^T) per kilobyte.
   auto issue = [&](int kb, int buf) {
-    uint8_t* Ks = smem + buf * 49152;
-    uint8_t* Vs = Ks + 16384;
-    uint8_t* KTs = Vs + 16384;
-    const int key0 = kb * 64;
+    uint8_t* Ks = smem + buf * STAGE;
+    uint8_t* Vs = Ks + 8192;
+    uint8_t* KTs = Vs + 8192;
+    const int key0 = kb * KB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = wave * 4 + i;
+    for (int i = 0; i < 2; ++i) {
+      const int j = wave * 2 + i;
       const int r = 4 * j + (lane >> 4), ch = (lane & 15) ^ (r & 15);
       const int voff = (r * ld + 8 * ch) * 2, soff = (int)((int64_t)key0 * ld * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_t*)(Ks + j * 1024), 16, voff, soff, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void_t*)(Vs + j * 1024), 16, voff, soff, 0, 0);
-      const int tr = 8 * j + (lane >> 3), tc = (lane & 7) ^ ((tr >> 1) & 7);
+      const int tr = 16 * j + (lane >> 2), tc = (lane & 3) ^ ((tr >> 2) & 3);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ktrsrc, (lds_void_t*)(KTs + j * 1024), 16,
                                                (int)((tr * ldT + 8 * tc) * 2), key0 * 2, 0, 0);
     }
@@ -538,15 +541,15 @@ __global__ void __launch_bounds__(256) k_attn_dq_bf16(const uint16_t* __restrict
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (kb + 1 < nkb) issue(kb + 1, buf ^ 1);
-    const uint8_t* Ks = smem + buf * 49152;
-    const uint8_t* Vs = Ks + 16384;
-    const uint8_t* KTs = Vs + 16384;
-    // Every wave runs every key sub-tile: one wholly after the wave's
-    // queries gets P = 0 from the causal mask.
+    const uint8_t* Ks = smem + buf * STAGE;
+    const uint8_t* Vs = Ks + 8192;
+    const uint8_t* KTs = Vs + 8192;
+    // Every wave runs every key tile: one wholly after the wave's queries
+    // gets P = 0 from the causal mask.
     {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int kstart = kb * 64 + 32 * kt;
+      {
+        const int kt = 0;
+        const int kstart = kb * KB;
         f32x16_t s_acc = zero16(), dp_acc = zero16();
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
@@ -576,7 +579,7 @@ __global__ void __launch_bounds__(256) k_attn_dq_bf16(const uint16_t* __restrict
           const bf16x8_t dsf = acc_to_frag(dp_acc, ks);
 #pragma unroll
           for (int ht = 0; ht < 4; ++ht) {
-            const bf16x8_t kT = frag_T(KTs, 32 * ht + (lane & 31), 32 * kt + 16 * ks, lane);
+            const bf16x8_t kT = frag_T64(KTs, 32 * ht + (lane & 31), 16 * ks, lane);
             acc_dq[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kT, dsf, acc_dq[ht], 0, 0, 0);
           }
         }
