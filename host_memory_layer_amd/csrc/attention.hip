@@ -49,10 +49,12 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Swizzled byte offsets for rows of 256 bytes (16 chunks) and of 128 bytes
-// (8 chunks; two rows share a bank row, so the key is row/2).
-__device__ inline int sw256(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
-__device__ inline int sw128(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+// Swizzled byte offsets for rows of 256 bytes (16 chunks).  The key swaps the two bit pairs of row % 16: any 16 consecutive rows get 16
+// different keys (row reads of one logical chunk), and the 4 rows r..r+3
+// (r % 4 == 0) move a group of 4 adjacent chunks to 4 different quarters of
+// the bank row (transposing reads).
+__device__ inline int swkey(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ inline int sw256(int row, int chunk) { return row * 256 + ((chunk ^ swkey(row)) << 4); }
 
 __device__ inline f32x16_t zero16() {
   f32x16_t z;
@@ -80,11 +82,31 @@ __device__ inline BlockXY xcd_block() {
 // Row index inside a 32x32 accumulator tile for register r of this lane.
 __device__ inline int acc_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
 
-// Fragment of a transposed tile in attention's token order (rows of 64
-// tokens, 128 bytes) for the contraction slice of 16 tokens starting at
-// column c0: chunk c0/8 + h.
-__device__ inline bf16x8_t frag_T(const uint8_t* base, int row, int c0, int lane) {
-  return *(const bf16x8_t*)(base + sw128(row, (c0 >> 3) + (lane >> 5)));
+// Transposed fragment from a row-major tile with 256-byte rows (128 bf16,
+// sw256), by two transposing LDS reads (ds_read_b64_tr_b16).  For the MFMA
+// A operand X^T (rows = tile columns c0 .. c0+31, contraction = tile rows
+// r0 .. r0+15), lane l gets column c0 + (l & 31) at rows
+// r0 + 8*(e/4) + 4*(l/32) + e%4 for element e: the pairing of a B operand
+// taken from an accumulator.
+//
+// A transposing read works on groups of 16 lanes: output lane i, element e
+// is element i%4 of the 8 bytes addressed by lane 4e + i/4 of its group.  So
+// lane 4e + j of group g addresses row r0 + 4*(g/2) + e (+8 for the second
+// read), columns c0 + 16*(g%2) + 4j .. +3, and output lane i receives
+// column c0 + 16*(g%2) + i of rows e = 0..3.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+__device__ inline bf16x8_t frag_tr(const uint8_t* tile, int r0, int c0, int lane) {
+  const int g = lane >> 4, e = (lane >> 2) & 3, j = lane & 3;
+  const int col = c0 + 16 * (g & 1) + 4 * j;
+  const int ra = r0 + 4 * (g >> 1) + e, rb = ra + 8;
+  const uint8_t* pa = tile + sw256(ra, col >> 3) + (col & 7) * 2;
+  const uint8_t* pb = tile + sw256(rb, col >> 3) + (col & 7) * 2;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(const void*)pa);
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(const void*)pb);
+  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x8_t f = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, f);
 }
 
 // Registers 8*ks .. 8*ks+7 of an accumulator tile, as a bf16 B operand.
@@ -122,14 +144,14 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
   }
 
   const int nkb = min(T, (qb + 1) * 128) / 64;
-  // K [64 keys x 256 B] and V^T [128 hd x 128 B] tiles go global -> LDS with
-  // buffer_load ... lds; kilobyte j = wave*4 + i of a tile is written by one
-  // instruction, so each lane's source is chosen to land in the swizzled
-  // layout the fragment reads expect.
+  // K and V tiles [64 keys x 256 B] go global -> LDS with buffer_load ...
+  // lds; kilobyte j = wave*4 + i of a tile is written by one instruction, so
+  // each lane's source is chosen to land in the swizzled layout the fragment
+  // reads expect.  V^T fragments come from the V tile by transposing reads.
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(qkv + rowbase * ld + d + h * HD), 0, (int)((int64_t)T * ld * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(qkvT + (int64_t)(2 * d + h * HD) * ldT + rowbase), 0, (int)((int64_t)HD * ldT * 2), 0x00020000);
+      (void*)(qkv + rowbase * ld + 2 * d + h * HD), 0, (int)((int64_t)T * ld * 2), 0x00020000);
   auto issue = [&](int kb, int buf) {
     uint8_t* Ks = smem + buf * 32768;
     uint8_t* Vs = Ks + 16384;
@@ -137,12 +159,10 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = wave * 4 + i;
-      const int kr = 4 * j + (lane >> 4), kc = (lane & 15) ^ (kr & 15);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_t*)(Ks + j * 1024), 16, (int)((kr * ld + 8 * kc) * 2),
-                                               (int)((int64_t)key0 * ld * 2), 0, 0);
-      const int vr = 8 * j + (lane >> 3), vc = (lane & 7) ^ ((vr >> 1) & 7);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void_t*)(Vs + j * 1024), 16, (int)((vr * ldT + 8 * vc) * 2),
-                                               key0 * 2, 0, 0);
+      const int kr = 4 * j + (lane >> 4), kc = (lane & 15) ^ swkey(kr);
+      const int off = (int)((kr * ld + 8 * kc) * 2), soff = (int)((int64_t)key0 * ld * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_t*)(Ks + j * 1024), 16, off, soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void_t*)(Vs + j * 1024), 16, off, soff, 0, 0);
     }
   };
 
@@ -217,7 +237,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
         const bf16x8_t pf = acc_to_frag(s_acc[ks >> 1], ks & 1);
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) {
-          const bf16x8_t vf = frag_T(Vs, 32 * ht + (lane & 31), 16 * ks, lane);
+          const bf16x8_t vf = frag_tr(Vs, 16 * ks, 32 * ht, lane);
           acc_o[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc_o[ht], 0, 0, 0);
         }
       }
@@ -282,15 +302,6 @@ __global__ void __launch_bounds__(256) k_dsum(const T* dO, const T* O, float* Ds
 }
 
 // ------------------------------------------------------- backward dK dV --
-// 64-byte rows (32 bf16): 16-byte chunk c stored at c ^ ((row >> 2) & 3).
-__device__ inline int sw64(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4); }
-
-// Fragment of a transposed tile in attention's token order with 64-byte
-// rows (32 tokens) for the contraction slice starting at column c0.
-__device__ inline bf16x8_t frag_T64(const uint8_t* base, int row, int c0, int lane) {
-  return *(const bf16x8_t*)(base + sw64(row, (c0 >> 3) + (lane >> 5)));
-}
-
 // One block = 128 keys of one (batch, head); query tiles of 32 stream
 // through a double-buffered LDS ring filled by buffer_load ... lds.
 __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restrict__ qkv,
@@ -302,7 +313,7 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
   constexpr int HD = 128;
   constexpr int QT = 32;                       // queries per tile
   constexpr int TILE = QT * HD * 2;            // 8 KiB per operand tile
-  constexpr int STAGE = 4 * TILE + 512;        // Q, dO, Q^T, dO^T, lse, D
+  constexpr int STAGE = 2 * TILE + 512;        // Q, dO, lse, D
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 32768 + 2 * STAGE];
   uint8_t* Ks = smem;
   uint8_t* Vs = smem + 32768;
@@ -338,30 +349,20 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
       (void*)(qkv + rowbase * ld + h * HD), 0, (int)((int64_t)T * ld * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(dO + rowbase * d + h * HD), 0, (int)((int64_t)T * d * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t qtrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(qkvT + (int64_t)(h * HD) * ldT + rowbase), 0, (int)((int64_t)HD * ldT * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t otrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(dOT + (int64_t)(h * HD) * ldT + rowbase), 0, (int)((int64_t)HD * ldT * 2), 0x00020000);
-  // Each operand tile is 8 KiB = 8 direct-load kilobytes: wave w writes
-  // kilobytes 2w and 2w+1 of each of the four tiles.
+  // Each operand tile is 8 KiB = 8 direct-load kilobytes (4 rows of 256 B
+  // each): wave w writes kilobytes 2w and 2w+1 of both tiles.  Q^T and dO^T
+  // fragments come from the same tiles by transposing reads.
   auto issue = [&](int n, int buf) {
     uint8_t* st = smem + 65536 + buf * STAGE;
     const int q0 = n * QT;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int j = wave * 2 + i;
-      // row-major tiles: 4 rows of 256 B per kilobyte
-      const int r = 4 * j + (lane >> 4), ch = (lane & 15) ^ (r & 15);
+      const int r = 4 * j + (lane >> 4), ch = (lane & 15) ^ swkey(r);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, (lds_void_t*)(st + j * 1024), 16, (int)((r * ld + 8 * ch) * 2),
                                                (int)((int64_t)q0 * ld * 2), 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(orsrc, (lds_void_t*)(st + TILE + j * 1024), 16,
                                                (int)((r * d + 8 * ch) * 2), (int)((int64_t)q0 * d * 2), 0, 0);
-      // transposed tiles: 16 rows of 64 B per kilobyte
-      const int tr = 16 * j + (lane >> 2), tc = (lane & 3) ^ ((tr >> 2) & 3);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qtrsrc, (lds_void_t*)(st + 2 * TILE + j * 1024), 16,
-                                               (int)((tr * ldT + 8 * tc) * 2), q0 * 2, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(otrsrc, (lds_void_t*)(st + 3 * TILE + j * 1024), 16,
-                                               (int)((tr * ldT + 8 * tc) * 2), q0 * 2, 0, 0);
     }
   };
   float ld_stat = 0.f;  // lse (threads 0..31) or D (threads 32..63) of the next tile
@@ -372,7 +373,7 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
     }
   };
   auto store_stats = [&](int buf) {
-    if (tid < 64) ((float*)(smem + 65536 + buf * STAGE + 4 * TILE))[tid] = ld_stat;
+    if (tid < 64) ((float*)(smem + 65536 + buf * STAGE + 2 * TILE))[tid] = ld_stat;
   };
 
   f32x16_t acc_dk[4], acc_dv[4];
@@ -399,9 +400,7 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
     const uint8_t* st = smem + 65536 + buf * STAGE;
     const uint8_t* Qs = st;
     const uint8_t* dOs = st + TILE;
-    const uint8_t* QTs = st + 2 * TILE;
-    const uint8_t* dOTs = st + 3 * TILE;
-    const float* lse_s = (const float*)(st + 4 * TILE);
+    const float* lse_s = (const float*)(st + 2 * TILE);
     const float* D_s = lse_s + 32;
     const int qbase = n * QT;
     // Every wave runs every tile: a tile wholly before the wave's keys gets
@@ -444,9 +443,9 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
         const bf16x8_t dsf = acc_to_frag(dp_acc, ks);
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) {
-          const bf16x8_t oT = frag_T64(dOTs, 32 * ht + (lane & 31), 16 * ks, lane);
+          const bf16x8_t oT = frag_tr(dOs, 16 * ks, 32 * ht, lane);
           acc_dv[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oT, pf, acc_dv[ht], 0, 0, 0);
-          const bf16x8_t qT = frag_T64(QTs, 32 * ht + (lane & 31), 16 * ks, lane);
+          const bf16x8_t qT = frag_tr(Qs, 16 * ks, 32 * ht, lane);
           acc_dk[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qT, dsf, acc_dk[ht], 0, 0, 0);
         }
       }
@@ -471,9 +470,9 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq_bf16(const uint16_t* __restr
                                                     const float* __restrict__ lse, const float* __restrict__ Dsum,
                                                     uint16_t* __restrict__ dqkvT, int64_t ldT, int T, int H) {
   constexpr int HD = 128;
-  // Two stages of 32 keys: K, V [32 keys x 256 B] and K^T [128 hd x 64 B],
-  // 24 KiB each, so that two blocks share a CU.
-  constexpr int KB = 32, STAGE = 3 * 8192;
+  // Two stages of 32 keys: K, V [32 keys x 256 B], 16 KiB each (K^T
+  // fragments come from the K tile by transposing reads).
+  constexpr int KB = 32, STAGE = 2 * 8192;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
   const int nqb = (T + 127) / 128;
   const BlockXY blk = xcd_block();
@@ -509,25 +508,19 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq_bf16(const uint16_t* __restr
       (void*)(qkv + rowbase * ld + d + h * HD), 0, (int)((int64_t)T * ld * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(qkv + rowbase * ld + 2 * d + h * HD), 0, (int)((int64_t)T * ld * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t ktrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(qkvT + (int64_t)(d + h * HD) * ldT + rowbase), 0, (int)((int64_t)HD * ldT * 2), 0x00020000);
-  // 8 direct-load kilobytes per tile; wave w writes kilobytes 2w, 2w+1 of
-  // each: 4 rows of 256 B (K, V) or 16 rows of 64 B (K^T) per kilobyte.
+  // 8 direct-load kilobytes per tile (4 rows of 256 B each); wave w writes
+  // kilobytes 2w, 2w+1 of each.
   auto issue = [&](int kb, int buf) {
     uint8_t* Ks = smem + buf * STAGE;
     uint8_t* Vs = Ks + 8192;
-    uint8_t* KTs = Vs + 8192;
     const int key0 = kb * KB;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int j = wave * 2 + i;
-      const int r = 4 * j + (lane >> 4), ch = (lane & 15) ^ (r & 15);
+      const int r = 4 * j + (lane >> 4), ch = (lane & 15) ^ swkey(r);
       const int voff = (r * ld + 8 * ch) * 2, soff = (int)((int64_t)key0 * ld * 2);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_t*)(Ks + j * 1024), 16, voff, soff, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void_t*)(Vs + j * 1024), 16, voff, soff, 0, 0);
-      const int tr = 16 * j + (lane >> 2), tc = (lane & 3) ^ ((tr >> 2) & 3);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ktrsrc, (lds_void_t*)(KTs + j * 1024), 16,
-                                               (int)((tr * ldT + 8 * tc) * 2), key0 * 2, 0, 0);
     }
   };
 
@@ -543,7 +536,6 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq_bf16(const uint16_t* __restr
     if (kb + 1 < nkb) issue(kb + 1, buf ^ 1);
     const uint8_t* Ks = smem + buf * STAGE;
     const uint8_t* Vs = Ks + 8192;
-    const uint8_t* KTs = Vs + 8192;
     // Every wave runs every key tile: one wholly after the wave's queries
     // gets P = 0 from the causal mask.
     {
@@ -579,7 +571,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq_bf16(const uint16_t* __restr
           const bf16x8_t dsf = acc_to_frag(dp_acc, ks);
 #pragma unroll
           for (int ht = 0; ht < 4; ++ht) {
-            const bf16x8_t kT = frag_T64(KTs, 32 * ht + (lane & 31), 16 * ks, lane);
+            const bf16x8_t kT = frag_tr(Ks, 16 * ks, 32 * ht, lane);
             acc_dq[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kT, dsf, acc_dq[ht], 0, 0, 0);
           }
         }

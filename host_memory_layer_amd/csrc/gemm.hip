@@ -364,51 +364,67 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_nt(const uint16_t* __restr
       // whose 4 columns lie past N aim beyond the descriptor
       const int c0 = 4 * (lane >> 5);
       const int ncol = (int)min<int64_t>(BN, N - n0) - wn;  // valid columns of the sub-tile
+      // EPI_ADD_F32: the residual of 32 x 32 block q = 4i + j is loaded one
+      // block ahead.  Vector memory operations complete in issue order, so
+      // waiting for block q leaves block q+1's loads and block q-1's stores
+      // in flight: at most 8.
+      u32x4_t rv[2][4];
+      auto load_res = [&](int q) {
+        const int row = wm + 32 * (q >> 2) + (lane & 31);
+        const int rbase = row * (int)ldr + (int)(n0 + wn) + c0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+        for (int g = 0; g < 4; ++g) {
+          const int col = 32 * (q & 3) + 8 * g;
+          const int off = col + c0 < ncol ? (rbase + col) * 4 : 0x7FFFFFF0;
+          rv[q & 1][g] = __builtin_amdgcn_raw_buffer_load_b128(rrs, off, 0, 0);
+        }
+      };
+      if (EPI == EPI_ADD_F32) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_res(0);
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int i = q >> 2, j = q & 3;
         const int row = wm + 32 * i + (lane & 31);
         const int cbase = row * (int)ldc + (int)(n0 + wn) + c0;
-        const int rbase = EPI == EPI_ADD_F32 ? row * (int)ldr + (int)(n0 + wn) + c0 : 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          u32x4_t rv[4];
-          if (EPI == EPI_ADD_F32) {
-            // the residual of this 32 x 32 block; the wait covers every
-            // earlier memory operation of the wave, earlier stores included
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int col = 32 * j + 8 * g;
-              const int off = col + c0 < ncol ? (rbase + col) * 4 : 0x7FFFFFF0;
-              rv[g] = __builtin_amdgcn_raw_buffer_load_b128(rrs, off, 0, 0);
-            }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __builtin_amdgcn_sched_barrier(0);
-          }
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int col = 32 * j + 8 * g;
-            const int off = col + c0 < ncol ? (cbase + col) * esize : 0x7FFFFFF0;
-            const f32x16_t& v = acc[i][j];
-            if (EPI == EPI_STORE) {
-              u32x2_t pk;
-              pk.x = (uint32_t)f32_to_bf16(v[4 * g]) | ((uint32_t)f32_to_bf16(v[4 * g + 1]) << 16);
-              pk.y = (uint32_t)f32_to_bf16(v[4 * g + 2]) | ((uint32_t)f32_to_bf16(v[4 * g + 3]) << 16);
-              __builtin_amdgcn_raw_buffer_store_b64(pk, crs, off, 0, 0);
-            } else {
-              float o0 = v[4 * g], o1 = v[4 * g + 1], o2 = v[4 * g + 2], o3 = v[4 * g + 3];
-              if (EPI == EPI_ADD_F32) {
-                o0 = __uint_as_float(rv[g].x) + o0;
-                o1 = __uint_as_float(rv[g].y) + o1;
-                o2 = __uint_as_float(rv[g].z) + o2;
-                o3 = __uint_as_float(rv[g].w) + o3;
-              }
-              u32x4_t pk = {__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2), __float_as_uint(o3)};
-              __builtin_amdgcn_raw_buffer_store_b128(pk, crs, off, 0, 0);
-            }
+        if (EPI == EPI_ADD_F32) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (q + 1 < 16) {
+            load_res(q + 1);
+            if (q == 0)
+              asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            else
+              asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+          } else {
+            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = 32 * j + 8 * g;
+          const int off = col + c0 < ncol ? (cbase + col) * esize : 0x7FFFFFF0;
+          const f32x16_t& v = acc[i][j];
+          if (EPI == EPI_STORE) {
+            u32x2_t pk;
+            pk.x = (uint32_t)f32_to_bf16(v[4 * g]) | ((uint32_t)f32_to_bf16(v[4 * g + 1]) << 16);
+            pk.y = (uint32_t)f32_to_bf16(v[4 * g + 2]) | ((uint32_t)f32_to_bf16(v[4 * g + 3]) << 16);
+            __builtin_amdgcn_raw_buffer_store_b64(pk, crs, off, 0, 0);
+          } else {
+            float o0 = v[4 * g], o1 = v[4 * g + 1], o2 = v[4 * g + 2], o3 = v[4 * g + 3];
+            if (EPI == EPI_ADD_F32) {
+              const u32x4_t r = rv[q & 1][g];
+              o0 = __uint_as_float(r.x) + o0;
+              o1 = __uint_as_float(r.y) + o1;
+              o2 = __uint_as_float(r.z) + o2;
+              o3 = __uint_as_float(r.w) + o3;
+            }
+            u32x4_t pk = {__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2), __float_as_uint(o3)};
+            __builtin_amdgcn_raw_buffer_store_b128(pk, crs, off, 0, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     } else {
 #pragma unroll
