@@ -304,7 +304,7 @@ __global__ void __launch_bounds__(256) k_dsum(const T* dO, const T* O, float* Ds
 // ------------------------------------------------------- backward dK dV --
 // One block = 128 keys of one (batch, head); query tiles of 32 stream
 // through a double-buffered LDS ring filled by buffer_load ... lds.
-__global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restrict__ qkv,
+__global__ void __launch_bounds__(256, 2) k_attn_dkdv_bf16(const uint16_t* __restrict__ qkv,
                                                       const uint16_t* __restrict__ qkvT,
                                                       const uint16_t* __restrict__ dO,
                                                       const uint16_t* __restrict__ dOT, const float* __restrict__ lse,
@@ -313,8 +313,9 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
   constexpr int HD = 128;
   constexpr int QT = 32;                       // queries per tile
   constexpr int TILE = QT * HD * 2;            // 8 KiB per operand tile
-  constexpr int STAGE = 2 * TILE + 512;        // Q, dO, lse, D
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 32768 + 2 * STAGE];
+  // K, V (64 KiB) and one stage of Q, dO (16 KiB): 80 KiB, so that two
+  // blocks share a CU and each hides the other's tile loads.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 32768 + 2 * TILE];
   uint8_t* Ks = smem;
   uint8_t* Vs = smem + 32768;
 
@@ -352,8 +353,8 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
   // Each operand tile is 8 KiB = 8 direct-load kilobytes (4 rows of 256 B
   // each): wave w writes kilobytes 2w and 2w+1 of both tiles.  Q^T and dO^T
   // fragments come from the same tiles by transposing reads.
-  auto issue = [&](int n, int buf) {
-    uint8_t* st = smem + 65536 + buf * STAGE;
+  auto issue = [&](int n) {
+    uint8_t* st = smem + 65536;
     const int q0 = n * QT;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -365,15 +366,17 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
                                                (int)((r * d + 8 * ch) * 2), (int)((int64_t)q0 * d * 2), 0, 0);
     }
   };
-  float ld_stat = 0.f;  // lse (threads 0..31) or D (threads 32..63) of the next tile
+  // lse and D of the tile's queries in this lane's accumulator rows: rows
+  // 4g .. 4g+3 are one 16-byte load.
+  float4 ls[4], ds[4];
   auto load_stats = [&](int n) {
-    if (tid < 64) {
-      const int q = n * QT + (tid & 31);
-      ld_stat = tid < 32 ? lse[(int64_t)bh * T + q] : Dsum[(int64_t)bh * T + q];
+    const float* lp = lse + (int64_t)bh * T + n * QT;
+    const float* dp = Dsum + (int64_t)bh * T + n * QT;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      ls[g] = *(const float4*)(lp + acc_row(4 * g, lane));
+      ds[g] = *(const float4*)(dp + acc_row(4 * g, lane));
     }
-  };
-  auto store_stats = [&](int buf) {
-    if (tid < 64) ((float*)(smem + 65536 + buf * STAGE + 2 * TILE))[tid] = ld_stat;
   };
 
   f32x16_t acc_dk[4], acc_dv[4];
@@ -385,23 +388,14 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
   const int key = k0 + (lane & 31);
   const int n0 = kbase / QT, n1 = T / QT;
 
-  issue(n0, 0);
-  load_stats(n0);
-  store_stats(0);
+  const uint8_t* Qs = smem + 65536;
+  const uint8_t* dOs = Qs + TILE;
   for (int n = n0; n < n1; ++n) {
-    const int buf = (n - n0) & 1;
+    if (n > n0) __syncthreads();  // every wave is done with tile n-1
+    issue(n);
+    load_stats(n);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const bool more = n + 1 < n1;
-    if (more) {
-      issue(n + 1, buf ^ 1);
-      load_stats(n + 1);
-    }
-    const uint8_t* st = smem + 65536 + buf * STAGE;
-    const uint8_t* Qs = st;
-    const uint8_t* dOs = st + TILE;
-    const float* lse_s = (const float*)(st + 2 * TILE);
-    const float* D_s = lse_s + 32;
     const int qbase = n * QT;
     // Every wave runs every tile: a tile wholly before the wave's keys gets
     // P = 0 from the causal mask, so the accumulators never leave the MFMA
@@ -418,14 +412,7 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
         const bf16x8_t vf = *(const bf16x8_t*)(Vs + sw256(32 * wave + (lane & 31), ch));
         dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, vf, dp_acc, 0, 0, 0);
       }
-      // rows = queries of the tile, column = this lane's key; the statistics
-      // of 4 consecutive rows come in one 16-byte read
-      float4 ls[4], ds[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        ls[g] = *(const float4*)(lse_s + acc_row(4 * g, lane));
-        ds[g] = *(const float4*)(D_s + acc_row(4 * g, lane));
-      }
+      // rows = queries of the tile, column = this lane's key
       const bool masked = k0 + 31 > qbase;  // wave-uniform
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -450,7 +437,6 @@ __global__ void __launch_bounds__(256) k_attn_dkdv_bf16(const uint16_t* __restri
         }
       }
     }
-    if (more) store_stats(buf ^ 1);
   }
   if (!active) return;
   // dK^T, dV^T: lane = key column, registers = hd rows.
