@@ -10,29 +10,26 @@
 //    queries.  Each wave computes S^T = K . Q^T, so that a lane owns one
 //    query column and the running max / sum stay in the lane (one exchange
 //    with the partner half-wave).  O^T = V^T . P^T takes P^T straight from
-//    the S^T accumulators as the B operand; V^T comes from the transposed
-//    copy qkvT made by the RoPE kernel.  K and V^T tiles of 64 keys are
+//    the S^T accumulators as the B operand.  K and V tiles of 64 keys are
 //    double-buffered in LDS.
 //  * backward, two kernels and no atomics (deterministic):
-//    dK/dV: one block = 128 keys, query tiles of 64 stream through LDS;
-//    S = Q . K^T and dP = dO . V^T have a lane per key, so
-//    dV^T += dO^T . P and dK^T += Q^T . dS take P and dS from registers.
-//    dQ: one block = 128 queries; S^T = K . Q^T, dP^T = V . dO^T,
-//    dQ^T += K^T . dS^T.
-//    Gradients are written transposed into dqkvT [3d x M], coalesced.
+//    dK/dV: one block = 128 keys (K, V held in LDS), query tiles of 32
+//    stream through one LDS stage, two blocks per CU; S = Q . K^T and
+//    dP = dO . V^T have a lane per key, so dV^T += dO^T . P and
+//    dK^T += Q^T . dS take P and dS from registers.
+//    dQ: one block = 128 queries, key tiles of 32 double-buffered, two
+//    blocks per CU; S^T = K . Q^T, dP^T = V . dO^T, dQ^T += K^T . dS^T.
+//    Gradients are written transposed into dqkvT [3d x M].
 //
-// An MFMA contracts over 16 indices; the A and B operands pair their
-// elements by (lane half, element), so any permutation of the contraction
-// index that both operands share is exact.  When P (or dS) comes from an
-// accumulator, element e of lane-half h holds key (or query) 8*(e/4)+4*h+(e%4)
-// of a 16-wide slice.  The transposed operands (qkvT, dOT) store tokens in
-// attention's token order (bits 2 and 3 swapped inside each 16-group), in
-// which exactly those 8 tokens are adjacent: the other operand's fragment is
-// one 16-byte LDS read of chunk 2*slice + h.
-//
-// LDS layouts are swizzled at 16-byte granularity so that the 16 lanes one
-// ds_read_b128 serves per cycle (16 consecutive tile rows, one logical
-// chunk) fall on 16 different 16-byte bank groups of the 256-byte bank row.
+// Every LDS tile is row-major (a token per 256-byte row).  The transposed
+// operands V^T, K^T, Q^T, dO^T are read from those tiles with transposing
+// LDS reads (ds_read_b64_tr_b16), so no transposed copy of q, k, v or dO
+// exists in memory.  An MFMA contracts over 16 indices; the A and B operands
+// pair their elements by (lane half, element), so any permutation of the
+// contraction index that both operands share is exact.  When P (or dS)
+// comes from an accumulator, element e of lane-half h holds key (or query)
+// 8*(e/4)+4*h+(e%4) of a 16-wide slice, and the transposing reads fetch the
+// other operand in the same order.
 #include <type_traits>
 
 #include "kernels.h"
@@ -118,9 +115,8 @@ __device__ inline bf16x8_t acc_to_frag(const f32x16_t& a, int ks) {
 }
 
 // ------------------------------------------------------------ forward ----
-__global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __restrict__ qkv,
-                                                     const uint16_t* __restrict__ qkvT, int64_t ldT,
-                                                     uint16_t* __restrict__ o, float* __restrict__ lse, int T, int H) {
+__global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ o,
+                                                          float* __restrict__ lse, int T, int H) {
   constexpr int HD = 128;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 32768];
   const int nqb = (T + 127) / 128;
@@ -305,11 +301,10 @@ __global__ void __launch_bounds__(256) k_dsum(const T* dO, const T* O, float* Ds
 // One block = 128 keys of one (batch, head); query tiles of 32 stream
 // through a double-buffered LDS ring filled by buffer_load ... lds.
 __global__ void __launch_bounds__(256, 2) k_attn_dkdv_bf16(const uint16_t* __restrict__ qkv,
-                                                      const uint16_t* __restrict__ qkvT,
-                                                      const uint16_t* __restrict__ dO,
-                                                      const uint16_t* __restrict__ dOT, const float* __restrict__ lse,
-                                                      const float* __restrict__ Dsum, uint16_t* __restrict__ dqkvT,
-                                                      int64_t ldT, int T, int H) {
+                                                           const uint16_t* __restrict__ dO,
+                                                           const float* __restrict__ lse,
+                                                           const float* __restrict__ Dsum,
+                                                           uint16_t* __restrict__ dqkvT, int64_t ldT, int T, int H) {
   constexpr int HD = 128;
   constexpr int QT = 32;                       // queries per tile
   constexpr int TILE = QT * HD * 2;            // 8 KiB per operand tile
@@ -452,9 +447,10 @@ __global__ void __launch_bounds__(256, 2) k_attn_dkdv_bf16(const uint16_t* __res
 
 // ----------------------------------------------------------- backward dQ --
 __global__ void __launch_bounds__(256, 2) k_attn_dq_bf16(const uint16_t* __restrict__ qkv,
-                                                    const uint16_t* __restrict__ qkvT, const uint16_t* __restrict__ dO,
-                                                    const float* __restrict__ lse, const float* __restrict__ Dsum,
-                                                    uint16_t* __restrict__ dqkvT, int64_t ldT, int T, int H) {
+                                                         const uint16_t* __restrict__ dO,
+                                                         const float* __restrict__ lse,
+                                                         const float* __restrict__ Dsum,
+                                                         uint16_t* __restrict__ dqkvT, int64_t ldT, int T, int H) {
   constexpr int HD = 128;
   // Two stages of 32 keys: K, V [32 keys x 256 B], 16 KiB each (K^T
   // fragments come from the K tile by transposing reads).
@@ -695,16 +691,13 @@ __global__ void __launch_bounds__(64) k_attn_dkdv_f32(const float* qkv, const fl
 }  // namespace
 
 template <>
-void attn_fwd<uint16_t>(const uint16_t* qkv, const uint16_t* qkvT, int64_t ldT, uint16_t* o, float* lse, int B,
-                        int T_, int H, int hd, hipStream_t s) {
+void attn_fwd<uint16_t>(const uint16_t* qkv, uint16_t* o, float* lse, int B, int T_, int H, int hd, hipStream_t s) {
   if (hd != 128 || T_ % 64) throw ApiError{MT_E_INVALID, "bf16 attention needs head_dim 128, seq_len % 64 == 0"};
-  if (ldT < (int64_t)B * T_ || ldT % 8) throw ApiError{MT_E_INVALID, "ldT must be >= batch*seq_len, multiple of 8"};
-  hipLaunchKernelGGL(k_attn_fwd_bf16, dim3((T_ + 127) / 128, B * H), dim3(256), 0, s, qkv, qkvT, ldT, o, lse, T_, H);
+  hipLaunchKernelGGL(k_attn_fwd_bf16, dim3((T_ + 127) / 128, B * H), dim3(256), 0, s, qkv, o, lse, T_, H);
 }
 
 template <>
-void attn_fwd<float>(const float* qkv, const float*, int64_t, float* o, float* lse, int B, int T_, int H, int hd,
-                     hipStream_t s) {
+void attn_fwd<float>(const float* qkv, float* o, float* lse, int B, int T_, int H, int hd, hipStream_t s) {
   if (hd > kMaxHd) throw ApiError{MT_E_INVALID, "fp32 attention needs head_dim <= 64"};
   hipLaunchKernelGGL(k_attn_fwd_f32, dim3((T_ + 63) / 64, B * H), dim3(64), 0, s, qkv, o, lse, T_, H, hd);
 }
@@ -748,20 +741,19 @@ template void attn_bwd_dsum<float>(const float*, const float*, float*, int, int,
 template void attn_bwd_dsum<uint16_t>(const uint16_t*, const uint16_t*, float*, int, int, int, int, hipStream_t);
 
 template <>
-void attn_bwd<uint16_t>(const uint16_t* qkv, const uint16_t* qkvT, const uint16_t* dO, const uint16_t* dOT,
-                        int64_t ldT, const float* lse, const float* Dsum, uint16_t* dqkvT, int B, int T_, int H,
-                        int hd, hipStream_t s) {
+void attn_bwd<uint16_t>(const uint16_t* qkv, const uint16_t* dO, const float* lse, const float* Dsum, uint16_t* dqkvT,
+                        int64_t ldT, int B, int T_, int H, int hd, hipStream_t s) {
   if (hd != 128 || T_ % 64) throw ApiError{MT_E_INVALID, "bf16 attention needs head_dim 128, seq_len % 64 == 0"};
-  if (ldT < (int64_t)B * T_ || ldT % 8) throw ApiError{MT_E_INVALID, "ldT must be >= batch*seq_len, multiple of 8"};
-  hipLaunchKernelGGL(k_attn_dkdv_bf16, dim3((T_ + 127) / 128, B * H), dim3(256), 0, s, qkv, qkvT, dO, dOT, lse, Dsum,
-                     dqkvT, ldT, T_, H);
-  hipLaunchKernelGGL(k_attn_dq_bf16, dim3((T_ + 127) / 128, B * H), dim3(256), 0, s, qkv, qkvT, dO, lse, Dsum, dqkvT,
-                     ldT, T_, H);
+  if (ldT < (int64_t)B * T_) throw ApiError{MT_E_INVALID, "ldT must be >= batch*seq_len"};
+  hipLaunchKernelGGL(k_attn_dkdv_bf16, dim3((T_ + 127) / 128, B * H), dim3(256), 0, s, qkv, dO, lse, Dsum, dqkvT, ldT,
+                     T_, H);
+  hipLaunchKernelGGL(k_attn_dq_bf16, dim3((T_ + 127) / 128, B * H), dim3(256), 0, s, qkv, dO, lse, Dsum, dqkvT, ldT,
+                     T_, H);
 }
 
 template <>
-void attn_bwd<float>(const float* qkv, const float*, const float* dO, const float*, int64_t ldT, const float* lse,
-                     const float* Dsum, float* dqkvT, int B, int T_, int H, int hd, hipStream_t s) {
+void attn_bwd<float>(const float* qkv, const float* dO, const float* lse, const float* Dsum, float* dqkvT,
+                     int64_t ldT, int B, int T_, int H, int hd, hipStream_t s) {
   if (hd > kMaxHd) throw ApiError{MT_E_INVALID, "fp32 attention needs head_dim <= 64"};
   if (ldT < (int64_t)B * T_) throw ApiError{MT_E_INVALID, "ldT must be >= batch*seq_len"};
   hipLaunchKernelGGL(k_attn_dkdv_f32, dim3((T_ + 63) / 64, B * H), dim3(64), 0, s, qkv, dO, lse, Dsum, dqkvT, ldT, T_,

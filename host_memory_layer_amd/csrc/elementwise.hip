@@ -274,56 +274,36 @@ void rmsnorm_bwd(const float* dy, const float* x, const T* g, const float* rstd,
 }
 
 // ----------------------------------------------------------------- RoPE --
-// One block: 64 tokens x one head of q, k or v.  q and k rotate in place;
-// all three are also written transposed into qkvT [3d x M].
+// Token-major transposed buffers [C x M] use a padded row stride (see
+// kernels.h).
 int64_t token_ld(int64_t M) {
   int64_t ld = (M + 127) / 128 * 128;
   if ((ld / 128) % 2 == 0) ld += 128;
   return ld;
 }
 
+// q and k rotate in place; one thread per (token, head of q or k, pair i):
+// x_i, x_{i+hd/2} -> x_i cos - x_{i+hd/2} sin, x_i sin + x_{i+hd/2} cos.
 template <typename T>
-__global__ void __launch_bounds__(256) k_rope_qkv(T* qkv, T* qkvT, int64_t ldT, const float* cosb, const float* sinb,
-                                                  int M, int T_, int d, int hd) {
-  __shared__ float tile[64][129];
-  const int64_t m0 = (int64_t)blockIdx.x * 64;
-  const int part = blockIdx.y / (d / hd);  // 0 q, 1 k, 2 v
-  const int head = blockIdx.y % (d / hd);
-  const int64_t col0 = (int64_t)part * d + (int64_t)head * hd;
-  const int64_t ld = 3LL * d;
-  for (int idx = threadIdx.x; idx < 64 * hd; idx += 256) {
-    int r = idx / hd, c = idx % hd;
-    int64_t m = m0 + r;
-    tile[r][c] = m < M ? ldf(qkv[m * ld + col0 + c]) : 0.f;
-  }
-  __syncthreads();
-  if (part < 2) {
-    const int h2 = hd / 2;
-    for (int idx = threadIdx.x; idx < 64 * h2; idx += 256) {
-      int r = idx / h2, i = idx % h2;
-      int64_t m = m0 + r;
-      if (m >= M) continue;
-      int t = (int)(m % T_);
-      float cs = cosb[(int64_t)t * h2 + i], sn = sinb[(int64_t)t * h2 + i];
-      float a = tile[r][i], b = tile[r][i + h2];
-      tile[r][i] = a * cs - b * sn;
-      tile[r][i + h2] = a * sn + b * cs;
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < 64 * hd; idx += 256) {
-      int r = idx / hd, c = idx % hd;
-      int64_t m = m0 + r;
-      if (m < M) qkv[m * ld + col0 + c] = stf<T>(tile[r][c]);
-    }
-  }
-  for (int idx = threadIdx.x; idx < 64 * hd; idx += 256) {
-    int c = idx / 64, r = idx % 64;
-    int64_t m = m0 + r;
-    if (m < M) qkvT[(col0 + c) * ldT + attn_token_col(m, M)] = stf<T>(tile[r][c]);
-  }
+__global__ void __launch_bounds__(256) k_rope_qkv(T* qkv, const float* cosb, const float* sinb, int M, int T_, int d,
+                                                  int hd) {
+  const int h2 = hd / 2;
+  const int64_t per_tok = (int64_t)2 * (d / hd) * h2;  // q and k heads x pairs
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (int64_t)M * per_tok) return;
+  const int64_t m = id / per_tok;
+  const int j = (int)(id % per_tok);
+  const int hh = j / h2, i = j % h2;
+  T* x = qkv + m * 3LL * d + (int64_t)hh * hd;
+  const int t = (int)(m % T_);
+  const float cs = cosb[(int64_t)t * h2 + i], sn = sinb[(int64_t)t * h2 + i];
+  const float a = ldf(x[i]), b = ldf(x[i + h2]);
+  x[i] = stf<T>(a * cs - b * sn);
+  x[i + h2] = stf<T>(a * sn + b * cs);
 }
 
-// bf16, head_dim 128, 64 whole tokens per block: 16-byte global accesses.
+// bf16, head_dim 128: one thread per (token, head of q or k, 8 adjacent
+// pairs), 16-byte accesses.
 __device__ inline void unpack8(const uint4 u, float* f) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -339,71 +319,45 @@ __device__ inline uint4 pack8(const float* f) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-__global__ void __launch_bounds__(256) k_rope_qkv_bf16(uint16_t* __restrict__ qkv, uint16_t* __restrict__ qkvT,
-                                                       int64_t ldT, const float* __restrict__ cosb,
-                                                       const float* __restrict__ sinb, int T_, int d) {
-  constexpr int HD = 128, H2 = 64;
-  __shared__ float tile[64][129];
-  const int64_t m0 = (int64_t)blockIdx.x * 64;
-  const int part = blockIdx.y / (d / HD);
-  const int head = blockIdx.y % (d / HD);
-  const int64_t col0 = (int64_t)part * d + (int64_t)head * HD;
-  const int64_t ld = 3LL * d;
+__global__ void __launch_bounds__(256) k_rope_qkv_bf16(uint16_t* __restrict__ qkv, const float* __restrict__ cosb,
+                                                       const float* __restrict__ sinb, int M, int T_, int d) {
+  const int per_tok = 2 * (d / 128) * 8;  // q and k heads x 8 groups of 8 pairs
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (int64_t)M * per_tok) return;
+  const int64_t m = id / per_tok;
+  const int j = (int)(id % per_tok);
+  const int hh = j >> 3, i0 = (j & 7) * 8;
+  uint16_t* x = qkv + m * 3LL * d + (int64_t)hh * 128 + i0;
+  const int t = (int)(m % T_);
+  const float4* cp = (const float4*)(cosb + (int64_t)t * 64 + i0);
+  const float4* sp = (const float4*)(sinb + (int64_t)t * 64 + i0);
+  const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+  const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+  float a[8], b[8], oa[8], ob[8];
+  unpack8(*(const uint4*)x, a);
+  unpack8(*(const uint4*)(x + 64), b);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int id = threadIdx.x + 256 * k;
-    const int r = id >> 4, c8 = id & 15;
-    float f[8];
-    unpack8(*(const uint4*)(qkv + (m0 + r) * ld + col0 + 8 * c8), f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tile[r][8 * c8 + e] = f[e];
+  for (int e = 0; e < 8; ++e) {
+    oa[e] = a[e] * cs[e] - b[e] * sn[e];
+    ob[e] = a[e] * sn[e] + b[e] * cs[e];
   }
-  __syncthreads();
-  if (part < 2) {
-#pragma unroll 4
-    for (int idx = threadIdx.x; idx < 64 * H2; idx += 256) {
-      const int r = idx / H2, i = idx % H2;
-      const int t = (int)((m0 + r) % T_);
-      const float cs = cosb[(int64_t)t * H2 + i], sn = sinb[(int64_t)t * H2 + i];
-      const float a = tile[r][i], b = tile[r][i + H2];
-      tile[r][i] = a * cs - b * sn;
-      tile[r][i + H2] = a * sn + b * cs;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int id = threadIdx.x + 256 * k;
-      const int r = id >> 4, c8 = id & 15;
-      float f[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = tile[r][8 * c8 + e];
-      *(uint4*)(qkv + (m0 + r) * ld + col0 + 8 * c8) = pack8(f);
-    }
-  }
-  // 64 whole tokens (m0 % 64 == 0): column m0 + j holds token m0 + j with
-  // bits 2 and 3 of j swapped (attention's token order).
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int id = threadIdx.x + 256 * k;
-    const int c = id >> 3, t8 = id & 7;
-    float f[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = tile[(int)attn_token_col(8 * t8 + e, 64)][c];
-    *(uint4*)(qkvT + (col0 + c) * ldT + m0 + 8 * t8) = pack8(f);
-  }
+  *(uint4*)x = pack8(oa);
+  *(uint4*)(x + 64) = pack8(ob);
 }
 
 template <typename T>
-void rope_qkv_fwd(T* qkv, T* qkvT, int64_t ldT, const float* cosb, const float* sinb, int M, int T_, int d, int hd,
-                  hipStream_t s) {
+void rope_qkv_fwd(T* qkv, const float* cosb, const float* sinb, int M, int T_, int d, int hd, hipStream_t s) {
   if (M <= 0) return;
-  if (std::is_same<T, uint16_t>::value && hd == 128 && M % 64 == 0 && ldT % 8 == 0) {
-    hipLaunchKernelGGL(k_rope_qkv_bf16, dim3(M / 64, 3 * (d / hd)), dim3(256), 0, s, (uint16_t*)qkv, (uint16_t*)qkvT,
-                       ldT, cosb, sinb, T_, d);
+  if (std::is_same<T, uint16_t>::value && hd == 128 && d % 128 == 0 && ((uintptr_t)qkv & 15) == 0 &&
+      ((uintptr_t)cosb & 15) == 0 && ((uintptr_t)sinb & 15) == 0) {
+    const int64_t n = (int64_t)M * 2 * (d / 128) * 8;
+    hipLaunchKernelGGL(k_rope_qkv_bf16, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, (uint16_t*)qkv, cosb, sinb,
+                       M, T_, d);
     return;
   }
-  hipLaunchKernelGGL(k_rope_qkv<T>, dim3(cdiv(M, 64), 3 * (d / hd)), dim3(256), 0, s, qkv, qkvT, ldT, cosb, sinb, M,
-                     T_, d, hd);
+  const int64_t n = (int64_t)M * 2 * (d / hd) * (hd / 2);
+  hipLaunchKernelGGL(k_rope_qkv<T>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, qkv, cosb, sinb, M, T_, d, hd);
 }
 
 // Inverse rotation on the transposed layout: one thread per (pair, 8 tokens)
@@ -579,8 +533,7 @@ void sum_fixed(const float* x, float* out, int n, float scale, hipStream_t s) {
 }
 
 // ------------------------------------------------------------ transpose --
-// TOKENS: the rows of `in` are tokens, placed in attention's token order.
-template <typename T, bool TOKENS>
+template <typename T>
 __global__ void __launch_bounds__(256) k_transpose(const T* in, int64_t ld_in, T* out, int64_t ld_out, int R, int C) {
   __shared__ T tile[64][65];
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
@@ -592,20 +545,18 @@ __global__ void __launch_bounds__(256) k_transpose(const T* in, int64_t ld_in, T
   for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
     int c = idx / 64, r = idx % 64;
     if (r0 + r < R && c0 + c < C)
-      out[(c0 + c) * ld_out + (TOKENS ? attn_token_col(r0 + r, R) : r0 + r)] = tile[r][c];
+      out[(c0 + c) * ld_out + r0 + r] = tile[r][c];
   }
 }
 
 // bf16 64x64 tile with 16-byte global loads and stores (8 elements per
 // access); rows and columns of the tile that fall outside R x C are skipped
-// per 8-element group, so R, C, ld_in, ld_out must be multiples of 8
-// (TOKENS: R a multiple of 16, so that every 16-group is whole).
+// per 8-element group, so R, C, ld_in, ld_out must be multiples of 8.
 //
 // The tile sits in LDS row-major, 128 bytes per input row, 16-byte chunk j
 // of row r at chunk j ^ ((r >> 3) & 7).  Each thread reads the 4-byte column
 // pair (2p, 2p+1) of 8 consecutive rows and packs the two output runs with
 // byte permutes; the 8 lanes of one output row cover 128 contiguous bytes.
-template <bool TOKENS>
 __global__ void __launch_bounds__(256) k_transpose_bf16(const uint16_t* __restrict__ in, int64_t ld_in,
                                                         uint16_t* __restrict__ out, int64_t ld_out, int R, int C) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[64 * 128];
@@ -624,7 +575,7 @@ __global__ void __launch_bounds__(256) k_transpose_bf16(const uint16_t* __restri
     uint32_t w[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int rr = TOKENS ? (int)attn_token_col(r8 + i, 64) : r8 + i;
+      const int rr = r8 + i;
       w[i] = *(const uint32_t*)(tile + rr * 128 + (((p >> 2) ^ ((rr >> 3) & 7)) << 4) + ((p & 3) << 2));
     }
     uint4 lo, hi;  // output columns 2p and 2p+1: the low and high halves of w
@@ -641,27 +592,16 @@ __global__ void __launch_bounds__(256) k_transpose_bf16(const uint16_t* __restri
   }
 }
 
-template <typename T, bool TOKENS>
-void transpose_any(const T* in, int64_t ld_in, T* out, int64_t ld_out, int R, int C, hipStream_t s) {
-  if (R <= 0 || C <= 0) return;
-  if (std::is_same<T, uint16_t>::value && R % (TOKENS ? 16 : 8) == 0 && C % 8 == 0 && ld_in % 8 == 0 &&
-      ld_out % 8 == 0 && ((uintptr_t)in & 15) == 0 && ((uintptr_t)out & 15) == 0) {
-    hipLaunchKernelGGL(k_transpose_bf16<TOKENS>, dim3(cdiv(C, 64), cdiv(R, 64)), dim3(256), 0, s, (const uint16_t*)in,
-                       ld_in, (uint16_t*)out, ld_out, R, C);
-    return;
-  }
-  hipLaunchKernelGGL((k_transpose<T, TOKENS>), dim3(cdiv(C, 64), cdiv(R, 64)), dim3(256), 0, s, in, ld_in, out, ld_out,
-                     R, C);
-}
-
 template <typename T>
 void transpose(const T* in, int64_t ld_in, T* out, int64_t ld_out, int R, int C, hipStream_t s) {
-  transpose_any<T, false>(in, ld_in, out, ld_out, R, C, s);
-}
-
-template <typename T>
-void transpose_tokens(const T* in, int64_t ld_in, T* out, int64_t ld_out, int M, int C, hipStream_t s) {
-  transpose_any<T, true>(in, ld_in, out, ld_out, M, C, s);
+  if (R <= 0 || C <= 0) return;
+  if (std::is_same<T, uint16_t>::value && R % 8 == 0 && C % 8 == 0 && ld_in % 8 == 0 && ld_out % 8 == 0 &&
+      ((uintptr_t)in & 15) == 0 && ((uintptr_t)out & 15) == 0) {
+    hipLaunchKernelGGL(k_transpose_bf16, dim3(cdiv(C, 64), cdiv(R, 64)), dim3(256), 0, s, (const uint16_t*)in, ld_in,
+                       (uint16_t*)out, ld_out, R, C);
+    return;
+  }
+  hipLaunchKernelGGL(k_transpose<T>, dim3(cdiv(C, 64), cdiv(R, 64)), dim3(256), 0, s, in, ld_in, out, ld_out, R, C);
 }
 
 template <typename T>
@@ -706,13 +646,12 @@ void fill_u32(void* p, uint32_t value, size_t n_words, hipStream_t s) {
   template void rmsnorm_fwd<T>(const float*, const T*, T*, float*, int, int, float, hipStream_t);               \
   template void rmsnorm_bwd<T>(const float*, const float*, const T*, const float*, const float*, float*, float*, T*, \
                                int, int, hipStream_t);                                                          \
-  template void rope_qkv_fwd<T>(T*, T*, int64_t, const float*, const float*, int, int, int, int, hipStream_t);  \
+  template void rope_qkv_fwd<T>(T*, const float*, const float*, int, int, int, int, hipStream_t);              \
   template void rope_bwd_T<T>(T*, int64_t, const float*, const float*, int, int, int, int, hipStream_t);        \
   template void swiglu_fwd<T>(const T*, T*, int, int, hipStream_t);                                             \
   template void swiglu_bwd<T>(const T*, const T*, T*, int, int, hipStream_t);                                   \
   template void xent<T>(const float*, const int32_t*, float*, T*, int, int, int, float, hipStream_t);           \
   template void transpose<T>(const T*, int64_t, T*, int64_t, int, int, hipStream_t);                            \
-  template void transpose_tokens<T>(const T*, int64_t, T*, int64_t, int, int, hipStream_t);                     \
   template void cast_transpose<T>(const float*, T*, T*, int64_t, int, int, hipStream_t);
 
 MT_INST(float)

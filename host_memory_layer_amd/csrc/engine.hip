@@ -58,13 +58,13 @@ double ms_between(hipEvent_t a, hipEvent_t b) {
 // ------------------------------------------------------------ buffers --
 template <typename T>
 struct Acts {  // forward intermediates of one layer
-  T *h, *qkv, *qkvT, *o, *h2, *gu, *y;
+  T *h, *qkv, *o, *h2, *gu, *y;
   float *r1, *lse, *x1, *r2;
 };
 
 template <typename T>
 struct BwdWs {  // backward workspace (one set)
-  T *dxb, *dxbT, *tmpT, *dy, *dgu, *dguT, *do_, *doT, *dqkvT, *dqkv;
+  T *dxb, *dxbT, *tmpT, *dy, *dgu, *dguT, *do_, *dqkvT, *dqkv;
   float *dh, *dx1, *Dsum, *part, *dxA, *dxB;
 };
 
@@ -147,7 +147,6 @@ struct Model {
     const uint64_t Md = (uint64_t)M * d;
     a.h = c.take<T>(Md * E);
     a.qkv = c.take<T>(3 * Md * E);
-    a.qkvT = c.take<T>(3 * (uint64_t)d * Mp * E);
     a.o = c.take<T>(Md * E);
     a.h2 = c.take<T>(Md * E);
     a.gu = c.take<T>((uint64_t)M * 2 * F * E);
@@ -167,7 +166,6 @@ struct Model {
     w.dgu = c.take<T>(2 * MF * E);
     w.dguT = c.take<T>(2 * (uint64_t)F * Mp * E);
     w.do_ = c.take<T>(Md * E);
-    w.doT = c.take<T>((uint64_t)d * Mp * E);
     w.dqkvT = c.take<T>(3 * (uint64_t)d * Mp * E);
     w.dqkv = c.take<T>(3 * Md * E);
     w.dh = c.take<float>(Md * 4);
@@ -312,10 +310,10 @@ struct Model {
     const float eps = (float)cfg.rms_eps;
     rmsnorm_fwd<T>(x, w.anorm, a.h, a.r1, M, d, eps, sc);
     gemm<T>(a.h, d, w.qkv, d, a.qkv, 3 * d, nullptr, 0, M, 3 * d, d, EPI_STORE);
-    rope_qkv_fwd<T>(a.qkv, a.qkvT, Mp, cosb, sinb, M, Tq, d, hd, sc);
+    rope_qkv_fwd<T>(a.qkv, cosb, sinb, M, Tq, d, hd, sc);
     const bool timed = cfg.flags & MT_FLAG_TIME_KERNELS;
     if (timed) record_kernel_start(attn_fwd_flops(), 1);
-    attn_fwd<T>(a.qkv, a.qkvT, Mp, a.o, a.lse, B, Tq, H, hd, sc);
+    attn_fwd<T>(a.qkv, a.o, a.lse, B, Tq, H, hd, sc);
     if (timed) record_kernel_end();
     gemm<T>(a.o, d, w.o, d, a.x1, d, x, d, M, d, d, EPI_ADD_F32);
     rmsnorm_fwd<T>(a.x1, w.fnorm, a.h2, a.r2, M, d, eps, sc);
@@ -354,11 +352,10 @@ struct Model {
     gemm<T>(ws.dxbT, Mp, ws.tmpT, Mp, g.o, d, nullptr, 0, d, d, M, EPI_STORE);
     gemm<T>(ws.dxb, d, wt_.o, d, ws.do_, d, nullptr, 0, M, d, d, EPI_STORE);
     // attention
-    transpose_tokens<T>(ws.do_, d, ws.doT, Mp, M, d, sc);
     attn_bwd_dsum<T>(ws.do_, a.o, ws.Dsum, B, Tq, H, hd, sc);
     const bool timed = cfg.flags & MT_FLAG_TIME_KERNELS;
     if (timed) record_kernel_start(2.5 * attn_fwd_flops(), 1);
-    attn_bwd<T>(a.qkv, a.qkvT, ws.do_, ws.doT, Mp, a.lse, ws.Dsum, ws.dqkvT, B, Tq, H, hd, sc);
+    attn_bwd<T>(a.qkv, ws.do_, a.lse, ws.Dsum, ws.dqkvT, Mp, B, Tq, H, hd, sc);
     if (timed) record_kernel_end();
     rope_bwd_T<T>(ws.dqkvT, Mp, cosT, sinT, M, Tq, d, hd, sc);
     // QKV projection

@@ -61,19 +61,6 @@ int mt_transpose(int32_t dtype, const void* in, int64_t ld_in, void* out, int64_
   });
 }
 
-int mt_transpose_tokens(int32_t dtype, const void* in, int64_t ld_in, void* out, int64_t ld_out, int32_t M,
-                        int32_t C, void* stream) {
-  return kguard([&] {
-    need(ld_in >= C && ld_out >= M, "leading dimensions");
-    if (dtype == MT_BF16)
-      transpose_tokens<uint16_t>((const uint16_t*)in, ld_in, (uint16_t*)out, ld_out, M, C, (hipStream_t)stream);
-    else if (dtype == MT_F32)
-      transpose_tokens<float>((const float*)in, ld_in, (float*)out, ld_out, M, C, (hipStream_t)stream);
-    else
-      need(false, "dtype");
-  });
-}
-
 int mt_rope_tables(int32_t T, int32_t hd, double theta, float* cos_out, float* sin_out) {
   return kguard([&] {
     need(T > 0 && hd > 0 && hd % 2 == 0 && cos_out && sin_out, "arguments");
@@ -88,49 +75,44 @@ int mt_rope_tables(int32_t T, int32_t hd, double theta, float* cos_out, float* s
 
 int64_t mt_token_ld(int64_t tokens) { return token_ld(tokens); }
 
-int mt_rope_qkv(int32_t dtype, void* qkv, void* qkvT, int64_t ldT, const float* cos_t, const float* sin_t, int32_t B,
-                int32_t T, int32_t H, int32_t hd, void* stream) {
+int mt_rope_qkv(int32_t dtype, void* qkv, const float* cos_t, const float* sin_t, int32_t B, int32_t T, int32_t H,
+                int32_t hd, void* stream) {
   return kguard([&] {
     need(B > 0 && T > 0 && H > 0 && hd > 0 && hd % 2 == 0 && hd <= 128, "shape");
     const int M = B * T, d = H * hd;
-    need(ldT >= M, "ldT < batch*seq_len");
     if (dtype == MT_BF16)
-      rope_qkv_fwd<uint16_t>((uint16_t*)qkv, (uint16_t*)qkvT, ldT, cos_t, sin_t, M, T, d, hd, (hipStream_t)stream);
+      rope_qkv_fwd<uint16_t>((uint16_t*)qkv, cos_t, sin_t, M, T, d, hd, (hipStream_t)stream);
     else if (dtype == MT_F32)
-      rope_qkv_fwd<float>((float*)qkv, (float*)qkvT, ldT, cos_t, sin_t, M, T, d, hd, (hipStream_t)stream);
+      rope_qkv_fwd<float>((float*)qkv, cos_t, sin_t, M, T, d, hd, (hipStream_t)stream);
     else
       need(false, "dtype");
   });
 }
 
-int mt_attention_fwd(int32_t dtype, const void* qkv, const void* qkvT, int64_t ldT, void* o, float* lse, int32_t B,
-                     int32_t T, int32_t H, int32_t hd, void* stream) {
+int mt_attention_fwd(int32_t dtype, const void* qkv, void* o, float* lse, int32_t B, int32_t T, int32_t H, int32_t hd,
+                     void* stream) {
   return kguard([&] {
     need(B > 0 && T > 0 && H > 0 && hd > 0, "shape");
     if (dtype == MT_BF16)
-      attn_fwd<uint16_t>((const uint16_t*)qkv, (const uint16_t*)qkvT, ldT, (uint16_t*)o, lse, B, T, H, hd,
-                         (hipStream_t)stream);
+      attn_fwd<uint16_t>((const uint16_t*)qkv, (uint16_t*)o, lse, B, T, H, hd, (hipStream_t)stream);
     else if (dtype == MT_F32)
-      attn_fwd<float>((const float*)qkv, (const float*)qkvT, ldT, (float*)o, lse, B, T, H, hd, (hipStream_t)stream);
+      attn_fwd<float>((const float*)qkv, (float*)o, lse, B, T, H, hd, (hipStream_t)stream);
     else
       need(false, "dtype");
   });
 }
 
-int mt_attention_bwd(int32_t dtype, const void* qkv, const void* qkvT, const void* o, const void* dO,
-                     const void* dOT, int64_t ldT, const float* lse, float* Dsum, void* dqkvT, int32_t B, int32_t T,
-                     int32_t H, int32_t hd, void* stream) {
+int mt_attention_bwd(int32_t dtype, const void* qkv, const void* o, const void* dO, const float* lse, float* Dsum,
+                     void* dqkvT, int64_t ldT, int32_t B, int32_t T, int32_t H, int32_t hd, void* stream) {
   return kguard([&] {
     need(B > 0 && T > 0 && H > 0 && hd > 0, "shape");
     hipStream_t s = (hipStream_t)stream;
     if (dtype == MT_BF16) {
       attn_bwd_dsum<uint16_t>((const uint16_t*)dO, (const uint16_t*)o, Dsum, B, T, H, hd, s);
-      attn_bwd<uint16_t>((const uint16_t*)qkv, (const uint16_t*)qkvT, (const uint16_t*)dO, (const uint16_t*)dOT, ldT,
-                         lse, Dsum, (uint16_t*)dqkvT, B, T, H, hd, s);
+      attn_bwd<uint16_t>((const uint16_t*)qkv, (const uint16_t*)dO, lse, Dsum, (uint16_t*)dqkvT, ldT, B, T, H, hd, s);
     } else if (dtype == MT_F32) {
       attn_bwd_dsum<float>((const float*)dO, (const float*)o, Dsum, B, T, H, hd, s);
-      attn_bwd<float>((const float*)qkv, (const float*)qkvT, (const float*)dO, (const float*)dOT, ldT, lse, Dsum,
-                      (float*)dqkvT, B, T, H, hd, s);
+      attn_bwd<float>((const float*)qkv, (const float*)dO, lse, Dsum, (float*)dqkvT, ldT, B, T, H, hd, s);
     } else {
       need(false, "dtype");
     }

@@ -40,22 +40,10 @@ void rmsnorm_bwd(const float* dy, const float* x, const T* g, const float* rstd,
 // (token_ld(M) >= M): a row stride that is a large power of two puts a
 // tile's rows on the same memory channels.
 int64_t token_ld(int64_t M);
-// Token order of attention's transposed operands (qkvT, dOT): inside every
-// complete group of 16 tokens, bits 2 and 3 of the token index are swapped
-// (columns hold tokens 0-3, 8-11, 4-7, 12-15); a trailing partial group
-// keeps its order.  An MFMA whose other operand comes from a 32x32
-// accumulator pairs, per lane half h, the contraction indices 4h..4h+3 and
-// 8+4h..8+4h+3 of each 16-slice; in this order they are 8 adjacent columns,
-// one 16-byte LDS read.  The map is its own inverse.
-__host__ __device__ inline int64_t attn_token_col(int64_t m, int64_t M) {
-  return (m | 15) < M ? (m & ~(int64_t)12) | ((m & 4) << 1) | ((m & 8) >> 1) : m;
-}
 // Rotate q and k of qkv [M x 3d] in place (pairs (i, i+hd/2), angle
-// t*theta^(-2i/hd), t = m mod T) and write the transpose qkvT [3d x M]
-// (row stride ldT) in attention's token order (attn_token_col).
+// t*theta^(-2i/hd), t = m mod T).
 template <typename T>
-void rope_qkv_fwd(T* qkv, T* qkvT, int64_t ldT, const float* cosb, const float* sinb, int M, int T_, int d, int hd,
-                  hipStream_t s);
+void rope_qkv_fwd(T* qkv, const float* cosb, const float* sinb, int M, int T_, int d, int hd, hipStream_t s);
 // Inverse rotation of the dq, dk rows of dqkvT [3d x M] (row stride ldT), in
 // place; cosT, sinT are the rotation tables transposed, [hd/2 x T].
 template <typename T>
@@ -75,30 +63,22 @@ void sum_fixed(const float* x, float* out, int n, float scale, hipStream_t s);
 // out[C x R] = in[R x C]^T.
 template <typename T>
 void transpose(const T* in, int64_t ld_in, T* out, int64_t ld_out, int R, int C, hipStream_t s);
-// The same with the rows of `in` (tokens, R = M) placed in attention's token
-// order: out[c][attn_token_col(m, M)] = in[m][c].
-template <typename T>
-void transpose_tokens(const T* in, int64_t ld_in, T* out, int64_t ld_out, int M, int C, hipStream_t s);
 // out = T(in) and outT = T(in)^T (row stride ldT) for in float [R x C].
 template <typename T>
 void cast_transpose(const float* in, T* out, T* outT, int64_t ldT, int R, int C, hipStream_t s);
 void fill_u32(void* p, uint32_t value, size_t n_words, hipStream_t s);
 
 // ------------------------------------------------------------ attention --
-// qkv [M x 3d] (q, k rotated), qkvT [3d x M] (row stride ldT, attention's
-// token order); o [M x d];
+// qkv [M x 3d] (q, k rotated); o [M x d];
 // lse [B*H x T] (base-2 log-sum-exp of the scaled scores).
 template <typename T>
-void attn_fwd(const T* qkv, const T* qkvT, int64_t ldT, T* o, float* lse, int B, int T_, int H, int hd,
-              hipStream_t s);
+void attn_fwd(const T* qkv, T* o, float* lse, int B, int T_, int H, int hd, hipStream_t s);
 // Dsum[b*H+h][t] = sum_i dO . O over the head.
 template <typename T>
 void attn_bwd_dsum(const T* dO, const T* O, float* Dsum, int B, int T_, int H, int hd, hipStream_t s);
-// dqkvT [3d x M] receives dq, dk, dv (transposed layout, natural token
-// order); qkvT and dOT are in attention's token order; all three share the
-// row stride ldT.
+// dqkvT [3d x M] (row stride ldT) receives dq, dk, dv transposed.
 template <typename T>
-void attn_bwd(const T* qkv, const T* qkvT, const T* dO, const T* dOT, int64_t ldT, const float* lse,
-              const float* Dsum, T* dqkvT, int B, int T_, int H, int hd, hipStream_t s);
+void attn_bwd(const T* qkv, const T* dO, const float* lse, const float* Dsum, T* dqkvT, int64_t ldT, int B, int T_,
+              int H, int hd, hipStream_t s);
 
 }  // namespace mt

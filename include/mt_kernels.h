@@ -32,19 +32,6 @@ int mt_gemm(int32_t dtype, const void* A, int64_t lda, const void* B, int64_t ld
 int mt_transpose(int32_t dtype, const void* in, int64_t ld_in, void* out, int64_t ld_out, int32_t R, int32_t C,
                  void* stream);
 
-/* Attention's token order for transposed operands [C x tokens]: inside
- * every complete group of 16 tokens, bits 2 and 3 of the token index are
- * swapped, so the columns of a group hold tokens 0-3, 8-11, 4-7, 12-15; a
- * trailing partial group keeps its order.  (The attention kernels read a
- * transposed operand against a probability tile held in MFMA accumulators,
- * which pairs contraction indices 4h..4h+3 with 8+4h..8+4h+3 in lane half h;
- * this order makes each such pair 8 adjacent columns.)
- *
- * out[c][col(m)] = in[m][c] for in [M x C] (row stride ld_in) and out
- * [C x M] (row stride ld_out >= M), col = attention's token order. */
-int mt_transpose_tokens(int32_t dtype, const void* in, int64_t ld_in, void* out, int64_t ld_out, int32_t M,
-                        int32_t C, void* stream);
-
 /* Host: RoPE tables cos/sin [T x hd/2] of angle t * theta^(-2i/hd), computed
  * in double and rounded to float (host buffers of T*hd/2 floats). */
 int mt_rope_tables(int32_t T, int32_t hd, double theta, float* cos_out, float* sin_out);
@@ -56,29 +43,24 @@ int mt_rope_tables(int32_t T, int32_t hd, double theta, float* cos_out, float* s
 int64_t mt_token_ld(int64_t tokens);
 
 /* qkv [B*T x 3d] (q | k | v columns, head-major inside each): rotate q and k
- * in place by +t*w_i on pairs (i, i+hd/2), t = position in the sequence, and
- * write the transpose qkvT [3d x B*T] with row stride ldT >= B*T, tokens in
- * attention's token order (as mt_transpose_tokens).  cos/sin: device tables
- * from mt_rope_tables. */
-int mt_rope_qkv(int32_t dtype, void* qkv, void* qkvT, int64_t ldT, const float* cos_t, const float* sin_t, int32_t B,
-                int32_t T, int32_t H, int32_t hd, void* stream);
+ * in place by +t*w_i on pairs (i, i+hd/2), t = position in the sequence.
+ * cos/sin: device tables from mt_rope_tables. */
+int mt_rope_qkv(int32_t dtype, void* qkv, const float* cos_t, const float* sin_t, int32_t B, int32_t T, int32_t H,
+                int32_t hd, void* stream);
 
 /* Causal softmax attention per (batch, head) with scale 1/sqrt(hd).
- * Inputs: rotated qkv and qkvT (row stride ldT) as left by mt_rope_qkv.
+ * Input: qkv with q, k rotated (as left by mt_rope_qkv).
  * Outputs: o [B*T x d] (dtype) and lse [B*H x T] (float, base-2
  * log-sum-exp of the scaled scores times log2(e)).  bf16: hd = 128 and
- * T % 64 == 0, ldT % 8 == 0; f32: hd <= 64. */
-int mt_attention_fwd(int32_t dtype, const void* qkv, const void* qkvT, int64_t ldT, void* o, float* lse, int32_t B,
-                     int32_t T, int32_t H, int32_t hd, void* stream);
+ * T % 64 == 0; f32: hd <= 64. */
+int mt_attention_fwd(int32_t dtype, const void* qkv, void* o, float* lse, int32_t B, int32_t T, int32_t H, int32_t hd,
+                     void* stream);
 
-/* Backward of mt_attention_fwd given dO [B*T x d] and dOT [d x B*T] (dO
- * transposed by mt_transpose_tokens, attention's token order):
- * writes Dsum [B*H x T] (float scratch, rowsum(dO * O)) and
- * dqkvT [3d x B*T] = (dq | dk | dv)^T with respect to the rotated q, k, in
- * natural token order.  qkvT, dOT and dqkvT have row stride ldT. */
-int mt_attention_bwd(int32_t dtype, const void* qkv, const void* qkvT, const void* o, const void* dO,
-                     const void* dOT, int64_t ldT, const float* lse, float* Dsum, void* dqkvT, int32_t B, int32_t T,
-                     int32_t H, int32_t hd, void* stream);
+/* Backward of mt_attention_fwd given dO [B*T x d]: writes Dsum [B*H x T]
+ * (float scratch, rowsum(dO * O)) and dqkvT [3d x B*T] (row stride
+ * ldT >= B*T) = (dq | dk | dv)^T with respect to the rotated q, k. */
+int mt_attention_bwd(int32_t dtype, const void* qkv, const void* o, const void* dO, const float* lse, float* Dsum,
+                     void* dqkvT, int64_t ldT, int32_t B, int32_t T, int32_t H, int32_t hd, void* stream);
 
 #ifdef __cplusplus
 }

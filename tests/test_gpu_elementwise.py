@@ -28,32 +28,3 @@ def test_transpose_exact(R, C, ld_in, ld_out):
     o = O.cpu().numpy().view(np.uint16)
     assert np.array_equal(o[:, :R], a[:, :C].T)
     assert np.all(o[:, R:] == 0xFFFF)
-
-
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("M,C,ld_in,ld_out", [(64, 64, 64, 64), (200, 136, 144, 208), (40, 24, 24, 48),
-                                              (4096, 128, 128, 4224), (13, 8, 8, 16)])
-def test_transpose_tokens_exact(dtype, M, C, ld_in, ld_out):
-    """out[c][col(m)] = in[m][c], col swapping bits 2 and 3 of m inside every
-    complete 16-group; a trailing partial group keeps natural order."""
-    from tests.test_gpu_kernels import attention_token_cols
-    rng = np.random.default_rng(M * 7 + C)
-    if dtype == "bf16":
-        a = rng.integers(0, 65535, (M, ld_in), dtype=np.uint16)
-        A = torch.from_numpy(a.view(np.int16)).to(dev())
-        O = torch.full((C, ld_out), -1, dtype=torch.int16, device=dev())
-        code = mt.MT_BF16
-    else:
-        a = rng.standard_normal((M, ld_in)).astype(np.float32)
-        A = torch.from_numpy(a).to(dev())
-        O = torch.full((C, ld_out), -1.0, dtype=torch.float32, device=dev())
-        code = mt.MT_F32
-    mt.check(mt.lib().mt_transpose_tokens(code, A.data_ptr(), ld_in, O.data_ptr(), ld_out, M, C, None))
-    torch.cuda.synchronize()
-    o = O.cpu().numpy()
-    if dtype == "bf16":
-        o = o.view(np.uint16)
-    cols = attention_token_cols(M)
-    assert sorted(cols.tolist()) == list(range(M))
-    assert np.array_equal(o[:, cols], a[:, :C].T)
-    assert np.all(o[:, M:] == (0xFFFF if dtype == "bf16" else -1.0))

@@ -155,24 +155,17 @@ def run_attention(dtype, B, T, H, hd, seed, theta=10000.0):
         et = torch.float32
     ldT = int(mt.lib().mt_token_ld(M))
     assert ldT >= M and ldT % 128 == 0 and (ldT // 128) % 2 == 1
-    qkvT = torch.empty((3 * d, ldT), dtype=et, device=dev())
-    mt.check(mt.lib().mt_rope_qkv(dtype, q_dev.data_ptr(), qkvT.data_ptr(), ldT, cos_t.data_ptr(), sin_t.data_ptr(),
-                                  B, T, H, hd, None))
+    mt.check(mt.lib().mt_rope_qkv(dtype, q_dev.data_ptr(), cos_t.data_ptr(), sin_t.data_ptr(), B, T, H, hd, None))
     o = torch.empty((M, d), dtype=et, device=dev())
     lse = torch.empty((B * H, T), dtype=torch.float32, device=dev())
-    mt.check(mt.lib().mt_attention_fwd(dtype, q_dev.data_ptr(), qkvT.data_ptr(), ldT, o.data_ptr(), lse.data_ptr(),
-                                       B, T, H, hd, None))
-    doT = torch.empty((d, ldT), dtype=et, device=dev())
-    mt.check(mt.lib().mt_transpose_tokens(dtype, do_dev.data_ptr(), d, doT.data_ptr(), ldT, M, d, None))
+    mt.check(mt.lib().mt_attention_fwd(dtype, q_dev.data_ptr(), o.data_ptr(), lse.data_ptr(), B, T, H, hd, None))
     Dsum = torch.empty((B * H, T), dtype=torch.float32, device=dev())
     dqkvT = torch.empty((3 * d, ldT), dtype=et, device=dev())
-    mt.check(mt.lib().mt_attention_bwd(dtype, q_dev.data_ptr(), qkvT.data_ptr(), o.data_ptr(), do_dev.data_ptr(),
-                                       doT.data_ptr(), ldT, lse.data_ptr(), Dsum.data_ptr(), dqkvT.data_ptr(),
-                                       B, T, H, hd, None))
+    mt.check(mt.lib().mt_attention_bwd(dtype, q_dev.data_ptr(), o.data_ptr(), do_dev.data_ptr(), lse.data_ptr(),
+                                       Dsum.data_ptr(), dqkvT.data_ptr(), ldT, B, T, H, hd, None))
     torch.cuda.synchronize()
     conv = to_f32 if dtype == mt.MT_BF16 else (lambda t: t.cpu().numpy().astype(np.float64))
-    out = dict(qkv=conv(q_dev), qkvT=conv(qkvT[:, :M]), o=conv(o), lse=lse.cpu().numpy(),
-               dqkvT=conv(dqkvT[:, :M]))
+    out = dict(qkv=conv(q_dev), qkv_in=qkv64, o=conv(o), lse=lse.cpu().numpy(), dqkvT=conv(dqkvT[:, :M]))
     # oracle in float64 on the values the kernel read
     c64, s64 = rope_tables(T, hd, theta, np.float64)
     heads = lambda x: x.reshape(B, T, H, hd).transpose(0, 2, 1, 3)
@@ -188,14 +181,6 @@ def run_attention(dtype, B, T, H, hd, seed, theta=10000.0):
     return out, ref, heads
 
 
-def attention_token_cols(M):
-    """Column of token m in attention's transposed operands: bits 2 and 3
-    of m swapped inside every complete group of 16 tokens."""
-    m = np.arange(M)
-    swapped = (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1)
-    return np.where((m | 15) < M, swapped, m)
-
-
 def close(got, ref, cos_min, rel_max):
     from tests.harness import cosine, maxnorm_rel
     c, r = cosine(got, ref), maxnorm_rel(got, ref)
@@ -207,10 +192,10 @@ def test_attention_bf16(B, T, H):
     hd = 128
     d = H * hd
     out, ref, heads = run_attention(mt.MT_BF16, B, T, H, hd, seed=T + H)
-    # rotated q, k stored back in qkv and transposed in qkvT
+    # rotated q, k stored back in qkv; v untouched
     close(heads(out["qkv"][:, :d]), ref["q"], 0.99999, 1e-2)
     close(heads(out["qkv"][:, d:2 * d]), ref["k"], 0.99999, 1e-2)
-    assert np.array_equal(out["qkvT"][:, attention_token_cols(B * T)], out["qkv"].T)
+    assert np.array_equal(out["qkv"][:, 2 * d:], out["qkv_in"][:, 2 * d:])
     close(heads(out["o"]), ref["o"], 0.9999, 2e-2)
     dq = heads(out["dqkvT"][:d].T)
     dk = heads(out["dqkvT"][d:2 * d].T)
