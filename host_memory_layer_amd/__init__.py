@@ -24,6 +24,7 @@ MODES = {"streamed": MT_STREAMED, "serialized": MT_SERIALIZED, "resident": MT_RE
 MT_BLOCK_EMBED, MT_BLOCK_LAYER, MT_BLOCK_HEAD = 0, 1, 2
 MT_FLAG_TIME_KERNELS, MT_FLAG_POISON = 1, 2
 EPI_STORE, EPI_F32, EPI_ADD_F32 = 0, 1, 2
+GEMM_A_KMAJOR, GEMM_B_KMAJOR = 1, 2
 
 
 class MtConfig(ctypes.Structure):
@@ -98,7 +99,7 @@ _SIGS = {
     "mt_version": (ctypes.c_char_p, []),
     "mt_gemm": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                                ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
-                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
+                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
     "mt_transpose": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                     ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
     "mt_rope_tables": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p,

@@ -33,6 +33,7 @@
 #include <type_traits>
 
 #include "kernels.h"
+#include "lds_tr.h"
 
 namespace mt {
 
@@ -40,7 +41,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 namespace {
 
@@ -91,17 +91,14 @@ __device__ inline int acc_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 
 // lane 4e + j of group g addresses row r0 + 4*(g/2) + e (+8 for the second
 // read), columns c0 + 16*(g%2) + 4j .. +3, and output lane i receives
 // column c0 + 16*(g%2) + i of rows e = 0..3.
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 __device__ inline bf16x8_t frag_tr(const uint8_t* tile, int r0, int c0, int lane) {
   const int g = lane >> 4, e = (lane >> 2) & 3, j = lane & 3;
   const int col = c0 + 16 * (g & 1) + 4 * j;
   const int ra = r0 + 4 * (g >> 1) + e, rb = ra + 8;
   const uint8_t* pa = tile + sw256(ra, col >> 3) + (col & 7) * 2;
   const uint8_t* pb = tile + sw256(rb, col >> 3) + (col & 7) * 2;
-  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(const void*)pa);
-  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(const void*)pb);
-  typedef short i16x8_t __attribute__((ext_vector_type(8)));
+  const i16x4_t lo = lds_read_tr16(pa);
+  const i16x4_t hi = lds_read_tr16(pb);
   const i16x8_t f = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8_t, f);
 }
@@ -144,10 +141,8 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
   // lds; kilobyte j = wave*4 + i of a tile is written by one instruction, so
   // each lane's source is chosen to land in the swizzled layout the fragment
   // reads expect.  V^T fragments come from the V tile by transposing reads.
-  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(qkv + rowbase * ld + d + h * HD), 0, (int)((int64_t)T * ld * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(qkv + rowbase * ld + 2 * d + h * HD), 0, (int)((int64_t)T * ld * 2), 0x00020000);
+  const i32x4_t krsrc = make_rsrc(qkv + rowbase * ld + d + h * HD, (uint32_t)((int64_t)T * ld * 2));
+  const i32x4_t vrsrc = make_rsrc(qkv + rowbase * ld + 2 * d + h * HD, (uint32_t)((int64_t)T * ld * 2));
   auto issue = [&](int kb, int buf) {
     uint8_t* Ks = smem + buf * 32768;
     uint8_t* Vs = Ks + 16384;
@@ -157,8 +152,8 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
       const int j = wave * 4 + i;
       const int kr = 4 * j + (lane >> 4), kc = (lane & 15) ^ swkey(kr);
       const int off = (int)((kr * ld + 8 * kc) * 2), soff = (int)((int64_t)key0 * ld * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_t*)(Ks + j * 1024), 16, off, soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void_t*)(Vs + j * 1024), 16, off, soff, 0, 0);
+      dma16(krsrc, Ks + j * 1024, off, soff);
+      dma16(vrsrc, Vs + j * 1024, off, soff);
     }
   };
 
@@ -341,10 +336,8 @@ __global__ void __launch_bounds__(256, 2) k_attn_dkdv_bf16(const uint16_t* __res
     *(u32x4_t*)(Vs + sw256(r, ch)) = vv;
   }
 
-  const __amdgpu_buffer_rsrc_t qrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(qkv + rowbase * ld + h * HD), 0, (int)((int64_t)T * ld * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(dO + rowbase * d + h * HD), 0, (int)((int64_t)T * d * 2), 0x00020000);
+  const i32x4_t qrsrc = make_rsrc(qkv + rowbase * ld + h * HD, (uint32_t)((int64_t)T * ld * 2));
+  const i32x4_t orsrc = make_rsrc(dO + rowbase * d + h * HD, (uint32_t)((int64_t)T * d * 2));
   // Each operand tile is 8 KiB = 8 direct-load kilobytes (4 rows of 256 B
   // each): wave w writes kilobytes 2w and 2w+1 of both tiles.  Q^T and dO^T
   // fragments come from the same tiles by transposing reads.
@@ -355,10 +348,9 @@ __global__ void __launch_bounds__(256, 2) k_attn_dkdv_bf16(const uint16_t* __res
     for (int i = 0; i < 2; ++i) {
       const int j = wave * 2 + i;
       const int r = 4 * j + (lane >> 4), ch = (lane & 15) ^ swkey(r);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, (lds_void_t*)(st + j * 1024), 16, (int)((r * ld + 8 * ch) * 2),
-                                               (int)((int64_t)q0 * ld * 2), 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(orsrc, (lds_void_t*)(st + TILE + j * 1024), 16,
-                                               (int)((r * d + 8 * ch) * 2), (int)((int64_t)q0 * d * 2), 0, 0);
+      dma16(qrsrc, st + j * 1024, (int)((r * ld + 8 * ch) * 2),
+                                               (int)((int64_t)q0 * ld * 2));
+      dma16(orsrc, st + TILE + j * 1024, (int)((r * d + 8 * ch) * 2), (int)((int64_t)q0 * d * 2));
     }
   };
   // lse and D of the tile's queries in this lane's accumulator rows: rows
@@ -486,10 +478,8 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq_bf16(const uint16_t* __restr
   }
 
   const int nkb = min(T, (qb + 1) * 128) / KB;
-  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(qkv + rowbase * ld + d + h * HD), 0, (int)((int64_t)T * ld * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(qkv + rowbase * ld + 2 * d + h * HD), 0, (int)((int64_t)T * ld * 2), 0x00020000);
+  const i32x4_t krsrc = make_rsrc(qkv + rowbase * ld + d + h * HD, (uint32_t)((int64_t)T * ld * 2));
+  const i32x4_t vrsrc = make_rsrc(qkv + rowbase * ld + 2 * d + h * HD, (uint32_t)((int64_t)T * ld * 2));
   // 8 direct-load kilobytes per tile (4 rows of 256 B each); wave w writes
   // kilobytes 2w, 2w+1 of each.
   auto issue = [&](int kb, int buf) {
@@ -501,8 +491,8 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq_bf16(const uint16_t* __restr
       const int j = wave * 2 + i;
       const int r = 4 * j + (lane >> 4), ch = (lane & 15) ^ swkey(r);
       const int voff = (r * ld + 8 * ch) * 2, soff = (int)((int64_t)key0 * ld * 2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_void_t*)(Ks + j * 1024), 16, voff, soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_void_t*)(Vs + j * 1024), 16, voff, soff, 0, 0);
+      dma16(krsrc, Ks + j * 1024, voff, soff);
+      dma16(vrsrc, Vs + j * 1024, voff, soff);
     }
   };
 

@@ -629,6 +629,26 @@ void cast_transpose(const float* in, T* out, T* outT, int64_t ldT, int R, int C,
   hipLaunchKernelGGL(k_cast_transpose<T>, dim3(cdiv(C, 64), cdiv(R, 64)), dim3(256), 0, s, in, out, outT, ldT, R, C);
 }
 
+// out = T(in), 4 elements per thread (n % 4 == 0, 16-byte aligned), else 1.
+template <typename T, bool V4_>
+__global__ void __launch_bounds__(256) k_cast(const float* __restrict__ in, T* __restrict__ out, int64_t n) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * (V4_ ? 4 : 1);
+  if (i >= n) return;
+  if (V4_)
+    V4<T>::st(out + i, *(const float4*)(in + i));
+  else
+    out[i] = stf<T>(in[i]);
+}
+
+template <typename T>
+void cast(const float* in, T* out, int64_t n, hipStream_t s) {
+  if (n <= 0) return;
+  if (n % 4 == 0 && ((uintptr_t)in & 15) == 0 && ((uintptr_t)out & 7) == 0)
+    hipLaunchKernelGGL((k_cast<T, true>), dim3((unsigned)cdiv(n / 4, 256)), dim3(256), 0, s, in, out, n);
+  else
+    hipLaunchKernelGGL((k_cast<T, false>), dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, in, out, n);
+}
+
 __global__ void k_fill_u32(uint32_t* p, uint32_t v, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = v;
 }
@@ -652,7 +672,8 @@ void fill_u32(void* p, uint32_t value, size_t n_words, hipStream_t s) {
   template void swiglu_bwd<T>(const T*, const T*, T*, int, int, hipStream_t);                                   \
   template void xent<T>(const float*, const int32_t*, float*, T*, int, int, int, float, hipStream_t);           \
   template void transpose<T>(const T*, int64_t, T*, int64_t, int, int, hipStream_t);                            \
-  template void cast_transpose<T>(const float*, T*, T*, int64_t, int, int, hipStream_t);
+  template void cast_transpose<T>(const float*, T*, T*, int64_t, int, int, hipStream_t);                       \
+  template void cast<T>(const float*, T*, int64_t, hipStream_t);
 
 MT_INST(float)
 MT_INST(uint16_t)

@@ -23,6 +23,7 @@
 #include <memory>
 #include <mutex>
 #include <thread>
+#include <type_traits>
 #include <vector>
 
 #include "adam.h"
@@ -98,6 +99,10 @@ struct Model {
   uint64_t store_bytes = 0, opt_bytes = 0, slot_bytes = 0;
   int L, d, H, hd, F, V, B, Tq, M;
   int64_t Mp;  // padded row stride of token-major transposed buffers
+  // bf16 with supported shapes: the data- and weight-gradient GEMMs read
+  // token-major activations and row-major weights as K-major operands, so
+  // no activation or weight is transposed (kmajor: layers, kmajor_head: head)
+  bool kmajor = false, kmajor_head = false;
   int E;  // bytes per weight element
 
   uint8_t* arena = nullptr;
@@ -160,14 +165,14 @@ struct Model {
   void carve_bwd(Carver& c, BwdWs<T>& w) {
     const uint64_t Md = (uint64_t)M * d, MF = (uint64_t)M * F;
     w.dxb = c.take<T>(Md * E);
-    w.dxbT = c.take<T>((uint64_t)d * Mp * E);
-    w.tmpT = c.take<T>((uint64_t)std::max(d, F) * Mp * E);
+    w.dxbT = kmajor ? nullptr : c.take<T>((uint64_t)d * Mp * E);
+    w.tmpT = kmajor && kmajor_head ? nullptr : c.take<T>((uint64_t)std::max(d, F) * Mp * E);
     w.dy = c.take<T>(MF * E);
     w.dgu = c.take<T>(2 * MF * E);
-    w.dguT = c.take<T>(2 * (uint64_t)F * Mp * E);
+    w.dguT = kmajor ? nullptr : c.take<T>(2 * (uint64_t)F * Mp * E);
     w.do_ = c.take<T>(Md * E);
     w.dqkvT = c.take<T>(3 * (uint64_t)d * Mp * E);
-    w.dqkv = c.take<T>(3 * Md * E);
+    w.dqkv = kmajor ? nullptr : c.take<T>(3 * Md * E);
     w.dh = c.take<float>(Md * 4);
     w.dx1 = c.take<float>(Md * 4);
     w.Dsum = c.take<float>((uint64_t)M * H * 4);
@@ -180,7 +185,7 @@ struct Model {
     const uint64_t MV = (uint64_t)M * V;
     w.z = c.take<T>((uint64_t)M * d * E);
     w.dlogits = c.take<T>(MV * E);
-    w.dlogitsT = c.take<T>((uint64_t)V * Mp * E);
+    w.dlogitsT = kmajor_head ? nullptr : c.take<T>((uint64_t)V * Mp * E);
     w.rz = c.take<float>((uint64_t)M * 4);
     w.logits = c.take<float>(MV * 4);
     w.row_loss = c.take<float>((uint64_t)M * 4);
@@ -192,7 +197,7 @@ struct Model {
     Carver c{base};
     for (int s = 0; s < 2; ++s) wslot[s] = c.take<uint8_t>(slot_bytes);
     for (int s = 0; s < 2; ++s) gslot[s] = c.take<uint8_t>(slot_bytes);
-    wt = c.take<uint8_t>(slot_bytes);
+    wt = kmajor && kmajor_head ? nullptr : c.take<uint8_t>(slot_bytes);
     if (cfg.mode == MT_RESIDENT) {
       uint64_t tot = 0;
       for (auto& b : blocks) tot += round_up(b.w_bytes, 256);
@@ -268,6 +273,16 @@ struct Model {
     M = B * Tq;
     Mp = token_ld(M);
     E = wbytes(c);
+    if (c.store_dtype == MT_BF16) {
+      const int A_ = GEMM_A_KMAJOR, B_ = GEMM_B_KMAJOR;
+      auto ok = [&](int m, int n, int k, int64_t lda, int64_t ldb, int lay) {
+        return gemm_layout_ok(m, n, k, lda, ldb, lay);
+      };
+      kmajor = ok(d, F, M, d, F, A_ | B_) && ok(M, F, d, d, F, B_) && ok(2 * F, d, M, 2 * F, d, A_ | B_) &&
+               ok(M, d, 2 * F, 2 * F, d, B_) && ok(d, d, M, d, d, A_ | B_) && ok(M, d, d, d, d, B_) &&
+               ok(3 * d, d, M, Mp, d, B_) && ok(M, d, 3 * d, Mp, d, A_ | B_);
+      kmajor_head = kmajor && ok(V, d, M, V, d, A_ | B_) && ok(M, d, V, V, d, B_);
+    }
     n_uses = 2 * L + 3;
   }
   uint64_t device_bytes() { return cfg.store_dtype == MT_BF16 ? carve_all<uint16_t>(nullptr) : carve_all<float>(nullptr); }
@@ -277,13 +292,16 @@ struct Model {
   // --------------------------------------------------------- kernels --
   template <typename T>
   void gemm(const T* A, int64_t lda, const T* Bm, int64_t ldb, void* C, int64_t ldc, const float* R, int64_t ldr,
-            int m, int n, int k, Epi epi) {
+            int m, int n, int k, Epi epi, int layout = 0) {
     const bool timed = cfg.flags & MT_FLAG_TIME_KERNELS;
     // operands read once, result written once (and the residual read once)
     const double out_b = epi == EPI_STORE ? sizeof(T) : 4.0;
     const double bytes = ((double)m * k + (double)n * k) * sizeof(T) + (double)m * n * (out_b + (epi == EPI_ADD_F32 ? 4 : 0));
     if (timed) record_kernel_start(2.0 * m * n * k, 0, bytes);
-    gemm_nt<T>(A, lda, Bm, ldb, C, ldc, R, ldr, m, n, k, epi, sc);
+    if constexpr (std::is_same<T, uint16_t>::value)
+      gemm_bf16(A, lda, Bm, ldb, layout, C, ldc, R, ldr, m, n, k, epi, sc);
+    else
+      gemm_nt<T>(A, lda, Bm, ldb, C, ldc, R, ldr, m, n, k, epi, sc);
     if (timed) record_kernel_end();
   }
   void record_kernel_start(double flops, int kind, double bytes = 0.0) {
@@ -334,6 +352,10 @@ struct Model {
   void layer_bwd(const LayerW<T>& w, const LayerWT<T>& wt_, const float* x, const Acts<T>& a, const float* dx2,
                  float* dx_out, const LayerW<T>& g) {
     BwdWs<T> ws = bwdws<T>();
+    if (kmajor) {
+      layer_bwd_kmajor<T>(w, x, a, dx2, dx_out, g, ws);
+      return;
+    }
     // down projection
     cast_transpose<T>(dx2, ws.dxb, ws.dxbT, Mp, M, d, sc);
     transpose<T>(a.y, F, ws.tmpT, Mp, M, F, sc);
@@ -366,6 +388,42 @@ struct Model {
     rmsnorm_bwd<T>(ws.dh, x, w.anorm, a.r1, ws.dx1, dx_out, ws.part, g.anorm, M, d, sc);
   }
 
+  // The same backward with K-major operands (no transposes).  C = A.B with
+  // A(i, k), B(j, k): a weight gradient dW[i][j] = sum over tokens m of
+  // dY[m][i] X[m][j] reads both token-major matrices as K-major; a data
+  // gradient dX[m][j] = sum_i dY[m][i] W[i][j] reads dY as is and the
+  // weight [out x in] as K-major.
+  template <typename T>
+  void layer_bwd_kmajor(const LayerW<T>& w, const float* x, const Acts<T>& a, const float* dx2, float* dx_out,
+                        const LayerW<T>& g, const BwdWs<T>& ws) {
+    const int KA = GEMM_A_KMAJOR, KB = GEMM_B_KMAJOR;
+    // down projection
+    cast<T>(dx2, ws.dxb, (int64_t)M * d, sc);
+    gemm<T>(ws.dxb, d, a.y, F, g.d, F, nullptr, 0, d, F, M, EPI_STORE, KA | KB);
+    gemm<T>(ws.dxb, d, w.d, F, ws.dy, F, nullptr, 0, M, F, d, EPI_STORE, KB);
+    // SwiGLU and gate/up projection
+    swiglu_bwd<T>(ws.dy, a.gu, ws.dgu, M, F, sc);
+    gemm<T>(ws.dgu, 2 * F, a.h2, d, g.gu, d, nullptr, 0, 2 * F, d, M, EPI_STORE, KA | KB);
+    gemm<T>(ws.dgu, 2 * F, w.gu, d, ws.dh, d, nullptr, 0, M, d, 2 * F, EPI_F32, KB);
+    rmsnorm_bwd<T>(ws.dh, a.x1, w.fnorm, a.r2, dx2, ws.dx1, ws.part, g.fnorm, M, d, sc);
+    // attention output projection
+    cast<T>(ws.dx1, ws.dxb, (int64_t)M * d, sc);
+    gemm<T>(ws.dxb, d, a.o, d, g.o, d, nullptr, 0, d, d, M, EPI_STORE, KA | KB);
+    gemm<T>(ws.dxb, d, w.o, d, ws.do_, d, nullptr, 0, M, d, d, EPI_STORE, KB);
+    // attention
+    attn_bwd_dsum<T>(ws.do_, a.o, ws.Dsum, B, Tq, H, hd, sc);
+    const bool timed = cfg.flags & MT_FLAG_TIME_KERNELS;
+    if (timed) record_kernel_start(2.5 * attn_fwd_flops(), 1);
+    attn_bwd<T>(a.qkv, ws.do_, a.lse, ws.Dsum, ws.dqkvT, Mp, B, Tq, H, hd, sc);
+    if (timed) record_kernel_end();
+    rope_bwd_T<T>(ws.dqkvT, Mp, cosT, sinT, M, Tq, d, hd, sc);
+    // QKV projection: dqkvT [3d x M] is K-contiguous for the weight gradient
+    // and K-major for the data gradient
+    gemm<T>(ws.dqkvT, Mp, a.h, d, g.qkv, d, nullptr, 0, 3 * d, d, M, EPI_STORE, KB);
+    gemm<T>(ws.dqkvT, Mp, w.qkv, d, ws.dh, d, nullptr, 0, M, d, 3 * d, EPI_F32, KA | KB);
+    rmsnorm_bwd<T>(ws.dh, x, w.anorm, a.r1, ws.dx1, dx_out, ws.part, g.anorm, M, d, sc);
+  }
+
   // Final norm, logits, loss, and the head's backward.  Returns dx^L in dx_out.
   template <typename T>
   void head_fwd_bwd(const mt_block_desc& b, uint8_t* wreg, uint8_t* greg, float* dx_out) {
@@ -383,12 +441,17 @@ struct Model {
     sum_fixed(hw.row_loss, hw.loss, M, inv_n, sc);
     MT_HIP(hipMemcpyAsync(h_loss, hw.loss, sizeof(float), hipMemcpyDeviceToHost, sc));
     MT_HIP(hipEventRecord(ev_loss, sc));
-    transpose<T>(hw.dlogits, V, hw.dlogitsT, Mp, M, V, sc);
-    transpose<T>(hw.z, d, ws.tmpT, Mp, M, d, sc);
-    gemm<T>(hw.dlogitsT, Mp, ws.tmpT, Mp, gwh, d, nullptr, 0, V, d, M, EPI_STORE);
-    T* whT = (T*)wt;
-    transpose<T>(wh, d, whT, V, V, d, sc);
-    gemm<T>(hw.dlogits, V, whT, V, ws.dh, d, nullptr, 0, M, d, V, EPI_F32);
+    if (kmajor_head) {
+      gemm<T>(hw.dlogits, V, hw.z, d, gwh, d, nullptr, 0, V, d, M, EPI_STORE, GEMM_A_KMAJOR | GEMM_B_KMAJOR);
+      gemm<T>(hw.dlogits, V, wh, d, ws.dh, d, nullptr, 0, M, d, V, EPI_F32, GEMM_B_KMAJOR);
+    } else {
+      transpose<T>(hw.dlogits, V, hw.dlogitsT, Mp, M, V, sc);
+      transpose<T>(hw.z, d, ws.tmpT, Mp, M, d, sc);
+      gemm<T>(hw.dlogitsT, Mp, ws.tmpT, Mp, gwh, d, nullptr, 0, V, d, M, EPI_STORE);
+      T* whT = (T*)wt;
+      transpose<T>(wh, d, whT, V, V, d, sc);
+      gemm<T>(hw.dlogits, V, whT, V, ws.dh, d, nullptr, 0, M, d, V, EPI_F32);
+    }
     rmsnorm_bwd<T>(ws.dh, xL, fin, hw.rz, nullptr, dx_out, ws.part, gfin, M, d, sc);
   }
 
@@ -410,11 +473,13 @@ struct Model {
     const int l = b.layer;
     LayerW<T> w = bind_layer<T>(wreg, b);
     LayerW<T> g = bind_layer<T>(greg, b);
-    LayerWT<T> t{(T*)wt, (T*)wt + (uint64_t)3 * d * d, (T*)wt + (uint64_t)4 * d * d,
-                 (T*)wt + (uint64_t)4 * d * d + (uint64_t)2 * F * d};
+    LayerWT<T> t{};
+    if (!kmajor)
+      t = LayerWT<T>{(T*)wt, (T*)wt + (uint64_t)3 * d * d, (T*)wt + (uint64_t)4 * d * d,
+                     (T*)wt + (uint64_t)4 * d * d + (uint64_t)2 * F * d};
     Acts<T> a = acts<T>(l);
     if (cfg.mode != MT_RESIDENT) layer_fwd<T>(w, x_ckpt(l), a, nullptr, false);  // recompute
-    weight_transposes<T>(w, t);
+    if (!kmajor) weight_transposes<T>(w, t);
     layer_bwd<T>(w, t, x_ckpt(l), a, dx_in, dx_out, g);
   }
 

@@ -35,13 +35,13 @@
 #include <type_traits>
 
 #include "kernels.h"
+#include "lds_tr.h"
 
 namespace mt {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 namespace {
 
@@ -169,6 +169,28 @@ __global__ void __launch_bounds__(NTHREADS) k_gemm_bf16_generic(const uint16_t* 
 constexpr int STAGE = 2 * BM * BK * 2;  // A and B tiles of one K step: 64 KiB
 
 __device__ inline int swz128(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+// K-major tiles [64 k x 256 columns] have 512-byte rows (two bank rows), so
+// only the chunk index picks the bank: rows r..r+3 (r % 4 == 0) move their
+// chunks to 4 different quarters of the bank row.
+__device__ inline int kmkey(int row) { return (row & 3) << 2; }
+__device__ inline int swz512(int row, int chunk) { return row * 512 + ((chunk ^ kmkey(row)) << 4); }
+
+
+// MFMA fragment of a K-major tile: lane l gets column c0 + (l & 31) at the
+// 8 contraction indices 16*ks + 8*(l/32) .. +7, by two transposing LDS
+// reads.  A transposing read works on groups of 16 lanes: output lane i,
+// element e is element i%4 of the 8 bytes addressed by lane 4e + i/4 of its
+// group; so lane 4e + j of group g addresses row 16*ks + 8*(g/2) + e (+4 for
+// the second read) at columns c0 + 16*(g%2) + 4j .. +3.
+__device__ inline bf16x8_t frag_kmajor(const uint8_t* tile, int ks, int c0, int lane) {
+  const int g = lane >> 4, e = (lane >> 2) & 3, j = lane & 3;
+  const int col = c0 + 16 * (g & 1) + 4 * j;
+  const int ra = 16 * ks + 8 * (g >> 1) + e, rb = ra + 4;
+  const i16x4_t lo = lds_read_tr16(tile + swz512(ra, col >> 3) + (col & 7) * 2);
+  const i16x4_t hi = lds_read_tr16(tile + swz512(rb, col >> 3) + (col & 7) * 2);
+  const i16x8_t f = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, f);
+}
 
 template <bool V>
 using Flag = std::integral_constant<bool, V>;
@@ -190,8 +212,10 @@ __device__ inline void tile_of(int lin, int tiles_m, int tiles_n, int64_t& m0, i
 // 4 consecutive outputs per store through a buffer descriptor that drops
 // rows past M, while lanes past N aim beyond the descriptor.  Otherwise
 // element stores.
-template <int EPI, bool VEC>
-__global__ void __launch_bounds__(256, 1) k_gemm_bf16_nt(const uint16_t* __restrict__ A, int64_t lda,
+// AKM / BKM: operand A (B) is K-major, [K x M] ([K x N]) with row stride
+// lda (ldb), instead of K-contiguous [M x K] ([N x K]).
+template <int EPI, bool VEC, bool AKM, bool BKM>
+__global__ void __launch_bounds__(256, 1) k_gemm_bf16_tile(const uint16_t* __restrict__ A, int64_t lda,
                                                        const uint16_t* __restrict__ B, int64_t ldb, void* C,
                                                        int64_t ldc, const float* R, int64_t ldr, int M, int N, int K,
                                                        int tiles_m, int tiles_n) {
@@ -223,25 +247,40 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_nt(const uint16_t* __restr
     return __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)base + row0 * ld * esize), 0,
                                              (int)(rows * ld * esize), 0x00020000);
   };
+  // operand tiles: descriptors for the inline-assembly direct loads
+  auto orsrc_of = [&](const uint16_t* base, int64_t row0, int64_t rows_total, int64_t ld) {
+    const int64_t rows = min<int64_t>(BM, rows_total - row0);
+    return make_rsrc(base + row0 * ld, (uint32_t)(rows * ld * 2));
+  };
+  // K-major operand: the descriptor starts at the tile's first column and
+  // runs to the end of the matrix.  Columns past M (N) of a last tile read
+  // neighbouring data, or zero past the end; they only reach outputs that
+  // are never stored.
+  auto rsrc_km = [&](const uint16_t* base, int64_t col0, int64_t ld) {
+    return make_rsrc(base + col0, (uint32_t)(((int64_t)K * ld - col0) * 2));
+  };
 
-  // Direct load i (0..7) of an operand tile: kilobyte j = wave*8 + i, rows
-  // 8j .. 8j+7; lane l reads row 8j + l/8, logical chunk (l%8) ^ ((row>>1)&7),
-  // which lands at physical chunk l%8 of that row.
+  // Direct load i (0..7) of an operand tile writes kilobyte j = wave*8 + i.
+  // K-contiguous tile [256 rows x 64 k]: rows 8j .. 8j+7; lane l reads row
+  // 8j + l/8, logical chunk (l%8) ^ ((row>>1)&7), which lands at physical
+  // chunk l%8.  K-major tile [64 k x 256 columns]: rows 2j, 2j+1; lane l
+  // reads row 2j + l/32, logical chunk (l%32) ^ kmkey(row).
   int aoff[8], boff[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int r = 8 * (wave * 8 + i) + (lane >> 3);
-    const int lc = (lane & 7) ^ ((r >> 1) & 7);
-    aoff[i] = (int)((r * lda + 8 * lc) * 2);
-    boff[i] = (int)((r * ldb + 8 * lc) * 2);
+    const int j = wave * 8 + i;
+    const int r = 8 * j + (lane >> 3), lc = (lane & 7) ^ ((r >> 1) & 7);
+    const int rk = 2 * j + (lane >> 5), lck = (lane & 31) ^ kmkey(rk);
+    aoff[i] = AKM ? (int)((rk * lda + 8 * lck) * 2) : (int)((r * lda + 8 * lc) * 2);
+    boff[i] = BKM ? (int)((rk * ldb + 8 * lck) * 2) : (int)((r * ldb + 8 * lc) * 2);
   }
-  auto load_a = [&](__amdgpu_buffer_rsrc_t rs, int kt, int i) {
-    uint8_t* dst = smem + (kt & 1) * STAGE + (wave * 8 + i) * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)dst, 16, aoff[i], kt * BK * 2, 0, 0);
+  const int astep = AKM ? (int)(BK * lda * 2) : BK * 2;  // bytes per K step
+  const int bstep = BKM ? (int)(BK * ldb * 2) : BK * 2;
+  auto load_a = [&](i32x4_t rs, int kt, int i) {
+    dma16(rs, smem + (kt & 1) * STAGE + (wave * 8 + i) * 1024, aoff[i], kt * astep);
   };
-  auto load_b = [&](__amdgpu_buffer_rsrc_t rs, int kt, int i) {
-    uint8_t* dst = smem + (kt & 1) * STAGE + STAGE / 2 + (wave * 8 + i) * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)dst, 16, boff[i], kt * BK * 2, 0, 0);
+  auto load_b = [&](i32x4_t rs, int kt, int i) {
+    dma16(rs, smem + (kt & 1) * STAGE + STAGE / 2 + (wave * 8 + i) * 1024, boff[i], kt * bstep);
   };
 
   const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
@@ -253,11 +292,13 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_nt(const uint16_t* __restr
     const uint8_t* As = smem + (kt & 1) * STAGE;
     const uint8_t* Bs = As + STAGE / 2;
     const int c = ks * 2 + (lane >> 5);
+    auto rd128 = [&](const uint8_t* p) { return *(const bf16x8_t*)p; };
     if (q == 0 || q > 4) {
       const int i = q == 0 ? 0 : q - 4;
-      a[set][i] = *(const bf16x8_t*)(As + swz128(wm + 32 * i + (lane & 31), c));
+      a[set][i] = AKM ? frag_kmajor(As, ks, wm + 32 * i, lane) : rd128(As + swz128(wm + 32 * i + (lane & 31), c));
     } else {
-      b[set][q - 1] = *(const bf16x8_t*)(Bs + swz128(wn + 32 * (q - 1) + (lane & 31), c));
+      b[set][q - 1] = BKM ? frag_kmajor(Bs, ks, wn + 32 * (q - 1), lane)
+                          : rd128(Bs + swz128(wn + 32 * (q - 1) + (lane & 31), c));
     }
   };
   // B fragments are the MFMA's first operand: the accumulator then holds
@@ -269,7 +310,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_nt(const uint16_t* __restr
 
   int64_t m0, n0;
   tile_of(t, tiles_m, tiles_n, m0, n0);
-  __amdgpu_buffer_rsrc_t ar = rsrc_of(A, m0, M, lda, 2), br = rsrc_of(B, n0, N, ldb, 2);
+  i32x4_t ar = AKM ? rsrc_km(A, m0, lda) : orsrc_of(A, m0, M, lda);
+  i32x4_t br = BKM ? rsrc_km(B, n0, ldb) : orsrc_of(B, n0, N, ldb);
 
   // One K step.  LOAD_B: load B of step kt+1 during sub-step 0; LOAD_A2:
   // load A of step kt+2 during sub-step 3; NEXT: read step kt+1's first
@@ -451,8 +493,8 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_nt(const uint16_t* __restr
     t += stride;
     if (t >= hi) break;
     tile_of(t, tiles_m, tiles_n, m0, n0);
-    ar = rsrc_of(A, m0, M, lda, 2);
-    br = rsrc_of(B, n0, N, ldb, 2);
+    ar = AKM ? rsrc_km(A, m0, lda) : orsrc_of(A, m0, M, lda);
+    br = BKM ? rsrc_km(B, n0, ldb) : orsrc_of(B, n0, N, ldb);
     prologue();
   }
 }
@@ -509,32 +551,53 @@ int persistent_workgroups() {
 
 }  // namespace
 
-template <>
-void gemm_nt<uint16_t>(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, void* C, int64_t ldc,
-                       const float* R, int64_t ldr, int M, int N, int K, Epi epi, hipStream_t s) {
+bool gemm_layout_ok(int M, int N, int K, int64_t lda, int64_t ldb, int layout) {
+  (void)M;
+  (void)N;
+  if (K % BK || K < 3 * BK || lda % 8 || ldb % 8) return false;
+  const int64_t lim = (int64_t)1 << 31;
+  // 32-bit buffer offsets: a K-major operand is addressed from its tile's
+  // first column to the end of the matrix
+  if ((layout & GEMM_A_KMAJOR) && (int64_t)K * lda * 2 >= lim) return false;
+  if ((layout & GEMM_B_KMAJOR) && (int64_t)K * ldb * 2 >= lim) return false;
+  return true;
+}
+
+void gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int layout, void* C, int64_t ldc,
+               const float* R, int64_t ldr, int M, int N, int K, Epi epi, hipStream_t s) {
   if (M <= 0 || N <= 0) return;
   if (K % 8 || lda % 8 || ldb % 8 || ((uintptr_t)A & 15) || ((uintptr_t)B & 15))
     throw ApiError{MT_E_INVALID, "bf16 GEMM needs K, lda, ldb multiples of 8 and 16-byte aligned operands"};
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const dim3 grid(tiles_m * tiles_n);
+  if (layout != 0 && !gemm_layout_ok(M, N, K, lda, ldb, layout))
+    throw ApiError{MT_E_INVALID, "K-major bf16 GEMM operands need K % 64 == 0, K >= 192, K*ld*2 < 2^31"};
   if (K % BK == 0 && K >= 3 * BK) {
     // buffer offsets are 32-bit: one 256-row panel of every operand must fit
     const int64_t lim = (int64_t)1 << 31;
-    if ((int64_t)BM * lda * 2 >= lim || (int64_t)BN * ldb * 2 >= lim || (int64_t)BM * ldc * 4 >= lim ||
+    if ((!(layout & GEMM_A_KMAJOR) && (int64_t)BM * lda * 2 >= lim) ||
+        (!(layout & GEMM_B_KMAJOR) && (int64_t)BN * ldb * 2 >= lim) || (int64_t)BM * ldc * 4 >= lim ||
         (R && (int64_t)BM * ldr * 4 >= lim))
       throw ApiError{MT_E_INVALID, "bf16 GEMM row stride too large"};
     const bool vec = N % 4 == 0 && ldc % 4 == 0 && ((uintptr_t)C & 15) == 0 &&
                      (epi != EPI_ADD_F32 || (ldr % 4 == 0 && ((uintptr_t)R & 15) == 0));
     const int ntiles = tiles_m * tiles_n;
     const dim3 pgrid(std::min(ntiles, persistent_workgroups()));
-#define L_(E, V)                                                                                                  \
-  hipLaunchKernelGGL((k_gemm_bf16_nt<E, V>), pgrid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, R, ldr, M, N, K, tiles_m, \
-                     tiles_n)
-#define LV_(E) \
-  if (vec) {   \
-    L_(E, true);  \
-  } else {     \
-    L_(E, false); \
+#define L_(E, V, AK, BK_)                                                                                      \
+  hipLaunchKernelGGL((k_gemm_bf16_tile<E, V, AK, BK_>), pgrid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, R, ldr, M, N, \
+                     K, tiles_m, tiles_n)
+#define LL_(E, V)                  \
+  switch (layout) {                \
+    case 0: L_(E, V, false, false); break; \
+    case 1: L_(E, V, true, false); break;  \
+    case 2: L_(E, V, false, true); break;  \
+    default: L_(E, V, true, true); break;  \
+  }
+#define LV_(E)     \
+  if (vec) {       \
+    LL_(E, true)   \
+  } else {         \
+    LL_(E, false)  \
   }
     switch (epi) {
       case EPI_STORE: LV_(EPI_STORE) break;
@@ -542,6 +605,7 @@ void gemm_nt<uint16_t>(const uint16_t* A, int64_t lda, const uint16_t* B, int64_
       case EPI_ADD_F32: LV_(EPI_ADD_F32) break;
     }
 #undef LV_
+#undef LL_
 #undef L_
     return;
   }
@@ -554,6 +618,12 @@ void gemm_nt<uint16_t>(const uint16_t* A, int64_t lda, const uint16_t* B, int64_
     case EPI_ADD_F32: L_(EPI_ADD_F32); break;
   }
 #undef L_
+}
+
+template <>
+void gemm_nt<uint16_t>(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, void* C, int64_t ldc,
+                       const float* R, int64_t ldr, int M, int N, int K, Epi epi, hipStream_t s) {
+  gemm_bf16(A, lda, B, ldb, 0, C, ldc, R, ldr, M, N, K, epi, s);
 }
 
 template <>

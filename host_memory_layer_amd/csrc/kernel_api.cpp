@@ -31,20 +31,23 @@ using namespace mt;
 extern "C" {
 
 int mt_gemm(int32_t dtype, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
-            const float* R, int64_t ldr, int32_t M, int32_t N, int32_t K, int32_t epi, void* stream) {
+            const float* R, int64_t ldr, int32_t M, int32_t N, int32_t K, int32_t epi, int32_t layout, void* stream) {
   return kguard([&] {
     need(epi >= 0 && epi <= 2, "epi");
+    need(layout >= 0 && layout <= 3, "layout");
     need(M >= 0 && N >= 0 && K >= 0, "negative size");
-    need(lda >= K && ldb >= K && ldc >= N, "leading dimensions");
+    need((layout & MT_GEMM_A_KMAJOR ? lda >= M : lda >= K) && (layout & MT_GEMM_B_KMAJOR ? ldb >= N : ldb >= K) &&
+             ldc >= N,
+         "leading dimensions");
     need(epi != 2 || (R && ldr >= N), "R");
     if (dtype == MT_BF16)
-      gemm_nt<uint16_t>((const uint16_t*)A, lda, (const uint16_t*)B, ldb, C, ldc, R, ldr, M, N, K, (Epi)epi,
-                        (hipStream_t)stream);
-    else if (dtype == MT_F32)
+      gemm_bf16((const uint16_t*)A, lda, (const uint16_t*)B, ldb, layout, C, ldc, R, ldr, M, N, K, (Epi)epi,
+                (hipStream_t)stream);
+    else if (dtype == MT_F32 && layout == 0)
       gemm_nt<float>((const float*)A, lda, (const float*)B, ldb, C, ldc, R, ldr, M, N, K, (Epi)epi,
                      (hipStream_t)stream);
     else
-      need(false, "dtype");
+      need(false, "dtype / layout");
   });
 }
 

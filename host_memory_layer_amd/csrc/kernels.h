@@ -18,6 +18,14 @@ enum Epi {
 template <typename T>
 void gemm_nt(const T* A, int64_t lda, const T* B, int64_t ldb, void* C, int64_t ldc, const float* R,
              int64_t ldr, int M, int N, int K, Epi epi, hipStream_t s);
+// bf16 with operand layouts: an operand is K-contiguous ([M x K] or [N x K],
+// as in gemm_nt) or, with its bit in `layout`, K-major ([K x M] or [K x N],
+// row stride lda / ldb), read through transposing LDS loads.  K-major
+// operands need gemm_layout_ok().
+enum GemmLayout { GEMM_A_KMAJOR = 1, GEMM_B_KMAJOR = 2 };
+bool gemm_layout_ok(int M, int N, int K, int64_t lda, int64_t ldb, int layout);
+void gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int layout, void* C, int64_t ldc,
+               const float* R, int64_t ldr, int M, int N, int K, Epi epi, hipStream_t s);
 
 // ---------------------------------------------------------- elementwise --
 template <typename T>
@@ -63,6 +71,9 @@ void sum_fixed(const float* x, float* out, int n, float scale, hipStream_t s);
 // out[C x R] = in[R x C]^T.
 template <typename T>
 void transpose(const T* in, int64_t ld_in, T* out, int64_t ld_out, int R, int C, hipStream_t s);
+// out = T(in) for n floats.
+template <typename T>
+void cast(const float* in, T* out, int64_t n, hipStream_t s);
 // out = T(in) and outT = T(in)^T (row stride ldT) for in float [R x C].
 template <typename T>
 void cast_transpose(const float* in, T* out, T* outT, int64_t ldT, int R, int C, hipStream_t s);

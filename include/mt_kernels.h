@@ -18,15 +18,21 @@
 extern "C" {
 #endif
 
-/* C[M x N] = A[M x K] . B[N x K]^T, fp32 accumulation.  A, B row-major with
- * row strides lda, ldb (elements).  epi 0: C has dtype (bf16 rounded to
- * nearest-even); epi 1: C is float; epi 2: C (float) = R + A.B^T with R float
- * [M x N], row stride ldr.  bf16 needs K, lda, ldb multiples of 8 and 16-byte
- * aligned A, B.  Every dense projection of the layer (forward, data gradient,
- * weight gradient) is this contraction once the operand that is not
- * contraction-contiguous is transposed. */
+/* C[M x N] = sum_k A(m, k) B(n, k), fp32 accumulation.  Operand layouts
+ * (bits of `layout`): A is [M x K] row-major (K-contiguous, row stride lda)
+ * or, with MT_GEMM_A_KMAJOR, [K x M] (row stride lda); B likewise [N x K] or,
+ * with MT_GEMM_B_KMAJOR, [K x N].  epi 0: C has dtype (bf16 rounded to
+ * nearest-even); epi 1: C is float; epi 2: C (float) = R + A.B with R float
+ * [M x N], row stride ldr.  bf16 needs K, lda, ldb multiples of 8 and
+ * 16-byte aligned A, B; K-major operands also need K % 64 == 0, K >= 192 and
+ * K * ld * 2 < 2^31 (else MT_E_INVALID); f32 supports layout 0 only.  Every
+ * dense projection of the layer is one of these: forward Y = X W^T (layout
+ * 0), data gradient dX = dY W (B K-major), weight gradient dW = dY^T X
+ * (both K-major, K = tokens). */
+#define MT_GEMM_A_KMAJOR 1
+#define MT_GEMM_B_KMAJOR 2
 int mt_gemm(int32_t dtype, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
-            const float* R, int64_t ldr, int32_t M, int32_t N, int32_t K, int32_t epi, void* stream);
+            const float* R, int64_t ldr, int32_t M, int32_t N, int32_t K, int32_t epi, int32_t layout, void* stream);
 
 /* out[C x R] = in[R x C]^T (row strides ld_in, ld_out). */
 int mt_transpose(int32_t dtype, const void* in, int64_t ld_in, void* out, int64_t ld_out, int32_t R, int32_t C,

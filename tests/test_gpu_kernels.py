@@ -36,9 +36,9 @@ def to_f32(t_bits):
     return datagen.bf16_bits_to_f32(t_bits.cpu().numpy().view(np.uint16)).astype(np.float64)
 
 
-def gemm(dtype, A, lda, B, ldb, C, ldc, M, N, K, epi, R=None, ldr=0):
+def gemm(dtype, A, lda, B, ldb, C, ldc, M, N, K, epi, R=None, ldr=0, layout=0):
     mt.check(mt.lib().mt_gemm(dtype, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
-                              R.data_ptr() if R is not None else None, ldr, M, N, K, epi, None))
+                              R.data_ptr() if R is not None else None, ldr, M, N, K, epi, layout, None))
 
 
 def acc_bound(a, b):
@@ -74,6 +74,54 @@ def test_gemm_bf16_small(M, N, K):
     cr = Cr.cpu().numpy().astype(np.float64)
     r = R.cpu().numpy().astype(np.float64)
     assert np.all(np.abs(cr - (r + ref)) <= bound + np.abs(r + ref) * 2.0 ** -23 + 1e-30)
+
+
+@pytest.mark.parametrize("layout", [mt.GEMM_A_KMAJOR, mt.GEMM_B_KMAJOR, mt.GEMM_A_KMAJOR | mt.GEMM_B_KMAJOR])
+@pytest.mark.parametrize("M,N,K,pad", [(300, 520, 192, 0), (513, 257, 1024, 8), (256, 256, 640, 0), (70, 1000, 256, 24)])
+def test_gemm_bf16_kmajor_operands(layout, M, N, K, pad):
+    """K-major operands ([K x M], [K x N], row stride a multiple of 8 >= M
+    (N), padding filled with NaN) give the same contraction; ragged M, N leave
+    the columns a last tile reads past M (N) out of the stored result."""
+    rng = np.random.default_rng(M + 3 * N + K + layout)
+    a32 = rng.standard_normal((M, K)).astype(np.float32)
+    b32 = rng.standard_normal((N, K)).astype(np.float32)
+    up8 = lambda x: (x + 7) // 8 * 8
+    if layout & mt.GEMM_A_KMAJOR:
+        lda = up8(M) + pad
+        buf = np.full((K, lda), np.nan, np.float32)
+        buf[:, :M] = a32.T
+        A, aw = bf16_tensor(buf)
+        a = aw[:, :M].T
+    else:
+        A, a = bf16_tensor(a32)
+        lda = K
+    if layout & mt.GEMM_B_KMAJOR:
+        ldb = up8(N) + pad
+        buf = np.full((K, ldb), np.nan, np.float32)
+        buf[:, :N] = b32.T
+        B, bw = bf16_tensor(buf)
+        b = bw[:, :N].T
+    else:
+        B, b = bf16_tensor(b32)
+        ldb = K
+    ref = a @ b.T
+    bound = acc_bound(a, b)
+    C = torch.full((M, N), np.nan, dtype=torch.float32, device=dev())
+    gemm(mt.MT_BF16, A, lda, B, ldb, C, N, M, N, K, mt.EPI_F32, layout=layout)
+    Cb = torch.empty((M, N), dtype=torch.int16, device=dev())
+    gemm(mt.MT_BF16, A, lda, B, ldb, Cb, N, M, N, K, mt.EPI_STORE, layout=layout)
+    torch.cuda.synchronize()
+    c = C.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(c - ref) <= bound + 1e-30)
+    assert np.array_equal(Cb.cpu().numpy().view(np.uint16), datagen.f32_to_bf16_bits(C.cpu().numpy()))
+
+
+def test_gemm_kmajor_rejects_unsupported_shapes():
+    A = torch.zeros((256, 256), dtype=torch.int16, device=dev())
+    C = torch.zeros((256, 256), dtype=torch.float32, device=dev())
+    rc = mt.lib().mt_gemm(mt.MT_BF16, A.data_ptr(), 256, A.data_ptr(), 256, C.data_ptr(), 256, None, 0, 256, 256, 128,
+                          mt.EPI_F32, mt.GEMM_A_KMAJOR, None)
+    assert rc != 0
 
 
 def test_gemm_bf16_strided_operands():
