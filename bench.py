@@ -139,7 +139,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="14b", choices=list(datagen.PRESETS))
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (same per-layer shape)")
-    ap.add_argument("--mode", default="streamed", choices=["streamed", "serialized", "resident"])
+    ap.add_argument("--mode", default="streamed", choices=["streamed", "serialized", "resident", "single_slot"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-kernel-timing", action="store_true")

@@ -19,8 +19,9 @@ LIB_PATH = os.path.join(PKG_DIR, "libmt.so")
 MT_OK = 0
 MT_E_INVALID, MT_E_SIZE, MT_E_ALIGN, MT_E_NOT_BOUND, MT_E_HIP, MT_E_NONFINITE, MT_E_OOM, MT_E_STATE = range(-1, -9, -1)
 MT_F32, MT_BF16 = 0, 1
-MT_STREAMED, MT_SERIALIZED, MT_RESIDENT = 0, 1, 2
-MODES = {"streamed": MT_STREAMED, "serialized": MT_SERIALIZED, "resident": MT_RESIDENT}
+MT_STREAMED, MT_SERIALIZED, MT_RESIDENT, MT_SINGLE_SLOT = 0, 1, 2, 3
+MODES = {"streamed": MT_STREAMED, "serialized": MT_SERIALIZED, "resident": MT_RESIDENT,
+         "single_slot": MT_SINGLE_SLOT}
 MT_BLOCK_EMBED, MT_BLOCK_LAYER, MT_BLOCK_HEAD = 0, 1, 2
 MT_FLAG_TIME_KERNELS, MT_FLAG_POISON = 1, 2
 EPI_STORE, EPI_F32, EPI_ADD_F32 = 0, 1, 2
@@ -81,6 +82,10 @@ _SIGS = {
     "mt_init_store_header": (ctypes.c_int, [ctypes.POINTER(MtConfig), ctypes.c_void_p, ctypes.c_size_t,
                                             ctypes.c_void_p, ctypes.c_size_t]),
     "mt_store_step": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)]),
+    "mt_store_save": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_char_p]),
+    "mt_store_load": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_char_p]),
     "mt_create_model": (ctypes.c_int, [ctypes.POINTER(MtConfig), ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]),
     "mt_bind_host_store": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
@@ -232,6 +237,14 @@ class HostStore:
         t = ctypes.c_int64()
         check(lib().mt_store_step(self.ptr, ctypes.byref(t)))
         return t.value
+
+    def save(self, path: str):
+        """Checkpoint: header, every block's W, and [m | v] (mt_store_save)."""
+        check(lib().mt_store_save(self.ptr, self.nbytes, self.opt_ptr, self.opt_nbytes, str(path).encode()))
+
+    def load(self, path: str):
+        """Resume from a checkpoint of a store with the same layout (mt_store_load)."""
+        check(lib().mt_store_load(self.ptr, self.nbytes, self.opt_ptr, self.opt_nbytes, str(path).encode()))
 
     def free(self):
         if self.ptr:

@@ -1,5 +1,7 @@
 // extern "C" entry points of include/mt.h: argument checks and translation
 // of internal errors into MT_E_* codes; no exception crosses the ABI.
+#include <cstdio>
+#include <cstring>
 #include <sched.h>
 #include <sys/mman.h>
 
@@ -181,6 +183,71 @@ int mt_store_step(const void* host_base, int64_t* t) {
     const StoreHeader* h = (const StoreHeader*)host_base;
     if (h->magic != kStoreMagic) throw ApiError{MT_E_INVALID, "bad store magic"};
     *t = h->step;
+    return MT_OK;
+  });
+}
+
+// Checkpoint file: an 8-byte tag, the store's header page, every block's W
+// region in block order, then the optimizer part [m | v].  Gradients are
+// overwritten by every step and are not part of the state.
+static const char kCkptTag[8] = {'M', 'T', 'C', 'K', 'P', 'T', '0', '1'};
+
+static const StoreHeader* checked_header(const void* dma_base, size_t dma_bytes, size_t opt_bytes,
+                                         std::vector<mt_block_desc>* blocks, uint64_t* opt_total) {
+  if (!dma_base) throw ApiError{MT_E_INVALID, "null argument"};
+  const StoreHeader* h = (const StoreHeader*)dma_base;
+  if (h->magic != kStoreMagic || h->version != kStoreVersion) throw ApiError{MT_E_INVALID, "bad store header"};
+  uint64_t total = 0;
+  *blocks = store_layout(h->cfg, &total, opt_total);
+  if (dma_bytes < total || opt_bytes < *opt_total) throw ApiError{MT_E_SIZE, "store parts smaller than the layout"};
+  return h;
+}
+
+static bool same_layout(const mt_config& a, const mt_config& b) {
+  return a.n_layers == b.n_layers && a.d_model == b.d_model && a.n_heads == b.n_heads &&
+         a.head_dim == b.head_dim && a.d_ff == b.d_ff && a.vocab == b.vocab && a.store_dtype == b.store_dtype;
+}
+
+int mt_store_save(const void* dma_base, size_t dma_bytes, const void* opt_base, size_t opt_bytes, const char* path) {
+  return guarded([&] {
+    if (!opt_base || !path) throw ApiError{MT_E_INVALID, "null argument"};
+    std::vector<mt_block_desc> blocks;
+    uint64_t opt = 0;
+    checked_header(dma_base, dma_bytes, opt_bytes, &blocks, &opt);
+    FILE* f = fopen(path, "wb");
+    if (!f) throw ApiError{MT_E_INVALID, std::string("cannot open ") + path};
+    bool ok = fwrite(kCkptTag, 1, 8, f) == 8 && fwrite(dma_base, 1, kHeaderBytes, f) == kHeaderBytes;
+    for (const auto& b : blocks)
+      ok = ok && fwrite((const uint8_t*)dma_base + b.w_off, 1, b.w_bytes, f) == b.w_bytes;
+    ok = ok && fwrite(opt_base, 1, opt, f) == opt;
+    ok = (fclose(f) == 0) && ok;
+    if (!ok) throw ApiError{MT_E_INVALID, std::string("short write to ") + path};
+    return MT_OK;
+  });
+}
+
+int mt_store_load(void* dma_base, size_t dma_bytes, void* opt_base, size_t opt_bytes, const char* path) {
+  return guarded([&] {
+    if (!opt_base || !path) throw ApiError{MT_E_INVALID, "null argument"};
+    std::vector<mt_block_desc> blocks;
+    uint64_t opt = 0;
+    StoreHeader* h = (StoreHeader*)checked_header(dma_base, dma_bytes, opt_bytes, &blocks, &opt);
+    FILE* f = fopen(path, "rb");
+    if (!f) throw ApiError{MT_E_INVALID, std::string("cannot open ") + path};
+    char tag[8];
+    std::vector<uint8_t> page(kHeaderBytes);
+    bool ok = fread(tag, 1, 8, f) == 8 && memcmp(tag, kCkptTag, 8) == 0 &&
+              fread(page.data(), 1, kHeaderBytes, f) == kHeaderBytes;
+    const StoreHeader* fh = (const StoreHeader*)page.data();
+    if (!ok || fh->magic != kStoreMagic || fh->version != kStoreVersion || !same_layout(fh->cfg, h->cfg)) {
+      fclose(f);
+      throw ApiError{MT_E_INVALID, "checkpoint does not match the store's configuration"};
+    }
+    for (const auto& b : blocks) ok = ok && fread((uint8_t*)dma_base + b.w_off, 1, b.w_bytes, f) == b.w_bytes;
+    ok = ok && fread(opt_base, 1, opt, f) == opt;
+    fclose(f);
+    if (!ok) throw ApiError{MT_E_INVALID, std::string("short checkpoint ") + path};
+    h->step = fh->step;
     return MT_OK;
   });
 }

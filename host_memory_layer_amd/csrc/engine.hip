@@ -195,7 +195,9 @@ struct Model {
   template <typename T>
   uint64_t carve_all(uint8_t* base) {
     Carver c{base};
-    for (int s = 0; s < 2; ++s) wslot[s] = c.take<uint8_t>(slot_bytes);
+    // MT_SINGLE_SLOT: one weight slot (the double-buffering ablation)
+    wslot[1] = nullptr;
+    for (int s = 0; s < (cfg.mode == MT_SINGLE_SLOT ? 1 : 2); ++s) wslot[s] = c.take<uint8_t>(slot_bytes);
     for (int s = 0; s < 2; ++s) gslot[s] = c.take<uint8_t>(slot_bytes);
     wt = kmajor && kmajor_head ? nullptr : c.take<uint8_t>(slot_bytes);
     if (cfg.mode == MT_RESIDENT) {
@@ -566,17 +568,23 @@ void Model::adam_worker(int64_t t, double* adam_total, double* adam_tail, std::a
   }
 }
 
-// Streamed (and serialized) schedule.  Uses: u = j for the forward of block
-// j (0 embed, 1..L layers, L+1 head, whose use also runs the head backward);
-// u = L+2+i for the backward of block L-i (i = 0..L-1: layers), and
-// u = 2L+2 for the embedding backward.  Block j always uses weight slot j%2,
-// and consecutive backward uses alternate between the two gradient slots.
-// A slot's next prefetch starts when the compute of its last use has ended;
-// a block's compute is enqueued once its prefetch is done.  The serialized
-// schedule lets nothing overlap: every copy starts after all compute
-// enqueued so far and ends before more work is enqueued.
+// Streamed (and serialized, single-slot) schedule.  Uses: u = j for the
+// forward of block j (0 embed, 1..L layers, L+1 head, whose use also runs the
+// head backward); u = L+2+i for the backward of block L-i (i = 0..L-1:
+// layers), and u = 2L+2 for the embedding backward.  Block j uses weight
+// slot j%2, and consecutive backward uses alternate between the two
+// gradient slots.  A slot's next prefetch starts when the compute of its
+// last use has ended; a block's compute is enqueued once its prefetch is
+// done.  The serialized schedule lets nothing overlap: every copy starts
+// after all compute enqueued so far and ends before more work is enqueued.
+// The single-slot schedule keeps every block in slot 0, so each prefetch
+// waits for the previous block's compute (weights are not double-buffered;
+// gradient offloads still overlap), and block L is fetched again for its
+// backward because the head has replaced it.
 template <typename T>
 void Model::step_streamed(bool serialize) {
+  const bool single = cfg.mode == MT_SINGLE_SLOT;
+  auto slot_of = [&](int j) { return single ? 0 : j % 2; };
   const bool poison = cfg.flags & MT_FLAG_POISON;
   const uint32_t nan_word = E == 2 ? 0x7FC07FC0u : 0x7FC00000u;
   std::vector<int> slot_last_use(2, -1);  // use that last bound each weight slot
@@ -586,7 +594,7 @@ void Model::step_streamed(bool serialize) {
   int last_out = -1;
 
   auto fetch = [&](int u, int j) {
-    const int s = j % 2;
+    const int s = slot_of(j);
     hipEvent_t ready = slot_last_use[s] >= 0 ? ev_c_e[slot_last_use[s]] : nullptr;
     if (poison) {
       // NaN-fill the slot on the compute stream, after its last use.
@@ -607,7 +615,7 @@ void Model::step_streamed(bool serialize) {
   };
   auto end = [&](int u, int j) {
     MT_HIP(hipEventRecord(ev_c_e[u], sc));
-    slot_last_use[j % 2] = u;
+    slot_last_use[slot_of(j)] = u;
   };
   // Grad slot for a backward use: the offload that last read it has finished.
   auto grad_slot = [&]() -> int {
@@ -631,16 +639,17 @@ void Model::step_streamed(bool serialize) {
   // ---- forward sweep (blocks 0 .. L+1)
   fetch(0, 0);
   for (int j = 0; j <= L + 1; ++j) {
-    if (j + 1 <= L + 1) fetch(j + 1, j + 1);
+    if (j > 0 && single) fetch(j, j);
+    if (j + 1 <= L + 1 && !single) fetch(j + 1, j + 1);
     if (j <= L) {
       begin(j);
-      compute_block_fwd<T>(j, wslot[j % 2]);
+      compute_block_fwd<T>(j, wslot[slot_of(j)]);
       end(j, j);
     } else {
       // head: forward, loss, backward; weights stay bound for both
       const int g = grad_slot();
       begin(j);
-      head_fwd_bwd<T>(blocks[j], wslot[j % 2], gslot[g], ws.dxA);
+      head_fwd_bwd<T>(blocks[j], wslot[slot_of(j)], gslot[g], ws.dxA);
       end(j, j);
       offload(j, j, g);
     }
@@ -653,10 +662,13 @@ void Model::step_streamed(bool serialize) {
     const int u = L + 2 + i;
     // block L is still in its slot from the forward; the others are fetched
     // again (the prefetch of use u+1 is issued before use u computes)
-    if (j - 1 >= 1) fetch(u + 1, j - 1);
+    if (single)
+      fetch(u, j);
+    else if (j - 1 >= 1)
+      fetch(u + 1, j - 1);
     const int g = grad_slot();
     begin(u);
-    compute_layer_bwd<T>(j, wslot[j % 2], gslot[g], dx_in, dx_out);
+    compute_layer_bwd<T>(j, wslot[slot_of(j)], gslot[g], dx_in, dx_out);
     end(u, j);
     offload(u, j, g);
     std::swap(dx_in, dx_out);
@@ -765,7 +777,7 @@ int Model::train_step(const int32_t* tokens) {
     if (!streamed) {
       bf ? step_resident<uint16_t>() : step_resident<float>();
     } else {
-      const bool ser = cfg.mode == MT_SERIALIZED;
+      const bool ser = cfg.mode == MT_SERIALIZED;  // MT_SINGLE_SLOT is read inside
       bf ? step_streamed<uint16_t>(ser) : step_streamed<float>(ser);
     }
   } catch (const HipError& e) {

@@ -15,7 +15,7 @@ int validate_config(const mt_config& c, std::string* why) {
   if (c.d_model % 4 || c.d_ff % 4) return bad("d_model and d_ff must be multiples of 4");
   if (c.d_model > 16384) return bad("d_model > 16384");
   if (c.store_dtype != MT_F32 && c.store_dtype != MT_BF16) return bad("store_dtype");
-  if (c.mode < MT_STREAMED || c.mode > MT_RESIDENT) return bad("mode");
+  if (c.mode < MT_STREAMED || c.mode > MT_SINGLE_SLOT) return bad("mode");
   if (c.store_dtype == MT_BF16) {
     // MFMA tiles move 8 bf16 (16 bytes) per lane along every contraction dim.
     if (c.d_model % 64 || c.d_ff % 64 || c.head_dim != 128)

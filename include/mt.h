@@ -46,6 +46,8 @@ extern "C" {
 #define MT_STREAMED 0        /* two weight slots; prefetch, compute and offload overlap (the method) */
 #define MT_SERIALIZED 1      /* the streamed schedule on the compute stream only */
 #define MT_RESIDENT 2        /* every block's W on the device, no recompute */
+#define MT_SINGLE_SLOT 3     /* one weight slot: each prefetch waits for the previous block's compute
+                                (the method without double buffering; offloads still overlap) */
 
 #define MT_BLOCK_EMBED 0
 #define MT_BLOCK_LAYER 1
@@ -64,7 +66,7 @@ typedef struct mt_config {
   double rms_eps;        /* added inside the square root (used as float32 on the device) */
   double rope_theta;     /* rotation frequency base */
   double lr, beta1, beta2, adam_eps;  /* Adam: rounded to float32 as the host update uses them */
-  int32_t mode;          /* MT_STREAMED, MT_SERIALIZED or MT_RESIDENT */
+  int32_t mode;          /* MT_STREAMED, MT_SERIALIZED, MT_RESIDENT or MT_SINGLE_SLOT */
   int32_t host_threads;  /* Adam worker threads; 0 = every core in the affinity mask */
   int32_t flags;         /* MT_FLAG_* bits */
 } mt_config;
@@ -156,6 +158,19 @@ void mt_free_host_opt(void* p, size_t bytes);
 int mt_init_store_header(const mt_config* cfg, void* dma_base, size_t dma_bytes, void* opt_base, size_t opt_bytes);
 /* Adam step counter t stored in the header (number of completed steps). */
 int mt_store_step(const void* dma_base, int64_t* t);
+
+/* Checkpoint and resume (steps 1..k, save, resume: the resumed run continues
+ * bit for bit).  mt_store_save writes the resumable state of a host store to
+ * the file `path`: the header page (configuration, completed Adam steps),
+ * every block's W region and the optimizer part [m | v]; gradients are
+ * rewritten by every step and are not saved.  mt_store_load reads such a
+ * file into a store initialised by mt_init_store_header with the same layout
+ * (layers, widths, vocabulary, store dtype): W, m, v and the step count.
+ * The caller owns the buffers; no model may be running a step on the store.
+ * Errors: MT_E_INVALID (bad header, layout mismatch, I/O failure or short
+ * file), MT_E_SIZE (parts smaller than the layout). */
+int mt_store_save(const void* dma_base, size_t dma_bytes, const void* opt_base, size_t opt_bytes, const char* path);
+int mt_store_load(void* dma_base, size_t dma_bytes, void* opt_base, size_t opt_bytes, const char* path);
 
 /* ------------------------------------------------------------- model ----- */
 /* Create a model.  dev_arena: device memory of at least mt_device_bytes(cfg),

@@ -16,8 +16,8 @@ that hold at any size.
   - the loss is the mean of the per-position losses;
   - the host Adam relation, bit for bit, on a slice of every tensor;
   - embedding-gradient rows of tokens that do not occur are exactly zero.
-* The streamed, serialized and resident schedules agree bit for bit at the
-  14B and 120B per-layer shapes with 2 layers.
+* The streamed, serialized, resident and single-slot schedules agree bit for
+  bit at the 14B and 120B per-layer shapes with 2 layers.
 """
 import gc
 from concurrent.futures import ThreadPoolExecutor
@@ -233,11 +233,11 @@ def test_fullsize_sampled_outputs_and_properties(shape):
 @pytest.mark.parametrize("shape", [P14.replace(n_layers=2), P120_L2], ids=["14b-2layers", "120b-2layers"])
 def test_fullsize_schedules_bitwise_equal(shape):
     need_gpu()
-    print(f"{shape.name} with {shape.n_layers} layers: streamed vs serialized vs resident", flush=True)
+    print(f"{shape.name} with {shape.n_layers} layers: streamed vs serialized vs resident vs single slot", flush=True)
     ref = Run(shape, "streamed")
     try:
         ref.drop_model()
-        for mode in ("serialized", "resident"):
+        for mode in ("serialized", "resident", "single_slot"):
             r = Run(shape, mode)
             try:
                 assert r.loss == ref.loss, mode

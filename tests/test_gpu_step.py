@@ -11,7 +11,7 @@ import pytest
 import datagen
 import host_memory_layer_amd as mt
 from oracle import Oracle
-from tests.harness import assert_parity, make_store, read_all
+from tests.harness import W_RTOL, assert_parity, frob_rel, make_store, read_all
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -60,7 +60,8 @@ def test_step_matches_oracle(shape):
 def test_schedules_bitwise_equal(shape):
     need_gpu()
     ref = run_step(shape, "streamed")
-    for mode, flags in (("serialized", 0), ("resident", 0), ("streamed", mt.MT_FLAG_POISON)):
+    for mode, flags in (("serialized", 0), ("resident", 0), ("single_slot", 0), ("streamed", mt.MT_FLAG_POISON),
+                        ("single_slot", mt.MT_FLAG_POISON)):
         r = run_step(shape, mode, flags)
         assert r["loss"] == ref["loss"], mode
         for key in ("g", "w", "m", "v"):
@@ -84,6 +85,43 @@ def test_repeated_step_is_deterministic_and_t_advances():
     l2, g2, P2, _ = o.step(P1, tok, t=2, moments=M1)
     assert abs(a["losses"][1] - l2) / abs(l2) < 1e-2
     assert a["losses"][1] < a["losses"][0]
+    # weights after the second Adam step (t = 2 bias corrections)
+    for k in a["w"]:
+        assert frob_rel(a["w"][k], P2[k]) <= W_RTOL, k
+
+
+@pytest.mark.parametrize("shape,resume_mode", [(datagen.PRESETS["tiny"], "streamed"), (SMALL_BF16, "single_slot")],
+                         ids=["tiny-f32", "small-bf16-single-slot"])
+def test_checkpoint_resume_continues_bit_for_bit(shape, resume_mode, tmp_path):
+    """Steps 1-2, checkpoint, steps 3-4 on one store; a fresh store resumed
+    from the checkpoint (in the streamed or the single-slot schedule) gives
+    the same losses and the same W, m, v bit for bit."""
+    need_gpu()
+    tok = datagen.tokens(shape)
+    cfg, store = make_store(shape)
+    model = mt.Model(cfg, store, "cuda:0")
+    first = [model.step(tok) for _ in range(2)]
+    path = tmp_path / "ckpt.bin"
+    store.save(path)
+    cont = [model.step(tok) for _ in range(2)]
+    ref = {k: read_all(store, k) for k in "wmv"}
+    assert store.step_count() == 4
+    model.close()
+    store.free()
+    cfg2, store2 = make_store(shape, resume_mode)
+    store2.load(path)
+    assert store2.step_count() == 2
+    model2 = mt.Model(cfg2, store2, "cuda:0")
+    again = [model2.step(tok) for _ in range(2)]
+    got = {k: read_all(store2, k) for k in "wmv"}
+    assert store2.step_count() == 4
+    model2.close()
+    store2.free()
+    print(f"losses {first} | {cont} | resumed {again}", flush=True)
+    assert again == cont
+    for k in "wmv":
+        for name in ref[k]:
+            assert np.array_equal(got[k][name], ref[k][name]), (k, name)
 
 
 def test_nonfinite_loss_leaves_store_untouched():

@@ -163,3 +163,60 @@ def test_api_errors_without_device():
     stream = 1  # never dereferenced: every call below fails its checks first
     assert L.mt_create_model(ctypes.byref(cfg), 0x1001, 1 << 30, stream, ctypes.byref(h)) == mt.MT_E_ALIGN
     assert L.mt_create_model(ctypes.byref(cfg), 0x1000, 16, stream, ctypes.byref(h)) == mt.MT_E_SIZE
+
+
+def _aligned(nbytes):
+    """A 4 KiB-aligned host buffer (numpy-owned) and its address."""
+    raw = np.zeros(nbytes + 4096, np.uint8)
+    off = (-raw.ctypes.data) % 4096
+    buf = raw[off:off + nbytes]
+    return raw, buf, buf.ctypes.data
+
+
+def _plain_store(cfg):
+    """Store parts in ordinary host memory, header initialised (no GPU)."""
+    n, no = mt.host_store_bytes(cfg), mt.host_opt_bytes(cfg)
+    keep_d, dma, pd = _aligned(n)
+    keep_o, opt, po = _aligned(no)
+    mt.check(mt.lib().mt_init_store_header(ctypes.byref(cfg), pd, n, po, no))
+    return (keep_d, keep_o), dma, opt, pd, po, n, no
+
+
+def test_store_checkpoint_round_trip(tmp_path):
+    """mt_store_save / mt_store_load: W regions, [m | v] and the step count
+    come back bit for bit into a fresh store; gradients are not part of the
+    checkpoint; a store of another layout or a short file is rejected."""
+    shape = datagen.PRESETS["tiny"]
+    cfg = mt.make_config(shape)
+    keep_a, dma_a, opt_a, pa, oa, n, no = _plain_store(cfg)
+    rng = np.random.default_rng(5)
+    dma_a[4096:] = rng.integers(0, 256, n - 4096, dtype=np.uint8)
+    opt_a[:] = rng.integers(0, 256, no, dtype=np.uint8)
+    # completed Adam steps: the int64 after magic, version, n_blocks and the config
+    step_off = 16 + ctypes.sizeof(mt.MtConfig)
+    step_off += (-step_off) % 8
+    dma_a[step_off:step_off + 8] = np.frombuffer(np.int64(7).tobytes(), np.uint8)
+    t = ctypes.c_int64()
+    mt.check(mt.lib().mt_store_step(pa, ctypes.byref(t)))
+    assert t.value == 7
+    path = str(tmp_path / "ckpt.bin")
+    mt.check(mt.lib().mt_store_save(pa, n, oa, no, path.encode()))
+    blocks = mt.block_infos(cfg)
+    assert os.path.getsize(path) == 8 + 4096 + sum(b.w_bytes for b in blocks) + no
+
+    keep_b, dma_b, opt_b, pb, ob, _, _ = _plain_store(cfg)
+    mt.check(mt.lib().mt_store_load(pb, n, ob, no, path.encode()))
+    mt.check(mt.lib().mt_store_step(pb, ctypes.byref(t)))
+    assert t.value == 7
+    for b in blocks:
+        assert np.array_equal(dma_b[b.w_off:b.w_off + b.w_bytes], dma_a[b.w_off:b.w_off + b.w_bytes])
+        assert not dma_b[b.g_off:b.g_off + b.w_bytes].any()
+    assert np.array_equal(opt_b, opt_a)
+
+    other = mt.make_config(shape.replace(d_ff=shape.d_ff * 2))
+    keep_c, _, _, pc, oc, nc, noc = _plain_store(other)
+    assert mt.lib().mt_store_load(pc, nc, oc, noc, path.encode()) == mt.MT_E_INVALID
+    with open(path, "r+b") as f:
+        f.truncate(os.path.getsize(path) - 100)
+    assert mt.lib().mt_store_load(pb, n, ob, no, path.encode()) == mt.MT_E_INVALID
+    assert mt.lib().mt_store_load(pb, n, ob, no, str(tmp_path / "missing.bin").encode()) == mt.MT_E_INVALID
