@@ -143,6 +143,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--duplex-link", action="store_true",
+                    help="let prefetches and offloads use the host link at the same time")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain 1 GiB device copy kernel first (the reference for HBM byte counters)")
     args = ap.parse_args()
@@ -159,6 +161,8 @@ def main():
         shape = shape.replace(n_layers=args.layers)
     dev = torch.device("cuda:0")
     flags = 0 if args.no_kernel_timing else mt.MT_FLAG_TIME_KERNELS
+    if args.duplex_link:
+        flags |= mt.MT_FLAG_DUPLEX_LINK
     cfg = mt.make_config(shape, mode=args.mode, flags=flags)
 
     t0 = time.perf_counter()

@@ -23,7 +23,7 @@ MT_STREAMED, MT_SERIALIZED, MT_RESIDENT, MT_SINGLE_SLOT = 0, 1, 2, 3
 MODES = {"streamed": MT_STREAMED, "serialized": MT_SERIALIZED, "resident": MT_RESIDENT,
          "single_slot": MT_SINGLE_SLOT}
 MT_BLOCK_EMBED, MT_BLOCK_LAYER, MT_BLOCK_HEAD = 0, 1, 2
-MT_FLAG_TIME_KERNELS, MT_FLAG_POISON = 1, 2
+MT_FLAG_TIME_KERNELS, MT_FLAG_POISON, MT_FLAG_DUPLEX_LINK = 1, 2, 4
 EPI_STORE, EPI_F32, EPI_ADD_F32 = 0, 1, 2
 GEMM_A_KMAJOR, GEMM_B_KMAJOR = 1, 2
 

@@ -91,6 +91,24 @@ void DmaEngines::copy(DmaDir dir, void* dst, const void* src, size_t bytes) {
                                  " failed (completion signal " + std::to_string(v) + ")"};
 }
 
+void DmaEngines::h2d_begin() {
+  std::lock_guard<std::mutex> g(link_mu_);
+  ++h2d_active_;
+}
+
+void DmaEngines::h2d_end() {
+  {
+    std::lock_guard<std::mutex> g(link_mu_);
+    --h2d_active_;
+  }
+  link_cv_.notify_all();
+}
+
+void DmaEngines::wait_no_h2d() {
+  std::unique_lock<std::mutex> lk(link_mu_);
+  link_cv_.wait(lk, [&] { return h2d_active_ == 0; });
+}
+
 // ----------------------------------------------------------- queue --
 void TransferQueue::start(std::vector<double>* job_ms, std::function<void(const Job&)> on_done) {
   stop();
@@ -144,10 +162,23 @@ void TransferQueue::run() {
     std::string err;
     try {
       if (job.ready) MT_HIP(hipEventSynchronize(job.ready));
+      const bool h2d = dir_ == DMA_H2D;
+      if (yield_) {
+        if (h2d)
+          dma_->h2d_begin();
+        else
+          dma_->wait_no_h2d();
+      }
       auto t0 = std::chrono::steady_clock::now();
-      dma_->copy(dir_, job.dst, job.src, job.bytes);
+      try {
+        dma_->copy(dir_, job.dst, job.src, job.bytes);
+      } catch (...) {
+        if (yield_ && h2d) dma_->h2d_end();
+        throw;
+      }
       if (job_ms_ && job.u >= 0 && (size_t)job.u < job_ms_->size())
         (*job_ms_)[job.u] = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+      if (yield_ && h2d) dma_->h2d_end();
       // Before the job counts as done: the enqueueing thread may close
       // what on_done feeds once the last job is done.
       if (on_done_) on_done_(job);

@@ -47,8 +47,17 @@ class DmaEngines {
   // direction must not.  Throws ApiError on failure.
   void copy(DmaDir dir, void* dst, const void* src, size_t bytes);
   uint32_t engine_id(DmaDir dir) const { return eng_[dir]; }
+  // Host-to-device jobs whose ready event has fired and whose copy has not
+  // finished; device-to-host copies wait for none to be left (see
+  // TransferQueue).
+  void h2d_begin();
+  void h2d_end();
+  void wait_no_h2d();
 
  private:
+  std::mutex link_mu_;
+  std::condition_variable link_cv_;
+  int h2d_active_ = 0;
   hsa_agent_t gpu_{}, cpu_{};
   hsa_signal_t sig_[2]{};
   uint32_t eng_[2]{};
@@ -68,7 +77,13 @@ class TransferQueue {
     const void* src;
     size_t bytes;
   };
-  TransferQueue(DmaEngines* dma, DmaDir dir) : dma_(dma), dir_(dir) {}
+  // yield_link: a device-to-host copy starts only when no host-to-device
+  // copy is ready or running, so offloads take the link between prefetches
+  // instead of halving their rate (the two directions share one host link:
+  // both at once move about as many bytes per second as one alone).
+  // Prefetches never wait for offloads.
+  TransferQueue(DmaEngines* dma, DmaDir dir, bool yield_link = true)
+      : dma_(dma), dir_(dir), yield_(yield_link) {}
   ~TransferQueue() { stop(); }
 
   // Starts the worker for one step; job_ms(u) is filled with each job's
@@ -83,6 +98,7 @@ class TransferQueue {
   void run();
   DmaEngines* dma_;
   DmaDir dir_;
+  bool yield_;
   std::mutex mu_;
   std::condition_variable cv_;
   std::vector<Job> jobs_;

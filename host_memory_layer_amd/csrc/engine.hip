@@ -759,8 +759,16 @@ int Model::train_step(const int32_t* tokens) {
   const bool streamed = cfg.mode != MT_RESIDENT;
   if (streamed && !dma) {
     dma.reset(new DmaEngines(gslot[0], host));
-    xq_in.reset(new TransferQueue(dma.get(), DMA_H2D));
-    xq_out.reset(new TransferQueue(dma.get(), DMA_D2H));
+    // Offloads yield the link to prefetches when a layer's backward is
+    // compute-bound against the link (its flops per transferred weight and
+    // gradient byte well above ~1 PFLOP/s over ~50 GB/s): the transfers are
+    // hidden either way and each then runs at the full one-way rate.  When
+    // the link is the bottleneck, both directions share it.
+    const double layer_bytes = 2.0 * (double)blocks[1].w_bytes;
+    const double bwd_flops = 3.0 * (2.0 * M * (4.0 * d * d + 3.0 * d * F)) + 3.5 * attn_fwd_flops();
+    const bool yield = !(cfg.flags & MT_FLAG_DUPLEX_LINK) && bwd_flops / layer_bytes > 30000.0;
+    xq_in.reset(new TransferQueue(dma.get(), DMA_H2D, yield));
+    xq_out.reset(new TransferQueue(dma.get(), DMA_D2H, yield));
   }
   h2d_host_ms.assign(n_uses, 0.0);
   d2h_host_ms.assign(n_uses, 0.0);

@@ -73,6 +73,10 @@ typedef struct mt_config {
 
 #define MT_FLAG_TIME_KERNELS 1  /* bracket every GEMM and attention launch with events */
 #define MT_FLAG_POISON 2        /* fill a weight slot with NaN before each prefetch */
+#define MT_FLAG_DUPLEX_LINK 4   /* let an offload start while a prefetch is ready or running.  Default:
+                                   offloads wait for prefetches (which never wait for offloads) when a
+                                   layer's backward does more than 30k flops per transferred byte, and
+                                   share the link otherwise */
 
 /* One tensor inside a block region: element offset from the region start,
  * row-major [rows x cols]. */
