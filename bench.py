@@ -139,6 +139,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="14b", choices=list(datagen.PRESETS))
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (same per-layer shape)")
+    ap.add_argument("--batch", type=int, default=0, help="override the batch size")
+    ap.add_argument("--seq-len", type=int, default=0, help="override the sequence length (long context)")
     ap.add_argument("--mode", default="streamed", choices=["streamed", "serialized", "resident", "single_slot"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
@@ -159,6 +161,10 @@ def main():
     shape = datagen.PRESETS[args.config]
     if args.layers:
         shape = shape.replace(n_layers=args.layers)
+    if args.batch:
+        shape = shape.replace(batch=args.batch)
+    if args.seq_len:
+        shape = shape.replace(seq_len=args.seq_len)
     dev = torch.device("cuda:0")
     flags = 0 if args.no_kernel_timing else mt.MT_FLAG_TIME_KERNELS
     if args.duplex_link:

@@ -16,13 +16,15 @@ bit for bit.
 
 Pins (tests marked "not gpu"): finite differences in float64 on the tiny
 shape, Adam's closed form at t = 1, streamed == resident, brute-force loops
-for attention and cross-entropy on tiny inputs, closed forms for RoPE,
+for attention and cross-entropy on tiny inputs, single rows and key tails
+of attention against the full matrices, closed forms for RoPE,
 RMSNorm, SiLU and the uniform-logit loss, and causality of the forward.
 Parity unpinned: the architectural readings (untied head, gains = 1, eps,
 RoPE base and half-split pairing) are not fixed by the pages; they are
 checked for internal consistency only.
 """
 from .model import (  # noqa: F401
-    Oracle, adam_update, attention_bwd, attention_fwd, cross_entropy,
+    Oracle, adam_update, attention_bwd, attention_fwd, attention_key_tail, attention_rows,
+    cross_entropy,
     rmsnorm_bwd, rmsnorm_fwd, rope_apply, rope_tables, silu, silu_grad,
 )

@@ -100,6 +100,50 @@ def attention_bwd(do, q, k, v, p):
     return dq, dk, dv
 
 
+def attention_rows(q, k, v, do, rows):
+    """Rows of attention_fwd / attention_bwd for one head, one query at a time.
+
+    q, k, v, do: [T, hd]; returns (o, dq) for the query rows ``rows``.  Query
+    i sees keys 0..i only, so its output and its query gradient need nothing
+    but its own score row; this evaluates single rows of sequences too long
+    for the T x T matrices.
+    """
+    hd = q.shape[-1]
+    scale = q.dtype.type(1.0 / np.sqrt(hd))
+    o = np.empty((len(rows), hd), q.dtype)
+    dq = np.empty((len(rows), hd), q.dtype)
+    for n, i in enumerate(rows):
+        s = (k[:i + 1] @ q[i]) * scale
+        e = np.exp(s - np.max(s))
+        p = e / np.sum(e)
+        o[n] = p @ v[:i + 1]
+        dp = v[:i + 1] @ do[i]
+        ds = p * (dp - np.sum(dp * p))
+        dq[n] = (ds @ k[:i + 1]) * scale
+    return o, dq
+
+
+def attention_key_tail(q, k, v, do, n):
+    """dk, dv of the last n keys of one head ([T, hd] operands).
+
+    Key j is seen only by queries i >= j, so the last n keys take gradient
+    from the last n queries alone: their full score rows (n x T) suffice.
+    """
+    T, hd = q.shape
+    scale = q.dtype.type(1.0 / np.sqrt(hd))
+    qi = np.arange(T - n, T)
+    s = (q[T - n:] @ k.T) * scale
+    s = np.where(np.arange(T)[None, :] > qi[:, None], -np.inf, s)
+    s = s - np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s)
+    p = e / np.sum(e, axis=-1, keepdims=True)
+    dp = do[T - n:] @ v.T
+    ds = p * (dp - np.sum(dp * p, axis=-1, keepdims=True))
+    dv = p[:, T - n:].T @ do[T - n:]
+    dk = (ds[:, T - n:].T @ q[T - n:]) * scale
+    return dk, dv
+
+
 # ----------------------------------------------------------------- SwiGLU --
 def silu(z):
     return z / (1 + np.exp(-z))

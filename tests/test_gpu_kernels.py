@@ -12,7 +12,7 @@ import pytest
 
 import datagen
 import host_memory_layer_amd as mt
-from oracle import attention_bwd, attention_fwd, rope_apply, rope_tables
+from oracle import attention_bwd, attention_fwd, attention_key_tail, attention_rows, rope_apply, rope_tables
 
 pytestmark = pytest.mark.gpu
 
@@ -270,3 +270,98 @@ def test_attention_bf16_14b_head_sampled():
     close(heads(out["dqkvT"][:128].T), ref["dq"], 0.999, 3e-2)
     close(heads(out["dqkvT"][128:256].T), ref["dk"], 0.999, 3e-2)
     close(heads(out["dqkvT"][256:].T), ref["dv"], 0.999, 3e-2)
+
+
+# Long context: one layer of the 7B shape (32 heads of 128) over a single
+# 65536-token sequence, so every offset and stride is the real one.  Heads 0
+# and 31 (the first and the last column block) carry random data, the others
+# zeros; the oracle evaluates single query rows and the last keys exactly,
+# and two identities cover every key: sum_j dv_j = sum_i dO_i (each
+# probability row sums to 1) and sum_j dk_j = 0 (each dS row sums to 0).
+def test_attention_bf16_long_context_7b_layer():
+    B, T, H, hd = 1, 65536, 32, 128
+    d = H * hd
+    live = (0, 31)
+    print(f"attention long context T={T} H={H}", flush=True)
+    rng = np.random.default_rng(65536)
+    qkv = torch.zeros((T, 3 * d), dtype=torch.int16, device=dev())
+    dO = torch.zeros((T, d), dtype=torch.int16, device=dev())
+    x64, do64 = {}, {}
+    for h in live:
+        cols = [slice(j * d + h * hd, j * d + (h + 1) * hd) for j in range(3)]
+        for j, c in enumerate(cols):
+            t, x64[h, j] = bf16_tensor((rng.standard_normal((T, hd)) * 1.5).astype(np.float32))
+            qkv[:, c] = t
+        t, do64[h] = bf16_tensor(rng.standard_normal((T, hd)).astype(np.float32))
+        dO[:, h * hd:(h + 1) * hd] = t
+    cos = np.empty((T, hd // 2), np.float32)
+    sin = np.empty((T, hd // 2), np.float32)
+    mt.check(mt.lib().mt_rope_tables(T, hd, 10000.0, cos.ctypes.data, sin.ctypes.data))
+    cos_t, sin_t = torch.from_numpy(cos).to(dev()), torch.from_numpy(sin).to(dev())
+    ldT = int(mt.lib().mt_token_ld(T))
+    o = torch.empty((T, d), dtype=torch.int16, device=dev())
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev())
+    Dsum = torch.empty((H, T), dtype=torch.float32, device=dev())
+    dqkvT = torch.empty((3 * d, ldT), dtype=torch.int16, device=dev())
+    mt.check(mt.lib().mt_rope_qkv(mt.MT_BF16, qkv.data_ptr(), cos_t.data_ptr(), sin_t.data_ptr(), B, T, H, hd, None))
+    mt.check(mt.lib().mt_attention_fwd(mt.MT_BF16, qkv.data_ptr(), o.data_ptr(), lse.data_ptr(), B, T, H, hd, None))
+    mt.check(mt.lib().mt_attention_bwd(mt.MT_BF16, qkv.data_ptr(), o.data_ptr(), dO.data_ptr(), lse.data_ptr(),
+                                       Dsum.data_ptr(), dqkvT.data_ptr(), ldT, B, T, H, hd, None))
+    torch.cuda.synchronize()
+    # a zero head stays zero: nothing leaks across the column blocks
+    quiet = 15
+    assert not torch.any(o[:, quiet * hd:(quiet + 1) * hd]).item()
+    for j in range(3):
+        assert not torch.any(dqkvT[j * d + quiet * hd:j * d + (quiet + 1) * hd, :T]).item()
+    c64, s64 = rope_tables(T, hd, 10000.0, np.float64)
+    rows = [0, 1, 2, 63, 64, 127, 128, 4095, 4096, 16383, 16384, 32767, 32768, 49151, 65000, 65535]
+    rows += sorted(np.random.default_rng(1).integers(0, T, 16).tolist())
+    tail = 128
+    for h in live:
+        q = rope_apply(x64[h, 0], c64, s64)
+        k = rope_apply(x64[h, 1], c64, s64)
+        v = x64[h, 2]
+        ro, rdq = attention_rows(q, k, v, do64[h], rows)
+        tk, tv = attention_key_tail(q, k, v, do64[h], tail)
+        got_o = to_f32(o[:, h * hd:(h + 1) * hd])
+        g = [to_f32(dqkvT[j * d + h * hd:j * d + (h + 1) * hd, :T]).T for j in range(3)]
+        close(got_o[rows], ro, 0.9999, 2e-2)
+        close(g[0][rows], rdq, 0.999, 3e-2)
+        close(g[0][T - tail:], attention_rows(q, k, v, do64[h], range(T - tail, T))[1], 0.999, 3e-2)
+        close(g[1][T - tail:], tk, 0.999, 3e-2)
+        close(g[2][T - tail:], tv, 0.999, 3e-2)
+        dv_sum, do_sum = g[2].sum(0), do64[h].sum(0)
+        tol = 0.02 * (np.sqrt(np.sum(do64[h] ** 2)) + np.sqrt(np.sum(g[2] ** 2)))
+        assert np.linalg.norm(dv_sum - do_sum) <= tol, (np.linalg.norm(dv_sum - do_sum), tol)
+        assert np.linalg.norm(g[1].sum(0)) <= 0.02 * np.sqrt(np.sum(g[1] ** 2))
+
+
+def test_gemm_bf16_kmajor_long_context_sampled():
+    """Weight gradient of the 7B QKV projection over 65536 tokens: both
+    operands token-major ([K x M] and [K x N]), the first at the largest row
+    stride the 32-bit buffer offsets allow (K * lda * 2 < 2^31); one stride
+    past the limit is refused."""
+    K, M, N = 65536, 12288, 4096
+    print(f"gemm kmajor {M}x{N}x{K}", flush=True)
+    g = torch.Generator(device=dev()).manual_seed(K + M + N)
+    A = torch.randn((K, M), generator=g, device=dev(), dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
+    B = torch.randn((K, N), generator=g, device=dev(), dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev())
+    gemm(mt.MT_BF16, A, M, B, N, C, N, M, N, K, mt.EPI_F32, layout=mt.GEMM_A_KMAJOR | mt.GEMM_B_KMAJOR)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    ri = torch.from_numpy(rng.integers(0, M, 512)).to(dev())
+    ci = torch.from_numpy(rng.integers(0, N, 512)).to(dev())
+    a = to_f32(A[:, ri]).T
+    b = to_f32(B[:, ci]).T
+    got = C[ri, ci].cpu().numpy().astype(np.float64)
+    ref = np.einsum("ij,ij->i", a, b)
+    bound = K * 2.0 ** -24 * np.einsum("ij,ij->i", np.abs(a), np.abs(b))
+    assert np.all(np.abs(got - ref) <= bound)
+    assert np.sqrt(np.mean((got - ref) ** 2)) < 1e-3 * np.sqrt(np.mean(ref ** 2))
+    del A
+    wide = 2 ** 30 // K + 8  # K * wide * 2 >= 2^31
+    Aw = torch.zeros((K, wide), dtype=torch.int16, device=dev())
+    rc = mt.lib().mt_gemm(mt.MT_BF16, Aw.data_ptr(), wide, B.data_ptr(), N, C.data_ptr(), N, None, 0, 256, N, K,
+                          mt.EPI_F32, mt.GEMM_A_KMAJOR | mt.GEMM_B_KMAJOR, None)
+    assert rc != 0

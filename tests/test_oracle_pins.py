@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 
 import datagen
-from oracle import (Oracle, adam_update, attention_bwd, attention_fwd, cross_entropy,
+from oracle import (Oracle, adam_update, attention_bwd, attention_fwd, attention_key_tail, attention_rows,
+                    cross_entropy,
                     rmsnorm_bwd, rmsnorm_fwd, rope_apply, rope_tables, silu, silu_grad)
 
 TINY = datagen.PRESETS["tiny"]
@@ -186,6 +187,25 @@ def test_attention_bwd_finite_differences():
             lm = np.sum(attention_fwd(q, k, v)[0] * do)
             X[idx] += h
             assert abs((lp - lm) / (2 * h) - dX[idx]) < 1e-8
+
+
+def test_attention_rows_and_key_tail_are_rows_of_the_full_result():
+    """The long-sequence evaluators return exactly the corresponding rows of
+    the full T x T computation (brute-force and finite-difference pinned
+    above), including the first query, tile-crossing rows and the last key."""
+    rng = np.random.default_rng(6)
+    T, hd = 70, 8
+    q, k, v, do = (rng.standard_normal((T, hd)) for _ in range(4))
+    o, p = attention_fwd(q, k, v)
+    dq, dk, dv = attention_bwd(do, q, k, v, p)
+    rows = [0, 1, 31, 32, 63, 69]
+    ro, rdq = attention_rows(q, k, v, do, rows)
+    np.testing.assert_allclose(ro, o[rows], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(rdq, dq[rows], rtol=1e-11, atol=1e-12)
+    for n in (1, 5, T):
+        tk, tv = attention_key_tail(q, k, v, do, n)
+        np.testing.assert_allclose(tk, dk[T - n:], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(tv, dv[T - n:], rtol=1e-12, atol=1e-13)
 
 
 # ---------------------------------------------------------------- RoPE --
