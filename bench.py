@@ -142,6 +142,8 @@ def main():
     ap.add_argument("--batch", type=int, default=0, help="override the batch size")
     ap.add_argument("--seq-len", type=int, default=0, help="override the sequence length (long context)")
     ap.add_argument("--mode", default="streamed", choices=["streamed", "serialized", "resident", "single_slot"])
+    ap.add_argument("--fp32-master", action="store_true",
+                    help="keep an fp32 master copy of the weights beside the Adam moments (bf16 still streamed)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-kernel-timing", action="store_true")
@@ -165,6 +167,8 @@ def main():
         shape = shape.replace(batch=args.batch)
     if args.seq_len:
         shape = shape.replace(seq_len=args.seq_len)
+    if args.fp32_master:
+        shape = shape.replace(store_dtype=datagen.BF16_MASTER)
     dev = torch.device("cuda:0")
     flags = 0 if args.no_kernel_timing else mt.MT_FLAG_TIME_KERNELS
     if args.duplex_link:
@@ -232,7 +236,7 @@ def main():
     d2h = float(np.mean([b["d2h_ms"] for b in mid]))
     h2d_gbs = last["h2d_bytes"] / (last["h2d_ms"] / 1e3) / 1e9 if last["h2d_ms"] > 0 else None
     d2h_gbs = last["d2h_bytes"] / (last["d2h_ms"] / 1e3) / 1e9 if last["d2h_ms"] > 0 else None
-    bf = shape.store_dtype == "bf16"
+    bf = shape.store_dtype != datagen.F32
     roof = None
     if gemm_ms > 0:
         achieved = gemm_fl / (gemm_ms / 1e3) / 1e12
@@ -265,7 +269,7 @@ def main():
                                f"{shape.n_heads}x{shape.head_dim} heads, SwiGLU {shape.d_ff}, vocab {shape.vocab}; "
                                f"batch {shape.batch} x seq {shape.seq_len}; {args.mode} from the host store "
                                f"({store.nbytes / 1e9:.1f} GB pinned W/G + {store.opt_nbytes / 1e9:.1f} GB "
-                               f"Adam m/v)",
+                               f"Adam m/v{' + fp32 master W' if args.fp32_master else ''})",
                    "global_batch": shape.batch, "seq_len": shape.seq_len, "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -39,6 +39,7 @@ TOKEN_STREAM = 0x70C
 
 F32 = "f32"
 BF16 = "bf16"
+BF16_MASTER = "bf16m"  # bf16 W streamed, fp32 master copy on the host: same initial values as bf16
 
 
 @dataclasses.dataclass(frozen=True)
@@ -141,7 +142,7 @@ def draw_flat(seed: int, tid: int, start: int, stop: int, store_dtype: str,
         vals = full[lo - c * CHUNK:]
         if res.dtype == np.uint16:
             res[lo - start: hi - start] = f32_to_bf16_bits(vals)
-        elif store_dtype == BF16:
+        elif store_dtype in (BF16, BF16_MASTER):
             res[lo - start: hi - start] = bf16_bits_to_f32(f32_to_bf16_bits(vals))
         else:
             res[lo - start: hi - start] = vals

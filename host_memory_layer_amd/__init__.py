@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(PKG_DIR, "libmt.so")
 
 MT_OK = 0
 MT_E_INVALID, MT_E_SIZE, MT_E_ALIGN, MT_E_NOT_BOUND, MT_E_HIP, MT_E_NONFINITE, MT_E_OOM, MT_E_STATE = range(-1, -9, -1)
-MT_F32, MT_BF16 = 0, 1
+MT_F32, MT_BF16, MT_BF16_MASTER = 0, 1, 2
+STORE_DTYPES = {"f32": MT_F32, "bf16": MT_BF16, "bf16m": MT_BF16_MASTER}
 MT_STREAMED, MT_SERIALIZED, MT_RESIDENT, MT_SINGLE_SLOT = 0, 1, 2, 3
 MODES = {"streamed": MT_STREAMED, "serialized": MT_SERIALIZED, "resident": MT_RESIDENT,
          "single_slot": MT_SINGLE_SLOT}
@@ -44,7 +45,7 @@ class MtBlockDesc(ctypes.Structure):
                 ("pad_", ctypes.c_int32)] + \
                [(n, ctypes.c_uint64) for n in ("base", "w_off", "g_off", "m_off", "v_off", "region_elems", "w_bytes",
                                                "mv_bytes")] + \
-               [("tensors", MtTensorDesc * 8)]
+               [("tensors", MtTensorDesc * 8), ("p_off", ctypes.c_uint64)]
 
 
 class MtStats(ctypes.Structure):
@@ -100,6 +101,10 @@ _SIGS = {
     "mt_host_adam": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_double,
                                     ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_int32]),
+    "mt_host_adam_master": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_double,
+                                           ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_int32]),
+    "mt_store_init_master": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t]),
     "mt_last_error": (ctypes.c_char_p, []),
     "mt_version": (ctypes.c_char_p, []),
     "mt_gemm": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
@@ -147,11 +152,11 @@ def check(rc):
 def make_config(shape, mode="streamed", host_threads=0, flags=0) -> MtConfig:
     """mt_config from any object with the model-shape attributes
     (n_layers, d_model, n_heads, head_dim, d_ff, vocab, batch, seq_len,
-    store_dtype 'f32'|'bf16', rms_eps, rope_theta, lr, beta1, beta2, adam_eps)."""
+    store_dtype 'f32'|'bf16'|'bf16m' (bf16 with an fp32 master copy), rms_eps, rope_theta, lr, beta1, beta2, adam_eps)."""
     c = MtConfig()
     for f in ("n_layers", "d_model", "n_heads", "head_dim", "d_ff", "vocab", "batch", "seq_len"):
         setattr(c, f, int(getattr(shape, f)))
-    c.store_dtype = MT_BF16 if getattr(shape, "store_dtype", "bf16") == "bf16" else MT_F32
+    c.store_dtype = STORE_DTYPES[getattr(shape, "store_dtype", "bf16")]
     for f in ("rms_eps", "rope_theta", "lr", "beta1", "beta2", "adam_eps"):
         setattr(c, f, float(getattr(shape, f)))
     c.mode = MODES[mode] if isinstance(mode, str) else int(mode)
@@ -200,7 +205,8 @@ def _view(addr: int, nbytes: int, dtype) -> np.ndarray:
 
 class HostStore:
     """Host store: pinned DMA part (header page + per-block [W | G]) and
-    pageable optimizer part (per-block [m | v])."""
+    pageable optimizer part (per-block [m | v], or [m | v | P] with the fp32
+    master weights P of a 'bf16m' store)."""
 
     def __init__(self, cfg: MtConfig):
         self.cfg = cfg
@@ -217,12 +223,14 @@ class HostStore:
         self.opt_ptr = q.value
         check(lib().mt_init_store_header(ctypes.byref(cfg), self.ptr, self.nbytes, self.opt_ptr, self.opt_nbytes))
         self.blocks = block_infos(cfg)
-        self.wdtype = np.uint16 if cfg.store_dtype == MT_BF16 else np.float32
+        self.wdtype = np.float32 if cfg.store_dtype == MT_F32 else np.uint16
 
     def region(self, block: int, which: str) -> np.ndarray:
         b = self.blocks[block]
         base = self.ptr if which in "wg" else self.opt_ptr
-        off = {"w": b.w_off, "g": b.g_off, "m": b.m_off, "v": b.v_off}[which]
+        if which == "p" and self.cfg.store_dtype != MT_BF16_MASTER:
+            raise ValueError("the store has no fp32 master copy")
+        off = {"w": b.w_off, "g": b.g_off, "m": b.m_off, "v": b.v_off, "p": b.p_off}[which]
         dt = self.wdtype if which in "wg" else np.float32
         n = b.region_elems
         return _view(base + off, n * np.dtype(dt).itemsize, dt)
@@ -367,7 +375,8 @@ def init_store_weights(store: HostStore, draw, threads: int = 0):
     """Fill every weight tensor from ``draw(name, layer, out, pool)``, which
     writes the initial value of a logical tensor into ``out`` (a flat uint16
     bf16 view or float32 view of the store).  Gains are set to 1.  G, m, v
-    and the padding were zeroed when the store header was written."""
+    and the padding were zeroed when the store header was written.  A 'bf16m'
+    store's fp32 master copy is then set to the widened bf16 weights."""
     from concurrent.futures import ThreadPoolExecutor
     one = np.float32(1.0)
     one_bits = np.uint16(0x3F80)
@@ -382,3 +391,5 @@ def init_store_weights(store: HostStore, draw, threads: int = 0):
     with ThreadPoolExecutor(max(1, nthreads)) as pool:
         for name, layer, view in jobs:
             draw(name, layer, view.reshape(-1), pool)
+    if store.cfg.store_dtype == MT_BF16_MASTER:
+        check(lib().mt_store_init_master(store.ptr, store.nbytes, store.opt_ptr, store.opt_nbytes))

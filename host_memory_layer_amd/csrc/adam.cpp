@@ -8,7 +8,10 @@
 //   m' = b1*m + (1-b1)*g
 //   v' = b2*v + ((1-b2)*g)*g
 //   w' = w - (lr * (m'/c1)) / (sqrt(v'/c2) + eps),  c1 = 1-b1^t, c2 = 1-b2^t
-// with w, g widened from bf16 and w' rounded to nearest-even bf16.
+// with w, g widened from bf16 and w' rounded to nearest-even bf16.  With an
+// fp32 master copy P of the weights (MT_BF16_MASTER) the update runs on P
+// instead of the widened w, P keeps the fp32 result, and w receives its
+// bf16 rounding.
 // This file is compiled with -ffp-contract=off.
 #include <immintrin.h>
 
@@ -111,6 +114,26 @@ __attribute__((target("avx512f,avx512bw,avx512bf16,avx512vl"))) static void adam
   adam_scalar_bf16(w + i, g + i, m + i, v + i, n - i, k);
 }
 
+static void adam_scalar_master(uint16_t* w, float* p, const uint16_t* g, float* m, float* v, size_t n,
+                               const AdamConsts& k) {
+  for (size_t i = 0; i < n; ++i) {
+    p[i] = adam_one(p[i], widen1(g[i]), m + i, v + i, k);
+    w[i] = round1(p[i]);
+  }
+}
+
+__attribute__((target("avx512f,avx512bw,avx512bf16,avx512vl"))) static void adam_avx512_master(
+    uint16_t* w, float* p, const uint16_t* g, float* m, float* v, size_t n, const AdamConsts& k) {
+  size_t i = 0;
+  for (; i + 16 <= n; i += 16) {
+    __m512 r = adam16(_mm512_loadu_ps(p + i), widen(g + i), m + i, v + i, k);
+    _mm512_storeu_ps(p + i, r);
+    __m256bh b = _mm512_cvtneps_pbh(r);
+    _mm256_storeu_si256((__m256i*)(w + i), (__m256i)b);
+  }
+  adam_scalar_master(w + i, p + i, g + i, m + i, v + i, n - i, k);
+}
+
 static bool cpu_has_avx512() {
   static int has = -1;
   if (has < 0) {
@@ -143,6 +166,23 @@ void adam_parallel(ThreadPool& pool, int32_t dtype, void* w, const void* g, floa
   pool.run(tasks, [&](int64_t i) {
     size_t lo = (size_t)i * chunk, cnt = std::min(chunk, n - lo);
     adam_range(dtype, (char*)w + lo * wb, (const char*)g + lo * wb, m + lo, v + lo, cnt, k);
+  });
+}
+
+void adam_master_range(uint16_t* w, float* p, const uint16_t* g, float* m, float* v, size_t n, const AdamConsts& k) {
+  if (cpu_has_avx512())
+    adam_avx512_master(w, p, g, m, v, n, k);
+  else
+    adam_scalar_master(w, p, g, m, v, n, k);
+}
+
+void adam_master_parallel(ThreadPool& pool, uint16_t* w, float* p, const uint16_t* g, float* m, float* v, size_t n,
+                          const AdamConsts& k) {
+  const size_t chunk = size_t(1) << 18;
+  int64_t tasks = (int64_t)((n + chunk - 1) / chunk);
+  pool.run(tasks, [&](int64_t i) {
+    size_t lo = (size_t)i * chunk, cnt = std::min(chunk, n - lo);
+    adam_master_range(w + lo, p + lo, g + lo, m + lo, v + lo, cnt, k);
   });
 }
 

@@ -208,6 +208,33 @@ static bool same_layout(const mt_config& a, const mt_config& b) {
          a.head_dim == b.head_dim && a.d_ff == b.d_ff && a.vocab == b.vocab && a.store_dtype == b.store_dtype;
 }
 
+int mt_store_init_master(const void* dma_base, size_t dma_bytes, void* opt_base, size_t opt_bytes) {
+  return guarded([&] {
+    if (!opt_base) throw ApiError{MT_E_INVALID, "null argument"};
+    std::vector<mt_block_desc> blocks;
+    uint64_t opt = 0;
+    const StoreHeader* h = checked_header(dma_base, dma_bytes, opt_bytes, &blocks, &opt);
+    if (!master_store(h->cfg)) throw ApiError{MT_E_STATE, "store has no fp32 master copy"};
+    int threads = h->cfg.host_threads;
+    if (threads <= 0) {
+      cpu_set_t set;
+      threads = sched_getaffinity(0, sizeof(set), &set) == 0 ? CPU_COUNT(&set) : 1;
+    }
+    ThreadPool pool(std::max(1, threads));
+    const uint64_t chunk = 1ull << 22;
+    for (const auto& b : blocks) {
+      const uint16_t* w = (const uint16_t*)((const uint8_t*)dma_base + b.w_off);
+      uint32_t* p = (uint32_t*)((uint8_t*)opt_base + b.p_off);
+      const uint64_t n = b.region_elems;
+      pool.run((int64_t)((n + chunk - 1) / chunk), [&](int64_t i) {
+        const uint64_t lo = (uint64_t)i * chunk, hi = std::min(n, lo + chunk);
+        for (uint64_t e = lo; e < hi; ++e) p[e] = (uint32_t)w[e] << 16;  // bf16 -> fp32 is exact
+      });
+    }
+    return MT_OK;
+  });
+}
+
 int mt_store_save(const void* dma_base, size_t dma_bytes, const void* opt_base, size_t opt_bytes, const char* path) {
   return guarded([&] {
     if (!opt_base || !path) throw ApiError{MT_E_INVALID, "null argument"};
@@ -313,6 +340,18 @@ int mt_host_adam(int32_t store_dtype, void* w, const void* g, float* m, float* v
     const AdamConsts k = adam_consts(t, lr, beta1, beta2, eps);
     ThreadPool pool(threads > 0 ? threads : 1);
     adam_parallel(pool, store_dtype, w, g, m, v, n, k);
+    return MT_OK;
+  });
+}
+
+int mt_host_adam_master(uint16_t* w, float* p, const uint16_t* g, float* m, float* v, size_t n, int64_t t, double lr,
+                        double beta1, double beta2, double eps, int32_t threads) {
+  return guarded([&] {
+    if ((!w || !p || !g || !m || !v) && n) throw ApiError{MT_E_INVALID, "null buffer"};
+    if (t < 1) throw ApiError{MT_E_INVALID, "step t must be >= 1"};
+    const AdamConsts k = adam_consts(t, lr, beta1, beta2, eps);
+    ThreadPool pool(threads > 0 ? threads : 1);
+    adam_master_parallel(pool, w, p, g, m, v, n, k);
     return MT_OK;
   });
 }

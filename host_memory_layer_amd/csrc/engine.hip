@@ -275,7 +275,7 @@ struct Model {
     M = B * Tq;
     Mp = token_ld(M);
     E = wbytes(c);
-    if (c.store_dtype == MT_BF16) {
+    if (bf16_store(c)) {
       const int A_ = GEMM_A_KMAJOR, B_ = GEMM_B_KMAJOR;
       auto ok = [&](int m, int n, int k, int64_t lda, int64_t ldb, int lay) {
         return gemm_layout_ok(m, n, k, lda, ldb, lay);
@@ -287,7 +287,7 @@ struct Model {
     }
     n_uses = 2 * L + 3;
   }
-  uint64_t device_bytes() { return cfg.store_dtype == MT_BF16 ? carve_all<uint16_t>(nullptr) : carve_all<float>(nullptr); }
+  uint64_t device_bytes() { return bf16_store(cfg) ? carve_all<uint16_t>(nullptr) : carve_all<float>(nullptr); }
 
   float* x_ckpt(int l) { return ckpt + (uint64_t)l * M * d; }
 
@@ -554,8 +554,13 @@ void Model::adam_worker(int64_t t, double* adam_total, double* adam_tail, std::a
       if (nonfinite) continue;
       auto t0 = std::chrono::steady_clock::now();
       const mt_block_desc& b = blocks[blk];
-      adam_parallel(*pool, cfg.store_dtype, host + b.w_off, host + b.g_off, (float*)(hopt + b.m_off),
-                    (float*)(hopt + b.v_off), b.region_elems, k);
+      if (master_store(cfg))
+        adam_master_parallel(*pool, (uint16_t*)(host + b.w_off), (float*)(hopt + b.p_off),
+                             (const uint16_t*)(host + b.g_off), (float*)(hopt + b.m_off), (float*)(hopt + b.v_off),
+                             b.region_elems, k);
+      else
+        adam_parallel(*pool, cfg.store_dtype, host + b.w_off, host + b.g_off, (float*)(hopt + b.m_off),
+                      (float*)(hopt + b.v_off), b.region_elems, k);
       double ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
       *adam_total += ms;
       bstats[blk].adam_ms = ms;
@@ -781,7 +786,7 @@ int Model::train_step(const int32_t* tokens) {
   std::string enqueue_error;
   int enqueue_code = MT_OK;
   try {
-    const bool bf = cfg.store_dtype == MT_BF16;
+    const bool bf = bf16_store(cfg);
     if (!streamed) {
       bf ? step_resident<uint16_t>() : step_resident<float>();
     } else {
@@ -915,7 +920,7 @@ Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void*
   m->arena = (uint8_t*)arena;
   m->arena_bytes = arena_bytes;
   m->sc = (hipStream_t)stream;
-  if (cfg->store_dtype == MT_BF16)
+  if (bf16_store(*cfg))
     m->carve_all<uint16_t>(m->arena);
   else
     m->carve_all<float>(m->arena);
@@ -1049,7 +1054,7 @@ int model_debug(const Model* m, int layer, void** ckpt, void** row_loss) {
   if (layer < 0 || layer > m->L) throw ApiError{MT_E_INVALID, "layer index"};
   if (ckpt) *ckpt = m->ckpt + (uint64_t)layer * m->M * m->d;
   if (row_loss) {
-    if (m->cfg.store_dtype == MT_BF16) {
+    if (bf16_store(m->cfg)) {
       HeadWs<uint16_t> h = const_cast<Model*>(m)->headws<uint16_t>();
       *row_loss = h.row_loss;
     } else {

@@ -14,9 +14,10 @@ int validate_config(const mt_config& c, std::string* why) {
   if (c.d_ff < 1 || c.vocab < 2 || c.batch < 1 || c.seq_len < 2) return bad("bad sizes");
   if (c.d_model % 4 || c.d_ff % 4) return bad("d_model and d_ff must be multiples of 4");
   if (c.d_model > 16384) return bad("d_model > 16384");
-  if (c.store_dtype != MT_F32 && c.store_dtype != MT_BF16) return bad("store_dtype");
+  if (c.store_dtype != MT_F32 && c.store_dtype != MT_BF16 && c.store_dtype != MT_BF16_MASTER)
+    return bad("store_dtype");
   if (c.mode < MT_STREAMED || c.mode > MT_SINGLE_SLOT) return bad("mode");
-  if (c.store_dtype == MT_BF16) {
+  if (bf16_store(c)) {
     // MFMA tiles move 8 bf16 (16 bytes) per lane along every contraction dim.
     if (c.d_model % 64 || c.d_ff % 64 || c.head_dim != 128)
       return bad("bf16 store needs d_model, d_ff multiples of 64 and head_dim 128");
@@ -78,6 +79,10 @@ std::vector<mt_block_desc> store_layout(const mt_config& c, uint64_t* dma_bytes,
     b.m_off = opos;
     b.v_off = b.m_off + b.mv_bytes;
     opos = b.v_off + b.mv_bytes;
+    if (master_store(c)) {
+      b.p_off = opos;
+      opos += b.mv_bytes;
+    }
   }
   *dma_bytes = pos;
   if (opt_bytes) *opt_bytes = opos;

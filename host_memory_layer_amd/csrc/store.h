@@ -5,8 +5,9 @@
 // gradients and both Adam moments, every region and tensor start 4 KiB-aligned
 // so one DMA burst moves a block's weights or gradients.  The weights and
 // gradients of all blocks sit in the pinned DMA part (after a 4 KiB header
-// page); the moments, which never leave the host, sit in a pageable
-// optimizer part with the same per-block order.
+// page); the moments, and the fp32 master weights of an MT_BF16_MASTER store,
+// never leave the host and sit in a pageable optimizer part with the same
+// per-block order.
 #pragma once
 
 #include <vector>
@@ -35,7 +36,10 @@ enum { T_QKV = 0, T_O = 1, T_GU = 2, T_D = 3, T_ANORM = 4, T_FNORM = 5 };
 enum { T_WH = 0, T_FINAL = 1 };
 
 int validate_config(const mt_config& c, std::string* why);
-inline int wbytes(const mt_config& c) { return c.store_dtype == MT_BF16 ? 2 : 4; }
+// bf16 W and G on the link and the device (MT_BF16 and MT_BF16_MASTER)
+inline bool bf16_store(const mt_config& c) { return c.store_dtype != MT_F32; }
+inline bool master_store(const mt_config& c) { return c.store_dtype == MT_BF16_MASTER; }
+inline int wbytes(const mt_config& c) { return bf16_store(c) ? 2 : 4; }
 std::vector<mt_block_desc> store_layout(const mt_config& c, uint64_t* dma_bytes, uint64_t* opt_bytes = nullptr);
 
 }  // namespace mt

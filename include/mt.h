@@ -42,6 +42,9 @@ extern "C" {
 /* ------------------------------------------------------------- constants -- */
 #define MT_F32 0             /* all-fp32 store: W, G, m, v in float32 */
 #define MT_BF16 1            /* bf16 W and G, fp32 m and v */
+#define MT_BF16_MASTER 2     /* bf16 W and G streamed as with MT_BF16, plus an fp32 master copy of W
+                                beside m and v on the host: Adam updates the master in fp32 and W is
+                                its bf16 rounding, so updates below bf16 resolution accumulate */
 
 #define MT_STREAMED 0        /* two weight slots; prefetch, compute and offload overlap (the method) */
 #define MT_SERIALIZED 1      /* the streamed schedule on the compute stream only */
@@ -62,7 +65,7 @@ extern "C" {
  * cross-entropy over batch*(seq_len-1) positions; Adam without weight decay. */
 typedef struct mt_config {
   int32_t n_layers, d_model, n_heads, head_dim, d_ff, vocab, batch, seq_len;
-  int32_t store_dtype;   /* MT_F32 or MT_BF16 */
+  int32_t store_dtype;   /* MT_F32, MT_BF16 or MT_BF16_MASTER */
   double rms_eps;        /* added inside the square root (used as float32 on the device) */
   double rope_theta;     /* rotation frequency base */
   double lr, beta1, beta2, adam_eps;  /* Adam: rounded to float32 as the host update uses them */
@@ -89,13 +92,15 @@ typedef struct mt_tensor_desc {
  *   - the DMA part (pinned, hipHostMalloc): a 4 KiB header page, then per
  *     block [W | G] — the only state that crosses the host link, one burst
  *     per region;
- *   - the optimizer part (pageable host memory): per block [m | v], read and
+ *   - the optimizer part (pageable host memory): per block [m | v], or
+ *     [m | v | P] with MT_BF16_MASTER (P: the fp32 master weights), read and
  *     written only by the host Adam.
  * Every region and tensor start is 4 KiB-aligned and each block's regions
  * are contiguous inside their part.  base, w_off, g_off are byte offsets in
- * the DMA part; m_off, v_off byte offsets in the optimizer part.  Region
- * element counts are equal for the four regions; W and G hold wb-byte
- * elements (2 for bf16, 4 for f32), m and v hold float32.
+ * the DMA part; m_off, v_off, p_off byte offsets in the optimizer part
+ * (p_off is 0 without a master copy).  Region element counts are equal for
+ * all regions; W and G hold wb-byte elements (2 for bf16, 4 for f32), m, v
+ * and P hold float32.
  * Tensor order — embed: E [V x d]; layer: Wqkv [3d x d] (q, k, v rows),
  * Wo [d x d], Wgu [2F x d] (gate rows then up rows), Wd [d x F],
  * attn_norm [1 x d], ffn_norm [1 x d]; head: Wh [V x d], final_norm [1 x d]. */
@@ -105,6 +110,7 @@ typedef struct mt_block_desc {
   uint64_t region_elems;
   uint64_t w_bytes, mv_bytes;
   mt_tensor_desc tensors[MT_MAX_TENSORS];
+  uint64_t p_off;
 } mt_block_desc;
 
 /* Step statistics (milliseconds unless named otherwise); filled by
@@ -160,13 +166,18 @@ void mt_free_host_opt(void* p, size_t bytes);
  * between tensors), using the host threads of cfg (host_threads, 0 = all
  * allowed cores). */
 int mt_init_store_header(const mt_config* cfg, void* dma_base, size_t dma_bytes, void* opt_base, size_t opt_bytes);
+/* MT_BF16_MASTER stores: set every block's fp32 master P to the exact
+ * widening of its bf16 W (call once, after writing the initial weights).
+ * MT_E_STATE for stores of another dtype. */
+int mt_store_init_master(const void* dma_base, size_t dma_bytes, void* opt_base, size_t opt_bytes);
 /* Adam step counter t stored in the header (number of completed steps). */
 int mt_store_step(const void* dma_base, int64_t* t);
 
 /* Checkpoint and resume (steps 1..k, save, resume: the resumed run continues
  * bit for bit).  mt_store_save writes the resumable state of a host store to
  * the file `path`: the header page (configuration, completed Adam steps),
- * every block's W region and the optimizer part [m | v]; gradients are
+ * every block's W region and the whole optimizer part ([m | v], with P for
+ * MT_BF16_MASTER); gradients are
  * rewritten by every step and are not saved.  mt_store_load reads such a
  * file into a store initialised by mt_init_store_header with the same layout
  * (layers, widths, vocabulary, store dtype): W, m, v and the step count.
@@ -212,6 +223,11 @@ void mt_destroy_model(void* model);
  * float32; updated in place; step number t >= 1; threads as in mt_config. */
 int mt_host_adam(int32_t store_dtype, void* w, const void* g, float* m, float* v, size_t n,
                  int64_t t, double lr, double beta1, double beta2, double eps, int32_t threads);
+/* The MT_BF16_MASTER update: the same fp32 arithmetic on the master p
+ * (float32, updated in place) with g widened from bf16; w (bf16 bits) receives
+ * p' rounded to nearest even. */
+int mt_host_adam_master(uint16_t* w, float* p, const uint16_t* g, float* m, float* v, size_t n,
+                        int64_t t, double lr, double beta1, double beta2, double eps, int32_t threads);
 
 const char* mt_last_error(void);
 const char* mt_version(void);

@@ -18,6 +18,8 @@ torch = pytest.importorskip("torch")
 
 # A small bf16 decoder: two layers, head_dim 128, ragged vocabulary.
 SMALL_BF16 = datagen.ModelShape("small-bf16", 2, 256, 2, 128, 512, 1000, 2, 128)
+# The same decoder with an fp32 master copy of the weights on the host.
+SMALL_MASTER = SMALL_BF16.replace(name="small-bf16m", store_dtype=datagen.BF16_MASTER)
 
 
 def need_gpu():
@@ -32,6 +34,8 @@ def run_step(shape, mode="streamed", flags=0, steps=1):
     losses = [model.step(tok) for _ in range(steps)]
     out = dict(loss=losses[-1], losses=losses, g=read_all(store, "g"), w=read_all(store, "w"),
                m=read_all(store, "m"), v=read_all(store, "v"), stats=model.stats(), t=store.step_count())
+    if shape.store_dtype == datagen.BF16_MASTER:
+        out["p"] = read_all(store, "p")
     model.close()
     store.free()
     return out
@@ -56,7 +60,8 @@ def test_step_matches_oracle(shape):
           f"max grad rel {max(x[2] for x in rows):.2e}; max w rel {max(x[3] for x in rows):.2e}")
 
 
-@pytest.mark.parametrize("shape", [datagen.PRESETS["tiny"], SMALL_BF16], ids=["tiny-f32", "small-bf16"])
+@pytest.mark.parametrize("shape", [datagen.PRESETS["tiny"], SMALL_BF16, SMALL_MASTER],
+                         ids=["tiny-f32", "small-bf16", "small-bf16m"])
 def test_schedules_bitwise_equal(shape):
     need_gpu()
     ref = run_step(shape, "streamed")
@@ -64,8 +69,8 @@ def test_schedules_bitwise_equal(shape):
                         ("single_slot", mt.MT_FLAG_POISON)):
         r = run_step(shape, mode, flags)
         assert r["loss"] == ref["loss"], mode
-        for key in ("g", "w", "m", "v"):
-            for k in ref[key]:
+        for key in ("g", "w", "m", "v", "p"):
+            for k in ref.get(key, {}):
                 assert np.array_equal(r[key][k], ref[key][k]), (mode, flags, key, k)
 
 
@@ -90,8 +95,39 @@ def test_repeated_step_is_deterministic_and_t_advances():
         assert frob_rel(a["w"][k], P2[k]) <= W_RTOL, k
 
 
-@pytest.mark.parametrize("shape,resume_mode", [(datagen.PRESETS["tiny"], "streamed"), (SMALL_BF16, "single_slot")],
-                         ids=["tiny-f32", "small-bf16-single-slot"])
+def test_fp32_master_store_matches_oracle():
+    """fp32 master store: the device step is the bf16 store's (same loss, G,
+    m, v and, after one step, the same streamed W bit for bit); the master P
+    follows the oracle's float32 weights over two steps, and W is P rounded
+    to nearest even."""
+    need_gpu()
+    print("fp32 master store", flush=True)
+    a = run_step(SMALL_BF16)
+    b = run_step(SMALL_MASTER)
+    assert b["loss"] == a["loss"]
+    for key in "gwmv":
+        for k in a[key]:
+            assert np.array_equal(b[key][k], a[key][k]), (key, k)
+    o_loss, o_g, o_w = oracle_step(SMALL_MASTER)
+    assert_parity(b["loss"], b["g"], b["p"], o_loss, o_g, o_w)
+    two = run_step(SMALL_MASTER, steps=2)
+    assert two["t"] == 2 and two["losses"][0] == b["loss"]
+    P = datagen.init_params(SMALL_MASTER)
+    tok = datagen.tokens(SMALL_MASTER)
+    o = Oracle(SMALL_MASTER, np.float32)
+    _, _, P1, M1 = o.step(P, tok, t=1)
+    l2, _, P2, _ = o.step(P1, tok, t=2, moments=M1)
+    assert abs(two["losses"][1] - l2) / abs(l2) < 1e-2
+    for k in two["p"]:
+        assert frob_rel(two["p"][k], P2[k]) <= W_RTOL, k
+        assert np.array_equal(datagen.f32_to_bf16_bits(two["p"][k]), datagen.f32_to_bf16_bits(two["w"][k])), k
+    # the master keeps what bf16 rounding drops: it is not its own rounding
+    assert any(not np.array_equal(two["p"][k], two["w"][k]) for k in two["p"])
+
+
+@pytest.mark.parametrize("shape,resume_mode", [(datagen.PRESETS["tiny"], "streamed"), (SMALL_BF16, "single_slot"),
+                                               (SMALL_MASTER, "streamed")],
+                         ids=["tiny-f32", "small-bf16-single-slot", "small-bf16m"])
 def test_checkpoint_resume_continues_bit_for_bit(shape, resume_mode, tmp_path):
     """Steps 1-2, checkpoint, steps 3-4 on one store; a fresh store resumed
     from the checkpoint (in the streamed or the single-slot schedule) gives
@@ -104,7 +140,8 @@ def test_checkpoint_resume_continues_bit_for_bit(shape, resume_mode, tmp_path):
     path = tmp_path / "ckpt.bin"
     store.save(path)
     cont = [model.step(tok) for _ in range(2)]
-    ref = {k: read_all(store, k) for k in "wmv"}
+    keys = "wmvp" if shape.store_dtype == datagen.BF16_MASTER else "wmv"
+    ref = {k: read_all(store, k) for k in keys}
     assert store.step_count() == 4
     model.close()
     store.free()
@@ -113,13 +150,13 @@ def test_checkpoint_resume_continues_bit_for_bit(shape, resume_mode, tmp_path):
     assert store2.step_count() == 2
     model2 = mt.Model(cfg2, store2, "cuda:0")
     again = [model2.step(tok) for _ in range(2)]
-    got = {k: read_all(store2, k) for k in "wmv"}
+    got = {k: read_all(store2, k) for k in keys}
     assert store2.step_count() == 4
     model2.close()
     store2.free()
     print(f"losses {first} | {cont} | resumed {again}", flush=True)
     assert again == cont
-    for k in "wmv":
+    for k in keys:
         for name in ref[k]:
             assert np.array_equal(got[k][name], ref[k][name]), (k, name)
 

@@ -36,18 +36,22 @@ def test_struct_sizes_match_header():
     # layout of the C structs, mirrored by ctypes
     assert ctypes.sizeof(mt.MtConfig) == 9 * 4 + 4 + 6 * 8 + 3 * 4 + 4
     assert ctypes.sizeof(mt.MtTensorDesc) == 16
-    assert ctypes.sizeof(mt.MtBlockDesc) == 16 + 8 * 8 + 8 * 16
+    assert ctypes.sizeof(mt.MtBlockDesc) == 16 + 8 * 8 + 8 * 16 + 8
     assert ctypes.sizeof(mt.MtStats) == 15 * 8 + 2 * 8 + 8 + 2 * 4 + 8
 
 
-@pytest.mark.parametrize("name", list(datagen.PRESETS))
-def test_store_layout(name):
+@pytest.mark.parametrize("name,dtype", [(n, None) for n in datagen.PRESETS] +
+                         [("1.3b", datagen.BF16_MASTER), ("14b", datagen.BF16_MASTER)])
+def test_store_layout(name, dtype):
     shape = datagen.PRESETS[name]
+    if dtype:
+        shape = shape.replace(store_dtype=dtype)
+    master = shape.store_dtype == datagen.BF16_MASTER
     cfg = mt.make_config(shape)
     blocks = mt.block_infos(cfg)
     total = mt.host_store_bytes(cfg)
     opt_total = mt.host_opt_bytes(cfg)
-    wb = 2 if shape.store_dtype == "bf16" else 4
+    wb = 4 if shape.store_dtype == "f32" else 2
     d, F, V, L = shape.d_model, shape.d_ff, shape.vocab, shape.n_layers
     assert len(blocks) == L + 2
     prev_end = 4096
@@ -57,12 +61,17 @@ def test_store_layout(name):
         assert b.kind == (mt.MT_BLOCK_EMBED if i == 0 else mt.MT_BLOCK_HEAD if i == L + 1 else mt.MT_BLOCK_LAYER)
         for off in (b.base, b.w_off, b.g_off, b.m_off, b.v_off):
             assert off % 4096 == 0
-        # per block: W | G contiguous in the DMA part, m | v contiguous in the optimizer part
+        # per block: W | G contiguous in the DMA part, m | v (| P) contiguous in the optimizer part
         assert b.base == prev_end == b.w_off
         assert b.g_off == b.w_off + b.w_bytes
         assert b.m_off == prev_opt and b.v_off == b.m_off + b.mv_bytes
         prev_end = b.g_off + b.w_bytes
         prev_opt = b.v_off + b.mv_bytes
+        if master:
+            assert b.p_off == prev_opt
+            prev_opt += b.mv_bytes
+        else:
+            assert b.p_off == 0
         assert b.w_bytes == b.region_elems * wb and b.mv_bytes == b.region_elems * 4
         end = 0
         for t in range(b.n_tensors):
@@ -87,6 +96,16 @@ def test_store_sizes_of_the_14b_shape():
     dma, opt = mt.host_store_bytes(cfg), mt.host_opt_bytes(cfg)
     assert abs((dma + opt) / 1e9 - 186.64) < 0.05
     assert abs(dma / (dma + opt) - 1 / 3) < 1e-3
+
+
+def test_store_sizes_with_fp32_master():
+    """The fp32 master copy adds 4 bytes/param to the pageable part only:
+    16 bytes/param, the pinned (streamed) part unchanged."""
+    base = mt.make_config(datagen.PRESETS["14b"])
+    cfg = mt.make_config(datagen.PRESETS["14b"].replace(store_dtype=datagen.BF16_MASTER))
+    assert mt.host_store_bytes(cfg) == mt.host_store_bytes(base)
+    assert mt.host_opt_bytes(cfg) * 2 == mt.host_opt_bytes(base) * 3
+    assert abs((mt.host_store_bytes(cfg) + mt.host_opt_bytes(cfg)) / 1e9 - 186.64 * 16 / 12) < 0.1
 
 
 def test_config_validation():
@@ -144,6 +163,57 @@ def test_host_adam_bf16_rounds_the_fp32_update():
     assert np.array_equal(m, om) and np.array_equal(v, ov)
 
 
+def _adam_master(w, p, g, m, v, t, lr):
+    mt.check(mt.lib().mt_host_adam_master(w.ctypes.data, p.ctypes.data, g.ctypes.data, m.ctypes.data, v.ctypes.data,
+                                          w.size, t, lr, 0.9, 0.95, 1e-8, 3))
+
+
+def test_host_adam_master_is_the_fp32_iteration():
+    """fp32 master store: over several steps the master p follows the
+    oracle's float32 Adam on float32 weights bit for bit (gradients widened
+    from bf16), and w is p rounded to nearest even after every step."""
+    rng = np.random.default_rng(3)
+    n = 70001
+    p0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    w = datagen.f32_to_bf16_bits(p0)
+    p = datagen.bf16_bits_to_f32(w).copy()
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    ow, om, ov = p.copy(), m.copy(), v.copy()
+    for t in range(1, 6):
+        gb = datagen.f32_to_bf16_bits((rng.standard_normal(n) * 10.0 ** rng.uniform(-7, -2, n)).astype(np.float32))
+        _adam_master(w, p, gb, m, v, t, 1e-3)
+        ow, om, ov = adam_update(ow, datagen.bf16_bits_to_f32(gb), om, ov, t, 1e-3, 0.9, 0.95, 1e-8)
+        assert np.array_equal(p, ow) and np.array_equal(m, om) and np.array_equal(v, ov), t
+        assert np.array_equal(w, datagen.f32_to_bf16_bits(p)), t
+
+
+def test_master_keeps_updates_below_bf16_resolution():
+    """A constant gradient makes every bias-corrected Adam step lr*g/(|g|+eps)
+    (closed form).  At |w| = 0.02 (bf16 spacing 2^-13) steps of lr = 1e-5 are
+    below half a bf16 spacing: a bf16 store never moves, while the fp32
+    master advances by the sum of the steps and its rounding moves w."""
+    n, k, lr = 4096, 60, 1e-5
+    w0 = np.full(n, 0.02, np.float32)
+    g = np.where(np.arange(n) % 2 == 0, 1e-3, -1e-3).astype(np.float32)
+    gb = datagen.f32_to_bf16_bits(g)
+    wb = datagen.f32_to_bf16_bits(w0)
+    w_bf16 = wb.copy()
+    m1, v1 = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    w_m, p = wb.copy(), datagen.bf16_bits_to_f32(wb).copy()
+    m2, v2 = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for t in range(1, k + 1):
+        mt.check(mt.lib().mt_host_adam(mt.MT_BF16, w_bf16.ctypes.data, gb.ctypes.data, m1.ctypes.data,
+                                       v1.ctypes.data, n, t, lr, 0.9, 0.95, 1e-8, 2))
+        _adam_master(w_m, p, gb, m2, v2, t, lr)
+    assert np.array_equal(w_bf16, wb)
+    gw = datagen.bf16_bits_to_f32(gb).astype(np.float64)
+    expect = datagen.bf16_bits_to_f32(wb).astype(np.float64) - k * lr * gw / (np.abs(gw) + 1e-8)
+    assert np.max(np.abs(p - expect)) < 1e-7
+    assert np.array_equal(w_m, datagen.f32_to_bf16_bits(p))
+    assert np.all(w_m != wb)
+
+
 def test_host_adam_rejects_bad_arguments():
     assert mt.lib().mt_host_adam(5, None, None, None, None, 0, 1, 1e-3, 0.9, 0.95, 1e-8, 1) == mt.MT_E_INVALID
     x = np.zeros(4, np.float32)
@@ -182,11 +252,33 @@ def _plain_store(cfg):
     return (keep_d, keep_o), dma, opt, pd, po, n, no
 
 
-def test_store_checkpoint_round_trip(tmp_path):
-    """mt_store_save / mt_store_load: W regions, [m | v] and the step count
-    come back bit for bit into a fresh store; gradients are not part of the
-    checkpoint; a store of another layout or a short file is rejected."""
-    shape = datagen.PRESETS["tiny"]
+SMALL_MASTER = datagen.ModelShape("small-bf16m", 2, 256, 2, 128, 512, 1000, 2, 128, store_dtype=datagen.BF16_MASTER)
+
+
+def test_store_init_master_widens_w():
+    cfg = mt.make_config(SMALL_MASTER)
+    keep, dma, opt, pd, po, n, no = _plain_store(cfg)
+    rng = np.random.default_rng(8)
+    blocks = mt.block_infos(cfg)
+    for b in blocks:
+        dma[b.w_off:b.w_off + b.w_bytes] = rng.integers(0, 256, b.w_bytes, dtype=np.uint8)
+    mt.check(mt.lib().mt_store_init_master(pd, n, po, no))
+    for b in blocks:
+        wbits = dma[b.w_off:b.w_off + b.w_bytes].view(np.uint16)
+        pw = opt[b.p_off:b.p_off + b.mv_bytes].view(np.uint32)
+        assert np.array_equal(pw, wbits.astype(np.uint32) << np.uint32(16))
+        assert not opt[b.m_off:b.v_off + b.mv_bytes].any()
+    plain = mt.make_config(SMALL_MASTER.replace(store_dtype=datagen.BF16))
+    keep2, _, _, pd2, po2, n2, no2 = _plain_store(plain)
+    assert mt.lib().mt_store_init_master(pd2, n2, po2, no2) == mt.MT_E_STATE
+
+
+@pytest.mark.parametrize("shape", [datagen.PRESETS["tiny"], SMALL_MASTER], ids=["tiny-f32", "small-bf16m"])
+def test_store_checkpoint_round_trip(shape, tmp_path):
+    """mt_store_save / mt_store_load: W regions, the optimizer part ([m | v],
+    with the fp32 master P when there is one) and the step count come back
+    bit for bit into a fresh store; gradients are not part of the checkpoint;
+    a store of another layout or a short file is rejected."""
     cfg = mt.make_config(shape)
     keep_a, dma_a, opt_a, pa, oa, n, no = _plain_store(cfg)
     rng = np.random.default_rng(5)
