@@ -142,6 +142,8 @@ def main():
     ap.add_argument("--batch", type=int, default=0, help="override the batch size")
     ap.add_argument("--seq-len", type=int, default=0, help="override the sequence length (long context)")
     ap.add_argument("--mode", default="streamed", choices=["streamed", "serialized", "resident", "single_slot"])
+    ap.add_argument("--micro-batches", type=int, default=1,
+                    help="gradient accumulation: this many micro-batches of the configured batch per step")
     ap.add_argument("--fp32-master", action="store_true",
                     help="keep an fp32 master copy of the weights beside the Adam moments (bf16 still streamed)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -173,7 +175,8 @@ def main():
     flags = 0 if args.no_kernel_timing else mt.MT_FLAG_TIME_KERNELS
     if args.duplex_link:
         flags |= mt.MT_FLAG_DUPLEX_LINK
-    cfg = mt.make_config(shape, mode=args.mode, flags=flags)
+    K = max(1, args.micro_batches)
+    cfg = mt.make_config(shape, mode=args.mode, flags=flags, micro_batches=K)
 
     t0 = time.perf_counter()
     store = mt.HostStore(cfg)
@@ -187,7 +190,7 @@ def main():
     layer_bytes = store.blocks[1].w_bytes
     link = link_probe(torch, dev, layer_bytes)
     log(f"host link: {link}")
-    tokens = datagen.tokens(shape)
+    tokens = datagen.tokens(shape.replace(batch=K * shape.batch))
     if args.copy_probe:
         # 1 GiB read + 1 GiB written per launch: what FETCH_SIZE / WRITE_SIZE
         # read for this kernel calibrates those counters to bytes
@@ -224,7 +227,7 @@ def main():
     elapsed = time.perf_counter() - t0
 
     fwd_layer, model_flops, hw_flops = flops(shape)
-    value = model_flops * args.steps / elapsed / 1e12
+    value = K * model_flops * args.steps / elapsed / 1e12
     last = st_acc[-1]
     L = shape.n_layers
     per_layer = [model.block_stats(j) for j in range(1, L + 1)]
@@ -267,15 +270,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{shape.name}-shape decoder: {L} layers, d {shape.d_model}, "
                                f"{shape.n_heads}x{shape.head_dim} heads, SwiGLU {shape.d_ff}, vocab {shape.vocab}; "
-                               f"batch {shape.batch} x seq {shape.seq_len}; {args.mode} from the host store "
+                               f"batch {shape.batch} x seq {shape.seq_len}"
+                               f"{f' x {K} micro-batches' if K > 1 else ''}; {args.mode} from the host store "
                                f"({store.nbytes / 1e9:.1f} GB pinned W/G + {store.opt_nbytes / 1e9:.1f} GB "
                                f"Adam m/v{' + fp32 master W' if args.fp32_master else ''})",
-                   "global_batch": shape.batch, "seq_len": shape.seq_len, "parallelism": "single GPU"},
+                   "global_batch": K * shape.batch, "seq_len": shape.seq_len, "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": {
-            "model_flops_per_step": model_flops, "hw_flops_per_step": hw_flops,
-            "hw_tflops": hw_flops * args.steps / elapsed / 1e12,
+            "model_flops_per_step": K * model_flops, "hw_flops_per_step": K * hw_flops,
+            "hw_tflops": K * hw_flops * args.steps / elapsed / 1e12,
             "device_ms": last["device_ms"], "step_ms": last["step_ms"], "loss": loss,
             "h2d_gbs_achieved": h2d_gbs, "d2h_gbs_achieved": d2h_gbs,
             "link_peak": link,

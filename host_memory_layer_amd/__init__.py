@@ -33,7 +33,7 @@ class MtConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("n_layers", "d_model", "n_heads", "head_dim", "d_ff", "vocab", "batch", "seq_len", "store_dtype")] + \
                [(n, ctypes.c_double) for n in ("rms_eps", "rope_theta", "lr", "beta1", "beta2", "adam_eps")] + \
-               [(n, ctypes.c_int32) for n in ("mode", "host_threads", "flags")]
+               [(n, ctypes.c_int32) for n in ("mode", "host_threads", "flags", "micro_batches")]
 
 
 class MtTensorDesc(ctypes.Structure):
@@ -45,7 +45,7 @@ class MtBlockDesc(ctypes.Structure):
                 ("pad_", ctypes.c_int32)] + \
                [(n, ctypes.c_uint64) for n in ("base", "w_off", "g_off", "m_off", "v_off", "region_elems", "w_bytes",
                                                "mv_bytes")] + \
-               [("tensors", MtTensorDesc * 8), ("p_off", ctypes.c_uint64)]
+               [("tensors", MtTensorDesc * 8), ("p_off", ctypes.c_uint64), ("a_off", ctypes.c_uint64)]
 
 
 class MtStats(ctypes.Structure):
@@ -149,7 +149,7 @@ def check(rc):
     return rc
 
 
-def make_config(shape, mode="streamed", host_threads=0, flags=0) -> MtConfig:
+def make_config(shape, mode="streamed", host_threads=0, flags=0, micro_batches=1) -> MtConfig:
     """mt_config from any object with the model-shape attributes
     (n_layers, d_model, n_heads, head_dim, d_ff, vocab, batch, seq_len,
     store_dtype 'f32'|'bf16'|'bf16m' (bf16 with an fp32 master copy), rms_eps, rope_theta, lr, beta1, beta2, adam_eps)."""
@@ -162,6 +162,7 @@ def make_config(shape, mode="streamed", host_threads=0, flags=0) -> MtConfig:
     c.mode = MODES[mode] if isinstance(mode, str) else int(mode)
     c.host_threads = int(host_threads)
     c.flags = int(flags)
+    c.micro_batches = int(micro_batches)
     return c
 
 
@@ -205,8 +206,9 @@ def _view(addr: int, nbytes: int, dtype) -> np.ndarray:
 
 class HostStore:
     """Host store: pinned DMA part (header page + per-block [W | G]) and
-    pageable optimizer part (per-block [m | v], or [m | v | P] with the fp32
-    master weights P of a 'bf16m' store)."""
+    pageable optimizer part (per-block [m | v], then the fp32 master weights
+    P of a 'bf16m' store, then the fp32 gradient accumulator A when the
+    configuration has micro-batches)."""
 
     def __init__(self, cfg: MtConfig):
         self.cfg = cfg
@@ -230,7 +232,9 @@ class HostStore:
         base = self.ptr if which in "wg" else self.opt_ptr
         if which == "p" and self.cfg.store_dtype != MT_BF16_MASTER:
             raise ValueError("the store has no fp32 master copy")
-        off = {"w": b.w_off, "g": b.g_off, "m": b.m_off, "v": b.v_off, "p": b.p_off}[which]
+        if which == "a" and self.cfg.micro_batches <= 1:
+            raise ValueError("the store has no gradient accumulator")
+        off = {"w": b.w_off, "g": b.g_off, "m": b.m_off, "v": b.v_off, "p": b.p_off, "a": b.a_off}[which]
         dt = self.wdtype if which in "wg" else np.float32
         n = b.region_elems
         return _view(base + off, n * np.dtype(dt).itemsize, dt)
@@ -319,8 +323,8 @@ class Model:
 
     def step(self, tokens: np.ndarray) -> float:
         tok = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
-        if tok.size != self.cfg.batch * self.cfg.seq_len:
-            raise ValueError("tokens must hold batch*seq_len values")
+        if tok.size != max(1, self.cfg.micro_batches) * self.cfg.batch * self.cfg.seq_len:
+            raise ValueError("tokens must hold micro_batches*batch*seq_len values")
         check(lib().mt_train_step(self.handle, tok.ctypes.data))
         return self.loss()
 

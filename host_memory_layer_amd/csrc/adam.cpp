@@ -12,6 +12,8 @@
 // fp32 master copy P of the weights (MT_BF16_MASTER) the update runs on P
 // instead of the widened w, P keeps the fp32 result, and w receives its
 // bf16 rounding.
+// With micro-batches the gradient is first summed in an fp32 accumulator
+// (acc + widen(g), one micro-batch after the other) and the update uses it.
 // This file is compiled with -ffp-contract=off.
 #include <immintrin.h>
 
@@ -166,6 +168,98 @@ void adam_parallel(ThreadPool& pool, int32_t dtype, void* w, const void* g, floa
   pool.run(tasks, [&](int64_t i) {
     size_t lo = (size_t)i * chunk, cnt = std::min(chunk, n - lo);
     adam_range(dtype, (char*)w + lo * wb, (const char*)g + lo * wb, m + lo, v + lo, cnt, k);
+  });
+}
+
+// ---------------------------------------------------- accumulation --
+static inline float gval(int32_t dtype, const void* g, size_t i) {
+  return dtype == MT_F32 ? ((const float*)g)[i] : widen1(((const uint16_t*)g)[i]);
+}
+
+static void accumulate_scalar(int32_t dtype, float* acc, const void* g, size_t n, bool first) {
+  for (size_t i = 0; i < n; ++i) acc[i] = first ? gval(dtype, g, i) : acc[i] + gval(dtype, g, i);
+}
+
+__attribute__((target("avx512f,avx512bw"))) static inline __m512 gvec(int32_t dtype, const void* g, size_t i) {
+  return dtype == MT_F32 ? _mm512_loadu_ps((const float*)g + i) : widen((const uint16_t*)g + i);
+}
+
+__attribute__((target("avx512f,avx512bw"))) static void accumulate_avx512(int32_t dtype, float* acc, const void* g,
+                                                                           size_t n, bool first) {
+  size_t i = 0;
+  for (; i + 16 <= n; i += 16) {
+    __m512 x = gvec(dtype, g, i);
+    _mm512_storeu_ps(acc + i, first ? x : _mm512_add_ps(_mm512_loadu_ps(acc + i), x));
+  }
+  accumulate_scalar(dtype, acc + i, (const char*)g + i * (dtype == MT_F32 ? 4 : 2), n - i, first);
+}
+
+static void adam_acc_scalar(int32_t dtype, void* w, float* p, float* acc, const void* g, float* m, float* v, size_t n,
+                            const AdamConsts& k) {
+  for (size_t i = 0; i < n; ++i) {
+    const float gi = acc[i] + gval(dtype, g, i);
+    acc[i] = gi;
+    if (dtype == MT_F32) {
+      ((float*)w)[i] = adam_one(((float*)w)[i], gi, m + i, v + i, k);
+    } else if (dtype == MT_BF16) {
+      ((uint16_t*)w)[i] = round1(adam_one(widen1(((uint16_t*)w)[i]), gi, m + i, v + i, k));
+    } else {
+      p[i] = adam_one(p[i], gi, m + i, v + i, k);
+      ((uint16_t*)w)[i] = round1(p[i]);
+    }
+  }
+}
+
+__attribute__((target("avx512f,avx512bw,avx512bf16,avx512vl"))) static void adam_acc_avx512(
+    int32_t dtype, void* w, float* p, float* acc, const void* g, float* m, float* v, size_t n, const AdamConsts& k) {
+  size_t i = 0;
+  for (; i + 16 <= n; i += 16) {
+    const __m512 gi = _mm512_add_ps(_mm512_loadu_ps(acc + i), gvec(dtype, g, i));
+    _mm512_storeu_ps(acc + i, gi);
+    if (dtype == MT_F32) {
+      float* wf = (float*)w + i;
+      _mm512_storeu_ps(wf, adam16(_mm512_loadu_ps(wf), gi, m + i, v + i, k));
+    } else {
+      uint16_t* wb = (uint16_t*)w + i;
+      __m512 r;
+      if (dtype == MT_BF16) {
+        r = adam16(widen(wb), gi, m + i, v + i, k);
+      } else {
+        r = adam16(_mm512_loadu_ps(p + i), gi, m + i, v + i, k);
+        _mm512_storeu_ps(p + i, r);
+      }
+      __m256bh b = _mm512_cvtneps_pbh(r);
+      _mm256_storeu_si256((__m256i*)wb, (__m256i)b);
+    }
+  }
+  const size_t wb = dtype == MT_F32 ? 4 : 2;
+  adam_acc_scalar(dtype, (char*)w + i * wb, p ? p + i : nullptr, acc + i, (const char*)g + i * wb, m + i, v + i, n - i,
+                  k);
+}
+
+void grad_accumulate_parallel(ThreadPool& pool, int32_t dtype, float* acc, const void* g, size_t n, bool first) {
+  const size_t chunk = size_t(1) << 18;
+  const size_t gb = dtype == MT_F32 ? 4 : 2;
+  pool.run((int64_t)((n + chunk - 1) / chunk), [&](int64_t i) {
+    size_t lo = (size_t)i * chunk, cnt = std::min(chunk, n - lo);
+    if (cpu_has_avx512())
+      accumulate_avx512(dtype, acc + lo, (const char*)g + lo * gb, cnt, first);
+    else
+      accumulate_scalar(dtype, acc + lo, (const char*)g + lo * gb, cnt, first);
+  });
+}
+
+void adam_accumulated_parallel(ThreadPool& pool, int32_t dtype, void* w, float* p, float* acc, const void* g,
+                               float* m, float* v, size_t n, const AdamConsts& k) {
+  const size_t chunk = size_t(1) << 18;
+  const size_t wb = dtype == MT_F32 ? 4 : 2;
+  pool.run((int64_t)((n + chunk - 1) / chunk), [&](int64_t i) {
+    size_t lo = (size_t)i * chunk, cnt = std::min(chunk, n - lo);
+    float* pl = p ? p + lo : nullptr;
+    if (cpu_has_avx512())
+      adam_acc_avx512(dtype, (char*)w + lo * wb, pl, acc + lo, (const char*)g + lo * wb, m + lo, v + lo, cnt, k);
+    else
+      adam_acc_scalar(dtype, (char*)w + lo * wb, pl, acc + lo, (const char*)g + lo * wb, m + lo, v + lo, cnt, k);
   });
 }
 

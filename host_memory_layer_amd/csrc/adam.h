@@ -24,4 +24,13 @@ void adam_master_range(uint16_t* w, float* p, const uint16_t* g, float* m, float
 void adam_master_parallel(ThreadPool& pool, uint16_t* w, float* p, const uint16_t* g, float* m, float* v, size_t n,
                           const AdamConsts& k);
 
+// Gradient accumulation over micro-batches, gradients g in the store dtype:
+// acc = widen(g) on the first micro-batch, acc = acc + widen(g) after it.
+void grad_accumulate_parallel(ThreadPool& pool, int32_t store_dtype, float* acc, const void* g, size_t n, bool first);
+// The last micro-batch: acc = acc + widen(g), then the Adam update of the
+// store's weights (w, and the fp32 master p of an MT_BF16_MASTER store) with
+// acc as the gradient.
+void adam_accumulated_parallel(ThreadPool& pool, int32_t store_dtype, void* w, float* p, float* acc, const void* g,
+                               float* m, float* v, size_t n, const AdamConsts& k);
+
 }  // namespace mt

@@ -205,7 +205,8 @@ static const StoreHeader* checked_header(const void* dma_base, size_t dma_bytes,
 
 static bool same_layout(const mt_config& a, const mt_config& b) {
   return a.n_layers == b.n_layers && a.d_model == b.d_model && a.n_heads == b.n_heads &&
-         a.head_dim == b.head_dim && a.d_ff == b.d_ff && a.vocab == b.vocab && a.store_dtype == b.store_dtype;
+         a.head_dim == b.head_dim && a.d_ff == b.d_ff && a.vocab == b.vocab && a.store_dtype == b.store_dtype &&
+         (micro_count(a) > 1) == (micro_count(b) > 1);
 }
 
 int mt_store_init_master(const void* dma_base, size_t dma_bytes, void* opt_base, size_t opt_bytes) {

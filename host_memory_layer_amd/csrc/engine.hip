@@ -436,7 +436,8 @@ struct Model {
     T* gwh = (T*)greg + b.tensors[T_WH].offset;
     T* gfin = (T*)greg + b.tensors[T_FINAL].offset;
     const float* xL = x_ckpt(L);
-    const float inv_n = 1.0f / (float)((int64_t)B * (Tq - 1));
+    // mean over the labelled positions of every micro-batch of the step
+    const float inv_n = 1.0f / (float)((int64_t)micro_count(cfg) * B * (Tq - 1));
     rmsnorm_fwd<T>(xL, fin, hw.z, hw.rz, M, d, (float)cfg.rms_eps, sc);
     gemm<T>(hw.z, d, wh, d, hw.logits, V, nullptr, 0, M, V, d, EPI_F32);
     xent<T>(hw.logits, d_tok, hw.row_loss, hw.dlogits, M, Tq, V, inv_n, sc);
@@ -490,7 +491,9 @@ struct Model {
   template <typename T>
   void step_resident();
   int train_step(const int32_t* tokens);
+  void run_pass(const int32_t* tokens, int64_t t, double* adam_total, double* adam_tail);
   void finish_stats(bool streamed, double wall_ms);
+  int mb = 0;  // micro-batch of the running pass
 
   // Adam worker coordination
   std::mutex q_mu;
@@ -538,6 +541,7 @@ void Model::adam_worker(int64_t t, double* adam_total, double* adam_tail, std::a
     MT_HIP(hipEventSynchronize(ev_loss));
     if (!std::isfinite(*h_loss)) nonfinite = true;
     const AdamConsts k = adam_consts(t, cfg.lr, cfg.beta1, cfg.beta2, cfg.adam_eps);
+    const int K = micro_count(cfg);
     size_t next = 0;
     for (;;) {
       int blk;
@@ -554,7 +558,14 @@ void Model::adam_worker(int64_t t, double* adam_total, double* adam_tail, std::a
       if (nonfinite) continue;
       auto t0 = std::chrono::steady_clock::now();
       const mt_block_desc& b = blocks[blk];
-      if (master_store(cfg))
+      float* acc = (float*)(hopt + b.a_off);
+      float* pm = master_store(cfg) ? (float*)(hopt + b.p_off) : nullptr;
+      if (K > 1 && mb < K - 1)
+        grad_accumulate_parallel(*pool, cfg.store_dtype, acc, host + b.g_off, b.region_elems, mb == 0);
+      else if (K > 1)
+        adam_accumulated_parallel(*pool, cfg.store_dtype, host + b.w_off, pm, acc, host + b.g_off,
+                                  (float*)(hopt + b.m_off), (float*)(hopt + b.v_off), b.region_elems, k);
+      else if (master_store(cfg))
         adam_master_parallel(*pool, (uint16_t*)(host + b.w_off), (float*)(hopt + b.p_off),
                              (const uint16_t*)(host + b.g_off), (float*)(hopt + b.m_off), (float*)(hopt + b.v_off),
                              b.region_elems, k);
@@ -733,12 +744,33 @@ int Model::train_step(const int32_t* tokens) {
   auto t0 = std::chrono::steady_clock::now();
   StoreHeader* hdr = (StoreHeader*)host;
   const int64_t t = hdr->step + 1;
+  const int K = micro_count(cfg);
+  for (int64_t m = 0; m < (int64_t)K * M; ++m)
+    if (tokens[m] < 0 || tokens[m] >= V) throw ApiError{MT_E_INVALID, "token out of range [0, vocab)"};
+  nonfinite = false;
+  double adam_total = 0, adam_tail = 0, loss_sum = 0;
+  for (mb = 0; mb < K; ++mb) {
+    run_pass(tokens + (int64_t)mb * M, t, &adam_total, &adam_tail);
+    loss_sum += (double)*h_loss;
+  }
+  last_loss = (float)loss_sum;
+  have_loss = true;
+  double wall = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+  stats.adam_ms = adam_total;
+  stats.adam_tail_ms = adam_tail;
+  finish_stats(cfg.mode != MT_RESIDENT, wall);
+  if (nonfinite) throw ApiError{MT_E_NONFINITE, "loss is not finite; Adam skipped, W/m/v unchanged"};
+  hdr->step = t;
+  return MT_OK;
+}
+
+// One forward and backward sweep over a micro-batch of M tokens; the host
+// worker accumulates or applies (last micro-batch) each block's gradients as
+// they land.  With one micro-batch this is the whole step.
+void Model::run_pass(const int32_t* tokens, int64_t t, double* adam_total, double* adam_tail) {
   // tokens and the stable token-sorted order for the embedding backward
   std::vector<int32_t> count(V + 1, 0);
-  for (int m = 0; m < M; ++m) {
-    if (tokens[m] < 0 || tokens[m] >= V) throw ApiError{MT_E_INVALID, "token out of range [0, vocab)"};
-    count[tokens[m] + 1]++;
-  }
+  for (int m = 0; m < M; ++m) count[tokens[m] + 1]++;
   memcpy(h_tok, tokens, sizeof(int32_t) * M);
   h_seg[0] = 0;
   for (int v = 0; v < V; ++v) h_seg[v + 1] = h_seg[v] + count[v + 1];
@@ -755,11 +787,9 @@ int Model::train_step(const int32_t* tokens) {
     q_events.clear();
     q_closed = false;
   }
-  nonfinite = false;
   adam_error.clear();
   kev_used = 0;
   for (auto& s : bstats) s = mt_block_stats{};
-  double adam_total = 0, adam_tail = 0;
   std::atomic<bool> device_done{false};
   const bool streamed = cfg.mode != MT_RESIDENT;
   if (streamed && !dma) {
@@ -777,7 +807,7 @@ int Model::train_step(const int32_t* tokens) {
   }
   h2d_host_ms.assign(n_uses, 0.0);
   d2h_host_ms.assign(n_uses, 0.0);
-  std::thread worker([&] { adam_worker(t, &adam_total, &adam_tail, &device_done); });
+  std::thread worker([&] { adam_worker(t, adam_total, adam_tail, &device_done); });
   if (streamed) {
     xq_in->start(&h2d_host_ms, nullptr);
     xq_out->start(&d2h_host_ms, [this](const TransferQueue::Job& job) { push_adam(job.j, nullptr); });
@@ -813,15 +843,6 @@ int Model::train_step(const int32_t* tokens) {
   if (enqueue_code != MT_OK) throw ApiError{enqueue_code, enqueue_error};
   if (e1 != hipSuccess) throw ApiError{MT_E_HIP, std::string("stream synchronize: ") + hipGetErrorString(e1)};
   if (!adam_error.empty()) throw ApiError{MT_E_HIP, "host Adam: " + adam_error};
-  last_loss = *h_loss;
-  have_loss = true;
-  double wall = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
-  stats.adam_ms = adam_total;
-  stats.adam_tail_ms = adam_tail;
-  finish_stats(cfg.mode != MT_RESIDENT, wall);
-  if (nonfinite) throw ApiError{MT_E_NONFINITE, "loss is not finite; Adam skipped, W/m/v unchanged"};
-  hdr->step = t;
-  return MT_OK;
 }
 
 void Model::finish_stats(bool streamed, double wall_ms) {
@@ -1013,6 +1034,8 @@ int bind_store(Model* m, void* host, size_t bytes, void* opt, size_t opt_bytes) 
   if (a.n_layers != c.n_layers || a.d_model != c.d_model || a.n_heads != c.n_heads || a.head_dim != c.head_dim ||
       a.d_ff != c.d_ff || a.vocab != c.vocab || a.store_dtype != c.store_dtype)
     throw ApiError{MT_E_INVALID, "store header describes another model shape"};
+  if ((micro_count(a) > 1) != (micro_count(c) > 1))
+    throw ApiError{MT_E_INVALID, "micro-batches need a store with a gradient accumulator (and only then)"};
   unsigned int flags = 0;
   if (hipHostGetFlags(&flags, host) != hipSuccess) {
     (void)hipGetLastError();

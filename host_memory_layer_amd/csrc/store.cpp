@@ -27,6 +27,8 @@ int validate_config(const mt_config& c, std::string* why) {
     if (c.seq_len > 4096) return bad("f32 store supports seq_len <= 4096");
   }
   if ((int64_t)c.batch * c.seq_len > (int64_t)1 << 30) return bad("too many tokens");
+  if (c.micro_batches < 0 || c.micro_batches > 4096) return bad("micro_batches must be in [0, 4096]");
+  if ((int64_t)micro_count(c) * c.batch * c.seq_len > ((int64_t)1 << 31) - 1) return bad("too many tokens per step");
   if (!(c.rms_eps > 0) || !(c.rope_theta > 1) || !(c.lr >= 0) || !(c.beta1 >= 0 && c.beta1 < 1) ||
       !(c.beta2 >= 0 && c.beta2 < 1) || !(c.adam_eps > 0))
     return bad("bad hyper-parameters");
@@ -81,6 +83,10 @@ std::vector<mt_block_desc> store_layout(const mt_config& c, uint64_t* dma_bytes,
     opos = b.v_off + b.mv_bytes;
     if (master_store(c)) {
       b.p_off = opos;
+      opos += b.mv_bytes;
+    }
+    if (micro_count(c) > 1) {
+      b.a_off = opos;
       opos += b.mv_bytes;
     }
   }

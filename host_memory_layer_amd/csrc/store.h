@@ -40,6 +40,8 @@ int validate_config(const mt_config& c, std::string* why);
 inline bool bf16_store(const mt_config& c) { return c.store_dtype != MT_F32; }
 inline bool master_store(const mt_config& c) { return c.store_dtype == MT_BF16_MASTER; }
 inline int wbytes(const mt_config& c) { return bf16_store(c) ? 2 : 4; }
+// micro-batches per step (gradient accumulation); 1 = none
+inline int micro_count(const mt_config& c) { return c.micro_batches > 1 ? c.micro_batches : 1; }
 std::vector<mt_block_desc> store_layout(const mt_config& c, uint64_t* dma_bytes, uint64_t* opt_bytes = nullptr);
 
 }  // namespace mt

@@ -72,6 +72,10 @@ typedef struct mt_config {
   int32_t mode;          /* MT_STREAMED, MT_SERIALIZED, MT_RESIDENT or MT_SINGLE_SLOT */
   int32_t host_threads;  /* Adam worker threads; 0 = every core in the affinity mask */
   int32_t flags;         /* MT_FLAG_* bits */
+  int32_t micro_batches; /* gradient accumulation: mt_train_step takes micro_batches * batch * seq_len
+                            tokens, runs one forward and backward sweep per micro-batch of `batch`
+                            sequences, sums the gradients in an fp32 accumulator on the host and
+                            applies one Adam step to the mean over all micro-batches.  0 or 1: none */
 } mt_config;
 
 #define MT_FLAG_TIME_KERNELS 1  /* bracket every GEMM and attention launch with events */
@@ -92,15 +96,18 @@ typedef struct mt_tensor_desc {
  *   - the DMA part (pinned, hipHostMalloc): a 4 KiB header page, then per
  *     block [W | G] — the only state that crosses the host link, one burst
  *     per region;
- *   - the optimizer part (pageable host memory): per block [m | v], or
- *     [m | v | P] with MT_BF16_MASTER (P: the fp32 master weights), read and
- *     written only by the host Adam.
+ *   - the optimizer part (pageable host memory): per block [m | v], then
+ *     P (the fp32 master weights) with MT_BF16_MASTER, then A (the fp32
+ *     gradient accumulator) with micro_batches > 1; read and written only by
+ *     the host.
  * Every region and tensor start is 4 KiB-aligned and each block's regions
  * are contiguous inside their part.  base, w_off, g_off are byte offsets in
- * the DMA part; m_off, v_off, p_off byte offsets in the optimizer part
- * (p_off is 0 without a master copy).  Region element counts are equal for
- * all regions; W and G hold wb-byte elements (2 for bf16, 4 for f32), m, v
- * and P hold float32.
+ * the DMA part; m_off, v_off, p_off, a_off byte offsets in the optimizer
+ * part (p_off, a_off are 0 when the region does not exist).  Region element
+ * counts are equal for all regions; W and G hold wb-byte elements (2 for
+ * bf16, 4 for f32), m, v, P and A hold float32.  After a step with
+ * micro-batches, A holds the summed gradient that Adam used and G the last
+ * micro-batch's gradient.
  * Tensor order — embed: E [V x d]; layer: Wqkv [3d x d] (q, k, v rows),
  * Wo [d x d], Wgu [2F x d] (gate rows then up rows), Wd [d x F],
  * attn_norm [1 x d], ffn_norm [1 x d]; head: Wh [V x d], final_norm [1 x d]. */
@@ -110,11 +117,13 @@ typedef struct mt_block_desc {
   uint64_t region_elems;
   uint64_t w_bytes, mv_bytes;
   mt_tensor_desc tensors[MT_MAX_TENSORS];
-  uint64_t p_off;
+  uint64_t p_off, a_off;
 } mt_block_desc;
 
 /* Step statistics (milliseconds unless named otherwise); filled by
- * mt_train_step, read by mt_get_stats. */
+ * mt_train_step, read by mt_get_stats.  With micro-batches, step_ms,
+ * adam_ms, adam_tail_ms and loss cover the whole step and the other fields
+ * (and mt_block_stats) the last micro-batch's sweep. */
 typedef struct mt_stats {
   double step_ms;            /* wall time of the last mt_train_step */
   double device_ms;          /* compute-stream events: step start to the end of the last offload */
@@ -202,8 +211,9 @@ int mt_create_model(const mt_config* cfg, void* dev_arena, size_t arena_bytes, v
  * mt_host_opt_bytes, 4 KiB alignment, header magic and shape; the DMA part
  * must be pinned. */
 int mt_bind_host_store(void* model, void* dma_base, size_t dma_bytes, void* opt_base, size_t opt_bytes);
-/* One training step on tokens (host int32 [batch*seq_len], values in
- * [0, vocab)).  Synchronous: on return 0 the store holds the post-Adam W, m,
+/* One training step on tokens (host int32 [micro_batches*batch*seq_len], or
+ * [batch*seq_len] without micro-batches, values in [0, vocab)).  The loss is
+ * the mean next-token loss over all micro-batches.  Synchronous: on return 0 the store holds the post-Adam W, m,
  * v, this step's G, and t+1 in the header.  On MT_E_NONFINITE no Adam ran. */
 int mt_train_step(void* model, const int32_t* tokens);
 /* Loss of the last completed step. */

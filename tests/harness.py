@@ -8,8 +8,8 @@ import datagen
 import host_memory_layer_amd as mt
 
 
-def make_store(shape, mode="streamed", flags=0, host_threads=0):
-    cfg = mt.make_config(shape, mode=mode, flags=flags, host_threads=host_threads)
+def make_store(shape, mode="streamed", flags=0, host_threads=0, micro_batches=1):
+    cfg = mt.make_config(shape, mode=mode, flags=flags, host_threads=host_threads, micro_batches=micro_batches)
     store = mt.HostStore(cfg)
     mt.init_store_weights(store, datagen.store_filler(shape))
     return cfg, store

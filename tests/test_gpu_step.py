@@ -10,7 +10,7 @@ import pytest
 
 import datagen
 import host_memory_layer_amd as mt
-from oracle import Oracle
+from oracle import Oracle, adam_update
 from tests.harness import W_RTOL, assert_parity, frob_rel, make_store, read_all
 
 pytestmark = pytest.mark.gpu
@@ -27,15 +27,17 @@ def need_gpu():
         pytest.skip("no GPU")
 
 
-def run_step(shape, mode="streamed", flags=0, steps=1):
-    cfg, store = make_store(shape, mode, flags=flags)
+def run_step(shape, mode="streamed", flags=0, steps=1, micro_batches=1, tok=None):
+    cfg, store = make_store(shape, mode, flags=flags, micro_batches=micro_batches)
     model = mt.Model(cfg, store, "cuda:0")
-    tok = datagen.tokens(shape)
+    tok = datagen.tokens(shape) if tok is None else tok
     losses = [model.step(tok) for _ in range(steps)]
     out = dict(loss=losses[-1], losses=losses, g=read_all(store, "g"), w=read_all(store, "w"),
                m=read_all(store, "m"), v=read_all(store, "v"), stats=model.stats(), t=store.step_count())
     if shape.store_dtype == datagen.BF16_MASTER:
         out["p"] = read_all(store, "p")
+    if micro_batches > 1:
+        out["a"] = read_all(store, "a")
     model.close()
     store.free()
     return out
@@ -123,6 +125,42 @@ def test_fp32_master_store_matches_oracle():
         assert np.array_equal(datagen.f32_to_bf16_bits(two["p"][k]), datagen.f32_to_bf16_bits(two["w"][k])), k
     # the master keeps what bf16 rounding drops: it is not its own rounding
     assert any(not np.array_equal(two["p"][k], two["w"][k]) for k in two["p"])
+
+
+@pytest.mark.parametrize("shape", [datagen.PRESETS["tiny"], SMALL_BF16], ids=["tiny-f32", "small-bf16"])
+def test_micro_batches_accumulate_the_batch_gradient(shape):
+    """Two micro-batches of one sequence each against the whole batch of two.
+
+    Exact: the loss scale of a micro-batch is 1/(2*(T-1)), half that of a
+    lone sequence, and halving commutes with every rounding, so the
+    accumulator equals (g0 + g1)/2 of two single-sequence runs bit for bit,
+    the loss is (l0 + l1)/2, and the update is the oracle's float32 Adam on
+    that accumulator.  Against the oracle's step on the whole batch: the
+    parity bars.  Streamed and resident schedules agree bit for bit."""
+    need_gpu()
+    print(f"micro-batches {shape.name}", flush=True)
+    tok = datagen.tokens(shape)
+    one = shape.replace(batch=1)
+    r = run_step(one, micro_batches=2, tok=tok)
+    s0 = run_step(one, tok=tok[0:1])
+    s1 = run_step(one, tok=tok[1:2])
+    assert r["loss"] == np.float32(0.5 * np.float64(s0["loss"]) + 0.5 * np.float64(s1["loss"]))
+    P0 = datagen.init_params(one)
+    for k in r["a"]:
+        a = (s0["g"][k] + s1["g"][k]) * np.float32(0.5)
+        assert np.array_equal(r["a"][k], a), k
+        w2, m2, v2 = adam_update(P0[k], a, np.zeros_like(a), np.zeros_like(a), 1, shape.lr, shape.beta1,
+                                 shape.beta2, shape.adam_eps)
+        if shape.store_dtype != datagen.F32:
+            w2 = datagen.bf16_bits_to_f32(datagen.f32_to_bf16_bits(w2))
+        assert np.array_equal(r["w"][k], w2) and np.array_equal(r["m"][k], m2) and np.array_equal(r["v"][k], v2), k
+    o_loss, o_g, o_w = oracle_step(shape)
+    assert_parity(r["loss"], r["a"], r["w"], o_loss, o_g, o_w)
+    res = run_step(one, "resident", micro_batches=2, tok=tok)
+    assert res["loss"] == r["loss"]
+    for key in "awmv":
+        for k in r[key]:
+            assert np.array_equal(res[key][k], r[key][k]), (key, k)
 
 
 @pytest.mark.parametrize("shape,resume_mode", [(datagen.PRESETS["tiny"], "streamed"), (SMALL_BF16, "single_slot"),

@@ -34,9 +34,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_sizes_match_header():
     # layout of the C structs, mirrored by ctypes
-    assert ctypes.sizeof(mt.MtConfig) == 9 * 4 + 4 + 6 * 8 + 3 * 4 + 4
+    assert ctypes.sizeof(mt.MtConfig) == 9 * 4 + 4 + 6 * 8 + 4 * 4
     assert ctypes.sizeof(mt.MtTensorDesc) == 16
-    assert ctypes.sizeof(mt.MtBlockDesc) == 16 + 8 * 8 + 8 * 16 + 8
+    assert ctypes.sizeof(mt.MtBlockDesc) == 16 + 8 * 8 + 8 * 16 + 2 * 8
     assert ctypes.sizeof(mt.MtStats) == 15 * 8 + 2 * 8 + 8 + 2 * 4 + 8
 
 
@@ -108,6 +108,26 @@ def test_store_sizes_with_fp32_master():
     assert abs((mt.host_store_bytes(cfg) + mt.host_opt_bytes(cfg)) / 1e9 - 186.64 * 16 / 12) < 0.1
 
 
+@pytest.mark.parametrize("name,dtype", [("1.3b", datagen.BF16), ("1.3b", datagen.BF16_MASTER), ("tiny", datagen.F32)])
+def test_store_layout_with_gradient_accumulator(name, dtype):
+    """micro_batches > 1 adds an fp32 accumulator A after m, v (and P) of
+    every block in the pageable part; the pinned part is unchanged."""
+    shape = datagen.PRESETS[name].replace(store_dtype=dtype)
+    base = mt.make_config(shape)
+    cfg = mt.make_config(shape, micro_batches=4)
+    assert mt.host_store_bytes(cfg) == mt.host_store_bytes(base)
+    regions = 3 if dtype == datagen.BF16_MASTER else 2
+    assert mt.host_opt_bytes(cfg) * regions == mt.host_opt_bytes(base) * (regions + 1)
+    prev = 0
+    for b in mt.block_infos(cfg):
+        assert b.m_off == prev and b.a_off % 4096 == 0
+        last = b.p_off if dtype == datagen.BF16_MASTER else b.v_off
+        assert b.a_off == last + b.mv_bytes
+        prev = b.a_off + b.mv_bytes
+    assert prev == mt.host_opt_bytes(cfg)
+    assert all(b.a_off == 0 for b in mt.block_infos(mt.make_config(shape, micro_batches=1)))
+
+
 def test_config_validation():
     shape = datagen.PRESETS["tiny"]
     bad = [shape.replace(n_heads=3), shape.replace(n_layers=0), shape.replace(vocab=1),
@@ -119,6 +139,9 @@ def test_config_validation():
     c.mode = 7
     with pytest.raises(mt.MtError):
         mt.device_bytes(c)
+    for k in (-1, 5000):
+        with pytest.raises(mt.MtError):
+            mt.host_store_bytes(mt.make_config(shape, micro_batches=k))
 
 
 def test_device_bytes_fit_one_gpu():
