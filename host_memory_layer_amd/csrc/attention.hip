@@ -141,19 +141,24 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
   // lds; kilobyte j = wave*4 + i of a tile is written by one instruction, so
   // each lane's source is chosen to land in the swizzled layout the fragment
   // reads expect.  V^T fragments come from the V tile by transposing reads.
-  const i32x4_t krsrc = make_rsrc(qkv + rowbase * ld + d + h * HD, (uint32_t)((int64_t)T * ld * 2));
-  const i32x4_t vrsrc = make_rsrc(qkv + rowbase * ld + 2 * d + h * HD, (uint32_t)((int64_t)T * ld * 2));
+  // Each tile's buffer descriptor starts at the tile's first key row, so the
+  // 32-bit offsets stay within one tile for any sequence length.
+  const uint16_t* kcol = qkv + rowbase * ld + d + h * HD;
+  const uint16_t* vcol = kcol + d;
+  const uint32_t tile_bytes = (uint32_t)(64 * ld * 2);
   auto issue = [&](int kb, int buf) {
     uint8_t* Ks = smem + buf * 32768;
     uint8_t* Vs = Ks + 16384;
-    const int key0 = kb * 64;
+    const int64_t key0 = (int64_t)kb * 64;
+    const i32x4_t krs = make_rsrc(kcol + key0 * ld, tile_bytes);
+    const i32x4_t vrs = make_rsrc(vcol + key0 * ld, tile_bytes);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = wave * 4 + i;
       const int kr = 4 * j + (lane >> 4), kc = (lane & 15) ^ swkey(kr);
-      const int off = (int)((kr * ld + 8 * kc) * 2), soff = (int)((int64_t)key0 * ld * 2);
-      dma16(krsrc, Ks + j * 1024, off, soff);
-      dma16(vrsrc, Vs + j * 1024, off, soff);
+      const int off = (int)((kr * ld + 8 * kc) * 2);
+      dma16(krs, Ks + j * 1024, off, 0);
+      dma16(vrs, Vs + j * 1024, off, 0);
     }
   };
 
@@ -336,21 +341,23 @@ __global__ void __launch_bounds__(256, 2) k_attn_dkdv_bf16(const uint16_t* __res
     *(u32x4_t*)(Vs + sw256(r, ch)) = vv;
   }
 
-  const i32x4_t qrsrc = make_rsrc(qkv + rowbase * ld + h * HD, (uint32_t)((int64_t)T * ld * 2));
-  const i32x4_t orsrc = make_rsrc(dO + rowbase * d + h * HD, (uint32_t)((int64_t)T * d * 2));
   // Each operand tile is 8 KiB = 8 direct-load kilobytes (4 rows of 256 B
   // each): wave w writes kilobytes 2w and 2w+1 of both tiles.  Q^T and dO^T
-  // fragments come from the same tiles by transposing reads.
+  // fragments come from the same tiles by transposing reads.  Descriptors
+  // start at the tile's first query row (32-bit offsets for any length).
+  const uint16_t* qcol = qkv + rowbase * ld + h * HD;
+  const uint16_t* ocol = dO + rowbase * d + h * HD;
   auto issue = [&](int n) {
     uint8_t* st = smem + 65536;
-    const int q0 = n * QT;
+    const int64_t q0 = (int64_t)n * QT;
+    const i32x4_t qrs = make_rsrc(qcol + q0 * ld, (uint32_t)(QT * ld * 2));
+    const i32x4_t ors = make_rsrc(ocol + q0 * d, (uint32_t)(QT * d * 2));
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int j = wave * 2 + i;
       const int r = 4 * j + (lane >> 4), ch = (lane & 15) ^ swkey(r);
-      dma16(qrsrc, st + j * 1024, (int)((r * ld + 8 * ch) * 2),
-                                               (int)((int64_t)q0 * ld * 2));
-      dma16(orsrc, st + TILE + j * 1024, (int)((r * d + 8 * ch) * 2), (int)((int64_t)q0 * d * 2));
+      dma16(qrs, st + j * 1024, (int)((r * ld + 8 * ch) * 2), 0);
+      dma16(ors, st + TILE + j * 1024, (int)((r * d + 8 * ch) * 2), 0);
     }
   };
   // lse and D of the tile's queries in this lane's accumulator rows: rows
@@ -478,21 +485,24 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq_bf16(const uint16_t* __restr
   }
 
   const int nkb = min(T, (qb + 1) * 128) / KB;
-  const i32x4_t krsrc = make_rsrc(qkv + rowbase * ld + d + h * HD, (uint32_t)((int64_t)T * ld * 2));
-  const i32x4_t vrsrc = make_rsrc(qkv + rowbase * ld + 2 * d + h * HD, (uint32_t)((int64_t)T * ld * 2));
   // 8 direct-load kilobytes per tile (4 rows of 256 B each); wave w writes
-  // kilobytes 2w, 2w+1 of each.
+  // kilobytes 2w, 2w+1 of each.  Descriptors start at the tile's first key
+  // row (32-bit offsets for any length).
+  const uint16_t* kcol = qkv + rowbase * ld + d + h * HD;
+  const uint16_t* vcol = kcol + d;
   auto issue = [&](int kb, int buf) {
     uint8_t* Ks = smem + buf * STAGE;
     uint8_t* Vs = Ks + 8192;
-    const int key0 = kb * KB;
+    const int64_t key0 = (int64_t)kb * KB;
+    const i32x4_t krs = make_rsrc(kcol + key0 * ld, (uint32_t)(KB * ld * 2));
+    const i32x4_t vrs = make_rsrc(vcol + key0 * ld, (uint32_t)(KB * ld * 2));
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int j = wave * 2 + i;
       const int r = 4 * j + (lane >> 4), ch = (lane & 15) ^ swkey(r);
-      const int voff = (r * ld + 8 * ch) * 2, soff = (int)((int64_t)key0 * ld * 2);
-      dma16(krsrc, Ks + j * 1024, voff, soff);
-      dma16(vrsrc, Vs + j * 1024, voff, soff);
+      const int voff = (int)((r * ld + 8 * ch) * 2);
+      dma16(krs, Ks + j * 1024, voff, 0);
+      dma16(vrs, Vs + j * 1024, voff, 0);
     }
   };
 

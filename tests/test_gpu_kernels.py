@@ -273,17 +273,19 @@ def test_attention_bf16_14b_head_sampled():
 
 
 # Long context: one layer of the 7B shape (32 heads of 128) over a single
-# 65536-token sequence, so every offset and stride is the real one.  Heads 0
+# sequence of 65536 or 131072 tokens, so every offset and stride is the real
+# one (at 131072 a key row's byte offset inside its head column exceeds 2^31).  Heads 0
 # and 31 (the first and the last column block) carry random data, the others
 # zeros; the oracle evaluates single query rows and the last keys exactly,
 # and two identities cover every key: sum_j dv_j = sum_i dO_i (each
 # probability row sums to 1) and sum_j dk_j = 0 (each dS row sums to 0).
-def test_attention_bf16_long_context_7b_layer():
-    B, T, H, hd = 1, 65536, 32, 128
+@pytest.mark.parametrize("T", [65536, 131072])
+def test_attention_bf16_long_context_7b_layer(T):
+    B, H, hd = 1, 32, 128
     d = H * hd
     live = (0, 31)
     print(f"attention long context T={T} H={H}", flush=True)
-    rng = np.random.default_rng(65536)
+    rng = np.random.default_rng(T)
     qkv = torch.zeros((T, 3 * d), dtype=torch.int16, device=dev())
     dO = torch.zeros((T, d), dtype=torch.int16, device=dev())
     x64, do64 = {}, {}
@@ -314,7 +316,9 @@ def test_attention_bf16_long_context_7b_layer():
     for j in range(3):
         assert not torch.any(dqkvT[j * d + quiet * hd:j * d + (quiet + 1) * hd, :T]).item()
     c64, s64 = rope_tables(T, hd, 10000.0, np.float64)
-    rows = [0, 1, 2, 63, 64, 127, 128, 4095, 4096, 16383, 16384, 32767, 32768, 49151, 65000, 65535]
+    rows = [0, 1, 2, 63, 64, 127, 128, 4095, 4096, 16383, 16384, 32767, 32768, 49151, 65535, 65536, 87381,
+            T - 300, T - 1]
+    rows = sorted(set(r for r in rows if r < T))
     rows += sorted(np.random.default_rng(1).integers(0, T, 16).tolist())
     tail = 128
     for h in live:
