@@ -64,6 +64,27 @@ def flops(shape, n_layers=None):
     return fwd_layer, model, model + L * fwd_layer
 
 
+ADAM_BYTES = {datagen.BF16: 22, datagen.BF16_MASTER: 28, datagen.F32: 28}
+
+
+def host_triad(torch, reps=3):
+    """Host DRAM bandwidth of a STREAM-style triad a = b + s*c (float32, 512 MiB
+    per array, 12 bytes per element counted) on every core of the affinity
+    mask, the threads the host Adam runs on."""
+    n_thr = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    prev = torch.get_num_threads()
+    torch.set_num_threads(n_thr)
+    n = 1 << 27
+    a, b, c = torch.empty(n), torch.ones(n), torch.ones(n)
+    torch.add(b, c, alpha=0.5, out=a)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        torch.add(b, c, alpha=0.5, out=a)
+    dt = (time.perf_counter() - t0) / reps
+    torch.set_num_threads(prev)
+    return {"triad_gbs": 12.0 * n / dt / 1e9, "threads": n_thr}
+
+
 def link_probe(torch, dev, nbytes, reps=4):
     """Pinned host <-> device copy bandwidth (GB/s): H2D, D2H, and both at once."""
     host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
@@ -190,6 +211,8 @@ def main():
     layer_bytes = store.blocks[1].w_bytes
     link = link_probe(torch, dev, layer_bytes)
     log(f"host link: {link}")
+    dram = host_triad(torch)
+    log(f"host DRAM: {dram}")
     tokens = datagen.tokens(shape.replace(batch=K * shape.batch))
     if args.copy_probe:
         # 1 GiB read + 1 GiB written per launch: what FETCH_SIZE / WRITE_SIZE
@@ -285,6 +308,11 @@ def main():
             "link_peak": link,
             "h2d_frac_of_link_peak": h2d_gbs / link["h2d_gbs"] if h2d_gbs else None,
             "stall_ms": last["stall_ms"], "adam_ms": last["adam_ms"], "adam_tail_ms": last["adam_tail_ms"],
+            "host_dram": dram,
+            # bytes the host Adam moves per parameter: bf16 store W, G, m, v in and W, m, v out (22);
+            # fp32 master or fp32 store 28 (gradient accumulation adds more and is not counted here)
+            "adam_gbs": (ADAM_BYTES[shape.store_dtype] * shape.n_params() / (last["adam_ms"] / 1e3) / 1e9
+                         if K == 1 and last["adam_ms"] > 0 else None),
             "per_layer_ms": {"fwd_compute": comp_f, "bwd_compute": comp_b, "h2d_fwd": h2d_f, "h2d_bwd": h2d_b,
                              "d2h": d2h},
             "attention": {"ms_per_step": attn_ms / args.steps,
