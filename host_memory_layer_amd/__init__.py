@@ -33,7 +33,8 @@ class MtConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("n_layers", "d_model", "n_heads", "head_dim", "d_ff", "vocab", "batch", "seq_len", "store_dtype")] + \
                [(n, ctypes.c_double) for n in ("rms_eps", "rope_theta", "lr", "beta1", "beta2", "adam_eps")] + \
-               [(n, ctypes.c_int32) for n in ("mode", "host_threads", "flags", "micro_batches")]
+               [(n, ctypes.c_int32) for n in ("mode", "host_threads", "flags", "micro_batches", "head_chunk_tokens",
+                                              "pad_")]
 
 
 class MtTensorDesc(ctypes.Structure):
@@ -149,7 +150,7 @@ def check(rc):
     return rc
 
 
-def make_config(shape, mode="streamed", host_threads=0, flags=0, micro_batches=1) -> MtConfig:
+def make_config(shape, mode="streamed", host_threads=0, flags=0, micro_batches=1, head_chunk_tokens=0) -> MtConfig:
     """mt_config from any object with the model-shape attributes
     (n_layers, d_model, n_heads, head_dim, d_ff, vocab, batch, seq_len,
     store_dtype 'f32'|'bf16'|'bf16m' (bf16 with an fp32 master copy), rms_eps, rope_theta, lr, beta1, beta2, adam_eps)."""
@@ -163,6 +164,7 @@ def make_config(shape, mode="streamed", host_threads=0, flags=0, micro_batches=1
     c.host_threads = int(host_threads)
     c.flags = int(flags)
     c.micro_batches = int(micro_batches)
+    c.head_chunk_tokens = int(head_chunk_tokens)
     return c
 
 

@@ -482,11 +482,12 @@ void swiglu_bwd(const T* dy, const T* gu, T* dgu, int M, int F, hipStream_t s) {
 // -------------------------------------------------------- cross-entropy --
 template <typename T>
 __global__ void __launch_bounds__(256) k_xent(const float* logits, const int32_t* tok, float* row_loss, T* dl, int T_,
-                                              int V, float inv_n) {
+                                              int V, float inv_n, int64_t row0) {
   __shared__ float red[4];
-  const int64_t m = blockIdx.x;
-  const float* z = logits + m * V;
-  T* out = dl + m * V;
+  // logits and dl hold the rows of one pass; m is the token's row in the batch
+  const int64_t m = row0 + blockIdx.x;
+  const float* z = logits + (int64_t)blockIdx.x * V;
+  T* out = dl + (int64_t)blockIdx.x * V;
   if ((int)(m % T_) == T_ - 1) {
     for (int v = threadIdx.x; v < V; v += 256) out[v] = stf<T>(0.f);
     if (threadIdx.x == 0) row_loss[m] = 0.f;
@@ -509,10 +510,10 @@ __global__ void __launch_bounds__(256) k_xent(const float* logits, const int32_t
 }
 
 template <typename T>
-void xent(const float* logits, const int32_t* tok, float* row_loss, T* dlogits, int M, int T_, int V, float inv_n,
-          hipStream_t s) {
-  if (M <= 0) return;
-  hipLaunchKernelGGL(k_xent<T>, dim3(M), dim3(256), 0, s, logits, tok, row_loss, dlogits, T_, V, inv_n);
+void xent(const float* logits, const int32_t* tok, float* row_loss, T* dlogits, int rows, int64_t row0, int T_, int V,
+          float inv_n, hipStream_t s) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(k_xent<T>, dim3(rows), dim3(256), 0, s, logits, tok, row_loss, dlogits, T_, V, inv_n, row0);
 }
 
 __global__ void __launch_bounds__(1024) k_sum_fixed(const float* x, float* out, int n, float scale) {
@@ -670,7 +671,7 @@ void fill_u32(void* p, uint32_t value, size_t n_words, hipStream_t s) {
   template void rope_bwd_T<T>(T*, int64_t, const float*, const float*, int, int, int, int, hipStream_t);        \
   template void swiglu_fwd<T>(const T*, T*, int, int, hipStream_t);                                             \
   template void swiglu_bwd<T>(const T*, const T*, T*, int, int, hipStream_t);                                   \
-  template void xent<T>(const float*, const int32_t*, float*, T*, int, int, int, float, hipStream_t);           \
+  template void xent<T>(const float*, const int32_t*, float*, T*, int, int64_t, int, int, float, hipStream_t);           \
   template void transpose<T>(const T*, int64_t, T*, int64_t, int, int, hipStream_t);                            \
   template void cast_transpose<T>(const float*, T*, T*, int64_t, int, int, hipStream_t);                       \
   template void cast<T>(const float*, T*, int64_t, hipStream_t);

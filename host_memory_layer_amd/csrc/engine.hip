@@ -71,8 +71,9 @@ struct BwdWs {  // backward workspace (one set)
 
 template <typename T>
 struct HeadWs {
-  T *z, *dlogits, *dlogitsT;
+  T *z, *dlogits, *dlogitsT;       // dlogits, dlogitsT: one pass of HC tokens
   float *rz, *logits, *row_loss, *loss;
+  float* gacc;                     // fp32 sum of the head weight gradient over passes (bf16, several passes)
 };
 
 template <typename T>
@@ -104,6 +105,8 @@ struct Model {
   // no activation or weight is transposed (kmajor: layers, kmajor_head: head)
   bool kmajor = false, kmajor_head = false;
   int E;  // bytes per weight element
+  int HC, n_hc;  // output head: tokens per pass and passes
+  int64_t HCp;   // padded row stride of one pass's transposed buffers
 
   uint8_t* arena = nullptr;
   size_t arena_bytes = 0;
@@ -182,14 +185,15 @@ struct Model {
   }
   template <typename T>
   void carve_head(Carver& c, HeadWs<T>& w) {
-    const uint64_t MV = (uint64_t)M * V;
+    const uint64_t CV = (uint64_t)HC * V;
     w.z = c.take<T>((uint64_t)M * d * E);
-    w.dlogits = c.take<T>(MV * E);
-    w.dlogitsT = kmajor_head ? nullptr : c.take<T>((uint64_t)V * Mp * E);
+    w.dlogits = c.take<T>(CV * E);
+    w.dlogitsT = kmajor_head ? nullptr : c.take<T>((uint64_t)V * HCp * E);
     w.rz = c.take<float>((uint64_t)M * 4);
-    w.logits = c.take<float>(MV * 4);
+    w.logits = c.take<float>(CV * 4);
     w.row_loss = c.take<float>((uint64_t)M * 4);
     w.loss = c.take<float>(256);
+    w.gacc = n_hc > 1 && E == 2 ? c.take<float>((uint64_t)V * d * 4) : nullptr;
   }
 
   template <typename T>
@@ -275,6 +279,17 @@ struct Model {
     M = B * Tq;
     Mp = token_ld(M);
     E = wbytes(c);
+    // Output head passes: all tokens at once unless their logits and logit
+    // gradients would take more than 16 GiB; then passes of at most 4 GiB.
+    const uint64_t head_row = (uint64_t)V * (4 + E);
+    if (c.head_chunk_tokens > 0)
+      HC = std::min(M, c.head_chunk_tokens);
+    else if ((uint64_t)M * head_row <= (16ull << 30))
+      HC = M;
+    else
+      HC = std::min<int64_t>(M, std::max<int64_t>(256, (int64_t)((4ull << 30) / head_row) / 256 * 256));
+    n_hc = (M + HC - 1) / HC;
+    HCp = token_ld(HC);
     if (bf16_store(c)) {
       const int A_ = GEMM_A_KMAJOR, B_ = GEMM_B_KMAJOR;
       auto ok = [&](int m, int n, int k, int64_t lda, int64_t ldb, int lay) {
@@ -283,7 +298,7 @@ struct Model {
       kmajor = ok(d, F, M, d, F, A_ | B_) && ok(M, F, d, d, F, B_) && ok(2 * F, d, M, 2 * F, d, A_ | B_) &&
                ok(M, d, 2 * F, 2 * F, d, B_) && ok(d, d, M, d, d, A_ | B_) && ok(M, d, d, d, d, B_) &&
                ok(3 * d, d, M, Mp, d, B_) && ok(M, d, 3 * d, Mp, d, A_ | B_);
-      kmajor_head = kmajor && ok(V, d, M, V, d, A_ | B_) && ok(M, d, V, V, d, B_);
+      kmajor_head = ok(V, d, HC, V, d, A_ | B_) && ok(HC, d, V, V, d, B_);
     }
     n_uses = 2 * L + 3;
   }
@@ -439,22 +454,36 @@ struct Model {
     // mean over the labelled positions of every micro-batch of the step
     const float inv_n = 1.0f / (float)((int64_t)micro_count(cfg) * B * (Tq - 1));
     rmsnorm_fwd<T>(xL, fin, hw.z, hw.rz, M, d, (float)cfg.rms_eps, sc);
-    gemm<T>(hw.z, d, wh, d, hw.logits, V, nullptr, 0, M, V, d, EPI_F32);
-    xent<T>(hw.logits, d_tok, hw.row_loss, hw.dlogits, M, Tq, V, inv_n, sc);
+    T* whT = (T*)wt;
+    if (!kmajor_head) transpose<T>(wh, d, whT, V, V, d, sc);
+    // One pass per HC tokens: logits, loss rows and logit gradients of the
+    // pass, its share of the head weight gradient, and its rows of dz.  With
+    // several passes the weight gradient is summed in fp32 (in place for an
+    // fp32 store) and rounded once at the end.
+    float* gsum = n_hc == 1 ? nullptr : (E == 2 ? hw.gacc : (float*)gwh);
+    for (int p = 0; p < n_hc; ++p) {
+      const int64_t r0 = (int64_t)p * HC;
+      const int rows = (int)std::min<int64_t>(HC, M - r0);
+      const T* zc = hw.z + r0 * d;
+      gemm<T>(zc, d, wh, d, hw.logits, V, nullptr, 0, rows, V, d, EPI_F32);
+      xent<T>(hw.logits, d_tok, hw.row_loss, hw.dlogits, rows, r0, Tq, V, inv_n, sc);
+      void* gout = gsum ? (void*)gsum : (void*)gwh;
+      const float* R = gsum && p > 0 ? gsum : nullptr;
+      const Epi epi = !gsum ? EPI_STORE : (p > 0 ? EPI_ADD_F32 : EPI_F32);
+      if (kmajor_head) {
+        gemm<T>(hw.dlogits, V, zc, d, gout, d, R, d, V, d, rows, epi, GEMM_A_KMAJOR | GEMM_B_KMAJOR);
+        gemm<T>(hw.dlogits, V, wh, d, ws.dh + r0 * d, d, nullptr, 0, rows, d, V, EPI_F32, GEMM_B_KMAJOR);
+      } else {
+        transpose<T>(hw.dlogits, V, hw.dlogitsT, HCp, rows, V, sc);
+        transpose<T>(zc, d, ws.tmpT, HCp, rows, d, sc);
+        gemm<T>(hw.dlogitsT, HCp, ws.tmpT, HCp, gout, d, R, d, V, d, rows, epi);
+        gemm<T>(hw.dlogits, V, whT, V, ws.dh + r0 * d, d, nullptr, 0, rows, d, V, EPI_F32);
+      }
+    }
+    if (gsum && E == 2) cast<T>(gsum, gwh, (int64_t)V * d, sc);
     sum_fixed(hw.row_loss, hw.loss, M, inv_n, sc);
     MT_HIP(hipMemcpyAsync(h_loss, hw.loss, sizeof(float), hipMemcpyDeviceToHost, sc));
     MT_HIP(hipEventRecord(ev_loss, sc));
-    if (kmajor_head) {
-      gemm<T>(hw.dlogits, V, hw.z, d, gwh, d, nullptr, 0, V, d, M, EPI_STORE, GEMM_A_KMAJOR | GEMM_B_KMAJOR);
-      gemm<T>(hw.dlogits, V, wh, d, ws.dh, d, nullptr, 0, M, d, V, EPI_F32, GEMM_B_KMAJOR);
-    } else {
-      transpose<T>(hw.dlogits, V, hw.dlogitsT, Mp, M, V, sc);
-      transpose<T>(hw.z, d, ws.tmpT, Mp, M, d, sc);
-      gemm<T>(hw.dlogitsT, Mp, ws.tmpT, Mp, gwh, d, nullptr, 0, V, d, M, EPI_STORE);
-      T* whT = (T*)wt;
-      transpose<T>(wh, d, whT, V, V, d, sc);
-      gemm<T>(hw.dlogits, V, whT, V, ws.dh, d, nullptr, 0, M, d, V, EPI_F32);
-    }
     rmsnorm_bwd<T>(ws.dh, xL, fin, hw.rz, nullptr, dx_out, ws.part, gfin, M, d, sc);
   }
 

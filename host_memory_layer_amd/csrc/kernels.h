@@ -61,10 +61,12 @@ template <typename T>
 void swiglu_fwd(const T* gu, T* y, int M, int F, hipStream_t s);
 template <typename T>
 void swiglu_bwd(const T* dy, const T* gu, T* dgu, int M, int F, hipStream_t s);
-// Row-wise loss and gradient of the mean next-token cross-entropy:
+// Row-wise loss and gradient of the mean next-token cross-entropy over the
+// token rows m = row0 .. row0+rows-1 (logits and dlogits hold those rows):
 // rows with t = m mod T < T-1 have label tok[m+1]; others get loss 0, grad 0.
+// row_loss is indexed by m.
 template <typename T>
-void xent(const float* logits, const int32_t* tok, float* row_loss, T* dlogits, int M, int T_, int V,
+void xent(const float* logits, const int32_t* tok, float* row_loss, T* dlogits, int rows, int64_t row0, int T_, int V,
           float inv_n, hipStream_t s);
 // out[0] = (sum of x[0..n) in a fixed order) * scale.
 void sum_fixed(const float* x, float* out, int n, float scale, hipStream_t s);

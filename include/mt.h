@@ -76,6 +76,12 @@ typedef struct mt_config {
                             tokens, runs one forward and backward sweep per micro-batch of `batch`
                             sequences, sums the gradients in an fp32 accumulator on the host and
                             applies one Adam step to the mean over all micro-batches.  0 or 1: none */
+  int32_t head_chunk_tokens; /* tokens per pass of the output head (logits, loss, head backward): the
+                                logits of that many tokens are held at once and the head's weight
+                                gradient is summed over the passes in fp32.  0: automatic (one pass
+                                while batch*seq_len*vocab*(4 + weight bytes) <= 16 GiB, else passes of
+                                at most 4 GiB) */
+  int32_t pad_;
 } mt_config;
 
 #define MT_FLAG_TIME_KERNELS 1  /* bracket every GEMM and attention launch with events */

@@ -27,8 +27,8 @@ def need_gpu():
         pytest.skip("no GPU")
 
 
-def run_step(shape, mode="streamed", flags=0, steps=1, micro_batches=1, tok=None):
-    cfg, store = make_store(shape, mode, flags=flags, micro_batches=micro_batches)
+def run_step(shape, mode="streamed", flags=0, steps=1, micro_batches=1, tok=None, head_chunk_tokens=0):
+    cfg, store = make_store(shape, mode, flags=flags, micro_batches=micro_batches, head_chunk_tokens=head_chunk_tokens)
     model = mt.Model(cfg, store, "cuda:0")
     tok = datagen.tokens(shape) if tok is None else tok
     losses = [model.step(tok) for _ in range(steps)]
@@ -159,6 +159,35 @@ def test_micro_batches_accumulate_the_batch_gradient(shape):
     res = run_step(one, "resident", micro_batches=2, tok=tok)
     assert res["loss"] == r["loss"]
     for key in "awmv":
+        for k in r[key]:
+            assert np.array_equal(res[key][k], r[key][k]), (key, k)
+
+
+@pytest.mark.parametrize("shape,chunk", [(datagen.PRESETS["tiny"], 48), (SMALL_BF16, 96)],
+                         ids=["tiny-f32", "small-bf16"])
+def test_head_in_passes(shape, chunk):
+    """The output head in passes of `chunk` tokens (the last one ragged).
+    Each token's logits, loss and logit gradients, and so dz and every
+    gradient below the head, do not depend on the pass: bit for bit equal to
+    the single pass.  The head weight gradient is summed over the passes in
+    fp32, so it differs by rounding only.  Parity with the oracle and across
+    schedules holds as for the single pass."""
+    need_gpu()
+    print(f"head passes {shape.name} chunk {chunk}", flush=True)
+    one = run_step(shape)
+    r = run_step(shape, head_chunk_tokens=chunk)
+    assert r["loss"] == one["loss"]
+    for k in r["g"]:
+        if k == "wh":
+            from tests.harness import cosine, maxnorm_rel
+            assert cosine(r["g"][k], one["g"][k]) > 0.99999 and maxnorm_rel(r["g"][k], one["g"][k]) < 1e-2
+        else:
+            assert np.array_equal(r["g"][k], one["g"][k]), k
+    o_loss, o_g, o_w = oracle_step(shape)
+    assert_parity(r["loss"], r["g"], r["w"], o_loss, o_g, o_w)
+    res = run_step(shape, "resident", head_chunk_tokens=chunk)
+    assert res["loss"] == r["loss"]
+    for key in "gwmv":
         for k in r[key]:
             assert np.array_equal(res[key][k], r[key][k]), (key, k)
 

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_sizes_match_header():
     # layout of the C structs, mirrored by ctypes
-    assert ctypes.sizeof(mt.MtConfig) == 9 * 4 + 4 + 6 * 8 + 4 * 4
+    assert ctypes.sizeof(mt.MtConfig) == 9 * 4 + 4 + 6 * 8 + 6 * 4
     assert ctypes.sizeof(mt.MtTensorDesc) == 16
     assert ctypes.sizeof(mt.MtBlockDesc) == 16 + 8 * 8 + 8 * 16 + 2 * 8
     assert ctypes.sizeof(mt.MtStats) == 15 * 8 + 2 * 8 + 8 + 2 * 4 + 8
