@@ -127,7 +127,8 @@ def test_fp32_master_store_matches_oracle():
     assert any(not np.array_equal(two["p"][k], two["w"][k]) for k in two["p"])
 
 
-@pytest.mark.parametrize("shape", [datagen.PRESETS["tiny"], SMALL_BF16], ids=["tiny-f32", "small-bf16"])
+@pytest.mark.parametrize("shape", [datagen.PRESETS["tiny"], SMALL_BF16, SMALL_MASTER],
+                         ids=["tiny-f32", "small-bf16", "small-bf16m"])
 def test_micro_batches_accumulate_the_batch_gradient(shape):
     """Two micro-batches of one sequence each against the whole batch of two.
 
@@ -151,6 +152,8 @@ def test_micro_batches_accumulate_the_batch_gradient(shape):
         assert np.array_equal(r["a"][k], a), k
         w2, m2, v2 = adam_update(P0[k], a, np.zeros_like(a), np.zeros_like(a), 1, shape.lr, shape.beta1,
                                  shape.beta2, shape.adam_eps)
+        if shape.store_dtype == datagen.BF16_MASTER:
+            assert np.array_equal(r["p"][k], w2), k
         if shape.store_dtype != datagen.F32:
             w2 = datagen.bf16_bits_to_f32(datagen.f32_to_bf16_bits(w2))
         assert np.array_equal(r["w"][k], w2) and np.array_equal(r["m"][k], m2) and np.array_equal(r["v"][k], v2), k
