@@ -18,6 +18,9 @@ that hold at any size.
   - embedding-gradient rows of tokens that do not occur are exactly zero.
 * The streamed, serialized, resident and single-slot schedules agree bit for
   bit at the 14B and 120B per-layer shapes with 2 layers.
+* Long context: the 7B width with 2 layers over one 131072-token sequence,
+  whose output head runs in passes of 22272 tokens: the same checks, with
+  head positions on both sides of every pass boundary.
 """
 import gc
 from concurrent.futures import ThreadPoolExecutor
@@ -224,6 +227,25 @@ def test_fullsize_sampled_outputs_and_properties(shape):
             check_layer_prefix(r, L - 1, shape.batch - 1, 512, ex)
             positions = [0, 1, T - 2, T - 1, T, 2 * T - 1, 3 * T // 2 + 5, shape.batch * T - 2, shape.batch * T - 1]
             check_head_rows(r, positions, ex)
+            check_adam_relation(r, ex)
+        check_embedding_rows(r)
+    finally:
+        r.close()
+
+
+def test_long_context_7b_width_two_layers():
+    shape = P7.replace(n_layers=2, batch=1, seq_len=131072)
+    T = shape.seq_len
+    print(f"{shape.name} long context: 2 layers, d {shape.d_model}, 1x{T} tokens", flush=True)
+    r = Run(shape)
+    try:
+        with pool() as ex:
+            check_layer_prefix(r, 0, 0, 4096, ex)
+            check_layer_prefix(r, 1, 0, 512, ex)
+            hc = 22272  # head pass: the largest multiple of 256 tokens within 4 GiB of logits and gradients
+            assert hc * shape.vocab * 6 <= 4 << 30 < (hc + 256) * shape.vocab * 6
+            edges = [p * hc + e for p in range(1, T // hc + 1) for e in (-1, 0) if p * hc + e < T]
+            check_head_rows(r, [0, 1] + edges + [T - 2, T - 1], ex)
             check_adam_relation(r, ex)
         check_embedding_rows(r)
     finally:
