@@ -406,11 +406,14 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_tile(const uint16_t* __res
       // whose 4 columns lie past N aim beyond the descriptor
       const int c0 = 4 * (lane >> 5);
       const int ncol = (int)min<int64_t>(BN, N - n0) - wn;  // valid columns of the sub-tile
-      // EPI_ADD_F32: the residual of 32 x 32 block q = 4i + j is loaded one
-      // block ahead.  Vector memory operations complete in issue order, so
-      // waiting for block q leaves block q+1's loads and block q-1's stores
-      // in flight: at most 8.
-      u32x4_t rv[2][4];
+      // EPI_ADD_F32: the residual of 32 x 32 block q = 4i + j is loaded
+      // RLA = 3 blocks ahead, so a block's loads have three blocks of stores
+      // to land.  Vector memory operations complete in issue order: block q
+      // has landed once no more than the 4-instruction groups issued after
+      // it are in flight, i.e. the loads of blocks q+1 .. min(q+3, 15) and
+      // the stores of blocks max(0, q-3) .. q-1.
+      constexpr int RLA = 3;
+      u32x4_t rv[RLA + 1][4];
       auto load_res = [&](int q) {
         const int row = wm + 32 * (q >> 2) + (lane & 31);
         const int rbase = row * (int)ldr + (int)(n0 + wn) + c0;
@@ -418,12 +421,13 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_tile(const uint16_t* __res
         for (int g = 0; g < 4; ++g) {
           const int col = 32 * (q & 3) + 8 * g;
           const int off = col + c0 < ncol ? (rbase + col) * 4 : 0x7FFFFFF0;
-          rv[q & 1][g] = __builtin_amdgcn_raw_buffer_load_b128(rrs, off, 0, 0);
+          rv[q % (RLA + 1)][g] = __builtin_amdgcn_raw_buffer_load_b128(rrs, off, 0, 0);
         }
       };
       if (EPI == EPI_ADD_F32) {
         __builtin_amdgcn_sched_barrier(0);
-        load_res(0);
+#pragma unroll
+        for (int q = 0; q < RLA; ++q) load_res(q);
       }
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
@@ -432,14 +436,14 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_tile(const uint16_t* __res
         const int cbase = row * (int)ldc + (int)(n0 + wn) + c0;
         if (EPI == EPI_ADD_F32) {
           __builtin_amdgcn_sched_barrier(0);
-          if (q + 1 < 16) {
-            load_res(q + 1);
-            if (q == 0)
-              asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-            else
-              asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-          } else {
-            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+          if (q + RLA < 16) load_res(q + RLA);
+          // groups in flight after block q's loads (q is a constant once unrolled)
+          const int after = (min(q + RLA, 15) - q) + min(q, RLA);
+          switch (after) {
+            case 3: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+            case 4: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+            case 5: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+            default: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -456,7 +460,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_tile(const uint16_t* __res
           } else {
             float o0 = v[4 * g], o1 = v[4 * g + 1], o2 = v[4 * g + 2], o3 = v[4 * g + 3];
             if (EPI == EPI_ADD_F32) {
-              const u32x4_t r = rv[q & 1][g];
+              const u32x4_t r = rv[q % (RLA + 1)][g];
               o0 = __uint_as_float(r.x) + o0;
               o1 = __uint_as_float(r.y) + o1;
               o2 = __uint_as_float(r.z) + o2;
