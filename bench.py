@@ -52,6 +52,39 @@ def gemm_traffic(shape_name, layers):
 PEAK_HBM_GBS = 8000.0
 
 
+def retained_variant(torch, mt, dev, shape, flags, K, store, tokens, warmup, steps, model_flops_step):
+    """The same step with the forward intermediates of as many layers as fit
+    in HBM kept on the device, so that their backward skips the recompute
+    (results bit for bit those of the full recompute).  Runs on the same
+    store after the main measurement."""
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
+    free = torch.cuda.mem_get_info(dev)[0]
+    base = mt.device_bytes(mt.make_config(shape, flags=flags, micro_batches=K))
+    per = mt.device_bytes(mt.make_config(shape, flags=flags, micro_batches=K, retain_layers=1)) - base
+    R = int(max(0, min(shape.n_layers, (free - base - (8 << 30)) // per)))
+    if R == 0:
+        return None
+    model = mt.Model(mt.make_config(shape, flags=flags, micro_batches=K, retain_layers=R), store, "cuda:0")
+    try:
+        for _ in range(warmup):
+            model.step(tokens)
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            model.step(tokens)
+            st = model.stats()
+        torch.cuda.synchronize(dev)
+        elapsed = time.perf_counter() - t0
+    finally:
+        model.close()
+    log(f"retained variant: {R} layers, {elapsed / steps * 1e3:.0f} ms per step")
+    return {"retain_layers": R, "arena_gb": (base + R * per) / 1e9, "ms_per_step": elapsed / steps * 1e3,
+            "model_tflops": model_flops_step * steps / elapsed / 1e12, "stall_ms": st["stall_ms"],
+            "gemm_tflops": st["gemm_flops"] / (st["gemm_ms"] / 1e3) / 1e12 if st["gemm_ms"] > 0 else None}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -172,6 +205,12 @@ def main():
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--duplex-link", action="store_true",
                     help="let prefetches and offloads use the host link at the same time")
+    ap.add_argument("--retain-layers", default="0",
+                    help="layers that keep their forward intermediates on the device, so that their backward "
+                         "skips the recompute (bit-identical results): a count, or 'auto' for as many as fit in "
+                         "HBM; 0 (default) recomputes every layer from its layer-boundary checkpoint")
+    ap.add_argument("--no-retained-variant", action="store_true",
+                    help="skip the second measurement, with as many layers' intermediates kept on the device as fit")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain 1 GiB device copy kernel first (the reference for HBM byte counters)")
     args = ap.parse_args()
@@ -198,6 +237,20 @@ def main():
         flags |= mt.MT_FLAG_DUPLEX_LINK
     K = max(1, args.micro_batches)
     cfg = mt.make_config(shape, mode=args.mode, flags=flags, micro_batches=K)
+    R = 0
+    if args.retain_layers == "auto":
+        # as many sets of one layer's intermediates as fit beside the arena,
+        # with 8 GiB left for the runtime and torch
+        free = torch.cuda.mem_get_info(dev)[0]
+        base = mt.device_bytes(cfg)
+        per = mt.device_bytes(mt.make_config(shape, mode=args.mode, flags=flags, micro_batches=K,
+                                             retain_layers=1)) - base
+        R = int(max(0, min(shape.n_layers, (free - base - (8 << 30)) // per)))
+    elif int(args.retain_layers):
+        R = int(args.retain_layers)
+    if R:
+        cfg = mt.make_config(shape, mode=args.mode, flags=flags, micro_batches=K, retain_layers=R)
+        log(f"retaining the forward intermediates of {R} of {shape.n_layers} layers on the device")
 
     t0 = time.perf_counter()
     store = mt.HostStore(cfg)
@@ -250,6 +303,7 @@ def main():
     elapsed = time.perf_counter() - t0
 
     fwd_layer, model_flops, hw_flops = flops(shape)
+    hw_flops -= R * fwd_layer  # retained layers skip their recompute
     value = K * model_flops * args.steps / elapsed / 1e12
     last = st_acc[-1]
     L = shape.n_layers
@@ -294,13 +348,15 @@ def main():
         "config": {"workload": f"{shape.name}-shape decoder: {L} layers, d {shape.d_model}, "
                                f"{shape.n_heads}x{shape.head_dim} heads, SwiGLU {shape.d_ff}, vocab {shape.vocab}; "
                                f"batch {shape.batch} x seq {shape.seq_len}"
-                               f"{f' x {K} micro-batches' if K > 1 else ''}; {args.mode} from the host store "
+                               f"{f' x {K} micro-batches' if K > 1 else ''}; {args.mode} from the host store"
+                               f"{f', forward intermediates of {R} layers kept on the device' if R else ''} "
                                f"({store.nbytes / 1e9:.1f} GB pinned W/G + {store.opt_nbytes / 1e9:.1f} GB "
                                f"Adam m/v{' + fp32 master W' if args.fp32_master else ''})",
                    "global_batch": K * shape.batch, "seq_len": shape.seq_len, "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": {
+            "retain_layers": R,
             "model_flops_per_step": K * model_flops, "hw_flops_per_step": K * hw_flops,
             "hw_tflops": K * hw_flops * args.steps / elapsed / 1e12,
             "device_ms": last["device_ms"], "step_ms": last["step_ms"], "loss": loss,
@@ -320,6 +376,9 @@ def main():
         },
     }
     model.close()
+    if R == 0 and args.mode == "streamed" and not args.no_retained_variant and not args.copy_probe:
+        out["detail"]["retained_variant"] = retained_variant(torch, mt, dev, shape, flags, K, store, tokens,
+                                                             args.warmup, args.steps, K * model_flops)
     store.free()
     print(json.dumps(out), flush=True)
 

@@ -34,7 +34,7 @@ class MtConfig(ctypes.Structure):
                 ("n_layers", "d_model", "n_heads", "head_dim", "d_ff", "vocab", "batch", "seq_len", "store_dtype")] + \
                [(n, ctypes.c_double) for n in ("rms_eps", "rope_theta", "lr", "beta1", "beta2", "adam_eps")] + \
                [(n, ctypes.c_int32) for n in ("mode", "host_threads", "flags", "micro_batches", "head_chunk_tokens",
-                                              "pad_")]
+                                              "retain_layers")]
 
 
 class MtTensorDesc(ctypes.Structure):
@@ -150,7 +150,8 @@ def check(rc):
     return rc
 
 
-def make_config(shape, mode="streamed", host_threads=0, flags=0, micro_batches=1, head_chunk_tokens=0) -> MtConfig:
+def make_config(shape, mode="streamed", host_threads=0, flags=0, micro_batches=1, head_chunk_tokens=0,
+                retain_layers=0) -> MtConfig:
     """mt_config from any object with the model-shape attributes
     (n_layers, d_model, n_heads, head_dim, d_ff, vocab, batch, seq_len,
     store_dtype 'f32'|'bf16'|'bf16m' (bf16 with an fp32 master copy), rms_eps, rope_theta, lr, beta1, beta2, adam_eps)."""
@@ -165,6 +166,7 @@ def make_config(shape, mode="streamed", host_threads=0, flags=0, micro_batches=1
     c.flags = int(flags)
     c.micro_batches = int(micro_batches)
     c.head_chunk_tokens = int(head_chunk_tokens)
+    c.retain_layers = int(retain_layers)
     return c
 
 
@@ -366,9 +368,11 @@ class Model:
         return self._arena_view(p.value, c.batch * c.seq_len, self.torch.float32)
 
     def close(self):
+        """Destroy the model and drop its reference to the device arena."""
         if getattr(self, "handle", None):
             lib().mt_destroy_model(self.handle)
             self.handle = None
+        self.arena = None
 
     def __del__(self):
         try:

@@ -218,7 +218,9 @@ struct Model {
     d_tok = c.take<int32_t>((uint64_t)M * 4);
     d_order = c.take<int32_t>((uint64_t)M * 4);
     d_seg = c.take<int32_t>((uint64_t)(V + 1) * 4);
-    const int nacts = cfg.mode == MT_RESIDENT ? L : 1;
+    // MT_RESIDENT: every layer's intermediates; otherwise one set per
+    // retained layer plus the set the other layers share
+    const int nacts = cfg.mode == MT_RESIDENT ? L : cfg.retain_layers + 1;
     acts_mem.assign(nacts, nullptr);
     for (int i = 0; i < nacts; ++i) {
       uint64_t start = round_up(c.off, 256);
@@ -241,9 +243,11 @@ struct Model {
     }
     return c.off;
   }
+  // Layers whose forward intermediates stay on the device until their backward.
+  bool retained(int layer) const { return cfg.mode != MT_RESIDENT && layer < cfg.retain_layers; }
   template <typename T>
   Acts<T> acts(int layer) {
-    Carver c{acts_mem[cfg.mode == MT_RESIDENT ? layer : 0]};
+    Carver c{acts_mem[cfg.mode == MT_RESIDENT || retained(layer) ? layer : cfg.retain_layers]};
     Acts<T> a;
     carve_acts(c, a);
     return a;
@@ -510,7 +514,7 @@ struct Model {
       t = LayerWT<T>{(T*)wt, (T*)wt + (uint64_t)3 * d * d, (T*)wt + (uint64_t)4 * d * d,
                      (T*)wt + (uint64_t)4 * d * d + (uint64_t)2 * F * d};
     Acts<T> a = acts<T>(l);
-    if (cfg.mode != MT_RESIDENT) layer_fwd<T>(w, x_ckpt(l), a, nullptr, false);  // recompute
+    if (cfg.mode != MT_RESIDENT && !retained(l)) layer_fwd<T>(w, x_ckpt(l), a, nullptr, false);  // recompute
     if (!kmajor) weight_transposes<T>(w, t);
     layer_bwd<T>(w, t, x_ckpt(l), a, dx_in, dx_out, g);
   }

@@ -81,7 +81,13 @@ typedef struct mt_config {
                                 gradient is summed over the passes in fp32.  0: automatic (one pass
                                 while batch*seq_len*vocab*(4 + weight bytes) <= 16 GiB, else passes of
                                 at most 4 GiB) */
-  int32_t pad_;
+  int32_t retain_layers; /* layers 0 .. retain_layers-1 keep their forward intermediates on the
+                            device until their backward, which then skips the recompute: every
+                            result is bit for bit that of the full recompute, the device arena
+                            grows by one layer's intermediates per retained layer (about 5.4 GB at
+                            d 5120, F 13824, 32768 tokens).  0: recompute every layer (the default:
+                            layer-boundary checkpoints only).  Ignored by MT_RESIDENT, which keeps
+                            every layer's */
 } mt_config;
 
 #define MT_FLAG_TIME_KERNELS 1  /* bracket every GEMM and attention launch with events */

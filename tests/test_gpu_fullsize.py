@@ -52,9 +52,9 @@ class Run:
     """One GPU training step on a fresh store; keeps model and store alive
     until close() so that checkpoints and the store can be read."""
 
-    def __init__(self, shape, mode="streamed", flags=0):
+    def __init__(self, shape, mode="streamed", flags=0, retain_layers=0):
         self.shape = shape
-        self.cfg, self.store = make_store(shape, mode, flags=flags)
+        self.cfg, self.store = make_store(shape, mode, flags=flags, retain_layers=retain_layers)
         self.model = mt.Model(self.cfg, self.store, "cuda:0")
         self.tok = datagen.tokens(shape)
         self.loss = self.model.step(self.tok)
@@ -255,12 +255,13 @@ def test_long_context_7b_width_two_layers():
 @pytest.mark.parametrize("shape", [P14.replace(n_layers=2), P120_L2], ids=["14b-2layers", "120b-2layers"])
 def test_fullsize_schedules_bitwise_equal(shape):
     need_gpu()
-    print(f"{shape.name} with {shape.n_layers} layers: streamed vs serialized vs resident vs single slot", flush=True)
+    print(f"{shape.name} with {shape.n_layers} layers: streamed vs serialized vs resident vs single slot "
+          "vs streamed with layer 0's intermediates retained", flush=True)
     ref = Run(shape, "streamed")
     try:
         ref.drop_model()
-        for mode in ("serialized", "resident", "single_slot"):
-            r = Run(shape, mode)
+        for mode, retain in (("serialized", 0), ("resident", 0), ("single_slot", 0), ("streamed", 1)):
+            r = Run(shape, mode, retain_layers=retain)
             try:
                 assert r.loss == ref.loss, mode
                 for b in range(len(ref.store.blocks)):

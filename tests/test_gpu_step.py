@@ -27,8 +27,10 @@ def need_gpu():
         pytest.skip("no GPU")
 
 
-def run_step(shape, mode="streamed", flags=0, steps=1, micro_batches=1, tok=None, head_chunk_tokens=0):
-    cfg, store = make_store(shape, mode, flags=flags, micro_batches=micro_batches, head_chunk_tokens=head_chunk_tokens)
+def run_step(shape, mode="streamed", flags=0, steps=1, micro_batches=1, tok=None, head_chunk_tokens=0,
+             retain_layers=0):
+    cfg, store = make_store(shape, mode, flags=flags, micro_batches=micro_batches, head_chunk_tokens=head_chunk_tokens,
+                            retain_layers=retain_layers)
     model = mt.Model(cfg, store, "cuda:0")
     tok = datagen.tokens(shape) if tok is None else tok
     losses = [model.step(tok) for _ in range(steps)]
@@ -67,13 +69,17 @@ def test_step_matches_oracle(shape):
 def test_schedules_bitwise_equal(shape):
     need_gpu()
     ref = run_step(shape, "streamed")
-    for mode, flags in (("serialized", 0), ("resident", 0), ("single_slot", 0), ("streamed", mt.MT_FLAG_POISON),
-                        ("single_slot", mt.MT_FLAG_POISON)):
-        r = run_step(shape, mode, flags)
-        assert r["loss"] == ref["loss"], mode
+    # retain: layers whose forward intermediates stay on the device, so that
+    # their backward skips the recompute
+    for mode, flags, retain in (("serialized", 0, 0), ("resident", 0, 0), ("single_slot", 0, 0),
+                                ("streamed", mt.MT_FLAG_POISON, 0), ("single_slot", mt.MT_FLAG_POISON, 0),
+                                ("streamed", 0, 1), ("streamed", mt.MT_FLAG_POISON, shape.n_layers),
+                                ("single_slot", 0, 1)):
+        r = run_step(shape, mode, flags, retain_layers=retain)
+        assert r["loss"] == ref["loss"], (mode, flags, retain)
         for key in ("g", "w", "m", "v", "p"):
             for k in ref.get(key, {}):
-                assert np.array_equal(r[key][k], ref[key][k]), (mode, flags, key, k)
+                assert np.array_equal(r[key][k], ref[key][k]), (mode, flags, retain, key, k)
 
 
 def test_repeated_step_is_deterministic_and_t_advances():

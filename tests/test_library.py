@@ -335,3 +335,25 @@ def test_store_checkpoint_round_trip(shape, tmp_path):
         f.truncate(os.path.getsize(path) - 100)
     assert mt.lib().mt_store_load(pb, n, ob, no, path.encode()) == mt.MT_E_INVALID
     assert mt.lib().mt_store_load(pb, n, ob, no, str(tmp_path / "missing.bin").encode()) == mt.MT_E_INVALID
+
+
+def test_retained_layers_grow_the_arena_by_one_intermediate_set_each():
+    """retain_layers = R keeps R more sets of one layer's forward
+    intermediates on the device (layer-boundary checkpoints only when 0);
+    MT_RESIDENT keeps every layer's already, so R changes nothing there."""
+    shape = datagen.PRESETS["14b"]
+    b0 = mt.device_bytes(mt.make_config(shape))
+    b1 = mt.device_bytes(mt.make_config(shape, retain_layers=1))
+    per = b1 - b0
+    # h, o, h2 (bf16 [M x d]), qkv (bf16 [M x 3d]), x1 (fp32 [M x d]), gu (bf16 [M x 2F]), y (bf16 [M x F])
+    M, d, F = shape.batch * shape.seq_len, shape.d_model, shape.d_ff
+    floor = M * d * 2 * 3 + M * 3 * d * 2 + M * d * 4 + M * 2 * F * 2 + M * F * 2
+    assert floor <= per <= floor * 1.01, (per, floor)
+    for R in (7, 30, shape.n_layers):
+        assert mt.device_bytes(mt.make_config(shape, retain_layers=R)) == b0 + R * per
+    res = mt.make_config(shape.replace(n_layers=2), mode="resident")
+    assert mt.device_bytes(res) == mt.device_bytes(mt.make_config(shape.replace(n_layers=2), mode="resident",
+                                                                  retain_layers=2))
+    for R in (-1, shape.n_layers + 1):
+        with pytest.raises(mt.MtError):
+            mt.device_bytes(mt.make_config(shape, retain_layers=R))
