@@ -165,11 +165,14 @@ def test_micro_batches_accumulate_the_batch_gradient(shape):
         assert np.array_equal(r["w"][k], w2) and np.array_equal(r["m"][k], m2) and np.array_equal(r["v"][k], v2), k
     o_loss, o_g, o_w = oracle_step(shape)
     assert_parity(r["loss"], r["a"], r["w"], o_loss, o_g, o_w)
-    res = run_step(one, "resident", micro_batches=2, tok=tok)
-    assert res["loss"] == r["loss"]
-    for key in "awmv":
-        for k in r[key]:
-            assert np.array_equal(res[key][k], r[key][k]), (key, k)
+    # resident, and streamed with layer 0's intermediates kept between the
+    # sweeps' forward and backward (each micro-batch overwrites them)
+    for mode, retain in (("resident", 0), ("streamed", 1)):
+        res = run_step(one, mode, micro_batches=2, tok=tok, retain_layers=retain)
+        assert res["loss"] == r["loss"], (mode, retain)
+        for key in "awmv":
+            for k in r[key]:
+                assert np.array_equal(res[key][k], r[key][k]), (mode, retain, key, k)
 
 
 @pytest.mark.parametrize("shape,chunk", [(datagen.PRESETS["tiny"], 48), (SMALL_BF16, 96)],
