@@ -124,6 +124,8 @@ struct Model {
   std::vector<uint8_t*> acts_mem;  // Acts storage per layer (1 in streamed modes)
   uint8_t* bwd_mem;
   uint8_t* head_mem;
+  float* gemm_ws = nullptr;  // stream-K partial tiles of the bf16 GEMMs
+  size_t gemm_ws_size = 0;
 
   // host pinned
   int32_t *h_tok = nullptr, *h_order = nullptr, *h_seg = nullptr;
@@ -241,6 +243,17 @@ struct Model {
       carve_head(c, w);
       head_mem = base ? base + start : nullptr;
     }
+    if (bf16_store(cfg)) {
+      // the largest split any GEMM of the step plans (the other GEMMs of the
+      // step share the same M or N and K)
+      gemm_ws_size = 0;
+      const int shapes[][3] = {{M, 3 * d, d},     {M, d, d},     {M, 2 * F, d},    {M, d, F},  {d, F, M},
+                               {M, F, d},         {2 * F, d, M}, {M, d, 2 * F},    {d, d, M},  {3 * d, d, M},
+                               {M, d, 3 * d},     {V, d, HC},    {HC, V, d},       {HC, d, V}};
+      for (const auto& sh : shapes) gemm_ws_size = std::max(gemm_ws_size, gemm_ws_bytes(sh[0], sh[1], sh[2]));
+      gemm_ws = gemm_ws_size ? c.take<float>(gemm_ws_size) : nullptr;
+      if (!base) gemm_ws = nullptr;
+    }
     return c.off;
   }
   // Layers whose forward intermediates stay on the device until their backward.
@@ -320,7 +333,7 @@ struct Model {
     const double bytes = ((double)m * k + (double)n * k) * sizeof(T) + (double)m * n * (out_b + (epi == EPI_ADD_F32 ? 4 : 0));
     if (timed) record_kernel_start(2.0 * m * n * k, 0, bytes);
     if constexpr (std::is_same<T, uint16_t>::value)
-      gemm_bf16(A, lda, Bm, ldb, layout, C, ldc, R, ldr, m, n, k, epi, sc);
+      gemm_bf16(A, lda, Bm, ldb, layout, C, ldc, R, ldr, m, n, k, epi, sc, gemm_ws, gemm_ws_size);
     else
       gemm_nt<T>(A, lda, Bm, ldb, C, ldc, R, ldr, m, n, k, epi, sc);
     if (timed) record_kernel_end();

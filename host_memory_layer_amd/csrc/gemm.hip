@@ -208,6 +208,22 @@ __device__ inline void tile_of(int lin, int tiles_m, int tiles_n, int64_t& m0, i
   n0 = (int64_t)((lin % group_size) / gm_cnt) * BN;
 }
 
+// Stream-K tail.  The K steps of the tiles [t_dp, ntiles) that do not fill a
+// whole round, taken in tile order, are cut into nwg contiguous ranges, one
+// per workgroup (logical index v).  A cut that falls within 3 steps of a tile
+// edge moves to that edge, so every segment of a tile has at least 3 K steps
+// (the pipeline's minimum).  Both the GEMM and its fix-up derive the cuts
+// from the shapes alone.
+__host__ __device__ inline int64_t sk_cut(int v, int nwg, int64_t total, int nk) {
+  int64_t x = total * v / nwg;
+  const int64_t r = x % nk;
+  if (r > 0 && r < 3)
+    x -= r;
+  else if (r > nk - 3)
+    x += nk - r;
+  return x;
+}
+
 // VEC: N and ldc multiples of 4 and C 16-byte aligned, so every lane writes
 // 4 consecutive outputs per store through a buffer descriptor that drops
 // rows past M, while lanes past N aim beyond the descriptor.  Otherwise
@@ -218,30 +234,62 @@ template <int EPI, bool VEC, bool AKM, bool BKM>
 __global__ void __launch_bounds__(256, 1) k_gemm_bf16_tile(const uint16_t* __restrict__ A, int64_t lda,
                                                        const uint16_t* __restrict__ B, int64_t ldb, void* C,
                                                        int64_t ldc, const float* R, int64_t ldr, int M, int N, int K,
-                                                       int tiles_m, int tiles_n) {
+                                                       int tiles_m, int tiles_n, float* ws, int t_dp, int maxseg) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
   const int ntiles = tiles_m * tiles_n;
   // Persistent schedule.  Workgroup w runs on XCD w % 8 (the dispatcher deals
   // workgroups round-robin over the XCDs); XCD x owns a contiguous range of
   // the grouped tile order, and its workgroups take turns through it.
+  // Whole tiles [0, t_dp): workgroup w runs on XCD w % 8 (the dispatcher
+  // deals workgroups round-robin over the XCDs); XCD x owns a contiguous
+  // range of the grouped tile order, and its workgroups take turns through
+  // it.  Tiles [t_dp, ntiles): the stream-K tail, whose segments are summed
+  // by k_gemm_sk_fixup (t_dp == ntiles: none).
   const int nwg = gridDim.x, w = blockIdx.x;
+  const int nk = K / BK;
   int t, hi, stride;
-  if (nwg % 8 == 0 && nwg < ntiles) {
-    const int per = (ntiles + 7) / 8;
+  if (nwg % 8 == 0 && nwg <= t_dp) {
+    const int per = (t_dp + 7) / 8;
     const int lo = (w % 8) * per;
-    hi = min(ntiles, lo + per);
+    hi = min(t_dp, lo + per);
     t = lo + w / 8;
     stride = nwg / 8;
   } else {
     t = w;
-    hi = ntiles;
+    hi = t_dp;
     stride = nwg;
   }
-  if (t >= hi) return;
+  // this workgroup's range of the tail's K steps, XCD-contiguous like the tiles
+  const int u = nwg % 8 == 0 ? (w % 8) * (nwg / 8) + w / 8 : w;
+  const int64_t sk_total = (int64_t)(ntiles - t_dp) * nk;
+  int64_t sk_p = sk_total ? sk_cut(u, nwg, sk_total, nk) : 0;
+  const int64_t sk_end = sk_total ? sk_cut(u + 1, nwg, sk_total, nk) : 0;
+  const int64_t sk_tile0 = sk_p / nk;
+  // Current work item: tile tc, K steps [kb, kb + n).  EPI_PARTIAL (the
+  // tail launch): a segment of a tail tile, its partial sum written to ws
+  // slot `slot`; otherwise a whole tile of [0, t_dp).
+  int tc = 0, kb = 0, n = nk, slot = 0;
+  auto take = [&]() -> bool {
+    if (EPI != EPI_PARTIAL) {
+      if (t >= hi) return false;
+      tc = t;
+      t += stride;
+      return true;
+    }
+    if (sk_p >= sk_end) return false;
+    const int64_t tile = sk_p / nk;
+    const int64_t e = min(sk_end, (tile + 1) * nk);
+    tc = t_dp + (int)tile;
+    kb = (int)(sk_p - tile * nk);
+    n = (int)(e - sk_p);
+    slot = u * maxseg + (int)(tile - sk_tile0);
+    sk_p = e;
+    return true;
+  };
+  if (!take()) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nk = K / BK;
   auto rsrc_of = [&](const void* base, int64_t row0, int64_t rows_total, int64_t ld, int esize) {
     const int rows = (int)min<int64_t>(BM, rows_total - row0);
     return __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)base + row0 * ld * esize), 0,
@@ -276,11 +324,13 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_tile(const uint16_t* __res
   }
   const int astep = AKM ? (int)(BK * lda * 2) : BK * 2;  // bytes per K step
   const int bstep = BKM ? (int)(BK * ldb * 2) : BK * 2;
+  // byte offsets of the item's first K step (kt counts from it)
+  int kofs_a = kb * astep, kofs_b = kb * bstep;
   auto load_a = [&](i32x4_t rs, int kt, int i) {
-    dma16(rs, smem + (kt & 1) * STAGE + (wave * 8 + i) * 1024, aoff[i], kt * astep);
+    dma16(rs, smem + (kt & 1) * STAGE + (wave * 8 + i) * 1024, aoff[i], kofs_a + kt * astep);
   };
   auto load_b = [&](i32x4_t rs, int kt, int i) {
-    dma16(rs, smem + (kt & 1) * STAGE + STAGE / 2 + (wave * 8 + i) * 1024, boff[i], kt * bstep);
+    dma16(rs, smem + (kt & 1) * STAGE + STAGE / 2 + (wave * 8 + i) * 1024, boff[i], kofs_b + kt * bstep);
   };
 
   const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
@@ -309,7 +359,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_tile(const uint16_t* __res
   };
 
   int64_t m0, n0;
-  tile_of(t, tiles_m, tiles_n, m0, n0);
+  tile_of(tc, tiles_m, tiles_n, m0, n0);
   i32x4_t ar = AKM ? rsrc_km(A, m0, lda) : orsrc_of(A, m0, M, lda);
   i32x4_t br = BKM ? rsrc_km(B, n0, ldb) : orsrc_of(B, n0, N, ldb);
 
@@ -391,13 +441,32 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_tile(const uint16_t* __res
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     step(0, F_, T_, T_);  // step 1 came with step 0
-    for (int kt = 1; kt + 2 < nk; ++kt) step(kt, T_, T_, T_);
-    step(nk - 2, T_, F_, T_);
-    step(nk - 1, F_, F_, F_);
+    for (int kt = 1; kt + 2 < n; ++kt) step(kt, T_, T_, T_);
+    step(n - 2, T_, F_, T_);
+    step(n - 1, F_, F_, F_);
 
     // Epilogue.  acc[i][j] register r holds row 32i + (lane & 31) and column
     // 32j + 8(r/4) + 4(lane/32) + r%4 of the wave's 128 x 128 sub-tile.
-    if (VEC) {
+    if (EPI == EPI_PARTIAL) {
+      // partial sum of a tail tile: the raw fp32 tile [256 x 256] into its slot
+      const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(ws + (int64_t)slot * (BM * BN)), 0, BM * BN * 4, 0x00020000);
+      const int c0 = 4 * (lane >> 5);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int i = q >> 2, j = q & 3;
+        const int row = wm + 32 * i + (lane & 31);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = wn + 32 * j + 8 * g + c0;
+          const f32x16_t& v = acc[i][j];
+          u32x4_t pk = {__float_as_uint(v[4 * g]), __float_as_uint(v[4 * g + 1]), __float_as_uint(v[4 * g + 2]),
+                        __float_as_uint(v[4 * g + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(pk, wrs, (row * BN + col) * 4, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if (VEC) {
       const int esize = EPI == EPI_STORE ? 2 : 4;
       const __amdgpu_buffer_rsrc_t crs = rsrc_of(C, m0, M, ldc, esize);
       __amdgpu_buffer_rsrc_t rrs = crs;
@@ -494,12 +563,67 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_tile(const uint16_t* __res
     }
     // Next tile: its loads go out right behind this tile's stores, so the
     // store drain, the load latency and the next tile's start overlap.
-    t += stride;
-    if (t >= hi) break;
-    tile_of(t, tiles_m, tiles_n, m0, n0);
+    if (!take()) break;
+    tile_of(tc, tiles_m, tiles_n, m0, n0);
     ar = AKM ? rsrc_km(A, m0, lda) : orsrc_of(A, m0, M, lda);
     br = BKM ? rsrc_km(B, n0, ldb) : orsrc_of(B, n0, N, ldb);
+    kofs_a = kb * astep;
+    kofs_b = kb * bstep;
     prologue();
+  }
+}
+
+// Fix-up of the stream-K tail: tail tile blockIdx.y is the sum of the
+// partial tiles of the workgroup ranges that cover its K steps, added in
+// K order (so the result depends only on the shapes), then the epilogue.
+// Each thread takes 4 consecutive columns of one row of the 256 x 256 tile.
+template <int EPI>
+__global__ void __launch_bounds__(256) k_gemm_sk_fixup(const float* __restrict__ ws, void* C, int64_t ldc,
+                                                       const float* R, int64_t ldr, int M, int N, int K, int tiles_m,
+                                                       int tiles_n, int t_dp, int nwg, int maxseg) {
+  const int nk = K / BK;
+  const int ntiles = tiles_m * tiles_n;
+  const int64_t total = (int64_t)(ntiles - t_dp) * nk;
+  const int tt = blockIdx.y;
+  const int64_t lo = (int64_t)tt * nk, hi = lo + nk;
+  // the range holding step lo: the largest v with cut(v) <= lo
+  int a = 0, b = nwg - 1;
+  while (a < b) {
+    const int mid = (a + b + 1) / 2;
+    if (sk_cut(mid, nwg, total, nk) <= lo)
+      a = mid;
+    else
+      b = mid - 1;
+  }
+  const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int row = e / BN, col = e % BN;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  for (int v = a; v < nwg; ++v) {
+    const int64_t cv = sk_cut(v, nwg, total, nk);
+    if (cv >= hi) break;
+    if (sk_cut(v + 1, nwg, total, nk) == cv) continue;  // empty range
+    const int slot = v * maxseg + (int)(tt - cv / nk);
+    const float4 p = *(const float4*)(ws + (int64_t)slot * (BM * BN) + e);
+    s0 += p.x;
+    s1 += p.y;
+    s2 += p.z;
+    s3 += p.w;
+  }
+  int64_t m0, n0;
+  tile_of(t_dp + tt, tiles_m, tiles_n, m0, n0);
+  const int64_t gm = m0 + row;
+  if (gm >= M) return;
+  const float sv[4] = {s0, s1, s2, s3};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int64_t gn = n0 + col + c;
+    if (gn >= N) break;
+    if (EPI == EPI_STORE)
+      ((uint16_t*)C)[gm * ldc + gn] = f32_to_bf16(sv[c]);
+    else if (EPI == EPI_F32)
+      ((float*)C)[gm * ldc + gn] = sv[c];
+    else
+      ((float*)C)[gm * ldc + gn] = R[gm * ldr + gn] + sv[c];
   }
 }
 
@@ -567,8 +691,40 @@ bool gemm_layout_ok(int M, int N, int K, int64_t lda, int64_t ldb, int layout) {
   return true;
 }
 
+// Stream-K plan for a bf16 GEMM on `nwg` persistent workgroups: the first
+// t_dp tiles in whole rounds, the rest split along K.  Used when the last
+// round would leave at least 5% of the launch idle, the tail holds at most
+// 0.45 of a round and gives every workgroup at least 16 K steps; maxseg
+// bounds the tail tiles one range touches.  Returns false (no split)
+// otherwise.  The 0.45: measured at the 14B weight-gradient shapes, a
+// split tail runs at about half the rate of whole tiles (its workgroups
+// stand at different K offsets, so they share no operand panels in L2, and
+// each segment pays a pipeline fill and a 256 KiB partial store): tails of
+// 0.22 and 0.44 of a round gained 10.5% and 3.1%, tails of 0.56 and 0.69
+// lost 7% and 1.5%.
+static bool sk_plan(int ntiles, int nk, int nwg, int* t_dp, int* maxseg) {
+  if (ntiles <= nwg || ntiles % nwg == 0 || nk < 8) return false;
+  const int rounds = (ntiles + nwg - 1) / nwg;
+  if ((int64_t)(rounds * nwg - ntiles) * 20 < (int64_t)rounds * nwg) return false;
+  if ((int64_t)(ntiles % nwg) * 20 > (int64_t)nwg * 9) return false;
+  const int64_t total = (int64_t)(ntiles % nwg) * nk;
+  if (total / nwg < 16) return false;
+  const int64_t longest = total / nwg + 1 + 4;  // a range, after its cuts moved by up to 2 each
+  *t_dp = ntiles - ntiles % nwg;
+  *maxseg = (int)((longest - 1) / nk) + 2;
+  return true;
+}
+
+size_t gemm_ws_bytes(int M, int N, int K) {
+  int t_dp = 0, maxseg = 0;
+  const int ntiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (K % BK || !sk_plan(ntiles, K / BK, persistent_workgroups(), &t_dp, &maxseg)) return 0;
+  return (size_t)persistent_workgroups() * maxseg * BM * BN * sizeof(float);
+}
+
 void gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int layout, void* C, int64_t ldc,
-               const float* R, int64_t ldr, int M, int N, int K, Epi epi, hipStream_t s) {
+               const float* R, int64_t ldr, int M, int N, int K, Epi epi, hipStream_t s, float* ws,
+               size_t ws_bytes) {
   if (M <= 0 || N <= 0) return;
   if (K % 8 || lda % 8 || ldb % 8 || ((uintptr_t)A & 15) || ((uintptr_t)B & 15))
     throw ApiError{MT_E_INVALID, "bf16 GEMM needs K, lda, ldb multiples of 8 and 16-byte aligned operands"};
@@ -586,10 +742,17 @@ void gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, i
     const bool vec = N % 4 == 0 && ldc % 4 == 0 && ((uintptr_t)C & 15) == 0 &&
                      (epi != EPI_ADD_F32 || (ldr % 4 == 0 && ((uintptr_t)R & 15) == 0));
     const int ntiles = tiles_m * tiles_n;
-    const dim3 pgrid(std::min(ntiles, persistent_workgroups()));
+    const int nwg = std::min(ntiles, persistent_workgroups());
+    const dim3 pgrid(nwg);
+    int t_dp = ntiles, maxseg = 0;
+    if (!ws || !sk_plan(ntiles, K / BK, nwg, &t_dp, &maxseg) ||
+        (size_t)nwg * maxseg * BM * BN * sizeof(float) > ws_bytes) {
+      t_dp = ntiles;  // whole tiles only
+      maxseg = 0;
+    }
 #define L_(E, V, AK, BK_)                                                                                      \
   hipLaunchKernelGGL((k_gemm_bf16_tile<E, V, AK, BK_>), pgrid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, R, ldr, M, N, \
-                     K, tiles_m, tiles_n)
+                     K, tiles_m, tiles_n, ws, t_dp, maxseg)
 #define LL_(E, V)                  \
   switch (layout) {                \
     case 0: L_(E, V, false, false); break; \
@@ -607,9 +770,29 @@ void gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, i
       case EPI_STORE: LV_(EPI_STORE) break;
       case EPI_F32: LV_(EPI_F32) break;
       case EPI_ADD_F32: LV_(EPI_ADD_F32) break;
+      default: throw ApiError{MT_E_INVALID, "GEMM epilogue"};
     }
 #undef LV_
 #undef LL_
+    if (t_dp < ntiles) {
+      // the tail's segments on every workgroup, then their sums
+      switch (layout) {
+        case 0: L_(EPI_PARTIAL, true, false, false); break;
+        case 1: L_(EPI_PARTIAL, true, true, false); break;
+        case 2: L_(EPI_PARTIAL, true, false, true); break;
+        default: L_(EPI_PARTIAL, true, true, true); break;
+      }
+      const dim3 fgrid(BM * BN / (256 * 4), ntiles - t_dp);
+#define F_(E)                                                                                                       \
+  hipLaunchKernelGGL(k_gemm_sk_fixup<E>, fgrid, dim3(256), 0, s, ws, C, ldc, R, ldr, M, N, K, tiles_m, tiles_n, t_dp, \
+                     nwg, maxseg)
+      switch (epi) {
+        case EPI_STORE: F_(EPI_STORE); break;
+        case EPI_F32: F_(EPI_F32); break;
+        default: F_(EPI_ADD_F32); break;
+      }
+#undef F_
+    }
 #undef L_
     return;
   }
@@ -620,6 +803,7 @@ void gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, i
     case EPI_STORE: L_(EPI_STORE); break;
     case EPI_F32: L_(EPI_F32); break;
     case EPI_ADD_F32: L_(EPI_ADD_F32); break;
+    default: throw ApiError{MT_E_INVALID, "GEMM epilogue"};
   }
 #undef L_
 }

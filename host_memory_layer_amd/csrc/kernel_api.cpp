@@ -51,6 +51,28 @@ int mt_gemm(int32_t dtype, const void* A, int64_t lda, const void* B, int64_t ld
   });
 }
 
+int mt_gemm_ws(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, const float* R,
+               int64_t ldr, int32_t M, int32_t N, int32_t K, int32_t epi, int32_t layout, void* ws, size_t ws_bytes,
+               void* stream) {
+  return kguard([&] {
+    need(epi >= 0 && epi <= 2, "epi");
+    need(layout >= 0 && layout <= 3, "layout");
+    need(M >= 0 && N >= 0 && K >= 0, "negative size");
+    need((layout & MT_GEMM_A_KMAJOR ? lda >= M : lda >= K) && (layout & MT_GEMM_B_KMAJOR ? ldb >= N : ldb >= K) &&
+             ldc >= N,
+         "leading dimensions");
+    need(epi != 2 || (R && ldr >= N), "R");
+    need(((uintptr_t)ws & 15) == 0, "workspace must be 16-byte aligned");
+    gemm_bf16((const uint16_t*)A, lda, (const uint16_t*)B, ldb, layout, C, ldc, R, ldr, M, N, K, (Epi)epi,
+              (hipStream_t)stream, (float*)ws, ws ? ws_bytes : 0);
+  });
+}
+
+size_t mt_gemm_ws_bytes(int32_t M, int32_t N, int32_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return gemm_ws_bytes(M, N, K);
+}
+
 int mt_transpose(int32_t dtype, const void* in, int64_t ld_in, void* out, int64_t ld_out, int32_t R, int32_t C,
                  void* stream) {
   return kguard([&] {

@@ -13,7 +13,8 @@ namespace mt {
 enum Epi {
   EPI_STORE = 0,   // C (type T) = acc, rounded to nearest-even for bf16
   EPI_F32 = 1,     // C (float) = acc
-  EPI_ADD_F32 = 2  // C (float) = R + acc, R float [M x N] with row stride ldr
+  EPI_ADD_F32 = 2,  // C (float) = R + acc, R float [M x N] with row stride ldr
+  EPI_PARTIAL = 3   // internal to the bf16 GEMM: a stream-K partial tile into the workspace
 };
 template <typename T>
 void gemm_nt(const T* A, int64_t lda, const T* B, int64_t ldb, void* C, int64_t ldc, const float* R,
@@ -24,8 +25,18 @@ void gemm_nt(const T* A, int64_t lda, const T* B, int64_t ldb, void* C, int64_t 
 // operands need gemm_layout_ok().
 enum GemmLayout { GEMM_A_KMAJOR = 1, GEMM_B_KMAJOR = 2 };
 bool gemm_layout_ok(int M, int N, int K, int64_t lda, int64_t ldb, int layout);
+// With a device workspace `ws` of at least gemm_ws_bytes(M, N, K) bytes,
+// a GEMM whose last round of tiles would leave part of the GPU idle splits
+// that round's tiles along K over every workgroup (stream-K) and adds the
+// partial tiles in a fixed order in a second kernel: the results then
+// differ from the unsplit GEMM by rounding in those tiles only, and still
+// depend only on the shapes.  Without it (or with a smaller one) every tile
+// is computed whole.
 void gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int layout, void* C, int64_t ldc,
-               const float* R, int64_t ldr, int M, int N, int K, Epi epi, hipStream_t s);
+               const float* R, int64_t ldr, int M, int N, int K, Epi epi, hipStream_t s, float* ws = nullptr,
+               size_t ws_bytes = 0);
+// Workspace bytes the split needs for this shape (0: no split planned).
+size_t gemm_ws_bytes(int M, int N, int K);
 
 // ---------------------------------------------------------- elementwise --
 template <typename T>

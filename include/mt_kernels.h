@@ -34,6 +34,25 @@ extern "C" {
 int mt_gemm(int32_t dtype, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
             const float* R, int64_t ldr, int32_t M, int32_t N, int32_t K, int32_t epi, int32_t layout, void* stream);
 
+/* mt_gemm for bf16 with a caller-owned device workspace `ws` (16-byte
+ * aligned, ws_bytes long, not read before it is written).  When the last
+ * round of 256 x 256 tiles would leave at least 5% of the persistent
+ * workgroups idle, the tiles of that round are split along K over every
+ * workgroup (stream-K) and a second kernel adds each tile's partial sums in
+ * K order, then applies the epilogue.  Those tiles then differ from mt_gemm
+ * by fp32 rounding; every other tile is bit-identical, and all results
+ * depend only on the shapes.  With ws null or ws_bytes <
+ * mt_gemm_ws_bytes(M, N, K) this is mt_gemm.  The training step uses the
+ * same split for its weight gradients (the layer's d x d and d x F shapes
+ * leave a partial last round on 256 compute units). */
+int mt_gemm_ws(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, const float* R,
+               int64_t ldr, int32_t M, int32_t N, int32_t K, int32_t epi, int32_t layout, void* ws, size_t ws_bytes,
+               void* stream);
+
+/* Workspace bytes mt_gemm_ws uses for a bf16 GEMM of this shape on the
+ * current device; 0 when it would not split. */
+size_t mt_gemm_ws_bytes(int32_t M, int32_t N, int32_t K);
+
 /* out[C x R] = in[R x C]^T (row strides ld_in, ld_out). */
 int mt_transpose(int32_t dtype, const void* in, int64_t ld_in, void* out, int64_t ld_out, int32_t R, int32_t C,
                  void* stream);

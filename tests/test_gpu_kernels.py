@@ -369,3 +369,73 @@ def test_gemm_bf16_kmajor_long_context_sampled():
     rc = mt.lib().mt_gemm(mt.MT_BF16, Aw.data_ptr(), wide, B.data_ptr(), N, C.data_ptr(), N, None, 0, 256, N, K,
                           mt.EPI_F32, mt.GEMM_A_KMAJOR | mt.GEMM_B_KMAJOR, None)
     assert rc != 0
+
+
+# ------------------------------------------------------------ stream-K tail --
+def gemm_ws(A, lda, B, ldb, C, ldc, M, N, K, epi, ws, ws_bytes, R=None, ldr=0, layout=0):
+    mt.check(mt.lib().mt_gemm_ws(A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
+                                 R.data_ptr() if R is not None else None, ldr, M, N, K, epi, layout,
+                                 ws.data_ptr() if ws is not None else None, ws_bytes, None))
+
+
+@pytest.mark.parametrize("M,N,K,layout", [(5000, 13800, 32768, 3), (5120, 13824, 32768, 3), (8192, 2304, 8192, 0),
+                                          (11008, 2048, 8192, 2)])
+def test_gemm_stream_k_tail(M, N, K, layout):
+    """A last round of tiles that would leave workgroups idle is split along
+    K over every workgroup and summed in K order by a fix-up kernel.  Every
+    output stays within the fp32 accumulation bound of the exact contraction
+    (float64 on sampled outputs; against the unsplit GEMM everywhere), the
+    tiles outside the tail are bit-identical to the unsplit GEMM, the bf16
+    and residual epilogues are those of the fp32 sum, and a workspace that
+    is too small gives the unsplit GEMM."""
+    print(f"stream-K gemm {M}x{N}x{K} layout {layout}", flush=True)
+    need = int(mt.lib().mt_gemm_ws_bytes(M, N, K))
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("tile rounds are planned for 256 compute units")
+    assert need > 0
+    # a tail of more than 0.45 of a round is not split (the 14B O and QKV
+    # weight gradients: 400 and 1200 tiles on 256 workgroups)
+    assert mt.lib().mt_gemm_ws_bytes(5120, 5120, 32768) == 0 and mt.lib().mt_gemm_ws_bytes(15360, 5120, 32768) == 0
+    g = torch.Generator(device=dev()).manual_seed(M + N + K)
+    akm, bkm = layout & mt.GEMM_A_KMAJOR, layout & mt.GEMM_B_KMAJOR
+    A = torch.randn((K, M) if akm else (M, K), generator=g, device=dev()).to(torch.bfloat16)
+    B = torch.randn((K, N) if bkm else (N, K), generator=g, device=dev()).to(torch.bfloat16)
+    lda, ldb = (M if akm else K), (N if bkm else K)
+    Ai, Bi = A.view(torch.int16), B.view(torch.int16)
+    ws = torch.empty(need // 4, dtype=torch.float32, device=dev())
+    plain = torch.empty((M, N), dtype=torch.float32, device=dev())
+    split = torch.empty((M, N), dtype=torch.float32, device=dev())
+    gemm(mt.MT_BF16, Ai, lda, Bi, ldb, plain, N, M, N, K, mt.EPI_F32, layout=layout)
+    gemm_ws(Ai, lda, Bi, ldb, split, N, M, N, K, mt.EPI_F32, ws, need, layout=layout)
+    # bf16 and residual epilogues of the split sums
+    sb = torch.empty((M, N), dtype=torch.int16, device=dev())
+    gemm_ws(Ai, lda, Bi, ldb, sb, N, M, N, K, mt.EPI_STORE, ws, need, layout=layout)
+    R = torch.randn((M, N), generator=g, device=dev())
+    sr = torch.empty((M, N), dtype=torch.float32, device=dev())
+    gemm_ws(Ai, lda, Bi, ldb, sr, N, M, N, K, mt.EPI_ADD_F32, ws, need, R=R, ldr=N, layout=layout)
+    # too small a workspace: the unsplit GEMM
+    small = torch.empty((M, N), dtype=torch.float32, device=dev())
+    gemm_ws(Ai, lda, Bi, ldb, small, N, M, N, K, mt.EPI_F32, ws, need - 4, layout=layout)
+    torch.cuda.synchronize()
+    assert torch.equal(small, plain)
+    # |A| |B|^T (fp32 on the device; used only as the error bound)
+    a_abs = A.float().abs()
+    b_abs = B.float().abs()
+    absprod = torch.mm(a_abs.t().contiguous() if akm else a_abs, b_abs if bkm else b_abs.t().contiguous())
+    bound = K * 2.0 ** -24 * absprod * 1.001
+    diff = (split - plain).abs()
+    assert bool((diff <= 2 * bound).all())
+    same = float((split == plain).float().mean())
+    assert 0.3 < same < 0.999, same  # the tail tiles differ by rounding, the rest is identical
+    assert np.array_equal(sb.cpu().numpy().view(np.uint16), datagen.f32_to_bf16_bits(split.cpu().numpy()))
+    assert torch.equal(sr, R + split)
+    # float64 on sampled outputs
+    rng = np.random.default_rng(1)
+    rows = torch.from_numpy(rng.integers(0, M, 2048)).to(dev())
+    cols = torch.from_numpy(rng.integers(0, N, 2048)).to(dev())
+    a = (A[:, rows].t() if akm else A[rows]).float().cpu().numpy().astype(np.float64)
+    b = (B[:, cols].t() if bkm else B[cols]).float().cpu().numpy().astype(np.float64)
+    ref = np.einsum("ij,ij->i", a, b)
+    bnd = K * 2.0 ** -24 * np.einsum("ij,ij->i", np.abs(a), np.abs(b))
+    got = split[rows, cols].cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= bnd)
