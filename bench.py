@@ -33,8 +33,8 @@ PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 # scaled by what each reads for a plain 1 GiB copy kernel in the same run
 # (profiles/gemm_14b_pmc_traffic.md).  Valid only for the GEMM source it was
 # measured on; reported as null once that file changes.
-GEMM_TRAFFIC = {"source_sha256_16": "7f70420b2646548f", "config": "14b", "layers": 48,
-                "bytes_per_launch": 9.785e9 + 0.729e9}
+GEMM_TRAFFIC = {"source_sha256_16": "f465259c6307aa15", "config": "14b", "layers": 48,
+                "bytes_per_launch": 9.499e9 + 0.741e9}
 
 
 def gemm_traffic(shape_name, layers):
