@@ -437,11 +437,37 @@ __global__ void __launch_bounds__(256) k_swiglu_fwd(const T* __restrict__ gu, T*
   }
 }
 
+// bf16 with d_ff % 8 == 0: eight outputs per thread, 16-byte accesses; one
+// grid row per token row (no index division).  Same arithmetic per element.
+
+__global__ void __launch_bounds__(256) k_swiglu_fwd8(const uint16_t* __restrict__ gu, uint16_t* __restrict__ y, int F) {
+  const int j = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (j >= F) return;
+  const int64_t m = blockIdx.y;
+  float g[8], u[8], o[8];
+  unpack8(*(const uint4*)(gu + m * 2 * F + j), g);
+  unpack8(*(const uint4*)(gu + m * 2 * F + F + j), u);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = silu_(g[i]) * u[i];
+  *(uint4*)(y + m * F + j) = pack8(o);
+}
+
 template <typename T>
 void swiglu_fwd(const T* gu, T* y, int M, int F, hipStream_t s) {
   if (F % 4) throw ApiError{MT_E_INVALID, "SwiGLU needs d_ff % 4 == 0"};
   const int64_t n4 = (int64_t)M * F / 4;
   if (n4 <= 0) return;
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    if (F % 8 == 0) {
+      // rows in chunks of at most 65535 grid rows
+      for (int r0 = 0; r0 < M; r0 += 65535) {
+        const int rows = std::min(65535, M - r0);
+        hipLaunchKernelGGL(k_swiglu_fwd8, dim3(cdiv(F / 8, 256), rows), dim3(256), 0, s, gu + (int64_t)r0 * 2 * F,
+                           y + (int64_t)r0 * F, F);
+      }
+      return;
+    }
+  }
   const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 65536);
   hipLaunchKernelGGL(k_swiglu_fwd<T>, dim3(blocks), dim3(256), 0, s, gu, y, n4, F);
 }
@@ -470,11 +496,36 @@ __global__ void __launch_bounds__(256) k_swiglu_bwd(const T* __restrict__ dy, co
   }
 }
 
+__global__ void __launch_bounds__(256) k_swiglu_bwd8(const uint16_t* __restrict__ dy, const uint16_t* __restrict__ gu,
+                                                     uint16_t* __restrict__ dgu, int F) {
+  const int j = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (j >= F) return;
+  const int64_t m = blockIdx.y;
+  float g[8], u[8], e[8], a[8], b[8];
+  unpack8(*(const uint4*)(gu + m * 2 * F + j), g);
+  unpack8(*(const uint4*)(gu + m * 2 * F + F + j), u);
+  unpack8(*(const uint4*)(dy + m * F + j), e);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) swiglu_grad1(e[i], g[i], u[i], &a[i], &b[i]);
+  *(uint4*)(dgu + m * 2 * F + j) = pack8(a);
+  *(uint4*)(dgu + m * 2 * F + F + j) = pack8(b);
+}
+
 template <typename T>
 void swiglu_bwd(const T* dy, const T* gu, T* dgu, int M, int F, hipStream_t s) {
   if (F % 4) throw ApiError{MT_E_INVALID, "SwiGLU needs d_ff % 4 == 0"};
   const int64_t n4 = (int64_t)M * F / 4;
   if (n4 <= 0) return;
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    if (F % 8 == 0) {
+      for (int r0 = 0; r0 < M; r0 += 65535) {
+        const int rows = std::min(65535, M - r0);
+        hipLaunchKernelGGL(k_swiglu_bwd8, dim3(cdiv(F / 8, 256), rows), dim3(256), 0, s, dy + (int64_t)r0 * F,
+                           gu + (int64_t)r0 * 2 * F, dgu + (int64_t)r0 * 2 * F, F);
+      }
+      return;
+    }
+  }
   const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 65536);
   hipLaunchKernelGGL(k_swiglu_bwd<T>, dim3(blocks), dim3(256), 0, s, dy, gu, dgu, n4, F);
 }
