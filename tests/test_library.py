@@ -357,3 +357,20 @@ def test_retained_layers_grow_the_arena_by_one_intermediate_set_each():
     for R in (-1, shape.n_layers + 1):
         with pytest.raises(mt.MtError):
             mt.device_bytes(mt.make_config(shape, retain_layers=R))
+
+
+def test_stream_k_plan_at_the_14b_shapes():
+    """Which GEMMs of the 14B-shape step split their last round of tiles
+    along K (planned for 256 persistent workgroups, the MI355X's compute
+    units and the count assumed without a GPU): the down and gate/up weight
+    gradients (1080 and 2160 tiles: last rounds of 0.22 and 0.44) do; the O
+    and QKV weight gradients (tails of 0.56 and 0.69 of a round) and every
+    GEMM whose tiles fill whole rounds do not."""
+    L = mt.lib()
+    M, d, F = 32768, 5120, 13824
+    mib = 1 << 20
+    assert L.mt_gemm_ws_bytes(d, F, M) == 128 * mib
+    assert L.mt_gemm_ws_bytes(2 * F, d, M) == 128 * mib
+    for shape in [(d, d, M), (3 * d, d, M), (M, 3 * d, d), (M, d, d), (M, 2 * F, d), (M, d, F), (M, F, d),
+                  (M, d, 2 * F), (M, d, 3 * d), (300, 520, 256), (0, 5, 64)]:
+        assert L.mt_gemm_ws_bytes(*shape) == 0, shape
