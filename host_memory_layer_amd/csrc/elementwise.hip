@@ -167,7 +167,7 @@ template <typename T, int VPT>
 __global__ void __launch_bounds__(256) k_rmsnorm_bwd(const float* __restrict__ dy, const float* __restrict__ x,
                                                      const T* __restrict__ g, const float* __restrict__ rstd,
                                                      const float* __restrict__ resid, float* __restrict__ dx,
-                                                     float* __restrict__ part, int M, int d) {
+                                                     T* __restrict__ dx_lp, float* __restrict__ part, int M, int d) {
   __shared__ float red[4];
   float4 gv[VPT], dg[VPT];
 #pragma unroll
@@ -209,6 +209,7 @@ __global__ void __launch_bounds__(256) k_rmsnorm_bwd(const float* __restrict__ d
           o = make_float4(rv.x + o.x, rv.y + o.y, rv.z + o.z, rv.w + o.w);
         }
         *(float4*)(dx + (int64_t)m * d + c) = o;
+        if (dx_lp) V4<T>::st(dx_lp + (int64_t)m * d + c, o);
         dg[k].x += e[k].x * xh[k].x;
         dg[k].y += e[k].y * xh[k].y;
         dg[k].z += e[k].z * xh[k].z;
@@ -260,13 +261,13 @@ __global__ void __launch_bounds__(256) k_dg_reduce(const float* __restrict__ par
 
 template <typename T>
 void rmsnorm_bwd(const float* dy, const float* x, const T* g, const float* rstd, const float* resid, float* dx,
-                 float* partial, T* dg, int M, int d, hipStream_t s) {
+                 float* partial, T* dg, int M, int d, hipStream_t s, T* dx_lp) {
   if (d % 4) throw ApiError{MT_E_INVALID, "RMSNorm needs d_model % 4 == 0"};
   const int blocks = cdiv(M, kRmsRows);
   if (blocks > 0) {
 #define L_(V)                                                                                                    \
-  hipLaunchKernelGGL((k_rmsnorm_bwd<T, V>), dim3(blocks), dim3(256), 0, s, dy, x, g, rstd, resid, dx, partial, M, \
-                     d)
+  hipLaunchKernelGGL((k_rmsnorm_bwd<T, V>), dim3(blocks), dim3(256), 0, s, dy, x, g, rstd, resid, dx, dx_lp, partial, \
+                     M, d)
     MT_RMS_DISPATCH(rms_vpt(d), L_)
 #undef L_
   }
@@ -717,7 +718,7 @@ void fill_u32(void* p, uint32_t value, size_t n_words, hipStream_t s) {
   template void embed_bwd<T>(const float*, const int32_t*, const int32_t*, T*, int, int, hipStream_t);          \
   template void rmsnorm_fwd<T>(const float*, const T*, T*, float*, int, int, float, hipStream_t);               \
   template void rmsnorm_bwd<T>(const float*, const float*, const T*, const float*, const float*, float*, float*, T*, \
-                               int, int, hipStream_t);                                                          \
+                               int, int, hipStream_t, T*);                                                          \
   template void rope_qkv_fwd<T>(T*, const float*, const float*, int, int, int, int, hipStream_t);              \
   template void rope_bwd_T<T>(T*, int64_t, const float*, const float*, int, int, int, int, hipStream_t);        \
   template void swiglu_fwd<T>(const T*, T*, int, int, hipStream_t);                                             \

@@ -431,17 +431,16 @@ struct Model {
   void layer_bwd_kmajor(const LayerW<T>& w, const float* x, const Acts<T>& a, const float* dx2, float* dx_out,
                         const LayerW<T>& g, const BwdWs<T>& ws) {
     const int KA = GEMM_A_KMAJOR, KB = GEMM_B_KMAJOR;
-    // down projection
-    cast<T>(dx2, ws.dxb, (int64_t)M * d, sc);
+    // down projection; ws.dxb = T(dx2) was written beside dx2 by the norm
+    // backward that produced it (the layer above, or the head)
     gemm<T>(ws.dxb, d, a.y, F, g.d, F, nullptr, 0, d, F, M, EPI_STORE, KA | KB);
     gemm<T>(ws.dxb, d, w.d, F, ws.dy, F, nullptr, 0, M, F, d, EPI_STORE, KB);
     // SwiGLU and gate/up projection
     swiglu_bwd<T>(ws.dy, a.gu, ws.dgu, M, F, sc);
     gemm<T>(ws.dgu, 2 * F, a.h2, d, g.gu, d, nullptr, 0, 2 * F, d, M, EPI_STORE, KA | KB);
     gemm<T>(ws.dgu, 2 * F, w.gu, d, ws.dh, d, nullptr, 0, M, d, 2 * F, EPI_F32, KB);
-    rmsnorm_bwd<T>(ws.dh, a.x1, w.fnorm, a.r2, dx2, ws.dx1, ws.part, g.fnorm, M, d, sc);
-    // attention output projection
-    cast<T>(ws.dx1, ws.dxb, (int64_t)M * d, sc);
+    rmsnorm_bwd<T>(ws.dh, a.x1, w.fnorm, a.r2, dx2, ws.dx1, ws.part, g.fnorm, M, d, sc, ws.dxb);
+    // attention output projection (ws.dxb = T(dx1))
     gemm<T>(ws.dxb, d, a.o, d, g.o, d, nullptr, 0, d, d, M, EPI_STORE, KA | KB);
     gemm<T>(ws.dxb, d, w.o, d, ws.do_, d, nullptr, 0, M, d, d, EPI_STORE, KB);
     // attention
@@ -455,7 +454,8 @@ struct Model {
     // and K-major for the data gradient
     gemm<T>(ws.dqkvT, Mp, a.h, d, g.qkv, d, nullptr, 0, 3 * d, d, M, EPI_STORE, KB);
     gemm<T>(ws.dqkvT, Mp, w.qkv, d, ws.dh, d, nullptr, 0, M, d, 3 * d, EPI_F32, KA | KB);
-    rmsnorm_bwd<T>(ws.dh, x, w.anorm, a.r1, ws.dx1, dx_out, ws.part, g.anorm, M, d, sc);
+    // dx_out, and T(dx_out) for the next layer's down projection
+    rmsnorm_bwd<T>(ws.dh, x, w.anorm, a.r1, ws.dx1, dx_out, ws.part, g.anorm, M, d, sc, ws.dxb);
   }
 
   // Final norm, logits, loss, and the head's backward.  Returns dx^L in dx_out.
@@ -501,7 +501,8 @@ struct Model {
     sum_fixed(hw.row_loss, hw.loss, M, inv_n, sc);
     MT_HIP(hipMemcpyAsync(h_loss, hw.loss, sizeof(float), hipMemcpyDeviceToHost, sc));
     MT_HIP(hipEventRecord(ev_loss, sc));
-    rmsnorm_bwd<T>(ws.dh, xL, fin, hw.rz, nullptr, dx_out, ws.part, gfin, M, d, sc);
+    // dx^L, and T(dx^L) for the top layer's down projection when it reads it
+    rmsnorm_bwd<T>(ws.dh, xL, fin, hw.rz, nullptr, dx_out, ws.part, gfin, M, d, sc, kmajor ? ws.dxb : nullptr);
   }
 
   // ------------------------------------------------------------ step --

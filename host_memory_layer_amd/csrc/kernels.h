@@ -48,13 +48,14 @@ void embed_bwd(const float* dx, const int32_t* order, const int32_t* seg, T* dE,
 template <typename T>
 void rmsnorm_fwd(const float* x, const T* g, T* y, float* rstd, int M, int d, float eps, hipStream_t s);
 // dx = resid + r*(dy*g - xh*mean(dy*g*xh)), xh = x*r (resid may be null),
+// (and, with dx_lp, dx rounded to T beside it: the operand of the next GEMM)
 // and dg = sum_rows dy*xh written as T: per-block partial sums in `partial`
 // (rmsnorm_dg_partial_elems(M, d) floats), then added in a fixed order that
 // depends only on (M, d).
 size_t rmsnorm_dg_partial_elems(int M, int d);
 template <typename T>
 void rmsnorm_bwd(const float* dy, const float* x, const T* g, const float* rstd, const float* resid, float* dx,
-                 float* partial, T* dg, int M, int d, hipStream_t s);
+                 float* partial, T* dg, int M, int d, hipStream_t s, T* dx_lp = nullptr);
 // Token-major transposed buffers [C x M] use a padded row stride
 // (token_ld(M) >= M): a row stride that is a large power of two puts a
 // tile's rows on the same memory channels.
