@@ -104,14 +104,28 @@ __attribute__((target("avx512f,avx512bw"))) static inline __m512 widen(const uin
   return _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(h), 16));
 }
 
-__attribute__((target("avx512f,avx512bw,avx512bf16,avx512vl"))) static void adam_avx512_bf16(
+// f32 -> bf16 round to nearest even on the bit pattern, as round1 does: add
+// 0x7FFF plus the lowest kept bit, keep the high half; NaN stays a quiet NaN.
+// Subnormal results keep their bits (the hardware conversion instruction
+// flushes them to zero, which would make the result depend on where a
+// vector chunk starts).
+__attribute__((target("avx512f,avx512bw"))) static inline void store_bf16x16(uint16_t* out, __m512 r) {
+  const __m512i u = _mm512_castps_si512(r);
+  const __m512i hi = _mm512_srli_epi32(u, 16);
+  const __m512i lsb = _mm512_and_si512(hi, _mm512_set1_epi32(1));
+  __m512i rn = _mm512_srli_epi32(_mm512_add_epi32(u, _mm512_add_epi32(lsb, _mm512_set1_epi32(0x7FFF))), 16);
+  const __mmask16 nan =
+      _mm512_cmpgt_epu32_mask(_mm512_and_si512(u, _mm512_set1_epi32(0x7FFFFFFF)), _mm512_set1_epi32(0x7F800000));
+  rn = _mm512_mask_mov_epi32(rn, nan, _mm512_or_si512(hi, _mm512_set1_epi32(0x40)));
+  _mm256_storeu_si256((__m256i*)out, _mm512_cvtepi32_epi16(rn));
+}
+
+__attribute__((target("avx512f,avx512bw"))) static void adam_avx512_bf16(
     uint16_t* w, const uint16_t* g, float* m, float* v, size_t n, const AdamConsts& k) {
   size_t i = 0;
   for (; i + 16 <= n; i += 16) {
     __m512 r = adam16(widen(w + i), widen(g + i), m + i, v + i, k);
-    // vcvtneps2bf16 rounds to nearest even, as f32_to_bf16 does for finite values
-    __m256bh b = _mm512_cvtneps_pbh(r);
-    _mm256_storeu_si256((__m256i*)(w + i), (__m256i)b);
+    store_bf16x16(w + i, r);
   }
   adam_scalar_bf16(w + i, g + i, m + i, v + i, n - i, k);
 }
@@ -124,14 +138,13 @@ static void adam_scalar_master(uint16_t* w, float* p, const uint16_t* g, float* 
   }
 }
 
-__attribute__((target("avx512f,avx512bw,avx512bf16,avx512vl"))) static void adam_avx512_master(
+__attribute__((target("avx512f,avx512bw"))) static void adam_avx512_master(
     uint16_t* w, float* p, const uint16_t* g, float* m, float* v, size_t n, const AdamConsts& k) {
   size_t i = 0;
   for (; i + 16 <= n; i += 16) {
     __m512 r = adam16(_mm512_loadu_ps(p + i), widen(g + i), m + i, v + i, k);
     _mm512_storeu_ps(p + i, r);
-    __m256bh b = _mm512_cvtneps_pbh(r);
-    _mm256_storeu_si256((__m256i*)(w + i), (__m256i)b);
+    store_bf16x16(w + i, r);
   }
   adam_scalar_master(w + i, p + i, g + i, m + i, v + i, n - i, k);
 }
@@ -140,8 +153,7 @@ static bool cpu_has_avx512() {
   static int has = -1;
   if (has < 0) {
     __builtin_cpu_init();
-    has = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
-          __builtin_cpu_supports("avx512bf16") && __builtin_cpu_supports("avx512vl");
+    has = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw");
   }
   return has == 1;
 }
@@ -210,7 +222,7 @@ static void adam_acc_scalar(int32_t dtype, void* w, float* p, float* acc, const 
   }
 }
 
-__attribute__((target("avx512f,avx512bw,avx512bf16,avx512vl"))) static void adam_acc_avx512(
+__attribute__((target("avx512f,avx512bw"))) static void adam_acc_avx512(
     int32_t dtype, void* w, float* p, float* acc, const void* g, float* m, float* v, size_t n, const AdamConsts& k) {
   size_t i = 0;
   for (; i + 16 <= n; i += 16) {
@@ -228,8 +240,7 @@ __attribute__((target("avx512f,avx512bw,avx512bf16,avx512vl"))) static void adam
         r = adam16(_mm512_loadu_ps(p + i), gi, m + i, v + i, k);
         _mm512_storeu_ps(p + i, r);
       }
-      __m256bh b = _mm512_cvtneps_pbh(r);
-      _mm256_storeu_si256((__m256i*)wb, (__m256i)b);
+      store_bf16x16(wb, r);
     }
   }
   const size_t wb = dtype == MT_F32 ? 4 : 2;

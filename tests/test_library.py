@@ -186,6 +186,35 @@ def test_host_adam_bf16_rounds_the_fp32_update():
     assert np.array_equal(m, om) and np.array_equal(v, ov)
 
 
+@pytest.mark.parametrize("n", [1, 15, 16, 20, 32, 33, 200, 4099])
+@pytest.mark.parametrize("threads", [1, 3])
+def test_host_adam_bf16_keeps_subnormal_results(n, threads):
+    """Subnormal bf16 weights and results round like every other value,
+    wherever the element falls in a vector chunk or the scalar tail: with
+    g = 0 the update is exactly 0 and W is unchanged; with the fp32 master
+    store, subnormal masters round to their nearest-even bf16 bits."""
+    sub = np.concatenate([np.arange(1, 0x80), np.arange(0x8001, 0x8080), [0x0080, 0x8080, 0x0081, 0]])
+    bits = np.resize(sub.astype(np.uint16), n)
+    g = np.zeros(n, np.uint16)
+    m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    w = bits.copy()
+    mt.check(mt.lib().mt_host_adam(mt.MT_BF16, w.ctypes.data, g.ctypes.data, m.ctypes.data, v.ctypes.data, n,
+                                   1, 1e-3, 0.9, 0.95, 1e-8, threads))
+    assert np.array_equal(w, bits)
+    # master: p holds fp32 subnormals between bf16 patterns (ties included)
+    rng = np.random.default_rng(n)
+    pu = (rng.integers(1, 1 << 23, n, dtype=np.uint32) | (rng.integers(0, 2, n, dtype=np.uint32) << 31))
+    pu[::5] = (pu[::5] & np.uint32(0xFFFF0000)) | np.uint32(0x8000)  # exact ties
+    p = pu.view(np.float32).copy()
+    wm = np.zeros(n, np.uint16)
+    m[:] = 0
+    v[:] = 0
+    mt.check(mt.lib().mt_host_adam_master(wm.ctypes.data, p.ctypes.data, g.ctypes.data, m.ctypes.data,
+                                          v.ctypes.data, n, 1, 1e-3, 0.9, 0.95, 1e-8, threads))
+    assert np.array_equal(p.view(np.uint32), pu)
+    assert np.array_equal(wm, datagen.f32_to_bf16_bits(p))
+
+
 def _adam_master(w, p, g, m, v, t, lr):
     mt.check(mt.lib().mt_host_adam_master(w.ctypes.data, p.ctypes.data, g.ctypes.data, m.ctypes.data, v.ctypes.data,
                                           w.size, t, lr, 0.9, 0.95, 1e-8, 3))
