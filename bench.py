@@ -90,11 +90,18 @@ def log(*a):
 
 
 def flops(shape, n_layers=None):
+    """(forward flops of one layer, model flops per step, flops the device
+    executes per step).  Model flops exclude the recompute and count
+    attention over the causal half.  The recompute inside the backward sweep
+    runs a layer's forward without its down projection (its output x^{l+1}
+    is the checkpoint already held), so the device executes
+    fwd_layer - 2*M*d*F more per layer."""
     L = shape.n_layers if n_layers is None else n_layers
     M, d, F, V, B, T = shape.tokens, shape.d_model, shape.d_ff, shape.vocab, shape.batch, shape.seq_len
     fwd_layer = 2.0 * M * (4 * d * d + 3 * d * F) + 2.0 * B * T * T * d
     model = 3.0 * (L * fwd_layer + 2.0 * M * d * V)
-    return fwd_layer, model, model + L * fwd_layer
+    recompute = fwd_layer - 2.0 * M * d * F
+    return fwd_layer, model, model + L * recompute
 
 
 ADAM_BYTES = {datagen.BF16: 22, datagen.BF16_MASTER: 28, datagen.F32: 28}
@@ -118,34 +125,74 @@ def host_triad(torch, reps=3):
     return {"triad_gbs": 12.0 * n / dt / 1e9, "threads": n_thr}
 
 
-def link_probe(torch, dev, nbytes, reps=4):
-    """Pinned host <-> device copy bandwidth (GB/s): H2D, D2H, and both at once."""
-    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
-    host2 = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
-    devb = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    devb2 = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    s1, s2 = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+# Layer-block burst sizes (bf16 W region of one layer) of the 1.3B, 7B, 14B
+# and 120B shapes.
+LINK_SIZES = (101_187_584, 404_774_912, 634_413_056, 2_537_619_456)
 
-    def timed(fn_list):
-        torch.cuda.synchronize(dev)
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            for s, fn in fn_list:
-                with torch.cuda.stream(s):
-                    fn()
-        torch.cuda.synchronize(dev)
-        return time.perf_counter() - t0
 
-    h2d = lambda: devb.copy_(host, non_blocking=True)
-    d2h = lambda: host2.copy_(devb2, non_blocking=True)
-    timed([(s1, h2d)])
-    t_h2d = timed([(s1, h2d)])
-    t_d2h = timed([(s2, d2h)])
-    t_bi = timed([(s1, h2d), (s2, d2h)])
-    gb = nbytes * reps / 1e9
-    out = {"h2d_gbs": gb / t_h2d, "d2h_gbs": gb / t_d2h, "bidir_gbs": 2 * gb / t_bi, "bytes": nbytes}
-    del host, host2, devb, devb2
-    return out
+def link_peak(mt, reps=4):
+    """Host-link GB/s with the library's own copies (mt_link_probe) at the
+    layer-block sizes, on the three streams' hipMemcpyAsync and on the SDMA
+    engine queues; the peak per direction is the best sustained rate over
+    every size and both paths."""
+    table = []
+    for sdma in (False, True):
+        for r in mt.link_probe(LINK_SIZES, reps=reps, sdma=sdma):
+            r["path"] = "sdma_queues" if sdma else "hip_streams"
+            table.append(r)
+    peak = {k: max(r[k] for r in table) for k in ("h2d_gbs", "d2h_gbs", "bidir_gbs")}
+    return {**peak, "table": table, "reps": reps}
+
+
+def host_description():
+    """CPU model, threads allowed, and the BLAS numpy uses."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = f"{b.get('name')} {b.get('version', '')}".strip()
+    except Exception:  # pragma: no cover - older numpy
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            blas = f"{blas} ({infos[0].get('internal_api')} {infos[0].get('version')}, " \
+                   f"{infos[0].get('num_threads')} threads)"
+    except Exception:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "blas": blas}
+
+
+def cpu_tiny_single_thread():
+    """The oracle's whole training step (forward, backward, Adam) of the tiny
+    fp32 decoder on one core: seconds and model TFLOPS."""
+    from threadpoolctl import threadpool_limits
+    from oracle import Oracle
+    shape = datagen.PRESETS["tiny"]
+    P = datagen.init_params(shape)
+    tok = datagen.tokens(shape)
+    prev = os.sched_getaffinity(0)
+    try:
+        os.sched_setaffinity(0, {min(prev)})
+        with threadpool_limits(1):
+            Oracle(shape, np.float32).step(P, tok)
+            t0 = time.perf_counter()
+            Oracle(shape, np.float32).step(P, tok)
+            dt = time.perf_counter() - t0
+    finally:
+        os.sched_setaffinity(0, prev)
+    return {"seconds": dt, "model_tflops": flops(shape)[1] / dt / 1e12, "threads": 1,
+            "workload": "tiny fp32 decoder, 2 x 64 tokens, whole step"}
 
 
 def cpu_baseline(shape, tokens_sample, seconds_hint):
@@ -180,6 +227,7 @@ def cpu_baseline(shape, tokens_sample, seconds_hint):
     except AttributeError:  # pragma: no cover
         cores = os.cpu_count()
     return {"value": model_flops / dt / 1e12, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
+            **host_description(),
             "sample": f"one {shape.name}-shape decoder layer (d {sub.d_model}, F {sub.d_ff}, {sub.n_heads} heads) "
                       f"on 1 x {tokens_sample} tokens: forward + recompute + backward + Adam, float32 NumPy; "
                       f"{dt:.1f} s",
@@ -209,8 +257,13 @@ def main():
                     help="layers that keep their forward intermediates on the device, so that their backward "
                          "skips the recompute (bit-identical results): a count, or 'auto' for as many as fit in "
                          "HBM; 0 (default) recomputes every layer from its layer-boundary checkpoint")
-    ap.add_argument("--no-retained-variant", action="store_true",
-                    help="skip the second measurement, with as many layers' intermediates kept on the device as fit")
+    ap.add_argument("--retained-variant", action="store_true",
+                    help="after the measurement, run the same step with as many layers' forward intermediates kept "
+                         "on the device as fit (their backward skips the recompute)")
+    ap.add_argument("--sdma-queues", action="store_true",
+                    help="prefetches and offloads on two SDMA engine queues fed by host threads instead of "
+                         "hipMemcpyAsync on the prefetch and offload streams")
+    ap.add_argument("--no-link-probe", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain 1 GiB device copy kernel first (the reference for HBM byte counters)")
     args = ap.parse_args()
@@ -235,6 +288,8 @@ def main():
     flags = 0 if args.no_kernel_timing else mt.MT_FLAG_TIME_KERNELS
     if args.duplex_link:
         flags |= mt.MT_FLAG_DUPLEX_LINK
+    if args.sdma_queues:
+        flags |= mt.MT_FLAG_SDMA_QUEUES
     K = max(1, args.micro_batches)
     cfg = mt.make_config(shape, mode=args.mode, flags=flags, micro_batches=K)
     R = 0
@@ -261,9 +316,11 @@ def main():
     log(f"initialised weights in {time.perf_counter() - t0:.1f} s")
     model = mt.Model(cfg, store, "cuda:0")
     log(f"device arena {model.arena.numel() / 1e9:.2f} GB")
-    layer_bytes = store.blocks[1].w_bytes
-    link = link_probe(torch, dev, layer_bytes)
-    log(f"host link: {link}")
+    link = None if args.no_link_probe else link_peak(mt)
+    if link:
+        for r in link["table"]:
+            log(f"host link {r['path']:11s} {r['bytes'] / 1e6:8.1f} MB: H2D {r['h2d_gbs']:.2f} D2H {r['d2h_gbs']:.2f} "
+                f"both {r['bidir_gbs']:.2f} GB/s")
     dram = host_triad(torch)
     log(f"host DRAM: {dram}")
     tokens = datagen.tokens(shape.replace(batch=K * shape.batch))
@@ -303,7 +360,7 @@ def main():
     elapsed = time.perf_counter() - t0
 
     fwd_layer, model_flops, hw_flops = flops(shape)
-    hw_flops -= R * fwd_layer  # retained layers skip their recompute
+    hw_flops -= R * (fwd_layer - 2.0 * shape.tokens * shape.d_model * shape.d_ff)  # retained layers skip their recompute
     value = K * model_flops * args.steps / elapsed / 1e12
     last = st_acc[-1]
     L = shape.n_layers
@@ -331,6 +388,7 @@ def main():
     if not args.no_cpu_baseline:
         log("oracle CPU baseline ...")
         cpu = cpu_baseline(shape, args.cpu_tokens, 20)
+        cpu["tiny_step_single_thread"] = cpu_tiny_single_thread()
         log(f"oracle: {cpu}")
     out = {
         "metric": "model TFLOPS/step on 1 MI355X (14B-shape) + H2D GB/s vs host-link peak",
@@ -361,8 +419,10 @@ def main():
             "hw_tflops": K * hw_flops * args.steps / elapsed / 1e12,
             "device_ms": last["device_ms"], "step_ms": last["step_ms"], "loss": loss,
             "h2d_gbs_achieved": h2d_gbs, "d2h_gbs_achieved": d2h_gbs,
+            "transfers": "sdma_queues" if args.sdma_queues else "hip_streams",
             "link_peak": link,
-            "h2d_frac_of_link_peak": h2d_gbs / link["h2d_gbs"] if h2d_gbs else None,
+            "h2d_frac_of_link_peak": h2d_gbs / link["h2d_gbs"] if h2d_gbs and link else None,
+            "d2h_frac_of_link_peak": d2h_gbs / link["d2h_gbs"] if d2h_gbs and link else None,
             "stall_ms": last["stall_ms"], "adam_ms": last["adam_ms"], "adam_tail_ms": last["adam_tail_ms"],
             "host_dram": dram,
             # bytes the host Adam moves per parameter: bf16 store W, G, m, v in and W, m, v out (22);
@@ -376,7 +436,7 @@ def main():
         },
     }
     model.close()
-    if R == 0 and args.mode == "streamed" and not args.no_retained_variant and not args.copy_probe:
+    if R == 0 and args.mode == "streamed" and args.retained_variant and not args.copy_probe:
         out["detail"]["retained_variant"] = retained_variant(torch, mt, dev, shape, flags, K, store, tokens,
                                                              args.warmup, args.steps, K * model_flops)
     store.free()

@@ -2,7 +2,8 @@
 
 Argument marshalling only: every step of the training step runs in the HIP
 library (include/mt.h, include/mt_kernels.h).  PyTorch provides the device
-arena and the compute stream; the pinned host store comes from the library.
+arena and the three streams (prefetch, compute, offload); the pinned host
+store comes from the library.
 The binding raises if the library has not been built — there is no
 fallback path.
 """
@@ -24,7 +25,7 @@ MT_STREAMED, MT_SERIALIZED, MT_RESIDENT, MT_SINGLE_SLOT = 0, 1, 2, 3
 MODES = {"streamed": MT_STREAMED, "serialized": MT_SERIALIZED, "resident": MT_RESIDENT,
          "single_slot": MT_SINGLE_SLOT}
 MT_BLOCK_EMBED, MT_BLOCK_LAYER, MT_BLOCK_HEAD = 0, 1, 2
-MT_FLAG_TIME_KERNELS, MT_FLAG_POISON, MT_FLAG_DUPLEX_LINK = 1, 2, 4
+MT_FLAG_TIME_KERNELS, MT_FLAG_POISON, MT_FLAG_DUPLEX_LINK, MT_FLAG_KEEP_DX, MT_FLAG_SDMA_QUEUES = 1, 2, 4, 8, 16
 EPI_STORE, EPI_F32, EPI_ADD_F32 = 0, 1, 2
 GEMM_A_KMAJOR, GEMM_B_KMAJOR = 1, 2
 
@@ -57,6 +58,11 @@ class MtStats(ctypes.Structure):
                 ("n_blocks", ctypes.c_int32), ("pad_", ctypes.c_int32), ("gemm_bytes", ctypes.c_double)]
 
 
+class MtLayout(ctypes.Structure):
+    _fields_ = [("dma_bytes", ctypes.c_uint64), ("opt_bytes", ctypes.c_uint64), ("n_blocks", ctypes.c_int32),
+                ("pad_", ctypes.c_int32)]
+
+
 class MtBlockStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_double) for n in
                 ("fwd_ms", "bwd_ms", "h2d_fwd_ms", "h2d_bwd_ms", "d2h_ms", "stall_fwd_ms", "stall_bwd_ms",
@@ -72,6 +78,8 @@ class MtError(RuntimeError):
 _lib = None
 
 _SIGS = {
+    "mt_host_store_layout": (ctypes.c_int, [ctypes.POINTER(MtConfig), ctypes.POINTER(MtLayout),
+                                            ctypes.POINTER(MtBlockDesc), ctypes.c_int32]),
     "mt_host_store_bytes": (ctypes.c_size_t, [ctypes.POINTER(MtConfig)]),
     "mt_host_opt_bytes": (ctypes.c_size_t, [ctypes.POINTER(MtConfig)]),
     "mt_alloc_host_opt": (ctypes.c_int, [ctypes.c_size_t, ctypes.POINTER(ctypes.c_void_p)]),
@@ -89,7 +97,7 @@ _SIGS = {
     "mt_store_load": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
                                      ctypes.c_char_p]),
     "mt_create_model": (ctypes.c_int, [ctypes.POINTER(MtConfig), ctypes.c_void_p, ctypes.c_size_t,
-                                       ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]),
+                                       ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p)]),
     "mt_bind_host_store": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                           ctypes.c_size_t]),
     "mt_train_step": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p]),
@@ -98,6 +106,7 @@ _SIGS = {
     "mt_get_block_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(MtBlockStats)]),
     "mt_debug_buffers": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
                                         ctypes.POINTER(ctypes.c_void_p)]),
+    "mt_debug_grad": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_void_p)]),
     "mt_destroy_model": (None, [ctypes.c_void_p]),
     "mt_host_adam": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_double,
@@ -106,6 +115,9 @@ _SIGS = {
                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_double,
                                            ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_int32]),
     "mt_store_init_master": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t]),
+    "mt_link_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
+                                     ctypes.POINTER(ctypes.c_double)]),
     "mt_last_error": (ctypes.c_char_p, []),
     "mt_version": (ctypes.c_char_p, []),
     "mt_gemm": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
@@ -196,16 +208,17 @@ def device_bytes(cfg: MtConfig) -> int:
     return n
 
 
+def store_layout(cfg: MtConfig):
+    """(mt_layout, [mt_block_desc per block]) of the host store of cfg."""
+    lay = MtLayout()
+    check(lib().mt_host_store_layout(ctypes.byref(cfg), ctypes.byref(lay), None, 0))
+    blocks = (MtBlockDesc * lay.n_blocks)()
+    check(lib().mt_host_store_layout(ctypes.byref(cfg), ctypes.byref(lay), blocks, lay.n_blocks))
+    return lay, list(blocks)
+
+
 def block_infos(cfg: MtConfig) -> list:
-    n = lib().mt_block_count(ctypes.byref(cfg))
-    if n < 0:
-        check(n)
-    out = []
-    for i in range(n):
-        b = MtBlockDesc()
-        check(lib().mt_block_info(ctypes.byref(cfg), i, ctypes.byref(b)))
-        out.append(b)
-    return out
+    return store_layout(cfg)[1]
 
 
 def _view(addr: int, nbytes: int, dtype) -> np.ndarray:
@@ -312,7 +325,8 @@ class HostStore:
 
 
 class Model:
-    """A model handle bound to a host store; device arena and compute stream from torch."""
+    """A model handle bound to a host store; device arena and the prefetch,
+    compute and offload streams (default priority) from torch."""
 
     def __init__(self, cfg: MtConfig, store: HostStore, device: str = "cuda:0"):
         import torch
@@ -322,11 +336,12 @@ class Model:
         self.device = torch.device(device)
         nbytes = device_bytes(cfg)
         self.arena = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
-        self.stream = torch.cuda.Stream(device=self.device)  # compute
+        self.streams = [torch.cuda.Stream(device=self.device) for _ in range(3)]  # prefetch, compute, offload
+        self.stream = self.streams[1]
+        sv = (ctypes.c_void_p * 3)(*[s.cuda_stream for s in self.streams])
         h = ctypes.c_void_p()
         torch.cuda.synchronize(self.device)
-        check(lib().mt_create_model(ctypes.byref(cfg), self.arena.data_ptr(), nbytes, self.stream.cuda_stream,
-                                    ctypes.byref(h)))
+        check(lib().mt_create_model(ctypes.byref(cfg), self.arena.data_ptr(), nbytes, sv, ctypes.byref(h)))
         self.handle = h.value
         check(lib().mt_bind_host_store(self.handle, store.ptr, store.nbytes, store.opt_ptr, store.opt_nbytes))
 
@@ -366,6 +381,15 @@ class Model:
         return self._arena_view(p.value, c.batch * c.seq_len * c.d_model, self.torch.float32).view(
             c.batch * c.seq_len, c.d_model)
 
+    def grad(self, layer: int):
+        """fp32 gradient dl/dx^layer arriving at layer boundary `layer` [B*T x d]
+        (device tensor view; needs MT_FLAG_KEEP_DX)."""
+        p = ctypes.c_void_p()
+        check(lib().mt_debug_grad(self.handle, layer, ctypes.byref(p)))
+        c = self.cfg
+        return self._arena_view(p.value, c.batch * c.seq_len * c.d_model, self.torch.float32).view(
+            c.batch * c.seq_len, c.d_model)
+
     def row_loss(self):
         p = ctypes.c_void_p()
         check(lib().mt_debug_buffers(self.handle, 0, None, ctypes.byref(p)))
@@ -384,6 +408,38 @@ class Model:
             self.close()
         except Exception:
             pass
+
+
+def link_probe(sizes, reps=4, sdma=False, device="cuda:0") -> list:
+    """Host-link GB/s (host->device, device->host, both at once) with the
+    library's own copy path (mt_link_probe) at each byte count in `sizes`."""
+    import torch
+    n = max(sizes)
+    ha, hb = ctypes.c_void_p(), ctypes.c_void_p()
+    check(lib().mt_alloc_host_store(n, ctypes.byref(ha)))
+    try:
+        check(lib().mt_alloc_host_store(n, ctypes.byref(hb)))
+    except MtError:
+        lib().mt_free_host_store(ha.value)
+        raise
+    try:
+        dev = torch.device(device)
+        da = torch.empty(n, dtype=torch.uint8, device=dev)
+        db = torch.empty(n, dtype=torch.uint8, device=dev)
+        ss = [torch.cuda.Stream(device=dev) for _ in range(2)]
+        sv = (ctypes.c_void_p * 2)(*[s.cuda_stream for s in ss])
+        torch.cuda.synchronize(dev)
+        out = []
+        for b in sizes:
+            r = (ctypes.c_double * 3)()
+            check(lib().mt_link_probe(da.data_ptr(), db.data_ptr(), ha.value, hb.value, int(b), int(reps),
+                                      MT_FLAG_SDMA_QUEUES if sdma else 0, sv, r))
+            out.append({"bytes": int(b), "h2d_gbs": r[0], "d2h_gbs": r[1], "bidir_gbs": r[2]})
+        del da, db
+        return out
+    finally:
+        lib().mt_free_host_store(ha.value)
+        lib().mt_free_host_store(hb.value)
 
 
 def init_store_weights(store: HostStore, draw, threads: int = 0):

@@ -30,7 +30,7 @@ HIP_SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "engine.hip"]
 # tile: MFMAs that write the general register file avoid copies through the
 # accumulation registers.
 FILE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
-HIPCC_HOST_SOURCES = ["store.cpp", "api.cpp", "kernel_api.cpp", "dma.cpp"]
+HIPCC_HOST_SOURCES = ["store.cpp", "api.cpp", "kernel_api.cpp", "dma.cpp", "linkprobe.cpp"]
 GXX_SOURCES = ["adam.cpp"]
 
 

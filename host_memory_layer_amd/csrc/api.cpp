@@ -41,7 +41,25 @@ static int guarded(F&& f) {
 
 using namespace mt;
 
+// The opaque handle of the C ABI is the engine's model object.
+static Model* M_(mt_model* h) { return reinterpret_cast<Model*>(h); }
+static const Model* M_(const mt_model* h) { return reinterpret_cast<const Model*>(h); }
+
 extern "C" {
+
+int mt_host_store_layout(const mt_config* cfg, mt_layout* out, mt_block_desc* blocks, int32_t capacity) {
+  return guarded([&] {
+    std::string why;
+    if (!cfg || !out) throw ApiError{MT_E_INVALID, "null argument"};
+    if (validate_config(*cfg, &why) != MT_OK) throw ApiError{MT_E_INVALID, why};
+    uint64_t dma = 0, opt = 0;
+    std::vector<mt_block_desc> b = store_layout(*cfg, &dma, &opt);
+    *out = mt_layout{dma, opt, (int32_t)b.size(), 0};
+    if (blocks)
+      for (int32_t i = 0; i < std::min<int32_t>(capacity, (int32_t)b.size()); ++i) blocks[i] = b[i];
+    return MT_OK;
+  });
+}
 
 size_t mt_host_store_bytes(const mt_config* cfg) {
   std::string why;
@@ -280,57 +298,65 @@ int mt_store_load(void* dma_base, size_t dma_bytes, void* opt_base, size_t opt_b
   });
 }
 
-int mt_create_model(const mt_config* cfg, void* dev_arena, size_t arena_bytes, void* stream, void** out) {
+int mt_create_model(const mt_config* cfg, void* dev_arena, size_t arena_bytes, void* const streams[3],
+                    mt_model** out) {
   return guarded([&] {
     if (!cfg || !out) throw ApiError{MT_E_INVALID, "null argument"};
-    *out = create_model(cfg, dev_arena, arena_bytes, stream);
+    *out = reinterpret_cast<mt_model*>(create_model(cfg, dev_arena, arena_bytes, streams));
     return MT_OK;
   });
 }
 
-int mt_bind_host_store(void* model, void* host_base, size_t bytes, void* opt_base, size_t opt_bytes) {
+int mt_bind_host_store(mt_model* model, void* host_base, size_t bytes, void* opt_base, size_t opt_bytes) {
   return guarded([&] {
     if (!model) throw ApiError{MT_E_INVALID, "null model"};
-    return bind_store((Model*)model, host_base, bytes, opt_base, opt_bytes);
+    return bind_store(M_(model), host_base, bytes, opt_base, opt_bytes);
   });
 }
 
-int mt_train_step(void* model, const int32_t* tokens) {
+int mt_train_step(mt_model* model, const int32_t* tokens) {
   return guarded([&] {
     if (!model) throw ApiError{MT_E_INVALID, "null model"};
-    return model_step((Model*)model, tokens);
+    return model_step(M_(model), tokens);
   });
 }
 
-int mt_get_loss(const void* model, float* out) {
+int mt_get_loss(const mt_model* model, float* out) {
   return guarded([&] {
     if (!model || !out) throw ApiError{MT_E_INVALID, "null argument"};
-    return model_loss((const Model*)model, out);
+    return model_loss(M_(model), out);
   });
 }
 
-int mt_get_stats(const void* model, mt_stats* out) {
+int mt_get_stats(const mt_model* model, mt_stats* out) {
   return guarded([&] {
     if (!model || !out) throw ApiError{MT_E_INVALID, "null argument"};
-    return model_stats((const Model*)model, out);
+    return model_stats(M_(model), out);
   });
 }
 
-int mt_get_block_stats(const void* model, int block, mt_block_stats* out) {
+int mt_get_block_stats(const mt_model* model, int block, mt_block_stats* out) {
   return guarded([&] {
     if (!model || !out) throw ApiError{MT_E_INVALID, "null argument"};
-    return model_block_stats((const Model*)model, block, out);
+    return model_block_stats(M_(model), block, out);
   });
 }
 
-int mt_debug_buffers(const void* model, int layer, void** ckpt, void** row_loss) {
+int mt_debug_buffers(const mt_model* model, int layer, void** ckpt, void** row_loss) {
   return guarded([&] {
     if (!model) throw ApiError{MT_E_INVALID, "null model"};
-    return model_debug((const Model*)model, layer, ckpt, row_loss);
+    return model_debug(M_(model), layer, ckpt, row_loss);
   });
 }
 
-void mt_destroy_model(void* model) { destroy_model((Model*)model); }
+int mt_debug_grad(const mt_model* model, int layer, void** dx) {
+  return guarded([&] {
+    if (!model || !dx) throw ApiError{MT_E_INVALID, "null argument"};
+    return model_debug_grad(M_(model), layer, dx);
+  });
+}
+
+void mt_destroy_model(mt_model* model) { destroy_model(M_(model)); }
 
 int mt_host_adam(int32_t store_dtype, void* w, const void* g, float* m, float* v, size_t n, int64_t t, double lr,
                  double beta1, double beta2, double eps, int32_t threads) {

@@ -6,7 +6,7 @@
 namespace mt {
 
 struct Model;
-Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void* stream);
+Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void* const streams[3]);
 void destroy_model(Model* m);
 uint64_t device_bytes_for(const mt_config& cfg);
 int bind_store(Model* m, void* host, size_t bytes, void* opt, size_t opt_bytes);
@@ -15,5 +15,6 @@ int model_loss(const Model* m, float* out);
 int model_stats(const Model* m, mt_stats* out);
 int model_block_stats(const Model* m, int block, mt_block_stats* out);
 int model_debug(const Model* m, int layer, void** ckpt, void** row_loss);
+int model_debug_grad(const Model* m, int layer, void** dx);
 
 }  // namespace mt

@@ -110,7 +110,11 @@ struct Model {
 
   uint8_t* arena = nullptr;
   size_t arena_bytes = 0;
-  hipStream_t sc;  // compute stream
+  hipStream_t sp, sc, so;  // prefetch, compute and offload streams (caller-owned)
+  // Transfers: hipMemcpyAsync on the prefetch and offload streams, ordered
+  // by events (hipq), or the two SDMA engine queues of dma.h
+  bool hipq = true;
+  bool yield_link = false;  // offloads give the host link to prefetches (see run_pass)
   uint8_t* host = nullptr;  // DMA part: header, [W | G] per block (pinned)
   uint8_t* hopt = nullptr;  // optimizer part: [m | v] per block
 
@@ -126,6 +130,11 @@ struct Model {
   uint8_t* head_mem;
   float* gemm_ws = nullptr;  // stream-K partial tiles of the bf16 GEMMs
   size_t gemm_ws_size = 0;
+  float* dxkeep = nullptr;   // MT_FLAG_KEEP_DX: dl/dx^l of every layer boundary, l = 0..L
+  // The bf16 copy ws.dxb mirrors one fp32 gradient at a time: the norm
+  // backward that writes it records which, and the K-major backward that
+  // reads it as the rounded dx2 checks that it is the dx2 it was given.
+  const float* dxb_holds = nullptr;
 
   // host pinned
   int32_t *h_tok = nullptr, *h_order = nullptr, *h_seg = nullptr;
@@ -135,6 +144,9 @@ struct Model {
   int n_uses;
   std::vector<hipEvent_t> ev_c_s, ev_c_e;  // compute of each use: start, end
   std::vector<hipEvent_t> ev_slot_free;    // MT_FLAG_POISON: slot NaN-filled, ready for the prefetch of a use
+  std::vector<hipEvent_t> ev_x_s, ev_x_e;  // prefetch stream: copy of each use's weights, start and end
+  std::vector<hipEvent_t> ev_o_s, ev_o_e;  // offload stream: copy of each use's gradients, start and end
+  std::vector<char> u_fetched, u_offloaded;  // which uses had a prefetch / an offload this pass
   hipEvent_t ev_h2d_s, ev_h2d_e, ev_d2h_s, ev_d2h_e;  // resident schedule: all uploads, all offloads
   hipEvent_t ev_loss, ev_start, ev_end;
   std::vector<hipEvent_t> kev;  // kernel timing pairs
@@ -254,6 +266,8 @@ struct Model {
       gemm_ws = gemm_ws_size ? c.take<float>(gemm_ws_size) : nullptr;
       if (!base) gemm_ws = nullptr;
     }
+    dxkeep = cfg.flags & MT_FLAG_KEEP_DX ? c.take<float>((uint64_t)(L + 1) * M * d * 4) : nullptr;
+    if (!base) dxkeep = nullptr;
     return c.off;
   }
   // Layers whose forward intermediates stay on the device until their backward.
@@ -322,6 +336,11 @@ struct Model {
   uint64_t device_bytes() { return bf16_store(cfg) ? carve_all<uint16_t>(nullptr) : carve_all<float>(nullptr); }
 
   float* x_ckpt(int l) { return ckpt + (uint64_t)l * M * d; }
+  // MT_FLAG_KEEP_DX: a copy of the gradient arriving at layer boundary l
+  void keep_dx(int l, const float* dx) {
+    if (dxkeep)
+      MT_HIP(hipMemcpyAsync(dxkeep + (uint64_t)l * M * d, dx, (uint64_t)M * d * 4, hipMemcpyDeviceToDevice, sc));
+  }
 
   // --------------------------------------------------------- kernels --
   template <typename T>
@@ -431,8 +450,9 @@ struct Model {
   void layer_bwd_kmajor(const LayerW<T>& w, const float* x, const Acts<T>& a, const float* dx2, float* dx_out,
                         const LayerW<T>& g, const BwdWs<T>& ws) {
     const int KA = GEMM_A_KMAJOR, KB = GEMM_B_KMAJOR;
-    // down projection; ws.dxb = T(dx2) was written beside dx2 by the norm
+    // down projection; ws.dxb = bf16(dx2) was written beside dx2 by the norm
     // backward that produced it (the layer above, or the head)
+    if (dxb_holds != dx2) throw ApiError{MT_E_STATE, "K-major layer backward: bf16 copy does not mirror its dx"};
     gemm<T>(ws.dxb, d, a.y, F, g.d, F, nullptr, 0, d, F, M, EPI_STORE, KA | KB);
     gemm<T>(ws.dxb, d, w.d, F, ws.dy, F, nullptr, 0, M, F, d, EPI_STORE, KB);
     // SwiGLU and gate/up projection
@@ -440,7 +460,8 @@ struct Model {
     gemm<T>(ws.dgu, 2 * F, a.h2, d, g.gu, d, nullptr, 0, 2 * F, d, M, EPI_STORE, KA | KB);
     gemm<T>(ws.dgu, 2 * F, w.gu, d, ws.dh, d, nullptr, 0, M, d, 2 * F, EPI_F32, KB);
     rmsnorm_bwd<T>(ws.dh, a.x1, w.fnorm, a.r2, dx2, ws.dx1, ws.part, g.fnorm, M, d, sc, ws.dxb);
-    // attention output projection (ws.dxb = T(dx1))
+    dxb_holds = ws.dx1;
+    // attention output projection (ws.dxb = bf16(dx1))
     gemm<T>(ws.dxb, d, a.o, d, g.o, d, nullptr, 0, d, d, M, EPI_STORE, KA | KB);
     gemm<T>(ws.dxb, d, w.o, d, ws.do_, d, nullptr, 0, M, d, d, EPI_STORE, KB);
     // attention
@@ -454,8 +475,9 @@ struct Model {
     // and K-major for the data gradient
     gemm<T>(ws.dqkvT, Mp, a.h, d, g.qkv, d, nullptr, 0, 3 * d, d, M, EPI_STORE, KB);
     gemm<T>(ws.dqkvT, Mp, w.qkv, d, ws.dh, d, nullptr, 0, M, d, 3 * d, EPI_F32, KA | KB);
-    // dx_out, and T(dx_out) for the next layer's down projection
+    // dx_out, and bf16(dx_out) for the next layer's down projection
     rmsnorm_bwd<T>(ws.dh, x, w.anorm, a.r1, ws.dx1, dx_out, ws.part, g.anorm, M, d, sc, ws.dxb);
+    dxb_holds = dx_out;
   }
 
   // Final norm, logits, loss, and the head's backward.  Returns dx^L in dx_out.
@@ -501,8 +523,10 @@ struct Model {
     sum_fixed(hw.row_loss, hw.loss, M, inv_n, sc);
     MT_HIP(hipMemcpyAsync(h_loss, hw.loss, sizeof(float), hipMemcpyDeviceToHost, sc));
     MT_HIP(hipEventRecord(ev_loss, sc));
-    // dx^L, and T(dx^L) for the top layer's down projection when it reads it
+    // dx^L, and bf16(dx^L) for the top layer's down projection when it reads it
     rmsnorm_bwd<T>(ws.dh, xL, fin, hw.rz, nullptr, dx_out, ws.part, gfin, M, d, sc, kmajor ? ws.dxb : nullptr);
+    dxb_holds = kmajor ? dx_out : nullptr;
+    keep_dx(L, dx_out);
   }
 
   // ------------------------------------------------------------ step --
@@ -531,6 +555,7 @@ struct Model {
     if (cfg.mode != MT_RESIDENT && !retained(l)) layer_fwd<T>(w, x_ckpt(l), a, nullptr, false);  // recompute
     if (!kmajor) weight_transposes<T>(w, t);
     layer_bwd<T>(w, t, x_ckpt(l), a, dx_in, dx_out, g);
+    keep_dx(l, dx_out);
   }
 
   template <typename T>
@@ -637,11 +662,25 @@ void Model::adam_worker(int64_t t, double* adam_total, double* adam_tail, std::a
 // layers), and u = 2L+2 for the embedding backward.  Block j uses weight
 // slot j%2, and consecutive backward uses alternate between the two
 // gradient slots.  A slot's next prefetch starts when the compute of its
-// last use has ended; a block's compute is enqueued once its prefetch is
-// done.  The serialized schedule lets nothing overlap: every copy starts
-// after all compute enqueued so far and ends before more work is enqueued.
-// The single-slot schedule keeps every block in slot 0, so each prefetch
-// waits for the previous block's compute (weights are not double-buffered;
+// last use has ended; a block's compute starts once its prefetch is done;
+// a gradient slot is written again once the offload that read it is done.
+//
+// With the three streams (the default) every one of these rules is an event
+// wait on the GPU: the prefetch stream waits for the compute-end event of
+// the slot's last use, the compute stream for the prefetch's copy-end event
+// and for the offload that last read the gradient slot, the offload stream
+// for the compute-end event of the use whose gradients it moves.  When the
+// offloads give the host link to the prefetches (yield_link), the offload of
+// a use is enqueued after the prefetch that becomes ready at the same moment
+// (the next one issued) and also waits for that prefetch's copy to end.
+// With MT_FLAG_SDMA_QUEUES the copies run on two SDMA engines fed by host
+// worker threads, and the enqueueing thread applies the same rules by
+// waiting on the host.
+//
+// The serialized schedule lets nothing overlap: every copy starts after all
+// compute enqueued so far and ends before more work is enqueued.  The
+// single-slot schedule keeps every block in slot 0, so each prefetch waits
+// for the previous block's compute (weights are not double-buffered;
 // gradient offloads still overlap), and block L is fetched again for its
 // backward because the head has replaced it.
 template <typename T>
@@ -650,11 +689,17 @@ void Model::step_streamed(bool serialize) {
   auto slot_of = [&](int j) { return single ? 0 : j % 2; };
   const bool poison = cfg.flags & MT_FLAG_POISON;
   const uint32_t nan_word = E == 2 ? 0x7FC07FC0u : 0x7FC00000u;
-  std::vector<int> slot_last_use(2, -1);  // use that last bound each weight slot
-  std::vector<int> fetch_job(n_uses, -1);  // prefetch job of each use
-  std::vector<int> gslot_last(2, -1);     // offload job that last read each grad slot
+  std::vector<int> slot_last_use(2, -1);   // use that last bound each weight slot
+  std::vector<int> fetch_job(n_uses, -1);  // SDMA queues: prefetch job of each use
+  std::vector<int> gslot_last(2, -1);      // the offload (job, or use on streams) that last read each grad slot
   int gcount = 0;
   int last_out = -1;
+  u_fetched.assign(n_uses, 0);
+  u_offloaded.assign(n_uses, 0);
+  struct Pending {
+    int u, j, g;
+  } pending{-1, -1, -1};
+  const bool defer = hipq && yield_link && !serialize;
 
   auto fetch = [&](int u, int j) {
     const int s = slot_of(j);
@@ -669,11 +714,24 @@ void Model::step_streamed(bool serialize) {
       MT_HIP(hipStreamSynchronize(sc));
       ready = nullptr;
     }
-    fetch_job[u] = xq_in->push({u, j, ready, wslot[s], host + blocks[j].w_off, (size_t)blocks[j].w_bytes});
-    if (serialize) xq_in->wait(fetch_job[u]);
+    u_fetched[u] = 1;
+    if (hipq) {
+      if (ready) MT_HIP(hipStreamWaitEvent(sp, ready, 0));
+      MT_HIP(hipEventRecord(ev_x_s[u], sp));
+      MT_HIP(hipMemcpyAsync(wslot[s], host + blocks[j].w_off, blocks[j].w_bytes, hipMemcpyHostToDevice, sp));
+      MT_HIP(hipEventRecord(ev_x_e[u], sp));
+      if (serialize) MT_HIP(hipStreamSynchronize(sp));
+    } else {
+      fetch_job[u] = xq_in->push({u, j, ready, wslot[s], host + blocks[j].w_off, (size_t)blocks[j].w_bytes});
+      if (serialize) xq_in->wait(fetch_job[u]);
+    }
   };
   auto begin = [&](int u) {
-    if (fetch_job[u] >= 0) xq_in->wait(fetch_job[u]);
+    if (hipq) {
+      if (u_fetched[u]) MT_HIP(hipStreamWaitEvent(sc, ev_x_e[u], 0));
+    } else if (fetch_job[u] >= 0) {
+      xq_in->wait(fetch_job[u]);
+    }
     MT_HIP(hipEventRecord(ev_c_s[u], sc));
   };
   auto end = [&](int u, int j) {
@@ -683,19 +741,48 @@ void Model::step_streamed(bool serialize) {
   // Grad slot for a backward use: the offload that last read it has finished.
   auto grad_slot = [&]() -> int {
     const int g = gcount % 2;
-    if (gslot_last[g] >= 0) xq_out->wait(gslot_last[g]);
+    if (gslot_last[g] >= 0) {
+      if (hipq)
+        MT_HIP(hipStreamWaitEvent(sc, ev_o_e[gslot_last[g]], 0));
+      else
+        xq_out->wait(gslot_last[g]);
+    }
     return g;
   };
-  auto offload = [&](int u, int j, int g) {
+  // after_fetch >= 0: the offload also waits for that use's prefetch copy
+  auto issue_offload = [&](int u, int j, int g, int after_fetch) {
     hipEvent_t ready = ev_c_e[u];
     if (serialize) {
       MT_HIP(hipStreamSynchronize(sc));
       ready = nullptr;
     }
-    last_out = xq_out->push({u, j, ready, host + blocks[j].g_off, gslot[g], (size_t)blocks[j].w_bytes});
+    u_offloaded[u] = 1;
+    if (hipq) {
+      if (ready) MT_HIP(hipStreamWaitEvent(so, ready, 0));
+      if (after_fetch >= 0) MT_HIP(hipStreamWaitEvent(so, ev_x_e[after_fetch], 0));
+      MT_HIP(hipEventRecord(ev_o_s[u], so));
+      MT_HIP(hipMemcpyAsync(host + blocks[j].g_off, gslot[g], blocks[j].w_bytes, hipMemcpyDeviceToHost, so));
+      MT_HIP(hipEventRecord(ev_o_e[u], so));
+      push_adam(j, ev_o_e[u]);
+      last_out = u;
+      if (serialize) MT_HIP(hipStreamSynchronize(so));
+    } else {
+      last_out = xq_out->push({u, j, ready, host + blocks[j].g_off, gslot[g], (size_t)blocks[j].w_bytes});
+      if (serialize) xq_out->wait(last_out);
+    }
     gslot_last[g] = last_out;
+  };
+  auto offload = [&](int u, int j, int g) {
     ++gcount;
-    if (serialize) xq_out->wait(last_out);
+    if (defer)
+      pending = Pending{u, j, g};
+    else
+      issue_offload(u, j, g, -1);
+  };
+  // the held offload, ordered after prefetch `after_fetch` (-1: none left)
+  auto flush = [&](int after_fetch) {
+    if (pending.u >= 0) issue_offload(pending.u, pending.j, pending.g, after_fetch);
+    pending = Pending{-1, -1, -1};
   };
 
   BwdWs<T> ws = bwdws<T>();
@@ -724,11 +811,17 @@ void Model::step_streamed(bool serialize) {
     const int j = L - i;
     const int u = L + 2 + i;
     // block L is still in its slot from the forward; the others are fetched
-    // again (the prefetch of use u+1 is issued before use u computes)
-    if (single)
+    // again (the prefetch of use u+1 is issued before use u computes).  The
+    // offload of use u-1 became ready when this prefetch did.
+    int fu = -1;
+    if (single) {
       fetch(u, j);
-    else if (j - 1 >= 1)
+      fu = u;
+    } else if (j - 1 >= 1) {
       fetch(u + 1, j - 1);
+      fu = u + 1;
+    }
+    flush(fu);
     const int g = grad_slot();
     begin(u);
     compute_layer_bwd<T>(j, wslot[slot_of(j)], gslot[g], dx_in, dx_out);
@@ -738,15 +831,20 @@ void Model::step_streamed(bool serialize) {
   }
   {
     const int u = 2 * L + 2;
+    flush(-1);
     const int g = grad_slot();
     begin(u);
     const mt_block_desc& b = blocks[0];
     embed_bwd<T>(dx_in, d_order, d_seg, (T*)gslot[g] + b.tensors[0].offset, V, d, sc);
     MT_HIP(hipEventRecord(ev_c_e[u], sc));
     offload(u, 0, g);
+    flush(-1);
   }
   // The step's device timeline ends once the last offload has landed.
-  xq_out->wait(last_out);
+  if (hipq)
+    MT_HIP(hipStreamWaitEvent(sc, ev_o_e[last_out], 0));
+  else
+    xq_out->wait(last_out);
   MT_HIP(hipEventRecord(ev_end, sc));
 }
 
@@ -839,23 +937,26 @@ void Model::run_pass(const int32_t* tokens, int64_t t, double* adam_total, doubl
   for (auto& s : bstats) s = mt_block_stats{};
   std::atomic<bool> device_done{false};
   const bool streamed = cfg.mode != MT_RESIDENT;
-  if (streamed && !dma) {
-    dma.reset(new DmaEngines(gslot[0], host));
-    // Offloads yield the link to prefetches when a layer's backward is
-    // compute-bound against the link (its flops per transferred weight and
-    // gradient byte well above ~1 PFLOP/s over ~50 GB/s): the transfers are
-    // hidden either way and each then runs at the full one-way rate.  When
-    // the link is the bottleneck, both directions share it.
+  // Offloads yield the link to prefetches when a layer's backward is
+  // compute-bound against the link (its flops per transferred weight and
+  // gradient byte well above ~1 PFLOP/s over ~50 GB/s): the transfers are
+  // hidden either way and each then runs at the full one-way rate.  When the
+  // link is the bottleneck, both directions share it.
+  {
     const double layer_bytes = 2.0 * (double)blocks[1].w_bytes;
     const double bwd_flops = 3.0 * (2.0 * M * (4.0 * d * d + 3.0 * d * F)) + 3.5 * attn_fwd_flops();
-    const bool yield = !(cfg.flags & MT_FLAG_DUPLEX_LINK) && bwd_flops / layer_bytes > 30000.0;
-    xq_in.reset(new TransferQueue(dma.get(), DMA_H2D, yield));
-    xq_out.reset(new TransferQueue(dma.get(), DMA_D2H, yield));
+    yield_link = !(cfg.flags & MT_FLAG_DUPLEX_LINK) && bwd_flops / layer_bytes > 30000.0;
+  }
+  const bool queues = streamed && !hipq;
+  if (queues && !dma) {
+    dma.reset(new DmaEngines(gslot[0], host));
+    xq_in.reset(new TransferQueue(dma.get(), DMA_H2D, yield_link));
+    xq_out.reset(new TransferQueue(dma.get(), DMA_D2H, yield_link));
   }
   h2d_host_ms.assign(n_uses, 0.0);
   d2h_host_ms.assign(n_uses, 0.0);
   std::thread worker([&] { adam_worker(t, adam_total, adam_tail, &device_done); });
-  if (streamed) {
+  if (queues) {
     xq_in->start(&h2d_host_ms, nullptr);
     xq_out->start(&d2h_host_ms, [this](const TransferQueue::Job& job) { push_adam(job.j, nullptr); });
   }
@@ -878,13 +979,16 @@ void Model::run_pass(const int32_t* tokens, int64_t t, double* adam_total, doubl
     enqueue_error = e.msg;
   }
   // Every copy that was enqueued finishes (or fails) before the Adam queue
-  // closes, so Adam sees every block whose gradients arrived.
-  if (streamed) {
+  // closes, so Adam sees every block whose gradients arrived.  On the
+  // streams, each offload was handed to Adam with its completion event.
+  if (queues) {
     xq_in->stop();
     xq_out->stop();
   }
   close_adam();
   hipError_t e1 = hipStreamSynchronize(sc);
+  if (e1 == hipSuccess) e1 = hipStreamSynchronize(sp);
+  if (e1 == hipSuccess) e1 = hipStreamSynchronize(so);
   device_done = true;
   worker.join();
   if (enqueue_code != MT_OK) throw ApiError{enqueue_code, enqueue_error};
@@ -904,9 +1008,13 @@ void Model::finish_stats(bool streamed, double wall_ms) {
   s.device_ms = ms_between(ev_start, ev_end);
   if (streamed) {
     for (int u = 0; u < n_uses; ++u) {
-      const bool has_h2d = (u <= L + 1) || (u >= L + 3 && u <= 2 * L + 1);
-      const bool has_d2h = (u >= L + 1);
+      const bool has_h2d = u < (int)u_fetched.size() && u_fetched[u];
+      const bool has_d2h = u < (int)u_offloaded.size() && u_offloaded[u];
       const int j = u <= L + 1 ? u : (u <= 2 * L + 1 ? L - (u - (L + 2)) : 0);
+      if (hipq) {
+        if (has_h2d) h2d_host_ms[u] = ms_between(ev_x_s[u], ev_x_e[u]);
+        if (has_d2h) d2h_host_ms[u] = ms_between(ev_o_s[u], ev_o_e[u]);
+      }
       const double c = ms_between(ev_c_s[u], ev_c_e[u]);
       // compute-stream idle time before this use: the enqueueing thread
       // held it back until the block's weights had arrived and its grad
@@ -976,10 +1084,13 @@ static std::vector<float> rope_table(int T, int hd, double theta, bool sine) {
   return out;
 }
 
-Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void* stream) {
+Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void* const streams[3]) {
   std::string why;
   if (validate_config(*cfg, &why) != MT_OK) throw ApiError{MT_E_INVALID, why};
-  if (!arena || !stream) throw ApiError{MT_E_INVALID, "null arena or compute stream"};
+  if (!arena || !streams || !streams[0] || !streams[1] || !streams[2])
+    throw ApiError{MT_E_INVALID, "null arena or stream"};
+  if (streams[0] == streams[1] || streams[1] == streams[2] || streams[0] == streams[2])
+    throw ApiError{MT_E_INVALID, "prefetch, compute and offload need three different streams"};
   if ((uintptr_t)arena & 255) throw ApiError{MT_E_ALIGN, "device arena must be 256-byte aligned"};
   std::unique_ptr<Model> m(new Model());
   m->init_dims(*cfg);
@@ -987,7 +1098,10 @@ Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void*
   if (arena_bytes < need) throw ApiError{MT_E_SIZE, "device arena smaller than mt_device_bytes"};
   m->arena = (uint8_t*)arena;
   m->arena_bytes = arena_bytes;
-  m->sc = (hipStream_t)stream;
+  m->sp = (hipStream_t)streams[0];
+  m->sc = (hipStream_t)streams[1];
+  m->so = (hipStream_t)streams[2];
+  m->hipq = !(cfg->flags & MT_FLAG_SDMA_QUEUES);
   if (bf16_store(*cfg))
     m->carve_all<uint16_t>(m->arena);
   else
@@ -1028,6 +1142,10 @@ Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void*
   mk(m->ev_c_s);
   mk(m->ev_c_e);
   mk(m->ev_slot_free);
+  mk(m->ev_x_s);
+  mk(m->ev_x_e);
+  mk(m->ev_o_s);
+  mk(m->ev_o_e);
   for (hipEvent_t* e : {&m->ev_h2d_s, &m->ev_h2d_e, &m->ev_d2h_s, &m->ev_d2h_e}) MT_HIP(hipEventCreate(e));
   MT_HIP(hipEventCreate(&m->ev_loss));
   MT_HIP(hipEventCreate(&m->ev_start));
@@ -1046,7 +1164,9 @@ Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void*
 void destroy_model(Model* m) {
   if (!m) return;
   hipStreamSynchronize(m->sc);
-  for (auto* v : {&m->ev_c_s, &m->ev_c_e, &m->ev_slot_free})
+  hipStreamSynchronize(m->sp);
+  hipStreamSynchronize(m->so);
+  for (auto* v : {&m->ev_c_s, &m->ev_c_e, &m->ev_slot_free, &m->ev_x_s, &m->ev_x_e, &m->ev_o_s, &m->ev_o_e})
     for (auto e : *v) hipEventDestroy(e);
   for (hipEvent_t e : {m->ev_h2d_s, m->ev_h2d_e, m->ev_d2h_s, m->ev_d2h_e}) hipEventDestroy(e);
   for (auto e : m->kev) hipEventDestroy(e);
@@ -1117,6 +1237,13 @@ int model_stats(const Model* m, mt_stats* out) {
 int model_block_stats(const Model* m, int block, mt_block_stats* out) {
   if (block < 0 || block >= (int)m->bstats.size()) throw ApiError{MT_E_INVALID, "block index"};
   *out = m->bstats[block];
+  return MT_OK;
+}
+
+int model_debug_grad(const Model* m, int layer, void** dx) {
+  if (!m->dxkeep) throw ApiError{MT_E_STATE, "gradients are kept only with MT_FLAG_KEEP_DX"};
+  if (layer < 0 || layer > m->L) throw ApiError{MT_E_INVALID, "layer index"};
+  *dx = m->dxkeep + (uint64_t)layer * m->M * m->d;
   return MT_OK;
 }
 

@@ -1,14 +1,23 @@
 /*
  * mt.h — C ABI of the MI355X layer-streamed training library.
  *
- * The method (MegaTrain, arXiv 2026; chatpaper.ai abstract and
- * radar.chestersoft.de "Methodik"): parameters and optimizer state live in
- * host memory; for each layer the weights stream in to the GPU and the
- * gradients stream out; a double-buffered engine overlaps prefetch, compute
- * and gradient offload on three streams; stateless layer templates bind the
- * incoming weights; every state of a layer (bf16 weights, bf16 gradients,
- * fp32 Adam moments) sits in one contiguous 4 KiB-aligned block; the Adam
- * step runs on the host CPU.
+ * The method (MegaTrain; pages cited as [Abstract] = chatpaper.ai,
+ * "MegaTrain: Full Precision Training of 100B+ Parameter Large Language
+ * Models on a Single GPU", Abstract; [Methodik], [Kernaussagen] =
+ * radar.chestersoft.de summary of the paper, those sections;
+ * [Innovaciones] = ecosistemastartup.com, "MegaTrain: entrena LLMs de 100B+
+ * en una sola GPU", section on the key technical innovations):
+ *   - parameters and optimizer state live in host memory and the GPU is a
+ *     transient engine: per layer, weights stream in and gradients stream
+ *     out [Abstract], [Kernaussagen], [Innovaciones] 1;
+ *   - a double-buffered engine overlaps weight prefetch, compute and
+ *     gradient offload on three streams in a ping-pong over two weight
+ *     buffers [Methodik] (execution engine), [Abstract] 1);
+ *   - stateless layer templates bind the incoming weights instead of an
+ *     autograd graph [Methodik], [Abstract] 2), [Innovaciones] 3;
+ *   - each layer's states (bf16 weights and gradients, fp32 Adam moments)
+ *     are packed into contiguous 4 KiB-aligned blocks, and the Adam step
+ *     runs on the host CPU with AVX-512 [Methodik] (layer-contiguous tiling).
  *
  * Conventions of every call:
  *   - return 0 (MT_OK) on success or a negative MT_E_* code; no exception or
@@ -38,6 +47,9 @@ extern "C" {
 #define MT_E_NONFINITE (-6)  /* loss not finite: no Adam ran, the store's W/m/v are untouched */
 #define MT_E_OOM (-7)        /* host allocation failed */
 #define MT_E_STATE (-8)      /* wrong call order or unsupported mode for this call */
+
+/* Opaque model handle (mt_create_model .. mt_destroy_model). */
+typedef struct mt_model mt_model;
 
 /* ------------------------------------------------------------- constants -- */
 #define MT_F32 0             /* all-fp32 store: W, G, m, v in float32 */
@@ -96,6 +108,16 @@ typedef struct mt_config {
                                    offloads wait for prefetches (which never wait for offloads) when a
                                    layer's backward does more than 30k flops per transferred byte, and
                                    share the link otherwise */
+#define MT_FLAG_KEEP_DX 8       /* keep the gradient of the loss at every layer boundary, dl/dx^l for
+                                   l = 0..n_layers (fp32, batch*seq_len x d_model each), in the device
+                                   arena until the next step, for inspection (mt_debug_grad); adds
+                                   (n_layers+1)*batch*seq_len*d_model*4 bytes to mt_device_bytes */
+#define MT_FLAG_SDMA_QUEUES 16  /* run the weight prefetches and gradient offloads on two of the GPU's
+                                   SDMA engines (one per direction), each fed in order by a host worker
+                                   thread that waits for the events the copy depends on, instead of
+                                   hipMemcpyAsync on the prefetch and offload streams; the schedule and
+                                   the results are the same.  The prefetch and offload streams then
+                                   carry no work */
 
 /* One tensor inside a block region: element offset from the region start,
  * row-major [rows x cols]. */
@@ -162,7 +184,21 @@ typedef struct mt_block_stats {
   double fwd_ms, bwd_ms, h2d_fwd_ms, h2d_bwd_ms, d2h_ms, stall_fwd_ms, stall_bwd_ms, adam_ms;
 } mt_block_stats;
 
+/* Sizes of the whole host store (mt_host_store_layout). */
+typedef struct mt_layout {
+  uint64_t dma_bytes;  /* pinned part: header page + [W | G] per block */
+  uint64_t opt_bytes;  /* pageable part: [m | v] (+ P, A) per block */
+  int32_t n_blocks;    /* embed, n_layers layers, head */
+  int32_t pad_;
+} mt_layout;
+
 /* ------------------------------------------------------------ layout ----- */
+/* Layout of the host store of cfg ([Methodik], layer-contiguous tiling: one
+ * contiguous 4 KiB-aligned block of states per layer).  Fills *out; when
+ * `blocks` is not null, also blocks[i] for every block i < min(n_blocks,
+ * capacity) (same contents as mt_block_info).  Returns MT_OK, or
+ * MT_E_INVALID for a bad configuration or a null `out`. */
+int mt_host_store_layout(const mt_config* cfg, mt_layout* out, mt_block_desc* blocks, int32_t capacity);
 /* Bytes of the DMA part of the host store (header page + [W | G] of every block). */
 size_t mt_host_store_bytes(const mt_config* cfg);
 /* Bytes of the optimizer part of the host store ([m | v] of every block). */
@@ -209,40 +245,68 @@ int mt_store_save(const void* dma_base, size_t dma_bytes, const void* opt_base, 
 int mt_store_load(void* dma_base, size_t dma_bytes, void* opt_base, size_t opt_bytes, const char* path);
 
 /* ------------------------------------------------------------- model ----- */
-/* Create a model.  dev_arena: device memory of at least mt_device_bytes(cfg),
- * 256-byte aligned, caller-owned.  stream: the compute hipStream_t (default
- * priority), caller-owned; every kernel of the step runs on it.  The other
- * two streams of the method, weight prefetch and gradient offload, are
- * queues on two of the GPU's SDMA engines, each fed in order by a host
- * worker thread of the model.  No device work except uploading the RoPE
- * table; *out receives the handle. */
-int mt_create_model(const mt_config* cfg, void* dev_arena, size_t arena_bytes, void* stream, void** out);
-/* Bind a host store (DMA part from mt_alloc_host_store, optimizer part from
- * mt_alloc_host_opt or any 4 KiB-aligned host memory; header written,
- * weights initialised).  Checked: sizes >= mt_host_store_bytes and
- * mt_host_opt_bytes, 4 KiB alignment, header magic and shape; the DMA part
- * must be pinned. */
-int mt_bind_host_store(void* model, void* dma_base, size_t dma_bytes, void* opt_base, size_t opt_bytes);
-/* One training step on tokens (host int32 [micro_batches*batch*seq_len], or
- * [batch*seq_len] without micro-batches, values in [0, vocab)).  The loss is
- * the mean next-token loss over all micro-batches.  Synchronous: on return 0 the store holds the post-Adam W, m,
- * v, this step's G, and t+1 in the header.  On MT_E_NONFINITE no Adam ran. */
-int mt_train_step(void* model, const int32_t* tokens);
-/* Loss of the last completed step. */
-int mt_get_loss(const void* model, float* out);
-int mt_get_stats(const void* model, mt_stats* out);
-int mt_get_block_stats(const void* model, int block, mt_block_stats* out);
+/* Create a model: the engine that streams each layer through the GPU
+ * ([Abstract]: the GPU as a transient compute engine; [Methodik]: the
+ * pipelined double-buffered engine on three streams).
+ *   dev_arena: device memory of at least mt_device_bytes(cfg) bytes,
+ *     256-byte aligned, caller-owned (e.g. a torch uint8 tensor); it holds
+ *     the two weight slots, two gradient slots, the fp32 layer-boundary
+ *     checkpoints and one layer's workspace;
+ *   streams[3]: hipStream_t values, caller-owned, three different streams,
+ *     default priority: [0] weight prefetch (host -> device copies into the
+ *     ping-pong slots), [1] compute (every kernel of the step), [2] gradient
+ *     offload (device -> host copies); the library orders them with its own
+ *     hipEvents;
+ *   *out receives the handle.
+ * The arena and the streams must outlive the handle.  No device work except
+ * uploading the RoPE tables and zeroing the gradient slots.  Errors:
+ * MT_E_INVALID (configuration, null or repeated stream), MT_E_ALIGN, MT_E_SIZE
+ * (arena too small), MT_E_HIP. */
+int mt_create_model(const mt_config* cfg, void* dev_arena, size_t arena_bytes, void* const streams[3],
+                    mt_model** out);
+/* Bind a host store ([Kernaussagen], [Innovaciones] 1: parameters and
+ * optimizer state live in host memory).  DMA part from mt_alloc_host_store,
+ * optimizer part from mt_alloc_host_opt or any 4 KiB-aligned host memory;
+ * header written, weights initialised; both caller-owned and must outlive
+ * the handle.  Checked: sizes >= mt_host_store_bytes and mt_host_opt_bytes,
+ * 4 KiB alignment (MT_E_ALIGN), header magic and shape (MT_E_INVALID); the
+ * DMA part must be pinned (MT_E_INVALID). */
+int mt_bind_host_store(mt_model* model, void* dma_base, size_t dma_bytes, void* opt_base, size_t opt_bytes);
+/* One training step ([Abstract]: for each layer, parameters stream in and
+ * gradients stream out; the Adam step on the host CPU, [Methodik]) on tokens:
+ * host int32 [micro_batches*batch*seq_len] (or [batch*seq_len] without
+ * micro-batches), values in [0, vocab), copied before the call returns.
+ * The loss is the mean next-token loss over all micro-batches.  Synchronous:
+ * on return 0 the store holds the post-Adam W, m, v, this step's G, and t+1
+ * in the header.  Errors: MT_E_NOT_BOUND, MT_E_INVALID (token out of range),
+ * MT_E_NONFINITE (no Adam ran: W, m, v untouched), MT_E_HIP. */
+int mt_train_step(mt_model* model, const int32_t* tokens);
+/* Loss of the last completed step (MT_E_STATE before the first). */
+int mt_get_loss(const mt_model* model, float* out);
+/* Timings of the last step: per-block compute against transfer time and the
+ * compute stream's idle time, the quantities the pages' overlap claim is
+ * about ([Methodik]: the ping-pong keeps the GPU busy). */
+int mt_get_stats(const mt_model* model, mt_stats* out);
+int mt_get_block_stats(const mt_model* model, int block, mt_block_stats* out);
 /* Device addresses inside the arena for inspection by tests: the fp32
  * layer-boundary checkpoint x^l [batch*seq_len x d_model] (l = 0..n_layers)
  * and the fp32 per-position loss [batch*seq_len] (0 on the last position of
- * each sequence).  Valid until the next step. */
-int mt_debug_buffers(const void* model, int layer, void** ckpt, void** row_loss);
-void mt_destroy_model(void* model);
+ * each sequence).  Either output may be null.  Valid until the next step. */
+int mt_debug_buffers(const mt_model* model, int layer, void** ckpt, void** row_loss);
+/* With MT_FLAG_KEEP_DX: device address of dl/dx^l, the gradient arriving at
+ * layer boundary l (l = n_layers: from the head; l = 0: the input of the
+ * embedding backward), fp32 [batch*seq_len x d_model], of the last
+ * micro-batch of the last step.  MT_E_STATE without the flag, MT_E_INVALID
+ * for l outside 0..n_layers. */
+int mt_debug_grad(const mt_model* model, int layer, void** dx);
+void mt_destroy_model(mt_model* model);
 
 /* ------------------------------------------------------------ host Adam -- */
-/* One Adam step over n elements on the host (the routine mt_train_step
- * uses per block): w, g of store dtype (bf16 as uint16 bits, or f32), m, v
- * float32; updated in place; step number t >= 1; threads as in mt_config. */
+/* One Adam step over n elements on the host ([Methodik]: the optimizer step
+ * runs on the CPU with AVX-512; the routine mt_train_step uses per block):
+ * w, g of store dtype (bf16 as uint16 bits, or f32), m, v float32; updated
+ * in place; step number t >= 1; threads as in mt_config.  bf16 results are
+ * rounded to nearest even (subnormals kept). */
 int mt_host_adam(int32_t store_dtype, void* w, const void* g, float* m, float* v, size_t n,
                  int64_t t, double lr, double beta1, double beta2, double eps, int32_t threads);
 /* The MT_BF16_MASTER update: the same fp32 arithmetic on the master p
@@ -250,6 +314,22 @@ int mt_host_adam(int32_t store_dtype, void* w, const void* g, float* m, float* v
  * p' rounded to nearest even. */
 int mt_host_adam_master(uint16_t* w, float* p, const uint16_t* g, float* m, float* v, size_t n,
                         int64_t t, double lr, double beta1, double beta2, double eps, int32_t threads);
+
+/* ------------------------------------------------------- measurement -- */
+/* Host-link bandwidth with the copies mt_train_step issues ([Methodik]:
+ * single DMA bursts of layer blocks are meant to fill the host link): `reps`
+ * copies of `bytes` host_a -> dev_a (host to device), dev_b -> host_b (device
+ * to host), and both directions at once.  Copies run as hipMemcpyAsync on
+ * streams[0] (host to device) and streams[1] (device to host), or, with
+ * MT_FLAG_SDMA_QUEUES in `flags`, on the SDMA engine queues (streams unused,
+ * may be null).  host_a, host_b: pinned (mt_alloc_host_store), dev_a, dev_b:
+ * device memory, each at least `bytes`; all caller-owned.  out_gbs[0..2]
+ * receive host->device, device->host and the two together in GB/s (1e9
+ * bytes; wall clock of the copies after one warm-up copy).  Synchronous.
+ * Errors: MT_E_INVALID (null or unpinned buffer, zero size, reps < 1,
+ * missing or equal streams), MT_E_HIP. */
+int mt_link_probe(void* dev_a, void* dev_b, void* host_a, void* host_b, size_t bytes, int32_t reps, int32_t flags,
+                  void* const streams[2], double out_gbs[3]);
 
 const char* mt_last_error(void);
 const char* mt_version(void);

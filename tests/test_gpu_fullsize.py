@@ -1,28 +1,40 @@
 """The training step at the full configuration sizes, through the C ABI,
-against the oracle on outputs it can compute one by one and on properties
-that hold at any size.
+against the oracle.
 
-* 1.3B shape (24 layers, d 2048, 16 heads, batch 4 x 2048): the loss of the
-  oracle's whole forward (float32); the head's and the top two layers'
-  gradients and post-Adam weights from the oracle's backward driven by the
-  GPU's checkpoints; to the bars of tests/harness.py.
-* 7B and 14B shapes with every layer, and the 120B shape with 2 layers (its
-  96 layers need 1.47 TB of host memory):
-  - one layer's forward, recomputed by the oracle from the GPU's own fp32
-    checkpoint x^l on a prefix of one sequence (attention is causal, so the
-    prefix is exact), at the first and the last layer; compared on the
-    layer's increment x^{l+1} - x^l with the gradient bars;
-  - per-position losses from the GPU's x^L, at sampled positions;
-  - the loss is the mean of the per-position losses;
-  - the host Adam relation, bit for bit, on a slice of every tensor;
-  - embedding-gradient rows of tokens that do not occur are exactly zero.
+The oracle cannot run a whole 7B, 14B or 120B step in a test, so it checks
+one block at a time, over every token, from the inputs the GPU gave that
+block.  The step runs with MT_FLAG_KEEP_DX, which keeps the gradient
+arriving at every layer boundary.  Then:
+  * head: loss, final-norm gain, head weight gradients and post-Adam
+    weights, from the GPU's fp32 x^L; dl/dx^L against the GPU's;
+  * top layer L-1: from the GPU's checkpoint x^{L-1} and the oracle's own
+    dl/dx^L (so head and top layer chain on the oracle side): every logical
+    tensor's gradient and post-Adam weight, the layer's forward output
+    x^L, and dl/dx^{L-1};
+  * layer 0 and the embedding: from x^0 and the GPU's dl/dx^1: every layer
+    tensor, dl/dx^0, and the embedding gradient and post-Adam weights from
+    the oracle's dl/dx^0.
+All of these to the bars of tests/harness.py.  Also: per-position losses at
+sampled positions, the loss is the mean of the per-position losses, the
+host Adam relation bit for bit on a slice of every tensor, and zero
+embedding-gradient rows for tokens with no labelled occurrence.
+
+* 1.3B (4 x 2048 tokens): the oracle's whole step end to end, every tensor
+  of every layer, against the bars; tensors whose end-to-end comparison
+  misses a bar are listed with their measured numbers (KNOWN_DRIFT) and
+  asserted in an expected-failure test of their own; the per-block check
+  above at layers 0, 11 and 23.
+* 7B and 14B at their batch x sequence: the per-block checks.
+* 120B at the depth that fits in host memory (L stated in the output),
+  batch 4 x 4096: the per-block checks; enabled by MT_PARITY_120B=1 (several
+  minutes of oracle time).
 * The streamed, serialized, resident and single-slot schedules agree bit for
   bit at the 14B and 120B per-layer shapes with 2 layers.
 * Long context: the 7B width with 2 layers over one 131072-token sequence,
-  whose output head runs in passes of 22272 tokens: the same checks, with
-  head positions on both sides of every pass boundary.
+  whose output head runs in passes: sampled-row checks.
 """
 import gc
+import os
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -31,8 +43,8 @@ import pytest
 import datagen
 import host_memory_layer_amd as mt
 from oracle import Oracle, adam_update
-from tests.harness import (GRAD_COS, GRAD_MAXREL, LOSS_RTOL, as_f32, assert_parity, cosine, frob_rel, make_store,
-                           maxnorm_rel, parity_report)
+from tests.harness import (GRAD_COS, GRAD_MAXREL, LOSS_RTOL, W_RTOL, as_f32, cosine, frob_rel, make_store,
+                           maxnorm_rel)
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -40,7 +52,9 @@ torch = pytest.importorskip("torch")
 P13 = datagen.PRESETS["1.3b"]
 P7 = datagen.PRESETS["7b"]
 P14 = datagen.PRESETS["14b"]
-P120_L2 = datagen.PRESETS["120b"].replace(n_layers=2)
+P120 = datagen.PRESETS["120b"]
+P120_L2 = P120.replace(n_layers=2)
+LAYER_KEYS = datagen.LAYER_TENSORS + ("attn_norm", "ffn_norm")
 
 
 def need_gpu():
@@ -74,12 +88,18 @@ class Run:
 
     def close(self):
         self.drop_model()
-        self.store.free()
+        if self.store is not None:
+            self.store.free()
+            self.store = None
         gc.collect()
 
 
 def pool():
     return ThreadPoolExecutor(datagen.default_threads())
+
+
+def key(name, layer):
+    return name if layer is None else f"{layer}.{name}"
 
 
 def layer_params(shape, l, ex):
@@ -89,64 +109,127 @@ def layer_params(shape, l, ex):
     return P
 
 
-# ------------------------------------------------------------ 1.3B parity --
-def test_1p3b_loss_head_and_top_layers_match_oracle():
-    """Loss: the oracle's whole forward from the seeded inputs.  Gradients
-    and post-Adam weights of the head and the top two layers: the oracle's
-    head and backward sweep driven by the GPU's own fp32 checkpoints x^l
-    (each layer recomputed from x^l, as the streamed schedule does), so that
-    every compared tensor measures the arithmetic of one block, not the drift
-    that 24 layers of bf16 operands leave in the checkpoints."""
-    need_gpu()
-    shape = P13
+def adam_t1(shape, w0, g):
+    z = np.zeros_like(w0)
+    return adam_update(w0, g, z, z, 1, shape.lr, shape.beta1, shape.beta2, shape.adam_eps)[0]
+
+
+class Report:
+    """Rows (what, cos, max-norm rel, W Frobenius rel) against the bars."""
+
+    def __init__(self, title):
+        self.title = title
+        self.rows = []
+
+    def grad(self, what, g, ref, w=None, w_ref=None):
+        row = (what, cosine(g, ref), maxnorm_rel(g, ref), None if w is None else frob_rel(w, w_ref))
+        self.rows.append(row)
+        extra = "" if row[3] is None else f" w_rel {row[3]:.2e}"
+        print(f"  {self.title} {what:18s} cos {row[1]:.6f} maxrel {row[2]:.2e}{extra}", flush=True)
+
+    def misses(self):
+        return [r for r in self.rows
+                if not (r[1] >= GRAD_COS and r[2] <= GRAD_MAXREL and (r[3] is None or r[3] <= W_RTOL))]
+
+
+# ------------------------------------------------------- GPU capture --
+def capture(shape, top, bottom, sampled_positions=None, rows_ex=None):
+    """Run the GPU step with MT_FLAG_KEEP_DX; copy out what the per-block
+    checks need; run the checks that need the live store; free everything.
+    top: compare the head and layer L-1; bottom: layer 0 and the embedding."""
     L = shape.n_layers
-    top = (L - 1, L - 2)
-    print(f"1.3B parity: {L} layers, {shape.batch}x{shape.seq_len} tokens", flush=True)
-    r = Run(shape)
+    r = Run(shape, flags=mt.MT_FLAG_KEEP_DX)
+    cap = {"loss": r.loss, "tok": r.tok, "g": {}, "w": {}, "x": {}, "dx": {}}
     try:
-        keys = [("wh", None), ("final_norm", None)] + [
-            (n, l) for l in top for n in datagen.LAYER_TENSORS + ("attn_norm", "ffn_norm")]
-        name = lambda n, l: n if l is None else f"{l}.{n}"
-        g = {name(n, l): as_f32(r.store.logical(n, l, "g")).copy() for n, l in keys}
-        w = {name(n, l): as_f32(r.store.logical(n, l, "w")).copy() for n, l in keys}
-        xs = {l: r.model.checkpoint(l).cpu().numpy() for l in top + (L,)}
-        loss = r.loss
+        names = []
+        if top:
+            names += [("wh", None), ("final_norm", None)] + [(n, L - 1) for n in LAYER_KEYS]
+            for l in (L - 1, L):
+                cap["x"][l] = r.model.checkpoint(l).cpu().numpy()
+            for l in (L - 1, L):
+                cap["dx"][l] = r.model.grad(l).cpu().numpy()
+        if bottom:
+            names += [("E", None)] + [(n, 0) for n in LAYER_KEYS]
+            for l in (0, 1):
+                cap["x"][l] = r.model.checkpoint(l).cpu().numpy()
+                cap["dx"][l] = r.model.grad(l).cpu().numpy()
+        for n, l in names:
+            cap["g"][key(n, l)] = as_f32(r.store.logical(n, l, "g")).copy()
+            cap["w"][key(n, l)] = as_f32(r.store.logical(n, l, "w")).copy()
+        with pool() as ex:
+            if sampled_positions is not None:
+                check_head_rows(r, sampled_positions, ex)
+            check_adam_relation(r, ex)
+        check_embedding_rows(r)
     finally:
         r.close()
-    P = datagen.init_params(shape, threads=datagen.default_threads())
+    return cap
+
+
+# ------------------------------------------------------ oracle checks --
+def oracle_head(shape, cap, rep, ex):
+    """Loss, head gradients and post-Adam weights from the GPU's x^L; returns
+    the oracle's dl/dx^L."""
+    L, tok = shape.n_layers, cap["tok"]
+    P = {"final_norm": datagen.init_tensor(shape, "final_norm"), "wh": datagen.init_tensor(shape, "wh", pool=ex)}
+    loss, dx, g, logits = Oracle(shape, np.float32).head(cap["x"][L], P, tok.reshape(shape.batch, shape.seq_len))
+    del logits
+    lrel = abs(cap["loss"] - float(loss)) / abs(float(loss))
+    print(f"  loss {cap['loss']:.6f} vs oracle head on the GPU's x^L {float(loss):.6f} rel {lrel:.2e}", flush=True)
+    assert lrel <= LOSS_RTOL
+    for k in ("wh", "final_norm"):
+        rep.grad(k, cap["g"][k], g[k], cap["w"][k], adam_t1(shape, P[k], g[k]))
+    rep.grad(f"dx^{L}", cap["dx"][L], dx)
+    return dx
+
+
+def oracle_layer(shape, cap, l, dx_next, rep, ex, out_key=None):
+    """Layer l's forward from the GPU's x^l and its backward from dx_next:
+    forward output, every gradient, post-Adam weights and dl/dx^l."""
+    P = layer_params(shape, l, ex)
     o = Oracle(shape, np.float32)
-    o_loss = float(o.loss_only(P, r.tok))
-    _, dx, o_g, _ = o.head(xs[L], P, r.tok.reshape(shape.batch, shape.seq_len))
-    for l in top:
-        _, cache = o.layer_fwd(xs[l], P, l)
-        dx = o.layer_bwd(dx, cache, P, l, o_g)
-        del cache
-    o_w = {}
-    for k in g:
-        z = np.zeros_like(P[k])
-        o_w[k] = adam_update(P[k], o_g[k], z, z, 1, shape.lr, shape.beta1, shape.beta2, shape.adam_eps)[0]
-    o_g = {k: o_g[k] for k in g}
-    for k, c, e, we in parity_report(loss, g, w, o_loss, o_g, o_w)[1]:
-        print(f"  {k:16s} cos {c:.6f} maxrel {e:.2e} frob {frob_rel(g[k], o_g[k]):.2e} w_rel {we:.2e}", flush=True)
-    lrel, rows = assert_parity(loss, g, w, o_loss, o_g, o_w)
-    print(f"loss {loss:.6f} vs {o_loss:.6f} rel {lrel:.2e}; min cos {min(x[1] for x in rows):.6f}; "
-          f"max grad rel {max(x[2] for x in rows):.2e}; max w rel {max(x[3] for x in rows):.2e}")
+    x_next, cache = o.layer_fwd(cap["x"][l], P, l)
+    if out_key is not None:
+        inc, ref = cap["x"][l + 1] - cap["x"][l], x_next - cap["x"][l]
+        rep.grad(f"x^{l + 1} - x^{l}", inc, ref)
+    del x_next
+    g = {}
+    dx = o.layer_bwd(dx_next, cache, P, l, g)
+    del cache
+    for n in LAYER_KEYS:
+        k = key(n, l)
+        rep.grad(k, cap["g"][k], g[k], cap["w"][k], adam_t1(shape, P[k], g[k]))
+    if l in cap["dx"]:
+        rep.grad(f"dx^{l}", cap["dx"][l], dx)
+    return dx
 
 
-# ------------------------------------------------------- sampled outputs --
-def check_layer_prefix(r, l, b, n, ex):
-    """Oracle layer l on the first n positions of sequence b, from the GPU's x^l."""
-    T = r.shape.seq_len
-    rows = np.arange(b * T, b * T + n)
-    x_in = r.rows(l, rows)
-    x_out = r.rows(l + 1, rows)
-    ref, _ = Oracle(r.shape.replace(batch=1, seq_len=n), np.float32).layer_fwd(x_in, layer_params(r.shape, l, ex), l)
-    d_gpu, d_ref = x_out - x_in, ref - x_in
-    c, e = cosine(d_gpu, d_ref), maxnorm_rel(d_gpu, d_ref)
-    print(f"  layer {l} sequence {b} prefix {n}: increment cos {c:.6f} maxrel {e:.2e}", flush=True)
-    assert c >= GRAD_COS and e <= GRAD_MAXREL, (l, b, n, c, e)
+def oracle_embedding(shape, cap, dx0, rep, ex):
+    tok = cap["tok"].reshape(-1)
+    dE = np.zeros((shape.vocab, shape.d_model), np.float32)
+    np.add.at(dE, tok, dx0)
+    E0 = datagen.init_tensor(shape, "E", pool=ex)
+    rep.grad("E", cap["g"]["E"], dE, cap["w"]["E"], adam_t1(shape, E0, dE))
 
 
+def per_block_checks(shape, cap, top=True, bottom=True):
+    L = shape.n_layers
+    rep = Report(shape.name)
+    with pool() as ex:
+        if top:
+            dxL = oracle_head(shape, cap, rep, ex)
+            oracle_layer(shape, cap, L - 1, dxL, rep, ex, out_key=True)
+            del dxL
+        if bottom:
+            dx0 = oracle_layer(shape, cap, 0, cap["dx"][1], rep, ex, out_key=True)
+            oracle_embedding(shape, cap, dx0, rep, ex)
+    bad = rep.misses()
+    assert not bad, "out of tolerance (what, cos, maxrel, w_rel): " + repr(bad)
+    print(f"{shape.name}: {len(rep.rows)} comparisons at the bars; min cos {min(r[1] for r in rep.rows):.6f}, "
+          f"max maxrel {max(r[2] for r in rep.rows):.2e}", flush=True)
+
+
+# ------------------------------------------------------- sampled checks --
 def check_head_rows(r, positions, ex):
     s = r.shape
     T, L = s.seq_len, s.n_layers
@@ -215,25 +298,135 @@ def check_embedding_rows(r):
     print(f"  embedding: {int((~live).sum())} tokens with zero rows, {int(live.sum())} with gradients", flush=True)
 
 
-@pytest.mark.parametrize("shape", [P7, P14, P120_L2], ids=["7b", "14b", "120b-2layers"])
-def test_fullsize_sampled_outputs_and_properties(shape):
+def positions_of(shape):
+    T = shape.seq_len
+    return [0, 1, T - 2, T - 1, T, 2 * T - 1, 3 * T // 2 + 5, shape.batch * T - 2, shape.batch * T - 1]
+
+
+# -------------------------------------------------- 1.3B end to end --
+# Tensors whose end-to-end comparison at the 1.3B shape misses a bar, with
+# the measured numbers (cos, max-norm rel, W rel).  Each layer's own
+# arithmetic meets the bars (the per-block test below); what misses is the
+# drift that many layers of bf16-operand forward leave in the checkpoints.
+KNOWN_DRIFT = {}
+
+
+@pytest.fixture(scope="module")
+def e2e_1p3b():
     need_gpu()
-    L, T = shape.n_layers, shape.seq_len
-    print(f"{shape.name}: {L} layers, d {shape.d_model}, {shape.batch}x{T} tokens", flush=True)
-    r = Run(shape)
+    shape = P13
+    L = shape.n_layers
+    print(f"1.3B end to end: {L} layers, {shape.batch}x{shape.seq_len} tokens", flush=True)
+    r = Run(shape, flags=mt.MT_FLAG_KEEP_DX)
     try:
-        with pool() as ex:
-            check_layer_prefix(r, 0, 1, T, ex)
-            check_layer_prefix(r, L - 1, shape.batch - 1, 512, ex)
-            positions = [0, 1, T - 2, T - 1, T, 2 * T - 1, 3 * T // 2 + 5, shape.batch * T - 2, shape.batch * T - 1]
-            check_head_rows(r, positions, ex)
-            check_adam_relation(r, ex)
-        check_embedding_rows(r)
+        g = {key(n, l): as_f32(r.store.logical(n, l, "g")).copy() for n, l in r.store.logical_names()}
+        w = {key(n, l): as_f32(r.store.logical(n, l, "w")).copy() for n, l in r.store.logical_names()}
+        blocks = (0, L // 2 - 1, L - 1)
+        x = {l: r.model.checkpoint(l).cpu().numpy() for l in sorted({b for b in blocks} | {b + 1 for b in blocks})}
+        dx = {l: r.model.grad(l).cpu().numpy() for l in sorted({b for b in blocks} | {b + 1 for b in blocks})}
+        loss, tok = r.loss, r.tok
     finally:
         r.close()
+    P = datagen.init_params(shape, threads=datagen.default_threads())
+    o_loss, o_g = Oracle(shape, np.float32).forward_backward(P, tok, mode="resident")
+    o_w = {k: adam_t1(shape, P[k], o_g[k]) for k in o_g}
+    rows = {k: (cosine(g[k], o_g[k]), maxnorm_rel(g[k], o_g[k]), frob_rel(w[k], o_w[k])) for k in o_g}
+    del o_g, o_w
+    return dict(shape=shape, loss=loss, o_loss=float(o_loss), rows=rows, x=x, dx=dx, tok=tok, g=g, w=w, P=P,
+                blocks=blocks)
 
 
+def _meets(row):
+    return row[0] >= GRAD_COS and row[1] <= GRAD_MAXREL and row[2] <= W_RTOL
+
+
+def test_1p3b_end_to_end_matches_oracle(e2e_1p3b):
+    """The whole 1.3B step against the oracle's whole step: the loss, and
+    every tensor's gradient and post-Adam weight except those listed in
+    KNOWN_DRIFT, at the bars."""
+    e = e2e_1p3b
+    lrel = abs(e["loss"] - e["o_loss"]) / abs(e["o_loss"])
+    print(f"loss {e['loss']:.6f} vs {e['o_loss']:.6f} rel {lrel:.2e}", flush=True)
+    for k, (c, m, wr) in e["rows"].items():
+        flag = "" if _meets((c, m, wr)) else "  <- misses a bar"
+        print(f"  {k:16s} cos {c:.6f} maxrel {m:.2e} w_rel {wr:.2e}{flag}", flush=True)
+    assert lrel <= LOSS_RTOL
+    bad = {k: r for k, r in e["rows"].items() if k not in KNOWN_DRIFT and not _meets(r)}
+    assert not bad, f"{len(bad)} tensors out of tolerance: {bad}"
+
+
+@pytest.mark.xfail(reason="end-to-end bf16 drift over 24 layers; measured numbers in KNOWN_DRIFT", strict=False)
+def test_1p3b_end_to_end_known_drift(e2e_1p3b):
+    """The tensors of KNOWN_DRIFT at the bars (expected to miss)."""
+    if not KNOWN_DRIFT:
+        pytest.skip("no tensor is known to miss")
+    bad = {k: e2e_1p3b["rows"][k] for k in KNOWN_DRIFT if not _meets(e2e_1p3b["rows"][k])}
+    assert not bad, f"misses: {bad}"
+
+
+def test_1p3b_per_block(e2e_1p3b):
+    """Layers 0, L/2-1 and L-1 each from the GPU's own x^l and dl/dx^{l+1}:
+    every gradient, post-Adam weight, forward output and dl/dx^l at the bars;
+    the embedding from the oracle's dl/dx^0."""
+    e = e2e_1p3b
+    shape = e["shape"]
+    rep = Report(shape.name)
+    cap = dict(x=e["x"], dx=e["dx"], g=e["g"], w=e["w"], tok=e["tok"])
+    with pool() as ex:
+        for l in e["blocks"]:
+            dx = oracle_layer(shape, cap, l, e["dx"][l + 1], rep, ex, out_key=True)
+            if l == 0:
+                oracle_embedding(shape, cap, dx, rep, ex)
+    bad = rep.misses()
+    assert not bad, "out of tolerance (what, cos, maxrel, w_rel): " + repr(bad)
+
+
+# ------------------------------------------------ 7B, 14B, 120B-L --
+@pytest.mark.parametrize("shape", [P7, P14], ids=["7b", "14b"])
+def test_fullsize_per_block(shape):
+    need_gpu()
+    print(f"{shape.name}: {shape.n_layers} layers, d {shape.d_model}, {shape.batch}x{shape.seq_len} tokens",
+          flush=True)
+    cap = capture(shape, top=True, bottom=True, sampled_positions=positions_of(shape))
+    per_block_checks(shape, cap)
+
+
+def layers_that_fit(shape, reserve_gb=24.0):
+    """The most layers of `shape` whose host store fits in the memory this
+    process may use, keeping `reserve_gb` for everything else."""
+    avail = None
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemAvailable:"):
+                    avail = int(line.split()[1]) * 1024
+    except OSError:
+        pass
+    if avail is None:
+        return 2
+    one = shape.replace(n_layers=1)
+    c1 = mt.make_config(one)
+    c2 = mt.make_config(shape.replace(n_layers=2))
+    per_layer = (mt.host_store_bytes(c2) + mt.host_opt_bytes(c2)) - (mt.host_store_bytes(c1) + mt.host_opt_bytes(c1))
+    fixed = mt.host_store_bytes(c1) + mt.host_opt_bytes(c1) - per_layer
+    return int(max(2, min(shape.n_layers, (avail - reserve_gb * 1e9 - fixed) // per_layer)))
+
+
+@pytest.mark.skipif(os.environ.get("MT_PARITY_120B") != "1",
+                    reason="several minutes of oracle time: set MT_PARITY_120B=1")
+def test_fullsize_per_block_120b_depth_that_fits():
+    need_gpu()
+    L = layers_that_fit(P120)
+    shape = P120.replace(n_layers=L)
+    print(f"120b: the first {L} of 96 layers (host memory), d {shape.d_model}, {shape.batch}x{shape.seq_len} tokens",
+          flush=True)
+    cap = capture(shape, top=True, bottom=True, sampled_positions=positions_of(shape))
+    per_block_checks(shape, cap)
+
+
+# ------------------------------------------------------- long context --
 def test_long_context_7b_width_two_layers():
+    need_gpu()
     shape = P7.replace(n_layers=2, batch=1, seq_len=131072)
     T = shape.seq_len
     print(f"{shape.name} long context: 2 layers, d {shape.d_model}, 1x{T} tokens", flush=True)
@@ -252,16 +445,31 @@ def test_long_context_7b_width_two_layers():
         r.close()
 
 
+def check_layer_prefix(r, l, b, n, ex):
+    """Oracle layer l on the first n positions of sequence b, from the GPU's x^l."""
+    T = r.shape.seq_len
+    rows = np.arange(b * T, b * T + n)
+    x_in = r.rows(l, rows)
+    x_out = r.rows(l + 1, rows)
+    ref, _ = Oracle(r.shape.replace(batch=1, seq_len=n), np.float32).layer_fwd(x_in, layer_params(r.shape, l, ex), l)
+    d_gpu, d_ref = x_out - x_in, ref - x_in
+    c, e = cosine(d_gpu, d_ref), maxnorm_rel(d_gpu, d_ref)
+    print(f"  layer {l} sequence {b} prefix {n}: increment cos {c:.6f} maxrel {e:.2e}", flush=True)
+    assert c >= GRAD_COS and e <= GRAD_MAXREL, (l, b, n, c, e)
+
+
+# ---------------------------------------------------------- schedules --
 @pytest.mark.parametrize("shape", [P14.replace(n_layers=2), P120_L2], ids=["14b-2layers", "120b-2layers"])
 def test_fullsize_schedules_bitwise_equal(shape):
     need_gpu()
     print(f"{shape.name} with {shape.n_layers} layers: streamed vs serialized vs resident vs single slot "
-          "vs streamed with layer 0's intermediates retained", flush=True)
+          "vs SDMA queues vs streamed with layer 0's intermediates retained", flush=True)
     ref = Run(shape, "streamed")
     try:
         ref.drop_model()
-        for mode, retain in (("serialized", 0), ("resident", 0), ("single_slot", 0), ("streamed", 1)):
-            r = Run(shape, mode, retain_layers=retain)
+        for mode, flags, retain in (("serialized", 0, 0), ("resident", 0, 0), ("single_slot", 0, 0),
+                                    ("streamed", mt.MT_FLAG_SDMA_QUEUES, 0), ("streamed", 0, 1)):
+            r = Run(shape, mode, flags=flags, retain_layers=retain)
             try:
                 assert r.loss == ref.loss, mode
                 for b in range(len(ref.store.blocks)):

@@ -11,7 +11,8 @@ import pytest
 import datagen
 import host_memory_layer_amd as mt
 from oracle import Oracle, adam_update
-from tests.harness import W_RTOL, assert_parity, frob_rel, make_store, read_all
+from tests.harness import (GRAD_COS, GRAD_MAXREL, W_RTOL, assert_parity, cosine, frob_rel, make_store,
+                           maxnorm_rel, read_all)
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -20,6 +21,10 @@ torch = pytest.importorskip("torch")
 SMALL_BF16 = datagen.ModelShape("small-bf16", 2, 256, 2, 128, 512, 1000, 2, 128)
 # The same decoder with an fp32 master copy of the weights on the host.
 SMALL_MASTER = SMALL_BF16.replace(name="small-bf16m", store_dtype=datagen.BF16_MASTER)
+# Sequences of 256 tokens: a micro-batch of one sequence still has 256
+# tokens, enough for the layer backward's K-major weight-gradient GEMMs
+# (contraction over tokens: a multiple of 64 and at least 192).
+SMALL_T256 = SMALL_BF16.replace(name="small-bf16-T256", seq_len=256)
 
 
 def need_gpu():
@@ -71,15 +76,56 @@ def test_schedules_bitwise_equal(shape):
     ref = run_step(shape, "streamed")
     # retain: layers whose forward intermediates stay on the device, so that
     # their backward skips the recompute
+    sdma = mt.MT_FLAG_SDMA_QUEUES
     for mode, flags, retain in (("serialized", 0, 0), ("resident", 0, 0), ("single_slot", 0, 0),
                                 ("streamed", mt.MT_FLAG_POISON, 0), ("single_slot", mt.MT_FLAG_POISON, 0),
                                 ("streamed", 0, 1), ("streamed", mt.MT_FLAG_POISON, shape.n_layers),
-                                ("single_slot", 0, 1)):
+                                ("single_slot", 0, 1), ("streamed", sdma, 0), ("serialized", sdma, 0),
+                                ("single_slot", sdma | mt.MT_FLAG_POISON, 0), ("streamed", mt.MT_FLAG_DUPLEX_LINK, 0),
+                                ("streamed", mt.MT_FLAG_KEEP_DX, 0), ("resident", mt.MT_FLAG_KEEP_DX, 0)):
         r = run_step(shape, mode, flags, retain_layers=retain)
         assert r["loss"] == ref["loss"], (mode, flags, retain)
         for key in ("g", "w", "m", "v", "p"):
             for k in ref.get(key, {}):
                 assert np.array_equal(r[key][k], ref[key][k]), (mode, flags, retain, key, k)
+
+
+@pytest.mark.parametrize("shape", [datagen.PRESETS["tiny"], SMALL_BF16], ids=["tiny-f32", "small-bf16"])
+def test_kept_layer_gradients_follow_the_oracle_chain(shape):
+    """MT_FLAG_KEEP_DX: the gradient arriving at every layer boundary,
+    dl/dx^l, against the oracle's: its head on the GPU's x^L gives dl/dx^L,
+    and each layer's backward, recomputed from the GPU's x^l, carries the
+    GPU's dl/dx^{l+1} down to dl/dx^l."""
+    need_gpu()
+    cfg, store = make_store(shape, flags=mt.MT_FLAG_KEEP_DX)
+    model = mt.Model(cfg, store, "cuda:0")
+    tok = datagen.tokens(shape)
+    model.step(tok)
+    L = shape.n_layers
+    x = [model.checkpoint(l).cpu().numpy() for l in range(L + 1)]
+    dx = [model.grad(l).cpu().numpy() for l in range(L + 1)]
+    gE = store.logical("E", None, "g").copy()
+    model.close()
+    store.free()
+    P = datagen.init_params(shape)
+    o = Oracle(shape, np.float32)
+    _, ref, _, _ = o.head(x[L], P, tok)
+    pairs = [(L, ref)]
+    for l in range(L - 1, -1, -1):
+        _, cache = o.layer_fwd(x[l], P, l)
+        pairs.append((l, o.layer_bwd(dx[l + 1], cache, P, l, {})))
+    for l, r in pairs:
+        c, m = cosine(dx[l], r), maxnorm_rel(dx[l], r)
+        print(f"  dx^{l}: cos {c:.6f} maxrel {m:.2e}", flush=True)
+        assert c >= GRAD_COS and m <= GRAD_MAXREL, (l, c, m)
+    # the embedding gradient is the fp32 sum of dl/dx^0 over each token's
+    # positions in increasing order, then rounded to the store: bit for bit
+    dE = np.zeros((shape.vocab, shape.d_model), np.float32)
+    np.add.at(dE, tok.reshape(-1), dx[0])
+    if shape.store_dtype == datagen.F32:
+        assert np.array_equal(gE, dE)
+    else:
+        assert np.array_equal(gE, datagen.f32_to_bf16_bits(dE))
 
 
 def test_repeated_step_is_deterministic_and_t_advances():
@@ -133,8 +179,8 @@ def test_fp32_master_store_matches_oracle():
     assert any(not np.array_equal(two["p"][k], two["w"][k]) for k in two["p"])
 
 
-@pytest.mark.parametrize("shape", [datagen.PRESETS["tiny"], SMALL_BF16, SMALL_MASTER],
-                         ids=["tiny-f32", "small-bf16", "small-bf16m"])
+@pytest.mark.parametrize("shape", [datagen.PRESETS["tiny"], SMALL_BF16, SMALL_MASTER, SMALL_T256],
+                         ids=["tiny-f32", "small-bf16", "small-bf16m", "small-bf16-T256-kmajor"])
 def test_micro_batches_accumulate_the_batch_gradient(shape):
     """Two micro-batches of one sequence each against the whole batch of two.
 

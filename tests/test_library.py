@@ -282,9 +282,42 @@ def test_api_errors_without_device():
     h = ctypes.c_void_p()
     assert L.mt_create_model(ctypes.byref(cfg), None, 0, None, ctypes.byref(h)) == mt.MT_E_INVALID
     assert L.mt_create_model(ctypes.byref(cfg), 0x1001, 1 << 30, None, ctypes.byref(h)) == mt.MT_E_INVALID
-    stream = 1  # never dereferenced: every call below fails its checks first
-    assert L.mt_create_model(ctypes.byref(cfg), 0x1001, 1 << 30, stream, ctypes.byref(h)) == mt.MT_E_ALIGN
-    assert L.mt_create_model(ctypes.byref(cfg), 0x1000, 16, stream, ctypes.byref(h)) == mt.MT_E_SIZE
+    # stream handles are never dereferenced: every call below fails its checks first
+    streams = (ctypes.c_void_p * 3)(1, 2, 3)
+    one_missing = (ctypes.c_void_p * 3)(1, None, 3)
+    repeated = (ctypes.c_void_p * 3)(1, 2, 1)
+    assert L.mt_create_model(ctypes.byref(cfg), 0x1000, 1 << 30, one_missing, ctypes.byref(h)) == mt.MT_E_INVALID
+    assert L.mt_create_model(ctypes.byref(cfg), 0x1000, 1 << 30, repeated, ctypes.byref(h)) == mt.MT_E_INVALID
+    assert b"three different streams" in L.mt_last_error()
+    assert L.mt_create_model(ctypes.byref(cfg), 0x1001, 1 << 30, streams, ctypes.byref(h)) == mt.MT_E_ALIGN
+    assert L.mt_create_model(ctypes.byref(cfg), 0x1000, 16, streams, ctypes.byref(h)) == mt.MT_E_SIZE
+    assert L.mt_debug_grad(None, 0, ctypes.byref(h)) == mt.MT_E_INVALID
+    out = (ctypes.c_double * 3)()
+    assert L.mt_link_probe(None, None, None, None, 1 << 20, 2, 0, None, out) == mt.MT_E_INVALID
+    assert L.mt_link_probe(0x1000, 0x2000, 0x3000, 0x4000, 0, 2, 0, None, out) == mt.MT_E_INVALID
+    assert L.mt_link_probe(0x1000, 0x2000, 0x3000, 0x4000, 1 << 20, 2, 0, None, out) == mt.MT_E_INVALID
+
+
+def test_host_store_layout_matches_block_info():
+    """mt_host_store_layout reports both part sizes and every block's
+    descriptor, the same as mt_host_store_bytes / mt_host_opt_bytes /
+    mt_block_info; a short capacity fills only that many blocks."""
+    for name in ("tiny", "1.3b", "14b"):
+        cfg = mt.make_config(datagen.PRESETS[name])
+        lay, blocks = mt.store_layout(cfg)
+        assert lay.dma_bytes == mt.host_store_bytes(cfg) and lay.opt_bytes == mt.host_opt_bytes(cfg)
+        assert lay.n_blocks == cfg.n_layers + 2 == len(blocks)
+        for i, b in enumerate(blocks):
+            ref = mt.MtBlockDesc()
+            mt.check(mt.lib().mt_block_info(ctypes.byref(cfg), i, ctypes.byref(ref)))
+            assert bytes(b) == bytes(ref), (name, i)
+        few = (mt.MtBlockDesc * 2)()
+        mt.check(mt.lib().mt_host_store_layout(ctypes.byref(cfg), ctypes.byref(lay), few, 1))
+        assert bytes(few[0]) == bytes(blocks[0]) and not any(bytes(few[1]))
+    bad = mt.make_config(datagen.PRESETS["tiny"])
+    bad.n_heads = 3
+    assert mt.lib().mt_host_store_layout(ctypes.byref(bad), ctypes.byref(mt.MtLayout()), None, 0) == mt.MT_E_INVALID
+    assert mt.lib().mt_host_store_layout(ctypes.byref(cfg), None, None, 0) == mt.MT_E_INVALID
 
 
 def _aligned(nbytes):
