@@ -25,7 +25,7 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I" + INCL
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-result", "-Wno-unused-value"]
 GXX_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-I" + INCLUDE, "-I" + CSRC]
 
-HIP_SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "engine.hip"]
+HIP_SOURCES = ["gemm.hip", "attention.hip", "elementwise.hip", "engine.hip", "noalloc.hip"]
 # The attention kernels feed MFMA results to vector ALU work (softmax) every
 # tile: MFMAs that write the general register file avoid copies through the
 # accumulation registers.

@@ -53,6 +53,22 @@ int mt_gemm_ws(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, 
  * current device; 0 when it would not split. */
 size_t mt_gemm_ws_bytes(int32_t M, int32_t N, int32_t K);
 
+/* mt_gemm_ws for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * stream-K partial tiles go to a static device buffer of the library,
+ * mt_gemm_noalloc_max_ws() = 128 MiB on each GPU it runs on, held until the
+ * process ends; the call allocates nothing and its results are bit for bit
+ * those of mt_gemm_ws with a large enough workspace.  The buffer is written
+ * before it is read within each call, so no clearing is needed.  Shapes whose
+ * split needs more than the buffer return MT_E_SIZE (on 256 compute units
+ * every split needs exactly 128 MiB).  All calls on one GPU share that GPU's
+ * buffer: calls that overlap in time on one GPU (on different streams or from
+ * different threads) race on it and must be ordered by the caller, e.g. on
+ * one stream. */
+int mt_gemm_noalloc(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, const float* R,
+                    int64_t ldr, int32_t M, int32_t N, int32_t K, int32_t epi, int32_t layout, void* stream);
+size_t mt_gemm_noalloc_max_ws(void);
+
 /* out[C x R] = in[R x C]^T (row strides ld_in, ld_out). */
 int mt_transpose(int32_t dtype, const void* in, int64_t ld_in, void* out, int64_t ld_out, int32_t R, int32_t C,
                  void* stream);
