@@ -144,4 +144,97 @@ int mt_attention_bwd(int32_t dtype, const void* qkv, const void* o, const void* 
   });
 }
 
+#define MT_DT_DISPATCH(dtype, F_)       \
+  if (dtype == MT_BF16) {               \
+    F_(uint16_t)                        \
+  } else if (dtype == MT_F32) {         \
+    F_(float)                           \
+  } else {                              \
+    need(false, "dtype");               \
+  }
+
+int mt_rmsnorm_fwd(int32_t dtype, const float* x, const void* g, void* y, float* rstd, int32_t M, int32_t d, float eps,
+                   void* stream) {
+  return kguard([&] {
+    need(M >= 0 && d > 0 && eps > 0, "shape");
+#define F_(T) rmsnorm_fwd<T>(x, (const T*)g, (T*)y, rstd, M, d, eps, (hipStream_t)stream);
+    MT_DT_DISPATCH(dtype, F_)
+#undef F_
+  });
+}
+
+size_t mt_rmsnorm_bwd_ws_bytes(int32_t M, int32_t d) {
+  if (M < 0 || d <= 0) return 0;
+  return rmsnorm_dg_partial_elems(M, d) * sizeof(float);
+}
+
+int mt_rmsnorm_bwd(int32_t dtype, const float* dy, const float* x, const void* g, const float* rstd,
+                   const float* resid, float* dx, void* dx_lp, void* dg, float* ws, int32_t M, int32_t d,
+                   void* stream) {
+  return kguard([&] {
+    need(M >= 0 && d > 0 && ws, "shape / workspace");
+#define F_(T) rmsnorm_bwd<T>(dy, x, (const T*)g, rstd, resid, dx, ws, (T*)dg, M, d, (hipStream_t)stream, (T*)dx_lp);
+    MT_DT_DISPATCH(dtype, F_)
+#undef F_
+  });
+}
+
+int mt_swiglu_fwd(int32_t dtype, const void* gu, void* y, int32_t M, int32_t F, void* stream) {
+  return kguard([&] {
+    need(M >= 0 && F > 0, "shape");
+#define F_(T) swiglu_fwd<T>((const T*)gu, (T*)y, M, F, (hipStream_t)stream);
+    MT_DT_DISPATCH(dtype, F_)
+#undef F_
+  });
+}
+
+int mt_swiglu_bwd(int32_t dtype, const void* dy, const void* gu, void* dgu, int32_t M, int32_t F, void* stream) {
+  return kguard([&] {
+    need(M >= 0 && F > 0, "shape");
+#define F_(T) swiglu_bwd<T>((const T*)dy, (const T*)gu, (T*)dgu, M, F, (hipStream_t)stream);
+    MT_DT_DISPATCH(dtype, F_)
+#undef F_
+  });
+}
+
+int mt_rope_bwd_t(int32_t dtype, void* dqkvT, int64_t ldT, const float* cos_T, const float* sin_T, int32_t B,
+                  int32_t T, int32_t H, int32_t hd, void* stream) {
+  return kguard([&] {
+    need(B > 0 && T > 0 && H > 0 && hd > 0 && hd % 2 == 0 && hd <= 128 && ldT >= (int64_t)B * T, "shape");
+    const int M = B * T, d = H * hd;
+#define F_(T_) rope_bwd_T<T_>((T_*)dqkvT, ldT, cos_T, sin_T, M, T, d, hd, (hipStream_t)stream);
+    MT_DT_DISPATCH(dtype, F_)
+#undef F_
+  });
+}
+
+int mt_xent(int32_t dtype, const float* logits, const int32_t* tok, float* row_loss, void* dlogits, int32_t rows,
+            int64_t row0, int32_t T, int32_t V, float inv_n, void* stream) {
+  return kguard([&] {
+    need(rows >= 0 && row0 >= 0 && T > 1 && V > 1, "shape");
+#define F_(T_) xent<T_>(logits, tok, row_loss, (T_*)dlogits, rows, row0, T, V, inv_n, (hipStream_t)stream);
+    MT_DT_DISPATCH(dtype, F_)
+#undef F_
+  });
+}
+
+int mt_embed_fwd(int32_t dtype, const int32_t* tok, const void* E, float* x, int32_t M, int32_t d, void* stream) {
+  return kguard([&] {
+    need(M >= 0 && d > 0, "shape");
+#define F_(T) embed_fwd<T>(tok, (const T*)E, x, M, d, (hipStream_t)stream);
+    MT_DT_DISPATCH(dtype, F_)
+#undef F_
+  });
+}
+
+int mt_embed_bwd(int32_t dtype, const float* dx, const int32_t* order, const int32_t* seg, void* dE, int32_t V,
+                 int32_t d, void* stream) {
+  return kguard([&] {
+    need(V > 0 && d > 0, "shape");
+#define F_(T) embed_bwd<T>(dx, order, seg, (T*)dE, V, d, (hipStream_t)stream);
+    MT_DT_DISPATCH(dtype, F_)
+#undef F_
+  });
+}
+
 }  // extern "C"

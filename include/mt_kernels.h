@@ -103,6 +103,50 @@ int mt_attention_fwd(int32_t dtype, const void* qkv, void* o, float* lse, int32_
 int mt_attention_bwd(int32_t dtype, const void* qkv, const void* o, const void* dO, const float* lse, float* Dsum,
                      void* dqkvT, int64_t ldT, int32_t B, int32_t T, int32_t H, int32_t hd, void* stream);
 
+/* ---- memory-bound kernels of the layer (the operations of the decoder the
+ * pages train, a Llama-style model: RMSNorm, rotary positions, SwiGLU,
+ * next-token cross-entropy; dtype as above, fp32 statistics) ---- */
+
+/* RMSNorm forward: y[m] = x[m] * rstd[m] * g, rstd[m] = 1/sqrt(mean(x[m]^2) +
+ * eps).  x float [M x d]; g, y dtype [d], [M x d]; rstd float [M].  d % 4 == 0. */
+int mt_rmsnorm_fwd(int32_t dtype, const float* x, const void* g, void* y, float* rstd, int32_t M, int32_t d, float eps,
+                   void* stream);
+/* RMSNorm backward given dy float [M x d] and the forward's rstd:
+ * dx = resid + rstd*(dy*g - xh*mean(dy*g*xh)), xh = x*rstd (resid float [M x
+ * d] or null); dx_lp (dtype [M x d], or null) receives dx rounded; dg (dtype
+ * [d]) = sum over rows of dy*xh, summed in a fixed order that depends only on
+ * (M, d).  ws: float scratch of mt_rmsnorm_bwd_ws_bytes(M, d) bytes. */
+size_t mt_rmsnorm_bwd_ws_bytes(int32_t M, int32_t d);
+int mt_rmsnorm_bwd(int32_t dtype, const float* dy, const float* x, const void* g, const float* rstd,
+                   const float* resid, float* dx, void* dx_lp, void* dg, float* ws, int32_t M, int32_t d,
+                   void* stream);
+/* SwiGLU: gu dtype [M x 2F] (gate columns then up columns); y [M x F] =
+ * silu(gate) * up.  Backward: dgu [M x 2F] = (dy * up * silu'(gate),
+ * dy * silu(gate)), silu'(z) = s(z)(1 + z(1 - s(z))).  F % 4 == 0. */
+int mt_swiglu_fwd(int32_t dtype, const void* gu, void* y, int32_t M, int32_t F, void* stream);
+int mt_swiglu_bwd(int32_t dtype, const void* dy, const void* gu, void* dgu, int32_t M, int32_t F, void* stream);
+/* RoPE backward on dqkvT [3d x ldT] (the attention backward's output): the
+ * dq and dk rows are rotated back by -t*w_i in place (the dv rows are left
+ * as they are); cos_T, sin_T: the tables of mt_rope_tables transposed,
+ * [hd/2 x T]. */
+int mt_rope_bwd_t(int32_t dtype, void* dqkvT, int64_t ldT, const float* cos_T, const float* sin_T, int32_t B,
+                  int32_t T, int32_t H, int32_t hd, void* stream);
+/* Next-token cross-entropy rows m = row0 .. row0+rows-1 of a batch of
+ * sequences of T tokens: logits float [rows x V] (row i is token row0+i);
+ * for t = m mod T < T-1, row_loss[m] = logsumexp(z) - z[tok[m+1]] and
+ * dlogits row = (softmax(z) - onehot(tok[m+1])) * inv_n; the last position of
+ * a sequence gets 0 and a zero row.  tok: device int32 of the whole batch;
+ * row_loss: float indexed by m. */
+int mt_xent(int32_t dtype, const float* logits, const int32_t* tok, float* row_loss, void* dlogits, int32_t rows,
+            int64_t row0, int32_t T, int32_t V, float inv_n, void* stream);
+/* Embedding: x[m] = float(E[tok[m]]) (x float [M x d]).  Backward: dE[v] =
+ * sum of dx[m] over the positions with tok[m] == v, in increasing m, fp32,
+ * then rounded to dtype (rows of absent tokens are 0); order: the positions
+ * stably sorted by token, seg [V+1]: the start of each token's run in it. */
+int mt_embed_fwd(int32_t dtype, const int32_t* tok, const void* E, float* x, int32_t M, int32_t d, void* stream);
+int mt_embed_bwd(int32_t dtype, const float* dx, const int32_t* order, const int32_t* seg, void* dE, int32_t V,
+                 int32_t d, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -305,10 +305,48 @@ def positions_of(shape):
 
 # -------------------------------------------------- 1.3B end to end --
 # Tensors whose end-to-end comparison at the 1.3B shape misses a bar, with
-# the measured numbers (cos, max-norm rel, W rel).  Each layer's own
-# arithmetic meets the bars (the per-block test below); what misses is the
-# drift that many layers of bf16-operand forward leave in the checkpoints.
-KNOWN_DRIFT = {}
+# the measured numbers (cos, max-norm rel, W rel); every miss is on the
+# max-norm bar (3e-2), by at most 27%.  Each layer's own arithmetic meets the
+# bars with a wide margin (the per-block test below).  End to end, the
+# roughly 16 bf16 roundings of each layer's forward and backward (operands
+# of every GEMM, probabilities, stored activations and gradients), none of
+# which dominates (tests/test_rounding_attribution.py), add up over 24
+# layers to about 3% relative error in every tensor (cos ~ 0.9995), which
+# grazes the max-norm bar.
+KNOWN_DRIFT = {
+    "23.ffn_norm": (0.999607, 3.80e-02, 9.99e-04),
+    "22.wq": (0.999514, 3.04e-02, 7.87e-03),
+    "21.ffn_norm": (0.999595, 3.36e-02, 9.99e-04),
+    "15.wq": (0.999509, 3.02e-02, 8.29e-03),
+    "14.ffn_norm": (0.999586, 3.56e-02, 9.99e-04),
+    "13.wq": (0.999501, 3.16e-02, 8.43e-03),
+    "12.ffn_norm": (0.999597, 3.02e-02, 9.99e-04),
+    "11.wg": (0.999565, 3.03e-02, 9.42e-03),
+    "11.ffn_norm": (0.999584, 3.08e-02, 9.99e-04),
+    "9.ffn_norm": (0.999569, 3.24e-02, 1.00e-03),
+    "9.wk": (0.999491, 3.25e-02, 8.76e-03),
+    "8.ffn_norm": (0.999596, 3.56e-02, 1.00e-03),
+    "7.ffn_norm": (0.999568, 3.30e-02, 9.99e-04),
+    "7.wq": (0.999510, 3.05e-02, 8.85e-03),
+    "6.ffn_norm": (0.999545, 3.28e-02, 1.00e-03),
+    "6.wk": (0.999516, 3.00e-02, 8.97e-03),
+    "5.wq": (0.999521, 3.01e-02, 9.04e-03),
+    "4.ffn_norm": (0.999564, 3.02e-02, 1.00e-03),
+    "4.wq": (0.999514, 3.05e-02, 9.17e-03),
+    "3.wg": (0.999551, 3.13e-02, 9.62e-03),
+    "3.wq": (0.999511, 3.18e-02, 9.34e-03),
+    "3.wk": (0.999507, 3.07e-02, 9.33e-03),
+    "1.wd": (0.999572, 3.16e-02, 9.56e-03),
+    "1.wu": (0.999568, 3.03e-02, 9.58e-03),
+    "1.wq": (0.999533, 3.20e-02, 9.51e-03),
+    "1.wk": (0.999535, 3.15e-02, 9.48e-03),
+    "1.wv": (0.999648, 3.18e-02, 9.07e-03),
+    "0.wd": (0.999585, 3.19e-02, 9.52e-03),
+    "0.wu": (0.999586, 3.04e-02, 9.52e-03),
+    "0.ffn_norm": (0.999573, 3.28e-02, 1.00e-03),
+    "0.wk": (0.999540, 3.04e-02, 9.76e-03),
+    "0.attn_norm": (0.999552, 3.59e-02, 1.00e-03),
+}
 
 
 @pytest.fixture(scope="module")
@@ -353,6 +391,11 @@ def test_1p3b_end_to_end_matches_oracle(e2e_1p3b):
     assert lrel <= LOSS_RTOL
     bad = {k: r for k, r in e["rows"].items() if k not in KNOWN_DRIFT and not _meets(r)}
     assert not bad, f"{len(bad)} tensors out of tolerance: {bad}"
+    # the known misses stay misses of the max-norm bar only, at their size
+    for k, (c, m, wr) in KNOWN_DRIFT.items():
+        got = e["rows"][k]
+        assert got[0] >= GRAD_COS and got[2] <= W_RTOL, (k, got)
+        assert got[1] <= 1.05 * m, (k, got, "drift grew beyond the recorded size")
 
 
 @pytest.mark.xfail(reason="end-to-end bf16 drift over 24 layers; measured numbers in KNOWN_DRIFT", strict=False)
