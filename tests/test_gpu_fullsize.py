@@ -122,6 +122,8 @@ class Report:
         self.rows = []
 
     def grad(self, what, g, ref, w=None, w_ref=None):
+        g = as_f32(g)
+        w = None if w is None else as_f32(w)
         row = (what, cosine(g, ref), maxnorm_rel(g, ref), None if w is None else frob_rel(w, w_ref))
         self.rows.append(row)
         extra = "" if row[3] is None else f" w_rel {row[3]:.2e}"
@@ -153,9 +155,9 @@ def capture(shape, top, bottom, sampled_positions=None, rows_ex=None):
             for l in (0, 1):
                 cap["x"][l] = r.model.checkpoint(l).cpu().numpy()
                 cap["dx"][l] = r.model.grad(l).cpu().numpy()
-        for n, l in names:
-            cap["g"][key(n, l)] = as_f32(r.store.logical(n, l, "g")).copy()
-            cap["w"][key(n, l)] = as_f32(r.store.logical(n, l, "w")).copy()
+        for n, l in names:  # store-dtype copies (bf16 bits): half the host memory of float32
+            cap["g"][key(n, l)] = np.array(r.store.logical(n, l, "g"), copy=True)
+            cap["w"][key(n, l)] = np.array(r.store.logical(n, l, "w"), copy=True)
         with pool() as ex:
             if sampled_positions is not None:
                 check_head_rows(r, sampled_positions, ex)
@@ -434,9 +436,13 @@ def test_fullsize_per_block(shape):
     per_block_checks(shape, cap)
 
 
-def layers_that_fit(shape, reserve_gb=24.0):
+HOST_LIMIT = 270 * 2 ** 30   # host memory one process may use on the GPU machines
+
+
+def layers_that_fit(shape, reserve_gb=40.0):
     """The most layers of `shape` whose host store fits in the memory this
-    process may use, keeping `reserve_gb` for everything else."""
+    process may use (the smaller of MemAvailable and HOST_LIMIT), keeping
+    `reserve_gb` for the tensors the checks copy out and the process itself."""
     avail = None
     try:
         with open("/proc/meminfo") as f:
@@ -447,6 +453,7 @@ def layers_that_fit(shape, reserve_gb=24.0):
         pass
     if avail is None:
         return 2
+    avail = min(avail, HOST_LIMIT)
     one = shape.replace(n_layers=1)
     c1 = mt.make_config(one)
     c2 = mt.make_config(shape.replace(n_layers=2))
@@ -460,10 +467,18 @@ def layers_that_fit(shape, reserve_gb=24.0):
 def test_fullsize_per_block_120b_depth_that_fits():
     need_gpu()
     L = layers_that_fit(P120)
-    shape = P120.replace(n_layers=L)
-    print(f"120b: the first {L} of 96 layers (host memory), d {shape.d_model}, {shape.batch}x{shape.seq_len} tokens",
-          flush=True)
-    cap = capture(shape, top=True, bottom=True, sampled_positions=positions_of(shape))
+    while True:
+        shape = P120.replace(n_layers=L)
+        print(f"120b: the first {L} of 96 layers (host memory), d {shape.d_model}, {shape.batch}x{shape.seq_len} "
+              "tokens", flush=True)
+        try:
+            cap = capture(shape, top=True, bottom=True, sampled_positions=positions_of(shape))
+            break
+        except mt.MtError as e:   # pinned host memory short of the estimate: fewer layers
+            if e.code != mt.MT_E_OOM or L <= 2:
+                raise
+            L = max(2, L * 3 // 4)
+            gc.collect()
     per_block_checks(shape, cap)
 
 
