@@ -264,6 +264,10 @@ def main():
                     help="prefetches and offloads on two SDMA engine queues fed by host threads instead of "
                          "hipMemcpyAsync on the prefetch and offload streams")
     ap.add_argument("--no-link-probe", action="store_true")
+    ap.add_argument("--token-chunk", type=int, default=0,
+                    help="tokens per pass of a layer's per-token work (0: automatic, passes only where needed)")
+    ap.add_argument("--ckpt-bf16", action="store_true",
+                    help="keep the layer-boundary checkpoints in bf16 (long contexts)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain 1 GiB device copy kernel first (the reference for HBM byte counters)")
     args = ap.parse_args()
@@ -290,8 +294,10 @@ def main():
         flags |= mt.MT_FLAG_DUPLEX_LINK
     if args.sdma_queues:
         flags |= mt.MT_FLAG_SDMA_QUEUES
+    if args.ckpt_bf16:
+        flags |= mt.MT_FLAG_CKPT_BF16
     K = max(1, args.micro_batches)
-    cfg = mt.make_config(shape, mode=args.mode, flags=flags, micro_batches=K)
+    cfg = mt.make_config(shape, mode=args.mode, flags=flags, micro_batches=K, token_chunk=args.token_chunk)
     R = 0
     if args.retain_layers == "auto":
         # as many sets of one layer's intermediates as fit beside the arena,
@@ -407,7 +413,8 @@ def main():
                                f"{shape.n_heads}x{shape.head_dim} heads, SwiGLU {shape.d_ff}, vocab {shape.vocab}; "
                                f"batch {shape.batch} x seq {shape.seq_len}"
                                f"{f' x {K} micro-batches' if K > 1 else ''}; {args.mode} from the host store"
-                               f"{f', forward intermediates of {R} layers kept on the device' if R else ''} "
+                               f"{f', forward intermediates of {R} layers kept on the device' if R else ''}"
+                               f"{', bf16 layer-boundary checkpoints' if args.ckpt_bf16 else ''} "
                                f"({store.nbytes / 1e9:.1f} GB pinned W/G + {store.opt_nbytes / 1e9:.1f} GB "
                                f"Adam m/v{' + fp32 master W' if args.fp32_master else ''})",
                    "global_batch": K * shape.batch, "seq_len": shape.seq_len, "parallelism": "single GPU"},

@@ -15,7 +15,9 @@ import os
 import numpy as np
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libmt.so")
+# MT_LIBRARY selects another build of the library (the AddressSanitizer
+# variant libmt_asan.so for the host-code tests)
+LIB_PATH = os.environ.get("MT_LIBRARY") or os.path.join(PKG_DIR, "libmt.so")
 
 MT_OK = 0
 MT_E_INVALID, MT_E_SIZE, MT_E_ALIGN, MT_E_NOT_BOUND, MT_E_HIP, MT_E_NONFINITE, MT_E_OOM, MT_E_STATE = range(-1, -9, -1)
@@ -26,6 +28,10 @@ MODES = {"streamed": MT_STREAMED, "serialized": MT_SERIALIZED, "resident": MT_RE
          "single_slot": MT_SINGLE_SLOT}
 MT_BLOCK_EMBED, MT_BLOCK_LAYER, MT_BLOCK_HEAD = 0, 1, 2
 MT_FLAG_TIME_KERNELS, MT_FLAG_POISON, MT_FLAG_DUPLEX_LINK, MT_FLAG_KEEP_DX, MT_FLAG_SDMA_QUEUES = 1, 2, 4, 8, 16
+MT_FLAG_CKPT_BF16, MT_FLAG_DELAYS = 32, 64
+MT_LANE_PREFETCH, MT_LANE_COMPUTE, MT_LANE_OFFLOAD, MT_LANE_HOST = 0, 1, 2, 3
+MT_OP_FETCH, MT_OP_POISON, MT_OP_COMPUTE, MT_OP_OFFLOAD, MT_OP_ADAM, MT_OP_END = range(6)
+MT_SCHED_MAX_WAITS = 8
 EPI_STORE, EPI_F32, EPI_ADD_F32 = 0, 1, 2
 GEMM_A_KMAJOR, GEMM_B_KMAJOR = 1, 2
 
@@ -35,7 +41,7 @@ class MtConfig(ctypes.Structure):
                 ("n_layers", "d_model", "n_heads", "head_dim", "d_ff", "vocab", "batch", "seq_len", "store_dtype")] + \
                [(n, ctypes.c_double) for n in ("rms_eps", "rope_theta", "lr", "beta1", "beta2", "adam_eps")] + \
                [(n, ctypes.c_int32) for n in ("mode", "host_threads", "flags", "micro_batches", "head_chunk_tokens",
-                                              "retain_layers")]
+                                              "retain_layers", "token_chunk")]
 
 
 class MtTensorDesc(ctypes.Structure):
@@ -67,6 +73,12 @@ class MtBlockStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_double) for n in
                 ("fwd_ms", "bwd_ms", "h2d_fwd_ms", "h2d_bwd_ms", "d2h_ms", "stall_fwd_ms", "stall_bwd_ms",
                  "adam_ms")]
+
+
+class MtSchedOp(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("lane", "kind", "use", "block", "wslot", "gslot", "n_waits",
+                                              "n_link")] + \
+               [("waits", ctypes.c_int32 * MT_SCHED_MAX_WAITS), ("link", ctypes.c_int32 * 2)]
 
 
 class MtError(RuntimeError):
@@ -127,6 +139,7 @@ _SIGS = {
     "mt_xent": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]),
     "mt_embed_fwd": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
     "mt_embed_bwd": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
+    "mt_schedule": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
     "mt_last_error": (ctypes.c_char_p, []),
     "mt_version": (ctypes.c_char_p, []),
     "mt_gemm": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
@@ -182,7 +195,7 @@ def check(rc):
 
 
 def make_config(shape, mode="streamed", host_threads=0, flags=0, micro_batches=1, head_chunk_tokens=0,
-                retain_layers=0) -> MtConfig:
+                retain_layers=0, token_chunk=0) -> MtConfig:
     """mt_config from any object with the model-shape attributes
     (n_layers, d_model, n_heads, head_dim, d_ff, vocab, batch, seq_len,
     store_dtype 'f32'|'bf16'|'bf16m' (bf16 with an fp32 master copy), rms_eps, rope_theta, lr, beta1, beta2, adam_eps)."""
@@ -198,6 +211,7 @@ def make_config(shape, mode="streamed", host_threads=0, flags=0, micro_batches=1
     c.micro_batches = int(micro_batches)
     c.head_chunk_tokens = int(head_chunk_tokens)
     c.retain_layers = int(retain_layers)
+    c.token_chunk = int(token_chunk)
     return c
 
 
@@ -229,6 +243,18 @@ def store_layout(cfg: MtConfig):
     blocks = (MtBlockDesc * lay.n_blocks)()
     check(lib().mt_host_store_layout(ctypes.byref(cfg), ctypes.byref(lay), blocks, lay.n_blocks))
     return lay, list(blocks)
+
+
+def schedule(cfg: MtConfig) -> list:
+    """The operations one streamed step of cfg issues (mt_schedule), as dicts
+    with lane, kind, use, block, wslot, gslot, waits and link."""
+    n = lib().mt_schedule(ctypes.byref(cfg), None, 0)
+    if n < 0:
+        check(n)
+    ops = (MtSchedOp * n)()
+    check(min(0, lib().mt_schedule(ctypes.byref(cfg), ops, n)))
+    return [dict(lane=o.lane, kind=o.kind, use=o.use, block=o.block, wslot=o.wslot, gslot=o.gslot,
+                 waits=list(o.waits[:o.n_waits]), link=list(o.link[:o.n_link])) for o in ops]
 
 
 def block_infos(cfg: MtConfig) -> list:
@@ -388,12 +414,15 @@ class Model:
         return self.arena[off:off + nelem * esz].view(dtype)
 
     def checkpoint(self, layer: int):
-        """fp32 layer-boundary activation x^layer [B*T x d] (device tensor view)."""
+        """Layer-boundary activation x^layer [B*T x d] as float32 (a device view
+        of the fp32 checkpoint, or the widened bf16 one with MT_FLAG_CKPT_BF16)."""
         p = ctypes.c_void_p()
         check(lib().mt_debug_buffers(self.handle, layer, ctypes.byref(p), None))
         c = self.cfg
-        return self._arena_view(p.value, c.batch * c.seq_len * c.d_model, self.torch.float32).view(
-            c.batch * c.seq_len, c.d_model)
+        lp = bool(c.flags & MT_FLAG_CKPT_BF16)
+        t = self._arena_view(p.value, c.batch * c.seq_len * c.d_model,
+                             self.torch.bfloat16 if lp else self.torch.float32).view(c.batch * c.seq_len, c.d_model)
+        return t.float() if lp else t
 
     def grad(self, layer: int):
         """fp32 gradient dl/dx^layer arriving at layer boundary `layer` [B*T x d]

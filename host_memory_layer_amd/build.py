@@ -4,6 +4,13 @@ Every .hip and host .cpp file under csrc/ is compiled to an object in
 _build/ (hipcc for HIP sources and for host files that use the HIP runtime
 headers, g++ for the AVX-512 host Adam, which must not be contracted into
 FMAs) and linked into host_memory_layer_amd/libmt.so.
+
+A second variant, libmt_asan.so (objects in _build_asan/), instruments the
+host code of every source with AddressSanitizer (device code is built as
+usual; the Adam file goes through clang++, whose sanitizer runtime the
+other objects use).  Its __asan_* references are resolved at load time by
+the clang runtime preloaded into the process (the host-code tests run it
+that way on the CPU).
 """
 from __future__ import annotations
 
@@ -33,6 +40,20 @@ FILE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 HIPCC_HOST_SOURCES = ["store.cpp", "api.cpp", "kernel_api.cpp", "dma.cpp", "linkprobe.cpp"]
 GXX_SOURCES = ["adam.cpp"]
 
+CLANGXX = "/opt/rocm/llvm/bin/clang++"
+ASAN_OUT_DIR = os.path.join(PKG, "_build_asan")
+ASAN_LIB = os.path.join(PKG, "libmt_asan.so")
+ASAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """Path of clang's shared AddressSanitizer runtime (to preload)."""
+    r = subprocess.run([CLANGXX, "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang's AddressSanitizer runtime was not found")
+    return path
+
 
 def _run(cmd):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -43,30 +64,44 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
-    cmds = []
-    objs = []
+def _commands(asan: bool):
+    out_dir = ASAN_OUT_DIR if asan else OUT_DIR
+    os.makedirs(out_dir, exist_ok=True)
+    extra = ASAN_HOST if asan else []
+    cmds, objs = [], []
     for src in HIP_SOURCES:
-        obj = os.path.join(OUT_DIR, src + ".o")
-        cmds.append([HIPCC] + HIP_FLAGS + FILE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(out_dir, src + ".o")
+        cmds.append([HIPCC] + HIP_FLAGS + extra + FILE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in HIPCC_HOST_SOURCES:
-        obj = os.path.join(OUT_DIR, src + ".o")
-        cmds.append([HIPCC] + HIP_FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(out_dir, src + ".o")
+        cmds.append([HIPCC] + HIP_FLAGS + extra + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in GXX_SOURCES:
-        obj = os.path.join(OUT_DIR, src + ".o")
-        cmds.append(["g++"] + GXX_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(out_dir, src + ".o")
+        cmds.append(([CLANGXX] if asan else ["g++"]) + GXX_FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
-    jobs = jobs or min(8, len(cmds))
+    return cmds, objs
+
+
+def _link(objs, lib):
+    tmp = lib + ".tmp"
+    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs + ["-L/opt/rocm/lib", "-lhsa-runtime64", "-lpthread"])
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, jobs: int | None = None, asan: bool = True) -> str:
+    """Builds libmt.so and, with asan, libmt_asan.so (compiled together)."""
+    cmds, objs = _commands(False)
+    acmds, aobjs = _commands(True) if asan else ([], [])
+    jobs = jobs or 8
     with ThreadPoolExecutor(jobs) as ex:
-        for out in ex.map(_run, cmds):
+        for out in ex.map(_run, cmds + acmds):
             if verbose and out.strip():
                 print(out)
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs + ["-L/opt/rocm/lib", "-lhsa-runtime64", "-lpthread"])
-    os.replace(tmp, LIB)
+    _link(objs, LIB)
+    if asan:
+        _link(aobjs, ASAN_LIB)
     return LIB
 
 

@@ -114,6 +114,19 @@ size_t mt_device_bytes(const mt_config* cfg) {
   return rc == MT_OK ? r : 0;
 }
 
+int mt_schedule(const mt_config* cfg, mt_sched_op* ops, int32_t capacity) {
+  int32_t n = 0;
+  int rc = guarded([&] {
+    if (!cfg) throw ApiError{MT_E_INVALID, "null config"};
+    if (capacity < 0 || (capacity > 0 && !ops)) throw ApiError{MT_E_INVALID, "null ops or negative capacity"};
+    std::vector<mt_sched_op> v = schedule_for(*cfg);
+    for (size_t i = 0; i < v.size() && (int64_t)i < capacity; ++i) ops[i] = v[i];
+    n = (int32_t)v.size();
+    return MT_OK;
+  });
+  return rc == MT_OK ? n : rc;
+}
+
 int mt_alloc_host_store(size_t bytes, void** out) {
   return guarded([&] {
     if (!out || bytes == 0) throw ApiError{MT_E_INVALID, "null out or zero size"};

@@ -162,6 +162,7 @@ void TransferQueue::run() {
     std::string err;
     try {
       if (job.ready) MT_HIP(hipEventSynchronize(job.ready));
+      if (job.delay_us > 0) std::this_thread::sleep_for(std::chrono::microseconds(job.delay_us));
       const bool h2d = dir_ == DMA_H2D;
       if (yield_) {
         if (h2d)

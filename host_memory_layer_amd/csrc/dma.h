@@ -65,8 +65,8 @@ class DmaEngines {
 };
 
 // One direction's copies, run in order by a worker thread.  A job first
-// waits for its `ready` event (null: no wait), then copies, then calls
-// `on_done`.  The enqueueing thread waits for a job with wait(); after a
+// waits for its `ready` event (null: no wait), sleeps delay_us, then copies,
+// then calls `on_done`.  The enqueueing thread waits for a job with wait(); after a
 // failure every wait() throws.
 class TransferQueue {
  public:
@@ -76,6 +76,7 @@ class TransferQueue {
     void* dst;
     const void* src;
     size_t bytes;
+    int delay_us = 0;  // the worker sleeps this long before the copy
   };
   // yield_link: a device-to-host copy starts only when no host-to-device
   // copy is ready or running, so offloads take the link between prefetches

@@ -271,8 +271,15 @@ void rmsnorm_bwd(const float* dy, const float* x, const T* g, const float* rstd,
     MT_RMS_DISPATCH(rms_vpt(d), L_)
 #undef L_
   }
+  if (dg) rmsnorm_dg_reduce<T>(partial, dg, blocks, d, s);
+}
+
+template <typename T>
+void rmsnorm_dg_reduce(const float* partial, T* dg, int blocks, int d, hipStream_t s) {
   hipLaunchKernelGGL(k_dg_reduce<T>, dim3(cdiv(d, 32)), dim3(256), 0, s, partial, dg, blocks, d);
 }
+
+int rmsnorm_rows_per_block() { return kRmsRows; }
 
 // ----------------------------------------------------------------- RoPE --
 // Token-major transposed buffers [C x M] use a padded row stride (see
@@ -287,7 +294,7 @@ int64_t token_ld(int64_t M) {
 // x_i, x_{i+hd/2} -> x_i cos - x_{i+hd/2} sin, x_i sin + x_{i+hd/2} cos.
 template <typename T>
 __global__ void __launch_bounds__(256) k_rope_qkv(T* qkv, const float* cosb, const float* sinb, int M, int T_, int d,
-                                                  int hd) {
+                                                  int hd, int64_t row0) {
   const int h2 = hd / 2;
   const int64_t per_tok = (int64_t)2 * (d / hd) * h2;  // q and k heads x pairs
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -296,7 +303,7 @@ __global__ void __launch_bounds__(256) k_rope_qkv(T* qkv, const float* cosb, con
   const int j = (int)(id % per_tok);
   const int hh = j / h2, i = j % h2;
   T* x = qkv + m * 3LL * d + (int64_t)hh * hd;
-  const int t = (int)(m % T_);
+  const int t = (int)((m + row0) % T_);
   const float cs = cosb[(int64_t)t * h2 + i], sn = sinb[(int64_t)t * h2 + i];
   const float a = ldf(x[i]), b = ldf(x[i + h2]);
   x[i] = stf<T>(a * cs - b * sn);
@@ -321,7 +328,8 @@ __device__ inline uint4 pack8(const float* f) {
 }
 
 __global__ void __launch_bounds__(256) k_rope_qkv_bf16(uint16_t* __restrict__ qkv, const float* __restrict__ cosb,
-                                                       const float* __restrict__ sinb, int M, int T_, int d) {
+                                                       const float* __restrict__ sinb, int M, int T_, int d,
+                                                       int64_t row0) {
   const int per_tok = 2 * (d / 128) * 8;  // q and k heads x 8 groups of 8 pairs
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (id >= (int64_t)M * per_tok) return;
@@ -329,7 +337,7 @@ __global__ void __launch_bounds__(256) k_rope_qkv_bf16(uint16_t* __restrict__ qk
   const int j = (int)(id % per_tok);
   const int hh = j >> 3, i0 = (j & 7) * 8;
   uint16_t* x = qkv + m * 3LL * d + (int64_t)hh * 128 + i0;
-  const int t = (int)(m % T_);
+  const int t = (int)((m + row0) % T_);
   const float4* cp = (const float4*)(cosb + (int64_t)t * 64 + i0);
   const float4* sp = (const float4*)(sinb + (int64_t)t * 64 + i0);
   const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
@@ -348,17 +356,18 @@ __global__ void __launch_bounds__(256) k_rope_qkv_bf16(uint16_t* __restrict__ qk
 }
 
 template <typename T>
-void rope_qkv_fwd(T* qkv, const float* cosb, const float* sinb, int M, int T_, int d, int hd, hipStream_t s) {
+void rope_qkv_fwd(T* qkv, const float* cosb, const float* sinb, int M, int T_, int d, int hd, hipStream_t s,
+                  int64_t row0) {
   if (M <= 0) return;
   if (std::is_same<T, uint16_t>::value && hd == 128 && d % 128 == 0 && ((uintptr_t)qkv & 15) == 0 &&
       ((uintptr_t)cosb & 15) == 0 && ((uintptr_t)sinb & 15) == 0) {
     const int64_t n = (int64_t)M * 2 * (d / 128) * 8;
     hipLaunchKernelGGL(k_rope_qkv_bf16, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, (uint16_t*)qkv, cosb, sinb,
-                       M, T_, d);
+                       M, T_, d, row0);
     return;
   }
   const int64_t n = (int64_t)M * 2 * (d / hd) * (hd / 2);
-  hipLaunchKernelGGL(k_rope_qkv<T>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, qkv, cosb, sinb, M, T_, d, hd);
+  hipLaunchKernelGGL(k_rope_qkv<T>, dim3((unsigned)cdiv(n, 256)), dim3(256), 0, s, qkv, cosb, sinb, M, T_, d, hd, row0);
 }
 
 // Inverse rotation on the transposed layout: one thread per (pair, 8 tokens)
@@ -712,6 +721,31 @@ void fill_u32(void* p, uint32_t value, size_t n_words, hipStream_t s) {
   hipLaunchKernelGGL(k_fill_u32, dim3(blocks), dim3(256), 0, s, (uint32_t*)p, value, n_words);
 }
 
+// bf16 -> fp32, 8 values (16 bytes in, 32 out) per thread when n % 8 == 0
+__global__ void __launch_bounds__(256) k_widen8(const uint16_t* __restrict__ in, float* __restrict__ out, int64_t n8) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    float f[8];
+    unpack8(*(const uint4*)(in + 8 * i), f);
+    *(float4*)(out + 8 * i) = make_float4(f[0], f[1], f[2], f[3]);
+    *(float4*)(out + 8 * i + 4) = make_float4(f[4], f[5], f[6], f[7]);
+  }
+}
+__global__ void __launch_bounds__(256) k_widen1(const uint16_t* __restrict__ in, float* __restrict__ out, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    out[i] = bf16_to_f32(in[i]);
+}
+
+void widen_bf16(const uint16_t* in, float* out, int64_t n, hipStream_t s) {
+  if (n <= 0) return;
+  if (n % 8 == 0 && ((uintptr_t)in & 15) == 0 && ((uintptr_t)out & 15) == 0) {
+    const int64_t n8 = n / 8;
+    hipLaunchKernelGGL(k_widen8, dim3((unsigned)std::min<int64_t>(cdiv(n8, 256), 65536)), dim3(256), 0, s, in, out,
+                       n8);
+  } else {
+    hipLaunchKernelGGL(k_widen1, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 65536)), dim3(256), 0, s, in, out, n);
+  }
+}
+
 // ------------------------------------------------------ instantiations --
 #define MT_INST(T)                                                                                              \
   template void embed_fwd<T>(const int32_t*, const T*, float*, int, int, hipStream_t);                          \
@@ -719,7 +753,8 @@ void fill_u32(void* p, uint32_t value, size_t n_words, hipStream_t s) {
   template void rmsnorm_fwd<T>(const float*, const T*, T*, float*, int, int, float, hipStream_t);               \
   template void rmsnorm_bwd<T>(const float*, const float*, const T*, const float*, const float*, float*, float*, T*, \
                                int, int, hipStream_t, T*);                                                          \
-  template void rope_qkv_fwd<T>(T*, const float*, const float*, int, int, int, int, hipStream_t);              \
+  template void rope_qkv_fwd<T>(T*, const float*, const float*, int, int, int, int, hipStream_t, int64_t);       \
+  template void rmsnorm_dg_reduce<T>(const float*, T*, int, int, hipStream_t);              \
   template void rope_bwd_T<T>(T*, int64_t, const float*, const float*, int, int, int, int, hipStream_t);        \
   template void swiglu_fwd<T>(const T*, T*, int, int, hipStream_t);                                             \
   template void swiglu_bwd<T>(const T*, const T*, T*, int, int, hipStream_t);                                   \

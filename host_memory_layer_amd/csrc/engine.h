@@ -1,6 +1,8 @@
 // Model handle of the layer-streamed training step (see engine.hip).
 #pragma once
 
+#include <vector>
+
 #include "common.h"
 
 namespace mt {
@@ -9,6 +11,8 @@ struct Model;
 Model* create_model(const mt_config* cfg, void* arena, size_t arena_bytes, void* const streams[3]);
 void destroy_model(Model* m);
 uint64_t device_bytes_for(const mt_config& cfg);
+// The operations of one streamed step as data (no device work).
+std::vector<mt_sched_op> schedule_for(const mt_config& cfg);
 int bind_store(Model* m, void* host, size_t bytes, void* opt, size_t opt_bytes);
 int model_step(Model* m, const int32_t* tokens);
 int model_loss(const Model* m, float* out);

@@ -107,6 +107,10 @@ struct Model {
   int E;  // bytes per weight element
   int HC, n_hc;  // output head: tokens per pass and passes
   int64_t HCp;   // padded row stride of one pass's transposed buffers
+  // Layer token passes: a layer's per-token work (norms, projections,
+  // SwiGLU) runs TC tokens at a time (n_tc passes; 1 = all tokens at once)
+  int TC = 0, n_tc = 1;
+  bool dqkv_kmajor = true;  // several passes: the q/k/v data gradient reads dqkvT as a K-major operand
 
   uint8_t* arena = nullptr;
   size_t arena_bytes = 0;
@@ -121,7 +125,13 @@ struct Model {
   // device
   uint8_t *wslot[2], *gslot[2], *wt;
   uint8_t *wres = nullptr, *gres = nullptr;  // resident mode: every block's W and G
-  float* ckpt;
+  float* ckpt;            // fp32 layer-boundary checkpoints x^0..x^L
+  // MT_FLAG_CKPT_BF16: the checkpoints are kept rounded to bf16 (ckpt16);
+  // the forward carries the fp32 residual stream in two rotating buffers
+  // (xrot), and the backward widens x^l into xrot[0]
+  bool ckpt_lp = false;
+  uint16_t* ckpt16 = nullptr;
+  float* xrot[2] = {nullptr, nullptr};
   float *cosb, *sinb;  // RoPE tables [T x hd/2]
   float *cosT, *sinT;  // the same, transposed [hd/2 x T]
   int32_t *d_tok, *d_order, *d_seg;
@@ -131,6 +141,7 @@ struct Model {
   float* gemm_ws = nullptr;  // stream-K partial tiles of the bf16 GEMMs
   size_t gemm_ws_size = 0;
   float* dxkeep = nullptr;   // MT_FLAG_KEEP_DX: dl/dx^l of every layer boundary, l = 0..L
+  float* wacc = nullptr;     // several token passes: fp32 sums of a layer's weight gradients (W region layout)
   // The bf16 copy ws.dxb mirrors one fp32 gradient at a time: the norm
   // backward that writes it records which, and the K-major backward that
   // reads it as the rounded dx2 checks that it is the dx2 it was given.
@@ -166,32 +177,37 @@ struct Model {
   // ------------------------------------------------------------ layout --
   template <typename T>
   void carve_acts(Carver& c, Acts<T>& a) {
-    const uint64_t Md = (uint64_t)M * d;
-    a.h = c.take<T>(Md * E);
+    // q/k/v, o and the statistics span every token (attention); the rest
+    // one token pass (TC = M with a single pass)
+    const uint64_t Md = (uint64_t)M * d, Cd = (uint64_t)TC * d;
+    a.h = c.take<T>(Cd * E);
     a.qkv = c.take<T>(3 * Md * E);
     a.o = c.take<T>(Md * E);
-    a.h2 = c.take<T>(Md * E);
-    a.gu = c.take<T>((uint64_t)M * 2 * F * E);
-    a.y = c.take<T>((uint64_t)M * F * E);
+    a.h2 = c.take<T>(Cd * E);
+    a.gu = c.take<T>((uint64_t)TC * 2 * F * E);
+    a.y = c.take<T>((uint64_t)TC * F * E);
     a.r1 = c.take<float>((uint64_t)M * 4);
     a.lse = c.take<float>((uint64_t)M * H * 4);
-    a.x1 = c.take<float>(Md * 4);
+    a.x1 = c.take<float>(Cd * 4);
     a.r2 = c.take<float>((uint64_t)M * 4);
   }
   template <typename T>
   void carve_bwd(Carver& c, BwdWs<T>& w) {
-    const uint64_t Md = (uint64_t)M * d, MF = (uint64_t)M * F;
+    // several token passes: dy, dgu, dh and the transposed q/k/v gradient
+    // hold one pass; dl/dx1 goes straight into the layer's output gradient
+    const uint64_t Md = (uint64_t)M * d, CF = (uint64_t)TC * F, Cd = (uint64_t)TC * d;
+    const bool tc = n_tc > 1;
     w.dxb = c.take<T>(Md * E);
     w.dxbT = kmajor ? nullptr : c.take<T>((uint64_t)d * Mp * E);
     w.tmpT = kmajor && kmajor_head ? nullptr : c.take<T>((uint64_t)std::max(d, F) * Mp * E);
-    w.dy = c.take<T>(MF * E);
-    w.dgu = c.take<T>(2 * MF * E);
+    w.dy = c.take<T>(CF * E);
+    w.dgu = c.take<T>(2 * CF * E);
     w.dguT = kmajor ? nullptr : c.take<T>(2 * (uint64_t)F * Mp * E);
     w.do_ = c.take<T>(Md * E);
     w.dqkvT = c.take<T>(3 * (uint64_t)d * Mp * E);
-    w.dqkv = kmajor ? nullptr : c.take<T>(3 * Md * E);
-    w.dh = c.take<float>(Md * 4);
-    w.dx1 = c.take<float>(Md * 4);
+    w.dqkv = (kmajor && !tc) || (tc && dqkv_kmajor) ? nullptr : c.take<T>(3 * Cd * E);
+    w.dh = c.take<float>(Cd * 4);
+    w.dx1 = c.take<float>((tc ? Cd : Md) * 4);
     w.Dsum = c.take<float>((uint64_t)M * H * 4);
     w.part = c.take<float>(rmsnorm_dg_partial_elems(M, d) * 4);
     w.dxA = c.take<float>(Md * 4);
@@ -224,7 +240,13 @@ struct Model {
       wres = c.take<uint8_t>(tot);
       gres = c.take<uint8_t>(tot);
     }
-    ckpt = c.take<float>((uint64_t)(L + 1) * M * d * 4);
+    if (ckpt_lp) {
+      ckpt = nullptr;
+      ckpt16 = c.take<uint16_t>((uint64_t)(L + 1) * M * d * 2);
+      for (int i = 0; i < 2; ++i) xrot[i] = c.take<float>((uint64_t)M * d * 4);
+    } else {
+      ckpt = c.take<float>((uint64_t)(L + 1) * M * d * 4);
+    }
     cosb = c.take<float>((uint64_t)Tq * (hd / 2) * 4);
     sinb = c.take<float>((uint64_t)Tq * (hd / 2) * 4);
     cosT = c.take<float>((uint64_t)Tq * (hd / 2) * 4);
@@ -268,6 +290,8 @@ struct Model {
     }
     dxkeep = cfg.flags & MT_FLAG_KEEP_DX ? c.take<float>((uint64_t)(L + 1) * M * d * 4) : nullptr;
     if (!base) dxkeep = nullptr;
+    wacc = n_tc > 1 ? c.take<float>(blocks[1].region_elems * 4) : nullptr;
+    if (!base) wacc = nullptr;
     return c.off;
   }
   // Layers whose forward intermediates stay on the device until their backward.
@@ -321,21 +345,72 @@ struct Model {
       HC = std::min<int64_t>(M, std::max<int64_t>(256, (int64_t)((4ull << 30) / head_row) / 256 * 256));
     n_hc = (M + HC - 1) / HC;
     HCp = token_ld(HC);
+    TC = M;
+    n_tc = 1;
     if (bf16_store(c)) {
       const int A_ = GEMM_A_KMAJOR, B_ = GEMM_B_KMAJOR;
       auto ok = [&](int m, int n, int k, int64_t lda, int64_t ldb, int lay) {
         return gemm_layout_ok(m, n, k, lda, ldb, lay);
       };
-      kmajor = ok(d, F, M, d, F, A_ | B_) && ok(M, F, d, d, F, B_) && ok(2 * F, d, M, 2 * F, d, A_ | B_) &&
-               ok(M, d, 2 * F, 2 * F, d, B_) && ok(d, d, M, d, d, A_ | B_) && ok(M, d, d, d, d, B_) &&
-               ok(3 * d, d, M, Mp, d, B_) && ok(M, d, 3 * d, Mp, d, A_ | B_);
+      // the layer's weight gradients contract over K = the tokens of a pass
+      auto wgrads_ok = [&](int K) {
+        return ok(d, F, K, d, F, A_ | B_) && ok(2 * F, d, K, 2 * F, d, A_ | B_) && ok(d, d, K, d, d, A_ | B_) &&
+               ok(3 * d, d, K, Mp, d, B_);
+      };
+      const bool dgrads_ok = ok(M, F, d, d, F, B_) && ok(M, d, 2 * F, 2 * F, d, B_) && ok(M, d, d, d, d, B_);
+      kmajor = wgrads_ok(M) && dgrads_ok && ok(M, d, 3 * d, Mp, d, A_ | B_);
       kmajor_head = ok(V, d, HC, V, d, A_ | B_) && ok(HC, d, V, V, d, B_);
+      // token passes: asked for, or needed to keep the K-major weight
+      // gradients within their operand addressing
+      int want = 0;
+      if (c.token_chunk > 0 && c.token_chunk < M)
+        want = c.token_chunk;
+      else if (c.token_chunk == 0 && !kmajor) {
+        const int64_t ldmax = std::max<int64_t>({d, F, 2 * (int64_t)F});
+        want = (int)std::min<int64_t>(32768, ((((int64_t)1 << 31) - 1) / (2 * ldmax)) / 256 * 256);
+      }
+      if (want > 0 && want < M) {
+        const int n = (M + want - 1) / want;
+        TC = (int)round_up((uint64_t)((M + n - 1) / n), 64);
+        n_tc = (M + TC - 1) / TC;
+        const int last = M - (n_tc - 1) * TC;
+        if (n_tc > 1) {
+          if (!(wgrads_ok(TC) && wgrads_ok(last) && dgrads_ok))
+            throw ApiError{MT_E_INVALID, "token passes: each pass needs at least 192 tokens, a multiple of 64, "
+                                         "within the matrix kernels' operand addressing"};
+          kmajor = true;
+          dqkv_kmajor = ok(TC, d, 3 * d, Mp, d, A_ | B_);
+        } else {
+          TC = M;
+        }
+      }
+    } else if (c.token_chunk > 0 && c.token_chunk < M) {
+      throw ApiError{MT_E_INVALID, "token passes need a bf16 store"};
     }
+    ckpt_lp = c.flags & MT_FLAG_CKPT_BF16;
+    if (ckpt_lp && (!bf16_store(c) || c.mode == MT_RESIDENT || c.retain_layers > 0))
+      throw ApiError{MT_E_INVALID, "bf16 checkpoints need a bf16 store and a streamed, serialized or single-slot "
+                                   "schedule without retained layers"};
+    if (n_tc > 1 && (c.mode == MT_RESIDENT || c.retain_layers > 0))
+      throw ApiError{MT_E_INVALID, "token passes need a streamed, serialized or single-slot schedule without "
+                                   "retained layers"};
     n_uses = 2 * L + 3;
   }
   uint64_t device_bytes() { return bf16_store(cfg) ? carve_all<uint16_t>(nullptr) : carve_all<float>(nullptr); }
 
   float* x_ckpt(int l) { return ckpt + (uint64_t)l * M * d; }
+  // x^l as the forward sweep reads and writes it (fp32)
+  float* x_fwd(int l) { return ckpt_lp ? xrot[l & 1] : x_ckpt(l); }
+  // after x^l is complete in the forward sweep: its bf16 checkpoint
+  void store_ckpt(int l) {
+    if (ckpt_lp) cast<uint16_t>(xrot[l & 1], ckpt16 + (uint64_t)l * M * d, (int64_t)M * d, sc);
+  }
+  // x^l for the backward sweep (widened from its bf16 checkpoint)
+  const float* x_bwd(int l) {
+    if (!ckpt_lp) return x_ckpt(l);
+    widen_bf16(ckpt16 + (uint64_t)l * M * d, xrot[0], (int64_t)M * d, sc);
+    return xrot[0];
+  }
   // MT_FLAG_KEEP_DX: a copy of the gradient arriving at layer boundary l
   void keep_dx(int l, const float* dx) {
     if (dxkeep)
@@ -480,16 +555,128 @@ struct Model {
     dxb_holds = dx_out;
   }
 
+  // ---- a layer in token passes (n_tc > 1) -------------------------------
+  // The per-token work of a layer runs TC tokens at a time; the attention
+  // runs over every token.  Rows [r0, r0 + rows) belong to pass p.
+  void pass_rows(int p, int64_t* r0, int* rows) const {
+    *r0 = (int64_t)p * TC;
+    *rows = (int)std::min<int64_t>(TC, M - *r0);
+  }
+  // The attention's input for one pass: h, then q, k, v (q, k rotated)
+  template <typename T>
+  void qkv_pass(const LayerW<T>& w, const float* x, const Acts<T>& a, int64_t r0, int rows) {
+    rmsnorm_fwd<T>(x + r0 * d, w.anorm, a.h, a.r1 + r0, rows, d, (float)cfg.rms_eps, sc);
+    gemm<T>(a.h, d, w.qkv, d, a.qkv + r0 * 3 * d, 3 * d, nullptr, 0, rows, 3 * d, d, EPI_STORE);
+    rope_qkv_fwd<T>(a.qkv + r0 * 3 * d, cosb, sinb, rows, Tq, d, hd, sc, r0);
+  }
+  // Output projection and FFN of one pass: x1, h2, gu, y (and x_out rows)
+  template <typename T>
+  void ffn_pass(const LayerW<T>& w, const float* x, const Acts<T>& a, int64_t r0, int rows, float* x_out) {
+    gemm<T>(a.o + r0 * d, d, w.o, d, a.x1, d, x + r0 * d, d, rows, d, d, EPI_ADD_F32);
+    rmsnorm_fwd<T>(a.x1, w.fnorm, a.h2, a.r2 + r0, rows, d, (float)cfg.rms_eps, sc);
+    gemm<T>(a.h2, d, w.gu, d, a.gu, 2 * F, nullptr, 0, rows, 2 * F, d, EPI_STORE);
+    swiglu_fwd<T>(a.gu, a.y, rows, F, sc);
+    if (x_out) gemm<T>(a.y, F, w.d, F, x_out + r0 * d, d, a.x1, d, rows, d, F, EPI_ADD_F32);
+  }
+  // Forward of a layer in passes; without x_out (the recompute inside the
+  // backward) it stops after the attention: the backward recomputes each
+  // pass's FFN input just before it needs it.
+  template <typename T>
+  void layer_fwd_passes(const LayerW<T>& w, const float* x, const Acts<T>& a, float* x_out) {
+    int64_t r0;
+    int rows;
+    for (int p = 0; p < n_tc; ++p) {
+      pass_rows(p, &r0, &rows);
+      qkv_pass<T>(w, x, a, r0, rows);
+    }
+    const bool timed = cfg.flags & MT_FLAG_TIME_KERNELS;
+    if (timed) record_kernel_start(attn_fwd_flops(), 1);
+    attn_fwd<T>(a.qkv, a.o, a.lse, B, Tq, H, hd, sc);
+    if (timed) record_kernel_end();
+    if (!x_out) return;
+    for (int p = 0; p < n_tc; ++p) {
+      pass_rows(p, &r0, &rows);
+      ffn_pass<T>(w, x, a, r0, rows, x_out);
+    }
+  }
+  // Backward of a layer in passes.  Weight gradients are summed over the
+  // passes in fp32 (wacc, in the W region's layout) and rounded once; the
+  // gain gradients' per-block partial sums cover all rows before their one
+  // reduction, in the order of a single pass.
+  template <typename T>
+  void layer_bwd_passes(const LayerW<T>& w, const float* x, const Acts<T>& a, const float* dx2, float* dx_out,
+                        const LayerW<T>& g, const mt_block_desc& b, const BwdWs<T>& ws) {
+    const int KA = GEMM_A_KMAJOR, KB = GEMM_B_KMAJOR;
+    if (dxb_holds != dx2) throw ApiError{MT_E_STATE, "layer backward in passes: bf16 copy does not mirror its dx"};
+    const LayerW<float> acc = bind_layer<float>((uint8_t*)wacc, b);
+    const int rpb = rmsnorm_rows_per_block();
+    const int nblk = (M + rpb - 1) / rpb;
+    int64_t r0;
+    int rows;
+    // FFN and output projection.  The pass's rows of dxb hold bf16(dx2),
+    // then bf16(dl/dx1); dl/dx1 itself goes into dx_out.
+    for (int p = 0; p < n_tc; ++p) {
+      pass_rows(p, &r0, &rows);
+      const Epi ep = p == 0 ? EPI_F32 : EPI_ADD_F32;
+      ffn_pass<T>(w, x, a, r0, rows, nullptr);
+      const T* dxb = ws.dxb + r0 * d;
+      gemm<T>(dxb, d, a.y, F, acc.d, F, p ? acc.d : nullptr, F, d, F, rows, ep, KA | KB);
+      gemm<T>(dxb, d, w.d, F, ws.dy, F, nullptr, 0, rows, F, d, EPI_STORE, KB);
+      swiglu_bwd<T>(ws.dy, a.gu, ws.dgu, rows, F, sc);
+      gemm<T>(ws.dgu, 2 * F, a.h2, d, acc.gu, d, p ? acc.gu : nullptr, d, 2 * F, d, rows, ep, KA | KB);
+      gemm<T>(ws.dgu, 2 * F, w.gu, d, ws.dh, d, nullptr, 0, rows, d, 2 * F, EPI_F32, KB);
+      rmsnorm_bwd<T>(ws.dh, a.x1, w.fnorm, a.r2 + r0, dx2 + r0 * d, dx_out + r0 * d, ws.part + (r0 / rpb) * d,
+                     nullptr, rows, d, sc, ws.dxb + r0 * d);
+      gemm<T>(dxb, d, a.o + r0 * d, d, acc.o, d, p ? acc.o : nullptr, d, d, d, rows, ep, KA | KB);
+      gemm<T>(dxb, d, w.o, d, ws.do_ + r0 * d, d, nullptr, 0, rows, d, d, EPI_STORE, KB);
+    }
+    rmsnorm_dg_reduce<T>(ws.part, g.fnorm, nblk, d, sc);
+    cast<T>(acc.d, g.d, (int64_t)d * F, sc);
+    cast<T>(acc.gu, g.gu, 2 * (int64_t)F * d, sc);
+    cast<T>(acc.o, g.o, (int64_t)d * d, sc);
+    // attention over every token
+    attn_bwd_dsum<T>(ws.do_, a.o, ws.Dsum, B, Tq, H, hd, sc);
+    const bool timed = cfg.flags & MT_FLAG_TIME_KERNELS;
+    if (timed) record_kernel_start(2.5 * attn_fwd_flops(), 1);
+    attn_bwd<T>(a.qkv, ws.do_, a.lse, ws.Dsum, ws.dqkvT, Mp, B, Tq, H, hd, sc);
+    if (timed) record_kernel_end();
+    rope_bwd_T<T>(ws.dqkvT, Mp, cosT, sinT, M, Tq, d, hd, sc);
+    // q/k/v projection (h of the pass recomputed); dx = dl/dx1 + the attention
+    // norm's gradient, computed into a pass buffer and copied into dx_out
+    for (int p = 0; p < n_tc; ++p) {
+      pass_rows(p, &r0, &rows);
+      const Epi ep = p == 0 ? EPI_F32 : EPI_ADD_F32;
+      rmsnorm_fwd<T>(x + r0 * d, w.anorm, a.h, a.r1 + r0, rows, d, (float)cfg.rms_eps, sc);
+      const T* dT = ws.dqkvT + r0;
+      gemm<T>(dT, Mp, a.h, d, acc.qkv, d, p ? acc.qkv : nullptr, d, 3 * d, d, rows, ep, KB);
+      if (dqkv_kmajor) {
+        gemm<T>(dT, Mp, w.qkv, d, ws.dh, d, nullptr, 0, rows, d, 3 * d, EPI_F32, KA | KB);
+      } else {
+        transpose<T>(dT, Mp, ws.dqkv, 3 * d, 3 * d, rows, sc);
+        gemm<T>(ws.dqkv, 3 * d, w.qkv, d, ws.dh, d, nullptr, 0, rows, d, 3 * d, EPI_F32, KB);
+      }
+      rmsnorm_bwd<T>(ws.dh, x + r0 * d, w.anorm, a.r1 + r0, dx_out + r0 * d, ws.dx1, ws.part + (r0 / rpb) * d,
+                     nullptr, rows, d, sc, ws.dxb + r0 * d);
+      MT_HIP(hipMemcpyAsync(dx_out + r0 * d, ws.dx1, (uint64_t)rows * d * 4, hipMemcpyDeviceToDevice, sc));
+    }
+    rmsnorm_dg_reduce<T>(ws.part, g.anorm, nblk, d, sc);
+    cast<T>(acc.qkv, g.qkv, 3 * (int64_t)d * d, sc);
+    dxb_holds = dx_out;
+  }
+
   // Final norm, logits, loss, and the head's backward.  Returns dx^L in dx_out.
+  // dl/dz for every token goes to the other dx buffer, free until the top
+  // layer's backward (the layer workspace holds one token pass).
   template <typename T>
   void head_fwd_bwd(const mt_block_desc& b, uint8_t* wreg, uint8_t* greg, float* dx_out) {
     HeadWs<T> hw = headws<T>();
     BwdWs<T> ws = bwdws<T>();
+    float* dz = dx_out == ws.dxA ? ws.dxB : ws.dxA;
     const T* wh = (const T*)wreg + b.tensors[T_WH].offset;
     const T* fin = (const T*)wreg + b.tensors[T_FINAL].offset;
     T* gwh = (T*)greg + b.tensors[T_WH].offset;
     T* gfin = (T*)greg + b.tensors[T_FINAL].offset;
-    const float* xL = x_ckpt(L);
+    const float* xL = x_fwd(L);
     // mean over the labelled positions of every micro-batch of the step
     const float inv_n = 1.0f / (float)((int64_t)micro_count(cfg) * B * (Tq - 1));
     rmsnorm_fwd<T>(xL, fin, hw.z, hw.rz, M, d, (float)cfg.rms_eps, sc);
@@ -511,12 +698,12 @@ struct Model {
       const Epi epi = !gsum ? EPI_STORE : (p > 0 ? EPI_ADD_F32 : EPI_F32);
       if (kmajor_head) {
         gemm<T>(hw.dlogits, V, zc, d, gout, d, R, d, V, d, rows, epi, GEMM_A_KMAJOR | GEMM_B_KMAJOR);
-        gemm<T>(hw.dlogits, V, wh, d, ws.dh + r0 * d, d, nullptr, 0, rows, d, V, EPI_F32, GEMM_B_KMAJOR);
+        gemm<T>(hw.dlogits, V, wh, d, dz + r0 * d, d, nullptr, 0, rows, d, V, EPI_F32, GEMM_B_KMAJOR);
       } else {
         transpose<T>(hw.dlogits, V, hw.dlogitsT, HCp, rows, V, sc);
         transpose<T>(zc, d, ws.tmpT, HCp, rows, d, sc);
         gemm<T>(hw.dlogitsT, HCp, ws.tmpT, HCp, gout, d, R, d, V, d, rows, epi);
-        gemm<T>(hw.dlogits, V, whT, V, ws.dh + r0 * d, d, nullptr, 0, rows, d, V, EPI_F32);
+        gemm<T>(hw.dlogits, V, whT, V, dz + r0 * d, d, nullptr, 0, rows, d, V, EPI_F32);
       }
     }
     if (gsum && E == 2) cast<T>(gsum, gwh, (int64_t)V * d, sc);
@@ -524,7 +711,7 @@ struct Model {
     MT_HIP(hipMemcpyAsync(h_loss, hw.loss, sizeof(float), hipMemcpyDeviceToHost, sc));
     MT_HIP(hipEventRecord(ev_loss, sc));
     // dx^L, and bf16(dx^L) for the top layer's down projection when it reads it
-    rmsnorm_bwd<T>(ws.dh, xL, fin, hw.rz, nullptr, dx_out, ws.part, gfin, M, d, sc, kmajor ? ws.dxb : nullptr);
+    rmsnorm_bwd<T>(dz, xL, fin, hw.rz, nullptr, dx_out, ws.part, gfin, M, d, sc, kmajor ? ws.dxb : nullptr);
     dxb_holds = kmajor ? dx_out : nullptr;
     keep_dx(L, dx_out);
   }
@@ -534,10 +721,15 @@ struct Model {
   void compute_block_fwd(int j, uint8_t* wreg) {
     const mt_block_desc& b = blocks[j];
     if (b.kind == MT_BLOCK_EMBED) {
-      embed_fwd<T>(d_tok, (const T*)wreg + b.tensors[0].offset, x_ckpt(0), M, d, sc);
+      embed_fwd<T>(d_tok, (const T*)wreg + b.tensors[0].offset, x_fwd(0), M, d, sc);
+      store_ckpt(0);
     } else {
       const int l = b.layer;
-      layer_fwd<T>(bind_layer<T>(wreg, b), x_ckpt(l), acts<T>(l), x_ckpt(l + 1), true);
+      if (n_tc > 1)
+        layer_fwd_passes<T>(bind_layer<T>(wreg, b), x_fwd(l), acts<T>(l), x_fwd(l + 1));
+      else
+        layer_fwd<T>(bind_layer<T>(wreg, b), x_fwd(l), acts<T>(l), x_fwd(l + 1), true);
+      store_ckpt(l + 1);
     }
   }
 
@@ -552,9 +744,16 @@ struct Model {
       t = LayerWT<T>{(T*)wt, (T*)wt + (uint64_t)3 * d * d, (T*)wt + (uint64_t)4 * d * d,
                      (T*)wt + (uint64_t)4 * d * d + (uint64_t)2 * F * d};
     Acts<T> a = acts<T>(l);
-    if (cfg.mode != MT_RESIDENT && !retained(l)) layer_fwd<T>(w, x_ckpt(l), a, nullptr, false);  // recompute
+    const float* x = x_bwd(l);
+    if (n_tc > 1) {
+      layer_fwd_passes<T>(w, x, a, nullptr);  // recompute up to the attention
+      layer_bwd_passes<T>(w, x, a, dx_in, dx_out, g, b, bwdws<T>());
+      keep_dx(l, dx_out);
+      return;
+    }
+    if (cfg.mode != MT_RESIDENT && !retained(l)) layer_fwd<T>(w, x, a, nullptr, false);  // recompute
     if (!kmajor) weight_transposes<T>(w, t);
-    layer_bwd<T>(w, t, x_ckpt(l), a, dx_in, dx_out, g);
+    layer_bwd<T>(w, t, x, a, dx_in, dx_out, g);
     keep_dx(l, dx_out);
   }
 
@@ -566,6 +765,24 @@ struct Model {
   void run_pass(const int32_t* tokens, int64_t t, double* adam_total, double* adam_tail);
   void finish_stats(bool streamed, double wall_ms);
   int mb = 0;  // micro-batch of the running pass
+  // MT_FLAG_DELAYS: the delay before operation (lane, use) of this step and
+  // micro-batch, 0 to 1999 us (0 for about half), from a splitmix64 hash
+  int64_t step_t = 0;
+  int delay_us(int lane, int use) const {
+    if (!(cfg.flags & MT_FLAG_DELAYS)) return 0;
+    uint64_t z = (uint64_t)step_t * 0x9E3779B97F4A7C15ull ^ (uint64_t)(mb * 4 + lane) * 0xD1B54A32D192ED03ull ^
+                 (uint64_t)(use + 1) * 0x8CB92BA72F3D8DD7ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return (z & 1) ? 0 : (int)((z >> 1) % 2000);
+  }
+  static void sleep_host(void* us) { std::this_thread::sleep_for(std::chrono::microseconds((intptr_t)us)); }
+  // the stream's later work waits for a host function that sleeps
+  void stream_delay(hipStream_t s, int lane, int use) {
+    const int us = delay_us(lane, use);
+    if (us > 0) MT_HIP(hipLaunchHostFunc(s, sleep_host, (void*)(intptr_t)us));
+  }
 
   // Adam worker coordination
   std::mutex q_mu;
@@ -592,6 +809,44 @@ struct Model {
     q_cv.notify_all();
   }
   void adam_worker(int64_t t, double* adam_total, double* adam_tail, std::atomic<bool>* device_done);
+
+  // ---- the streamed schedule as data (mt_schedule) --------------------
+  // A dry run of step_streamed records every operation it would issue and
+  // the earlier operations each one waits for, and issues no device work.
+  struct TraceOp {
+    int lane, kind, use, block, wslot, gslot;
+    std::vector<int> waits;  // data and ordering dependencies
+    std::vector<int> link;   // orderings that only share out the host link
+  };
+  std::vector<TraceOp>* trace = nullptr;
+  // Per ordered lane, the latest operation the enqueueing thread has waited
+  // for: every operation issued after that wait follows it.
+  int fence[3] = {-1, -1, -1};
+  int tr_add(int lane, int kind, int use, int block, int ws, int gs, std::vector<int> waits, std::vector<int> link) {
+    if (!trace) return -1;
+    for (int f : fence) waits.push_back(f);
+    waits.erase(std::remove(waits.begin(), waits.end(), -1), waits.end());
+    std::sort(waits.begin(), waits.end());
+    waits.erase(std::unique(waits.begin(), waits.end()), waits.end());
+    link.erase(std::remove(link.begin(), link.end(), -1), link.end());
+    trace->push_back(TraceOp{lane, kind, use, block, ws, gs, waits, link});
+    return (int)trace->size() - 1;
+  }
+  void tr_fence(int op) {
+    if (!trace || op < 0) return;
+    const int lane = (*trace)[op].lane;
+    fence[lane] = std::max(fence[lane], op);
+  }
+  // Offloads yield the host link to prefetches when a layer's backward is
+  // compute-bound against the link (its flops per transferred weight and
+  // gradient byte well above ~1 PFLOP/s over ~50 GB/s): the transfers are
+  // hidden either way and each then runs at the full one-way rate.  When the
+  // link is the bottleneck, both directions share it.
+  bool link_yields() const {
+    const double layer_bytes = 2.0 * (double)blocks[1].w_bytes;
+    const double bwd_flops = 3.0 * (2.0 * M * (4.0 * d * d + 3.0 * d * F)) + 3.5 * attn_fwd_flops();
+    return !(cfg.flags & MT_FLAG_DUPLEX_LINK) && bwd_flops / layer_bytes > 30000.0;
+  }
 
   // Streamed schedules: weight prefetches and gradient offloads run on two
   // SDMA engines, each fed in order by a worker thread (dma.h).  The
@@ -627,6 +882,7 @@ void Model::adam_worker(int64_t t, double* adam_total, double* adam_tail, std::a
         ++next;
       }
       if (ev) MT_HIP(hipEventSynchronize(ev));
+      if (const int us = delay_us(MT_LANE_HOST, blk)) std::this_thread::sleep_for(std::chrono::microseconds(us));
       if (nonfinite) continue;
       auto t0 = std::chrono::steady_clock::now();
       const mt_block_desc& b = blocks[blk];
@@ -685,6 +941,7 @@ void Model::adam_worker(int64_t t, double* adam_total, double* adam_tail, std::a
 // backward because the head has replaced it.
 template <typename T>
 void Model::step_streamed(bool serialize) {
+  const bool dry = trace != nullptr;  // record the schedule, issue nothing
   const bool single = cfg.mode == MT_SINGLE_SLOT;
   auto slot_of = [&](int j) { return single ? 0 : j % 2; };
   const bool poison = cfg.flags & MT_FLAG_POISON;
@@ -700,66 +957,113 @@ void Model::step_streamed(bool serialize) {
     int u, j, g;
   } pending{-1, -1, -1};
   const bool defer = hipq && yield_link && !serialize;
+  // dry run: the operation each event or job stands for
+  std::vector<int> op_fetch(n_uses, -1), op_poison(n_uses, -1), op_comp(n_uses, -1), op_off(n_uses, -1);
+  std::vector<int> op_gslot_last(2, -1);
+  int op_last_comp = -1, op_last_out = -1;
+  std::vector<int> comp_waits;  // dependencies gathered for the next compute operation
+  for (int& f : fence) f = -1;
 
   auto fetch = [&](int u, int j) {
     const int s = slot_of(j);
     hipEvent_t ready = slot_last_use[s] >= 0 ? ev_c_e[slot_last_use[s]] : nullptr;
+    int op_ready = slot_last_use[s] >= 0 ? op_comp[slot_last_use[s]] : -1;
     if (poison) {
       // NaN-fill the slot on the compute stream, after its last use.
-      fill_u32(wslot[s], nan_word, slot_bytes / 4, sc);
-      MT_HIP(hipEventRecord(ev_slot_free[u], sc));
+      if (!dry) {
+        fill_u32(wslot[s], nan_word, slot_bytes / 4, sc);
+        MT_HIP(hipEventRecord(ev_slot_free[u], sc));
+      }
+      op_poison[u] = tr_add(MT_LANE_COMPUTE, MT_OP_POISON, u, j, s, -1, {op_last_comp}, {});
+      op_last_comp = op_poison[u];
       ready = ev_slot_free[u];
+      op_ready = op_poison[u];
     }
     if (serialize) {
-      MT_HIP(hipStreamSynchronize(sc));
+      if (!dry) MT_HIP(hipStreamSynchronize(sc));
+      tr_fence(op_last_comp);
       ready = nullptr;
+      op_ready = -1;
     }
     u_fetched[u] = 1;
-    if (hipq) {
+    op_fetch[u] = tr_add(MT_LANE_PREFETCH, MT_OP_FETCH, u, j, s, -1, {op_ready}, {});
+    if (dry) {
+      if (serialize) tr_fence(op_fetch[u]);
+    } else if (hipq) {
       if (ready) MT_HIP(hipStreamWaitEvent(sp, ready, 0));
+      stream_delay(sp, MT_LANE_PREFETCH, u);
       MT_HIP(hipEventRecord(ev_x_s[u], sp));
       MT_HIP(hipMemcpyAsync(wslot[s], host + blocks[j].w_off, blocks[j].w_bytes, hipMemcpyHostToDevice, sp));
       MT_HIP(hipEventRecord(ev_x_e[u], sp));
       if (serialize) MT_HIP(hipStreamSynchronize(sp));
     } else {
-      fetch_job[u] = xq_in->push({u, j, ready, wslot[s], host + blocks[j].w_off, (size_t)blocks[j].w_bytes});
+      fetch_job[u] = xq_in->push({u, j, ready, wslot[s], host + blocks[j].w_off, (size_t)blocks[j].w_bytes,
+                                  delay_us(MT_LANE_PREFETCH, u)});
       if (serialize) xq_in->wait(fetch_job[u]);
     }
   };
   auto begin = [&](int u) {
-    if (hipq) {
-      if (u_fetched[u]) MT_HIP(hipStreamWaitEvent(sc, ev_x_e[u], 0));
-    } else if (fetch_job[u] >= 0) {
-      xq_in->wait(fetch_job[u]);
+    if (u_fetched[u]) {
+      if (hipq) {
+        if (!dry) MT_HIP(hipStreamWaitEvent(sc, ev_x_e[u], 0));
+        comp_waits.push_back(op_fetch[u]);
+      } else {
+        if (!dry) xq_in->wait(fetch_job[u]);
+        tr_fence(op_fetch[u]);
+      }
     }
-    MT_HIP(hipEventRecord(ev_c_s[u], sc));
+    if (!dry) {
+      stream_delay(sc, MT_LANE_COMPUTE, u);
+      MT_HIP(hipEventRecord(ev_c_s[u], sc));
+    }
   };
-  auto end = [&](int u, int j) {
-    MT_HIP(hipEventRecord(ev_c_e[u], sc));
-    slot_last_use[slot_of(j)] = u;
+  // the compute operation of use u: block j, weight slot ws (-1: none),
+  // gradient slot gs (-1: none)
+  auto end = [&](int u, int j, int ws, int gs) {
+    if (!dry) MT_HIP(hipEventRecord(ev_c_e[u], sc));
+    comp_waits.push_back(op_last_comp);
+    op_comp[u] = tr_add(MT_LANE_COMPUTE, MT_OP_COMPUTE, u, j, ws, gs, comp_waits, {});
+    op_last_comp = op_comp[u];
+    comp_waits.clear();
+    if (ws >= 0) slot_last_use[ws] = u;
   };
   // Grad slot for a backward use: the offload that last read it has finished.
   auto grad_slot = [&]() -> int {
     const int g = gcount % 2;
     if (gslot_last[g] >= 0) {
-      if (hipq)
-        MT_HIP(hipStreamWaitEvent(sc, ev_o_e[gslot_last[g]], 0));
-      else
-        xq_out->wait(gslot_last[g]);
+      if (hipq) {
+        if (!dry) MT_HIP(hipStreamWaitEvent(sc, ev_o_e[gslot_last[g]], 0));
+        comp_waits.push_back(op_gslot_last[g]);
+      } else {
+        if (!dry) xq_out->wait(gslot_last[g]);
+        tr_fence(op_gslot_last[g]);
+      }
     }
     return g;
   };
   // after_fetch >= 0: the offload also waits for that use's prefetch copy
   auto issue_offload = [&](int u, int j, int g, int after_fetch) {
     hipEvent_t ready = ev_c_e[u];
+    int op_ready = op_comp[u];
     if (serialize) {
-      MT_HIP(hipStreamSynchronize(sc));
+      if (!dry) MT_HIP(hipStreamSynchronize(sc));
+      tr_fence(op_last_comp);
       ready = nullptr;
+      op_ready = -1;
     }
     u_offloaded[u] = 1;
-    if (hipq) {
+    op_off[u] = tr_add(MT_LANE_OFFLOAD, MT_OP_OFFLOAD, u, j, -1, g, {op_ready},
+                       {after_fetch >= 0 ? op_fetch[after_fetch] : -1});
+    tr_add(MT_LANE_HOST, MT_OP_ADAM, u, j, -1, -1, {op_off[u]}, {});
+    op_last_out = op_off[u];
+    op_gslot_last[g] = op_off[u];
+    if (dry) {
+      last_out = u;
+      if (serialize) tr_fence(op_off[u]);
+    } else if (hipq) {
       if (ready) MT_HIP(hipStreamWaitEvent(so, ready, 0));
       if (after_fetch >= 0) MT_HIP(hipStreamWaitEvent(so, ev_x_e[after_fetch], 0));
+      stream_delay(so, MT_LANE_OFFLOAD, u);
       MT_HIP(hipEventRecord(ev_o_s[u], so));
       MT_HIP(hipMemcpyAsync(host + blocks[j].g_off, gslot[g], blocks[j].w_bytes, hipMemcpyDeviceToHost, so));
       MT_HIP(hipEventRecord(ev_o_e[u], so));
@@ -767,7 +1071,8 @@ void Model::step_streamed(bool serialize) {
       last_out = u;
       if (serialize) MT_HIP(hipStreamSynchronize(so));
     } else {
-      last_out = xq_out->push({u, j, ready, host + blocks[j].g_off, gslot[g], (size_t)blocks[j].w_bytes});
+      last_out = xq_out->push({u, j, ready, host + blocks[j].g_off, gslot[g], (size_t)blocks[j].w_bytes,
+                               delay_us(MT_LANE_OFFLOAD, u)});
       if (serialize) xq_out->wait(last_out);
     }
     gslot_last[g] = last_out;
@@ -793,14 +1098,14 @@ void Model::step_streamed(bool serialize) {
     if (j + 1 <= L + 1 && !single) fetch(j + 1, j + 1);
     if (j <= L) {
       begin(j);
-      compute_block_fwd<T>(j, wslot[slot_of(j)]);
-      end(j, j);
+      if (!dry) compute_block_fwd<T>(j, wslot[slot_of(j)]);
+      end(j, j, slot_of(j), -1);
     } else {
       // head: forward, loss, backward; weights stay bound for both
       const int g = grad_slot();
       begin(j);
-      head_fwd_bwd<T>(blocks[j], wslot[slot_of(j)], gslot[g], ws.dxA);
-      end(j, j);
+      if (!dry) head_fwd_bwd<T>(blocks[j], wslot[slot_of(j)], gslot[g], ws.dxA);
+      end(j, j, slot_of(j), g);
       offload(j, j, g);
     }
   }
@@ -824,8 +1129,8 @@ void Model::step_streamed(bool serialize) {
     flush(fu);
     const int g = grad_slot();
     begin(u);
-    compute_layer_bwd<T>(j, wslot[slot_of(j)], gslot[g], dx_in, dx_out);
-    end(u, j);
+    if (!dry) compute_layer_bwd<T>(j, wslot[slot_of(j)], gslot[g], dx_in, dx_out);
+    end(u, j, slot_of(j), g);
     offload(u, j, g);
     std::swap(dx_in, dx_out);
   }
@@ -835,17 +1140,21 @@ void Model::step_streamed(bool serialize) {
     const int g = grad_slot();
     begin(u);
     const mt_block_desc& b = blocks[0];
-    embed_bwd<T>(dx_in, d_order, d_seg, (T*)gslot[g] + b.tensors[0].offset, V, d, sc);
-    MT_HIP(hipEventRecord(ev_c_e[u], sc));
+    if (!dry) embed_bwd<T>(dx_in, d_order, d_seg, (T*)gslot[g] + b.tensors[0].offset, V, d, sc);
+    end(u, 0, -1, g);
     offload(u, 0, g);
     flush(-1);
   }
   // The step's device timeline ends once the last offload has landed.
-  if (hipq)
-    MT_HIP(hipStreamWaitEvent(sc, ev_o_e[last_out], 0));
-  else
-    xq_out->wait(last_out);
-  MT_HIP(hipEventRecord(ev_end, sc));
+  if (hipq) {
+    if (!dry) MT_HIP(hipStreamWaitEvent(sc, ev_o_e[last_out], 0));
+    tr_add(MT_LANE_COMPUTE, MT_OP_END, -1, -1, -1, -1, {op_last_comp, op_last_out}, {});
+  } else {
+    if (!dry) xq_out->wait(last_out);
+    tr_fence(op_last_out);
+    tr_add(MT_LANE_COMPUTE, MT_OP_END, -1, -1, -1, -1, {op_last_comp}, {});
+  }
+  if (!dry) MT_HIP(hipEventRecord(ev_end, sc));
 }
 
 // Resident schedule: every block's weights are copied once into device
@@ -913,6 +1222,7 @@ int Model::train_step(const int32_t* tokens) {
 // worker accumulates or applies (last micro-batch) each block's gradients as
 // they land.  With one micro-batch this is the whole step.
 void Model::run_pass(const int32_t* tokens, int64_t t, double* adam_total, double* adam_tail) {
+  step_t = t;
   // tokens and the stable token-sorted order for the embedding backward
   std::vector<int32_t> count(V + 1, 0);
   for (int m = 0; m < M; ++m) count[tokens[m] + 1]++;
@@ -937,16 +1247,7 @@ void Model::run_pass(const int32_t* tokens, int64_t t, double* adam_total, doubl
   for (auto& s : bstats) s = mt_block_stats{};
   std::atomic<bool> device_done{false};
   const bool streamed = cfg.mode != MT_RESIDENT;
-  // Offloads yield the link to prefetches when a layer's backward is
-  // compute-bound against the link (its flops per transferred weight and
-  // gradient byte well above ~1 PFLOP/s over ~50 GB/s): the transfers are
-  // hidden either way and each then runs at the full one-way rate.  When the
-  // link is the bottleneck, both directions share it.
-  {
-    const double layer_bytes = 2.0 * (double)blocks[1].w_bytes;
-    const double bwd_flops = 3.0 * (2.0 * M * (4.0 * d * d + 3.0 * d * F)) + 3.5 * attn_fwd_flops();
-    yield_link = !(cfg.flags & MT_FLAG_DUPLEX_LINK) && bwd_flops / layer_bytes > 30000.0;
-  }
+  yield_link = link_yields();
   const bool queues = streamed && !hipq;
   if (queues && !dma) {
     dma.reset(new DmaEngines(gslot[0], host));
@@ -1180,6 +1481,40 @@ void destroy_model(Model* m) {
   delete m;
 }
 
+std::vector<mt_sched_op> schedule_for(const mt_config& cfg) {
+  std::string why;
+  if (validate_config(cfg, &why) != MT_OK) throw ApiError{MT_E_INVALID, why};
+  if (cfg.mode == MT_RESIDENT) throw ApiError{MT_E_INVALID, "the resident schedule moves no weights"};
+  Model m;
+  m.init_dims(cfg);
+  m.hipq = !(cfg.flags & MT_FLAG_SDMA_QUEUES);
+  m.yield_link = m.link_yields();
+  for (auto* v : {&m.ev_c_s, &m.ev_c_e, &m.ev_slot_free, &m.ev_x_s, &m.ev_x_e, &m.ev_o_s, &m.ev_o_e})
+    v->assign(m.n_uses, nullptr);
+  std::vector<Model::TraceOp> tr;
+  m.trace = &tr;
+  const bool ser = cfg.mode == MT_SERIALIZED;
+  bf16_store(cfg) ? m.step_streamed<uint16_t>(ser) : m.step_streamed<float>(ser);
+  std::vector<mt_sched_op> out(tr.size());
+  for (size_t i = 0; i < tr.size(); ++i) {
+    const auto& t = tr[i];
+    if (t.waits.size() > MT_SCHED_MAX_WAITS || t.link.size() > 2) throw ApiError{MT_E_STATE, "schedule operation waits"};
+    mt_sched_op& o = out[i];
+    o = mt_sched_op{};
+    o.lane = t.lane;
+    o.kind = t.kind;
+    o.use = t.use;
+    o.block = t.block;
+    o.wslot = t.wslot;
+    o.gslot = t.gslot;
+    o.n_waits = (int32_t)t.waits.size();
+    o.n_link = (int32_t)t.link.size();
+    for (size_t k = 0; k < t.waits.size(); ++k) o.waits[k] = t.waits[k];
+    for (size_t k = 0; k < t.link.size(); ++k) o.link[k] = t.link[k];
+  }
+  return out;
+}
+
 uint64_t device_bytes_for(const mt_config& cfg) {
   std::string why;
   if (validate_config(cfg, &why) != MT_OK) throw ApiError{MT_E_INVALID, why};
@@ -1249,7 +1584,9 @@ int model_debug_grad(const Model* m, int layer, void** dx) {
 
 int model_debug(const Model* m, int layer, void** ckpt, void** row_loss) {
   if (layer < 0 || layer > m->L) throw ApiError{MT_E_INVALID, "layer index"};
-  if (ckpt) *ckpt = m->ckpt + (uint64_t)layer * m->M * m->d;
+  if (ckpt)
+    *ckpt = m->ckpt_lp ? (void*)(m->ckpt16 + (uint64_t)layer * m->M * m->d)
+                       : (void*)(m->ckpt + (uint64_t)layer * m->M * m->d);
   if (row_loss) {
     if (bf16_store(m->cfg)) {
       HeadWs<uint16_t> h = const_cast<Model*>(m)->headws<uint16_t>();

@@ -56,14 +56,24 @@ size_t rmsnorm_dg_partial_elems(int M, int d);
 template <typename T>
 void rmsnorm_bwd(const float* dy, const float* x, const T* g, const float* rstd, const float* resid, float* dx,
                  float* partial, T* dg, int M, int d, hipStream_t s, T* dx_lp = nullptr);
+// With dg null, rmsnorm_bwd writes only the per-block partial sums (blocks
+// of rmsnorm_rows_per_block() consecutive rows); rmsnorm_dg_reduce adds
+// `blocks` of them in block order.  Rows processed in several calls, each
+// starting at a multiple of the block rows with its partials at the matching
+// block offset, reduce to the same dg as one call over all rows.
+template <typename T>
+void rmsnorm_dg_reduce(const float* partial, T* dg, int blocks, int d, hipStream_t s);
+int rmsnorm_rows_per_block();
 // Token-major transposed buffers [C x M] use a padded row stride
 // (token_ld(M) >= M): a row stride that is a large power of two puts a
 // tile's rows on the same memory channels.
 int64_t token_ld(int64_t M);
 // Rotate q and k of qkv [M x 3d] in place (pairs (i, i+hd/2), angle
-// t*theta^(-2i/hd), t = m mod T).
+// t*theta^(-2i/hd), t = (row0 + m) mod T: row0 is the batch row of qkv's
+// first row when qkv points into a larger buffer).
 template <typename T>
-void rope_qkv_fwd(T* qkv, const float* cosb, const float* sinb, int M, int T_, int d, int hd, hipStream_t s);
+void rope_qkv_fwd(T* qkv, const float* cosb, const float* sinb, int M, int T_, int d, int hd, hipStream_t s,
+                  int64_t row0 = 0);
 // Inverse rotation of the dq, dk rows of dqkvT [3d x M] (row stride ldT), in
 // place; cosT, sinT are the rotation tables transposed, [hd/2 x T].
 template <typename T>
@@ -88,6 +98,8 @@ void transpose(const T* in, int64_t ld_in, T* out, int64_t ld_out, int R, int C,
 // out = T(in) for n floats.
 template <typename T>
 void cast(const float* in, T* out, int64_t n, hipStream_t s);
+// out = float(in) for n bf16 values (exact).
+void widen_bf16(const uint16_t* in, float* out, int64_t n, hipStream_t s);
 // out = T(in) and outT = T(in)^T (row stride ldT) for in float [R x C].
 template <typename T>
 void cast_transpose(const float* in, T* out, T* outT, int64_t ldT, int R, int C, hipStream_t s);

@@ -20,7 +20,7 @@ constexpr uint64_t kStoreAlign = MT_STORE_ALIGN;
 constexpr uint64_t kTensorAlignElems = 2048;  // 4 KiB of bf16, 8 KiB of f32
 constexpr uint64_t kHeaderBytes = 4096;
 constexpr uint64_t kStoreMagic = 0x3145524f5453544dull;  // "MTSTORE1"
-constexpr int32_t kStoreVersion = 1;
+constexpr int32_t kStoreVersion = 2;
 
 struct StoreHeader {
   uint64_t magic;

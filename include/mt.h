@@ -100,6 +100,15 @@ typedef struct mt_config {
                             d 5120, F 13824, 32768 tokens).  0: recompute every layer (the default:
                             layer-boundary checkpoints only).  Ignored by MT_RESIDENT, which keeps
                             every layer's */
+  int32_t token_chunk;   /* tokens per pass of a layer's per-token work (the two norms, the q/k/v, output,
+                            gate/up and down projections, SwiGLU): a layer runs its attention over all
+                            tokens and the rest pass by pass, and its weight gradients are summed over
+                            the passes in fp32 (gain gradients reduce in the same order as in one pass).
+                            Passes are evened out to multiples of 64 tokens, each at least 192.  0:
+                            automatic, one pass unless a weight gradient contracting over all tokens
+                            would exceed the 2^31-byte operand addressing of the matrix kernels, then
+                            passes of at most 32768 tokens.  Several passes need a bf16 store and a
+                            streamed, serialized or single-slot schedule without retained layers */
 } mt_config;
 
 #define MT_FLAG_TIME_KERNELS 1  /* bracket every GEMM and attention launch with events */
@@ -112,6 +121,17 @@ typedef struct mt_config {
                                    l = 0..n_layers (fp32, batch*seq_len x d_model each), in the device
                                    arena until the next step, for inspection (mt_debug_grad); adds
                                    (n_layers+1)*batch*seq_len*d_model*4 bytes to mt_device_bytes */
+#define MT_FLAG_CKPT_BF16 32    /* keep the layer-boundary checkpoints x^0..x^n_layers rounded to bf16 (nearest
+                                   even) instead of fp32, halving their device memory (long contexts): the
+                                   forward still carries the fp32 residual stream from layer to layer, and
+                                   the backward recomputes each layer from its rounded checkpoint.  Needs a
+                                   bf16 store and a streamed, serialized or single-slot schedule without
+                                   retained layers; mt_debug_buffers then returns bf16 checkpoints */
+#define MT_FLAG_DELAYS 64       /* a test aid for ordering bugs: seeded host-side delays of 0 to 2 ms (about
+                                   half of them 0), drawn per step, micro-batch, lane and use, before each
+                                   prefetch copy, each compute use and each offload copy (a sleeping host
+                                   function on the stream, or a sleep in the SDMA queue's worker) and before
+                                   each host Adam update.  The results are bit for bit those without */
 #define MT_FLAG_SDMA_QUEUES 16  /* run the weight prefetches and gradient offloads on two of the GPU's
                                    SDMA engines (one per direction), each fed in order by a host worker
                                    thread that waits for the events the copy depends on, instead of
@@ -288,8 +308,9 @@ int mt_get_loss(const mt_model* model, float* out);
  * about ([Methodik]: the ping-pong keeps the GPU busy). */
 int mt_get_stats(const mt_model* model, mt_stats* out);
 int mt_get_block_stats(const mt_model* model, int block, mt_block_stats* out);
-/* Device addresses inside the arena for inspection by tests: the fp32
- * layer-boundary checkpoint x^l [batch*seq_len x d_model] (l = 0..n_layers)
+/* Device addresses inside the arena for inspection by tests: the fp32 (bf16
+ * with MT_FLAG_CKPT_BF16) layer-boundary checkpoint x^l [batch*seq_len x
+ * d_model] (l = 0..n_layers)
  * and the fp32 per-position loss [batch*seq_len] (0 on the last position of
  * each sequence).  Either output may be null.  Valid until the next step. */
 int mt_debug_buffers(const mt_model* model, int layer, void** ckpt, void** row_loss);
@@ -330,6 +351,46 @@ int mt_host_adam_master(uint16_t* w, float* p, const uint16_t* g, float* m, floa
  * missing or equal streams), MT_E_HIP. */
 int mt_link_probe(void* dev_a, void* dev_b, void* host_a, void* host_b, size_t bytes, int32_t reps, int32_t flags,
                   void* const streams[2], double out_gbs[3]);
+
+/* ------------------------------------------------------------ schedule -- */
+/* The operations one streamed step issues, in issue order, as data: the
+ * double-buffered pipeline of [Methodik] (weights of the next block stream in
+ * while the current one computes; gradients stream out behind it) for the
+ * schedule `cfg` selects.  Nothing is allocated on or sent to the device; the
+ * result depends only on `cfg` and lets a checker prove from the waits alone
+ * that no operation can read a weight slot, gradient slot or host region
+ * before the write it needs, or while another write to it is in flight.
+ *
+ * Lanes: operations of one lane 0..2 run in issue order (a HIP stream or an
+ * SDMA queue's worker); MT_LANE_HOST operations (per-block Adam updates) are
+ * not ordered among themselves.  An operation starts after every operation in
+ * `waits` has finished; `link` lists orderings that only share out the host
+ * link (an offload held back behind a prefetch) and carry no data.  The host
+ * thread's own waits (serialized schedule, SDMA queues) appear as waits of
+ * every later operation. */
+#define MT_LANE_PREFETCH 0
+#define MT_LANE_COMPUTE 1
+#define MT_LANE_OFFLOAD 2
+#define MT_LANE_HOST 3
+#define MT_OP_FETCH 0    /* host W of `block` -> weight slot `wslot` */
+#define MT_OP_POISON 1   /* NaN fill of weight slot `wslot` (MT_FLAG_POISON) */
+#define MT_OP_COMPUTE 2  /* use `use` of `block`: reads weight slot `wslot` (-1: none), writes gradient
+                            slot `gslot` (-1: none) */
+#define MT_OP_OFFLOAD 3  /* gradient slot `gslot` -> host G of `block` */
+#define MT_OP_ADAM 4     /* host Adam of `block`: reads its G, writes its W, m, v */
+#define MT_OP_END 5      /* the step's device timeline ends (its completion event) */
+#define MT_SCHED_MAX_WAITS 8
+typedef struct mt_sched_op {
+  int32_t lane, kind, use, block, wslot, gslot;
+  int32_t n_waits, n_link;
+  int32_t waits[MT_SCHED_MAX_WAITS];  /* indices of earlier operations */
+  int32_t link[2];
+} mt_sched_op;
+/* Writes up to `capacity` operations to `ops` (may be null with capacity 0)
+ * and returns how many the step has (call again with that capacity), or a
+ * negative error: MT_E_INVALID (bad config, or MT_RESIDENT, whose step moves
+ * no weights). */
+int mt_schedule(const mt_config* cfg, mt_sched_op* ops, int32_t capacity);
 
 const char* mt_last_error(void);
 const char* mt_version(void);

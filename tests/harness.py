@@ -9,9 +9,9 @@ import host_memory_layer_amd as mt
 
 
 def make_store(shape, mode="streamed", flags=0, host_threads=0, micro_batches=1, head_chunk_tokens=0,
-               retain_layers=0):
+               retain_layers=0, token_chunk=0):
     cfg = mt.make_config(shape, mode=mode, flags=flags, host_threads=host_threads, micro_batches=micro_batches,
-                         head_chunk_tokens=head_chunk_tokens, retain_layers=retain_layers)
+                         head_chunk_tokens=head_chunk_tokens, retain_layers=retain_layers, token_chunk=token_chunk)
     store = mt.HostStore(cfg)
     mt.init_store_weights(store, datagen.store_filler(shape))
     return cfg, store

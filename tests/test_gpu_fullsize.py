@@ -30,8 +30,10 @@ embedding-gradient rows for tokens with no labelled occurrence.
   minutes of oracle time).
 * The streamed, serialized, resident and single-slot schedules agree bit for
   bit at the 14B and 120B per-layer shapes with 2 layers.
-* Long context: the 7B width with 2 layers over one 131072-token sequence,
-  whose output head runs in passes: sampled-row checks.
+* Long context: the 7B width with 2 layers over one 262144-token sequence,
+  with the layers' per-token work and the output head in passes: a prefix
+  of each layer, late rows of layer 0 against the oracle's single-row
+  attention over every earlier key, and the head at every pass boundary.
 """
 import gc
 import os
@@ -42,7 +44,7 @@ import pytest
 
 import datagen
 import host_memory_layer_amd as mt
-from oracle import Oracle, adam_update
+from oracle import Oracle, adam_update, attention_rows, rmsnorm_fwd, rope_apply, rope_tables, silu
 from tests.harness import (GRAD_COS, GRAD_MAXREL, LOSS_RTOL, W_RTOL, as_f32, cosine, frob_rel, make_store,
                            maxnorm_rel)
 
@@ -483,9 +485,50 @@ def test_fullsize_per_block_120b_depth_that_fits():
 
 
 # ------------------------------------------------------- long context --
+def check_layer_rows(r, l, rows, ex):
+    """Oracle layer l at sampled query rows of one long sequence, from the
+    GPU's x^l: each sampled query's attention over every earlier key (the
+    oracle's single-row evaluator), then its output projection and FFN;
+    compared on the layer's increment."""
+    s = r.shape
+    T, d, H, hd = s.seq_len, s.d_model, s.n_heads, s.head_dim
+    x = r.model.checkpoint(l).cpu().numpy()
+    xr = x[rows].copy()
+    x_out = r.rows(l + 1, rows)
+    P = layer_params(s, l, ex)
+    h = rmsnorm_fwd(x, P[f"{l}.attn_norm"], s.rms_eps)[0]
+    del x
+    cos, sin = rope_tables(T, hd, s.rope_theta, np.float32)
+    heads = lambda a: a.reshape(a.shape[0], H, hd).transpose(1, 0, 2)
+    k = rope_apply(heads(h @ P[f"{l}.wk"].T), cos, sin)
+    v = heads(h @ P[f"{l}.wv"].T)
+    q_rows = rope_apply(heads(h[rows] @ P[f"{l}.wq"].T), cos[rows], sin[rows])
+    del h
+    o = np.empty((len(rows), H, hd), np.float32)
+    zero = np.zeros((T, hd), np.float32)
+    for hh in range(H):
+        q = np.zeros((T, hd), np.float32)
+        q[rows] = q_rows[hh]
+        o[:, hh], _ = attention_rows(q, k[hh], v[hh], zero, rows)
+    del k, v
+    x1 = xr + o.reshape(len(rows), d) @ P[f"{l}.wo"].T
+    h2 = rmsnorm_fwd(x1, P[f"{l}.ffn_norm"], s.rms_eps)[0]
+    ref = x1 + (silu(h2 @ P[f"{l}.wg"].T) * (h2 @ P[f"{l}.wu"].T)) @ P[f"{l}.wd"].T
+    d_gpu, d_ref = x_out - xr, ref - xr
+    c, e = cosine(d_gpu, d_ref), maxnorm_rel(d_gpu, d_ref)
+    print(f"  layer {l} rows {list(rows)}: increment cos {c:.6f} maxrel {e:.2e}", flush=True)
+    assert c >= GRAD_COS and e <= GRAD_MAXREL, (l, c, e)
+
+
 def test_long_context_7b_width_two_layers():
+    """The 7B width with 2 layers over one sequence of 262144 tokens: the
+    layers run their per-token work in passes (taken automatically at this
+    length) and the head in passes of 22272 tokens.  Layer 0 on a 4096-token
+    prefix and at late rows over all earlier keys, layer 1 on a 512-token
+    prefix; per-position losses on both sides of every head-pass boundary;
+    the host Adam relation; the embedding rows."""
     need_gpu()
-    shape = P7.replace(n_layers=2, batch=1, seq_len=131072)
+    shape = P7.replace(n_layers=2, batch=1, seq_len=262144)
     T = shape.seq_len
     print(f"{shape.name} long context: 2 layers, d {shape.d_model}, 1x{T} tokens", flush=True)
     r = Run(shape)
@@ -493,6 +536,7 @@ def test_long_context_7b_width_two_layers():
         with pool() as ex:
             check_layer_prefix(r, 0, 0, 4096, ex)
             check_layer_prefix(r, 1, 0, 512, ex)
+            check_layer_rows(r, 0, np.array([70001, 131071, 131072, 200003, T - 2, T - 1]), ex)
             hc = 22272  # head pass: the largest multiple of 256 tokens within 4 GiB of logits and gradients
             assert hc * shape.vocab * 6 <= 4 << 30 < (hc + 256) * shape.vocab * 6
             edges = [p * hc + e for p in range(1, T // hc + 1) for e in (-1, 0) if p * hc + e < T]

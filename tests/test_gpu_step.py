@@ -33,9 +33,9 @@ def need_gpu():
 
 
 def run_step(shape, mode="streamed", flags=0, steps=1, micro_batches=1, tok=None, head_chunk_tokens=0,
-             retain_layers=0):
+             retain_layers=0, token_chunk=0):
     cfg, store = make_store(shape, mode, flags=flags, micro_batches=micro_batches, head_chunk_tokens=head_chunk_tokens,
-                            retain_layers=retain_layers)
+                            retain_layers=retain_layers, token_chunk=token_chunk)
     model = mt.Model(cfg, store, "cuda:0")
     tok = datagen.tokens(shape) if tok is None else tok
     losses = [model.step(tok) for _ in range(steps)]
@@ -126,6 +126,84 @@ def test_kept_layer_gradients_follow_the_oracle_chain(shape):
         assert np.array_equal(gE, dE)
     else:
         assert np.array_equal(gE, datagen.f32_to_bf16_bits(dE))
+
+
+def _bitwise_same(a, b, what):
+    assert a["loss"] == b["loss"], what
+    for key in ("g", "w", "m", "v"):
+        for k in a[key]:
+            assert np.array_equal(a[key][k], b[key][k]), (what, key, k)
+
+
+@pytest.mark.parametrize("shape,chunk", [(SMALL_T256, 256), (SMALL_T256.replace(name="small-bf16-3x256", batch=3), 256),
+                                         (SMALL_T256.replace(name="small-bf16-5x256", batch=5), 448)],
+                         ids=["2-passes", "3-passes", "3-ragged-passes"])
+def test_token_passes(shape, chunk):
+    """A layer's per-token work in passes of `chunk` tokens.  Everything
+    computed per token does not depend on the passes: the loss, the gain
+    gradients (their partial sums reduce in the single pass's order), the
+    head and embedding gradients are bit for bit those of a single pass; the
+    weight gradients are summed over the passes in fp32 and differ by
+    rounding.  Parity with the oracle; the streamed, serialized and
+    single-slot schedules (with poison, with SDMA queues) agree bit for bit."""
+    need_gpu()
+    print(f"token passes {shape.name} chunk {chunk}", flush=True)
+    one = run_step(shape)
+    r = run_step(shape, token_chunk=chunk)
+    assert r["loss"] == one["loss"]
+    for k in r["g"]:
+        if k.endswith("norm") or k in ("E", "wh"):
+            assert np.array_equal(r["g"][k], one["g"][k]), k
+        else:
+            assert cosine(r["g"][k], one["g"][k]) > 0.99999, k
+    o_loss, o_g, o_w = oracle_step(shape)
+    assert_parity(r["loss"], r["g"], r["w"], o_loss, o_g, o_w)
+    for mode, flags in (("serialized", 0), ("single_slot", mt.MT_FLAG_POISON), ("streamed", mt.MT_FLAG_SDMA_QUEUES)):
+        _bitwise_same(run_step(shape, mode, flags, token_chunk=chunk), r, (mode, flags))
+
+
+@pytest.mark.parametrize("shape,chunk", [(SMALL_BF16, 0), (SMALL_T256, 256)], ids=["one-pass", "2-passes"])
+def test_bf16_checkpoints(shape, chunk):
+    """MT_FLAG_CKPT_BF16: the forward still carries the fp32 residual stream
+    (the loss is bit for bit the fp32 checkpoints' one); the backward
+    recomputes each layer from its rounded checkpoint.  Parity with the
+    oracle; schedules bit for bit."""
+    need_gpu()
+    print(f"bf16 checkpoints {shape.name} chunk {chunk}", flush=True)
+    ref = run_step(shape, token_chunk=chunk)
+    r = run_step(shape, flags=mt.MT_FLAG_CKPT_BF16, token_chunk=chunk)
+    assert r["loss"] == ref["loss"]
+    o_loss, o_g, o_w = oracle_step(shape)
+    lrel, rows = assert_parity(r["loss"], r["g"], r["w"], o_loss, o_g, o_w)
+    print(f"  min cos {min(x[1] for x in rows):.6f} max grad rel {max(x[2] for x in rows):.2e}", flush=True)
+    ck = mt.MT_FLAG_CKPT_BF16
+    for mode, flags in (("serialized", ck), ("single_slot", ck | mt.MT_FLAG_POISON), ("streamed", ck | mt.MT_FLAG_SDMA_QUEUES)):
+        _bitwise_same(run_step(shape, mode, flags, token_chunk=chunk), r, (mode, flags))
+
+
+SMALL_L4 = SMALL_BF16.replace(name="small-bf16-L4", n_layers=4)
+# a layer's backward outlasts moving its weights and gradients: offloads are
+# held behind the next prefetch
+YIELDING = SMALL_BF16.replace(name="small-bf16-16k", n_layers=3, batch=1, seq_len=16384)
+
+
+@pytest.mark.parametrize("shape,mode,flags", [
+    (datagen.PRESETS["tiny"], "streamed", 0), (SMALL_L4, "streamed", 0), (SMALL_L4, "serialized", 0),
+    (SMALL_L4, "single_slot", mt.MT_FLAG_POISON), (SMALL_L4, "streamed", mt.MT_FLAG_POISON | mt.MT_FLAG_SDMA_QUEUES),
+    (YIELDING, "streamed", 0), (YIELDING, "streamed", mt.MT_FLAG_SDMA_QUEUES)],
+    ids=["tiny", "streamed", "serialized", "single-slot-poison", "sdma-poison", "yield", "yield-sdma"])
+def test_injected_delays_change_nothing(shape, mode, flags):
+    """MT_FLAG_DELAYS holds back prefetches, compute uses, offloads and Adam
+    updates by seeded host-side delays of up to 2 ms: over two steps (the
+    second fetches what the first step's Adam wrote) every result is bit for
+    bit that of the undelayed run."""
+    need_gpu()
+    print(f"delays {shape.name} {mode} flags {flags}", flush=True)
+    ref = run_step(shape, mode, flags, steps=2)
+    r = run_step(shape, mode, flags | mt.MT_FLAG_DELAYS, steps=2)
+    assert r["losses"] == ref["losses"]
+    _bitwise_same(r, ref, (mode, flags))
+    assert r["stats"]["step_ms"] > ref["stats"]["step_ms"]
 
 
 def test_repeated_step_is_deterministic_and_t_advances():

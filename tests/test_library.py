@@ -34,10 +34,11 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_sizes_match_header():
     # layout of the C structs, mirrored by ctypes
-    assert ctypes.sizeof(mt.MtConfig) == 9 * 4 + 4 + 6 * 8 + 6 * 4
+    assert ctypes.sizeof(mt.MtConfig) == 9 * 4 + 4 + 6 * 8 + 7 * 4 + 4
     assert ctypes.sizeof(mt.MtTensorDesc) == 16
     assert ctypes.sizeof(mt.MtBlockDesc) == 16 + 8 * 8 + 8 * 16 + 2 * 8
     assert ctypes.sizeof(mt.MtStats) == 15 * 8 + 2 * 8 + 8 + 2 * 4 + 8
+    assert ctypes.sizeof(mt.MtSchedOp) == (8 + mt.MT_SCHED_MAX_WAITS + 2) * 4
 
 
 @pytest.mark.parametrize("name,dtype", [(n, None) for n in datagen.PRESETS] +
@@ -142,6 +143,50 @@ def test_config_validation():
     for k in (-1, 5000):
         with pytest.raises(mt.MtError):
             mt.host_store_bytes(mt.make_config(shape, micro_batches=k))
+
+
+SMALL_T256 = datagen.ModelShape("small-bf16-T256", 2, 256, 2, 128, 512, 1000, 2, 256)
+
+
+def test_token_passes_and_bf16_checkpoints_validation():
+    """Token passes: evened out to multiples of 64, each at least 192 tokens;
+    only with a bf16 store and without the resident schedule or retained
+    layers.  bf16 checkpoints: the same schedule conditions."""
+    with pytest.raises(mt.MtError, match="192 tokens"):
+        mt.device_bytes(mt.make_config(SMALL_T256, token_chunk=192))  # passes of 192, 192, 128
+    with pytest.raises(mt.MtError):
+        mt.host_store_bytes(mt.make_config(SMALL_T256, token_chunk=-1))
+    with pytest.raises(mt.MtError, match="bf16 store"):
+        mt.device_bytes(mt.make_config(datagen.PRESETS["tiny"], token_chunk=64))
+    for kw in (dict(mode="resident"), dict(retain_layers=1)):
+        with pytest.raises(mt.MtError, match="token passes"):
+            mt.device_bytes(mt.make_config(SMALL_T256, token_chunk=256, **kw))
+        with pytest.raises(mt.MtError, match="bf16 checkpoints"):
+            mt.device_bytes(mt.make_config(SMALL_T256, flags=mt.MT_FLAG_CKPT_BF16, **kw))
+    with pytest.raises(mt.MtError, match="bf16 checkpoints"):
+        mt.device_bytes(mt.make_config(datagen.PRESETS["tiny"], flags=mt.MT_FLAG_CKPT_BF16))
+    # a chunk at least as long as the step, or 0 on a shape that needs no
+    # passes, is one pass: the same arena as no chunk at all
+    one = mt.device_bytes(mt.make_config(SMALL_T256))
+    assert mt.device_bytes(mt.make_config(SMALL_T256, token_chunk=512)) == one
+    assert mt.device_bytes(mt.make_config(SMALL_T256, token_chunk=320)) != one  # two passes of 256 (+ fp32 sums)
+
+
+def test_long_context_arena_with_passes_and_bf16_checkpoints():
+    """The 7B width over one sequence: token passes are taken automatically
+    once the weight-gradient operands outgrow 32-bit addressing, and keep
+    the per-layer workspace at about 76 GB at 512K tokens; bf16 checkpoints
+    halve the rest, so 512K fits the device.  The 14B-shape step (one pass)
+    is unchanged."""
+    GB = 1e9
+    s7 = datagen.PRESETS["7b"]
+    assert mt.device_bytes(mt.make_config(datagen.PRESETS["14b"])) == 54704961024
+    for T, fp32_gb, bf16_gb in ((262144, 186.9, 124.6), (524288, 359.2, 234.6)):
+        s = s7.replace(batch=1, seq_len=T)
+        a = mt.device_bytes(mt.make_config(s)) / GB
+        b = mt.device_bytes(mt.make_config(s, flags=mt.MT_FLAG_CKPT_BF16)) / GB
+        assert abs(a - fp32_gb) < 0.1 and abs(b - bf16_gb) < 0.1, (T, a, b)
+    assert mt.device_bytes(mt.make_config(s7.replace(batch=1, seq_len=524288), flags=mt.MT_FLAG_CKPT_BF16)) < 280 * GB
 
 
 def test_device_bytes_fit_one_gpu():
