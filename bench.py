@@ -268,6 +268,8 @@ def main():
                     help="tokens per pass of a layer's per-token work (0: automatic, passes only where needed)")
     ap.add_argument("--ckpt-bf16", action="store_true",
                     help="keep the layer-boundary checkpoints in bf16 (long contexts)")
+    ap.add_argument("--progress", action="store_true",
+                    help="print a line to stderr as each block use of a step finishes (steps that take minutes)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run a plain 1 GiB device copy kernel first (the reference for HBM byte counters)")
     args = ap.parse_args()
@@ -296,6 +298,8 @@ def main():
         flags |= mt.MT_FLAG_SDMA_QUEUES
     if args.ckpt_bf16:
         flags |= mt.MT_FLAG_CKPT_BF16
+    if args.progress:
+        flags |= mt.MT_FLAG_PROGRESS
     K = max(1, args.micro_batches)
     cfg = mt.make_config(shape, mode=args.mode, flags=flags, micro_batches=K, token_chunk=args.token_chunk)
     R = 0

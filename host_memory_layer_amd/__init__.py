@@ -28,7 +28,7 @@ MODES = {"streamed": MT_STREAMED, "serialized": MT_SERIALIZED, "resident": MT_RE
          "single_slot": MT_SINGLE_SLOT}
 MT_BLOCK_EMBED, MT_BLOCK_LAYER, MT_BLOCK_HEAD = 0, 1, 2
 MT_FLAG_TIME_KERNELS, MT_FLAG_POISON, MT_FLAG_DUPLEX_LINK, MT_FLAG_KEEP_DX, MT_FLAG_SDMA_QUEUES = 1, 2, 4, 8, 16
-MT_FLAG_CKPT_BF16, MT_FLAG_DELAYS = 32, 64
+MT_FLAG_CKPT_BF16, MT_FLAG_DELAYS, MT_FLAG_PROGRESS = 32, 64, 128
 MT_LANE_PREFETCH, MT_LANE_COMPUTE, MT_LANE_OFFLOAD, MT_LANE_HOST = 0, 1, 2, 3
 MT_OP_FETCH, MT_OP_POISON, MT_OP_COMPUTE, MT_OP_OFFLOAD, MT_OP_ADAM, MT_OP_END = range(6)
 MT_SCHED_MAX_WAITS = 8

@@ -778,6 +778,13 @@ struct Model {
     return (z & 1) ? 0 : (int)((z >> 1) % 2000);
   }
   static void sleep_host(void* us) { std::this_thread::sleep_for(std::chrono::microseconds((intptr_t)us)); }
+  // MT_FLAG_PROGRESS: packed (use, block, uses per pass) of a finished use
+  static void print_progress(void* packed) {
+    const uint64_t v = (uint64_t)(uintptr_t)packed;
+    fprintf(stderr, "mt: use %d of %d (block %d) done\n", (int)(v & 0xFFFFF) + 1, (int)((v >> 40) & 0xFFFFF),
+            (int)((v >> 20) & 0xFFFFF));
+    fflush(stderr);
+  }
   // the stream's later work waits for a host function that sleeps
   void stream_delay(hipStream_t s, int lane, int use) {
     const int us = delay_us(lane, use);
@@ -1021,6 +1028,9 @@ void Model::step_streamed(bool serialize) {
   // gradient slot gs (-1: none)
   auto end = [&](int u, int j, int ws, int gs) {
     if (!dry) MT_HIP(hipEventRecord(ev_c_e[u], sc));
+    if (!dry && (cfg.flags & MT_FLAG_PROGRESS))
+      MT_HIP(hipLaunchHostFunc(sc, print_progress,
+                               (void*)(uintptr_t)((uint64_t)u | (uint64_t)j << 20 | (uint64_t)n_uses << 40)));
     comp_waits.push_back(op_last_comp);
     op_comp[u] = tr_add(MT_LANE_COMPUTE, MT_OP_COMPUTE, u, j, ws, gs, comp_waits, {});
     op_last_comp = op_comp[u];

@@ -32,7 +32,7 @@ int validate_config(const mt_config& c, std::string* why) {
   if (c.retain_layers < 0 || c.retain_layers > c.n_layers) return bad("retain_layers must be in [0, n_layers]");
   if (c.token_chunk < 0) return bad("token_chunk must be >= 0");
   if (c.flags & ~(MT_FLAG_TIME_KERNELS | MT_FLAG_POISON | MT_FLAG_DUPLEX_LINK | MT_FLAG_KEEP_DX | MT_FLAG_SDMA_QUEUES |
-                  MT_FLAG_CKPT_BF16 | MT_FLAG_DELAYS))
+                  MT_FLAG_CKPT_BF16 | MT_FLAG_DELAYS | MT_FLAG_PROGRESS))
     return bad("unknown flag bits");
   if ((int64_t)micro_count(c) * c.batch * c.seq_len > ((int64_t)1 << 31) - 1) return bad("too many tokens per step");
   if (!(c.rms_eps > 0) || !(c.rope_theta > 1) || !(c.lr >= 0) || !(c.beta1 >= 0 && c.beta1 < 1) ||

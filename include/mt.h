@@ -132,6 +132,9 @@ typedef struct mt_config {
                                    prefetch copy, each compute use and each offload copy (a sleeping host
                                    function on the stream, or a sleep in the SDMA queue's worker) and before
                                    each host Adam update.  The results are bit for bit those without */
+#define MT_FLAG_PROGRESS 128    /* print one line to stderr as each block use of a streamed step finishes
+                                   on the device (a host function on the compute stream): progress for
+                                   steps that run for minutes (very long contexts) */
 #define MT_FLAG_SDMA_QUEUES 16  /* run the weight prefetches and gradient offloads on two of the GPU's
                                    SDMA engines (one per direction), each fed in order by a host worker
                                    thread that waits for the events the copy depends on, instead of
