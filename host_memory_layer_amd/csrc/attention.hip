@@ -181,9 +181,12 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
   for (int t = 0; t < 4; ++t) acc_o[t] = zero16();
   const int tq = q0 + (lane & 31);
 
-  issue(0, 0);
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
+  // One key block on LDS stage BUF.  The loop below runs the blocks in
+  // pairs so that the stage is a constant: every LDS address is then a
+  // loop-invariant register plus an immediate offset, with no per-block
+  // address arithmetic on the vector ALU.
+  auto key_block = [&](int kb, auto stage) {
+    constexpr int buf = decltype(stage)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (kb + 1 < nkb) issue(kb + 1, buf ^ 1);
@@ -251,6 +254,11 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
         }
       }
     }
+  };
+  issue(0, 0);
+  for (int kb = 0; kb < nkb; kb += 2) {
+    key_block(kb, std::integral_constant<int, 0>{});
+    if (kb + 1 < nkb) key_block(kb + 1, std::integral_constant<int, 1>{});
   }
   __syncthreads();
 
@@ -523,9 +531,10 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq_bf16(const uint16_t* __restr
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc_dq[t] = zero16();
 
-  issue(0, 0);
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
+  // One key tile on LDS stage BUF; tiles run in pairs so that the stage is
+  // a constant (immediate LDS offsets, as in the forward).
+  auto key_tile = [&](int kb, auto stage) {
+    constexpr int buf = decltype(stage)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (kb + 1 < nkb) issue(kb + 1, buf ^ 1);
@@ -572,6 +581,11 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq_bf16(const uint16_t* __restr
         }
       }
     }
+  };
+  issue(0, 0);
+  for (int kb = 0; kb < nkb; kb += 2) {
+    key_tile(kb, std::integral_constant<int, 0>{});
+    if (kb + 1 < nkb) key_tile(kb + 1, std::integral_constant<int, 1>{});
   }
   if (!active) return;
 #pragma unroll

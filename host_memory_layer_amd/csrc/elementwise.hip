@@ -97,6 +97,17 @@ void embed_bwd(const float* dx, const int32_t* order, const int32_t* seg, T* dE,
 // -------------------------------------------------------------- RMSNorm --
 // A row of d floats lives in registers: thread t owns the 4-wide chunks
 // t, t+256, ... (VPT of them); d must be a multiple of 4.
+// ss + x^2 + y^2 + z^2 + w^2 as a fixed chain of fused multiply-adds: the
+// forward norms (plain and with the residual add) round their statistics
+// identically by construction, whatever contraction the compiler would
+// choose for a written-out sum.
+__device__ inline float sumsq4(float4 v, float ss) {
+  ss = fmaf(v.x, v.x, ss);
+  ss = fmaf(v.y, v.y, ss);
+  ss = fmaf(v.z, v.z, ss);
+  return fmaf(v.w, v.w, ss);
+}
+
 template <typename T, int VPT>
 __global__ void __launch_bounds__(256) k_rmsnorm_fwd(const float* __restrict__ x, const T* __restrict__ g,
                                                      T* __restrict__ y, float* __restrict__ rstd, int d, float eps) {
@@ -109,7 +120,45 @@ __global__ void __launch_bounds__(256) k_rmsnorm_fwd(const float* __restrict__ x
   for (int k = 0; k < VPT; ++k) {
     const int c = (threadIdx.x + 256 * k) * 4;
     v[k] = c < d ? *(const float4*)(xr + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-    ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
+    ss = sumsq4(v[k], ss);
+  }
+  ss = block_sum256(ss, red);
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+  if (threadIdx.x == 0) rstd[m] = r;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int c = (threadIdx.x + 256 * k) * 4;
+    if (c < d) {
+      const float4 gg = V4<T>::ld(g + c);
+      V4<T>::st(y + m * d + c, make_float4(v[k].x * r * gg.x, v[k].y * r * gg.y, v[k].z * r * gg.z, v[k].w * r * gg.w));
+    }
+  }
+}
+
+// The same norm of x = res + x (x updated in place): the residual add of a
+// projection whose GEMM wrote only its product, done where the row is read
+// anyway.  The add is the fp32 add the GEMM's residual epilogue would do.
+template <typename T, int VPT>
+__global__ void __launch_bounds__(256) k_rmsnorm_fwd_res(const float* __restrict__ res, float* __restrict__ x,
+                                                         const T* __restrict__ g, T* __restrict__ y,
+                                                         float* __restrict__ rstd, int d, float eps) {
+  __shared__ float red[4];
+  const int64_t m = blockIdx.x;
+  const float* rr = res + m * d;
+  float* xr = x + m * d;
+  float4 v[VPT];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int c = (threadIdx.x + 256 * k) * 4;
+    if (c < d) {
+      const float4 a = *(const float4*)(rr + c), p = *(const float4*)(xr + c);
+      v[k] = make_float4(a.x + p.x, a.y + p.y, a.z + p.z, a.w + p.w);
+      *(float4*)(xr + c) = v[k];
+    } else {
+      v[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    ss = sumsq4(v[k], ss);
   }
   ss = block_sum256(ss, red);
   const float r = 1.0f / sqrtf(ss / (float)d + eps);
@@ -151,6 +200,16 @@ void rmsnorm_fwd(const float* x, const T* g, T* y, float* rstd, int M, int d, fl
   if (M <= 0) return;
   if (d % 4) throw ApiError{MT_E_INVALID, "RMSNorm needs d_model % 4 == 0"};
 #define L_(V) hipLaunchKernelGGL((k_rmsnorm_fwd<T, V>), dim3(M), dim3(256), 0, s, x, g, y, rstd, d, eps)
+  MT_RMS_DISPATCH(rms_vpt(d), L_)
+#undef L_
+}
+
+template <typename T>
+void rmsnorm_fwd_res(const float* res, float* x, const T* g, T* y, float* rstd, int M, int d, float eps,
+                     hipStream_t s) {
+  if (M <= 0) return;
+  if (d % 4) throw ApiError{MT_E_INVALID, "RMSNorm needs d_model % 4 == 0"};
+#define L_(V) hipLaunchKernelGGL((k_rmsnorm_fwd_res<T, V>), dim3(M), dim3(256), 0, s, res, x, g, y, rstd, d, eps)
   MT_RMS_DISPATCH(rms_vpt(d), L_)
 #undef L_
 }
@@ -751,6 +810,7 @@ void widen_bf16(const uint16_t* in, float* out, int64_t n, hipStream_t s) {
   template void embed_fwd<T>(const int32_t*, const T*, float*, int, int, hipStream_t);                          \
   template void embed_bwd<T>(const float*, const int32_t*, const int32_t*, T*, int, int, hipStream_t);          \
   template void rmsnorm_fwd<T>(const float*, const T*, T*, float*, int, int, float, hipStream_t);               \
+  template void rmsnorm_fwd_res<T>(const float*, float*, const T*, T*, float*, int, int, float, hipStream_t);    \
   template void rmsnorm_bwd<T>(const float*, const float*, const T*, const float*, const float*, float*, float*, T*, \
                                int, int, hipStream_t, T*);                                                          \
   template void rope_qkv_fwd<T>(T*, const float*, const float*, int, int, int, int, hipStream_t, int64_t);       \

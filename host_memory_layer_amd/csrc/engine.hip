@@ -461,8 +461,9 @@ struct Model {
     if (timed) record_kernel_start(attn_fwd_flops(), 1);
     attn_fwd<T>(a.qkv, a.o, a.lse, B, Tq, H, hd, sc);
     if (timed) record_kernel_end();
-    gemm<T>(a.o, d, w.o, d, a.x1, d, x, d, M, d, d, EPI_ADD_F32);
-    rmsnorm_fwd<T>(a.x1, w.fnorm, a.h2, a.r2, M, d, eps, sc);
+    // x1 = x + o.Wo^T: the GEMM writes the product, the norm that reads it adds x
+    gemm<T>(a.o, d, w.o, d, a.x1, d, nullptr, 0, M, d, d, EPI_F32);
+    rmsnorm_fwd_res<T>(x, a.x1, w.fnorm, a.h2, a.r2, M, d, eps, sc);
     gemm<T>(a.h2, d, w.gu, d, a.gu, 2 * F, nullptr, 0, M, 2 * F, d, EPI_STORE);
     swiglu_fwd<T>(a.gu, a.y, M, F, sc);
     if (full) gemm<T>(a.y, F, w.d, F, x_out, d, a.x1, d, M, d, F, EPI_ADD_F32);
@@ -572,8 +573,8 @@ struct Model {
   // Output projection and FFN of one pass: x1, h2, gu, y (and x_out rows)
   template <typename T>
   void ffn_pass(const LayerW<T>& w, const float* x, const Acts<T>& a, int64_t r0, int rows, float* x_out) {
-    gemm<T>(a.o + r0 * d, d, w.o, d, a.x1, d, x + r0 * d, d, rows, d, d, EPI_ADD_F32);
-    rmsnorm_fwd<T>(a.x1, w.fnorm, a.h2, a.r2 + r0, rows, d, (float)cfg.rms_eps, sc);
+    gemm<T>(a.o + r0 * d, d, w.o, d, a.x1, d, nullptr, 0, rows, d, d, EPI_F32);
+    rmsnorm_fwd_res<T>(x + r0 * d, a.x1, w.fnorm, a.h2, a.r2 + r0, rows, d, (float)cfg.rms_eps, sc);
     gemm<T>(a.h2, d, w.gu, d, a.gu, 2 * F, nullptr, 0, rows, 2 * F, d, EPI_STORE);
     swiglu_fwd<T>(a.gu, a.y, rows, F, sc);
     if (x_out) gemm<T>(a.y, F, w.d, F, x_out + r0 * d, d, a.x1, d, rows, d, F, EPI_ADD_F32);

@@ -163,6 +163,16 @@ int mt_rmsnorm_fwd(int32_t dtype, const float* x, const void* g, void* y, float*
   });
 }
 
+int mt_rmsnorm_fwd_res(int32_t dtype, const float* res, float* x, const void* g, void* y, float* rstd, int32_t M,
+                       int32_t d, float eps, void* stream) {
+  return kguard([&] {
+    need(M >= 0 && d > 0 && eps > 0, "shape");
+#define F_(T) rmsnorm_fwd_res<T>(res, x, (const T*)g, (T*)y, rstd, M, d, eps, (hipStream_t)stream);
+    MT_DT_DISPATCH(dtype, F_)
+#undef F_
+  });
+}
+
 size_t mt_rmsnorm_bwd_ws_bytes(int32_t M, int32_t d) {
   if (M < 0 || d <= 0) return 0;
   return rmsnorm_dg_partial_elems(M, d) * sizeof(float);

@@ -47,6 +47,11 @@ template <typename T>
 void embed_bwd(const float* dx, const int32_t* order, const int32_t* seg, T* dE, int V, int d, hipStream_t s);
 template <typename T>
 void rmsnorm_fwd(const float* x, const T* g, T* y, float* rstd, int M, int d, float eps, hipStream_t s);
+// x = res + x in place (fp32 add), then the same norm of x: the residual
+// add of a projection whose GEMM wrote only its product.
+template <typename T>
+void rmsnorm_fwd_res(const float* res, float* x, const T* g, T* y, float* rstd, int M, int d, float eps,
+                     hipStream_t s);
 // dx = resid + r*(dy*g - xh*mean(dy*g*xh)), xh = x*r (resid may be null),
 // (and, with dx_lp, dx rounded to T beside it: the operand of the next GEMM)
 // and dg = sum_rows dy*xh written as T: per-block partial sums in `partial`

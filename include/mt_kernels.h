@@ -111,6 +111,12 @@ int mt_attention_bwd(int32_t dtype, const void* qkv, const void* o, const void* 
  * eps).  x float [M x d]; g, y dtype [d], [M x d]; rstd float [M].  d % 4 == 0. */
 int mt_rmsnorm_fwd(int32_t dtype, const float* x, const void* g, void* y, float* rstd, int32_t M, int32_t d, float eps,
                    void* stream);
+/* The same with the residual add in front: x = res + x (fp32, x updated in
+ * place), then y, rstd of that x.  The layer's attention output projection
+ * writes o.Wo^T and this adds the residual stream (the add the projection's
+ * epilogue would otherwise do).  res float [M x d]. */
+int mt_rmsnorm_fwd_res(int32_t dtype, const float* res, float* x, const void* g, void* y, float* rstd, int32_t M,
+                       int32_t d, float eps, void* stream);
 /* RMSNorm backward given dy float [M x d] and the forward's rstd:
  * dx = resid + rstd*(dy*g - xh*mean(dy*g*xh)), xh = x*rstd (resid float [M x
  * d] or null); dx_lp (dtype [M x d], or null) receives dx rounded; dg (dtype

@@ -125,6 +125,29 @@ def test_rmsnorm_fwd_bwd_against_oracle(M, d):
     assert np.all(np.abs(dg - dg_ref) <= UB * np.abs(dg_ref) + (M + 8) * 2 * U * np.abs(terms).sum(axis=0) + 1e-30)
 
 
+@pytest.mark.parametrize("M,d", [(32768, 5120), (37, 136), (1, 4096)])
+def test_rmsnorm_fwd_with_residual_is_the_add_then_the_norm(M, d):
+    """mt_rmsnorm_fwd_res: x becomes res + x, the fp32 add, bit for bit; y and
+    rstd are bit for bit those of mt_rmsnorm_fwd on that sum (whose parity
+    with the oracle the test above checks)."""
+    eps = 1e-5
+    res = _tiled_normal(M, d, 512, 7)
+    prod = _tiled_normal(M, d, 384, 8, 0.3)
+    g_dev, _ = _bf16_dev(1.0 + 0.1 * np.random.default_rng(9).standard_normal(d).astype(np.float32))
+    RES, X = torch.from_numpy(res).to(dev()), torch.from_numpy(prod).to(dev())
+    Y, Y2 = (torch.empty((M, d), dtype=torch.int16, device=dev()) for _ in range(2))
+    R, R2 = (torch.empty(M, dtype=torch.float32, device=dev()) for _ in range(2))
+    mt.check(mt.lib().mt_rmsnorm_fwd_res(mt.MT_BF16, RES.data_ptr(), X.data_ptr(), g_dev.data_ptr(), Y.data_ptr(),
+                                         R.data_ptr(), M, d, eps, None))
+    SUM = torch.from_numpy(res + prod).to(dev())  # numpy float32 add: round to nearest
+    mt.check(mt.lib().mt_rmsnorm_fwd(mt.MT_BF16, SUM.data_ptr(), g_dev.data_ptr(), Y2.data_ptr(), R2.data_ptr(), M, d,
+                                     eps, None))
+    torch.cuda.synchronize()
+    assert np.array_equal(X.cpu().numpy().view(np.uint32), (res + prod).view(np.uint32))
+    assert torch.equal(Y, Y2)
+    assert torch.equal(R.view(torch.int32), R2.view(torch.int32))
+
+
 @pytest.mark.parametrize("M,F", [(32768, 13824), (33, 520), (3, 12)])
 def test_swiglu_fwd_bwd_against_oracle(M, F):
     GU, gu_bits = _bf16_dev(_tiled_normal(M, 2 * F, 64, 5, 2.0))

@@ -32,6 +32,18 @@ def test_library_exports_every_declared_symbol():
     assert set(mt._SIGS) == names
 
 
+def test_torch_runtime_loads_before_the_library():
+    """torch's HIP runtime and the system one share a soname: the binding
+    must load torch's first, or torch finds no GPU in that process."""
+    import subprocess
+    import sys
+    code = ("import sys, host_memory_layer_amd as mt; assert 'torch' not in sys.modules; mt.lib(); "
+            "assert 'torch' in sys.modules; print('ok')")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                       text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout[-2000:]
+
+
 def test_struct_sizes_match_header():
     # layout of the C structs, mirrored by ctypes
     assert ctypes.sizeof(mt.MtConfig) == 9 * 4 + 4 + 6 * 8 + 7 * 4 + 4
