@@ -310,7 +310,9 @@ def positions_of(shape):
 # -------------------------------------------------- 1.3B end to end --
 # Tensors whose end-to-end comparison at the 1.3B shape misses a bar, with
 # the measured numbers (cos, max-norm rel, W rel); every miss is on the
-# max-norm bar (3e-2), by at most 27%.  Each layer's own arithmetic meets the
+# max-norm bar (3e-2), by at most 20%.  Which tensors graze the bar changes
+# whenever a rounding point of the step moves (the set is re-measured then;
+# the step itself is bit-reproducible).  Each layer's own arithmetic meets the
 # bars with a wide margin (the per-block test below).  End to end, the
 # roughly 16 bf16 roundings of each layer's forward and backward (operands
 # of every GEMM, probabilities, stored activations and gradients), none of
@@ -318,38 +320,34 @@ def positions_of(shape):
 # layers to about 3% relative error in every tensor (cos ~ 0.9995), which
 # grazes the max-norm bar.
 KNOWN_DRIFT = {
-    "23.ffn_norm": (0.999607, 3.80e-02, 9.99e-04),
-    "22.wq": (0.999514, 3.04e-02, 7.87e-03),
-    "21.ffn_norm": (0.999595, 3.36e-02, 9.99e-04),
-    "15.wq": (0.999509, 3.02e-02, 8.29e-03),
-    "14.ffn_norm": (0.999586, 3.56e-02, 9.99e-04),
-    "13.wq": (0.999501, 3.16e-02, 8.43e-03),
-    "12.ffn_norm": (0.999597, 3.02e-02, 9.99e-04),
-    "11.wg": (0.999565, 3.03e-02, 9.42e-03),
-    "11.ffn_norm": (0.999584, 3.08e-02, 9.99e-04),
-    "9.ffn_norm": (0.999569, 3.24e-02, 1.00e-03),
-    "9.wk": (0.999491, 3.25e-02, 8.76e-03),
-    "8.ffn_norm": (0.999596, 3.56e-02, 1.00e-03),
-    "7.ffn_norm": (0.999568, 3.30e-02, 9.99e-04),
-    "7.wq": (0.999510, 3.05e-02, 8.85e-03),
-    "6.ffn_norm": (0.999545, 3.28e-02, 1.00e-03),
-    "6.wk": (0.999516, 3.00e-02, 8.97e-03),
-    "5.wq": (0.999521, 3.01e-02, 9.04e-03),
-    "4.ffn_norm": (0.999564, 3.02e-02, 1.00e-03),
-    "4.wq": (0.999514, 3.05e-02, 9.17e-03),
-    "3.wg": (0.999551, 3.13e-02, 9.62e-03),
-    "3.wq": (0.999511, 3.18e-02, 9.34e-03),
-    "3.wk": (0.999507, 3.07e-02, 9.33e-03),
-    "1.wd": (0.999572, 3.16e-02, 9.56e-03),
-    "1.wu": (0.999568, 3.03e-02, 9.58e-03),
-    "1.wq": (0.999533, 3.20e-02, 9.51e-03),
-    "1.wk": (0.999535, 3.15e-02, 9.48e-03),
-    "1.wv": (0.999648, 3.18e-02, 9.07e-03),
-    "0.wd": (0.999585, 3.19e-02, 9.52e-03),
-    "0.wu": (0.999586, 3.04e-02, 9.52e-03),
-    "0.ffn_norm": (0.999573, 3.28e-02, 1.00e-03),
-    "0.wk": (0.999540, 3.04e-02, 9.76e-03),
-    "0.attn_norm": (0.999552, 3.59e-02, 1.00e-03),
+    "23.ffn_norm": (0.999614, 3.29e-02, 9.99e-04),
+    "22.ffn_norm": (0.999630, 3.12e-02, 9.99e-04),
+    "21.ffn_norm": (0.999577, 3.13e-02, 9.99e-04),
+    "14.ffn_norm": (0.999593, 3.23e-02, 9.99e-04),
+    "13.wq": (0.999500, 3.18e-02, 8.44e-03),
+    "12.ffn_norm": (0.999598, 3.31e-02, 9.99e-04),
+    "11.ffn_norm": (0.999563, 3.05e-02, 9.99e-04),
+    "10.ffn_norm": (0.999584, 3.12e-02, 1.00e-03),
+    "10.wk": (0.999508, 3.40e-02, 8.62e-03),
+    "9.ffn_norm": (0.999588, 3.03e-02, 1.00e-03),
+    "9.wk": (0.999492, 3.32e-02, 8.77e-03),
+    "8.ffn_norm": (0.999579, 3.27e-02, 1.00e-03),
+    "7.ffn_norm": (0.999550, 3.15e-02, 9.99e-04),
+    "7.wq": (0.999508, 3.52e-02, 8.84e-03),
+    "7.wk": (0.999506, 3.06e-02, 8.91e-03),
+    "6.wk": (0.999515, 3.23e-02, 8.96e-03),
+    "6.attn_norm": (0.999726, 3.59e-02, 9.99e-04),
+    "5.wu": (0.999577, 3.05e-02, 9.48e-03),
+    "5.wq": (0.999519, 3.09e-02, 9.02e-03),
+    "3.wu": (0.999567, 3.04e-02, 9.53e-03),
+    "3.wq": (0.999510, 3.41e-02, 9.35e-03),
+    "2.wg": (0.999552, 3.07e-02, 9.64e-03),
+    "2.wk": (0.999526, 3.08e-02, 9.37e-03),
+    "1.wq": (0.999537, 3.45e-02, 9.49e-03),
+    "0.ffn_norm": (0.999578, 3.28e-02, 1.00e-03),
+    "0.wo": (0.999590, 3.12e-02, 9.46e-03),
+    "0.wq": (0.999540, 3.05e-02, 9.78e-03),
+    "0.attn_norm": (0.999556, 3.49e-02, 1.00e-03),
 }
 
 
