@@ -89,6 +89,29 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_shapes(times):
+    """Per-shape rates of the last timed step's launches (HIP events around
+    each launch on the compute stream; no profiler): GEMMs by (m, n, k,
+    epilogue, operand layout), attention launches by their flop count."""
+    groups = {}
+    for t in times:
+        key = ("gemm", t["m"], t["n"], t["k"], t["epi"], t["layout"]) if t["kind"] == 0 else ("attention", t["flops"])
+        g = groups.setdefault(key, [0, 0.0, 0.0])
+        g[0] += 1
+        g[1] += t["ms"]
+        g[2] += t["flops"]
+    out = []
+    for key, (n, ms, fl) in sorted(groups.items(), key=lambda kv: -kv[1][2]):
+        row = {"kind": key[0], "launches": n, "avg_ms": ms / n, "tflops": fl / (ms / 1e3) / 1e12 if ms > 0 else None,
+               "frac_of_peak": fl / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS if ms > 0 else None}
+        if key[0] == "gemm":
+            row.update(m=key[1], n=key[2], k=key[3], epi=key[4], layout=key[5])
+        else:
+            row.update(flops=key[1])
+        out.append(row)
+    return out
+
+
 def flops(shape, n_layers=None):
     """(forward flops of one layer, model flops per step, flops the device
     executes per step).  Model flops exclude the recompute and count
@@ -368,6 +391,7 @@ def main():
             f"stall {st['stall_ms']:.1f} ms adam {st['adam_ms']:.0f} ms (tail {st['adam_tail_ms']:.0f})")
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
+    kshapes = kernel_shapes(model.kernel_times()) if flags & mt.MT_FLAG_TIME_KERNELS else None
 
     fwd_layer, model_flops, hw_flops = flops(shape)
     hw_flops -= R * (fwd_layer - 2.0 * shape.tokens * shape.d_model * shape.d_ff)  # retained layers skip their recompute
@@ -444,6 +468,7 @@ def main():
                              "d2h": d2h},
             "attention": {"ms_per_step": attn_ms / args.steps,
                           "tflops": attn_fl / (attn_ms / 1e3) / 1e12 if attn_ms > 0 else None},
+            "kernel_shapes": kshapes,
         },
     }
     model.close()

@@ -75,6 +75,11 @@ class MtBlockStats(ctypes.Structure):
                  "adam_ms")]
 
 
+class MtKernelTime(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("kind", "m", "n", "k", "epi", "layout")] + \
+               [(n, ctypes.c_double) for n in ("flops", "bytes", "ms")]
+
+
 class MtSchedOp(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("lane", "kind", "use", "block", "wslot", "gslot", "n_waits",
                                               "n_link")] + \
@@ -143,6 +148,7 @@ _SIGS = {
     "mt_embed_fwd": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
     "mt_embed_bwd": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
     "mt_schedule": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
+    "mt_get_kernel_times": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
     "mt_last_error": (ctypes.c_char_p, []),
     "mt_version": (ctypes.c_char_p, []),
     "mt_gemm": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
@@ -409,6 +415,15 @@ class Model:
         s = MtStats()
         check(lib().mt_get_stats(self.handle, ctypes.byref(s)))
         return {f: getattr(s, f) for f, _ in MtStats._fields_ if f != "pad_"}
+
+    def kernel_times(self) -> list:
+        """Every timed launch of the last step (MT_FLAG_TIME_KERNELS), as dicts."""
+        n = lib().mt_get_kernel_times(self.handle, None, 0)
+        if n < 0:
+            check(n)
+        out = (MtKernelTime * n)()
+        check(min(0, lib().mt_get_kernel_times(self.handle, out, n)))
+        return [{f: getattr(o, f) for f, _ in MtKernelTime._fields_} for o in out]
 
     def block_stats(self, block: int) -> dict:
         s = MtBlockStats()

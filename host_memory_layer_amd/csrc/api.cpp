@@ -348,6 +348,13 @@ int mt_get_stats(const mt_model* model, mt_stats* out) {
   });
 }
 
+int mt_get_kernel_times(const mt_model* model, mt_kernel_time* out, int32_t capacity) {
+  return guarded([&] {
+    if (!model) throw ApiError{MT_E_INVALID, "null model"};
+    return model_kernel_times(M_(model), out, capacity);
+  });
+}
+
 int mt_get_block_stats(const mt_model* model, int block, mt_block_stats* out) {
   return guarded([&] {
     if (!model || !out) throw ApiError{MT_E_INVALID, "null argument"};

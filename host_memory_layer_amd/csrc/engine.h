@@ -17,6 +17,7 @@ int bind_store(Model* m, void* host, size_t bytes, void* opt, size_t opt_bytes);
 int model_step(Model* m, const int32_t* tokens);
 int model_loss(const Model* m, float* out);
 int model_stats(const Model* m, mt_stats* out);
+int model_kernel_times(const Model* m, mt_kernel_time* out, int32_t capacity);
 int model_block_stats(const Model* m, int block, mt_block_stats* out);
 int model_debug(const Model* m, int layer, void** ckpt, void** row_loss);
 int model_debug_grad(const Model* m, int layer, void** dx);

@@ -164,7 +164,9 @@ struct Model {
   struct KernelMeta {
     double flops, bytes;  // algorithmic work of the launch
     int kind;             // 0 gemm, 1 attention
+    int m, n, k, epi, layout;
   };
+  std::vector<mt_kernel_time> ktimes;  // the last pass's timed launches
   std::vector<KernelMeta> kev_meta;
   size_t kev_used = 0;
 
@@ -425,23 +427,24 @@ struct Model {
     // operands read once, result written once (and the residual read once)
     const double out_b = epi == EPI_STORE ? sizeof(T) : 4.0;
     const double bytes = ((double)m * k + (double)n * k) * sizeof(T) + (double)m * n * (out_b + (epi == EPI_ADD_F32 ? 4 : 0));
-    if (timed) record_kernel_start(2.0 * m * n * k, 0, bytes);
+    if (timed) record_kernel_start(2.0 * m * n * k, 0, bytes, m, n, k, (int)epi, layout);
     if constexpr (std::is_same<T, uint16_t>::value)
       gemm_bf16(A, lda, Bm, ldb, layout, C, ldc, R, ldr, m, n, k, epi, sc, gemm_ws, gemm_ws_size);
     else
       gemm_nt<T>(A, lda, Bm, ldb, C, ldc, R, ldr, m, n, k, epi, sc);
     if (timed) record_kernel_end();
   }
-  void record_kernel_start(double flops, int kind, double bytes = 0.0) {
+  void record_kernel_start(double flops, int kind, double bytes = 0.0, int m = 0, int n = 0, int k = 0, int epi = 0,
+                           int layout = 0) {
     if (kev_used + 2 > kev.size()) {
       hipEvent_t e0, e1;
       MT_HIP(hipEventCreate(&e0));
       MT_HIP(hipEventCreate(&e1));
       kev.push_back(e0);
       kev.push_back(e1);
-      kev_meta.push_back(KernelMeta{0.0, 0.0, 0});
+      kev_meta.push_back(KernelMeta{0.0, 0.0, 0, 0, 0, 0, 0, 0});
     }
-    kev_meta[kev_used / 2] = KernelMeta{flops, bytes, kind};
+    kev_meta[kev_used / 2] = KernelMeta{flops, bytes, kind, m, n, k, epi, layout};
     MT_HIP(hipEventRecord(kev[kev_used], sc));
   }
   void record_kernel_end() {
@@ -1368,9 +1371,11 @@ void Model::finish_stats(bool streamed, double wall_ms) {
     }
     s.fwd_ms = ms_between(ev_c_s[0], ev_c_e[0]);
   }
+  ktimes.clear();
   for (size_t i = 0; i + 1 < kev_used + 1 && i < kev_used; i += 2) {
     const double ms = ms_between(kev[i], kev[i + 1]);
     const auto& meta = kev_meta[i / 2];
+    ktimes.push_back(mt_kernel_time{meta.kind, meta.m, meta.n, meta.k, meta.epi, meta.layout, meta.flops, meta.bytes, ms});
     if (meta.kind == 0) {
       s.gemm_ms += ms;
       s.gemm_flops += meta.flops;
@@ -1573,6 +1578,14 @@ int model_loss(const Model* m, float* out) {
   if (!m->have_loss) throw ApiError{MT_E_STATE, "no completed step"};
   *out = m->last_loss;
   return MT_OK;
+}
+
+int model_kernel_times(const Model* m, mt_kernel_time* out, int32_t capacity) {
+  if (!m->have_loss) throw ApiError{MT_E_STATE, "no step has run"};
+  if (!(m->cfg.flags & MT_FLAG_TIME_KERNELS)) throw ApiError{MT_E_STATE, "kernel times need MT_FLAG_TIME_KERNELS"};
+  if (capacity < 0 || (capacity > 0 && !out)) throw ApiError{MT_E_INVALID, "null out or negative capacity"};
+  for (size_t i = 0; i < m->ktimes.size() && (int64_t)i < capacity; ++i) out[i] = m->ktimes[i];
+  return (int)m->ktimes.size();
 }
 
 int model_stats(const Model* m, mt_stats* out) {

@@ -311,6 +311,20 @@ int mt_get_loss(const mt_model* model, float* out);
  * about ([Methodik]: the ping-pong keeps the GPU busy). */
 int mt_get_stats(const mt_model* model, mt_stats* out);
 int mt_get_block_stats(const mt_model* model, int block, mt_block_stats* out);
+/* With MT_FLAG_TIME_KERNELS: every timed launch of the last step (the last
+ * micro-batch's pass), in launch order, split by kernel so that the step
+ * time [Rendimiento] reports can be traced to each kernel's rate.  Writes up
+ * to `capacity` records and returns how many there are, or a negative error
+ * (MT_E_STATE before the first step or without the flag). */
+typedef struct mt_kernel_time {
+  int32_t kind;          /* 0: GEMM, 1: attention */
+  int32_t m, n, k;       /* GEMM: C [m x n] contracted over k (0 for attention) */
+  int32_t epi, layout;   /* GEMM epilogue (0 bf16/store type, 1 fp32, 2 fp32 + residual) and K-major bits */
+  double flops, bytes;   /* algorithmic work: 2mnk (attention: the causal forward's or 2.5x it), and
+                            operands read once plus the result written once */
+  double ms;             /* duration between HIP events around the launch on the compute stream */
+} mt_kernel_time;
+int mt_get_kernel_times(const mt_model* model, mt_kernel_time* out, int32_t capacity);
 /* Device addresses inside the arena for inspection by tests: the fp32 (bf16
  * with MT_FLAG_CKPT_BF16) layer-boundary checkpoint x^l [batch*seq_len x
  * d_model] (l = 0..n_layers)

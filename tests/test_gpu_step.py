@@ -206,6 +206,27 @@ def test_injected_delays_change_nothing(shape, mode, flags):
     assert r["stats"]["step_ms"] > ref["stats"]["step_ms"]
 
 
+def test_kernel_times_add_up_to_the_step_totals():
+    """mt_get_kernel_times: one record per timed launch of the last step,
+    GEMM flops 2mnk, and the records sum to the step's totals."""
+    need_gpu()
+    shape = SMALL_L4
+    cfg, store = make_store(shape, flags=mt.MT_FLAG_TIME_KERNELS)
+    model = mt.Model(cfg, store, "cuda:0")
+    model.step(datagen.tokens(shape))
+    st, kt = model.stats(), model.kernel_times()
+    model.close()
+    store.free()
+    g = [t for t in kt if t["kind"] == 0]
+    a = [t for t in kt if t["kind"] == 1]
+    assert len(g) == st["gemm_launches"] and len(a) == st["attn_launches"] > 0
+    assert all(t["flops"] == 2.0 * t["m"] * t["n"] * t["k"] and t["ms"] > 0 for t in g)
+    assert abs(sum(t["ms"] for t in g) - st["gemm_ms"]) <= 1e-6 * st["gemm_ms"]
+    assert sum(t["flops"] for t in g) == st["gemm_flops"]
+    # 15 GEMMs per layer (forward, recompute without the down projection, backward) and 3 in the head
+    assert len(g) == 15 * shape.n_layers + 3
+
+
 def test_repeated_step_is_deterministic_and_t_advances():
     need_gpu()
     shape = datagen.PRESETS["tiny"]

@@ -51,6 +51,7 @@ def test_struct_sizes_match_header():
     assert ctypes.sizeof(mt.MtBlockDesc) == 16 + 8 * 8 + 8 * 16 + 2 * 8
     assert ctypes.sizeof(mt.MtStats) == 15 * 8 + 2 * 8 + 8 + 2 * 4 + 8
     assert ctypes.sizeof(mt.MtSchedOp) == (8 + mt.MT_SCHED_MAX_WAITS + 2) * 4
+    assert ctypes.sizeof(mt.MtKernelTime) == 6 * 4 + 3 * 8
 
 
 @pytest.mark.parametrize("name,dtype", [(n, None) for n in datagen.PRESETS] +
@@ -349,6 +350,7 @@ def test_api_errors_without_device():
     assert L.mt_create_model(ctypes.byref(cfg), 0x1001, 1 << 30, streams, ctypes.byref(h)) == mt.MT_E_ALIGN
     assert L.mt_create_model(ctypes.byref(cfg), 0x1000, 16, streams, ctypes.byref(h)) == mt.MT_E_SIZE
     assert L.mt_debug_grad(None, 0, ctypes.byref(h)) == mt.MT_E_INVALID
+    assert L.mt_get_kernel_times(None, None, 0) == mt.MT_E_INVALID
     out = (ctypes.c_double * 3)()
     assert L.mt_link_probe(None, None, None, None, 1 << 20, 2, 0, None, out) == mt.MT_E_INVALID
     assert L.mt_link_probe(0x1000, 0x2000, 0x3000, 0x4000, 0, 2, 0, None, out) == mt.MT_E_INVALID
