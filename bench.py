@@ -29,12 +29,12 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 
 # HBM traffic of the bf16 GEMM at the 14B shape, bytes per launch averaged
-# over the 723 launches of a step: rocprofv3 FETCH_SIZE and WRITE_SIZE,
+# over the 627 launches of a step (the grouped weight-gradient launch counts once): rocprofv3 FETCH_SIZE and WRITE_SIZE,
 # scaled by what each reads for a plain 1 GiB copy kernel in the same run
 # (profiles/gemm_14b_pmc_traffic.md).  Valid only for the GEMM source it was
 # measured on; reported as null once that file changes.
-GEMM_TRAFFIC = {"source_sha256_16": "f465259c6307aa15", "config": "14b", "layers": 48,
-                "bytes_per_launch": 9.499e9 + 0.741e9}
+GEMM_TRAFFIC = {"source_sha256_16": "a1c148a5d1caa1b9", "config": "14b", "layers": 48,
+                "bytes_per_launch": 10.553e9 + 0.848e9}
 
 
 def gemm_traffic(shape_name, layers):
@@ -92,10 +92,16 @@ def log(*a):
 def kernel_shapes(times):
     """Per-shape rates of the last timed step's launches (HIP events around
     each launch on the compute stream; no profiler): GEMMs by (m, n, k,
-    epilogue, operand layout), attention launches by their flop count."""
+    epilogue, operand layout), the grouped weight-gradient launches and the
+    attention launches by their flop count."""
     groups = {}
     for t in times:
-        key = ("gemm", t["m"], t["n"], t["k"], t["epi"], t["layout"]) if t["kind"] == 0 else ("attention", t["flops"])
+        if t["kind"] == 0:
+            key = ("gemm", t["m"], t["n"], t["k"], t["epi"], t["layout"])
+        elif t["kind"] == 2:  # the layer's grouped weight gradients (down, gate/up, output projection)
+            key = ("gemm_group", t["flops"])
+        else:
+            key = ("attention", t["flops"])
         g = groups.setdefault(key, [0, 0.0, 0.0])
         g[0] += 1
         g[1] += t["ms"]
@@ -107,7 +113,7 @@ def kernel_shapes(times):
         if key[0] == "gemm":
             row.update(m=key[1], n=key[2], k=key[3], epi=key[4], layout=key[5])
         else:
-            row.update(flops=key[1])
+            row.update(flops_per_launch=key[1])
         out.append(row)
     return out
 

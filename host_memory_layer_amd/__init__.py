@@ -80,6 +80,11 @@ class MtKernelTime(ctypes.Structure):
                [(n, ctypes.c_double) for n in ("flops", "bytes", "ms")]
 
 
+class MtGemmDesc(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_void_p), ("lda", ctypes.c_int64), ("B", ctypes.c_void_p), ("ldb", ctypes.c_int64),
+                ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64), ("M", ctypes.c_int32), ("N", ctypes.c_int32)]
+
+
 class MtSchedOp(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("lane", "kind", "use", "block", "wslot", "gslot", "n_waits",
                                               "n_link")] + \
@@ -159,6 +164,9 @@ _SIGS = {
                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                   ctypes.c_void_p]),
     "mt_gemm_ws_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
+    "mt_gemm_group_ws": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "mt_gemm_group_ws_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32]),
     "mt_gemm_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,

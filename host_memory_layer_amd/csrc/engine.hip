@@ -65,7 +65,7 @@ struct Acts {  // forward intermediates of one layer
 
 template <typename T>
 struct BwdWs {  // backward workspace (one set)
-  T *dxb, *dxbT, *tmpT, *dy, *dgu, *dguT, *do_, *dqkvT, *dqkv;
+  T *dxb, *dxb1, *dxbT, *tmpT, *dy, *dgu, *dguT, *do_, *dqkvT, *dqkv;
   float *dh, *dx1, *Dsum, *part, *dxA, *dxB;
 };
 
@@ -200,6 +200,8 @@ struct Model {
     const uint64_t Md = (uint64_t)M * d, CF = (uint64_t)TC * F, Cd = (uint64_t)TC * d;
     const bool tc = n_tc > 1;
     w.dxb = c.take<T>(Md * E);
+    // bf16(dl/dx1) beside bf16(dl/dx2): the grouped weight gradients read both
+    w.dxb1 = kmajor && !tc ? c.take<T>(Md * E) : nullptr;
     w.dxbT = kmajor ? nullptr : c.take<T>((uint64_t)d * Mp * E);
     w.tmpT = kmajor && kmajor_head ? nullptr : c.take<T>((uint64_t)std::max(d, F) * Mp * E);
     w.dy = c.take<T>(CF * E);
@@ -287,6 +289,10 @@ struct Model {
                                {M, F, d},         {2 * F, d, M}, {M, d, 2 * F},    {d, d, M},  {3 * d, d, M},
                                {M, d, 3 * d},     {V, d, HC},    {HC, V, d},       {HC, d, V}};
       for (const auto& sh : shapes) gemm_ws_size = std::max(gemm_ws_size, gemm_ws_bytes(sh[0], sh[1], sh[2]));
+      if (kmajor && n_tc == 1) {
+        const int gm[3] = {2 * F, d, d}, gn[3] = {d, F, d};
+        gemm_ws_size = std::max(gemm_ws_size, gemm_group_ws_bytes(gm, gn, 3, M));
+      }
       gemm_ws = gemm_ws_size ? c.take<float>(gemm_ws_size) : nullptr;
       if (!base) gemm_ws = nullptr;
     }
@@ -434,6 +440,25 @@ struct Model {
       gemm_nt<T>(A, lda, Bm, ldb, C, ldc, R, ldr, m, n, k, epi, sc);
     if (timed) record_kernel_end();
   }
+  // The layer's down, gate/up and output projection weight gradients in one
+  // launch (K-major operands, contraction over the M tokens): their tiles
+  // fill the device together where the output projection's 400 tiles alone
+  // leave a half-empty last round.
+  void wgrad_group(const uint16_t* dxb2, const uint16_t* y, uint16_t* gd, const uint16_t* dgu, const uint16_t* h2,
+                   uint16_t* ggu, const uint16_t* dxb1, const uint16_t* o, uint16_t* go) {
+    const GemmDesc g[3] = {{dgu, 2 * (int64_t)F, h2, d, ggu, d, 2 * F, d},
+                           {dxb2, d, y, F, gd, F, d, F},
+                           {dxb1, d, o, d, go, d, d, d}};
+    const bool timed = cfg.flags & MT_FLAG_TIME_KERNELS;
+    double flops = 0.0, bytes = 0.0;
+    for (const auto& p : g) {
+      flops += 2.0 * p.M * p.N * M;
+      bytes += ((double)p.M + p.N) * M * 2 + (double)p.M * p.N * 2;
+    }
+    if (timed) record_kernel_start(flops, 2, bytes, 0, 0, M, (int)EPI_STORE, GEMM_A_KMAJOR | GEMM_B_KMAJOR);
+    gemm_bf16_group(g, 3, M, GEMM_A_KMAJOR | GEMM_B_KMAJOR, EPI_STORE, sc, gemm_ws, gemm_ws_size);
+    if (timed) record_kernel_end();
+  }
   void record_kernel_start(double flops, int kind, double bytes = 0.0, int m = 0, int n = 0, int k = 0, int epi = 0,
                            int layout = 0) {
     if (kev_used + 2 > kev.size()) {
@@ -532,17 +557,19 @@ struct Model {
     // down projection; ws.dxb = bf16(dx2) was written beside dx2 by the norm
     // backward that produced it (the layer above, or the head)
     if (dxb_holds != dx2) throw ApiError{MT_E_STATE, "K-major layer backward: bf16 copy does not mirror its dx"};
-    gemm<T>(ws.dxb, d, a.y, F, g.d, F, nullptr, 0, d, F, M, EPI_STORE, KA | KB);
     gemm<T>(ws.dxb, d, w.d, F, ws.dy, F, nullptr, 0, M, F, d, EPI_STORE, KB);
     // SwiGLU and gate/up projection
     swiglu_bwd<T>(ws.dy, a.gu, ws.dgu, M, F, sc);
-    gemm<T>(ws.dgu, 2 * F, a.h2, d, g.gu, d, nullptr, 0, 2 * F, d, M, EPI_STORE, KA | KB);
     gemm<T>(ws.dgu, 2 * F, w.gu, d, ws.dh, d, nullptr, 0, M, d, 2 * F, EPI_F32, KB);
-    rmsnorm_bwd<T>(ws.dh, a.x1, w.fnorm, a.r2, dx2, ws.dx1, ws.part, g.fnorm, M, d, sc, ws.dxb);
-    dxb_holds = ws.dx1;
-    // attention output projection (ws.dxb = bf16(dx1))
-    gemm<T>(ws.dxb, d, a.o, d, g.o, d, nullptr, 0, d, d, M, EPI_STORE, KA | KB);
-    gemm<T>(ws.dxb, d, w.o, d, ws.do_, d, nullptr, 0, M, d, d, EPI_STORE, KB);
+    // dl/dx1, and bf16(dl/dx1) beside bf16(dl/dx2) (still in ws.dxb)
+    rmsnorm_bwd<T>(ws.dh, a.x1, w.fnorm, a.r2, dx2, ws.dx1, ws.part, g.fnorm, M, d, sc, ws.dxb1);
+    // attention output projection
+    gemm<T>(ws.dxb1, d, w.o, d, ws.do_, d, nullptr, 0, M, d, d, EPI_STORE, KB);
+    // weight gradients of the down, gate/up and output projections
+    if constexpr (std::is_same<T, uint16_t>::value)
+      wgrad_group(ws.dxb, a.y, g.d, ws.dgu, a.h2, g.gu, ws.dxb1, a.o, g.o);
+    else
+      throw ApiError{MT_E_STATE, "K-major layer backward needs a bf16 store"};
     // attention
     attn_bwd_dsum<T>(ws.do_, a.o, ws.Dsum, B, Tq, H, hd, sc);
     const bool timed = cfg.flags & MT_FLAG_TIME_KERNELS;
@@ -1376,7 +1403,7 @@ void Model::finish_stats(bool streamed, double wall_ms) {
     const double ms = ms_between(kev[i], kev[i + 1]);
     const auto& meta = kev_meta[i / 2];
     ktimes.push_back(mt_kernel_time{meta.kind, meta.m, meta.n, meta.k, meta.epi, meta.layout, meta.flops, meta.bytes, ms});
-    if (meta.kind == 0) {
+    if (meta.kind == 0 || meta.kind == 2) {
       s.gemm_ms += ms;
       s.gemm_flops += meta.flops;
       s.gemm_bytes += meta.bytes;

@@ -224,6 +224,30 @@ __host__ __device__ inline int64_t sk_cut(int v, int nwg, int64_t total, int nk)
   return x;
 }
 
+// The problems one launch of k_gemm_bf16_tile computes: one, or a group
+// that shares K and the operand layouts (a layer's weight gradients), whose
+// tiles form one combined order, problem after problem, split over the
+// persistent workgroups as a single tile space.
+struct GemmProblem {
+  const uint16_t* A;
+  const uint16_t* B;
+  void* C;
+  int64_t lda, ldb, ldc;
+  int M, N, tiles_m, tiles_n;
+  int t0;  // first tile of the problem in the combined order
+};
+struct GemmGroup {
+  GemmProblem p[kGemmGroupMax];
+  int n;
+  int ntiles;  // tiles of all problems
+};
+// the problem holding combined tile t (problems are few: a linear scan)
+__device__ inline int problem_of(const GemmGroup& G, int t) {
+  int i = 0;
+  while (i + 1 < G.n && t >= G.p[i + 1].t0) ++i;
+  return i;
+}
+
 // VEC: N and ldc multiples of 4 and C 16-byte aligned, so every lane writes
 // 4 consecutive outputs per store through a buffer descriptor that drops
 // rows past M, while lanes past N aim beyond the descriptor.  Otherwise
@@ -231,12 +255,16 @@ __host__ __device__ inline int64_t sk_cut(int v, int nwg, int64_t total, int nk)
 // AKM / BKM: operand A (B) is K-major, [K x M] ([K x N]) with row stride
 // lda (ldb), instead of K-contiguous [M x K] ([N x K]).
 template <int EPI, bool VEC, bool AKM, bool BKM>
-__global__ void __launch_bounds__(256, 1) k_gemm_bf16_tile(const uint16_t* __restrict__ A, int64_t lda,
-                                                       const uint16_t* __restrict__ B, int64_t ldb, void* C,
-                                                       int64_t ldc, const float* R, int64_t ldr, int M, int N, int K,
-                                                       int tiles_m, int tiles_n, float* ws, int t_dp, int maxseg) {
+__global__ void __launch_bounds__(256, 1) k_gemm_bf16_tile(const GemmGroup G, const float* R, int64_t ldr, int K,
+                                                       float* ws, int t_dp, int maxseg) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
-  const int ntiles = tiles_m * tiles_n;
+  const int ntiles = G.ntiles;
+  // the current tile's problem (set by bind below)
+  const uint16_t* A = nullptr;
+  const uint16_t* B = nullptr;
+  void* C = nullptr;
+  int64_t lda = 0, ldb = 0, ldc = 0;
+  int M = 0, N = 0;
   // Persistent schedule.  Workgroup w runs on XCD w % 8 (the dispatcher deals
   // workgroups round-robin over the XCDs); XCD x owns a contiguous range of
   // the grouped tile order, and its workgroups take turns through it.
@@ -314,18 +342,9 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_tile(const uint16_t* __res
   // chunk l%8.  K-major tile [64 k x 256 columns]: rows 2j, 2j+1; lane l
   // reads row 2j + l/32, logical chunk (l%32) ^ kmkey(row).
   int aoff[8], boff[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int j = wave * 8 + i;
-    const int r = 8 * j + (lane >> 3), lc = (lane & 7) ^ ((r >> 1) & 7);
-    const int rk = 2 * j + (lane >> 5), lck = (lane & 31) ^ kmkey(rk);
-    aoff[i] = AKM ? (int)((rk * lda + 8 * lck) * 2) : (int)((r * lda + 8 * lc) * 2);
-    boff[i] = BKM ? (int)((rk * ldb + 8 * lck) * 2) : (int)((r * ldb + 8 * lc) * 2);
-  }
-  const int astep = AKM ? (int)(BK * lda * 2) : BK * 2;  // bytes per K step
-  const int bstep = BKM ? (int)(BK * ldb * 2) : BK * 2;
+  int astep = 0, bstep = 0;  // bytes per K step
   // byte offsets of the item's first K step (kt counts from it)
-  int kofs_a = kb * astep, kofs_b = kb * bstep;
+  int kofs_a = 0, kofs_b = 0;
   auto load_a = [&](i32x4_t rs, int kt, int i) {
     dma16(rs, smem + (kt & 1) * STAGE + (wave * 8 + i) * 1024, aoff[i], kofs_a + kt * astep);
   };
@@ -358,10 +377,37 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_tile(const uint16_t* __res
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[set][j], a[set][i], acc[i][j], 0, 0, 0);
   };
 
-  int64_t m0, n0;
-  tile_of(tc, tiles_m, tiles_n, m0, n0);
-  i32x4_t ar = AKM ? rsrc_km(A, m0, lda) : orsrc_of(A, m0, M, lda);
-  i32x4_t br = BKM ? rsrc_km(B, n0, ldb) : orsrc_of(B, n0, N, ldb);
+  int64_t m0 = 0, n0 = 0;
+  i32x4_t ar, br;
+  // Bind the work item's tile: its problem's operands, strides and output,
+  // the per-lane load offsets, the tile origin and the operand descriptors.
+  auto bind = [&]() {
+    const GemmProblem& P = G.p[problem_of(G, tc)];
+    A = P.A;
+    B = P.B;
+    C = P.C;
+    lda = P.lda;
+    ldb = P.ldb;
+    ldc = P.ldc;
+    M = P.M;
+    N = P.N;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = wave * 8 + i;
+      const int r = 8 * j + (lane >> 3), lc = (lane & 7) ^ ((r >> 1) & 7);
+      const int rk = 2 * j + (lane >> 5), lck = (lane & 31) ^ kmkey(rk);
+      aoff[i] = AKM ? (int)((rk * lda + 8 * lck) * 2) : (int)((r * lda + 8 * lc) * 2);
+      boff[i] = BKM ? (int)((rk * ldb + 8 * lck) * 2) : (int)((r * ldb + 8 * lc) * 2);
+    }
+    astep = AKM ? (int)(BK * lda * 2) : BK * 2;
+    bstep = BKM ? (int)(BK * ldb * 2) : BK * 2;
+    kofs_a = kb * astep;
+    kofs_b = kb * bstep;
+    tile_of(tc - P.t0, P.tiles_m, P.tiles_n, m0, n0);
+    ar = AKM ? rsrc_km(A, m0, lda) : orsrc_of(A, m0, M, lda);
+    br = BKM ? rsrc_km(B, n0, ldb) : orsrc_of(B, n0, N, ldb);
+  };
+  bind();
 
   // One K step.  LOAD_B: load B of step kt+1 during sub-step 0; LOAD_A2:
   // load A of step kt+2 during sub-step 3; NEXT: read step kt+1's first
@@ -564,11 +610,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_tile(const uint16_t* __res
     // Next tile: its loads go out right behind this tile's stores, so the
     // store drain, the load latency and the next tile's start overlap.
     if (!take()) break;
-    tile_of(tc, tiles_m, tiles_n, m0, n0);
-    ar = AKM ? rsrc_km(A, m0, lda) : orsrc_of(A, m0, M, lda);
-    br = BKM ? rsrc_km(B, n0, ldb) : orsrc_of(B, n0, N, ldb);
-    kofs_a = kb * astep;
-    kofs_b = kb * bstep;
+    bind();
     prologue();
   }
 }
@@ -578,11 +620,10 @@ __global__ void __launch_bounds__(256, 1) k_gemm_bf16_tile(const uint16_t* __res
 // K order (so the result depends only on the shapes), then the epilogue.
 // Each thread takes 4 consecutive columns of one row of the 256 x 256 tile.
 template <int EPI>
-__global__ void __launch_bounds__(256) k_gemm_sk_fixup(const float* __restrict__ ws, void* C, int64_t ldc,
-                                                       const float* R, int64_t ldr, int M, int N, int K, int tiles_m,
-                                                       int tiles_n, int t_dp, int nwg, int maxseg) {
+__global__ void __launch_bounds__(256) k_gemm_sk_fixup(const float* __restrict__ ws, const GemmGroup G, const float* R,
+                                                       int64_t ldr, int K, int t_dp, int nwg, int maxseg) {
   const int nk = K / BK;
-  const int ntiles = tiles_m * tiles_n;
+  const int ntiles = G.ntiles;
   const int64_t total = (int64_t)(ntiles - t_dp) * nk;
   const int tt = blockIdx.y;
   const int64_t lo = (int64_t)tt * nk, hi = lo + nk;
@@ -609,8 +650,12 @@ __global__ void __launch_bounds__(256) k_gemm_sk_fixup(const float* __restrict__
     s2 += p.z;
     s3 += p.w;
   }
+  const GemmProblem& P = G.p[problem_of(G, t_dp + tt)];
+  void* C = P.C;
+  const int64_t ldc = P.ldc;
+  const int M = P.M, N = P.N;
   int64_t m0, n0;
-  tile_of(t_dp + tt, tiles_m, tiles_n, m0, n0);
+  tile_of(t_dp + tt - P.t0, P.tiles_m, P.tiles_n, m0, n0);
   const int64_t gm = m0 + row;
   if (gm >= M) return;
   const float sv[4] = {s0, s1, s2, s3};
@@ -722,37 +767,30 @@ size_t gemm_ws_bytes(int M, int N, int K) {
   return (size_t)persistent_workgroups() * maxseg * BM * BN * sizeof(float);
 }
 
-void gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int layout, void* C, int64_t ldc,
-               const float* R, int64_t ldr, int M, int N, int K, Epi epi, hipStream_t s, float* ws,
-               size_t ws_bytes) {
-  if (M <= 0 || N <= 0) return;
-  if (K % 8 || lda % 8 || ldb % 8 || ((uintptr_t)A & 15) || ((uintptr_t)B & 15))
-    throw ApiError{MT_E_INVALID, "bf16 GEMM needs K, lda, ldb multiples of 8 and 16-byte aligned operands"};
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const dim3 grid(tiles_m * tiles_n);
-  if (layout != 0 && !gemm_layout_ok(M, N, K, lda, ldb, layout))
-    throw ApiError{MT_E_INVALID, "K-major bf16 GEMM operands need K % 64 == 0, K >= 192, K*ld*2 < 2^31"};
-  if (K % BK == 0 && K >= 3 * BK) {
-    // buffer offsets are 32-bit: one 256-row panel of every operand must fit
-    const int64_t lim = (int64_t)1 << 31;
-    if ((!(layout & GEMM_A_KMAJOR) && (int64_t)BM * lda * 2 >= lim) ||
-        (!(layout & GEMM_B_KMAJOR) && (int64_t)BN * ldb * 2 >= lim) || (int64_t)BM * ldc * 4 >= lim ||
-        (R && (int64_t)BM * ldr * 4 >= lim))
-      throw ApiError{MT_E_INVALID, "bf16 GEMM row stride too large"};
-    const bool vec = N % 4 == 0 && ldc % 4 == 0 && ((uintptr_t)C & 15) == 0 &&
-                     (epi != EPI_ADD_F32 || (ldr % 4 == 0 && ((uintptr_t)R & 15) == 0));
-    const int ntiles = tiles_m * tiles_n;
-    const int nwg = std::min(ntiles, persistent_workgroups());
-    const dim3 pgrid(nwg);
-    int t_dp = ntiles, maxseg = 0;
-    if (!ws || !sk_plan(ntiles, K / BK, nwg, &t_dp, &maxseg) ||
-        (size_t)nwg * maxseg * BM * BN * sizeof(float) > ws_bytes) {
-      t_dp = ntiles;  // whole tiles only
-      maxseg = 0;
-    }
-#define L_(E, V, AK, BK_)                                                                                      \
-  hipLaunchKernelGGL((k_gemm_bf16_tile<E, V, AK, BK_>), pgrid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, R, ldr, M, N, \
-                     K, tiles_m, tiles_n, ws, t_dp, maxseg)
+size_t gemm_group_ws_bytes(const int* M, const int* N, int n, int K) {
+  int ntiles = 0;
+  for (int i = 0; i < n; ++i) ntiles += ((M[i] + BM - 1) / BM) * ((N[i] + BN - 1) / BN);
+  int t_dp = 0, maxseg = 0;
+  if (K % BK || !sk_plan(ntiles, K / BK, persistent_workgroups(), &t_dp, &maxseg)) return 0;
+  return (size_t)persistent_workgroups() * maxseg * BM * BN * sizeof(float);
+}
+
+// The persistent tile kernel over a group (one problem or several), then
+// the stream-K tail's segments and their fix-up when a split is planned and
+// the workspace holds it.
+static void launch_tiles(const GemmGroup& G, const float* R, int64_t ldr, int K, int layout, Epi epi, bool vec,
+                         hipStream_t s, float* ws, size_t ws_bytes) {
+  const int ntiles = G.ntiles;
+  const int nwg = std::min(ntiles, persistent_workgroups());
+  const dim3 pgrid(nwg);
+  int t_dp = ntiles, maxseg = 0;
+  if (!ws || !sk_plan(ntiles, K / BK, nwg, &t_dp, &maxseg) ||
+      (size_t)nwg * maxseg * BM * BN * sizeof(float) > ws_bytes) {
+    t_dp = ntiles;  // whole tiles only
+    maxseg = 0;
+  }
+#define L_(E, V, AK, BK_) \
+  hipLaunchKernelGGL((k_gemm_bf16_tile<E, V, AK, BK_>), pgrid, dim3(256), 0, s, G, R, ldr, K, ws, t_dp, maxseg)
 #define LL_(E, V)                  \
   switch (layout) {                \
     case 0: L_(E, V, false, false); break; \
@@ -766,34 +804,99 @@ void gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, i
   } else {         \
     LL_(E, false)  \
   }
-    switch (epi) {
-      case EPI_STORE: LV_(EPI_STORE) break;
-      case EPI_F32: LV_(EPI_F32) break;
-      case EPI_ADD_F32: LV_(EPI_ADD_F32) break;
-      default: throw ApiError{MT_E_INVALID, "GEMM epilogue"};
-    }
+  switch (epi) {
+    case EPI_STORE: LV_(EPI_STORE) break;
+    case EPI_F32: LV_(EPI_F32) break;
+    case EPI_ADD_F32: LV_(EPI_ADD_F32) break;
+    default: throw ApiError{MT_E_INVALID, "GEMM epilogue"};
+  }
 #undef LV_
 #undef LL_
-    if (t_dp < ntiles) {
-      // the tail's segments on every workgroup, then their sums
-      switch (layout) {
-        case 0: L_(EPI_PARTIAL, true, false, false); break;
-        case 1: L_(EPI_PARTIAL, true, true, false); break;
-        case 2: L_(EPI_PARTIAL, true, false, true); break;
-        default: L_(EPI_PARTIAL, true, true, true); break;
-      }
-      const dim3 fgrid(BM * BN / (256 * 4), ntiles - t_dp);
-#define F_(E)                                                                                                       \
-  hipLaunchKernelGGL(k_gemm_sk_fixup<E>, fgrid, dim3(256), 0, s, ws, C, ldc, R, ldr, M, N, K, tiles_m, tiles_n, t_dp, \
-                     nwg, maxseg)
-      switch (epi) {
-        case EPI_STORE: F_(EPI_STORE); break;
-        case EPI_F32: F_(EPI_F32); break;
-        default: F_(EPI_ADD_F32); break;
-      }
-#undef F_
+  if (t_dp < ntiles) {
+    // the tail's segments on every workgroup, then their sums
+    switch (layout) {
+      case 0: L_(EPI_PARTIAL, true, false, false); break;
+      case 1: L_(EPI_PARTIAL, true, true, false); break;
+      case 2: L_(EPI_PARTIAL, true, false, true); break;
+      default: L_(EPI_PARTIAL, true, true, true); break;
     }
+    const dim3 fgrid(BM * BN / (256 * 4), ntiles - t_dp);
+#define F_(E) hipLaunchKernelGGL(k_gemm_sk_fixup<E>, fgrid, dim3(256), 0, s, ws, G, R, ldr, K, t_dp, nwg, maxseg)
+    switch (epi) {
+      case EPI_STORE: F_(EPI_STORE); break;
+      case EPI_F32: F_(EPI_F32); break;
+      default: F_(EPI_ADD_F32); break;
+    }
+#undef F_
+  }
 #undef L_
+}
+
+static void add_problem(GemmGroup& G, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, void* C,
+                        int64_t ldc, int M, int N) {
+  GemmProblem& P = G.p[G.n++];
+  P.A = A;
+  P.B = B;
+  P.C = C;
+  P.lda = lda;
+  P.ldb = ldb;
+  P.ldc = ldc;
+  P.M = M;
+  P.N = N;
+  P.tiles_m = (M + BM - 1) / BM;
+  P.tiles_n = (N + BN - 1) / BN;
+  P.t0 = G.ntiles;
+  G.ntiles += P.tiles_m * P.tiles_n;
+}
+
+// operand checks shared by the single and the grouped launch
+static void check_tile_operands(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t ldc,
+                                const float* R, int64_t ldr, int M, int N, int K, int layout) {
+  if (K % 8 || lda % 8 || ldb % 8 || ((uintptr_t)A & 15) || ((uintptr_t)B & 15))
+    throw ApiError{MT_E_INVALID, "bf16 GEMM needs K, lda, ldb multiples of 8 and 16-byte aligned operands"};
+  if (layout != 0 && !gemm_layout_ok(M, N, K, lda, ldb, layout))
+    throw ApiError{MT_E_INVALID, "K-major bf16 GEMM operands need K % 64 == 0, K >= 192, K*ld*2 < 2^31"};
+  // buffer offsets are 32-bit: one 256-row panel of every operand must fit
+  const int64_t lim = (int64_t)1 << 31;
+  if ((!(layout & GEMM_A_KMAJOR) && (int64_t)BM * lda * 2 >= lim) ||
+      (!(layout & GEMM_B_KMAJOR) && (int64_t)BN * ldb * 2 >= lim) || (int64_t)BM * ldc * 4 >= lim ||
+      (R && (int64_t)BM * ldr * 4 >= lim))
+    throw ApiError{MT_E_INVALID, "bf16 GEMM row stride too large"};
+}
+
+void gemm_bf16_group(const GemmDesc* d, int n, int K, int layout, Epi epi, hipStream_t s, float* ws,
+                     size_t ws_bytes) {
+  if (n < 1 || n > kGemmGroupMax) throw ApiError{MT_E_INVALID, "GEMM group size"};
+  if (epi != EPI_STORE && epi != EPI_F32) throw ApiError{MT_E_INVALID, "grouped GEMM epilogue"};
+  if (K % BK || K < 3 * BK) throw ApiError{MT_E_INVALID, "grouped GEMM needs K % 64 == 0 and K >= 192"};
+  GemmGroup G{};
+  bool vec = true;
+  for (int i = 0; i < n; ++i) {
+    if (d[i].M <= 0 || d[i].N <= 0) throw ApiError{MT_E_INVALID, "grouped GEMM problem size"};
+    check_tile_operands(d[i].A, d[i].lda, d[i].B, d[i].ldb, d[i].ldc, nullptr, 0, d[i].M, d[i].N, K, layout);
+    vec = vec && d[i].N % 4 == 0 && d[i].ldc % 4 == 0 && ((uintptr_t)d[i].C & 15) == 0;
+    add_problem(G, d[i].A, d[i].lda, d[i].B, d[i].ldb, d[i].C, d[i].ldc, d[i].M, d[i].N);
+  }
+  launch_tiles(G, nullptr, 0, K, layout, epi, vec, s, ws, ws_bytes);
+}
+
+void gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int layout, void* C, int64_t ldc,
+               const float* R, int64_t ldr, int M, int N, int K, Epi epi, hipStream_t s, float* ws,
+               size_t ws_bytes) {
+  if (M <= 0 || N <= 0) return;
+  if (K % 8 || lda % 8 || ldb % 8 || ((uintptr_t)A & 15) || ((uintptr_t)B & 15))
+    throw ApiError{MT_E_INVALID, "bf16 GEMM needs K, lda, ldb multiples of 8 and 16-byte aligned operands"};
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const dim3 grid(tiles_m * tiles_n);
+  if (layout != 0 && !gemm_layout_ok(M, N, K, lda, ldb, layout))
+    throw ApiError{MT_E_INVALID, "K-major bf16 GEMM operands need K % 64 == 0, K >= 192, K*ld*2 < 2^31"};
+  if (K % BK == 0 && K >= 3 * BK) {
+    check_tile_operands(A, lda, B, ldb, ldc, R, ldr, M, N, K, layout);
+    const bool vec = N % 4 == 0 && ldc % 4 == 0 && ((uintptr_t)C & 15) == 0 &&
+                     (epi != EPI_ADD_F32 || (ldr % 4 == 0 && ((uintptr_t)R & 15) == 0));
+    GemmGroup G{};
+    add_problem(G, A, lda, B, ldb, C, ldc, M, N);
+    launch_tiles(G, R, ldr, K, layout, epi, vec, s, ws, ws_bytes);
     return;
   }
 #define L_(E)                                                                                                      \

@@ -73,6 +73,39 @@ size_t mt_gemm_ws_bytes(int32_t M, int32_t N, int32_t K) {
   return gemm_ws_bytes(M, N, K);
 }
 
+static_assert(MT_GEMM_GROUP_MAX == kGemmGroupMax, "group size");
+
+int mt_gemm_group_ws(int32_t n, const mt_gemm_desc* d, int32_t K, int32_t epi, int32_t layout, void* ws,
+                     size_t ws_bytes, void* stream) {
+  return kguard([&] {
+    need(n >= 1 && n <= MT_GEMM_GROUP_MAX && d, "group size");
+    need(epi == 0 || epi == 1, "epi");
+    need(layout >= 0 && layout <= 3, "layout");
+    need(((uintptr_t)ws & 15) == 0, "workspace must be 16-byte aligned");
+    GemmDesc g[kGemmGroupMax];
+    for (int i = 0; i < n; ++i) {
+      need(d[i].M > 0 && d[i].N > 0 && K > 0, "sizes");
+      need((layout & MT_GEMM_A_KMAJOR ? d[i].lda >= d[i].M : d[i].lda >= K) &&
+               (layout & MT_GEMM_B_KMAJOR ? d[i].ldb >= d[i].N : d[i].ldb >= K) && d[i].ldc >= d[i].N,
+           "leading dimensions");
+      g[i] = GemmDesc{(const uint16_t*)d[i].A, d[i].lda, (const uint16_t*)d[i].B, d[i].ldb, d[i].C, d[i].ldc,
+                      d[i].M, d[i].N};
+    }
+    gemm_bf16_group(g, n, K, layout, (Epi)epi, (hipStream_t)stream, (float*)ws, ws ? ws_bytes : 0);
+  });
+}
+
+size_t mt_gemm_group_ws_bytes(int32_t n, const mt_gemm_desc* d, int32_t K) {
+  if (n < 1 || n > MT_GEMM_GROUP_MAX || !d || K <= 0) return 0;
+  int M[kGemmGroupMax], N[kGemmGroupMax];
+  for (int i = 0; i < n; ++i) {
+    if (d[i].M <= 0 || d[i].N <= 0) return 0;
+    M[i] = d[i].M;
+    N[i] = d[i].N;
+  }
+  return gemm_group_ws_bytes(M, N, n, K);
+}
+
 int mt_transpose(int32_t dtype, const void* in, int64_t ld_in, void* out, int64_t ld_out, int32_t R, int32_t C,
                  void* stream) {
   return kguard([&] {

@@ -37,6 +37,25 @@ void gemm_bf16(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, i
                size_t ws_bytes = 0);
 // Workspace bytes the split needs for this shape (0: no split planned).
 size_t gemm_ws_bytes(int M, int N, int K);
+// Up to kGemmGroupMax bf16 products sharing K and the operand layout (store
+// or fp32 epilogue, no residual) in one persistent launch: their tiles form
+// one tile space, so one product's partial last round is filled with
+// another's tiles, and a stream-K split covers the group's last round.
+// Every tile is computed as by gemm_bf16; tiles in the group's split tail
+// differ from an unsplit tile by rounding only.
+constexpr int kGemmGroupMax = 3;
+struct GemmDesc {
+  const uint16_t* A;
+  int64_t lda;
+  const uint16_t* B;
+  int64_t ldb;
+  void* C;
+  int64_t ldc;
+  int M, N;
+};
+void gemm_bf16_group(const GemmDesc* d, int n, int K, int layout, Epi epi, hipStream_t s, float* ws = nullptr,
+                     size_t ws_bytes = 0);
+size_t gemm_group_ws_bytes(const int* M, const int* N, int n, int K);
 
 // ---------------------------------------------------------- elementwise --
 template <typename T>

@@ -317,7 +317,8 @@ int mt_get_block_stats(const mt_model* model, int block, mt_block_stats* out);
  * to `capacity` records and returns how many there are, or a negative error
  * (MT_E_STATE before the first step or without the flag). */
 typedef struct mt_kernel_time {
-  int32_t kind;          /* 0: GEMM, 1: attention */
+  int32_t kind;          /* 0: GEMM, 1: attention, 2: the layer's grouped weight-gradient GEMM (down,
+                            gate/up and output projections in one launch; m, n 0, k the tokens) */
   int32_t m, n, k;       /* GEMM: C [m x n] contracted over k (0 for attention) */
   int32_t epi, layout;   /* GEMM epilogue (0 bf16/store type, 1 fp32, 2 fp32 + residual) and K-major bits */
   double flops, bytes;   /* algorithmic work: 2mnk (attention: the causal forward's or 2.5x it), and

@@ -53,6 +53,29 @@ int mt_gemm_ws(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, 
  * current device; 0 when it would not split. */
 size_t mt_gemm_ws_bytes(int32_t M, int32_t N, int32_t K);
 
+/* Up to MT_GEMM_GROUP_MAX bf16 products C_i[M_i x N_i] = A_i . B_i^T that
+ * share K and the operand layout, in one persistent launch: the layer's
+ * weight gradients ([Abstract]: every layer's backward produces them on the
+ * GPU) have one contraction length, the tokens, and together fill the
+ * device where one alone leaves a partial last round.  Each product's tiles
+ * are those of mt_gemm_ws; with a workspace of mt_gemm_group_ws_bytes, the
+ * group's last partial round is split along K as in mt_gemm_ws.  epi 0
+ * (bf16 C) or 1 (fp32 C), no residual.  K % 64 == 0, K >= 192.  Errors:
+ * MT_E_INVALID (group size, shapes, strides, alignment), MT_E_HIP. */
+#define MT_GEMM_GROUP_MAX 3
+typedef struct mt_gemm_desc {
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  void* C;
+  int64_t ldc;
+  int32_t M, N;
+} mt_gemm_desc;
+int mt_gemm_group_ws(int32_t n, const mt_gemm_desc* d, int32_t K, int32_t epi, int32_t layout, void* ws,
+                     size_t ws_bytes, void* stream);
+size_t mt_gemm_group_ws_bytes(int32_t n, const mt_gemm_desc* d, int32_t K);
+
 /* mt_gemm_ws for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
  * stream-K partial tiles go to a static device buffer of the library,

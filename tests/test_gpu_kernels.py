@@ -439,3 +439,61 @@ def test_gemm_stream_k_tail(M, N, K, layout):
     bnd = K * 2.0 ** -24 * np.einsum("ij,ij->i", np.abs(a), np.abs(b))
     got = split[rows, cols].cpu().numpy().astype(np.float64)
     assert np.all(np.abs(got - ref) <= bnd)
+
+
+# --------------------------------------------------------- grouped GEMM --
+def test_gemm_group_is_each_gemm():
+    """mt_gemm_group_ws at the 14B weight-gradient shapes (gate/up, down,
+    output projection; K = 32768 tokens, both operands K-major): without a
+    workspace every product is bit for bit its own mt_gemm_ws; with one, the
+    group's last partial round (tiles of the last product) is split along K,
+    those outputs stay within the fp32 accumulation bound of the unsplit
+    product and the rest is bit-identical; the split result repeats exactly;
+    the bf16 epilogue is the fp32 sum rounded."""
+    dev()
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("tile rounds are planned for 256 compute units")
+    K, d, F = 32768, 5120, 13824
+    shapes = [(2 * F, d), (d, F), (d, d)]
+    print("grouped gemm " + ", ".join(f"{m}x{n}" for m, n in shapes) + f" K {K}", flush=True)
+    g = torch.Generator(device=dev()).manual_seed(7)
+    A = [torch.randn((K, m), generator=g, device=dev()).to(torch.bfloat16).view(torch.int16) for m, _ in shapes]
+    B = [torch.randn((K, n), generator=g, device=dev()).to(torch.bfloat16).view(torch.int16) for _, n in shapes]
+    lay = mt.GEMM_A_KMAJOR | mt.GEMM_B_KMAJOR
+
+    def group(outs, ws, ws_bytes, epi):
+        descs = (mt.MtGemmDesc * 3)(*[mt.MtGemmDesc(A[i].data_ptr(), shapes[i][0], B[i].data_ptr(), shapes[i][1],
+                                                     outs[i].data_ptr(), shapes[i][1], shapes[i][0], shapes[i][1])
+                                      for i in range(3)])
+        mt.check(mt.lib().mt_gemm_group_ws(3, descs, K, epi, lay, ws.data_ptr() if ws is not None else None,
+                                           ws_bytes, None))
+        return descs
+
+    plain = [torch.empty(s, dtype=torch.float32, device=dev()) for s in shapes]
+    for i, (m, n) in enumerate(shapes):
+        gemm_ws(A[i], m, B[i], n, plain[i], n, m, n, K, mt.EPI_F32, None, 0, layout=lay)
+    whole = [torch.empty(s, dtype=torch.float32, device=dev()) for s in shapes]
+    descs = group(whole, None, 0, mt.EPI_F32)
+    need = int(mt.lib().mt_gemm_group_ws_bytes(3, descs, K))
+    assert need > 0  # 3640 tiles: a last round of 56 on 256 workgroups is split
+    ws = torch.empty(need // 4, dtype=torch.float32, device=dev())
+    split = [torch.empty(s, dtype=torch.float32, device=dev()) for s in shapes]
+    again = [torch.empty(s, dtype=torch.float32, device=dev()) for s in shapes]
+    group(split, ws, need, mt.EPI_F32)
+    group(again, ws, need, mt.EPI_F32)
+    sb = [torch.empty(s, dtype=torch.int16, device=dev()) for s in shapes]
+    group(sb, ws, need, mt.EPI_STORE)
+    torch.cuda.synchronize()
+    for i in range(3):
+        assert torch.equal(whole[i], plain[i]), i
+        assert torch.equal(split[i], again[i]), i
+        assert np.array_equal(sb[i].cpu().numpy().view(np.uint16), datagen.f32_to_bf16_bits(split[i].cpu().numpy()))
+    assert torch.equal(split[0], plain[0]) and torch.equal(split[1], plain[1])
+    absprod = torch.mm(A[2].view(torch.bfloat16).float().abs().t().contiguous(), B[2].view(torch.bfloat16).float().abs())
+    diff = (split[2] - plain[2]).abs()
+    assert bool((diff <= 2 * K * 2.0 ** -24 * absprod * 1.001).all())
+    same = float((split[2] == plain[2]).float().mean())
+    assert 0.5 < same < 1.0, same  # 56 of the product's 400 tiles are split
+    bad = (mt.MtGemmDesc * 1)(mt.MtGemmDesc(A[0].data_ptr(), 2 * F, B[0].data_ptr(), d, whole[0].data_ptr(), d, 2 * F, d))
+    assert mt.lib().mt_gemm_group_ws(0, bad, K, 0, lay, None, 0, None) == mt.MT_E_INVALID
+    assert mt.lib().mt_gemm_group_ws(1, bad, K, 2, lay, None, 0, None) == mt.MT_E_INVALID

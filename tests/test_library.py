@@ -190,10 +190,11 @@ def test_long_context_arena_with_passes_and_bf16_checkpoints():
     once the weight-gradient operands outgrow 32-bit addressing, and keep
     the per-layer workspace at about 76 GB at 512K tokens; bf16 checkpoints
     halve the rest, so 512K fits the device.  The 14B-shape step (one pass)
-    is unchanged."""
+    holds one more bf16 [tokens x d] buffer than the pass form needs: the
+    grouped weight gradients read bf16(dl/dx2) and bf16(dl/dx1) together."""
     GB = 1e9
     s7 = datagen.PRESETS["7b"]
-    assert mt.device_bytes(mt.make_config(datagen.PRESETS["14b"])) == 54704961024
+    assert mt.device_bytes(mt.make_config(datagen.PRESETS["14b"])) == 54704961024 + 32768 * 5120 * 2
     for T, fp32_gb, bf16_gb in ((262144, 186.9, 124.6), (524288, 359.2, 234.6)):
         s = s7.replace(batch=1, seq_len=T)
         a = mt.device_bytes(mt.make_config(s)) / GB
