@@ -256,6 +256,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
     }
   };
   issue(0, 0);
+  vm_wait_all();
   for (int kb = 0; kb < nkb; kb += 2) {
     key_block(kb, std::integral_constant<int, 0>{});
     if (kb + 1 < nkb) key_block(kb + 1, std::integral_constant<int, 1>{});
@@ -583,6 +584,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_dq_bf16(const uint16_t* __restr
     }
   };
   issue(0, 0);
+  vm_wait_all();
   for (int kb = 0; kb < nkb; kb += 2) {
     key_tile(kb, std::integral_constant<int, 0>{});
     if (kb + 1 < nkb) key_tile(kb + 1, std::integral_constant<int, 1>{});

@@ -34,6 +34,15 @@ __device__ inline void dma16(i32x4_t rsrc, const void* lds_dst, int voff, int so
                : "memory", "m0");
 }
 
+// s_waitcnt vmcnt(0) as an instruction the compiler knows (expcnt and
+// lgkmcnt left at their maxima, 7 and 15).  The compiler tracks only the
+// global loads it issued itself; one still pending where a loop begins makes
+// it wait for it inside the loop, and the hardware counter there also counts
+// the direct loads of the next tile just issued, so that wait would drain the
+// prefetch.  Called before such a loop, it retires the register loads ahead
+// of it and no wait is left inside.
+__device__ inline void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
