@@ -89,6 +89,21 @@ __device__ inline BlockXY xcd_block() {
   return BlockXY{l % gx, l / gx};
 }
 
+// x of this lane combined with x of lane l ^ 32 (the partner half-wave) by
+// one lane swap between the wave's halves (v_permlane32_swap), instead of a
+// shuffle through LDS and its lane-index arithmetic.  The swap leaves lane l
+// holding x[l] and x[l ^ 32] in the two halves of the result, lower lane's
+// value first; max and + are commutative, so the result is that of
+// op(x, shuffle_xor(x, 32)).
+__device__ inline float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Row index inside a 32x32 accumulator tile for register r of this lane.
 __device__ inline int acc_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
 
@@ -219,7 +234,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_acc[kt][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+      mx = max_halves(mx) * c;
       // Lazy rescaling: the reference max m_i moves only when the block max
       // exceeds it by more than 8 (in log2 units), so probabilities stay
       // below 2^8; the final O / l uses the same reference, so the result is
@@ -243,7 +258,7 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
           s_acc[kt][r] = p;
           rs += p;
         }
-      l_i += rs + __shfl_xor(rs, 32);
+      l_i += sum_halves(rs);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8_t pf = acc_to_frag(s_acc[ks >> 1], ks & 1);
