@@ -210,30 +210,16 @@ __global__ void __launch_bounds__(256, 2) k_attn_fwd_bf16(const uint16_t* __rest
     // Every wave runs every key block: a block wholly after the wave's
     // queries is fully masked (P = 0) and changes neither m nor l.
     {
-      // The two 32-key tiles' score chains run interleaved, and each step's
-      // K fragments are read two steps (four MFMAs) before their use: reads
-      // of steps 0 and 1, then per step two MFMAs and the reads of step s+2
-      // (scheduling groups: LDS reads 0x100, MFMA 0x008).  Each chain keeps
-      // its own order, so this is bit-identical to one tile after the other.
-      f32x16_t s_acc[2] = {zero16(), zero16()};
-      bf16x8_t kf[8][2];
+      f32x16_t s_acc[2];
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
+      for (int kt = 0; kt < 2; ++kt) {
+        s_acc[kt] = zero16();
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-          kf[s][kt] = *(const bf16x8_t*)(Ks + sw256(32 * kt + (lane & 31), 2 * s + (lane >> 5)));
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-          s_acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s][kt], qf[s], s_acc[kt], 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int q = 0; q < 6; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int s = 0; s < 8; ++s) {
+          bf16x8_t kf = *(const bf16x8_t*)(Ks + sw256(32 * kt + (lane & 31), 2 * s + (lane >> 5)));
+          s_acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], s_acc[kt], 0, 0, 0);
+        }
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       // Only blocks that reach past the wave's first query need the causal
       // mask (wave-uniform branch).
       if (kb * 64 + 63 > q0) {
