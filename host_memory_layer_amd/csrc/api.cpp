@@ -138,7 +138,7 @@ int mt_alloc_host_store(size_t bytes, void** out) {
       throw ApiError{MT_E_OOM, std::string("hipHostMalloc: ") + hipGetErrorString(e)};
     }
     if ((uintptr_t)p % kStoreAlign) {
-      hipHostFree(p);
+      (void)hipHostFree(p);
       throw ApiError{MT_E_ALIGN, "pinned allocation not 4 KiB aligned"};
     }
     *out = p;
@@ -147,7 +147,7 @@ int mt_alloc_host_store(size_t bytes, void** out) {
 }
 
 void mt_free_host_store(void* p) {
-  if (p) hipHostFree(p);
+  if (p) (void)hipHostFree(p);  // nothing to report from a void free
 }
 
 int mt_alloc_host_opt(size_t bytes, void** out) {
